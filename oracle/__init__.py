@@ -1,0 +1,23 @@
+"""fp64 CPU oracle for RLT exact replay (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package.
+"""
+from .rlt_oracle import (  # noqa: F401
+    OracleModel,
+    OracleState,
+    attend,
+    causal_attention,
+    decode,
+    decoder_step,
+    encode,
+    gelu,
+    init_state,
+    logits,
+    replay,
+    replay_batch,
+    rms_norm,
+    sigmoid,
+    silu,
+    step,
+)
