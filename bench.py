@@ -1,0 +1,181 @@
+"""RLT exact-replay benchmark on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic sequences:
+state reset to H_0, causal encoder over all T tokens (e_t and memory M), the
+recurrent decoder over t = 1..T for all B sequences (one persistent launch), and
+logits for every position.  value = B*T / step time (tokens/s), inputs resident in
+HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--config small] [--no-cpu-baseline]
+
+Prints ONE JSON line.  Extra per-phase timings (HIP events on the launch stream)
+and the decoder kernel's roofline figures are included in the same line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_decoder_bytes(cfg, B: int, T: int) -> float:
+    """Bytes the decoder replay must move, summed over t = 1..T for the whole batch.
+
+    Per step: the in-loop weights once (shared by the B sequences), and per sequence
+    the window cache read + write, every layer's read of memory entries 1..t, e_t in
+    and s_t out (fp32, plus the fp32 state)."""
+    d, L, F, W = cfg.d_model, cfg.n_layers, cfg.ffn_dim, cfg.window
+    p = 2 if cfg.dtype == "bf16" else 4
+    ffn = (2 if cfg.ffn_kind == "gelu" else 3) * d * F
+    p_loop = L * (6 * d * d + ffn) + 2 * d * d
+    total = 0.0
+    for t in range(1, T + 1):
+        ring = L * 2 * d * p * (min(t - 1, W - 1) + 1)
+        mem = L * 2 * d * p * t
+        io = d * (p + 4 + 4)
+        total += p_loop * p + B * (ring + mem + io)
+    return total
+
+
+def _oracle_one(args):
+    """Worker: oracle replay of one sequence (imports only numpy/scipy and the oracle)."""
+    cfg, weights, tok, t_limit = args
+    import oracle
+    m = oracle.OracleModel.from_config(cfg, weights)
+    return oracle.replay(m, tok, t_limit)
+
+
+def cpu_baseline(wl, weights, tokens, budget_s: float = 20.0):
+    """The fp64 oracle (test infrastructure) timed on this host's cores over a bounded
+    sample of whole sequences of the same workload."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    # one probe sequence prefix sizes the sample to about budget_s of CPU work
+    t_probe = min(wl.seq_len, 128)
+    t0 = time.perf_counter()
+    _oracle_one((wl.model, weights, tokens[0], t_probe))
+    probe = time.perf_counter() - t0
+    # cost grows ~linearly in t for the memory part; scale by (T/t_probe)^1.5 as an estimate
+    est_seq = probe * (wl.seq_len / t_probe) ** 1.5
+    n_seq = int(max(1, min(wl.batch, round(budget_s / max(est_seq, 1e-3)))))
+    workers = min(cores, n_seq)
+    jobs = [(wl.model, weights, tokens[b], None) for b in range(n_seq)]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_one, jobs)
+    wall = time.perf_counter() - t0
+    return {"value": n_seq * wl.seq_len / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{n_seq} of {wl.batch} sequences x T={wl.seq_len} (full replay incl. encoder and logits), "
+                      f"fp64 numpy, one sequence per worker process, {wall:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="small")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the replay shards over sequences with no communication, "
+              "so a multi-GPU figure is not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import cross_token_recurrent_amd as rlt
+    from workloads import CONFIGS, make_tokens, make_weights
+
+    wl = CONFIGS[args.config]
+    cfg = wl.model
+    B, T = wl.batch, wl.seq_len
+    dev = torch.device("cuda:0")
+    weights = make_weights(cfg, wl.weight_seed)
+    tokens = make_tokens(cfg.vocab, B, T, wl.token_dist, wl.token_seed)
+
+    model = rlt.Model(cfg, weights, device=dev)
+    state = rlt.State(model, B, T, keep_encoder_cache=False)
+    tok = torch.from_numpy(tokens).to(dev)
+    S = torch.empty(B, T, cfg.d_model, dtype=torch.float32, device=dev)
+    Z = torch.empty(B, T, cfg.vocab, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        state.reset()
+        rlt.rlt_encoder_forward(model, state, tok)
+        if ev:
+            ev[1].record(stream)
+        rlt.rlt_decoder_replay(model, state, T, S)
+        if ev:
+            ev[2].record(stream)
+        rlt.rlt_logits(model, S, Z)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    head_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+
+    path = model.decoder_path(B)
+    dec_bytes = algorithmic_decoder_bytes(cfg, B, T)
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    line = {
+        "metric": "RLT replay decoder tokens/sec (B*T/s) at 1 GPU; % of HBM/MFMA roofline",
+        "value": B * T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,0.02) weights, uniform/Zipf token ids)",
+        "config": {"workload": f"{wl.name}: RLT d={cfg.d_model} H={cfg.n_heads} L_E=L_D={cfg.n_layers} "
+                               f"F={cfg.ffn_dim} {cfg.ffn_kind} W={cfg.window} G={cfg.mem_groups} "
+                               f"V={cfg.vocab}, B={B} T={T}, exact replay",
+                   "batch": B, "seq_len": T},
+        "decoder_only_tokens_per_s": B * T / (dec_ms * 1e-3),
+        "phase_ms": {"encoder": enc_ms, "decoder_replay": dec_ms, "logits": head_ms},
+        "decoder_path": ["persistent-per-sequence", "batched-phases"][path],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "dec_small_k" if path == 0 else "batched decoder phases",
+                     "algorithmic_bytes_per_launch": dec_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, weights, tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

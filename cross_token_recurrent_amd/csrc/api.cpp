@@ -1,0 +1,687 @@
+// Host runtime of librlt: configuration checks, packed-weight and state layouts,
+// state counters and versioning, and the launch sequences of the three hot-path calls.
+//
+// Pages: [FI] feinterview "普林斯顿提出 RLT：跨 Token 携带解码器状态的循环 Transformer";
+//        [DS] deepsonar "技术拆解 009｜RLT：给 Transformer 接一条时间回路…".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "rlt_internal.h"
+
+using namespace rlt;
+
+struct rlt_model {
+  rlt_config cfg;
+  ModelLayout lay;
+  uint64_t version;
+  char* ws;
+  size_t ws_bytes;
+};
+
+struct rlt_state {
+  rlt_config cfg;
+  StateLayout lay;
+  uint64_t version;
+  int t_enc, t_dec;
+  char* buf;
+  size_t bytes;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  g_err = std::string(where) + ": " + hipGetErrorString(e);
+  return RLT_ERR_HIP;
+}
+
+#define RLT_HIP(call, where)                    \
+  do {                                          \
+    hipError_t _e = (call);                     \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_config(const rlt_config* c) {
+  if (!c) return fail(RLT_ERR_INVALID, "config is NULL");
+  if (c->vocab < 1 || c->d_model < 1 || c->n_heads < 1 || c->n_layers < 1 || c->ffn_dim < 1)
+    return fail(RLT_ERR_INVALID, "vocab, d_model, n_heads, n_layers and ffn_dim must be >= 1");
+  if (c->window < 1) return fail(RLT_ERR_INVALID, "window must be >= 1 (it counts the current token)");
+  if (c->ffn_kind != RLT_FFN_GELU && c->ffn_kind != RLT_FFN_SWIGLU)
+    return fail(RLT_ERR_INVALID, "ffn_kind must be RLT_FFN_GELU or RLT_FFN_SWIGLU");
+  if (c->dtype != RLT_DTYPE_FP32 && c->dtype != RLT_DTYPE_BF16)
+    return fail(RLT_ERR_INVALID, "dtype must be RLT_DTYPE_FP32 or RLT_DTYPE_BF16");
+  if (!(c->norm_eps > 0.0f)) return fail(RLT_ERR_INVALID, "norm_eps must be > 0");
+  if (c->d_model % c->n_heads != 0) return fail(RLT_ERR_UNSUPPORTED, "d_model must be a multiple of n_heads");
+  if (c->mem_groups != 1 && c->mem_groups != c->n_layers)
+    return fail(RLT_ERR_UNSUPPORTED, "mem_groups must be 1 or n_layers");
+  const int dh = c->d_model / c->n_heads;
+  if (dh != 16 && dh != 32 && dh != 64 && dh != 128)
+    return fail(RLT_ERR_UNSUPPORTED, "head_dim must be 16, 32, 64 or 128");
+  if (c->d_model % 64 != 0 || c->ffn_dim % 64 != 0)
+    return fail(RLT_ERR_UNSUPPORTED, "d_model and ffn_dim must be multiples of 64");
+  return RLT_OK;
+}
+
+struct ParamDesc {
+  const char* name;
+  int64_t numel;
+};
+
+std::vector<ParamDesc> param_table(const rlt_config& c) {
+  const int64_t V = c.vocab, d = c.d_model, L = c.n_layers, F = c.ffn_dim, G = c.mem_groups;
+  std::vector<ParamDesc> t = {
+      {"embed", V * d}, {"w_out", V * d}, {"s_star", d}, {"w_ge", d * d}, {"w_gs", d * d},
+      {"w_fb", d * d},  {"b_g", d},       {"wq", L * d * d}, {"wk", L * d * d}, {"wv", L * d * d},
+      {"wo", L * d * d}};
+  if (c.ffn_kind == RLT_FFN_GELU) {
+    t.push_back({"ffn_w1", L * F * d});
+    t.push_back({"ffn_w2", L * d * F});
+  } else {
+    t.push_back({"ffn_gate", L * F * d});
+    t.push_back({"ffn_up", L * F * d});
+    t.push_back({"ffn_down", L * d * F});
+  }
+  const ParamDesc rest[] = {{"wqx", L * d * d},   {"wox", L * d * d},   {"wkm", G * d * d},
+                            {"wvm", G * d * d},   {"g_enc_attn", L * d}, {"g_enc_ffn", L * d},
+                            {"g_enc_final", d},   {"g_dec_self", L * d}, {"g_dec_cross", L * d},
+                            {"g_dec_ffn", L * d}, {"g_dec_final", d}};
+  for (const auto& r : rest) t.push_back(r);
+  return t;
+}
+
+int64_t param_offset(const rlt_config& c, const char* name, int64_t* numel) {
+  int64_t off = 0;
+  for (const auto& p : param_table(c)) {
+    if (std::strcmp(p.name, name) == 0) {
+      if (numel) *numel = p.numel;
+      return off;
+    }
+    off += p.numel;
+  }
+  return -1;
+}
+
+// Packs the canonical fp32 buffer into the workspace layout (enqueued on `st`).
+int pack_weights(const rlt_model& m, const float* w, hipStream_t st) {
+  const rlt_config& c = m.cfg;
+  const ModelLayout& L = m.lay;
+  const int D = L.D, F = L.F, dt = L.dtype;
+  char* ws = m.ws;
+  auto src = [&](const char* name) { return w + param_offset(c, name, nullptr); };
+  auto mat = [&](const float* s, size_t dst, int rows, int cols, int ld, int row_off, int col_off,
+                 int mode) -> int {
+    RLT_HIP(launch_pack_matrix(s, ws + dst, rows, cols, ld, row_off, col_off, mode, dt, st), "pack");
+    return RLT_OK;
+  };
+  auto f32 = [&](const float* s, size_t dst, size_t n) -> int {
+    RLT_HIP(launch_copy_f32(s, reinterpret_cast<float*>(ws + dst), n, st), "pack gains");
+    return RLT_OK;
+  };
+  int rc;
+#define TRY(x) \
+  if ((rc = (x)) != RLT_OK) return rc
+  TRY(mat(src("embed"), L.embed, L.V, D, D, 0, 0, 0));
+  TRY(mat(src("w_out"), L.wout, L.V, D, D, 0, 0, 0));
+  TRY(f32(src("s_star"), L.sstar, D));
+  TRY(mat(src("w_ge"), L.wgate, D, D, 2 * D, 0, 0, 0));
+  TRY(mat(src("w_gs"), L.wgate, D, D, 2 * D, 0, D, 0));
+  TRY(mat(src("w_fb"), L.wfb, D, D, D, 0, 0, 0));
+  TRY(f32(src("b_g"), L.bg, D));
+  const size_t dd = static_cast<size_t>(D) * D, fd = static_cast<size_t>(F) * D;
+  for (int l = 0; l < L.L; ++l) {
+    const size_t base = L.layers + l * L.layer_stride;
+    TRY(mat(src("wq") + l * dd, base + L.l_qkv, D, D, D, 0, 0, 0));
+    TRY(mat(src("wk") + l * dd, base + L.l_qkv, D, D, D, D, 0, 0));
+    TRY(mat(src("wv") + l * dd, base + L.l_qkv, D, D, D, 2 * D, 0, 0));
+    TRY(mat(src("wo") + l * dd, base + L.l_wo, D, D, D, 0, 0, 0));
+    TRY(mat(src("wqx") + l * dd, base + L.l_wqx, D, D, D, 0, 0, 0));
+    TRY(mat(src("wox") + l * dd, base + L.l_wox, D, D, D, 0, 0, 0));
+    if (L.ffn_kind == RLT_FFN_GELU) {
+      TRY(mat(src("ffn_w1") + l * fd, base + L.l_fin, F, D, D, 0, 0, 0));
+      TRY(mat(src("ffn_w2") + l * fd, base + L.l_fout, D, F, F, 0, 0, 0));
+    } else {
+      TRY(mat(src("ffn_gate") + l * fd, base + L.l_fin, F, D, D, 0, 0, 1));
+      TRY(mat(src("ffn_up") + l * fd, base + L.l_fin, F, D, D, 16, 0, 1));
+      TRY(mat(src("ffn_down") + l * fd, base + L.l_fout, D, F, F, 0, 0, 0));
+    }
+  }
+  for (int g = 0; g < L.G; ++g) {
+    const size_t base = L.wkvm + g * L.group_stride;
+    TRY(mat(src("wkm") + g * dd, base, D, D, D, 0, 0, 0));
+    TRY(mat(src("wvm") + g * dd, base, D, D, D, D, 0, 0));
+  }
+  TRY(f32(src("g_enc_attn"), L.g_enc_attn, static_cast<size_t>(L.L) * D));
+  TRY(f32(src("g_enc_ffn"), L.g_enc_ffn, static_cast<size_t>(L.L) * D));
+  TRY(f32(src("g_enc_final"), L.g_enc_final, D));
+  TRY(f32(src("g_dec_self"), L.g_dec_self, static_cast<size_t>(L.L) * D));
+  TRY(f32(src("g_dec_cross"), L.g_dec_cross, static_cast<size_t>(L.L) * D));
+  TRY(f32(src("g_dec_ffn"), L.g_dec_ffn, static_cast<size_t>(L.L) * D));
+  TRY(f32(src("g_dec_final"), L.g_dec_final, D));
+#undef TRY
+  return RLT_OK;
+}
+
+int check_pair(const rlt_model* m, const rlt_state* s) {
+  if (!m || !s) return fail(RLT_ERR_INVALID, "model or state is NULL");
+  if (std::memcmp(&m->cfg, &s->cfg, sizeof(rlt_config)) != 0)
+    return fail(RLT_ERR_INVALID, "state was built for a different model configuration");
+  if (m->version != s->version)
+    return fail(RLT_ERR_STALE_STATE,
+                "state was built under weights version " + std::to_string(s->version) +
+                    " but the model is at version " + std::to_string(m->version) +
+                    "; reset the state and replay from the sequence start");
+  return RLT_OK;
+}
+
+int reset_state(const rlt_model* m, rlt_state* s, hipStream_t st) {
+  const StateLayout& S = s->lay;
+  RLT_HIP(launch_zero(s->buf + S.flags, 256, st), "reset flags");
+  RLT_HIP(launch_broadcast_rows(reinterpret_cast<const float*>(m->ws + m->lay.sstar),
+                                reinterpret_cast<float*>(s->buf + S.s), S.B, m->lay.D, st),
+          "reset s");
+  if (S.ring_v > S.ring_k) {
+    RLT_HIP(launch_zero(s->buf + S.ring_k, S.e - S.ring_k, st), "reset window caches");
+  }
+  s->version = m->version;
+  s->t_enc = 0;
+  s->t_dec = 0;
+  return RLT_OK;
+}
+
+}  // namespace
+
+namespace rlt {
+
+bool compute_model_layout(const rlt_config& c, ModelLayout* m) {
+  ModelLayout& L = *m;
+  L.D = c.d_model;
+  L.H = c.n_heads;
+  L.DH = c.d_model / c.n_heads;
+  L.L = c.n_layers;
+  L.F = c.ffn_dim;
+  L.F2 = c.ffn_kind == RLT_FFN_SWIGLU ? 2 * c.ffn_dim : c.ffn_dim;
+  L.V = c.vocab;
+  L.W = c.window;
+  L.G = c.mem_groups;
+  L.ffn_kind = c.ffn_kind;
+  L.dtype = c.dtype;
+  L.eps = c.norm_eps;
+  L.esz = c.dtype == RLT_DTYPE_BF16 ? 2 : 4;
+  const size_t D = L.D, V = L.V, F = L.F, F2 = L.F2, e = L.esz;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.embed = take(V * D * e);
+  L.wout = take(V * D * e);
+  L.sstar = take(D * 4);
+  L.wgate = take(2 * D * D * e);
+  L.wfb = take(D * D * e);
+  L.bg = take(D * 4);
+  size_t rel = 0;
+  auto take_rel = [&](size_t bytes) {
+    size_t o = rel;
+    rel = align_up(rel + bytes);
+    return o;
+  };
+  L.l_qkv = take_rel(3 * D * D * e);
+  L.l_wo = take_rel(D * D * e);
+  L.l_wqx = take_rel(D * D * e);
+  L.l_wox = take_rel(D * D * e);
+  L.l_fin = take_rel(F2 * D * e);
+  L.l_fout = take_rel(D * F * e);
+  L.layer_stride = rel;
+  L.layers = take(L.L * L.layer_stride);
+  L.group_stride = align_up(2 * D * D * e);
+  L.wkvm = take(L.G * L.group_stride);
+  L.gains = off;
+  L.g_enc_attn = take(L.L * D * 4);
+  L.g_enc_ffn = take(L.L * D * 4);
+  L.g_enc_final = take(D * 4);
+  L.g_dec_self = take(L.L * D * 4);
+  L.g_dec_cross = take(L.L * D * 4);
+  L.g_dec_ffn = take(L.L * D * 4);
+  L.g_dec_final = take(D * 4);
+  L.total = off;
+  return true;
+}
+
+void compute_state_layout(const ModelLayout& m, int B, int T, int keep, StateLayout* s) {
+  StateLayout& S = *s;
+  S.B = B;
+  S.T = T;
+  S.keep = keep;
+  S.Wm1 = m.W - 1;
+  const size_t D = m.D, e = m.esz, Bz = B, Tz = T, L = m.L, G = m.G, F = m.F;
+  const size_t heads_tokens = static_cast<size_t>(m.H) * m.DH;  // = D
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  S.flags = take(256);
+  S.s = take(Bz * D * 4);
+  S.ring_k = take(L * Bz * S.Wm1 * heads_tokens * e);
+  S.ring_v = take(L * Bz * S.Wm1 * heads_tokens * e);
+  S.e = take(Bz * Tz * D * e);
+  S.mem_k = take(G * Bz * Tz * D * e);
+  S.mem_v = take(G * Bz * Tz * D * e);
+  if (keep) {
+    S.enc_k = take(L * Bz * Tz * D * e);
+    S.enc_v = take(L * Bz * Tz * D * e);
+  } else {
+    S.enc_k = S.enc_v = 0;
+  }
+  const size_t budget = 65536;
+  size_t nc = std::min(Bz * Tz, budget);
+  nc = std::max(nc, std::max(Tz, Bz));
+  S.Nc = static_cast<int>(nc);
+  S.x = take(nc * D * 4);
+  S.h = take(nc * D * e);
+  S.qkv = take(nc * 3 * D * e);
+  S.attn = take(nc * D * e);
+  S.act = take(nc * F * e);
+  S.dec_scratch_bytes = dec_batched_scratch_bytes(m, B, T);
+  S.dec_scratch = take(S.dec_scratch_bytes);
+  S.total = off;
+}
+
+}  // namespace rlt
+
+extern "C" {
+
+const char* rlt_last_error(void) { return g_err.c_str(); }
+const char* rlt_version_string(void) { return "librlt 0.1 (gfx950)"; }
+
+int rlt_param_count(const rlt_config* cfg, int32_t* n_tensors, int64_t* total_numel) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  auto t = param_table(*cfg);
+  int64_t tot = 0;
+  for (auto& p : t) tot += p.numel;
+  if (n_tensors) *n_tensors = static_cast<int32_t>(t.size());
+  if (total_numel) *total_numel = tot;
+  return RLT_OK;
+}
+
+int rlt_param_info(const rlt_config* cfg, int32_t index, const char** name, int64_t* offset,
+                   int64_t* numel) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  auto t = param_table(*cfg);
+  if (index < 0 || index >= static_cast<int32_t>(t.size())) return fail(RLT_ERR_INVALID, "index out of range");
+  int64_t off = 0;
+  for (int i = 0; i < index; ++i) off += t[i].numel;
+  if (name) *name = t[index].name;
+  if (offset) *offset = off;
+  if (numel) *numel = t[index].numel;
+  return RLT_OK;
+}
+
+int rlt_model_workspace_bytes(const rlt_config* cfg, size_t* bytes) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(RLT_ERR_INVALID, "bytes is NULL");
+  ModelLayout L;
+  compute_model_layout(*cfg, &L);
+  *bytes = L.total;
+  return RLT_OK;
+}
+
+int rlt_model_create(const rlt_config* cfg, const float* weights, uint64_t version, void* workspace,
+                     size_t workspace_bytes, void* stream, rlt_model** out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!weights || !workspace || !out) return fail(RLT_ERR_INVALID, "weights, workspace and out must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return fail(RLT_ERR_INVALID, "workspace must be 256-byte aligned");
+  ModelLayout L;
+  compute_model_layout(*cfg, &L);
+  if (workspace_bytes < L.total)
+    return fail(RLT_ERR_INVALID, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  rlt_model* m = new (std::nothrow) rlt_model;
+  if (!m) return fail(RLT_ERR_INVALID, "out of host memory");
+  m->cfg = *cfg;
+  m->lay = L;
+  m->version = version;
+  m->ws = static_cast<char*>(workspace);
+  m->ws_bytes = workspace_bytes;
+  rc = pack_weights(*m, weights, as_stream(stream));
+  if (rc) {
+    delete m;
+    return rc;
+  }
+  *out = m;
+  return RLT_OK;
+}
+
+int rlt_model_update_weights(rlt_model* model, const float* weights, uint64_t new_version, void* stream) {
+  if (!model || !weights) return fail(RLT_ERR_INVALID, "model and weights must be non-NULL");
+  if (new_version == model->version)
+    return fail(RLT_ERR_INVALID, "a weight update must carry a new version");
+  int rc = pack_weights(*model, weights, as_stream(stream));
+  if (rc) return rc;
+  model->version = new_version;
+  return RLT_OK;
+}
+
+int rlt_model_get_config(const rlt_model* model, rlt_config* cfg, uint64_t* version) {
+  if (!model) return fail(RLT_ERR_INVALID, "model is NULL");
+  if (cfg) *cfg = model->cfg;
+  if (version) *version = model->version;
+  return RLT_OK;
+}
+
+void rlt_model_release(rlt_model* model) { delete model; }
+
+int rlt_state_bytes(const rlt_model* model, int32_t batch, int32_t t_max, int32_t keep_encoder_cache,
+                    size_t* bytes) {
+  if (!model || !bytes) return fail(RLT_ERR_INVALID, "model and bytes must be non-NULL");
+  if (batch < 1 || t_max < 1) return fail(RLT_ERR_INVALID, "batch and t_max must be >= 1");
+  StateLayout S;
+  compute_state_layout(model->lay, batch, t_max, keep_encoder_cache ? 1 : 0, &S);
+  *bytes = S.total;
+  return RLT_OK;
+}
+
+int rlt_state_init(const rlt_model* model, void* buffer, size_t buffer_bytes, int32_t batch, int32_t t_max,
+                   int32_t keep_encoder_cache, void* stream, rlt_state** out) {
+  if (!model || !buffer || !out) return fail(RLT_ERR_INVALID, "model, buffer and out must be non-NULL");
+  if (batch < 1 || t_max < 1) return fail(RLT_ERR_INVALID, "batch and t_max must be >= 1");
+  if (reinterpret_cast<uintptr_t>(buffer) % kAlign != 0)
+    return fail(RLT_ERR_INVALID, "state buffer must be 256-byte aligned");
+  StateLayout S;
+  compute_state_layout(model->lay, batch, t_max, keep_encoder_cache ? 1 : 0, &S);
+  if (buffer_bytes < S.total)
+    return fail(RLT_ERR_INVALID, "state buffer too small: need " + std::to_string(S.total) + " bytes");
+  rlt_state* s = new (std::nothrow) rlt_state;
+  if (!s) return fail(RLT_ERR_INVALID, "out of host memory");
+  s->cfg = model->cfg;
+  s->lay = S;
+  s->buf = static_cast<char*>(buffer);
+  s->bytes = buffer_bytes;
+  int rc = reset_state(model, s, as_stream(stream));
+  if (rc) {
+    delete s;
+    return rc;
+  }
+  *out = s;
+  return RLT_OK;
+}
+
+int rlt_state_reset(const rlt_model* model, rlt_state* state, void* stream) {
+  if (!model || !state) return fail(RLT_ERR_INVALID, "model and state must be non-NULL");
+  if (std::memcmp(&model->cfg, &state->cfg, sizeof(rlt_config)) != 0)
+    return fail(RLT_ERR_INVALID, "state was built for a different model configuration");
+  return reset_state(model, state, as_stream(stream));
+}
+
+void rlt_state_release(rlt_state* state) { delete state; }
+
+int rlt_state_position(const rlt_state* state, int32_t* t_enc, int32_t* t_dec, uint64_t* version) {
+  if (!state) return fail(RLT_ERR_INVALID, "state is NULL");
+  if (t_enc) *t_enc = state->t_enc;
+  if (t_dec) *t_dec = state->t_dec;
+  if (version) *version = state->version;
+  return RLT_OK;
+}
+
+int rlt_state_device_error(rlt_state* state, void* stream, int32_t* flags) {
+  if (!state || !flags) return fail(RLT_ERR_INVALID, "state and flags must be non-NULL");
+  int32_t v = 0;
+  RLT_HIP(hipMemcpyAsync(&v, state->buf + state->lay.flags, sizeof(v), hipMemcpyDeviceToHost,
+                         as_stream(stream)),
+          "read device flags");
+  RLT_HIP(hipStreamSynchronize(as_stream(stream)), "synchronise");
+  *flags = v;
+  return RLT_OK;
+}
+
+int rlt_decoder_path(const rlt_model* model, int32_t batch, int32_t* path) {
+  if (!model || !path) return fail(RLT_ERR_INVALID, "model and path must be non-NULL");
+  (void)batch;
+  *path = dec_small_supported(model->lay, 1) ? 0 : 1;
+  return RLT_OK;
+}
+
+int rlt_encoder_forward(const rlt_model* model, rlt_state* state, const int32_t* tokens, int32_t n,
+                        void* stream) {
+  int rc = check_pair(model, state);
+  if (rc) return rc;
+  if (!tokens) return fail(RLT_ERR_INVALID, "tokens is NULL");
+  if (n < 1) return fail(RLT_ERR_INVALID, "n must be >= 1");
+  const StateLayout& S = state->lay;
+  const ModelLayout& M = model->lay;
+  if (static_cast<int64_t>(state->t_enc) + n > S.T)
+    return fail(RLT_ERR_CAPACITY, "encoder positions would exceed the state's T_max");
+  if (state->t_enc > 0 && !S.keep)
+    return fail(RLT_ERR_NO_ENC_CACHE,
+                "the state keeps no encoder cache, so the known sequence must be encoded in one call");
+  hipStream_t st = as_stream(stream);
+  char* sb = state->buf;
+  const char* ws = model->ws;
+  const int D = M.D, H = M.H, DH = M.DH, dt = M.dtype;
+  const int t0 = state->t_enc;
+  const int bc_max = std::max(1, std::min(S.B, S.Nc / n));
+  float* x = reinterpret_cast<float*>(sb + S.x);
+  int32_t* flags = reinterpret_cast<int32_t*>(sb + S.flags);
+  const float* gains = nullptr;
+  (void)gains;
+  for (int b0 = 0; b0 < S.B; b0 += bc_max) {
+    const int bc = std::min(bc_max, S.B - b0);
+    const int rows = bc * n;
+    RLT_HIP(launch_embed(tokens + static_cast<size_t>(b0) * n, n, b0, rows, ws + M.embed, M.V, D, dt, x,
+                         flags, st),
+            "embed");
+    for (int l = 0; l < M.L; ++l) {
+      const char* lw = ws + M.layers + l * M.layer_stride;
+      RLT_HIP(launch_rmsnorm_rows(x, reinterpret_cast<const float*>(ws + M.g_enc_attn) + l * D, sb + S.h,
+                                  rows, D, M.eps, dt, nullptr, n, b0, t0, S.T, st),
+              "encoder norm");
+      GemmArgs g{};
+      g.A = sb + S.h; g.W = lw + M.l_qkv; g.out = sb + S.qkv;
+      g.M = rows; g.N = 3 * D; g.K = D; g.lda = D; g.ldw = D; g.ldo = 3 * D;
+      g.epi = EPI_STORE;
+      const size_t cache_layer = static_cast<size_t>(l) * S.B * S.T * D * M.esz;
+      if (S.keep) {
+        g.sc_k = sb + S.enc_k + cache_layer;
+        g.sc_v = sb + S.enc_v + cache_layer;
+        g.sc_c0 = D;
+        g.sc_n = n; g.sc_b0 = b0; g.sc_t0 = t0; g.sc_T = S.T; g.sc_H = H; g.sc_dh = DH; g.sc_D = D;
+        g.sc_B = S.B;
+      }
+      RLT_HIP(launch_gemm(g, dt, st), "encoder qkv");
+      AttnArgs a{};
+      a.q = sb + S.qkv; a.ldq = 3 * D;
+      if (S.keep) {
+        const size_t bo = static_cast<size_t>(b0) * H * S.T * DH * M.esz;
+        a.k = sb + S.enc_k + cache_layer + bo;
+        a.v = sb + S.enc_v + cache_layer + bo;
+        a.kv_ld_b = static_cast<long long>(H) * S.T * DH;
+        a.kv_ld_h = static_cast<long long>(S.T) * DH;
+        a.kv_ld_t = DH;
+        a.t0 = t0;
+      } else {
+        a.k = sb + S.qkv + static_cast<size_t>(D) * M.esz;
+        a.v = sb + S.qkv + static_cast<size_t>(2 * D) * M.esz;
+        a.kv_ld_b = static_cast<long long>(n) * 3 * D;
+        a.kv_ld_h = DH;
+        a.kv_ld_t = 3 * D;
+        a.t0 = 0;
+      }
+      a.out = sb + S.attn; a.ldo = D;
+      a.Bc = bc; a.H = H; a.dh = DH; a.n = n;
+      RLT_HIP(launch_enc_attention(a, dt, st), "encoder attention");
+      GemmArgs o{};
+      o.A = sb + S.attn; o.W = lw + M.l_wo; o.out = x;
+      o.M = rows; o.N = D; o.K = D; o.lda = D; o.ldw = D; o.ldo = D; o.epi = EPI_RESID_F32;
+      RLT_HIP(launch_gemm(o, dt, st), "encoder attention output");
+      RLT_HIP(launch_rmsnorm_rows(x, reinterpret_cast<const float*>(ws + M.g_enc_ffn) + l * D, sb + S.h,
+                                  rows, D, M.eps, dt, nullptr, n, b0, t0, S.T, st),
+              "encoder norm");
+      GemmArgs f{};
+      f.A = sb + S.h; f.W = lw + M.l_fin; f.out = sb + S.act;
+      f.M = rows; f.N = M.F2; f.K = D; f.lda = D; f.ldw = D; f.ldo = M.F;
+      f.epi = M.ffn_kind == RLT_FFN_GELU ? EPI_GELU : EPI_SWIGLU;
+      RLT_HIP(launch_gemm(f, dt, st), "encoder ffn in");
+      GemmArgs f2{};
+      f2.A = sb + S.act; f2.W = lw + M.l_fout; f2.out = x;
+      f2.M = rows; f2.N = D; f2.K = M.F; f2.lda = M.F; f2.ldw = M.F; f2.ldo = D; f2.epi = EPI_RESID_F32;
+      RLT_HIP(launch_gemm(f2, dt, st), "encoder ffn out");
+    }
+    RLT_HIP(launch_rmsnorm_rows(x, reinterpret_cast<const float*>(ws + M.g_enc_final), sb + S.h, rows, D,
+                                M.eps, dt, sb + S.e, n, b0, t0, S.T, st),
+            "encoder final norm");
+    for (int gi = 0; gi < M.G; ++gi) {
+      const size_t goff = static_cast<size_t>(gi) * S.B * S.T * D * M.esz;
+      GemmArgs g{};
+      g.A = sb + S.h; g.W = ws + M.wkvm + gi * M.group_stride; g.out = nullptr;
+      g.M = rows; g.N = 2 * D; g.K = D; g.lda = D; g.ldw = D; g.ldo = 0;
+      g.epi = EPI_SCATTER_HEADS;
+      g.sc_k = sb + S.mem_k + goff;
+      g.sc_v = sb + S.mem_v + goff;
+      g.sc_c0 = 0;
+      g.sc_n = n; g.sc_b0 = b0; g.sc_t0 = t0; g.sc_T = S.T; g.sc_H = H; g.sc_dh = DH; g.sc_D = D; g.sc_B = S.B;
+      RLT_HIP(launch_gemm(g, dt, st), "memory projection");
+    }
+  }
+  state->t_enc += n;
+  return RLT_OK;
+}
+
+int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, float* s_out, void* stream) {
+  int rc = check_pair(model, state);
+  if (rc) return rc;
+  if (n < 1) return fail(RLT_ERR_INVALID, "n must be >= 1");
+  if (static_cast<int64_t>(state->t_dec) + n > state->t_enc)
+    return fail(RLT_ERR_ORDER, "decoder would run ahead of the encoder (t_dec + n > t_enc)");
+  const ModelLayout& M = model->lay;
+  const StateLayout& S = state->lay;
+  hipStream_t st = as_stream(stream);
+  if (dec_small_supported(M, S.T)) {
+    DecSmallArgs a{};
+    a.ws = model->ws;
+    a.state = state->buf;
+    a.s_out = s_out;
+    a.B = S.B;
+    a.T = S.T;
+    a.t0 = state->t_dec;
+    a.n = n;
+    RLT_HIP(launch_dec_small(M, S, a, st), "decoder replay (persistent)");
+  } else if (dec_batched_supported(M)) {
+    RLT_HIP(run_dec_batched(M, S, model->ws, state->buf, s_out, state->t_dec, n, st), "decoder replay (batched)");
+  } else {
+    return fail(RLT_ERR_UNSUPPORTED, "no decoder implementation for this configuration");
+  }
+  state->t_dec += n;
+  return RLT_OK;
+}
+
+int rlt_logits(const rlt_model* model, const float* s, int64_t n_rows, float* logits, void* stream) {
+  if (!model || !s || !logits) return fail(RLT_ERR_INVALID, "model, s and logits must be non-NULL");
+  if (n_rows < 1 || n_rows > 0x7fffffff) return fail(RLT_ERR_INVALID, "n_rows out of range");
+  const ModelLayout& M = model->lay;
+  GemmArgs g{};
+  g.A = s; g.a_f32 = 1; g.W = model->ws + M.wout; g.out = logits;
+  g.M = static_cast<int>(n_rows); g.N = M.V; g.K = M.D; g.lda = M.D; g.ldw = M.D; g.ldo = M.V;
+  g.epi = EPI_STORE_F32;
+  RLT_HIP(launch_gemm(g, M.dtype, as_stream(stream)), "logits");
+  return RLT_OK;
+}
+
+int rlt_decoder_step(const rlt_model* model, rlt_state* state, const int32_t* tokens, float* s_out,
+                     float* logits, void* stream) {
+  int rc = check_pair(model, state);
+  if (rc) return rc;
+  if (state->t_dec != state->t_enc)
+    return fail(RLT_ERR_ORDER, "decoder_step needs t_dec == t_enc (every encoded position decoded)");
+  if (state->t_enc >= state->lay.T) return fail(RLT_ERR_CAPACITY, "state is full (t == T_max)");
+  if (state->t_enc > 0 && !state->lay.keep)
+    return fail(RLT_ERR_NO_ENC_CACHE, "incremental generation needs keep_encoder_cache");
+  rc = rlt_encoder_forward(model, state, tokens, 1, stream);
+  if (rc) return rc;
+  rc = rlt_decoder_replay(model, state, 1, s_out, stream);
+  if (rc) return rc;
+  if (logits) {
+    const float* s = reinterpret_cast<const float*>(state->buf + state->lay.s);
+    rc = rlt_logits(model, s, state->lay.B, logits, stream);
+    if (rc) return rc;
+  }
+  return RLT_OK;
+}
+
+int rlt_state_load_encoder_outputs(const rlt_model* model, rlt_state* state, const float* e,
+                                   const float* mem_k, const float* mem_v, int32_t n, void* stream) {
+  int rc = check_pair(model, state);
+  if (rc) return rc;
+  if (!e || !mem_k || !mem_v) return fail(RLT_ERR_INVALID, "e, mem_k and mem_v must be non-NULL");
+  if (n < 1) return fail(RLT_ERR_INVALID, "n must be >= 1");
+  const StateLayout& S = state->lay;
+  const ModelLayout& M = model->lay;
+  if (static_cast<int64_t>(state->t_enc) + n > S.T) return fail(RLT_ERR_CAPACITY, "positions exceed T_max");
+  hipStream_t st = as_stream(stream);
+  const int t0 = state->t_enc;
+  RLT_HIP(launch_store_tokens(e, state->buf + S.e, S.B, n, M.D, t0, S.T, M.dtype, 0, M.H, M.DH, 1, st),
+          "load e");
+  const size_t gsrc = static_cast<size_t>(S.B) * n * M.D;
+  const size_t gdst = static_cast<size_t>(S.B) * S.T * M.D * M.esz;
+  for (int g = 0; g < M.G; ++g) {
+    RLT_HIP(launch_store_tokens(mem_k + g * gsrc, state->buf + S.mem_k + g * gdst, S.B, n, M.D, t0, S.T,
+                                M.dtype, 1, M.H, M.DH, 1, st),
+            "load memory keys");
+    RLT_HIP(launch_store_tokens(mem_v + g * gsrc, state->buf + S.mem_v + g * gdst, S.B, n, M.D, t0, S.T,
+                                M.dtype, 1, M.H, M.DH, 1, st),
+            "load memory values");
+  }
+  state->t_enc += n;
+  return RLT_OK;
+}
+
+int rlt_state_read_encoder_outputs(const rlt_model* model, const rlt_state* state, int32_t t0, int32_t n,
+                                   float* e, float* mem_k, float* mem_v, void* stream) {
+  if (!model || !state) return fail(RLT_ERR_INVALID, "model and state must be non-NULL");
+  if (std::memcmp(&model->cfg, &state->cfg, sizeof(rlt_config)) != 0)
+    return fail(RLT_ERR_INVALID, "state was built for a different model configuration");
+  if (n < 1 || t0 < 0 || t0 + n > state->t_enc) return fail(RLT_ERR_INVALID, "positions not encoded yet");
+  const StateLayout& S = state->lay;
+  const ModelLayout& M = model->lay;
+  hipStream_t st = as_stream(stream);
+  if (e) {
+    RLT_HIP(launch_store_tokens(e, state->buf + S.e, S.B, n, M.D, t0, S.T, M.dtype, 0, M.H, M.DH, 0, st),
+            "read e");
+  }
+  const size_t gsrc = static_cast<size_t>(S.B) * n * M.D;
+  const size_t gdst = static_cast<size_t>(S.B) * S.T * M.D * M.esz;
+  for (int g = 0; g < M.G; ++g) {
+    if (mem_k) {
+      RLT_HIP(launch_store_tokens(mem_k + g * gsrc, state->buf + S.mem_k + g * gdst, S.B, n, M.D, t0, S.T,
+                                  M.dtype, 1, M.H, M.DH, 0, st),
+              "read memory keys");
+    }
+    if (mem_v) {
+      RLT_HIP(launch_store_tokens(mem_v + g * gsrc, state->buf + S.mem_v + g * gdst, S.B, n, M.D, t0, S.T,
+                                  M.dtype, 1, M.H, M.DH, 0, st),
+              "read memory values");
+    }
+  }
+  return RLT_OK;
+}
+
+}  // extern "C"

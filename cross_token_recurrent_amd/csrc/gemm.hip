@@ -1,0 +1,207 @@
+// Token-parallel matrix products on the MFMA units: C[M,N] = A[M,K] * W[N,K]^T.
+//
+// Used for every dense contraction the encoder runs over known tokens (QKV, attention
+// output, FFN, memory projections) and for the output head ([FI] model-hardware
+// co-design: encoder features and memory projections are token-parallel).
+// bf16 mode: v_mfma_f32_16x16x32_bf16 with fp32 accumulation; fp32 mode:
+// v_mfma_f32_16x16x4_f32.  A block computes a 128x128 tile with 4 waves (2x2), each
+// wave a 64x64 sub-tile of 4x4 MFMA 16x16 tiles; K advances 32 per LDS stage, with the
+// next stage's global loads issued before the current stage's MFMAs.
+#include "device_common.h"
+#include "rlt_internal.h"
+
+namespace rlt {
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int NTH = 256;
+
+template <typename TW> struct Tile;
+template <> struct Tile<bf16_t> { static constexpr int PAD = 8; };   // row pitch 80 B
+template <> struct Tile<float> { static constexpr int PAD = 4; };    // row pitch 144 B
+
+// Number of 16-byte chunks of one BMxBK (or BNxBK) tile, per thread.
+template <typename TW> constexpr int chunks_per_thread() { return (BM * BK * sizeof(TW) / 16) / NTH; }
+
+// Load one tile's chunks into registers (as packed storage words).
+template <typename TW, bool SRC_F32>
+__device__ __forceinline__ void load_tile(const void* __restrict__ base, int ld, int row0, int rows_valid, int k0,
+                                          uint4 (&r)[chunks_per_thread<TW>()]) {
+  constexpr int EPC = 16 / sizeof(TW);     // elements per chunk
+  constexpr int CPR = BK / EPC;            // chunks per row
+#pragma unroll
+  for (int i = 0; i < chunks_per_thread<TW>(); ++i) {
+    const int c = threadIdx.x + i * NTH;
+    const int row = c / CPR, kc = (c % CPR) * EPC;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < rows_valid) {
+      if constexpr (SRC_F32 && sizeof(TW) == 2) {
+        // fp32 source converted to bf16 storage (8 elements = 32 source bytes)
+        const float* p = static_cast<const float*>(base) + static_cast<size_t>(row0 + row) * ld + k0 + kc;
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        v.x = f32_to_bf16(a.x) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16);
+        v.y = f32_to_bf16(a.z) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16);
+        v.z = f32_to_bf16(b.x) | (static_cast<uint32_t>(f32_to_bf16(b.y)) << 16);
+        v.w = f32_to_bf16(b.z) | (static_cast<uint32_t>(f32_to_bf16(b.w)) << 16);
+      } else {
+        const TW* p = static_cast<const TW*>(base) + static_cast<size_t>(row0 + row) * ld + k0 + kc;
+        v = *reinterpret_cast<const uint4*>(p);
+      }
+    }
+    r[i] = v;
+  }
+}
+
+template <typename TW>
+__device__ __forceinline__ void store_tile(TW* __restrict__ lds, const uint4 (&r)[chunks_per_thread<TW>()]) {
+  constexpr int EPC = 16 / sizeof(TW);
+  constexpr int CPR = BK / EPC;
+  constexpr int PITCH = BK + Tile<TW>::PAD;
+#pragma unroll
+  for (int i = 0; i < chunks_per_thread<TW>(); ++i) {
+    const int c = threadIdx.x + i * NTH;
+    const int row = c / CPR, kc = (c % CPR) * EPC;
+    *reinterpret_cast<uint4*>(lds + row * PITCH + kc) = r[i];
+  }
+}
+
+template <typename TW>
+__device__ __forceinline__ void store_out(const GemmArgs& g, int m, int n, float v) {
+  const int epi = g.epi;
+  if (epi == EPI_STORE_F32) {
+    static_cast<float*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = v;
+  } else if (epi == EPI_RESID_F32) {
+    static_cast<float*>(g.out)[static_cast<size_t>(m) * g.ldo + n] += v;
+  } else if (epi == EPI_GELU) {
+    store_from_f32(static_cast<TW*>(g.out) + static_cast<size_t>(m) * g.ldo + n, gelu_erf(v));
+  } else {  // EPI_STORE / EPI_SCATTER_HEADS
+    if (epi == EPI_STORE) store_from_f32(static_cast<TW*>(g.out) + static_cast<size_t>(m) * g.ldo + n, v);
+    if (g.sc_k && n >= g.sc_c0) {
+      const int rel = n - g.sc_c0;
+      const int which = rel / g.sc_D;
+      if (which < 2) {
+        const int c = rel % g.sc_D, h = c / g.sc_dh, cc = c % g.sc_dh;
+        const int b = g.sc_b0 + m / g.sc_n, t = g.sc_t0 + m % g.sc_n;
+        TW* dst = static_cast<TW*>(which == 0 ? g.sc_k : g.sc_v);
+        store_from_f32(dst + ((static_cast<size_t>(b) * g.sc_H + h) * g.sc_T + t) * g.sc_dh + cc, v);
+      }
+    }
+  }
+}
+
+template <typename TW, bool A_F32>
+__global__ __launch_bounds__(NTH) void gemm_nt_k(GemmArgs g) {
+  constexpr int PITCH = BK + Tile<TW>::PAD;
+  __shared__ __attribute__((aligned(16))) TW As[BM * PITCH];
+  __shared__ __attribute__((aligned(16))) TW Ws[BN * PITCH];
+
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wm = wave / 2, wn = wave % 2;
+  const int mrows = min(BM, g.M - m0), nrows = min(BN, g.N - n0);
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[chunks_per_thread<TW>()], rw[chunks_per_thread<TW>()];
+  load_tile<TW, A_F32>(g.A, g.lda, m0, mrows, 0, ra);
+  load_tile<TW, false>(g.W, g.ldw, n0, nrows, 0, rw);
+
+  for (int k0 = 0; k0 < g.K; k0 += BK) {
+    __syncthreads();
+    store_tile<TW>(As, ra);
+    store_tile<TW>(Ws, rw);
+    __syncthreads();
+    if (k0 + BK < g.K) {
+      load_tile<TW, A_F32>(g.A, g.lda, m0, mrows, k0 + BK, ra);
+      load_tile<TW, false>(g.W, g.ldw, n0, nrows, k0 + BK, rw);
+    }
+    const int r16 = lane % 16, kq = lane / 16;
+    if constexpr (sizeof(TW) == 2) {
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 16 + r16) * PITCH + kq * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Ws + (wn * 64 + j * 16 + r16) * PITCH + kq * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < BK / 4; ++kk) {
+        float af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = As[(wm * 64 + i * 16 + r16) * PITCH + kk * 4 + kq];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bfr[j] = Ws[(wn * 64 + j * 16 + r16) * PITCH + kk * 4 + kq];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // Epilogue.  MFMA 16x16 output: lane holds rows 4*(lane/16)+v, column lane%16.
+  const int col_l = lane % 16, row_q = (lane / 16) * 4;
+  if (g.epi == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const int nb = n0 + wn * 64 + j * 16;   // multiple of 32: gate block, nb+16: up block
+        if (nb >= g.N) continue;
+        const int ocol = (nb / 32) * 16 + col_l;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = m0 + wm * 64 + i * 16 + row_q + v;
+          if (m < g.M) {
+            const float gt = acc[i][j][v], up = acc[i][j + 1][v];
+            store_from_f32(static_cast<TW*>(g.out) + static_cast<size_t>(m) * g.ldo + ocol, silu_f(gt) * up);
+          }
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + j * 16 + col_l;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * 64 + i * 16 + row_q + v;
+        if (m < g.M) store_out<TW>(g, m, n, acc[i][j][v]);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.K % BK != 0) return hipErrorInvalidValue;
+  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
+  if (grid.y > 65535u) return hipErrorInvalidValue;
+  if (dtype == RLT_DTYPE_BF16) {
+    if (g.a_f32)
+      gemm_nt_k<bf16_t, true><<<grid, NTH, 0, st>>>(g);
+    else
+      gemm_nt_k<bf16_t, false><<<grid, NTH, 0, st>>>(g);
+  } else {
+    gemm_nt_k<float, false><<<grid, NTH, 0, st>>>(g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rlt

@@ -1,0 +1,184 @@
+// Weight packing, embedding gather, row RMSNorm and layout conversions.
+#include "device_common.h"
+#include "rlt_internal.h"
+
+namespace rlt {
+namespace {
+
+constexpr int kThreads = 256;
+
+inline int grid_for(size_t n, int per_block = kThreads, int cap = 65536) {
+  size_t g = (n + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > static_cast<size_t>(cap)) g = cap;
+  return static_cast<int>(g);
+}
+
+template <typename T>
+__global__ void pack_matrix_k(const float* __restrict__ src, T* __restrict__ dst, int rows, int cols, int ld,
+                              int row_off, int col_off, int mode) {
+  const size_t total = static_cast<size_t>(rows) * cols;
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const int r = static_cast<int>(i / cols), c = static_cast<int>(i % cols);
+    const int dr = mode == 0 ? r + row_off : (r / 16) * 32 + row_off + r % 16;
+    store_from_f32(&dst[static_cast<size_t>(dr) * ld + col_off + c], src[i]);
+  }
+}
+
+__global__ void copy_f32_k(const float* __restrict__ src, float* __restrict__ dst, size_t n) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    dst[i] = src[i];
+}
+
+__global__ void broadcast_rows_k(const float* __restrict__ src, float* __restrict__ dst, int rows, int cols) {
+  const size_t total = static_cast<size_t>(rows) * cols;
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    dst[i] = src[i % cols];
+}
+
+__global__ void zero_k(uint32_t* __restrict__ dst, size_t n_words) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n_words;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    dst[i] = 0u;
+}
+
+// One wave per row; D is a multiple of 64.
+template <typename T>
+__global__ void embed_k(const int32_t* __restrict__ tokens, int n, int rows, const T* __restrict__ E, int V,
+                        int D, float* __restrict__ x, int32_t* __restrict__ flags) {
+  const int row = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  if (row >= rows) return;
+  int tok = tokens[row];  // tokens are [Bc, n] contiguous, same order as rows
+  if (tok < 0 || tok >= V) {
+    if (lane == 0) atomicOr(flags, 1);
+    tok = 0;
+  }
+  const T* src = E + static_cast<size_t>(tok) * D;
+  float* dst = x + static_cast<size_t>(row) * D;
+  for (int c = lane; c < D; c += 64) dst[c] = load_as_f32(src + c);
+  (void)n;
+}
+
+// One wave per row.
+template <typename T>
+__global__ void rmsnorm_rows_k(const float* __restrict__ x, const float* __restrict__ gain, T* __restrict__ out,
+                               int rows, int D, float eps, T* __restrict__ e_store, int n, int b0, int t0,
+                               int Tmax) {
+  const int row = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  if (row >= rows) return;
+  const float* xr = x + static_cast<size_t>(row) * D;
+  float ss = 0.f;
+  for (int c = lane; c < D; c += 64) ss += xr[c] * xr[c];
+  ss = group_sum<64>(ss);
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  T* o = out + static_cast<size_t>(row) * D;
+  T* es = nullptr;
+  if (e_store) {
+    const int b = b0 + row / n, t = t0 + row % n;
+    es = e_store + (static_cast<size_t>(b) * Tmax + t) * D;
+  }
+  for (int c = lane; c < D; c += 64) {
+    const float v = gain[c] * (xr[c] * inv);
+    store_from_f32(o + c, v);
+    if (es) store_from_f32(es + c, v);
+  }
+}
+
+// fp32 [B, n, D] <-> stored layout.  heads_layout 0: [B][T][D]; 1: [B][H][T][dh].
+template <typename T>
+__global__ void store_tokens_k(float* __restrict__ flat, T* __restrict__ dev, int B, int n, int D, int t0, int Tmax,
+                               int heads_layout, int H, int dh, int to_device) {
+  const size_t total = static_cast<size_t>(B) * n * D;
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const int c = static_cast<int>(i % D);
+    const size_t bj = i / D;
+    const int j = static_cast<int>(bj % n), b = static_cast<int>(bj / n);
+    size_t di;
+    if (heads_layout) {
+      const int h = c / dh, cc = c % dh;
+      di = ((static_cast<size_t>(b) * H + h) * Tmax + t0 + j) * dh + cc;
+    } else {
+      di = (static_cast<size_t>(b) * Tmax + t0 + j) * D + c;
+    }
+    if (to_device)
+      store_from_f32(dev + di, flat[i]);
+    else
+      flat[i] = load_as_f32(dev + di);
+  }
+  (void)H;
+}
+
+}  // namespace
+
+hipError_t launch_pack_matrix(const float* src, void* dst, int rows, int cols, int ld, int row_off, int col_off,
+                              int mode, int dtype, hipStream_t st) {
+  const int g = grid_for(static_cast<size_t>(rows) * cols);
+  if (dtype == RLT_DTYPE_BF16)
+    pack_matrix_k<bf16_t><<<g, kThreads, 0, st>>>(src, static_cast<bf16_t*>(dst), rows, cols, ld, row_off, col_off,
+                                                  mode);
+  else
+    pack_matrix_k<float><<<g, kThreads, 0, st>>>(src, static_cast<float*>(dst), rows, cols, ld, row_off, col_off,
+                                                 mode);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t st) {
+  copy_f32_k<<<grid_for(n), kThreads, 0, st>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_broadcast_rows(const float* src, float* dst, int rows, int cols, hipStream_t st) {
+  broadcast_rows_k<<<grid_for(static_cast<size_t>(rows) * cols), kThreads, 0, st>>>(src, dst, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t st) {
+  // All regions are 256-byte aligned and sized in whole 4-byte words.
+  const size_t words = bytes / 4;
+  zero_k<<<grid_for(words), kThreads, 0, st>>>(static_cast<uint32_t*>(dst), words);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const int32_t* tokens, int n, int b0, int rows, const void* embed, int V, int D, int dtype,
+                        float* x, int32_t* flags, hipStream_t st) {
+  (void)b0;
+  const int g = (rows + 3) / 4;
+  if (dtype == RLT_DTYPE_BF16)
+    embed_k<bf16_t><<<g, 256, 0, st>>>(tokens, n, rows, static_cast<const bf16_t*>(embed), V, D, x, flags);
+  else
+    embed_k<float><<<g, 256, 0, st>>>(tokens, n, rows, static_cast<const float*>(embed), V, D, x, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_rows(const float* x, const float* gain, void* out, int rows, int D, float eps, int dtype,
+                               void* e_store, int n, int b0, int t0, int Tmax, hipStream_t st) {
+  const int g = (rows + 3) / 4;
+  if (dtype == RLT_DTYPE_BF16)
+    rmsnorm_rows_k<bf16_t><<<g, 256, 0, st>>>(x, gain, static_cast<bf16_t*>(out), rows, D, eps,
+                                              static_cast<bf16_t*>(e_store), n, b0, t0, Tmax);
+  else
+    rmsnorm_rows_k<float><<<g, 256, 0, st>>>(x, gain, static_cast<float*>(out), rows, D, eps,
+                                             static_cast<float*>(e_store), n, b0, t0, Tmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_tokens(const float* src, void* dst, int B, int n, int D, int t0, int Tmax, int dtype,
+                               int heads_layout, int H, int dh, int to_device_layout, hipStream_t st) {
+  const int g = grid_for(static_cast<size_t>(B) * n * D);
+  float* flat = const_cast<float*>(src);
+  if (dtype == RLT_DTYPE_BF16)
+    store_tokens_k<bf16_t><<<g, kThreads, 0, st>>>(flat, static_cast<bf16_t*>(dst), B, n, D, t0, Tmax, heads_layout,
+                                                   H, dh, to_device_layout);
+  else
+    store_tokens_k<float><<<g, kThreads, 0, st>>>(flat, static_cast<float*>(dst), B, n, D, t0, Tmax, heads_layout, H,
+                                                  dh, to_device_layout);
+  return hipGetLastError();
+}
+
+}  // namespace rlt

@@ -1,0 +1,149 @@
+// Internal layouts and kernel launchers of librlt (host side; no torch types).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rlt.h"
+
+namespace rlt {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// ---------------------------------------------------------------------------
+// Packed model workspace (byte offsets from the workspace base).
+// Matrices are stored in the model's storage type (bf16 or fp32), [rows, K]
+// row-major with K contiguous, which is the "B^T" operand of every
+// A[M,K] x W[N,K]^T product and the row order of every matrix-vector product.
+//   wgate  [d, 2d]: row j = [W_ge[j,:], W_gs[j,:]]   (gate pre-activation from [e; s])
+//   wfb    [d, d]
+//   layer l block: wqkv [3d, d] (rows W_Q; W_K; W_V), wo [d, d], wqx [d, d],
+//                  wox [d, d], ffn_in [F or 2F, d], ffn_out [d, F]
+//     SwiGLU ffn_in interleaves gate and up rows in blocks of 16:
+//     rows 32j..32j+15 = W_gate rows 16j..16j+15, rows 32j+16..32j+31 = W_up rows.
+//   wkvm per group [2d, d]: rows W_KM; W_VM
+//   gains (fp32): g_enc_attn[L][d], g_enc_ffn[L][d], g_enc_final[d],
+//                 g_dec_self[L][d], g_dec_cross[L][d], g_dec_ffn[L][d], g_dec_final[d]
+// ---------------------------------------------------------------------------
+struct ModelLayout {
+  int D, H, DH, L, F, F2, V, W, G, ffn_kind, dtype;
+  float eps;
+  size_t esz;  // bytes per stored element
+  size_t embed, wout, sstar, wgate, wfb, bg;
+  size_t layers, layer_stride;
+  size_t l_qkv, l_wo, l_wqx, l_wox, l_fin, l_fout;  // relative to the layer block
+  size_t wkvm, group_stride;
+  size_t gains;  // fp32 region
+  size_t g_enc_attn, g_enc_ffn, g_enc_final, g_dec_self, g_dec_cross, g_dec_ffn, g_dec_final;  // byte offsets
+  size_t total;
+};
+
+// ---------------------------------------------------------------------------
+// State blob (byte offsets from the state base).
+//   flags   int32[64]            device error flags
+//   s       fp32 [B][d]          recurrent output s_t
+//   ring_k/v  [L][B][H][W-1][dh] window caches (entry of position p in slot p mod (W-1))
+//   e         [B][T_max][d]
+//   mem_k/v   [G][B][H][T_max][dh]
+//   enc_k/v   [L][B][H][T_max][dh]  (only with keep_encoder_cache)
+//   encoder scratch for a chunk of Nc tokens: x fp32 [Nc][d], h [Nc][d], qkv [Nc][3d],
+//                                              attn [Nc][d], act [Nc][F]
+//   decoder scratch (batched path): see dec_batched.hip
+// ---------------------------------------------------------------------------
+struct StateLayout {
+  int B, T, keep, Wm1, Nc;
+  size_t flags, s, ring_k, ring_v, e, mem_k, mem_v, enc_k, enc_v;
+  size_t x, h, qkv, attn, act;
+  size_t dec_scratch, dec_scratch_bytes;
+  size_t total;
+};
+
+bool compute_model_layout(const rlt_config& c, ModelLayout* m);
+void compute_state_layout(const ModelLayout& m, int B, int T, int keep, StateLayout* s);
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (defined in the .hip files).  All return hipError_t of the launch.
+// ---------------------------------------------------------------------------
+
+// dst rows r (< rows) of a [rows, cols] fp32 source go to dst row map(r):
+//   mode 0: r + row_off;  mode 1 (SwiGLU interleave): (r/16)*32 + row_off + r%16
+// and to columns col_off .. col_off+cols-1 of a destination with row length ld.
+hipError_t launch_pack_matrix(const float* src, void* dst, int rows, int cols, int ld, int row_off,
+                              int col_off, int mode, int dtype, hipStream_t st);
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t st);
+hipError_t launch_broadcast_rows(const float* src, float* dst, int rows, int cols, hipStream_t st);
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t st);
+
+// x[m, :] = E[tok(m)] for chunk rows m = i*n + j (sequence b0+i, position j of the call).
+hipError_t launch_embed(const int32_t* tokens, int n, int b0, int rows, const void* embed, int V,
+                        int D, int dtype, float* x, int32_t* flags, hipStream_t st);
+
+// out[m,:] = storage(g * x[m,:] / rms(x[m,:])); optionally also e[b, t0+j, :] for m = i*n+j.
+hipError_t launch_rmsnorm_rows(const float* x, const float* gain, void* out, int rows, int D,
+                               float eps, int dtype, void* e_store, int n, int b0, int t0,
+                               int Tmax, hipStream_t st);
+
+enum GemmEpi {
+  EPI_STORE = 0,        // out[m, n] = storage(acc)          (storage dtype)
+  EPI_STORE_F32 = 1,    // outf[m, n] = acc                    (fp32)
+  EPI_RESID_F32 = 2,    // outf[m, n] += acc                   (fp32 residual)
+  EPI_GELU = 3,         // out[m, n] = storage(gelu(acc))
+  EPI_SWIGLU = 4,       // out[m, n/32*16 + n%16] = storage(silu(gate) * up), interleaved rows
+  EPI_SCATTER_HEADS = 5 // columns [c0, c0+2D) scattered to [B][H][T][dh] (K half, V half)
+};
+
+struct GemmArgs {
+  const void* A;      // [M, K] row-major, lda
+  const void* W;      // [N, K] row-major, ldw
+  void* out;          // epilogue destination
+  int M, N, K, lda, ldw, ldo;
+  int a_f32;          // A is fp32 (converted to the storage type on load)
+  int epi;
+  // EPI_STORE with scatter of columns >= scatter_c0 (K/V of QKV into a cache) and
+  // EPI_SCATTER_HEADS: destination [B][H][T][dh] for which = (n - c0) / D in {0 (k), 1 (v)}.
+  void* sc_k;
+  void* sc_v;
+  int sc_c0;          // first scattered column (D for QKV, 0 for memory projections)
+  int sc_n, sc_b0, sc_t0, sc_T, sc_H, sc_dh, sc_D, sc_B;  // row m -> (b0 + m/n, t0 + m%n)
+};
+hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
+
+// Causal attention for Bc sequences x H heads, queries at positions t0..t0+n-1
+// (q rows from a [Bc*n, ldq] buffer, head h at column h*dh), keys/values at positions
+// 0..t0+n-1 read from a [B][H][T][dh] layout (kv_ld_b = stride between sequences,
+// kv_ld_h = between heads, kv_ld_t = between positions).  Output [Bc*n, D] storage dtype.
+struct AttnArgs {
+  const void* q; int ldq;
+  const void* k; const void* v;
+  long long kv_ld_b, kv_ld_h, kv_ld_t;
+  void* out; int ldo;
+  int Bc, H, dh, n, t0;
+};
+hipError_t launch_enc_attention(const AttnArgs& a, int dtype, hipStream_t st);
+
+// Persistent small-d decoder: one workgroup per sequence, steps t0 .. t0+n-1.
+struct DecSmallArgs {
+  const char* ws;      // packed model workspace
+  char* state;         // state blob
+  float* s_out;        // [B][n][D] or null
+  int B, T, t0, n;
+};
+bool dec_small_supported(const ModelLayout& m, int T);
+size_t dec_small_lds_bytes(const ModelLayout& m, int T);
+hipError_t launch_dec_small(const ModelLayout& m, const StateLayout& s, const DecSmallArgs& a,
+                            hipStream_t st);
+
+// Test-hook conversions between fp32 [.., n, d] and the stored layouts.
+hipError_t launch_store_tokens(const float* src, void* dst, int B, int n, int D, int t0, int Tmax,
+                               int dtype, int heads_layout, int H, int dh, int to_device_layout,
+                               hipStream_t st);
+
+// Batched (large-d) decoder step loop.
+bool dec_batched_supported(const ModelLayout& m);
+size_t dec_batched_scratch_bytes(const ModelLayout& m, int B, int T);
+hipError_t run_dec_batched(const ModelLayout& m, const StateLayout& s, const char* ws, char* state,
+                           float* s_out, int t0, int n, hipStream_t st);
+
+}  // namespace rlt

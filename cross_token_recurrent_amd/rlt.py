@@ -1,0 +1,302 @@
+"""Thin Python binding of librlt.so (argument marshalling only).
+
+Every function named ``rlt_*`` here calls the C entry point of the same name with
+device pointers taken from torch tensors and the current torch stream; all compute
+runs in the HIP kernels of the library.  The classes ``Model`` and ``State`` only own
+the device buffers (allocated through torch) and the C handles.
+
+There is no fallback: if librlt.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librlt.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "rlt.h")
+
+RLT_OK = 0
+ERRORS = {
+    -1: "RLT_ERR_INVALID", -2: "RLT_ERR_UNSUPPORTED", -3: "RLT_ERR_CAPACITY", -4: "RLT_ERR_ORDER",
+    -5: "RLT_ERR_STALE_STATE", -6: "RLT_ERR_NO_ENC_CACHE", -7: "RLT_ERR_HIP",
+}
+FFN_KINDS = {"gelu": 0, "swiglu": 1}
+DTYPES = {"fp32": 0, "bf16": 1}
+
+
+class RltError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+
+
+class rlt_config(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("ffn_dim", ctypes.c_int32), ("ffn_kind", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("mem_groups", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIGS = {
+    "rlt_param_count": [ctypes.POINTER(rlt_config), ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_int64)],
+    "rlt_param_info": [ctypes.POINTER(rlt_config), _I32, ctypes.POINTER(ctypes.c_char_p),
+                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)],
+    "rlt_model_workspace_bytes": [ctypes.POINTER(rlt_config), ctypes.POINTER(ctypes.c_size_t)],
+    "rlt_model_create": [ctypes.POINTER(rlt_config), _P, ctypes.c_uint64, _P, ctypes.c_size_t, _P,
+                         ctypes.POINTER(_P)],
+    "rlt_model_update_weights": [_P, _P, ctypes.c_uint64, _P],
+    "rlt_model_get_config": [_P, ctypes.POINTER(rlt_config), ctypes.POINTER(ctypes.c_uint64)],
+    "rlt_model_release": [_P],
+    "rlt_state_bytes": [_P, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)],
+    "rlt_state_init": [_P, _P, ctypes.c_size_t, _I32, _I32, _I32, _P, ctypes.POINTER(_P)],
+    "rlt_state_reset": [_P, _P, _P],
+    "rlt_state_release": [_P],
+    "rlt_state_position": [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_uint64)],
+    "rlt_state_device_error": [_P, _P, ctypes.POINTER(_I32)],
+    "rlt_encoder_forward": [_P, _P, _P, _I32, _P],
+    "rlt_decoder_replay": [_P, _P, _I32, _P, _P],
+    "rlt_decoder_step": [_P, _P, _P, _P, _P, _P],
+    "rlt_logits": [_P, _P, ctypes.c_int64, _P, _P],
+    "rlt_state_load_encoder_outputs": [_P, _P, _P, _P, _P, _I32, _P],
+    "rlt_state_read_encoder_outputs": [_P, _P, _I32, _I32, _P, _P, _P, _P],
+    "rlt_decoder_path": [_P, _I32, ctypes.POINTER(_I32)],
+    "rlt_last_error": [],
+    "rlt_version_string": [],
+}
+_VOID = {"rlt_model_release", "rlt_state_release"}
+_STR = {"rlt_last_error", "rlt_version_string"}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def header_symbols() -> list:
+    """Entry points declared in include/rlt.h."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"\b(rlt_[a-z_0-9]+)\s*\(", text)))
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"librlt.so not built ({path}); run `python -m cross_token_recurrent_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = None if name in _VOID else (ctypes.c_char_p if name in _STR else ctypes.c_int)
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != RLT_OK:
+        raise RltError(rc, load_library().rlt_last_error().decode())
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def make_config(model_cfg) -> rlt_config:
+    """rlt_config from any object with the model-shape attributes (e.g. workloads.ModelConfig)."""
+    c = model_cfg
+    return rlt_config(c.vocab, c.d_model, c.n_heads, c.n_layers, c.ffn_dim, FFN_KINDS[c.ffn_kind], c.window,
+                      c.mem_groups, DTYPES[c.dtype], c.norm_eps)
+
+
+# ---- C entry points with the same names -------------------------------------------------
+
+def rlt_param_table(cfg: rlt_config) -> Dict[str, Tuple[int, int]]:
+    lib = load_library()
+    n, tot = _I32(), ctypes.c_int64()
+    _check(lib.rlt_param_count(ctypes.byref(cfg), ctypes.byref(n), ctypes.byref(tot)))
+    out = {}
+    for i in range(n.value):
+        name, off, numel = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.rlt_param_info(ctypes.byref(cfg), i, ctypes.byref(name), ctypes.byref(off), ctypes.byref(numel)))
+        out[name.value.decode()] = (off.value, numel.value)
+    return out
+
+
+def rlt_model_workspace_bytes(cfg: rlt_config) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().rlt_model_workspace_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def rlt_encoder_forward(model: "Model", state: "State", tokens: torch.Tensor, stream=None) -> None:
+    assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tokens.dim() == 2
+    assert tokens.shape[0] == state.batch and tokens.device == state.device
+    _check(load_library().rlt_encoder_forward(model.handle, state.handle, _ptr(tokens), tokens.shape[1],
+                                              _stream(stream)))
+
+
+def rlt_decoder_replay(model: "Model", state: "State", n: int, s_out: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    if s_out is not None:
+        assert s_out.dtype == torch.float32 and s_out.is_contiguous()
+        assert tuple(s_out.shape) == (state.batch, n, model.d_model) and s_out.device == state.device
+    _check(load_library().rlt_decoder_replay(model.handle, state.handle, n, _ptr(s_out), _stream(stream)))
+
+
+def rlt_decoder_step(model: "Model", state: "State", tokens: torch.Tensor, s_out: Optional[torch.Tensor] = None,
+                     logits: Optional[torch.Tensor] = None, stream=None) -> None:
+    assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tuple(tokens.shape) == (state.batch,)
+    if s_out is not None:
+        assert s_out.dtype == torch.float32 and tuple(s_out.shape) == (state.batch, model.d_model)
+    if logits is not None:
+        assert logits.dtype == torch.float32 and tuple(logits.shape) == (state.batch, model.vocab)
+    _check(load_library().rlt_decoder_step(model.handle, state.handle, _ptr(tokens), _ptr(s_out), _ptr(logits),
+                                           _stream(stream)))
+
+
+def rlt_logits(model: "Model", s: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    assert s.dtype == torch.float32 and s.is_contiguous() and s.shape[-1] == model.d_model
+    rows = s.numel() // model.d_model
+    if out is None:
+        out = torch.empty(*s.shape[:-1], model.vocab, dtype=torch.float32, device=s.device)
+    assert out.is_contiguous() and out.numel() == rows * model.vocab
+    _check(load_library().rlt_logits(model.handle, _ptr(s), rows, _ptr(out), _stream(stream)))
+    return out
+
+
+def rlt_state_load_encoder_outputs(model: "Model", state: "State", e: torch.Tensor, mem_k: torch.Tensor,
+                                   mem_v: torch.Tensor, stream=None) -> None:
+    n = e.shape[1]
+    G = model.mem_groups
+    assert e.dtype == mem_k.dtype == mem_v.dtype == torch.float32
+    assert tuple(e.shape) == (state.batch, n, model.d_model)
+    assert tuple(mem_k.shape) == (G, state.batch, n, model.d_model) == tuple(mem_v.shape)
+    _check(load_library().rlt_state_load_encoder_outputs(model.handle, state.handle, _ptr(e.contiguous()),
+                                                         _ptr(mem_k.contiguous()), _ptr(mem_v.contiguous()), n,
+                                                         _stream(stream)))
+
+
+def rlt_state_read_encoder_outputs(model: "Model", state: "State", t0: int, n: int, stream=None):
+    B, d, G = state.batch, model.d_model, model.mem_groups
+    e = torch.empty(B, n, d, dtype=torch.float32, device=state.device)
+    mk = torch.empty(G, B, n, d, dtype=torch.float32, device=state.device)
+    mv = torch.empty_like(mk)
+    _check(load_library().rlt_state_read_encoder_outputs(model.handle, state.handle, t0, n, _ptr(e), _ptr(mk),
+                                                         _ptr(mv), _stream(stream)))
+    return e, mk, mv
+
+
+# ---- owners of device memory and handles --------------------------------------------------
+
+class Model:
+    """Packed weights (device workspace owned here) and the C model handle."""
+
+    def __init__(self, model_cfg, weights: Dict[str, np.ndarray], version: int = 1, device="cuda:0",
+                 stream=None):
+        lib = load_library()
+        self.cfg = make_config(model_cfg)
+        self.device = torch.device(device)
+        self.d_model, self.vocab = self.cfg.d_model, self.cfg.vocab
+        self.mem_groups = self.cfg.mem_groups
+        ws_bytes = rlt_model_workspace_bytes(self.cfg)
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
+        flat = self._flatten(weights)
+        h = ctypes.c_void_p()
+        _check(lib.rlt_model_create(ctypes.byref(self.cfg), _ptr(flat), version, _ptr(self.workspace), ws_bytes,
+                                    _stream(stream), ctypes.byref(h)))
+        self.handle = h
+        self._sync(stream)   # the fp32 source buffer must outlive the pack kernels
+        del flat
+
+    def _flatten(self, weights: Dict[str, np.ndarray]) -> torch.Tensor:
+        table = rlt_param_table(self.cfg)
+        total = sum(n for _, n in table.values())
+        flat = torch.empty(total, dtype=torch.float32, device=self.device)
+        for name, (off, numel) in table.items():
+            w = np.ascontiguousarray(weights[name], dtype=np.float32).reshape(-1)
+            if w.size != numel:
+                raise ValueError(f"weight {name}: {w.size} elements, expected {numel}")
+            flat[off:off + numel].copy_(torch.from_numpy(w))
+        return flat
+
+    def _sync(self, stream=None):
+        (stream or torch.cuda.current_stream()).synchronize()
+
+    def update_weights(self, weights: Dict[str, np.ndarray], version: int, stream=None) -> None:
+        flat = self._flatten(weights)
+        _check(load_library().rlt_model_update_weights(self.handle, _ptr(flat), version, _stream(stream)))
+        self._sync(stream)
+
+    @property
+    def version(self) -> int:
+        v = ctypes.c_uint64()
+        _check(load_library().rlt_model_get_config(self.handle, None, ctypes.byref(v)))
+        return v.value
+
+    def decoder_path(self, batch: int) -> int:
+        p = _I32()
+        _check(load_library().rlt_decoder_path(self.handle, batch, ctypes.byref(p)))
+        return p.value
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.rlt_model_release(self.handle)
+            self.handle = None
+
+
+class State:
+    """H_t = (s_t, window caches) plus the encoder side, in one device blob owned here."""
+
+    def __init__(self, model: Model, batch: int, t_max: int, keep_encoder_cache: bool = False, stream=None):
+        lib = load_library()
+        self.model, self.batch, self.t_max = model, batch, t_max
+        self.device = model.device
+        nbytes = ctypes.c_size_t()
+        _check(lib.rlt_state_bytes(model.handle, batch, t_max, int(keep_encoder_cache), ctypes.byref(nbytes)))
+        self.buffer = torch.empty(nbytes.value, dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        _check(lib.rlt_state_init(model.handle, _ptr(self.buffer), nbytes.value, batch, t_max,
+                                  int(keep_encoder_cache), _stream(stream), ctypes.byref(h)))
+        self.handle = h
+
+    def reset(self, stream=None) -> None:
+        _check(load_library().rlt_state_reset(self.model.handle, self.handle, _stream(stream)))
+
+    def position(self) -> Tuple[int, int, int]:
+        te, td, v = _I32(), _I32(), ctypes.c_uint64()
+        _check(load_library().rlt_state_position(self.handle, ctypes.byref(te), ctypes.byref(td), ctypes.byref(v)))
+        return te.value, td.value, v.value
+
+    def device_error(self, stream=None) -> int:
+        f = _I32()
+        _check(load_library().rlt_state_device_error(self.handle, _stream(stream), ctypes.byref(f)))
+        return f.value
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.rlt_state_release(self.handle)
+            self.handle = None
+
+
+def replay(model: Model, state: State, tokens: torch.Tensor, with_logits: bool = True, stream=None):
+    """Exact replay from H_0: reset, encode all tokens, decode all positions, logits."""
+    B, T = tokens.shape
+    state.reset(stream)
+    rlt_encoder_forward(model, state, tokens, stream)
+    S = torch.empty(B, T, model.d_model, dtype=torch.float32, device=state.device)
+    rlt_decoder_replay(model, state, T, S, stream)
+    Z = rlt_logits(model, S, stream=stream) if with_logits else None
+    return S, Z

@@ -1,0 +1,202 @@
+/*
+ * rlt.h — C ABI of librlt.so: Recurrent Looped Transformer (RLT) exact replay on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles as printed):
+ *   [FI] feinterview: "普林斯顿提出 RLT：跨 Token 携带解码器状态的循环 Transformer"
+ *   [DS] deepsonar:   "技术拆解 009｜RLT：给 Transformer 接一条时间回路，潜变量推理与「无限时间深度」的真面目"
+ *   [AL] alphalab:    "Recurrent Looped Transformer：路徑變深，就真的更會推理嗎？（2026）"
+ *
+ * The library computes one sequence family in three calls that follow the pages'
+ * state contract ([FI] decoder-state paragraph; [DS] §2.3, §2.5):
+ *   rlt_encoder_forward  causal encoder over known tokens, token-parallel: e_t and
+ *                        the key/value memory M_{<=t} ([FI] architecture paragraph).
+ *   rlt_decoder_replay   the recurrent decoder, stepping t in order, batched over
+ *                        B independent sequences ([FI] model-hardware co-design).
+ *   rlt_decoder_step     incremental generation: encode one token per sequence,
+ *                        one transition, logits ([DS] §2.5).
+ * Exact current-policy replay ([FI] model-RL co-design; [AL] §四) is
+ *   rlt_state_reset + rlt_encoder_forward(T) + rlt_decoder_replay(T) + rlt_logits.
+ * There is no prompt/response argument anywhere: the split never touches the state
+ * (Proposition 3.1 on [FI]; [AL] §一).
+ *
+ * Conventions
+ *  - Every pointer marked "device" is device memory owned by the caller; the
+ *    library never allocates or frees device memory.  It keeps small host handles.
+ *  - Every call that takes a stream only enqueues work on that stream (a
+ *    hipStream_t passed as void*; NULL = the default stream) and returns before the
+ *    work runs.  Host-side argument and ordering checks happen before anything is
+ *    enqueued, so a non-zero return means nothing was enqueued.
+ *  - A model is immutable between rlt_model_update_weights calls and may be shared by
+ *    states on several streams; one state must be used by one stream at a time.
+ *  - Return value: RLT_OK (0) or a negative RLT_ERR_* code; rlt_last_error() gives a
+ *    thread-local message for the last failure.  No C++ exception crosses the ABI.
+ *  - Matrices are [out, in] row-major (y = W x).
+ */
+#ifndef RLT_H
+#define RLT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RLT_OK 0
+#define RLT_ERR_INVALID (-1)       /* bad argument or configuration value            */
+#define RLT_ERR_UNSUPPORTED (-2)   /* configuration outside what the kernels support */
+#define RLT_ERR_CAPACITY (-3)      /* position would exceed the state's T_max        */
+#define RLT_ERR_ORDER (-4)         /* decoder would run ahead of the encoder, etc.   */
+#define RLT_ERR_STALE_STATE (-5)   /* state built under another weights version      */
+#define RLT_ERR_NO_ENC_CACHE (-6)  /* incremental encoding without an encoder cache  */
+#define RLT_ERR_HIP (-7)           /* a HIP runtime call failed                      */
+
+#define RLT_FFN_GELU 0             /* W_2 gelu(W_1 h), exact erf GELU                */
+#define RLT_FFN_SWIGLU 1           /* W_down(silu(W_gate h) * W_up h)                */
+#define RLT_DTYPE_FP32 0           /* all storage and arithmetic fp32                */
+#define RLT_DTYPE_BF16 1           /* bf16 storage of weights, e, M, window caches and
+                                      matrix-product operands; fp32 accumulation,
+                                      residual stream, s_t, softmax and logits      */
+
+typedef struct rlt_model rlt_model;
+typedef struct rlt_state rlt_state;
+
+/* Model shape.  L = n_layers is both L_E and L_D: encoder layer l and decoder layer l
+ * share W_Q, W_K, W_V, W_O and the FFN ([FI] tied-configuration paragraph; [DS] §2.1).
+ * window W >= 1 counts the current token, so W-1 past entries are cached per decoder
+ * layer ([DS] §2.2; [FI] decoder-state paragraph).  mem_groups G is 1 (one memory for
+ * all decoder layers) or n_layers (one per layer) ([FI] architecture paragraph); any
+ * other value is RLT_ERR_UNSUPPORTED.  Kernel limits (RLT_ERR_UNSUPPORTED otherwise):
+ * d_model % 64 == 0, ffn_dim % 64 == 0, head_dim = d_model / n_heads in {16,32,64,128}. */
+typedef struct {
+  int32_t vocab;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_layers;
+  int32_t ffn_dim;
+  int32_t ffn_kind;    /* RLT_FFN_*   */
+  int32_t window;      /* W >= 1      */
+  int32_t mem_groups;  /* 1 or L      */
+  int32_t dtype;       /* RLT_DTYPE_* */
+  float norm_eps;      /* RMSNorm epsilon, > 0 */
+} rlt_config;
+
+/* ---- canonical flat weight layout ------------------------------------------------
+ * rlt_model_create reads all parameters from ONE fp32 buffer holding the tensors
+ * below back to back, in this order, each row-major (per-layer tensors carry a
+ * leading L axis, memory projections a leading G axis):
+ *   embed [V,d]; w_out [V,d]; s_star [d]; w_ge, w_gs, w_fb [d,d]; b_g [d];
+ *   wq, wk, wv, wo [L,d,d];
+ *   GELU:   ffn_w1 [L,F,d]; ffn_w2 [L,d,F]
+ *   SwiGLU: ffn_gate [L,F,d]; ffn_up [L,F,d]; ffn_down [L,d,F]
+ *   wqx, wox [L,d,d]; wkm, wvm [G,d,d];
+ *   g_enc_attn, g_enc_ffn [L,d]; g_enc_final [d];
+ *   g_dec_self, g_dec_cross, g_dec_ffn [L,d]; g_dec_final [d].
+ * rlt_param_info gives each tensor's name, element offset and element count, so a
+ * caller can fill the buffer by name. */
+int rlt_param_count(const rlt_config* cfg, int32_t* n_tensors, int64_t* total_numel);
+int rlt_param_info(const rlt_config* cfg, int32_t index, const char** name,
+                   int64_t* offset, int64_t* numel);
+
+/* ---- model: packed weights ----------------------------------------------------------
+ * rlt_model_workspace_bytes: bytes of the device workspace that rlt_model_create packs
+ * the weights into (bf16 or fp32 per cfg->dtype, kernel-friendly layout).
+ * rlt_model_create: validates cfg, packs the canonical fp32 buffer `weights` (device,
+ * read only during the enqueued pack kernels) into `workspace` (device, >= the size
+ * above, caller-owned, must outlive the model) on `stream`, and returns a host handle.
+ * `version` tags every state built from this model ([FI] serving paragraph: a weight
+ * update invalidates old states). */
+int rlt_model_workspace_bytes(const rlt_config* cfg, size_t* bytes);
+int rlt_model_create(const rlt_config* cfg, const float* weights, uint64_t version,
+                     void* workspace, size_t workspace_bytes, void* stream, rlt_model** out);
+/* Re-packs new weights into the same workspace and sets a new version (must differ
+ * from the current one).  States built under the old version then fail every call
+ * with RLT_ERR_STALE_STATE until rlt_state_reset. */
+int rlt_model_update_weights(rlt_model* model, const float* weights, uint64_t new_version,
+                             void* stream);
+int rlt_model_get_config(const rlt_model* model, rlt_config* cfg, uint64_t* version);
+void rlt_model_release(rlt_model* model);
+
+/* ---- state H_t = (s_t, C^D_t) plus the encoder side ---------------------------------
+ * One device blob holds: s [B,d] fp32; the per-layer window caches (ring buffers of
+ * W-1 entries); e [B,T_max,d]; the memory K^M,V^M [G][B][H][T_max][d_h]; optionally the
+ * encoder key/value cache (needed to encode incrementally); scratch; an error flag.
+ * keep_encoder_cache = 0 allows only one rlt_encoder_forward call per reset (the whole
+ * known sequence at once), which is what exact replay needs.
+ * rlt_state_init sets H_0 = (s*, empty caches), t_enc = t_dec = 0 ([FI] decoder-state
+ * paragraph: initialised once before BOS with the learned start state and empty caches). */
+int rlt_state_bytes(const rlt_model* model, int32_t batch, int32_t t_max,
+                    int32_t keep_encoder_cache, size_t* bytes);
+int rlt_state_init(const rlt_model* model, void* buffer, size_t buffer_bytes, int32_t batch,
+                   int32_t t_max, int32_t keep_encoder_cache, void* stream, rlt_state** out);
+/* Back to H_0 under the model's current weights and version; exact replay always starts
+ * here ([FI] model-RL co-design: rebuild everything from the sequence start). */
+int rlt_state_reset(const rlt_model* model, rlt_state* state, void* stream);
+void rlt_state_release(rlt_state* state);
+
+/* Host-side counters (no device access): positions encoded, positions decoded, version. */
+int rlt_state_position(const rlt_state* state, int32_t* t_enc, int32_t* t_dec,
+                       uint64_t* version);
+/* Reads the device error flag (bit 0: a token id outside [0, V) was seen and replaced
+ * by 0).  Synchronises `stream` first.  Writes 0 when no device error occurred. */
+int rlt_state_device_error(rlt_state* state, void* stream, int32_t* flags);
+
+/* ---- the hot path --------------------------------------------------------------------
+ * rlt_encoder_forward: tokens (device int32 [B, n], row stride n) are positions
+ * t_enc .. t_enc+n-1 of every sequence.  Runs the causal encoder over them (each new
+ * position attends to every earlier one), writes e and the G memory rows, advances
+ * t_enc by n.  Errors: RLT_ERR_CAPACITY if t_enc+n > T_max; RLT_ERR_NO_ENC_CACHE if
+ * t_enc > 0 and the state keeps no encoder cache; RLT_ERR_INVALID if n < 1. */
+int rlt_encoder_forward(const rlt_model* model, rlt_state* state, const int32_t* tokens,
+                        int32_t n, void* stream);
+
+/* rlt_decoder_replay: n recurrent transitions at positions t_dec+1 .. t_dec+n for all B
+ * sequences, in order, inside the library (no host round trip per step).  Each step:
+ * gated merge of e_t with s_{t-1}; L blocks of sliding-window self-attention over the
+ * layer's cache plus the current entry, cross-attention to memory entries 1..t, tied
+ * FFN; final RMSNorm gives s_t ([FI] decoder-state paragraph; [DS] §2.2, §2.4).
+ * s_out (device fp32 [B, n, d], row stride n*d per sequence) receives s_t for every
+ * step, or is NULL.  Requires t_dec + n <= t_enc (RLT_ERR_ORDER otherwise).  Advances
+ * t_dec by n.  Each position is consumed exactly once; there is no rewind. */
+int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, float* s_out,
+                       void* stream);
+
+/* rlt_decoder_step: incremental generation ([DS] §2.5): equals
+ * rlt_encoder_forward(n = 1) + rlt_decoder_replay(n = 1) + rlt_logits on s_t.
+ * tokens: device int32 [B]; s_out: device fp32 [B, d] or NULL; logits: device fp32
+ * [B, V] or NULL.  Needs keep_encoder_cache unless t_enc == 0. */
+int rlt_decoder_step(const rlt_model* model, rlt_state* state, const int32_t* tokens,
+                     float* s_out, float* logits, void* stream);
+
+/* rlt_logits: logits = W_out s for N state rows (next-token distribution read from s_t,
+ * [FI] decoder-state paragraph), token-parallel, off the recurrent loop.
+ * s: device fp32 [N, d]; logits: device fp32 [N, V]. */
+int rlt_logits(const rlt_model* model, const float* s, int64_t n_rows, float* logits,
+               void* stream);
+
+/* ---- test hooks (decoder in isolation, encoder outputs) -----------------------------
+ * rlt_state_load_encoder_outputs writes externally computed e (device fp32 [B, n, d])
+ * and memory rows (device fp32 [G, B, n, d] each for keys and values) for positions
+ * t_enc .. t_enc+n-1 (converted to the storage dtype) and advances t_enc, so the
+ * decoder can be checked on its own.  rlt_state_read_encoder_outputs copies positions
+ * t0 .. t0+n-1 (< t_enc) back out as fp32 in the same layouts. */
+int rlt_state_load_encoder_outputs(const rlt_model* model, rlt_state* state, const float* e,
+                                   const float* mem_k, const float* mem_v, int32_t n,
+                                   void* stream);
+int rlt_state_read_encoder_outputs(const rlt_model* model, const rlt_state* state, int32_t t0,
+                                   int32_t n, float* e, float* mem_k, float* mem_v,
+                                   void* stream);
+
+/* Which decoder implementation rlt_decoder_replay uses for this model and batch:
+ * 0 = one persistent workgroup per sequence (small d_model), 1 = batched per-phase
+ * kernels (large d_model). */
+int rlt_decoder_path(const rlt_model* model, int32_t batch, int32_t* path);
+
+const char* rlt_last_error(void);
+const char* rlt_version_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RLT_H */
