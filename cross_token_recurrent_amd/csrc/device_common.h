@@ -16,12 +16,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (NaN kept quiet).
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+// Two values packed low | high << 16, both rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2_v;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+  const f32x2_v x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_v));
 }
 
 // Value after a round trip through the storage type (identity for fp32).
@@ -71,17 +76,53 @@ __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + e
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-// Butterfly sums / maxima over groups of 2^k lanes (all lanes get the result).
+// Cross-lane data movement inside a row of 16 lanes (DPP, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;       // lane i <-> 15-i within 16
+
+// All-reduce over aligned groups of WIDTH lanes (all lanes of a group must be active).
+// Groups up to 16 use DPP butterflies; 64 adds the four row results read back with
+// v_readlane in a fixed order, so every lane (and every wave) gets bit-identical results.
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  static_assert(WIDTH == 1 || WIDTH == 2 || WIDTH == 4 || WIDTH == 8 || WIDTH == 16 || WIDTH == 32 || WIDTH == 64,
+                "group width");
+  if constexpr (WIDTH >= 2) v += dpp_mov<kDppXor1>(v);
+  if constexpr (WIDTH >= 4) v += dpp_mov<kDppXor2>(v);
+  if constexpr (WIDTH >= 8) v += dpp_mov<kDppHalfMirror>(v);
+  if constexpr (WIDTH >= 16) v += dpp_mov<kDppMirror>(v);
+  if constexpr (WIDTH == 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (WIDTH == 64) {
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    v = (a + b) + (c + d);
+  }
   return v;
 }
 template <int WIDTH>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  static_assert(WIDTH == 1 || WIDTH == 2 || WIDTH == 4 || WIDTH == 8 || WIDTH == 16 || WIDTH == 32 || WIDTH == 64,
+                "group width");
+  if constexpr (WIDTH >= 2) v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  if constexpr (WIDTH >= 4) v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  if constexpr (WIDTH >= 8) v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  if constexpr (WIDTH >= 16) v = fmaxf(v, dpp_mov<kDppMirror>(v));
+  if constexpr (WIDTH == 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+  if constexpr (WIDTH == 64) {
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    v = fmaxf(fmaxf(a, b), fmaxf(c, d));
+  }
   return v;
 }
 
