@@ -9,19 +9,22 @@
 // feedback of s_{t-1}, final norm gives s_t).
 //
 // Why this shape on MI355X: at d_model <= 128 a decoder layer is a handful of 64..256-wide
-// matrix-vector products, so a step is bound by latency (dependent phases, memory round
-// trips), not by HBM or MFMA throughput.  Independent sequences never synchronise, so each
-// sequence gets one 8-wave workgroup that keeps its window caches, running state, gains
-// and small vectors in LDS and synchronises only with s_barrier.  Latency is hidden by:
-//   * weight prefetch: the next matrix-vector product's weights are loaded into registers
-//     one phase ahead (s_barrier does not wait for outstanding global loads);
-//   * RMSNorm fused into the consuming product (each wave recomputes the statistic);
-//   * window self-attention done per head inside one wave (no workgroup barrier);
-//   * cross-attention as one online-softmax pass over memory rows with batched,
-//     pipelined loads whose first batch is issued two phases before it is needed.
+// matrix-vector products and two single-query attentions, so a step is bound by VALU issue
+// and latency, not by HBM or MFMA throughput.  Independent sequences never synchronise,
+// so each sequence gets one workgroup of 4 waves (one per SIMD) that keeps its window
+// caches, running state, gains and small vectors in LDS.  The design keeps the number of
+// wave instructions per step low and the latency hidden:
+//   * matrix-vector products: 8-lane groups per row, weights for the next product
+//     prefetched into registers one phase ahead (s_barrier does not wait for global
+//     loads), RMSNorm fused into the product's operand fetch;
+//   * both attentions run one head per wave with lanes over keys; partial softmax states
+//     are combined inside the wave through LDS (no workgroup barrier);
+//   * cross-attention streams memory rows with batched loads requested two batches ahead,
+//     the first two batches issued two phases before they are needed.
 // bf16 mode: matrix-product operands are packed bf16 in LDS and consumed with
-// v_dot2c_f32_bf16 (exact bf16 products, fp32 accumulation); the residual stream,
-// softmax statistics, attention math and s_t stay fp32.
+// v_dot2c_f32_bf16 (exact bf16 products, fp32 accumulation); the query is split into
+// bf16 hi + lo parts for the score dot products, so attention math keeps ~fp32 accuracy;
+// the residual stream, softmax statistics and s_t stay fp32.
 #include <algorithm>
 
 #include "device_common.h"
@@ -30,26 +33,30 @@
 namespace rlt {
 namespace {
 
-constexpr int NT = 512;          // threads per workgroup (8 waves)
+constexpr int NT = 256;          // threads per workgroup (4 waves, one per SIMD)
 constexpr int NWAVE = NT / 64;
 constexpr int NG = NT / 8;       // 8-lane groups for matrix-vector products
-constexpr int CMAX = 4;          // prefetched (row, chunk) pairs per lane and product
-constexpr int EMAX = 4;          // window entries per lane (window <= 256)
+constexpr int CMAX = 8;          // prefetched (row, chunk) pairs per lane and product
+constexpr int WCAP = 256;        // largest window (entries held at once) supported
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // ---- storage-type operations on 8-element chunks -----------------------------------
 template <typename WT> struct Ops;
 
 template <> struct Ops<bf16_t> {
   struct Chunk { uint4 v; };
-  struct QPack { uint32_t hi[4], lo[4]; };  // query split into bf16 hi + lo parts
   static __device__ __forceinline__ Chunk load(const bf16_t* p) { return {*reinterpret_cast<const uint4*>(p)}; }
   static __device__ __forceinline__ Chunk zero() { return {make_uint4(0u, 0u, 0u, 0u)}; }
-  static __device__ __forceinline__ Chunk lds(const bf16_t* p) { return {*reinterpret_cast<const uint4*>(p)}; }
-  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
   static __device__ __forceinline__ Chunk pack(const float (&f)[8]) {
-    return {make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]))};
+    return {make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                       pack_bf16x2(f[6], f[7]))};
   }
   static __device__ __forceinline__ float d2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
@@ -60,26 +67,6 @@ template <> struct Ops<bf16_t> {
     acc = d2(w.v.y, x.v.y, acc);
     acc = d2(w.v.z, x.v.z, acc);
     return d2(w.v.w, x.v.w, acc);
-  }
-  static __device__ __forceinline__ QPack qpack(const float (&q)[8]) {
-    QPack r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = q[2 * i], b = q[2 * i + 1];
-      const float ah = bf16_to_f32(f32_to_bf16(a)), bh = bf16_to_f32(f32_to_bf16(b));
-      r.hi[i] = pack2(ah, bh);
-      r.lo[i] = pack2(a - ah, b - bh);
-    }
-    return r;
-  }
-  static __device__ __forceinline__ float qdot(const Chunk& k, const QPack& q) {
-    const uint32_t kv[4] = {k.v.x, k.v.y, k.v.z, k.v.w};
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = d2(kv[i], q.lo[i], acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = d2(kv[i], q.hi[i], acc);
-    return acc;
   }
   static __device__ __forceinline__ void unpack(const Chunk& c, float (&f)[8]) {
     const uint32_t w[4] = {c.v.x, c.v.y, c.v.z, c.v.w};
@@ -93,12 +80,12 @@ template <> struct Ops<bf16_t> {
 
 template <> struct Ops<float> {
   struct Chunk { float4 a, b; };
-  struct QPack { float q[8]; };
   static __device__ __forceinline__ Chunk load(const float* p) {
     return {*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
-  static __device__ __forceinline__ Chunk zero() { return {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)}; }
-  static __device__ __forceinline__ Chunk lds(const float* p) { return load(p); }
+  static __device__ __forceinline__ Chunk zero() {
+    return {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  }
   static __device__ __forceinline__ Chunk pack(const float (&f)[8]) {
     return {make_float4(f[0], f[1], f[2], f[3]), make_float4(f[4], f[5], f[6], f[7])};
   }
@@ -107,21 +94,60 @@ template <> struct Ops<float> {
     acc += w.b.x * x.b.x; acc += w.b.y * x.b.y; acc += w.b.z * x.b.z; acc += w.b.w * x.b.w;
     return acc;
   }
-  static __device__ __forceinline__ QPack qpack(const float (&q)[8]) {
-    QPack r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r.q[i] = q[i];
-    return r;
-  }
-  static __device__ __forceinline__ float qdot(const Chunk& k, const QPack& q) {
-    return q.q[0] * k.a.x + q.q[1] * k.a.y + q.q[2] * k.a.z + q.q[3] * k.a.w + q.q[4] * k.b.x + q.q[5] * k.b.y +
-           q.q[6] * k.b.z + q.q[7] * k.b.w;
-  }
   static __device__ __forceinline__ void unpack(const Chunk& c, float (&f)[8]) {
     f[0] = c.a.x; f[1] = c.a.y; f[2] = c.a.z; f[3] = c.a.w;
     f[4] = c.b.x; f[5] = c.b.y; f[6] = c.b.z; f[7] = c.b.w;
   }
 };
+
+// A 16-element query slice, prepared for dot products with 16-element key rows.
+template <typename WT> struct QSlice;
+template <> struct QSlice<bf16_t> {
+  uint32_t hi[8], lo[8];   // q = hi + lo, both bf16 pairs (~16 significant bits)
+  __device__ __forceinline__ void set(const float* q) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a = q[2 * i], b = q[2 * i + 1];
+      const uint32_t h = pack_bf16x2(a, b);
+      hi[i] = h;
+      lo[i] = pack_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+    }
+  }
+  __device__ __forceinline__ float dot(const Ops<bf16_t>::Chunk& k0, const Ops<bf16_t>::Chunk& k1) const {
+    const uint32_t kv[8] = {k0.v.x, k0.v.y, k0.v.z, k0.v.w, k1.v.x, k1.v.y, k1.v.z, k1.v.w};
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = Ops<bf16_t>::d2(kv[i], lo[i], a);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b = Ops<bf16_t>::d2(kv[i], hi[i], b);
+    return a + b;
+  }
+};
+template <> struct QSlice<float> {
+  float q[16];
+  __device__ __forceinline__ void set(const float* src) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = src[i];
+  }
+  __device__ __forceinline__ float dot(const Ops<float>::Chunk& k0, const Ops<float>::Chunk& k1) const {
+    return q[0] * k0.a.x + q[1] * k0.a.y + q[2] * k0.a.z + q[3] * k0.a.w + q[4] * k0.b.x + q[5] * k0.b.y +
+           q[6] * k0.b.z + q[7] * k0.b.w + q[8] * k1.a.x + q[9] * k1.a.y + q[10] * k1.a.z + q[11] * k1.a.w +
+           q[12] * k1.b.x + q[13] * k1.b.y + q[14] * k1.b.z + q[15] * k1.b.w;
+  }
+};
+
+// o[0..16) += w * v (v = two 8-element chunks)
+template <typename WT>
+__device__ __forceinline__ void axpy16(float (&o)[16], float w, const typename Ops<WT>::Chunk& v0,
+                                       const typename Ops<WT>::Chunk& v1) {
+  float f[8];
+  Ops<WT>::unpack(v0, f);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o[c] += w * f[c];
+  Ops<WT>::unpack(v1, f);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o[8 + c] += w * f[c];
+}
 
 // ---- matrix-vector products out[r] = W[r,:] . x ----------------------------------------
 // Lane (grp, sub) owns rows grp, grp+NG, ... and the 8-element chunks sub*8 + 64*c of each
@@ -136,8 +162,8 @@ __device__ __forceinline__ void wprefetch(WBuf<WT>& buf, const WT* __restrict__ 
 #pragma unroll
   for (int p = 0; p < CMAX; ++p) {
     const int ri = p / cpl, ci = p - ri * cpl;
-    const int r = grp + ri * NG;
-    buf.c[p] = r < N ? Ops<WT>::load(W + static_cast<size_t>(r) * K + sub * 8 + ci * 64) : Ops<WT>::zero();
+    const int r = min(grp + ri * NG, N - 1);   // rows past N are loaded but never used
+    buf.c[p] = Ops<WT>::load(W + static_cast<size_t>(r) * K + sub * 8 + ci * 64);
   }
 }
 
@@ -170,7 +196,7 @@ __device__ __forceinline__ void wcompute_c(const WBuf<WT>& buf, const WT* __rest
     float acc = 0.f;
 #pragma unroll
     for (int ci = 0; ci < CPL; ++ci) {
-      const typename O::Chunk w = r < N ? O::load(W + static_cast<size_t>(r) * K + sub * 8 + ci * 64) : O::zero();
+      const typename O::Chunk w = O::load(W + static_cast<size_t>(min(r, N - 1)) * K + sub * 8 + ci * 64);
       acc = O::dot(w, xr[ci], acc);
     }
     acc = group_sum<8>(acc);
@@ -202,6 +228,7 @@ __device__ __forceinline__ void wcompute(const WBuf<WT>& buf, const WT* __restri
     case 2: wcompute_c<2>(buf, W, N, xf, epi); break;
     case 3: wcompute_c<3>(buf, W, N, xf, epi); break;
     case 4: wcompute_c<4>(buf, W, N, xf, epi); break;
+    case 8: wcompute_c<8>(buf, W, N, xf, epi); break;
     default: wcompute_any(W, N, K, xf, epi); break;
   }
 }
@@ -215,6 +242,68 @@ __device__ __forceinline__ float wave_rms_inv(const float* __restrict__ y, float
   for (int c = lane; c < D; c += 64) ss += y[c] * y[c];
   ss = group_sum<64>(ss);
   return 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+}
+
+// Operand chunk k..k+8 of RMS(y; g) in the storage precision.
+template <typename WT>
+__device__ __forceinline__ typename Ops<WT>::Chunk norm_chunk(const float* __restrict__ y,
+                                                              const float* __restrict__ g, float inv, int k) {
+  const float4 y0 = *reinterpret_cast<const float4*>(y + k), y1 = *reinterpret_cast<const float4*>(y + k + 4);
+  const float4 g0 = *reinterpret_cast<const float4*>(g + k), g1 = *reinterpret_cast<const float4*>(g + k + 4);
+  const float f[8] = {g0.x * (y0.x * inv), g0.y * (y0.y * inv), g0.z * (y0.z * inv), g0.w * (y0.w * inv),
+                      g1.x * (y1.x * inv), g1.y * (y1.y * inv), g1.z * (y1.z * inv), g1.w * (y1.w * inv)};
+  return Ops<WT>::pack(f);
+}
+
+// Inside one wave: lanes hold partial softmax states (m, l, o[16]) for the 16 dims starting
+// at dim 16*sub of one head (sub = lane % LPK).  Writes o / l (DH dims) to dst.
+// wbuf: this wave's LDS scratch of 64*17 + 64 floats.
+template <typename WT, int DH>
+__device__ __forceinline__ void wave_combine(float m, float l, float (&o)[16], float* __restrict__ wbuf,
+                                             WT* __restrict__ dst) {
+  constexpr int LPK = DH / 16;
+  constexpr int SLOTS = 64 / LPK;
+  const int lane = threadIdx.x & 63;
+  const float mw = group_max<64>(m);
+  const float f = __expf(m - mw);   // lanes without keys: m = -inf -> 0
+  float* ob = wbuf;                 // [64][17]
+  float* lb = wbuf + 64 * 17;       // [64]
+#pragma unroll
+  for (int c = 0; c < 16; ++c) ob[lane * 17 + c] = o[c] * f;
+  lb[lane] = l * f;
+  wave_sync_lds();
+  if constexpr (DH <= 64) {
+    constexpr int GS = 64 / DH;     // slot groups per dim
+    const int d = lane % DH, g = lane / DH;
+    const int sub = d / 16, c = d % 16;
+    constexpr int PER = SLOTS / GS;
+    float acc = 0.f, lacc = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int s = g + GS * k;
+      acc += ob[(s * LPK + sub) * 17 + c];
+      lacc += lb[s * LPK];
+    }
+#pragma unroll
+    for (int off = DH; off < 64; off <<= 1) {
+      acc += __shfl_xor(acc, off, 64);
+      lacc += __shfl_xor(lacc, off, 64);
+    }
+    if (g == 0) store_from_f32(&dst[d], acc / lacc);
+  } else {
+#pragma unroll
+    for (int d = lane; d < DH; d += 64) {
+      const int sub = d / 16, c = d % 16;
+      float acc = 0.f, lacc = 0.f;
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        acc += ob[(s * LPK + sub) * 17 + c];
+        lacc += lb[s * LPK];
+      }
+      store_from_f32(&dst[d], acc / lacc);
+    }
+  }
+  wave_sync_lds();
 }
 
 struct DecSmallParams {
@@ -242,17 +331,18 @@ template <typename WT, int D, int DH>
 __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   using O = Ops<WT>;
   using Chunk = typename O::Chunk;
-  constexpr int KB = sizeof(WT) == 2 ? 4 : 2;   // memory rows per lane per cross-attention batch
   constexpr int H = D / DH;
-  constexpr int LPK = DH / 8;            // lanes per memory row (8 elements each)
-  constexpr int PARTS = NT / (H * LPK);  // key slices per head in cross-attention
-  static_assert(PARTS >= 8 && PARTS % 8 == 0, "cross-attention partition");
-  static_assert(H <= NWAVE, "one wave per head in window attention");
+  constexpr int LPK = DH / 16;            // lanes per key row (16 elements each)
+  constexpr int SLOTS = 64 / LPK;         // keys per wave pass
+  constexpr int KQ = sizeof(WT) == 2 ? 4 : 2;   // memory rows per lane per load batch
+  constexpr int NSC = 16;                        // scores per lane per chunk
+  static_assert(DH % 16 == 0 && DH <= 128, "head width");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int slot = lane / LPK, sub = lane % LPK;
   const int L = p.L, Wm1 = p.Wm1, T = p.T, F = p.F, F2 = p.F2, G = p.G;
   const float scale = 1.0f / sqrtf(static_cast<float>(DH));
   const int XOPN = 2 * D > F ? 2 * D : F;
@@ -271,11 +361,9 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   float* fbv = gpre + D;                                // [D]
   float* gains = fbv + D;                               // [(3L+1) D]: self, cross, ffn per layer, final
   float* bgl = gains + (3 * L + 1) * D;                 // [D]
-  float* part_m = bgl + D;                              // [H][PARTS]
-  float* part_l = part_m + H * PARTS;                   // [H][PARTS]
-  float* part_o = part_l + H * PARTS;                   // [H][PARTS][DH]
-  float* swa_p = part_o + H * PARTS * DH;               // [H][EMAX*64] window probabilities
-  float* act_raw = swa_p + H * EMAX * 64;               // [F2] (SwiGLU gate/up pre-activations)
+  float* wscr = bgl + D;                                // [NWAVE][64*17 + 64] wave scratch
+  float* act_raw = wscr + NWAVE * (64 * 17 + 64);       // [F2] (SwiGLU gate/up pre-activations)
+  float* my_scr = wscr + wave * (64 * 17 + 64);
 
   // ---- carried state, gains ----
   {
@@ -303,11 +391,8 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
     }
   }
   const WT* e_seq = static_cast<const WT*>(p.e) + static_cast<size_t>(b) * T * D;
-  // e_{t0} -> xop[0, D)
-  for (int c = tid * 8; c < D; c += NT * 8) {
-    const Chunk ec = O::load(e_seq + static_cast<size_t>(p.t0) * D + c);
-    *reinterpret_cast<Chunk*>(xop + c) = ec;
-  }
+  for (int c = tid * 8; c < D; c += NT * 8)
+    *reinterpret_cast<Chunk*>(xop + c) = O::load(e_seq + static_cast<size_t>(p.t0) * D + c);
   const WT* wgate = static_cast<const WT*>(p.wgate);
   const WT* wfb = static_cast<const WT*>(p.wfb);
   auto layer_w = [&](int l, size_t off) {
@@ -319,16 +404,10 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   wprefetch(wb, wfb, D, D);
   __syncthreads();
 
-  auto xf_op = [&](const WT* v) { return [=](int k) { return O::lds(v + k); }; };
-
-  // cross-attention lane roles
-  const int xh = tid / (PARTS * LPK);
-  const int xpart = (tid / LPK) % PARTS;
-  const int xsub = tid % LPK;
+  auto xf_op = [&](const WT* v) { return [=](int k) { return O::load(v + k); }; };
 
   for (int step = 0; step < p.n; ++step) {
     const int t = p.t0 + step;   // 0-based position of this transition
-    // prefetch e_{t+1} for the next step's merge
     Chunk e_next = O::zero();
     const bool has_next = step + 1 < p.n;
     if (has_next && tid * 8 < D) e_next = O::load(e_seq + static_cast<size_t>(t + 1) * D + tid * 8);
@@ -352,121 +431,66 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       WT* rK = ringK + static_cast<size_t>(l) * H * Wm1 * DH;
       WT* rV = ringV + static_cast<size_t>(l) * H * Wm1 * DH;
 
-      // ---- P1: q,k,v = W_{Q,K,V} RMS(y; g_self) ----
+      // ---- P1: q,k,v = W_{Q,K,V} RMS(y; g_self); q pre-scaled by 1/sqrt(d_h) ----
       {
         const float inv = wave_rms_inv<D>(y, p.eps);
-        auto xf = [&](int k) {
-          float f[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = g_self[k + i] * (y[k + i] * inv);
-          return O::pack(f);
-        };
-        wcompute(wa, layer_w(l, p.l_qkv), 3 * D, D, xf,
-                 [&](int r, float v) { qkv[r] = r < D ? v : round_to<WT>(v); });
+        wcompute(wa, layer_w(l, p.l_qkv), 3 * D, D, [&](int k) { return norm_chunk<WT>(y, g_self, inv, k); },
+                 [&](int r, float v) { qkv[r] = r < D ? v * scale : round_to<WT>(v); });
         wprefetch(wa, layer_w(l, p.l_wqx), D, D);
       }
       __syncthreads();
 
-      // ---- P2: window self-attention, one wave per head ----
+      // ---- P2: window self-attention, one head per wave, lanes over window entries ----
       const int npast = min(t, Wm1);        // cached entries in the window
       const int ne = npast + 1;             // plus the current token
-      const int slot0 = Wm1 > 0 ? (t - npast) % Wm1 : 0;   // slot of the oldest cached entry
-      auto slot_of = [&](int i) {
-        const int sl = slot0 + i;
-        return sl >= Wm1 ? sl - Wm1 : sl;
-      };
+      const int slot0 = Wm1 > 0 ? (t - npast) % Wm1 : 0;   // ring slot of the oldest entry
       for (int h = wave; h < H; h += NWAVE) {
-        const float* q = qkv + h * DH;
-        float sc[EMAX];
-        float mx = -INFINITY;
+        QSlice<WT> qs;
+        qs.set(qkv + h * DH + sub * 16);
+        float m = -INFINITY, lsum = 0.f;
+        float o[16];
 #pragma unroll
-        for (int k = 0; k < EMAX; ++k) {
-          const int i = lane + 64 * k;
-          float acc = -INFINITY;
-          if (i < ne) {
-            acc = 0.f;
-            if (i < npast) {
-              const WT* kr = rK + (static_cast<size_t>(h) * Wm1 + slot_of(i)) * DH;
+        for (int c = 0; c < 16; ++c) o[c] = 0.f;
+        for (int i0 = 0; i0 < ne; i0 += SLOTS) {
+          const int i = i0 + slot;
+          const bool ok = i < ne;
+          Chunk k0, k1, v0, v1;
+          if (i < npast) {
+            int sl = slot0 + i;
+            sl = sl >= Wm1 ? sl - Wm1 : sl;
+            const WT* kr = rK + (static_cast<size_t>(h) * Wm1 + sl) * DH + sub * 16;
+            const WT* vr = rV + (static_cast<size_t>(h) * Wm1 + sl) * DH + sub * 16;
+            k0 = O::load(kr); k1 = O::load(kr + 8); v0 = O::load(vr); v1 = O::load(vr + 8);
+          } else {
+            // the current entry (values already rounded to the storage precision)
+            float kf[8], vf[8];
+            const float* kq = qkv + D + h * DH + sub * 16;
 #pragma unroll
-              for (int c8 = 0; c8 < DH; c8 += 8) {
-                float kf[8];
-                O::unpack(O::lds(kr + c8), kf);
-                const float4 q0 = *reinterpret_cast<const float4*>(q + c8);
-                const float4 q1 = *reinterpret_cast<const float4*>(q + c8 + 4);
-                acc += q0.x * kf[0] + q0.y * kf[1] + q0.z * kf[2] + q0.w * kf[3] + q1.x * kf[4] + q1.y * kf[5] +
-                       q1.z * kf[6] + q1.w * kf[7];
-              }
-            } else {
-              const float* kr = qkv + D + h * DH;
+            for (int c = 0; c < 8; ++c) { kf[c] = kq[c]; vf[c] = kq[D + c]; }
+            k0 = O::pack(kf); v0 = O::pack(vf);
 #pragma unroll
-              for (int c = 0; c < DH; ++c) acc += q[c] * kr[c];
-            }
-            acc *= scale;
+            for (int c = 0; c < 8; ++c) { kf[c] = kq[8 + c]; vf[c] = kq[D + 8 + c]; }
+            k1 = O::pack(kf); v1 = O::pack(vf);
           }
-          sc[k] = acc;
-          mx = fmaxf(mx, acc);
+          float s = qs.dot(k0, k1);
+          if constexpr (LPK > 1) s = group_sum<LPK>(s);
+          s = ok ? s : -INFINITY;
+          const float mnew = fmaxf(m, s);
+          const float corr = m == mnew ? 1.f : __expf(m - mnew);   // m = mnew = -inf: nothing seen yet
+          const float w = ok ? __expf(s - mnew) : 0.f;
+          lsum = lsum * corr + w;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) o[c] *= corr;
+          axpy16<WT>(o, w, v0, v1);
+          m = mnew;
         }
-        mx = group_max<64>(mx);
-        float den = 0.f;
-        float* ph = swa_p + h * (EMAX * 64);
-#pragma unroll
-        for (int k = 0; k < EMAX; ++k) {
-          const int i = lane + 64 * k;
-          const float w = i < ne ? __expf(sc[k] - mx) : 0.f;
-          den += w;
-          if (i < ne) ph[i] = w;
-        }
-        den = group_sum<64>(den);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if constexpr (DH >= 64) {
-          // lane owns dims lane, lane+64, ...; all entries
-#pragma unroll
-          for (int c = lane; c < DH; c += 64) {
-            float o = 0.f;
-            for (int i = 0; i < ne; ++i) {
-              float v;
-              if (i < npast) {
-                v = load_as_f32(rV + (static_cast<size_t>(h) * Wm1 + slot_of(i)) * DH + c);
-              } else {
-                v = qkv[2 * D + h * DH + c];
-              }
-              o += ph[i] * v;
-            }
-            store_from_f32(&xop[h * DH + c], o / den);
-          }
-        } else {
-          // lane (c, g): dim c, entries i = g, g + 64/DH, ...; then a sum over the groups
-          constexpr int GS = 64 / DH;
-          constexpr int UN = 8;   // entries per lane issued together
-          const int c = lane % DH, g0 = lane / DH;
-          float o = 0.f;
-          for (int i0 = g0; i0 < ne; i0 += GS * UN) {
-            float pv[UN], vv[UN];
-#pragma unroll
-            for (int u = 0; u < UN; ++u) {
-              const int i = min(i0 + GS * u, ne - 1);
-              pv[u] = i0 + GS * u < ne ? ph[i] : 0.f;
-              vv[u] = i < npast ? load_as_f32(rV + (static_cast<size_t>(h) * Wm1 + slot_of(i)) * DH + c)
-                                : qkv[2 * D + h * DH + c];
-            }
-#pragma unroll
-            for (int u = 0; u < UN; ++u) o += pv[u] * vv[u];
-          }
-#pragma unroll
-          for (int off = DH; off < 64; off <<= 1) o += __shfl_xor(o, off, 64);
-          if (g0 == 0) store_from_f32(&xop[h * DH + c], o / den);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // the current entry replaces the oldest one (position t - (W-1)) after the reads above
+        wave_combine<WT, DH>(m, lsum, o, my_scr, xop + h * DH);
+        // the current entry replaces the oldest one (position t - (W-1))
         if (Wm1 > 0) {
-          const int slot = t % Wm1;
+          const int sl = t % Wm1;
           const size_t gbase = (static_cast<size_t>(l) * p.B + b) * H * Wm1 * DH;
           for (int c = lane; c < DH; c += 64) {
-            const size_t o_ = (static_cast<size_t>(h) * Wm1 + slot) * DH + c;
+            const size_t o_ = (static_cast<size_t>(h) * Wm1 + sl) * DH + c;
             WT kq, vq;
             store_from_f32(&kq, qkv[D + h * DH + c]);
             store_from_f32(&vq, qkv[2 * D + h * DH + c]);
@@ -479,126 +503,118 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       }
       __syncthreads();
 
-      // ---- P3: y += W_O attn; first memory batch of this layer issued here ----
+      // ---- P3: y += W_O attn; the first key batch of this layer's memory is issued here ----
       const int grp_l = G == 1 ? 0 : l;
-      // memory rows of (group, sequence): uniform base + 32-bit per-lane byte offsets
       const size_t mrow0 = (static_cast<size_t>(grp_l) * p.B + b) * H * static_cast<size_t>(T) * DH * sizeof(WT);
       const char* mkb = static_cast<const char*>(p.mem_k) + mrow0;
       const char* mvb = static_cast<const char*>(p.mem_v) + mrow0;
-      const uint32_t lane_off = static_cast<uint32_t>((xh * T * DH + xsub * 8) * sizeof(WT));
-      constexpr int STRIDE = PARTS * KB;     // key distance between a lane's consecutive batches
-      auto issue = [&](Chunk (&kx)[KB], Chunk (&vx)[KB], int jb) {
+      // lane byte offset of key row j of head hh: ((hh*T + j)*DH + 16*sub) * sizeof(WT)
+      auto row_off = [&](int hh, int j) {
+        return static_cast<uint32_t>(((hh * T + j) * DH + sub * 16) * sizeof(WT));
+      };
+      // rows j = base + SLOTS*i (i < KQ), clamped to t (clamped rows are masked out later)
+      auto load_rows = [&](const char* mb, int hh, int base, Chunk (&x)[KQ][2]) {
 #pragma unroll
-        for (int i = 0; i < KB; ++i) {
-          const int j = jb + PARTS * i;
-          const uint32_t off = lane_off + static_cast<uint32_t>(j * DH * sizeof(WT));
-          kx[i] = j <= t ? O::load(reinterpret_cast<const WT*>(mkb + off)) : O::zero();
-          vx[i] = j <= t ? O::load(reinterpret_cast<const WT*>(mvb + off)) : O::zero();
+        for (int i = 0; i < KQ; ++i) {
+          const uint32_t off = row_off(hh, min(base + SLOTS * i, t));
+          x[i][0] = O::load(reinterpret_cast<const WT*>(mb + off));
+          x[i][1] = O::load(reinterpret_cast<const WT*>(mb + off) + 8);
         }
       };
-      Chunk kA[KB], vA[KB], kB_[KB], vB_[KB];
-      issue(kA, vA, xpart);
+      Chunk kq0[KQ][2];
+      const int h0 = wave < H ? wave : 0;
+      load_rows(mkb, h0, slot, kq0);
       wcompute(wb, layer_w(l, p.l_wo), D, D, xf_op(xop), [&](int r, float v) { y[r] += v; });
       wprefetch(wb, layer_w(l, p.l_wox), D, D);
       __syncthreads();
 
-      // ---- P4: q_x = W_Qx RMS(y; g_cross) (pre-scaled by 1/sqrt(d_h)) ----
-      issue(kB_, vB_, xpart + STRIDE);
+      // ---- P4: q_x = W_Qx RMS(y; g_cross) (pre-scaled by 1/sqrt(d_h)); first value batch ----
+      Chunk vq0[KQ][2];
+      load_rows(mvb, h0, slot, vq0);
       {
         const float inv = wave_rms_inv<D>(y, p.eps);
-        auto xf = [&](int k) {
-          float f[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = g_cross[k + i] * (y[k + i] * inv);
-          return O::pack(f);
-        };
-        wcompute(wa, layer_w(l, p.l_wqx), D, D, xf, [&](int r, float v) { qkv[r] = v * scale; });
+        wcompute(wa, layer_w(l, p.l_wqx), D, D, [&](int k) { return norm_chunk<WT>(y, g_cross, inv, k); },
+                 [&](int r, float v) { qkv[r] = v * scale; });
         wprefetch(wa, layer_w(l, p.l_fin), F2, D);
       }
       __syncthreads();
 
-      // ---- P5: cross-attention over memory rows 0..t, online softmax per lane ----
-      {
-        float q8[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) q8[c] = qkv[xh * DH + xsub * 8 + c];
-        const typename O::QPack qp = O::qpack(q8);
+      // ---- P5: cross-attention over memory rows 0..t, one head per wave ----
+      // Keys are taken in chunks of NSC*SLOTS rows.  Per chunk: pass 1 computes every score of
+      // the lane into registers (K rows in batches of KQ, the next batch in flight while the
+      // current one is used); pass 2 streams the V rows and accumulates exp(s - m) v.  The
+      // running (m, l, o) is rescaled once per chunk.
+      for (int h = wave; h < H; h += NWAVE) {
+        QSlice<WT> qs;
+        qs.set(qkv + h * DH + sub * 16);
         float m = -INFINITY, lsum = 0.f;
-        float o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        auto process = [&](const Chunk (&kx)[KB], const Chunk (&vx)[KB], int jb) {
-          float s[KB];
-          float bm = -INFINITY;
+        float o[16];
 #pragma unroll
-          for (int i = 0; i < KB; ++i) {
-            float a = O::qdot(kx[i], qp);
-            if constexpr (LPK > 1) a = group_sum<LPK>(a);
-            s[i] = (jb + PARTS * i <= t) ? a : -INFINITY;
-            bm = fmaxf(bm, s[i]);
+        for (int c = 0; c < 16; ++c) o[c] = 0.f;
+        const bool first_head = h == wave;
+        for (int c0 = 0; c0 <= t; c0 += NSC * SLOTS) {
+          const int cb = c0 + slot;                 // this lane's first row in the chunk
+          float sc[NSC];
+          float cmax = -INFINITY;
+          Chunk kx[KQ][2];
+          if (first_head && c0 == 0) {
+#pragma unroll
+            for (int i = 0; i < KQ; ++i) { kx[i][0] = kq0[i][0]; kx[i][1] = kq0[i][1]; }
+          } else {
+            load_rows(mkb, h, cb, kx);
           }
-          const float mnew = fmaxf(m, bm);
-          const float corr = __expf(m - mnew);
+#pragma unroll
+          for (int q0 = 0; q0 < NSC; q0 += KQ) {
+            if (c0 + SLOTS * q0 > t) break;         // uniform: no row of this batch exists
+            Chunk kn[KQ][2];
+            const bool more = q0 + KQ < NSC && c0 + SLOTS * (q0 + KQ) <= t;
+            if (more) load_rows(mkb, h, cb + SLOTS * (q0 + KQ), kn);
+#pragma unroll
+            for (int i = 0; i < KQ; ++i) {
+              float a = qs.dot(kx[i][0], kx[i][1]);
+              if constexpr (LPK > 1) a = group_sum<LPK>(a);
+              a = cb + SLOTS * (q0 + i) <= t ? a : -INFINITY;
+              sc[q0 + i] = a;
+              cmax = fmaxf(cmax, a);
+            }
+            if (more) {
+#pragma unroll
+              for (int i = 0; i < KQ; ++i) { kx[i][0] = kn[i][0]; kx[i][1] = kn[i][1]; }
+            }
+          }
+          const float mnew = fmaxf(m, cmax);
+          const float corr = m == mnew ? 1.f : __expf(m - mnew);
           lsum *= corr;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) o8[c] *= corr;
-#pragma unroll
-          for (int i = 0; i < KB; ++i) {
-            const float w = __expf(s[i] - mnew);
-            float vv[8];
-            O::unpack(vx[i], vv);
-            lsum += w;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) o8[c] += w * vv[c];
-          }
+          for (int c = 0; c < 16; ++c) o[c] *= corr;
           m = mnew;
-        };
-        // two rotating buffers: batches 0 and 1 were requested two phases earlier; batch
-        // i+2 is requested while batch i is processed
-        for (int jb = xpart; jb <= t;) {
-          process(kA, vA, jb);
-          issue(kA, vA, jb + 2 * STRIDE);
-          jb += STRIDE;
-          if (jb > t) break;
-          process(kB_, vB_, jb);
-          issue(kB_, vB_, jb + 2 * STRIDE);
-          jb += STRIDE;
-        }
-        float* po = part_o + (static_cast<size_t>(xh) * PARTS + xpart) * DH + xsub * 8;
+          const float mref = m == -INFINITY ? 0.f : m;   // lane without rows: every exp(-inf - 0) = 0
+          Chunk vx[KQ][2];
+          if (first_head && c0 == 0) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) po[c] = o8[c];
-        if (xsub == 0) {
-          part_m[xh * PARTS + xpart] = m;
-          part_l[xh * PARTS + xpart] = lsum;
-        }
-      }
-      __syncthreads();
-
-      // ---- P6: combine the PARTS partial softmax states of every (head, dim), fixed order ----
-      for (int idx = tid; idx < D * 8; idx += NT) {
-        const int k = idx & 7, hc = idx >> 3;
-        const int h = hc / DH, c = hc % DH;
-        constexpr int QN = PARTS / 8;
-        float pm[QN], pl[QN], pov[QN];
+            for (int i = 0; i < KQ; ++i) { vx[i][0] = vq0[i][0]; vx[i][1] = vq0[i][1]; }
+          } else {
+            load_rows(mvb, h, cb, vx);
+          }
 #pragma unroll
-        for (int qq = 0; qq < QN; ++qq) {
-          const int q = k + 8 * qq;
-          pm[qq] = part_m[h * PARTS + q];
-          pl[qq] = part_l[h * PARTS + q];
-          pov[qq] = part_o[(static_cast<size_t>(h) * PARTS + q) * DH + c];
-        }
-        float mloc = pm[0];
+          for (int q0 = 0; q0 < NSC; q0 += KQ) {
+            if (c0 + SLOTS * q0 > t) break;
+            Chunk vn[KQ][2];
+            const bool more = q0 + KQ < NSC && c0 + SLOTS * (q0 + KQ) <= t;
+            if (more) load_rows(mvb, h, cb + SLOTS * (q0 + KQ), vn);
 #pragma unroll
-        for (int qq = 1; qq < QN; ++qq) mloc = fmaxf(mloc, pm[qq]);
-        const float mh = group_max<8>(mloc);
-        float o = 0.f, l_ = 0.f;
+            for (int i = 0; i < KQ; ++i) {
+              const float w = __expf(sc[q0 + i] - mref);   // masked rows: exp(-inf) = 0
+              lsum += w;
+              axpy16<WT>(o, w, vx[i][0], vx[i][1]);
+            }
+            if (more) {
 #pragma unroll
-        for (int qq = 0; qq < QN; ++qq) {
-          const float w = __expf(pm[qq] - mh);
-          o += w * pov[qq];
-          l_ += w * pl[qq];
+              for (int i = 0; i < KQ; ++i) { vx[i][0] = vn[i][0]; vx[i][1] = vn[i][1]; }
+            }
+          }
         }
-        o = group_sum<8>(o);
-        l_ = group_sum<8>(l_);
-        if (k == 0) store_from_f32(&xop[hc], o / l_);
+        wave_combine<WT, DH>(m, lsum, o, my_scr, xop + h * DH);
       }
       __syncthreads();
 
@@ -611,12 +627,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       const bool last = l + 1 == L;
       {
         const float inv = wave_rms_inv<D>(y, p.eps);
-        auto xf = [&](int k) {
-          float f[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) f[i] = g_ffn[k + i] * (y[k + i] * inv);
-          return O::pack(f);
-        };
+        auto xf = [&](int k) { return norm_chunk<WT>(y, g_ffn, inv, k); };
         if (p.ffn_kind == RLT_FFN_GELU) {
           wcompute(wa, layer_w(l, p.l_fin), F, D, xf,
                    [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); });
@@ -660,10 +671,8 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
 size_t lds_bytes(const ModelLayout& m) {
   const size_t H = m.H, DH = m.DH, D = m.D, L = m.L;
   const size_t ring = 2 * L * H * (m.W - 1) * DH * m.esz;
-  const size_t parts = NT / (H * (DH / 8));
   const size_t xopn = 2 * D > static_cast<size_t>(m.F) ? 2 * D : m.F;
-  const size_t floats = D + D + 3 * D + D + D + (3 * L + 1) * D + D + H * parts + H * parts + H * parts * DH +
-                        H * EMAX * 64 + m.F2;
+  const size_t floats = D + D + 3 * D + D + D + (3 * L + 1) * D + D + NWAVE * (64 * 17 + 64) + m.F2;
   return (ring + 15) / 16 * 16 + (xopn * m.esz + 15) / 16 * 16 + floats * 4;
 }
 
@@ -705,7 +714,9 @@ bool dec_small_supported(const ModelLayout& m, int T) {
   const bool shape = (m.D == 64 && (m.DH == 16 || m.DH == 32 || m.DH == 64)) ||
                      (m.D == 128 && (m.DH == 16 || m.DH == 32 || m.DH == 64 || m.DH == 128));
   const int entries = std::min(m.W, T);   // window entries ever held at once
-  return shape && entries <= EMAX * 64 && m.F2 <= 4096 && lds_bytes(m) <= kMaxLds;
+  // 32-bit memory-row offsets within one (group, sequence)
+  const bool offsets = static_cast<size_t>(T) * m.D * m.esz < (size_t(1) << 31);
+  return shape && entries <= WCAP && offsets && m.F2 <= 4096 && lds_bytes(m) <= kMaxLds;
 }
 
 size_t dec_small_lds_bytes(const ModelLayout& m, int T) {
