@@ -104,14 +104,13 @@ template <> struct Ops<float> {
 template <typename WT> struct QSlice;
 template <> struct QSlice<bf16_t> {
   uint32_t hi[8], lo[8];   // q = hi + lo, both bf16 pairs (~16 significant bits)
-  __device__ __forceinline__ void set(const float* q) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float a = q[2 * i], b = q[2 * i + 1];
-      const uint32_t h = pack_bf16x2(a, b);
-      hi[i] = h;
-      lo[i] = pack_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
-    }
+  // qf: fp32 query (unused); qh / ql: bf16 hi and lo halves, 16 elements each
+  __device__ __forceinline__ void set(const float* qf, const bf16_t* qh, const bf16_t* ql) {
+    (void)qf;
+    const uint4 h0 = *reinterpret_cast<const uint4*>(qh), h1 = *reinterpret_cast<const uint4*>(qh + 8);
+    const uint4 l0 = *reinterpret_cast<const uint4*>(ql), l1 = *reinterpret_cast<const uint4*>(ql + 8);
+    hi[0] = h0.x; hi[1] = h0.y; hi[2] = h0.z; hi[3] = h0.w; hi[4] = h1.x; hi[5] = h1.y; hi[6] = h1.z; hi[7] = h1.w;
+    lo[0] = l0.x; lo[1] = l0.y; lo[2] = l0.z; lo[3] = l0.w; lo[4] = l1.x; lo[5] = l1.y; lo[6] = l1.z; lo[7] = l1.w;
   }
   __device__ __forceinline__ float dot(const Ops<bf16_t>::Chunk& k0, const Ops<bf16_t>::Chunk& k1) const {
     const uint32_t kv[8] = {k0.v.x, k0.v.y, k0.v.z, k0.v.w, k1.v.x, k1.v.y, k1.v.z, k1.v.w};
@@ -125,7 +124,9 @@ template <> struct QSlice<bf16_t> {
 };
 template <> struct QSlice<float> {
   float q[16];
-  __device__ __forceinline__ void set(const float* src) {
+  __device__ __forceinline__ void set(const float* src, const float* qh, const float* ql) {
+    (void)qh;
+    (void)ql;
 #pragma unroll
     for (int i = 0; i < 16; ++i) q[i] = src[i];
   }
@@ -180,6 +181,9 @@ __device__ __forceinline__ void wcompute_c(const WBuf<WT>& buf, const WT* __rest
 #pragma unroll
   for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf(sub * 8 + ci * 64);
   const int nrows = (N + NG - 1) / NG;
+  // every lane of the 8-lane group gets every row total; lane `sub` then runs the epilogue
+  // of row `sub`, so each epilogue is executed once per row, not once per group lane
+  float mine = 0.f;
 #pragma unroll
   for (int ri = 0; ri < RB; ++ri) {
     if (ri < nrows) {
@@ -187,9 +191,12 @@ __device__ __forceinline__ void wcompute_c(const WBuf<WT>& buf, const WT* __rest
 #pragma unroll
       for (int ci = 0; ci < CPL; ++ci) acc = O::dot(buf.c[ri * CPL + ci], xr[ci], acc);
       acc = group_sum<8>(acc);
-      const int r = grp + ri * NG;
-      if (sub == 0 && r < N) epi(r, acc);
+      mine = sub == ri ? acc : mine;
     }
+  }
+  {
+    const int r = grp + sub * NG;
+    if (sub < RB && sub < nrows && r < N) epi(r, mine);
   }
   for (int ri = RB; ri < nrows; ++ri) {
     const int r = grp + ri * NG;
@@ -363,6 +370,8 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   float* bgl = gains + (3 * L + 1) * D;                 // [D]
   float* wscr = bgl + D;                                // [NWAVE][64*17 + 64] wave scratch
   float* act_raw = wscr + NWAVE * (64 * 17 + 64);       // [F2] (SwiGLU gate/up pre-activations)
+  WT* q_hi = reinterpret_cast<WT*>(act_raw + F2);       // [D] query, storage-precision high part
+  WT* q_lo = q_hi + D;                                  // [D] low part (bf16 mode only)
   float* my_scr = wscr + wave * (64 * 17 + 64);
 
   // ---- carried state, gains ----
@@ -405,6 +414,12 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   __syncthreads();
 
   auto xf_op = [&](const WT* v) { return [=](int k) { return O::load(v + k); }; };
+  // query element r (pre-scaled): fp32 copy and, in bf16 mode, its hi/lo split
+  auto put_q = [&](int r, float v) {
+    qkv[r] = v;
+    store_from_f32(&q_hi[r], v);
+    store_from_f32(&q_lo[r], v - round_to<WT>(v));
+  };
 
   for (int step = 0; step < p.n; ++step) {
     const int t = p.t0 + step;   // 0-based position of this transition
@@ -435,7 +450,10 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       {
         const float inv = wave_rms_inv<D>(y, p.eps);
         wcompute(wa, layer_w(l, p.l_qkv), 3 * D, D, [&](int k) { return norm_chunk<WT>(y, g_self, inv, k); },
-                 [&](int r, float v) { qkv[r] = r < D ? v * scale : round_to<WT>(v); });
+                 [&](int r, float v) {
+                   if (r < D) put_q(r, v * scale);
+                   else qkv[r] = round_to<WT>(v);
+                 });
         wprefetch(wa, layer_w(l, p.l_wqx), D, D);
       }
       __syncthreads();
@@ -446,7 +464,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       const int slot0 = Wm1 > 0 ? (t - npast) % Wm1 : 0;   // ring slot of the oldest entry
       for (int h = wave; h < H; h += NWAVE) {
         QSlice<WT> qs;
-        qs.set(qkv + h * DH + sub * 16);
+        qs.set(qkv + h * DH + sub * 16, q_hi + h * DH + sub * 16, q_lo + h * DH + sub * 16);
         float m = -INFINITY, lsum = 0.f;
         float o[16];
 #pragma unroll
@@ -534,7 +552,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       {
         const float inv = wave_rms_inv<D>(y, p.eps);
         wcompute(wa, layer_w(l, p.l_wqx), D, D, [&](int k) { return norm_chunk<WT>(y, g_cross, inv, k); },
-                 [&](int r, float v) { qkv[r] = v * scale; });
+                 [&](int r, float v) { put_q(r, v * scale); });
         wprefetch(wa, layer_w(l, p.l_fin), F2, D);
       }
       __syncthreads();
@@ -546,7 +564,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       // running (m, l, o) is rescaled once per chunk.
       for (int h = wave; h < H; h += NWAVE) {
         QSlice<WT> qs;
-        qs.set(qkv + h * DH + sub * 16);
+        qs.set(qkv + h * DH + sub * 16, q_hi + h * DH + sub * 16, q_lo + h * DH + sub * 16);
         float m = -INFINITY, lsum = 0.f;
         float o[16];
 #pragma unroll
@@ -556,30 +574,27 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
           const int cb = c0 + slot;                 // this lane's first row in the chunk
           float sc[NSC];
           float cmax = -INFINITY;
-          Chunk kx[KQ][2];
+          // two load buffers used alternately by the unrolled batch sequence (no copies)
+          Chunk xa[KQ][2], xb[KQ][2];
           if (first_head && c0 == 0) {
 #pragma unroll
-            for (int i = 0; i < KQ; ++i) { kx[i][0] = kq0[i][0]; kx[i][1] = kq0[i][1]; }
+            for (int i = 0; i < KQ; ++i) { xa[i][0] = kq0[i][0]; xa[i][1] = kq0[i][1]; }
           } else {
-            load_rows(mkb, h, cb, kx);
+            load_rows(mkb, h, cb, xa);
           }
 #pragma unroll
           for (int q0 = 0; q0 < NSC; q0 += KQ) {
             if (c0 + SLOTS * q0 > t) break;         // uniform: no row of this batch exists
-            Chunk kn[KQ][2];
-            const bool more = q0 + KQ < NSC && c0 + SLOTS * (q0 + KQ) <= t;
-            if (more) load_rows(mkb, h, cb + SLOTS * (q0 + KQ), kn);
+            Chunk (&cur)[KQ][2] = ((q0 / KQ) & 1) ? xb : xa;
+            Chunk (&nxt)[KQ][2] = ((q0 / KQ) & 1) ? xa : xb;
+            if (q0 + KQ < NSC && c0 + SLOTS * (q0 + KQ) <= t) load_rows(mkb, h, cb + SLOTS * (q0 + KQ), nxt);
 #pragma unroll
             for (int i = 0; i < KQ; ++i) {
-              float a = qs.dot(kx[i][0], kx[i][1]);
+              float a = qs.dot(cur[i][0], cur[i][1]);
               if constexpr (LPK > 1) a = group_sum<LPK>(a);
               a = cb + SLOTS * (q0 + i) <= t ? a : -INFINITY;
               sc[q0 + i] = a;
               cmax = fmaxf(cmax, a);
-            }
-            if (more) {
-#pragma unroll
-              for (int i = 0; i < KQ; ++i) { kx[i][0] = kn[i][0]; kx[i][1] = kn[i][1]; }
             }
           }
           const float mnew = fmaxf(m, cmax);
@@ -589,28 +604,23 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
           for (int c = 0; c < 16; ++c) o[c] *= corr;
           m = mnew;
           const float mref = m == -INFINITY ? 0.f : m;   // lane without rows: every exp(-inf - 0) = 0
-          Chunk vx[KQ][2];
           if (first_head && c0 == 0) {
 #pragma unroll
-            for (int i = 0; i < KQ; ++i) { vx[i][0] = vq0[i][0]; vx[i][1] = vq0[i][1]; }
+            for (int i = 0; i < KQ; ++i) { xa[i][0] = vq0[i][0]; xa[i][1] = vq0[i][1]; }
           } else {
-            load_rows(mvb, h, cb, vx);
+            load_rows(mvb, h, cb, xa);
           }
 #pragma unroll
           for (int q0 = 0; q0 < NSC; q0 += KQ) {
             if (c0 + SLOTS * q0 > t) break;
-            Chunk vn[KQ][2];
-            const bool more = q0 + KQ < NSC && c0 + SLOTS * (q0 + KQ) <= t;
-            if (more) load_rows(mvb, h, cb + SLOTS * (q0 + KQ), vn);
+            Chunk (&cur)[KQ][2] = ((q0 / KQ) & 1) ? xb : xa;
+            Chunk (&nxt)[KQ][2] = ((q0 / KQ) & 1) ? xa : xb;
+            if (q0 + KQ < NSC && c0 + SLOTS * (q0 + KQ) <= t) load_rows(mvb, h, cb + SLOTS * (q0 + KQ), nxt);
 #pragma unroll
             for (int i = 0; i < KQ; ++i) {
               const float w = __expf(sc[q0 + i] - mref);   // masked rows: exp(-inf) = 0
               lsum += w;
-              axpy16<WT>(o, w, vx[i][0], vx[i][1]);
-            }
-            if (more) {
-#pragma unroll
-              for (int i = 0; i < KQ; ++i) { vx[i][0] = vn[i][0]; vx[i][1] = vn[i][1]; }
+              axpy16<WT>(o, w, cur[i][0], cur[i][1]);
             }
           }
         }
@@ -673,7 +683,7 @@ size_t lds_bytes(const ModelLayout& m) {
   const size_t ring = 2 * L * H * (m.W - 1) * DH * m.esz;
   const size_t xopn = 2 * D > static_cast<size_t>(m.F) ? 2 * D : m.F;
   const size_t floats = D + D + 3 * D + D + D + (3 * L + 1) * D + D + NWAVE * (64 * 17 + 64) + m.F2;
-  return (ring + 15) / 16 * 16 + (xopn * m.esz + 15) / 16 * 16 + floats * 4;
+  return (ring + 15) / 16 * 16 + (xopn * m.esz + 15) / 16 * 16 + floats * 4 + 2 * D * m.esz;
 }
 
 template <typename WT, int D, int DH>
