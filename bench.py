@@ -143,7 +143,7 @@ def main():
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     head_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
 
-    path = model.decoder_path(B)
+    path = model.decoder_path(T)
     dec_bytes = algorithmic_decoder_bytes(cfg, B, T)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
     line = {
@@ -165,10 +165,10 @@ def main():
                    "batch": B, "seq_len": T},
         "decoder_only_tokens_per_s": B * T / (dec_ms * 1e-3),
         "phase_ms": {"encoder": enc_ms, "decoder_replay": dec_ms, "logits": head_ms},
-        "decoder_path": ["persistent-per-sequence", "batched-phases"][path],
+        "decoder_path": {1: "persistent-per-sequence", 2: "batched-phases"}[path],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "dec_small_k" if path == 0 else "batched decoder phases",
+                     "kernel": "dec_small_k" if path == 1 else "batched decoder phases",
                      "algorithmic_bytes_per_launch": dec_bytes},
         "cpu_baseline": None,
     }

@@ -19,6 +19,7 @@ using namespace rlt;
 struct rlt_model {
   rlt_config cfg;
   ModelLayout lay;
+  int path;  // RLT_PATH_*
   uint64_t version;
   char* ws;
   size_t ws_bytes;
@@ -360,6 +361,7 @@ int rlt_model_create(const rlt_config* cfg, const float* weights, uint64_t versi
   if (!m) return fail(RLT_ERR_INVALID, "out of host memory");
   m->cfg = *cfg;
   m->lay = L;
+  m->path = RLT_PATH_AUTO;
   m->version = version;
   m->ws = static_cast<char*>(workspace);
   m->ws_bytes = workspace_bytes;
@@ -454,10 +456,31 @@ int rlt_state_device_error(rlt_state* state, void* stream, int32_t* flags) {
   return RLT_OK;
 }
 
-int rlt_decoder_path(const rlt_model* model, int32_t batch, int32_t* path) {
+int rlt_model_set_decoder_path(rlt_model* model, int32_t path) {
+  if (!model) return fail(RLT_ERR_INVALID, "model is NULL");
+  if (path != RLT_PATH_AUTO && path != RLT_PATH_PERSISTENT && path != RLT_PATH_BATCHED)
+    return fail(RLT_ERR_INVALID, "path must be RLT_PATH_AUTO, RLT_PATH_PERSISTENT or RLT_PATH_BATCHED");
+  if (path == RLT_PATH_PERSISTENT && !dec_small_supported(model->lay, 1))
+    return fail(RLT_ERR_UNSUPPORTED, "the persistent decoder does not support this model shape");
+  if (path == RLT_PATH_BATCHED && !dec_batched_supported(model->lay))
+    return fail(RLT_ERR_UNSUPPORTED, "the batched decoder does not support this model shape");
+  model->path = path;
+  return RLT_OK;
+}
+
+static int choose_path(const rlt_model* model, int t_max) {
+  if (model->path == RLT_PATH_BATCHED) return RLT_PATH_BATCHED;
+  if (dec_small_supported(model->lay, t_max)) return RLT_PATH_PERSISTENT;
+  if (model->path == RLT_PATH_PERSISTENT) return -1;
+  return dec_batched_supported(model->lay) ? RLT_PATH_BATCHED : -1;
+}
+
+int rlt_decoder_path(const rlt_model* model, int32_t t_max, int32_t* path) {
   if (!model || !path) return fail(RLT_ERR_INVALID, "model and path must be non-NULL");
-  (void)batch;
-  *path = dec_small_supported(model->lay, 1) ? 0 : 1;
+  if (t_max < 1) return fail(RLT_ERR_INVALID, "t_max must be >= 1");
+  const int p = choose_path(model, t_max);
+  if (p < 0) return fail(RLT_ERR_UNSUPPORTED, "no decoder implementation for this configuration");
+  *path = p;
   return RLT_OK;
 }
 
@@ -575,7 +598,8 @@ int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, floa
   const ModelLayout& M = model->lay;
   const StateLayout& S = state->lay;
   hipStream_t st = as_stream(stream);
-  if (dec_small_supported(M, S.T)) {
+  const int path = choose_path(model, S.T);
+  if (path == RLT_PATH_PERSISTENT) {
     DecSmallArgs a{};
     a.ws = model->ws;
     a.state = state->buf;
@@ -585,7 +609,7 @@ int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, floa
     a.t0 = state->t_dec;
     a.n = n;
     RLT_HIP(launch_dec_small(M, S, a, st), "decoder replay (persistent)");
-  } else if (dec_batched_supported(M)) {
+  } else if (path == RLT_PATH_BATCHED) {
     RLT_HIP(run_dec_batched(M, S, model->ws, state->buf, s_out, state->t_dec, n, st), "decoder replay (batched)");
   } else {
     return fail(RLT_ERR_UNSUPPORTED, "no decoder implementation for this configuration");

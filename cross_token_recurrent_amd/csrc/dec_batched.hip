@@ -1,23 +1,434 @@
-// Batched per-phase decoder for large d_model (not built yet: reports unsupported).
+// Batched recurrent decoder for large d_model: every step is a fixed sequence of
+// B-batched kernels enqueued on the caller's stream (no host synchronisation).
+//
+// Pages: [FI] feinterview "普林斯顿提出 RLT：跨 Token 携带解码器状态的循环 Transformer"
+// (decoder-state paragraph; model-hardware co-design principle: the transition is
+// sequential within a sequence while ready updates of independent sequences share one
+// batched kernel); [DS] deepsonar "技术拆解 009｜RLT…" §2.2, §2.4.
+//
+// At d_model >= 1024 one step streams the tied layer weights (hundreds of MB) and, late in
+// the sequence, every sequence's encoder memory (tens of GB), so each phase is a
+// device-wide kernel:
+//   merge:   gpre = [e_t; s] W_gate^T, f = s W_fb^T (MFMA GEMMs), y = g*e + (1-g)*f
+//   layer l: h = RMS(y) -> qkv = h W_{Q,K,V}^T -> window attention (one wave per
+//            (sequence, head), ring buffer in HBM) -> y += attn W_O^T
+//            h = RMS(y) -> q_x = h W_Qx^T -> cross-attention split over key chunks (one
+//            wave per (chunk, head, sequence), partial softmax states) -> fixed-order
+//            combine -> y += attn W_Ox^T
+//            h = RMS(y) -> FFN GEMMs (GELU or SwiGLU epilogue) -> y += act W_2^T
+//   final:   s_t = RMS(y; g_dec_final)
+// Decoder scratch layout (inside the state's decoder scratch region):
+//   y fp32 [B][D] | h [B][D] | xin [B][2D] | gpre fp32 [B][D] | fb fp32 [B][D] |
+//   qkv fp32 [B][3D] | attn [B][D] | act [B][F] | part fp32 [B][H][NSMAX][DH+2]
+#include <algorithm>
+
 #include "device_common.h"
 #include "rlt_internal.h"
 
 namespace rlt {
+namespace {
+
+constexpr int KCHUNK = 256;   // memory rows per cross-attention work item
+
+struct Scratch {
+  size_t y, h, xin, gpre, fb, qkv, attn, act, part, total;
+  int nsmax;
+};
+
+Scratch scratch_layout(const ModelLayout& m, int B, int T) {
+  Scratch s{};
+  const size_t D = m.D, Bz = B, e = m.esz;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  s.nsmax = (T + KCHUNK - 1) / KCHUNK;
+  s.y = take(Bz * D * 4);
+  s.h = take(Bz * D * e);
+  s.xin = take(Bz * 2 * D * e);
+  s.gpre = take(Bz * D * 4);
+  s.fb = take(Bz * D * 4);
+  s.qkv = take(Bz * 3 * D * 4);
+  s.attn = take(Bz * D * e);
+  s.act = take(Bz * static_cast<size_t>(m.F) * e);
+  s.part = take(Bz * m.H * static_cast<size_t>(s.nsmax) * (m.DH + 2) * 4);
+  s.total = off;
+  return s;
+}
+
+// xin[b] = [e_t[b] ; storage(s[b])]
+template <typename WT>
+__global__ void merge_prep_k(const WT* __restrict__ e, const float* __restrict__ s, WT* __restrict__ xin, int T,
+                             int D, int t) {
+  const int b = blockIdx.x;
+  const WT* er = e + (static_cast<size_t>(b) * T + t) * D;
+  WT* xr = xin + static_cast<size_t>(b) * 2 * D;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    xr[c] = er[c];
+    store_from_f32(&xr[D + c], s[static_cast<size_t>(b) * D + c]);
+  }
+}
+
+// y = g * e + (1 - g) * f with g = sigmoid(gpre + b_g)
+template <typename WT>
+__global__ void merge_combine_k(const float* __restrict__ gpre, const float* __restrict__ fb,
+                                const float* __restrict__ bg, const WT* __restrict__ xin, float* __restrict__ y,
+                                int D) {
+  const int b = blockIdx.x;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    const size_t i = static_cast<size_t>(b) * D + c;
+    const float g = sigmoid_f(gpre[i] + bg[c]);
+    y[i] = g * load_as_f32(xin + static_cast<size_t>(b) * 2 * D + c) + (1.0f - g) * fb[i];
+  }
+}
+
+// s = RMS(y; g) -> state s and s_out[b][step]; one wave per row
+__global__ void final_norm_k(const float* __restrict__ y, const float* __restrict__ gain, float* __restrict__ s,
+                             float* __restrict__ s_out, int B, int D, float eps, int step, int n) {
+  const int row = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  if (row >= B) return;
+  const float* yr = y + static_cast<size_t>(row) * D;
+  float ss = 0.f;
+  for (int c = lane; c < D; c += 64) ss += yr[c] * yr[c];
+  ss = group_sum<64>(ss);
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  for (int c = lane; c < D; c += 64) {
+    const float v = gain[c] * (yr[c] * inv);
+    s[static_cast<size_t>(row) * D + c] = v;
+    if (s_out) s_out[(static_cast<size_t>(row) * n + step) * D + c] = v;
+  }
+}
+
+template <typename WT> struct Row16;   // 16 stored elements of a key/value row as fp32
+template <> struct Row16<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float (&f)[16]) {
+    float a[8];
+    load8(p, a);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = a[i];
+    load8(p + 8, a);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[8 + i] = a[i];
+  }
+};
+template <> struct Row16<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&f)[16]) {
+    float a[8];
+    load8(p, a);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = a[i];
+    load8(p + 8, a);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[8 + i] = a[i];
+  }
+};
+
+// Per-lane online softmax state over 16 output dims.
+struct SoftState {
+  float m = -INFINITY, l = 0.f, o[16];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[c] = 0.f;
+  }
+  // score s (already masked to -inf when invalid), value row v
+  __device__ __forceinline__ void add(float s, const float (&v)[16]) {
+    const float mn = fmaxf(m, s);
+    if (mn == -INFINITY) return;   // nothing valid yet (uniform within a key group)
+    const float corr = m == mn ? 1.f : __expf(m - mn);
+    const float w = __expf(s - mn);
+    l = l * corr + w;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[c] = o[c] * corr + w * v[c];
+    m = mn;
+  }
+};
+
+// Combine the per-lane states of one wave (lanes = (slot, sub), sub = lane % LPK owns dims
+// 16*sub .. 16*sub+15) into (m, l, o[DH]) of the whole wave, written by lanes 0..DH-1 to
+// m_out / l_out / o_out (or finished as o / l into out when out != null).
+template <int DH>
+__device__ __forceinline__ void wave_finish(const SoftState& st, float* __restrict__ lds, float* __restrict__ m_out,
+                                            float* __restrict__ l_out, float* __restrict__ o_out,
+                                            float* __restrict__ out_f, int lane) {
+  constexpr int LPK = DH / 16;
+  constexpr int SLOTS = 64 / LPK;
+  const float mw = group_max<64>(st.m);
+  const float f = mw == -INFINITY ? 0.f : __expf(st.m - mw);
+  float* ob = lds;              // [64][17]
+  float* lb = lds + 64 * 17;    // [64]
+#pragma unroll
+  for (int c = 0; c < 16; ++c) ob[lane * 17 + c] = st.o[c] * f;
+  lb[lane] = st.l * f;
+  __syncthreads();
+  for (int d = lane; d < DH; d += 64) {
+    const int sub = d / 16, c = d % 16;
+    float acc = 0.f, lacc = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < SLOTS; ++s) {
+      acc += ob[(s * LPK + sub) * 17 + c];
+      lacc += lb[s * LPK];
+    }
+    if (out_f) {
+      out_f[d] = acc / lacc;
+    } else {
+      o_out[d] = acc;
+      if (d == 0) {
+        *m_out = mw;
+        *l_out = lacc;
+      }
+    }
+  }
+}
+
+// Window self-attention, one wave per (head, sequence).
+template <typename WT, int DH>
+__global__ __launch_bounds__(64) void swa_k(const float* __restrict__ qkv, WT* __restrict__ ring_k,
+                                            WT* __restrict__ ring_v, WT* __restrict__ attn, int B, int H, int Wm1,
+                                            int t, float scale) {
+  constexpr int LPK = DH / 16;
+  constexpr int SLOTS = 64 / LPK;
+  __shared__ float lds[64 * 17 + 64];
+  __shared__ float outf[DH];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int slot = lane / LPK, sub = lane % LPK;
+  const int D = H * DH;
+  const float* qr = qkv + static_cast<size_t>(b) * 3 * D + h * DH + sub * 16;
+  float q[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) q[c] = qr[c] * scale;
+  const int npast = min(t, Wm1);
+  const int ne = npast + 1;
+  const int slot0 = Wm1 > 0 ? (t - npast) % Wm1 : 0;
+  const size_t rbase = ((static_cast<size_t>(b) * H + h) * Wm1) * DH;   // ring is pre-offset to layer l
+  SoftState st;
+  st.init();
+  for (int i0 = 0; i0 < ne; i0 += SLOTS) {
+    const int i = i0 + slot;
+    float k[16], v[16];
+    if (i < npast) {
+      int sl = slot0 + i;
+      sl = sl >= Wm1 ? sl - Wm1 : sl;
+      Row16<WT>::load(ring_k + rbase + static_cast<size_t>(sl) * DH + sub * 16, k);
+      Row16<WT>::load(ring_v + rbase + static_cast<size_t>(sl) * DH + sub * 16, v);
+    } else {
+      const float* kr = qkv + static_cast<size_t>(b) * 3 * D + D + h * DH + sub * 16;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        k[c] = round_to<WT>(kr[c]);
+        v[c] = round_to<WT>(kr[D + c]);
+      }
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) a += q[c] * k[c];
+    a = group_sum<LPK>(a);
+    st.add(i < ne ? a : -INFINITY, v);
+  }
+  wave_finish<DH>(st, lds, nullptr, nullptr, nullptr, outf, lane);
+  __syncthreads();
+  for (int d = lane; d < DH; d += 64) store_from_f32(&attn[static_cast<size_t>(b) * D + h * DH + d], outf[d]);
+  // the current entry replaces the oldest one (position t - (W-1)); all reads are done
+  if (Wm1 > 0) {
+    const int sl = t % Wm1;
+    const float* kr = qkv + static_cast<size_t>(b) * 3 * D + D + h * DH;
+    for (int d = lane; d < DH; d += 64) {
+      store_from_f32(&ring_k[rbase + static_cast<size_t>(sl) * DH + d], kr[d]);
+      store_from_f32(&ring_v[rbase + static_cast<size_t>(sl) * DH + d], kr[D + d]);
+    }
+  }
+}
+
+// Cross-attention partial states: one wave per (key chunk, head, sequence).
+template <typename WT, int DH>
+__global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx, const WT* __restrict__ mem_k,
+                                                   const WT* __restrict__ mem_v, float* __restrict__ part, int B,
+                                                   int H, int T, int t, int nsmax, float scale) {
+  constexpr int LPK = DH / 16;
+  constexpr int SLOTS = 64 / LPK;
+  __shared__ float lds[64 * 17 + 64];
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int slot = lane / LPK, sub = lane % LPK;
+  const int D = H * DH;
+  const float* qr = qx + static_cast<size_t>(b) * D + h * DH + sub * 16;
+  float q[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) q[c] = qr[c] * scale;
+  const size_t hb = (static_cast<size_t>(b) * H + h) * static_cast<size_t>(T) * DH;   // memory pre-offset to group
+  const int j0 = split * KCHUNK, j1 = min(j0 + KCHUNK, t + 1);
+  SoftState st;
+  st.init();
+  int j = j0 + slot;
+  float kc[16], vc[16];
+  {
+    const int jj = min(j, j1 - 1);
+    Row16<WT>::load(mem_k + hb + static_cast<size_t>(jj) * DH + sub * 16, kc);
+    Row16<WT>::load(mem_v + hb + static_cast<size_t>(jj) * DH + sub * 16, vc);
+  }
+  for (; j0 + (j - j0) - slot < j1; j += SLOTS) {
+    // next row in flight while this one is used
+    float kn[16], vn[16];
+    const int jn = min(j + SLOTS, j1 - 1);
+    Row16<WT>::load(mem_k + hb + static_cast<size_t>(jn) * DH + sub * 16, kn);
+    Row16<WT>::load(mem_v + hb + static_cast<size_t>(jn) * DH + sub * 16, vn);
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) a += q[c] * kc[c];
+    a = group_sum<LPK>(a);
+    st.add(j < j1 ? a : -INFINITY, vc);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      kc[c] = kn[c];
+      vc[c] = vn[c];
+    }
+  }
+  float* pr = part + ((static_cast<size_t>(b) * H + h) * nsmax + split) * (DH + 2);
+  wave_finish<DH>(st, lds, pr, pr + 1, pr + 2, nullptr, lane);
+}
+
+// attn[b, h*DH + d] = sum_s e^{m_s - M} o_s[d] / sum_s e^{m_s - M} l_s, splits in order.
+template <typename WT>
+__global__ void cross_combine_k(const float* __restrict__ part, WT* __restrict__ attn, int H, int DH, int ns,
+                                int nsmax) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const float* pr = part + (static_cast<size_t>(b) * H + h) * nsmax * (DH + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pr[s * (DH + 2)]);
+  for (int d = threadIdx.x; d < DH; d += blockDim.x) {
+    float o = 0.f, l = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float w = __expf(pr[s * (DH + 2)] - M);
+      l += w * pr[s * (DH + 2) + 1];
+      o += w * pr[s * (DH + 2) + 2 + d];
+    }
+    store_from_f32(&attn[static_cast<size_t>(b) * H * DH + h * DH + d], o / l);
+  }
+}
+
+template <typename WT, int DH>
+hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratch& sc, char* base, char* state,
+                                   const StateLayout& S, int l, int t, hipStream_t st) {
+  const int B = S.B, H = m.H;
+  const float scale = 1.0f / sqrtf(static_cast<float>(DH));
+  if (self) {
+    const size_t lay = static_cast<size_t>(l) * B * H * S.Wm1 * DH;
+    swa_k<WT, DH><<<dim3(H, B), 64, 0, st>>>(reinterpret_cast<const float*>(base + sc.qkv),
+                                             reinterpret_cast<WT*>(state + S.ring_k) + lay,
+                                             reinterpret_cast<WT*>(state + S.ring_v) + lay,
+                                             reinterpret_cast<WT*>(base + sc.attn), B, H, S.Wm1, t, scale);
+  } else {
+    const int g = m.G == 1 ? 0 : l;
+    const size_t goff = static_cast<size_t>(g) * B * S.T * m.D;
+    const int ns = (t + 1 + KCHUNK - 1) / KCHUNK;
+    cross_part_k<WT, DH><<<dim3(ns, H, B), 64, 0, st>>>(
+        reinterpret_cast<const float*>(base + sc.qkv), reinterpret_cast<const WT*>(state + S.mem_k) + goff,
+        reinterpret_cast<const WT*>(state + S.mem_v) + goff, reinterpret_cast<float*>(base + sc.part), B, H, S.T, t,
+        sc.nsmax, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    cross_combine_k<WT><<<dim3(H, B), std::min(DH, 128), 0, st>>>(reinterpret_cast<const float*>(base + sc.part),
+                                                                  reinterpret_cast<WT*>(base + sc.attn), H, DH, ns,
+                                                                  sc.nsmax);
+  }
+  return hipGetLastError();
+}
+
+template <typename WT>
+hipError_t attention(bool self, const ModelLayout& m, const Scratch& sc, char* base, char* state, const StateLayout& S,
+                     int l, int t, hipStream_t st) {
+  switch (m.DH) {
+    case 16: return step_attention_launches<WT, 16>(self, m, sc, base, state, S, l, t, st);
+    case 32: return step_attention_launches<WT, 32>(self, m, sc, base, state, S, l, t, st);
+    case 64: return step_attention_launches<WT, 64>(self, m, sc, base, state, S, l, t, st);
+    case 128: return step_attention_launches<WT, 128>(self, m, sc, base, state, S, l, t, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename WT>
+hipError_t run_t(const ModelLayout& m, const StateLayout& S, const char* ws, char* state, float* s_out, int t0, int n,
+                 hipStream_t st) {
+  const Scratch sc = scratch_layout(m, S.B, S.T);
+  char* base = state + S.dec_scratch;
+  const int B = S.B, D = m.D, dt = m.dtype;
+  float* y = reinterpret_cast<float*>(base + sc.y);
+  float* s = reinterpret_cast<float*>(state + S.s);
+  const float* gains_self = reinterpret_cast<const float*>(ws + m.g_dec_self);
+  const float* gains_cross = reinterpret_cast<const float*>(ws + m.g_dec_cross);
+  const float* gains_ffn = reinterpret_cast<const float*>(ws + m.g_dec_ffn);
+  hipError_t e;
+#define RLT_CK(x)                        \
+  do {                                   \
+    e = (x);                             \
+    if (e != hipSuccess) return e;       \
+  } while (0)
+  auto gemm = [&](const void* A, int lda, const void* W, int N, int K, void* out, int ldo, int epi) {
+    GemmArgs g{};
+    g.A = A; g.W = W; g.out = out;
+    g.M = B; g.N = N; g.K = K; g.lda = lda; g.ldw = K; g.ldo = ldo; g.epi = epi;
+    return launch_gemm(g, dt, st);
+  };
+  const int nt = std::min(256, std::max(64, D / 4));
+  for (int step = 0; step < n; ++step) {
+    const int t = t0 + step;
+    // gated merge
+    merge_prep_k<WT><<<B, nt, 0, st>>>(reinterpret_cast<const WT*>(state + S.e), s,
+                                       reinterpret_cast<WT*>(base + sc.xin), S.T, D, t);
+    RLT_CK(hipGetLastError());
+    RLT_CK(gemm(base + sc.xin, 2 * D, ws + m.wgate, D, 2 * D, base + sc.gpre, D, EPI_STORE_F32));
+    RLT_CK(gemm(base + sc.xin + static_cast<size_t>(D) * m.esz, 2 * D, ws + m.wfb, D, D, base + sc.fb, D,
+                EPI_STORE_F32));
+    merge_combine_k<WT><<<B, nt, 0, st>>>(reinterpret_cast<const float*>(base + sc.gpre),
+                                          reinterpret_cast<const float*>(base + sc.fb),
+                                          reinterpret_cast<const float*>(ws + m.bg),
+                                          reinterpret_cast<const WT*>(base + sc.xin), y, D);
+    RLT_CK(hipGetLastError());
+    for (int l = 0; l < m.L; ++l) {
+      const char* lw = ws + m.layers + l * m.layer_stride;
+      // window self-attention
+      RLT_CK(launch_rmsnorm_rows(y, gains_self + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr,
+                                 1, 0, 0, 1, st));
+      RLT_CK(gemm(base + sc.h, D, lw + m.l_qkv, 3 * D, D, base + sc.qkv, 3 * D, EPI_STORE_F32));
+      RLT_CK(attention<WT>(true, m, sc, base, state, S, l, t, st));
+      RLT_CK(gemm(base + sc.attn, D, lw + m.l_wo, D, D, y, D, EPI_RESID_F32));
+      // cross-attention to memory entries 0..t
+      RLT_CK(launch_rmsnorm_rows(y, gains_cross + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr,
+                                 1, 0, 0, 1, st));
+      RLT_CK(gemm(base + sc.h, D, lw + m.l_wqx, D, D, base + sc.qkv, D, EPI_STORE_F32));
+      RLT_CK(attention<WT>(false, m, sc, base, state, S, l, t, st));
+      RLT_CK(gemm(base + sc.attn, D, lw + m.l_wox, D, D, y, D, EPI_RESID_F32));
+      // FFN
+      RLT_CK(launch_rmsnorm_rows(y, gains_ffn + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr, 1,
+                                 0, 0, 1, st));
+      RLT_CK(gemm(base + sc.h, D, lw + m.l_fin, m.F2, D, base + sc.act, m.F,
+                  m.ffn_kind == RLT_FFN_GELU ? EPI_GELU : EPI_SWIGLU));
+      RLT_CK(gemm(base + sc.act, m.F, lw + m.l_fout, D, m.F, y, D, EPI_RESID_F32));
+    }
+    final_norm_k<<<(B + 3) / 4, 256, 0, st>>>(y, reinterpret_cast<const float*>(ws + m.g_dec_final), s, s_out, B, D,
+                                             m.eps, step, n);
+    RLT_CK(hipGetLastError());
+  }
+#undef RLT_CK
+  return hipSuccess;
+}
+
+}  // namespace
 
 bool dec_batched_supported(const ModelLayout& m) {
-  (void)m;
-  return false;
+  return (m.DH == 16 || m.DH == 32 || m.DH == 64 || m.DH == 128) && m.D % 64 == 0 && m.F % 64 == 0;
 }
 
-size_t dec_batched_scratch_bytes(const ModelLayout& m, int B, int T) {
-  (void)m; (void)B; (void)T;
-  return 0;
-}
+size_t dec_batched_scratch_bytes(const ModelLayout& m, int B, int T) { return scratch_layout(m, B, T).total; }
 
 hipError_t run_dec_batched(const ModelLayout& m, const StateLayout& s, const char* ws, char* state, float* s_out,
                            int t0, int n, hipStream_t st) {
-  (void)m; (void)s; (void)ws; (void)state; (void)s_out; (void)t0; (void)n; (void)st;
-  return hipErrorInvalidValue;
+  if (!dec_batched_supported(m)) return hipErrorInvalidValue;
+  return m.dtype == RLT_DTYPE_BF16 ? run_t<bf16_t>(m, s, ws, state, s_out, t0, n, st)
+                                   : run_t<float>(m, s, ws, state, s_out, t0, n, st);
 }
 
 }  // namespace rlt

@@ -69,6 +69,7 @@ _SIGS = {
     "rlt_state_load_encoder_outputs": [_P, _P, _P, _P, _P, _I32, _P],
     "rlt_state_read_encoder_outputs": [_P, _P, _I32, _I32, _P, _P, _P, _P],
     "rlt_decoder_path": [_P, _I32, ctypes.POINTER(_I32)],
+    "rlt_model_set_decoder_path": [_P, _I32],
     "rlt_last_error": [],
     "rlt_version_string": [],
 }
@@ -246,10 +247,15 @@ class Model:
         _check(load_library().rlt_model_get_config(self.handle, None, ctypes.byref(v)))
         return v.value
 
-    def decoder_path(self, batch: int) -> int:
+    def decoder_path(self, t_max: int) -> int:
+        """RLT_PATH_PERSISTENT (1) or RLT_PATH_BATCHED (2) for a state of t_max positions."""
         p = _I32()
-        _check(load_library().rlt_decoder_path(self.handle, batch, ctypes.byref(p)))
+        _check(load_library().rlt_decoder_path(self.handle, t_max, ctypes.byref(p)))
         return p.value
+
+    def set_decoder_path(self, path: int) -> None:
+        """0 = automatic, 1 = persistent per-sequence kernel, 2 = batched per-phase kernels."""
+        _check(load_library().rlt_model_set_decoder_path(self.handle, path))
 
     def __del__(self):
         if getattr(self, "handle", None) and _lib is not None:

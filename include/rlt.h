@@ -188,10 +188,19 @@ int rlt_state_read_encoder_outputs(const rlt_model* model, const rlt_state* stat
                                    int32_t n, float* e, float* mem_k, float* mem_v,
                                    void* stream);
 
-/* Which decoder implementation rlt_decoder_replay uses for this model and batch:
- * 0 = one persistent workgroup per sequence (small d_model), 1 = batched per-phase
- * kernels (large d_model). */
-int rlt_decoder_path(const rlt_model* model, int32_t batch, int32_t* path);
+/* Decoder implementations.  RLT_PATH_PERSISTENT: one persistent workgroup per sequence
+ * runs all n steps (d_model in {64, 128}, window entries <= 256).  RLT_PATH_BATCHED: each
+ * step is a sequence of B-batched device-wide kernels (any supported shape).  Both compute
+ * the same function and keep the same state layout, so calls may alternate between them.
+ * rlt_model_set_decoder_path selects one (RLT_PATH_AUTO = persistent when supported, else
+ * batched); RLT_ERR_UNSUPPORTED if the persistent path cannot run this shape.
+ * rlt_decoder_path reports the path rlt_decoder_replay would take for a state of
+ * t_max positions. */
+#define RLT_PATH_AUTO 0
+#define RLT_PATH_PERSISTENT 1
+#define RLT_PATH_BATCHED 2
+int rlt_model_set_decoder_path(rlt_model* model, int32_t path);
+int rlt_decoder_path(const rlt_model* model, int32_t t_max, int32_t* path);
 
 const char* rlt_last_error(void);
 const char* rlt_version_string(void);

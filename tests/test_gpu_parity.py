@@ -24,8 +24,9 @@ def dev():
     return torch.device("cuda:0")
 
 
-def gpu_replay(cfg, weights, tokens, dev, keep=False, t_max=None):
+def gpu_replay(cfg, weights, tokens, dev, keep=False, t_max=None, path=0):
     model = rlt.Model(cfg, weights, device=dev)
+    model.set_decoder_path(path)
     B, T = tokens.shape
     state = rlt.State(model, B, t_max or T, keep)
     S, Z = rlt.replay(model, state, torch.from_numpy(tokens).to(dev))
@@ -52,7 +53,7 @@ def test_tiny_replay_all_sequences(dev):
     w = make_weights(cfg, wl.weight_seed)
     tok = make_tokens(cfg.vocab, wl.batch, wl.seq_len, wl.token_dist, wl.token_seed)
     S, Z, model, _ = gpu_replay(cfg, w, tok, dev)
-    assert model.decoder_path(wl.batch) == 0
+    assert model.decoder_path(wl.seq_len) == 1
     S_ref, Z_ref = oracle_replay(cfg, w, tok)
     check("tiny s_t", S, S_ref, "fp32")
     check("tiny logits", Z, Z_ref, "fp32")
@@ -66,7 +67,7 @@ def test_small_replay_full_size(dev):
     w = make_weights(cfg, wl.weight_seed)
     tok = make_tokens(cfg.vocab, wl.batch, wl.seq_len, wl.token_dist, wl.token_seed)
     S, Z, model, _ = gpu_replay(cfg, w, tok, dev)
-    assert model.decoder_path(wl.batch) == 0
+    assert model.decoder_path(wl.seq_len) == 1
     seqs = [0, 21, 42, 63]
     S_ref, Z_ref = oracle_replay(cfg, w, tok, seqs)
     check("small s_t", S[seqs], S_ref, "bf16")
@@ -159,12 +160,14 @@ EDGE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", [1, 2], ids=["persistent", "batched"])
 @pytest.mark.parametrize("over,B,T", EDGE_CASES, ids=[f"case{i}" for i in range(len(EDGE_CASES))])
-def test_edge_configs(dev, over, B, T):
+def test_edge_configs(dev, over, B, T, path):
     cfg = mcfg(**over)
     w = perturb_untied(make_weights(cfg, 31), cfg, 32)
     tok = make_tokens(cfg.vocab, B, T, "uniform", 33)
-    S, Z, _, _ = gpu_replay(cfg, w, tok, dev)
+    S, Z, model, _ = gpu_replay(cfg, w, tok, dev, path=path)
+    assert model.decoder_path(T) == path
     S_ref, Z_ref = oracle_replay(cfg, w, tok)
     check(f"{over} s_t", S, S_ref, cfg.dtype)
     check(f"{over} logits", Z, Z_ref, cfg.dtype)
@@ -306,3 +309,42 @@ def test_state_contract_errors(dev):
     bad[1, 3] = cfg.vocab + 5
     rlt.rlt_encoder_forward(model, state, bad)
     assert state.device_error() == 1
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_batched_decoder_matches_persistent_and_oracle(dev, name):
+    """The two decoder implementations compute the same function on the same state."""
+    wl = CONFIGS[name]
+    cfg = wl.model
+    B, T = min(wl.batch, 8), min(wl.seq_len, 200)
+    w = perturb_untied(make_weights(cfg, wl.weight_seed), cfg, 90)
+    tok = make_tokens(cfg.vocab, B, T, wl.token_dist, wl.token_seed)
+    S1, Z1, _, _ = gpu_replay(cfg, w, tok, dev, path=1)
+    S2, Z2, _, _ = gpu_replay(cfg, w, tok, dev, path=2)
+    S_ref, Z_ref = oracle_replay(cfg, w, tok, [0, B - 1])
+    check(f"{name} batched s_t", S2[[0, B - 1]], S_ref, cfg.dtype)
+    check(f"{name} batched logits", Z2[[0, B - 1]], Z_ref, cfg.dtype)
+    rel = np.linalg.norm(S1 - S2, axis=-1) / np.linalg.norm(S1, axis=-1)
+    print(f"  persistent vs batched: max row-rel {rel.max():.2e}")
+    assert rel.max() < (1e-5 if cfg.dtype == "fp32" else 2e-2)
+
+
+def test_paths_can_alternate_on_one_state(dev):
+    """Prefill with the batched path, continue with the persistent one: same state layout."""
+    wl = CONFIGS["tiny"]
+    cfg = wl.model
+    w = make_weights(cfg, 3)
+    B, T = 3, 40
+    tok = make_tokens(cfg.vocab, B, T, "uniform", 4)
+    S_ref, _, model, _ = gpu_replay(cfg, w, tok, dev, path=1)
+    state = rlt.State(model, B, T)
+    rlt.rlt_encoder_forward(model, state, torch.from_numpy(tok).to(dev))
+    S = torch.empty(B, T, cfg.d_model, dtype=torch.float32, device=dev)
+    model.set_decoder_path(2)
+    Sa = torch.empty(B, 17, cfg.d_model, dtype=torch.float32, device=dev)
+    rlt.rlt_decoder_replay(model, state, 17, Sa)
+    model.set_decoder_path(1)
+    Sb = torch.empty(B, T - 17, cfg.d_model, dtype=torch.float32, device=dev)
+    rlt.rlt_decoder_replay(model, state, T - 17, Sb)
+    S = torch.cat([Sa, Sb], 1).cpu().numpy()
+    np.testing.assert_allclose(S, S_ref, rtol=0, atol=2e-5)
