@@ -23,6 +23,47 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_small_k_small_traffic.md")
+KERNEL_SOURCES = ["cross_token_recurrent_amd/csrc/dec_small.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decoder launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing or was taken on a different version of the kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel source sha256/16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_kernel(gib: float = 1.0):
+    """A plain device copy of known size (calibrates the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4}), flush=True)
 
 
 def algorithmic_decoder_bytes(cfg, B: int, T: int) -> float:
@@ -87,7 +128,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="small")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-kernel", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.copy_kernel:
+        copy_kernel()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the replay shards over sequences with no communication, "
               "so a multi-GPU figure is not measured here.", file=sys.stderr)
@@ -167,7 +212,7 @@ def main():
         "phase_ms": {"encoder": enc_ms, "decoder_replay": dec_ms, "logits": head_ms},
         "decoder_path": {1: "persistent-per-sequence", 2: "batched-phases"}[path],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if path == 1 else None,
                      "kernel": "dec_small_k" if path == 1 else "batched decoder phases",
                      "algorithmic_bytes_per_launch": dec_bytes},
         "cpu_baseline": None,

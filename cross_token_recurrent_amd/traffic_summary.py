@@ -1,0 +1,73 @@
+"""Turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs into the decoder traffic summary.
+
+    python -m cross_token_recurrent_amd.traffic_summary <fetch_dir> <write_dir> \
+        <copy_fetch_dir> <copy_write_dir> <out.md>
+
+Each directory holds the counter_collection.csv of one `rocprofv3 --pmc <counter>` run:
+the decoder runs come from `bench.py --steps 1 --warmup 0 --no-cpu-baseline`, the copy
+runs from `bench.py --copy-kernel` (1 GiB read + 1 GiB written).  The counters report
+KiB per dispatch; each is scaled by the ratio true bytes / counter bytes measured on the
+copy kernel, and the decoder's per-launch traffic is reported together with the kernel
+source hash so that a stale summary is never used for a changed kernel.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def _rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def _value(d, counter, kernel_sub):
+    vals = [float(r["Counter_Value"]) for r in _rows(d)
+            if r["Counter_Name"] == counter and kernel_sub in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"{counter} for a kernel matching {kernel_sub!r} not found in {d}")
+    return max(vals)
+
+
+def main(argv):
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir, out = argv
+    import bench  # noqa: E402  (repository root on sys.path)
+    copy_bytes = float(1 << 30)
+    c_fetch = _value(cfetch_dir, "FETCH_SIZE", "copy") * 1024.0
+    c_write = _value(cwrite_dir, "WRITE_SIZE", "copy") * 1024.0
+    k_fetch = _value(fetch_dir, "FETCH_SIZE", "dec_small_k") * 1024.0
+    k_write = _value(write_dir, "WRITE_SIZE", "dec_small_k") * 1024.0
+    f_fetch, f_write = copy_bytes / c_fetch, copy_bytes / c_write
+    traffic = k_fetch * f_fetch + k_write * f_write
+    from workloads import CONFIGS
+    wl = CONFIGS["small"]
+    alg = bench.algorithmic_decoder_bytes(wl.model, wl.batch, wl.seq_len)
+    with open(out, "w") as f:
+        f.write("# dec_small_k on the small workload: HBM traffic per launch (rocprofv3 counters)\n\n")
+        f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -- python3 <repo>/bench.py --copy-kernel\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -- python3 <repo>/bench.py --copy-kernel\n")
+        f.write("    python -m cross_token_recurrent_amd.traffic_summary <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/dec_small_k_small_traffic.md\n\n")
+        f.write(f"- copy kernel: 1 GiB read / 1 GiB written; FETCH_SIZE reads {c_fetch:.4e} B, WRITE_SIZE {c_write:.4e} B\n")
+        f.write(f"- fetch scale: {f_fetch:.4f}\n")
+        f.write(f"- write scale: {f_write:.4f}\n")
+        f.write(f"- decoder FETCH_SIZE bytes per launch (raw): {k_fetch:.4e}\n")
+        f.write(f"- decoder WRITE_SIZE bytes per launch (raw): {k_write:.4e}\n")
+        f.write(f"- traffic bytes per launch: {traffic:.6e}\n")
+        f.write(f"- algorithmic bytes per launch: {alg:.6e}\n")
+        f.write(f"- traffic / algorithmic: {traffic / alg:.4f}\n")
+        f.write(f"- kernel source sha256/16: `{bench.kernel_source_hash()}`\n")
+    print(open(out).read())
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
