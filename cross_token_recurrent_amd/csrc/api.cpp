@@ -267,6 +267,7 @@ void compute_state_layout(const ModelLayout& m, int B, int T, int keep, StateLay
   StateLayout& S = *s;
   S.B = B;
   S.T = T;
+  S.T8 = (T + 7) / 8 * 8;
   S.keep = keep;
   S.Wm1 = m.W - 1;
   const size_t D = m.D, e = m.esz, Bz = B, Tz = T, L = m.L, G = m.G, F = m.F;
@@ -283,7 +284,7 @@ void compute_state_layout(const ModelLayout& m, int B, int T, int keep, StateLay
   S.ring_v = take(L * Bz * S.Wm1 * heads_tokens * e);
   S.e = take(Bz * Tz * D * e);
   S.mem_k = take(G * Bz * Tz * D * e);
-  S.mem_v = take(G * Bz * Tz * D * e);
+  S.mem_v = take(G * Bz * static_cast<size_t>(S.T8) * D * e);
   if (keep) {
     S.enc_k = take(L * Bz * Tz * D * e);
     S.enc_v = take(L * Bz * Tz * D * e);
@@ -419,6 +420,16 @@ int rlt_state_init(const rlt_model* model, void* buffer, size_t buffer_bytes, in
   s->lay = S;
   s->buf = static_cast<char*>(buffer);
   s->bytes = buffer_bytes;
+  // Memory rows are zeroed once: the decoder reads whole 8-key value blocks, and rows past
+  // the current position (multiplied by a zero weight) must hold finite values.
+  const ModelLayout& M = model->lay;
+  const size_t memv_bytes = static_cast<size_t>(M.G) * S.B * S.T8 * M.D * M.esz;
+  hipError_t ze = launch_zero(s->buf + S.mem_k, S.mem_v - S.mem_k, as_stream(stream));
+  if (ze == hipSuccess) ze = launch_zero(s->buf + S.mem_v, memv_bytes, as_stream(stream));
+  if (ze != hipSuccess) {
+    delete s;
+    return fail(RLT_ERR_HIP, std::string("zero memory rows: ") + hipGetErrorString(ze));
+  }
   int rc = reset_state(model, s, as_stream(stream));
   if (rc) {
     delete s;
@@ -574,12 +585,13 @@ int rlt_encoder_forward(const rlt_model* model, rlt_state* state, const int32_t*
             "encoder final norm");
     for (int gi = 0; gi < M.G; ++gi) {
       const size_t goff = static_cast<size_t>(gi) * S.B * S.T * D * M.esz;
+      const size_t goff_v = static_cast<size_t>(gi) * S.B * S.T8 * D * M.esz;
       GemmArgs g{};
       g.A = sb + S.h; g.W = ws + M.wkvm + gi * M.group_stride; g.out = nullptr;
       g.M = rows; g.N = 2 * D; g.K = D; g.lda = D; g.ldw = D; g.ldo = 0;
       g.epi = EPI_SCATTER_HEADS;
       g.sc_k = sb + S.mem_k + goff;
-      g.sc_v = sb + S.mem_v + goff;
+      g.sc_v = sb + S.mem_v + goff_v;
       g.sc_c0 = 0;
       g.sc_n = n; g.sc_b0 = b0; g.sc_t0 = t0; g.sc_T = S.T; g.sc_H = H; g.sc_dh = DH; g.sc_D = D; g.sc_B = S.B;
       RLT_HIP(launch_gemm(g, dt, st), "memory projection");
@@ -666,12 +678,13 @@ int rlt_state_load_encoder_outputs(const rlt_model* model, rlt_state* state, con
           "load e");
   const size_t gsrc = static_cast<size_t>(S.B) * n * M.D;
   const size_t gdst = static_cast<size_t>(S.B) * S.T * M.D * M.esz;
+  const size_t gdst_v = static_cast<size_t>(S.B) * S.T8 * M.D * M.esz;
   for (int g = 0; g < M.G; ++g) {
     RLT_HIP(launch_store_tokens(mem_k + g * gsrc, state->buf + S.mem_k + g * gdst, S.B, n, M.D, t0, S.T,
                                 M.dtype, 1, M.H, M.DH, 1, st),
             "load memory keys");
-    RLT_HIP(launch_store_tokens(mem_v + g * gsrc, state->buf + S.mem_v + g * gdst, S.B, n, M.D, t0, S.T,
-                                M.dtype, 1, M.H, M.DH, 1, st),
+    RLT_HIP(launch_store_tokens(mem_v + g * gsrc, state->buf + S.mem_v + g * gdst_v, S.B, n, M.D, t0, S.T,
+                                M.dtype, 2, M.H, M.DH, 1, st),
             "load memory values");
   }
   state->t_enc += n;
@@ -693,6 +706,7 @@ int rlt_state_read_encoder_outputs(const rlt_model* model, const rlt_state* stat
   }
   const size_t gsrc = static_cast<size_t>(S.B) * n * M.D;
   const size_t gdst = static_cast<size_t>(S.B) * S.T * M.D * M.esz;
+  const size_t gdst_v = static_cast<size_t>(S.B) * S.T8 * M.D * M.esz;
   for (int g = 0; g < M.G; ++g) {
     if (mem_k) {
       RLT_HIP(launch_store_tokens(mem_k + g * gsrc, state->buf + S.mem_k + g * gdst, S.B, n, M.D, t0, S.T,
@@ -700,8 +714,8 @@ int rlt_state_read_encoder_outputs(const rlt_model* model, const rlt_state* stat
               "read memory keys");
     }
     if (mem_v) {
-      RLT_HIP(launch_store_tokens(mem_v + g * gsrc, state->buf + S.mem_v + g * gdst, S.B, n, M.D, t0, S.T,
-                                  M.dtype, 1, M.H, M.DH, 0, st),
+      RLT_HIP(launch_store_tokens(mem_v + g * gsrc, state->buf + S.mem_v + g * gdst_v, S.B, n, M.D, t0, S.T,
+                                  M.dtype, 2, M.H, M.DH, 0, st),
               "read memory values");
     }
   }

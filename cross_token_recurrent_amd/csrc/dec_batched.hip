@@ -243,13 +243,18 @@ __global__ __launch_bounds__(64) void swa_k(const float* __restrict__ qkv, WT* _
 }
 
 // Cross-attention partial states: one wave per (key chunk, head, sequence).
+// Scores with lanes over keys (LPK lanes per key row), then exp(s - M) for the chunk in
+// LDS, then P.V with lanes over (dim, 8-key block) reading the key-blocked value layout.
 template <typename WT, int DH>
 __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx, const WT* __restrict__ mem_k,
                                                    const WT* __restrict__ mem_v, float* __restrict__ part, int B,
                                                    int H, int T, int t, int nsmax, float scale) {
   constexpr int LPK = DH / 16;
   constexpr int SLOTS = 64 / LPK;
-  __shared__ float lds[64 * 17 + 64];
+  constexpr int DL = DH < 64 ? DH : 64;   // lanes per block in the P.V pass
+  constexpr int BSTEP = 64 / DL;          // blocks taken at once
+  constexpr int ND = DH / DL;             // dims per lane (2 when DH = 128)
+  __shared__ float ps[KCHUNK];
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int slot = lane / LPK, sub = lane % LPK;
@@ -258,36 +263,64 @@ __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx,
   float q[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) q[c] = qr[c] * scale;
-  const size_t hb = (static_cast<size_t>(b) * H + h) * static_cast<size_t>(T) * DH;   // memory pre-offset to group
+  const size_t T8 = (static_cast<size_t>(T) + 7) / 8 * 8;
+  const WT* kb = mem_k + (static_cast<size_t>(b) * H + h) * static_cast<size_t>(T) * DH;   // pre-offset to group
+  const WT* vb = mem_v + (static_cast<size_t>(b) * H + h) * T8 * DH;
   const int j0 = split * KCHUNK, j1 = min(j0 + KCHUNK, t + 1);
-  SoftState st;
-  st.init();
-  int j = j0 + slot;
-  float kc[16], vc[16];
-  {
-    const int jj = min(j, j1 - 1);
-    Row16<WT>::load(mem_k + hb + static_cast<size_t>(jj) * DH + sub * 16, kc);
-    Row16<WT>::load(mem_v + hb + static_cast<size_t>(jj) * DH + sub * 16, vc);
-  }
-  for (; j0 + (j - j0) - slot < j1; j += SLOTS) {
-    // next row in flight while this one is used
-    float kn[16], vn[16];
-    const int jn = min(j + SLOTS, j1 - 1);
-    Row16<WT>::load(mem_k + hb + static_cast<size_t>(jn) * DH + sub * 16, kn);
-    Row16<WT>::load(mem_v + hb + static_cast<size_t>(jn) * DH + sub * 16, vn);
+  float mloc = -INFINITY;
+  for (int i = slot; i < KCHUNK; i += SLOTS) {
+    const int j = min(j0 + i, j1 - 1);   // rows past the chunk end are loaded but masked
+    float k[16];
+    Row16<WT>::load(kb + static_cast<size_t>(j) * DH + sub * 16, k);
     float a = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) a += q[c] * kc[c];
+    for (int c = 0; c < 16; ++c) a += q[c] * k[c];
     a = group_sum<LPK>(a);
-    st.add(j < j1 ? a : -INFINITY, vc);
+    a = j0 + i < j1 ? a : -INFINITY;
+    if (sub == 0) ps[i] = a;
+    mloc = fmaxf(mloc, a);
+  }
+  const float M = group_max<64>(mloc);   // finite: key j0 <= t is in the chunk
+  __syncthreads();
+  float lsum = 0.f;
+  for (int i = lane; i < KCHUNK; i += 64) {
+    const float pr = __expf(ps[i] - M);   // masked keys: exp(-inf) = 0
+    ps[i] = pr;
+    lsum += pr;
+  }
+  lsum = group_sum<64>(lsum);
+  __syncthreads();
+  const int d0 = lane % DL, bq = lane / DL;
+  const int nblk = (j1 - j0 + 7) / 8;
+  float o[ND];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      kc[c] = kn[c];
-      vc[c] = vn[c];
+  for (int nd = 0; nd < ND; ++nd) o[nd] = 0.f;
+  for (int blk = bq; blk < nblk; blk += BSTEP) {
+    const float4 p0 = *reinterpret_cast<const float4*>(ps + blk * 8);
+    const float4 p1 = *reinterpret_cast<const float4*>(ps + blk * 8 + 4);
+    const float pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) {
+      float v[8];
+      load8(vb + ((static_cast<size_t>(j0 / 8 + blk)) * DH + d0 + nd * 64) * 8, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[nd] += pw[k] * v[k];
     }
   }
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) {
+#pragma unroll
+    for (int off = DL; off < 64; off <<= 1) o[nd] += __shfl_xor(o[nd], off, 64);
+  }
   float* pr = part + ((static_cast<size_t>(b) * H + h) * nsmax + split) * (DH + 2);
-  wave_finish<DH>(st, lds, pr, pr + 1, pr + 2, nullptr, lane);
+  if (bq == 0) {
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) pr[2 + d0 + nd * 64] = o[nd];
+  }
+  if (lane == 0) {
+    pr[0] = M;
+    pr[1] = lsum;
+  }
 }
 
 // attn[b, h*DH + d] = sum_s e^{m_s - M} o_s[d] / sum_s e^{m_s - M} l_s, splits in order.
@@ -323,10 +356,11 @@ hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratc
   } else {
     const int g = m.G == 1 ? 0 : l;
     const size_t goff = static_cast<size_t>(g) * B * S.T * m.D;
+    const size_t goff_v = static_cast<size_t>(g) * B * S.T8 * m.D;
     const int ns = (t + 1 + KCHUNK - 1) / KCHUNK;
     cross_part_k<WT, DH><<<dim3(ns, H, B), 64, 0, st>>>(
         reinterpret_cast<const float*>(base + sc.qkv), reinterpret_cast<const WT*>(state + S.mem_k) + goff,
-        reinterpret_cast<const WT*>(state + S.mem_v) + goff, reinterpret_cast<float*>(base + sc.part), B, H, S.T, t,
+        reinterpret_cast<const WT*>(state + S.mem_v) + goff_v, reinterpret_cast<float*>(base + sc.part), B, H, S.T, t,
         sc.nsmax, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

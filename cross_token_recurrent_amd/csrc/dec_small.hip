@@ -9,23 +9,34 @@
 // feedback of s_{t-1}, final norm gives s_t).
 //
 // Why this shape on MI355X: at d_model <= 128 a decoder layer is a handful of 64..256-wide
-// matrix-vector products and two single-query attentions, so a step is bound by VALU issue
-// and latency, not by HBM or MFMA throughput.  Independent sequences never synchronise,
-// so each sequence gets one workgroup of 4 waves (one per SIMD) that keeps its window
-// caches, running state, gains and small vectors in LDS.  The design keeps the number of
-// wave instructions per step low and the latency hidden:
-//   * matrix-vector products: 8-lane groups per row, weights for the next product
-//     prefetched into registers one phase ahead (s_barrier does not wait for global
-//     loads), RMSNorm fused into the product's operand fetch;
-//   * both attentions run one head per wave with lanes over keys; partial softmax states
-//     are combined inside the wave through LDS (no workgroup barrier);
-//   * cross-attention streams memory rows with batched loads requested two batches ahead,
-//     the first two batches issued two phases before they are needed.
-// bf16 mode: matrix-product operands are packed bf16 in LDS and consumed with
-// v_dot2c_f32_bf16 (exact bf16 products, fp32 accumulation); the query is split into
-// bf16 hi + lo parts for the score dot products, so attention math keeps ~fp32 accuracy;
-// the residual stream, softmax statistics and s_t stay fp32.
+// matrix-vector products and two single-query attentions, so a step is a chain of short,
+// latency-bound phases, while the memory rows of the cross-attention (a few hundred KB per
+// step and sequence) must stream from HBM or the Infinity Cache without stalling that
+// chain.  Independent sequences never synchronise, so each sequence gets one workgroup of
+// 12 waves (three per SIMD) that keeps its window caches, residual stream, gains and small
+// vectors in LDS and splits the work by role, each role running its own loop through the
+// same sequence of workgroup barriers:
+//   * 4 product waves run the gated merge and every matrix-vector product: 8- or 16-lane
+//     groups per row, the weights of each product requested two products ahead into
+//     registers (the merge weights stay resident), RMSNorm fused into the operand fetch,
+//     the gated merge fused into the gate/feedback products and SwiGLU into the FFN input
+//     product;
+//   * 8 attention waves hold the memory rows of one layer in registers (each a head and a
+//     contiguous share of its rows).  The rows of the next layer are requested over the
+//     four phases after the current cross-attention, while the product waves compute, so
+//     the requests drain in the background and have a whole layer to arrive; the product
+//     waves request only weights, so their loads never queue behind rows (the vector
+//     memory counter of a wave retires in order).  Scores use lanes over keys; P.V uses
+//     lanes over (dim, 8-key block) on the key-blocked value layout, so a lane's dot
+//     products run over keys and the lane reduction at the end is at most two steps;
+//   * window self-attention runs on one attention wave per head: scores with lanes over
+//     the ring slots, P.V with lanes over (dim, 8-slot block) of a key-blocked copy of the
+//     value ring.
+// bf16 mode: matrix-product operands (activations, q, P) are bf16 and every product
+// accumulates in fp32 (v_dot2c_f32_bf16); the residual stream, softmax statistics and s_t
+// stay fp32.  Scores are kept in the log2 domain (q pre-scaled by log2(e)/sqrt(d_h)).
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "rlt_internal.h"
@@ -33,18 +44,39 @@
 namespace rlt {
 namespace {
 
-constexpr int NT = 256;          // threads per workgroup (4 waves, one per SIMD)
-constexpr int NWAVE = NT / 64;
-constexpr int NG = NT / 8;       // 8-lane groups for matrix-vector products
-constexpr int CMAX = 8;          // prefetched (row, chunk) pairs per lane and product
-constexpr int WCAP = 256;        // largest window (entries held at once) supported
+// Wave roles: waves 0..NA-1 do the attention (they hold the memory rows), waves
+// NA..NA+NM-1 do the matrix-vector products (they hold the weights).  Each SIMD runs two
+// attention waves and one product wave.
+constexpr int NA = 8;
+constexpr int NM = 4;
+constexpr int NT = 64 * (NA + NM);   // 768 threads
+constexpr int NTM = 64 * NM;         // product threads
+constexpr int WCAP = 256;            // largest window (entries held at once) supported
+constexpr float kLog2e = 1.4426950408889634f;
 
+template <int V> using IC = std::integral_constant<int, V>;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// threadIdx.x through an empty asm: lane-dependent offsets derived from it are recomputed
+// where they are used instead of being hoisted out of the step loop and held in registers.
+__device__ __forceinline__ unsigned tid_here() {
+  unsigned t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// base + element offset with 32-bit offset arithmetic (scalar base + vector offset loads)
+template <typename WT>
+__device__ __forceinline__ const WT* at(const WT* base, uint32_t off) {
+  return reinterpret_cast<const WT*>(reinterpret_cast<const char*>(base) + off * static_cast<uint32_t>(sizeof(WT)));
 }
 
 // ---- storage-type operations on 8-element chunks -----------------------------------
@@ -54,6 +86,7 @@ template <> struct Ops<bf16_t> {
   struct Chunk { uint4 v; };
   static __device__ __forceinline__ Chunk load(const bf16_t* p) { return {*reinterpret_cast<const uint4*>(p)}; }
   static __device__ __forceinline__ Chunk zero() { return {make_uint4(0u, 0u, 0u, 0u)}; }
+  static __device__ __forceinline__ void store(bf16_t* p, const Chunk& c) { *reinterpret_cast<uint4*>(p) = c.v; }
   static __device__ __forceinline__ Chunk pack(const float (&f)[8]) {
     return {make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                        pack_bf16x2(f[6], f[7]))};
@@ -67,6 +100,14 @@ template <> struct Ops<bf16_t> {
     acc = d2(w.v.y, x.v.y, acc);
     acc = d2(w.v.z, x.v.z, acc);
     return d2(w.v.w, x.v.w, acc);
+  }
+  // acc + sum of the 8 elements
+  static __device__ __forceinline__ float sum(const Chunk& c, float acc) {
+    constexpr uint32_t ones = 0x3F803F80u;   // bf16 pair (1, 1)
+    acc = d2(c.v.x, ones, acc);
+    acc = d2(c.v.y, ones, acc);
+    acc = d2(c.v.z, ones, acc);
+    return d2(c.v.w, ones, acc);
   }
   static __device__ __forceinline__ void unpack(const Chunk& c, float (&f)[8]) {
     const uint32_t w[4] = {c.v.x, c.v.y, c.v.z, c.v.w};
@@ -86,6 +127,10 @@ template <> struct Ops<float> {
   static __device__ __forceinline__ Chunk zero() {
     return {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
   }
+  static __device__ __forceinline__ void store(float* p, const Chunk& c) {
+    *reinterpret_cast<float4*>(p) = c.a;
+    *reinterpret_cast<float4*>(p + 4) = c.b;
+  }
   static __device__ __forceinline__ Chunk pack(const float (&f)[8]) {
     return {make_float4(f[0], f[1], f[2], f[3]), make_float4(f[4], f[5], f[6], f[7])};
   }
@@ -94,156 +139,258 @@ template <> struct Ops<float> {
     acc += w.b.x * x.b.x; acc += w.b.y * x.b.y; acc += w.b.z * x.b.z; acc += w.b.w * x.b.w;
     return acc;
   }
+  static __device__ __forceinline__ float sum(const Chunk& c, float acc) {
+    acc += c.a.x; acc += c.a.y; acc += c.a.z; acc += c.a.w;
+    acc += c.b.x; acc += c.b.y; acc += c.b.z; acc += c.b.w;
+    return acc;
+  }
   static __device__ __forceinline__ void unpack(const Chunk& c, float (&f)[8]) {
     f[0] = c.a.x; f[1] = c.a.y; f[2] = c.a.z; f[3] = c.a.w;
     f[4] = c.b.x; f[5] = c.b.y; f[6] = c.b.z; f[7] = c.b.w;
   }
 };
 
-// A 16-element query slice, prepared for dot products with 16-element key rows.
-template <typename WT> struct QSlice;
-template <> struct QSlice<bf16_t> {
-  uint32_t hi[8], lo[8];   // q = hi + lo, both bf16 pairs (~16 significant bits)
-  // qf: fp32 query (unused); qh / ql: bf16 hi and lo halves, 16 elements each
-  __device__ __forceinline__ void set(const float* qf, const bf16_t* qh, const bf16_t* ql) {
-    (void)qf;
-    const uint4 h0 = *reinterpret_cast<const uint4*>(qh), h1 = *reinterpret_cast<const uint4*>(qh + 8);
-    const uint4 l0 = *reinterpret_cast<const uint4*>(ql), l1 = *reinterpret_cast<const uint4*>(ql + 8);
-    hi[0] = h0.x; hi[1] = h0.y; hi[2] = h0.z; hi[3] = h0.w; hi[4] = h1.x; hi[5] = h1.y; hi[6] = h1.z; hi[7] = h1.w;
-    lo[0] = l0.x; lo[1] = l0.y; lo[2] = l0.z; lo[3] = l0.w; lo[4] = l1.x; lo[5] = l1.y; lo[6] = l1.z; lo[7] = l1.w;
+// A 16-element query slice in the storage precision, for dot products with key rows.
+template <typename WT> struct QVec;
+template <> struct QVec<bf16_t> {
+  uint32_t q[8];
+  __device__ __forceinline__ void load(const bf16_t* p) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p), b = *reinterpret_cast<const uint4*>(p + 8);
+    q[0] = a.x; q[1] = a.y; q[2] = a.z; q[3] = a.w; q[4] = b.x; q[5] = b.y; q[6] = b.z; q[7] = b.w;
   }
   __device__ __forceinline__ float dot(const Ops<bf16_t>::Chunk& k0, const Ops<bf16_t>::Chunk& k1) const {
-    const uint32_t kv[8] = {k0.v.x, k0.v.y, k0.v.z, k0.v.w, k1.v.x, k1.v.y, k1.v.z, k1.v.w};
-    float a = 0.f, b = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a = Ops<bf16_t>::d2(kv[i], lo[i], a);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b = Ops<bf16_t>::d2(kv[i], hi[i], b);
-    return a + b;
+    float a = Ops<bf16_t>::d2(q[0], k0.v.x, 0.f);
+    a = Ops<bf16_t>::d2(q[1], k0.v.y, a);
+    a = Ops<bf16_t>::d2(q[2], k0.v.z, a);
+    a = Ops<bf16_t>::d2(q[3], k0.v.w, a);
+    a = Ops<bf16_t>::d2(q[4], k1.v.x, a);
+    a = Ops<bf16_t>::d2(q[5], k1.v.y, a);
+    a = Ops<bf16_t>::d2(q[6], k1.v.z, a);
+    return Ops<bf16_t>::d2(q[7], k1.v.w, a);
   }
 };
-template <> struct QSlice<float> {
+template <> struct QVec<float> {
   float q[16];
-  __device__ __forceinline__ void set(const float* src, const float* qh, const float* ql) {
-    (void)qh;
-    (void)ql;
+  __device__ __forceinline__ void load(const float* p) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = src[i];
+    for (int i = 0; i < 16; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(p + i);
+      q[i] = v.x; q[i + 1] = v.y; q[i + 2] = v.z; q[i + 3] = v.w;
+    }
   }
   __device__ __forceinline__ float dot(const Ops<float>::Chunk& k0, const Ops<float>::Chunk& k1) const {
-    return q[0] * k0.a.x + q[1] * k0.a.y + q[2] * k0.a.z + q[3] * k0.a.w + q[4] * k0.b.x + q[5] * k0.b.y +
-           q[6] * k0.b.z + q[7] * k0.b.w + q[8] * k1.a.x + q[9] * k1.a.y + q[10] * k1.a.z + q[11] * k1.a.w +
-           q[12] * k1.b.x + q[13] * k1.b.y + q[14] * k1.b.z + q[15] * k1.b.w;
+    float a = q[0] * k0.a.x;
+    a += q[1] * k0.a.y; a += q[2] * k0.a.z; a += q[3] * k0.a.w;
+    a += q[4] * k0.b.x; a += q[5] * k0.b.y; a += q[6] * k0.b.z; a += q[7] * k0.b.w;
+    a += q[8] * k1.a.x; a += q[9] * k1.a.y; a += q[10] * k1.a.z; a += q[11] * k1.a.w;
+    a += q[12] * k1.b.x; a += q[13] * k1.b.y; a += q[14] * k1.b.z; a += q[15] * k1.b.w;
+    return a;
   }
 };
 
-// o[0..16) += w * v (v = two 8-element chunks)
-template <typename WT>
-__device__ __forceinline__ void axpy16(float (&o)[16], float w, const typename Ops<WT>::Chunk& v0,
-                                       const typename Ops<WT>::Chunk& v1) {
-  float f[8];
-  Ops<WT>::unpack(v0, f);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) o[c] += w * f[c];
-  Ops<WT>::unpack(v1, f);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) o[8 + c] += w * f[c];
-}
+// ---- matrix-vector products out[r] = W[r,:] . x -----------------------------------------
+// Products run on the NTM threads of the product waves; mt = thread index among them.
+// With GL lanes per row, thread mt (grp = mt / GL, sub = mt % GL) owns rows grp, grp + NGR,
+// ... (NGR = NTM / GL) and, of each row, the 8-element chunks sub + GL*ci (ci < CPL), so
+// K = 8 * GL * CPL.  The first CB (row, chunk) pairs come from a register buffer filled
+// ahead of time (wpre); the rest are loaded when needed.  Rows past N are clamped on
+// load; a wave whose groups all lie past N skips the row.
+__device__ __forceinline__ unsigned mtid_here() { return tid_here() - 64u * NA; }
 
-// ---- matrix-vector products out[r] = W[r,:] . x ----------------------------------------
-// Lane (grp, sub) owns rows grp, grp+NG, ... and the 8-element chunks sub*8 + 64*c of each
-// row; (row, chunk) pairs are enumerated row-major.  The first CMAX pairs are loaded into
-// registers ahead of time (wprefetch); the rest, if any, are loaded when needed.
-template <typename WT> struct WBuf { typename Ops<WT>::Chunk c[CMAX]; };
-
-template <typename WT>
-__device__ __forceinline__ void wprefetch(WBuf<WT>& buf, const WT* __restrict__ W, int N, int K) {
-  const int sub = threadIdx.x & 7, grp = threadIdx.x >> 3;
-  const int cpl = K >> 6;
+template <typename WT, int GL, int CPL, int CB>
+__device__ __forceinline__ void wpre(typename Ops<WT>::Chunk* buf, const WT* __restrict__ W, int N) {
+  constexpr int K = 8 * GL * CPL, NGR = NTM / GL;
+  const unsigned mt = mtid_here();
+  const int sub = mt % GL, grp = mt / GL;
 #pragma unroll
-  for (int p = 0; p < CMAX; ++p) {
-    const int ri = p / cpl, ci = p - ri * cpl;
-    const int r = min(grp + ri * NG, N - 1);   // rows past N are loaded but never used
-    buf.c[p] = Ops<WT>::load(W + static_cast<size_t>(r) * K + sub * 8 + ci * 64);
+  for (int p = 0; p < CB; ++p) {
+    const int ri = p / CPL, ci = p % CPL;
+    const int r = min(grp + ri * NGR, N - 1);
+    buf[p] = Ops<WT>::load(at(W, r * K + (sub + GL * ci) * 8));
   }
 }
 
-// K = CPL * 64 with CPL <= CMAX: the lane's operand chunks are computed once (xr) and the
-// first CMAX / CPL rows come from the prefetched buffer.
-template <int CPL, typename WT, typename XF, typename Epi>
-__device__ __forceinline__ void wcompute_c(const WBuf<WT>& buf, const WT* __restrict__ W, int N, XF&& xf,
-                                           Epi&& epi) {
+// Lane sub runs the epilogue of the group's rows base + sub (one per lane and round of
+// GL rows), so each epilogue runs once per row.
+template <typename WT, int GL, int CPL, int CB, typename XF, typename Epi>
+__device__ __forceinline__ void wmv(const typename Ops<WT>::Chunk* buf, const WT* __restrict__ W, int N, XF&& xf,
+                                    Epi&& epi) {
   using O = Ops<WT>;
-  constexpr int K = CPL * 64;
-  constexpr int RB = CMAX / CPL;
-  const int sub = threadIdx.x & 7, grp = threadIdx.x >> 3;
+  constexpr int K = 8 * GL * CPL, NGR = NTM / GL;
+  constexpr int RBU = (CB + CPL - 1) / CPL;   // rows that take chunks from the buffer
+  const unsigned mt = mtid_here();
+  const int sub = mt % GL, grp = mt / GL;
+  const int grp0 = (mt & ~63u) / GL;            // first group of this wave (uniform)
+  const int nrows = (N - grp0 + NGR - 1) / NGR; // rows with at least one group of this wave
+  if (nrows <= 0) return;
   typename O::Chunk xr[CPL];
 #pragma unroll
-  for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf(sub * 8 + ci * 64);
-  const int nrows = (N + NG - 1) / NG;
-  // every lane of the 8-lane group gets every row total; lane `sub` then runs the epilogue
-  // of row `sub`, so each epilogue is executed once per row, not once per group lane
+  for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf((sub + GL * ci) * 8);
   float mine = 0.f;
+  int base = 0;
 #pragma unroll
-  for (int ri = 0; ri < RB; ++ri) {
+  for (int ri = 0; ri < RBU; ++ri) {
     if (ri < nrows) {
+      if (ri - base == GL) {   // every lane of the round holds its row: run the epilogues
+        const int r = grp + (base + sub) * NGR;
+        if (r < N) epi(r, mine);
+        base += GL;
+      }
+      const int r = min(grp + ri * NGR, N - 1);
       float acc = 0.f;
 #pragma unroll
-      for (int ci = 0; ci < CPL; ++ci) acc = O::dot(buf.c[ri * CPL + ci], xr[ci], acc);
-      acc = group_sum<8>(acc);
-      mine = sub == ri ? acc : mine;
+      for (int ci = 0; ci < CPL; ++ci) {
+        const int p = ri * CPL + ci;
+        const typename O::Chunk w = p < CB ? buf[p < CB ? p : 0] : O::load(at(W, r * K + (sub + GL * ci) * 8));
+        acc = O::dot(w, xr[ci], acc);
+      }
+      acc = group_sum<GL>(acc);
+      mine = sub == ri - base ? acc : mine;
     }
   }
-  {
-    const int r = grp + sub * NG;
-    if (sub < RB && sub < nrows && r < N) epi(r, mine);
-  }
-  for (int ri = RB; ri < nrows; ++ri) {
-    const int r = grp + ri * NG;
+  for (int ri = RBU; ri < nrows; ++ri) {
+    if (ri - base == GL) {
+      const int r = grp + (base + sub) * NGR;
+      if (r < N) epi(r, mine);
+      base += GL;
+    }
+    const int r = min(grp + ri * NGR, N - 1);
     float acc = 0.f;
 #pragma unroll
-    for (int ci = 0; ci < CPL; ++ci) {
-      const typename O::Chunk w = O::load(W + static_cast<size_t>(min(r, N - 1)) * K + sub * 8 + ci * 64);
-      acc = O::dot(w, xr[ci], acc);
-    }
-    acc = group_sum<8>(acc);
-    if (sub == 0 && r < N) epi(r, acc);
+    for (int ci = 0; ci < CPL; ++ci) acc = O::dot(O::load(at(W, r * K + (sub + GL * ci) * 8)), xr[ci], acc);
+    acc = group_sum<GL>(acc);
+    mine = sub == ri - base ? acc : mine;
+  }
+  {
+    const int r = grp + (base + sub) * NGR;
+    if (base + sub < nrows && r < N) epi(r, mine);
   }
 }
 
-// Any K (multiple of 64): every chunk loaded when needed.
-template <typename WT, typename XF, typename Epi>
-__device__ __forceinline__ void wcompute_any(const WT* __restrict__ W, int N, int K, XF&& xf, Epi&& epi) {
+// SwiGLU input product: rows come in (gate, up) pairs of the interleaved ffn_in layout
+// (activation i: gate row (i/16)*32 + i%16, up row 16 further).  Pair i = grp + k*NGR;
+// lane sub stores act = silu(gate) * up of the round's pair base + sub.
+__device__ __forceinline__ int swiglu_gate_row(int i) { return (i / 16) * 32 + i % 16; }
+
+template <typename WT, int CPL, int CB>
+__device__ __forceinline__ void wpre_swiglu(typename Ops<WT>::Chunk* buf, const WT* __restrict__ W, int F) {
+  constexpr int GL = 8, K = 8 * GL * CPL, NGR = NTM / GL;
+  const unsigned mt = mtid_here();
+  const int sub = mt % GL, grp = mt / GL;
+#pragma unroll
+  for (int p = 0; p < CB; ++p) {
+    const int k = p / (2 * CPL), u = (p / CPL) % 2, ci = p % CPL;   // pair k, gate (u = 0) or up row
+    const int gr = swiglu_gate_row(min(grp + k * NGR, F - 1));
+    buf[p] = Ops<WT>::load(at(W, (gr + 16 * u) * K + (sub + GL * ci) * 8));
+  }
+}
+
+template <typename WT, int CPL, int CB, typename XF>
+__device__ __forceinline__ void wmv_swiglu(const typename Ops<WT>::Chunk* buf, const WT* __restrict__ W, int F,
+                                           XF&& xf, WT* __restrict__ out) {
   using O = Ops<WT>;
-  const int sub = threadIdx.x & 7, grp = threadIdx.x >> 3;
-  for (int r0 = grp; r0 < ((N + NG - 1) / NG) * NG; r0 += NG) {
-    float acc = 0.f;
-    for (int k = sub * 8; k < K; k += 64) {
-      const typename O::Chunk w = r0 < N ? O::load(W + static_cast<size_t>(r0) * K + k) : O::zero();
-      acc = O::dot(w, xf(k), acc);
+  constexpr int GL = 8, K = 8 * GL * CPL, NGR = NTM / GL;
+  constexpr int KBU = (CB + 2 * CPL - 1) / (2 * CPL);   // pairs that take chunks from the buffer
+  const unsigned mt = mtid_here();
+  const int sub = mt % GL, grp = mt / GL;
+  const int grp0 = (mt & ~63u) / GL;
+  const int npairs = (F - grp0 + NGR - 1) / NGR;
+  if (npairs <= 0) return;
+  typename O::Chunk xr[CPL];
+#pragma unroll
+  for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf((sub + GL * ci) * 8);
+  float mine = 0.f;
+  int base = 0;
+  auto pair = [&](int k, auto from_buf) {
+    const int gr = swiglu_gate_row(min(grp + k * NGR, F - 1));
+    float a[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int ci = 0; ci < CPL; ++ci) {
+        typename O::Chunk w;
+        if constexpr (decltype(from_buf)::value >= 0) {
+          constexpr int k0 = decltype(from_buf)::value;
+          const int p = (2 * k0 + u) * CPL + ci;
+          w = p < CB ? buf[p < CB ? p : 0] : O::load(at(W, (gr + 16 * u) * K + (sub + GL * ci) * 8));
+        } else {
+          w = O::load(at(W, (gr + 16 * u) * K + (sub + GL * ci) * 8));
+        }
+        acc = O::dot(w, xr[ci], acc);
+      }
+      a[u] = group_sum<GL>(acc);
     }
-    acc = group_sum<8>(acc);
-    if (sub == 0 && r0 < N) epi(r0, acc);
+    return silu_f(a[0]) * a[1];
+  };
+  auto flush_if_full = [&](int k) {
+    if (k - base == GL) {
+      const int i = grp + (base + sub) * NGR;
+      if (i < F) store_from_f32(&out[i], mine);
+      base += GL;
+    }
+  };
+  if (KBU > 0 && npairs > 0) { flush_if_full(0); const float v = pair(0, IC<0>{}); mine = sub == 0 ? v : mine; }
+  if (KBU > 1 && npairs > 1) { flush_if_full(1); const float v = pair(1, IC<1>{}); mine = sub == 1 - base ? v : mine; }
+  if (KBU > 2 && npairs > 2) { flush_if_full(2); const float v = pair(2, IC<2>{}); mine = sub == 2 - base ? v : mine; }
+  if (KBU > 3 && npairs > 3) { flush_if_full(3); const float v = pair(3, IC<3>{}); mine = sub == 3 - base ? v : mine; }
+  for (int k = KBU < 4 ? KBU : 4; k < npairs; ++k) {
+    flush_if_full(k);
+    const float v = pair(k, IC<-1>{});
+    mine = sub == k - base ? v : mine;
+  }
+  {
+    const int i = grp + (base + sub) * NGR;
+    if (base + sub < npairs && i < F) store_from_f32(&out[i], mine);
   }
 }
 
+// Products with K = F (the FFN output product): 16 lanes per row when a 64-row product
+// would leave lanes idle and F allows it, else 8; the common chunk counts are unrolled,
+// others loop.
+template <typename Fn>
+__device__ __forceinline__ void dispatch_ffn_out(int D, int F, Fn&& fn) {
+  if (D == 64 && F % 128 == 0) {
+    switch (F / 128) {
+      case 1: fn(IC<16>{}, IC<1>{}); return;
+      case 2: fn(IC<16>{}, IC<2>{}); return;
+      case 3: fn(IC<16>{}, IC<3>{}); return;
+      case 4: fn(IC<16>{}, IC<4>{}); return;
+      default: break;
+    }
+  }
+  switch (F / 64) {
+    case 1: fn(IC<8>{}, IC<1>{}); return;
+    case 2: fn(IC<8>{}, IC<2>{}); return;
+    case 3: fn(IC<8>{}, IC<3>{}); return;
+    case 4: fn(IC<8>{}, IC<4>{}); return;
+    case 6: fn(IC<8>{}, IC<6>{}); return;
+    case 8: fn(IC<8>{}, IC<8>{}); return;
+    default: fn(IC<8>{}, IC<0>{}); return;   // generic: every chunk loaded when needed
+  }
+}
+
+// Generic K (multiple of 64), 8 lanes per row, no prefetch.
 template <typename WT, typename XF, typename Epi>
-__device__ __forceinline__ void wcompute(const WBuf<WT>& buf, const WT* __restrict__ W, int N, int K, XF&& xf,
-                                         Epi&& epi) {
-  switch (K >> 6) {
-    case 1: wcompute_c<1>(buf, W, N, xf, epi); break;
-    case 2: wcompute_c<2>(buf, W, N, xf, epi); break;
-    case 3: wcompute_c<3>(buf, W, N, xf, epi); break;
-    case 4: wcompute_c<4>(buf, W, N, xf, epi); break;
-    case 8: wcompute_c<8>(buf, W, N, xf, epi); break;
-    default: wcompute_any(W, N, K, xf, epi); break;
+__device__ __forceinline__ void wmv_any(const WT* __restrict__ W, int N, int K, XF&& xf, Epi&& epi) {
+  using O = Ops<WT>;
+  constexpr int NGR = NTM / 8;
+  const unsigned mt = mtid_here();
+  const int sub = mt & 7, grp = mt >> 3;
+  const int nrows = (N + NGR - 1) / NGR;
+  for (int ri = 0; ri < nrows; ++ri) {
+    const int r = min(grp + ri * NGR, N - 1);
+    float acc = 0.f;
+    for (int k = sub * 8; k < K; k += 64) acc = O::dot(O::load(W + static_cast<size_t>(r) * K + k), xf(k), acc);
+    acc = group_sum<8>(acc);
+    if (sub == 0 && grp + ri * NGR < N) epi(grp + ri * NGR, acc);
   }
 }
 
 // 1 / rms(y) over D values in LDS, computed by every wave on its own.
 template <int D>
 __device__ __forceinline__ float wave_rms_inv(const float* __restrict__ y, float eps) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid_here() & 63;
   float ss = 0.f;
 #pragma unroll
   for (int c = lane; c < D; c += 64) ss += y[c] * y[c];
@@ -262,57 +409,6 @@ __device__ __forceinline__ typename Ops<WT>::Chunk norm_chunk(const float* __res
   return Ops<WT>::pack(f);
 }
 
-// Inside one wave: lanes hold partial softmax states (m, l, o[16]) for the 16 dims starting
-// at dim 16*sub of one head (sub = lane % LPK).  Writes o / l (DH dims) to dst.
-// wbuf: this wave's LDS scratch of 64*17 + 64 floats.
-template <typename WT, int DH>
-__device__ __forceinline__ void wave_combine(float m, float l, float (&o)[16], float* __restrict__ wbuf,
-                                             WT* __restrict__ dst) {
-  constexpr int LPK = DH / 16;
-  constexpr int SLOTS = 64 / LPK;
-  const int lane = threadIdx.x & 63;
-  const float mw = group_max<64>(m);
-  const float f = __expf(m - mw);   // lanes without keys: m = -inf -> 0
-  float* ob = wbuf;                 // [64][17]
-  float* lb = wbuf + 64 * 17;       // [64]
-#pragma unroll
-  for (int c = 0; c < 16; ++c) ob[lane * 17 + c] = o[c] * f;
-  lb[lane] = l * f;
-  wave_sync_lds();
-  if constexpr (DH <= 64) {
-    constexpr int GS = 64 / DH;     // slot groups per dim
-    const int d = lane % DH, g = lane / DH;
-    const int sub = d / 16, c = d % 16;
-    constexpr int PER = SLOTS / GS;
-    float acc = 0.f, lacc = 0.f;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int s = g + GS * k;
-      acc += ob[(s * LPK + sub) * 17 + c];
-      lacc += lb[s * LPK];
-    }
-#pragma unroll
-    for (int off = DH; off < 64; off <<= 1) {
-      acc += __shfl_xor(acc, off, 64);
-      lacc += __shfl_xor(lacc, off, 64);
-    }
-    if (g == 0) store_from_f32(&dst[d], acc / lacc);
-  } else {
-#pragma unroll
-    for (int d = lane; d < DH; d += 64) {
-      const int sub = d / 16, c = d % 16;
-      float acc = 0.f, lacc = 0.f;
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        acc += ob[(s * LPK + sub) * 17 + c];
-        lacc += lb[s * LPK];
-      }
-      store_from_f32(&dst[d], acc / lacc);
-    }
-  }
-  wave_sync_lds();
-}
-
 struct DecSmallParams {
   const void* wgate;   // [D, 2D]
   const void* wfb;     // [D, D]
@@ -328,11 +424,52 @@ struct DecSmallParams {
   void* ring_v;
   const void* e;         // [B][T][D]
   const void* mem_k;     // [G][B][H][T][DH]
-  const void* mem_v;
+  const void* mem_v;     // [G][B][H][T8/8][DH][8]
   float* s_out;          // [B][n][D] or null
-  int B, T, t0, n, L, F, F2, Wm1, G, ffn_kind;
+  int B, T, T8, t0, n, L, F, F2, Wm1, G, ffn_kind;
   float eps;
 };
+
+// Memory row blocks (of SLOTS rows) per attention wave and chunk; weight chunks per product
+// buffer and for the gated merge (kept resident).  bf16: 4 VGPRs per chunk, fp32: 8.
+template <typename WT> constexpr int kq_of() { return sizeof(WT) == 2 ? 7 : 2; }
+template <typename WT> constexpr int cbx_of() { return sizeof(WT) == 2 ? 8 : 2; }
+template <typename WT> constexpr int cbz_of() { return sizeof(WT) == 2 ? 6 : 3; }
+constexpr unsigned al16(unsigned x) { return (x + 15u) / 16u * 16u; }
+
+// LDS plan.  The buffers whose size depends only on (storage type, D, DH) come first at
+// compile-time offsets; the gains, the operand vector and the window caches follow.
+template <int ESZ, int D, int DH, int KQ>
+struct Fixed {
+  static constexpr unsigned H = D / DH, SLOTS = 64 / (DH / 16);
+  static constexpr unsigned eb = 0;                                 // e_t
+  static constexpr unsigned sb = al16(eb + D * ESZ);                 // s_{t0-1} operand of the first step
+  static constexpr unsigned y0 = al16(sb + D * ESZ);                 // residual stream, two buffers
+  static constexpr unsigned y1 = al16(y0 + D * 4);
+  static constexpr unsigned kv = al16(y1 + D * 4);                   // current key, value
+  static constexpr unsigned qb = al16(kv + 2 * D * 4);               // query (self or cross)
+  static constexpr unsigned bg = al16(qb + D * ESZ);
+  static constexpr unsigned cpart = al16(bg + D * 4);                // cross partial states per attention wave
+  static constexpr unsigned pbuf = al16(cpart + NA * (DH + 2) * 4);  // cross weights per attention wave
+  static constexpr unsigned PSW = WCAP + 8;                         // window entries per head, padded
+  static constexpr unsigned sws = al16(pbuf + NA * KQ * SLOTS * ESZ);    // window scores per head (fp32)
+  static constexpr unsigned swp = al16(sws + H * PSW * 4);           // window weights per head
+  static constexpr unsigned end = al16(swp + H * PSW * ESZ);
+};
+struct SmemTail {
+  unsigned gains, xop, ring, total;
+};
+// Window caches in LDS: keys [L][H][Wm1][DH] (row per ring slot), values key-blocked
+// [L][H][NB][DH][8] with NB = ceil(Wm1 / 8) (slots past Wm1 stay zero).
+__host__ __device__ inline SmemTail smem_tail(unsigned fixed_end, int D, int DH, int L, int Wm1, int F, int esz) {
+  SmemTail p{};
+  const unsigned nb = (Wm1 + 7) / 8;
+  p.gains = fixed_end;                                               // self, cross, ffn per layer, final
+  p.xop = al16(p.gains + (3u * L + 1u) * D * 4u);                    // attention output, FFN activation
+  p.ring = al16(p.xop + static_cast<unsigned>(F > D ? F : D) * esz);
+  p.total = al16(p.ring + static_cast<unsigned>(L) * (D / DH) * (Wm1 + 8u * nb) * DH * esz);
+  return p;
+}
 
 template <typename WT, int D, int DH>
 __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
@@ -341,49 +478,58 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   constexpr int H = D / DH;
   constexpr int LPK = DH / 16;            // lanes per key row (16 elements each)
   constexpr int SLOTS = 64 / LPK;         // keys per wave pass
-  constexpr int KQ = sizeof(WT) == 2 ? 4 : 2;   // memory rows per lane per load batch
-  constexpr int NSC = 16;                        // scores per lane per chunk
-  static_assert(DH % 16 == 0 && DH <= 128, "head width");
+  constexpr int WPH = NA / H;             // attention waves per head
+  constexpr int KQ = kq_of<WT>();         // memory row blocks per attention wave and chunk
+  constexpr int RW = KQ * SLOTS;          // memory rows per attention wave and chunk
+  constexpr int R1 = WPH * RW;            // memory rows per chunk and head
+  constexpr int CPD = D / 64;             // chunks per lane of a K = D product (8 lanes per row)
+  constexpr int CBX = cbx_of<WT>(), CBZ = cbz_of<WT>();
+  constexpr int MGR = NTM / 8;            // 8-lane groups of the product waves
+  constexpr int MRG = D / MGR;            // merge rows per group
+  using FX = Fixed<sizeof(WT), D, DH, KQ>;
+  static_assert(DH % 16 == 0 && DH <= 128 && H <= NA && NA % H == 0, "head shape");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int slot = lane / LPK, sub = lane % LPK;
-  const int L = p.L, Wm1 = p.Wm1, T = p.T, F = p.F, F2 = p.F2, G = p.G;
-  const float scale = 1.0f / sqrtf(static_cast<float>(DH));
-  const int XOPN = 2 * D > F ? 2 * D : F;
+  const int L = p.L, Wm1 = p.Wm1, T = p.T, F = p.F;
+  const float qscale = kLog2e / sqrtf(static_cast<float>(DH));
+  const SmemTail sp = smem_tail(FX::end, D, DH, L, Wm1, F, sizeof(WT));
+  const int rpl = H * Wm1 * DH;            // key ring elements per layer (and per layer in the state)
+  const int nbw = (Wm1 + 7) / 8;           // value blocks of the ring
+  const int vpl = H * nbw * 8 * DH;        // value ring elements per layer (key-blocked)
+  WT* ringK = reinterpret_cast<WT*>(smem + sp.ring);
+  WT* ringV = ringK + L * rpl;
+  WT* xop = reinterpret_cast<WT*>(smem + sp.xop);
+  float* gains = reinterpret_cast<float*>(smem + sp.gains);
+  WT* eb = reinterpret_cast<WT*>(smem + FX::eb);
+  WT* sb = reinterpret_cast<WT*>(smem + FX::sb);
+  float* y0 = reinterpret_cast<float*>(smem + FX::y0);
+  float* y1 = reinterpret_cast<float*>(smem + FX::y1);
+  float* kv = reinterpret_cast<float*>(smem + FX::kv);
+  WT* qb = reinterpret_cast<WT*>(smem + FX::qb);
+  float* bgl = reinterpret_cast<float*>(smem + FX::bg);
+  float* sws = reinterpret_cast<float*>(smem + FX::sws);
+  WT* swp = reinterpret_cast<WT*>(smem + FX::swp);
+  WT* pbuf = reinterpret_cast<WT*>(smem + FX::pbuf);
+  float* cpart = reinterpret_cast<float*>(smem + FX::cpart);
+  const float* g_fin = gains + 3 * L * D;
 
-  // ---- LDS carve-up ----
-  WT* ringK = reinterpret_cast<WT*>(smem);                       // [L][H][Wm1][DH]
-  const size_t ring_elems = static_cast<size_t>(L) * H * Wm1 * DH;
-  WT* ringV = ringK + ring_elems;
-  unsigned char* cur = smem + ((2 * ring_elems * sizeof(WT) + 15) / 16) * 16;
-  WT* xop = reinterpret_cast<WT*>(cur);                 // operand vector [max(2D, F)]
-  cur += ((XOPN * sizeof(WT) + 15) / 16) * 16;
-  float* y = reinterpret_cast<float*>(cur);             // [D] residual stream
-  float* s_l = y + D;                                   // [D] s_t
-  float* qkv = s_l + D;                                 // [3D]
-  float* gpre = qkv + 3 * D;                            // [D]
-  float* fbv = gpre + D;                                // [D]
-  float* gains = fbv + D;                               // [(3L+1) D]: self, cross, ffn per layer, final
-  float* bgl = gains + (3 * L + 1) * D;                 // [D]
-  float* wscr = bgl + D;                                // [NWAVE][64*17 + 64] wave scratch
-  float* act_raw = wscr + NWAVE * (64 * 17 + 64);       // [F2] (SwiGLU gate/up pre-activations)
-  WT* q_hi = reinterpret_cast<WT*>(act_raw + F2);       // [D] query, storage-precision high part
-  WT* q_lo = q_hi + D;                                  // [D] low part (bf16 mode only)
-  float* my_scr = wscr + wave * (64 * 17 + 64);
-
-  // ---- carried state, gains ----
+  // ---- carried state, gains, first e ----
+  const WT* e_seq = static_cast<const WT*>(p.e) + static_cast<size_t>(b) * T * D;
   {
+    const int tid = threadIdx.x;
     const WT* gk = static_cast<const WT*>(p.ring_k);
     const WT* gv = static_cast<const WT*>(p.ring_v);
-    const size_t per_lb = static_cast<size_t>(H) * Wm1 * DH;
     for (int l = 0; l < L; ++l) {
-      const size_t src = (static_cast<size_t>(l) * p.B + b) * per_lb;
-      for (size_t i = tid; i < per_lb; i += NT) {
-        ringK[l * per_lb + i] = gk[src + i];
-        ringV[l * per_lb + i] = gv[src + i];
+      const size_t src = (static_cast<size_t>(l) * p.B + b) * rpl;
+      for (int i = tid; i < rpl; i += NT) ringK[l * rpl + i] = gk[src + i];
+      // values: state rows [H][Wm1][DH] -> key-blocked [H][NB][DH][8], padding slots zero
+      for (int i = tid; i < vpl; i += NT) {
+        const int k8 = i % 8, d = (i / 8) % DH, blk = (i / (8 * DH)) % nbw, h = i / (8 * DH * nbw);
+        const int sl = blk * 8 + k8;
+        WT v{};
+        if (sl < Wm1) v = gv[src + (h * Wm1 + sl) * DH + d];
+        ringV[l * vpl + i] = v;
       }
     }
     for (int i = tid; i < L * D; i += NT) {
@@ -394,296 +540,463 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
     for (int c = tid; c < D; c += NT) {
       gains[3 * L * D + c] = p.g_final[c];
       bgl[c] = p.bg[c];
-      const float s0 = p.s[static_cast<size_t>(b) * D + c];
-      s_l[c] = s0;
-      store_from_f32(&xop[D + c], s0);
+      store_from_f32(&sb[c], p.s[static_cast<size_t>(b) * D + c]);
     }
+    if (tid * 8 < D) O::store(eb + tid * 8, O::load(e_seq + static_cast<size_t>(p.t0) * D + tid * 8));
   }
-  const WT* e_seq = static_cast<const WT*>(p.e) + static_cast<size_t>(b) * T * D;
-  for (int c = tid * 8; c < D; c += NT * 8)
-    *reinterpret_cast<Chunk*>(xop + c) = O::load(e_seq + static_cast<size_t>(p.t0) * D + c);
   const WT* wgate = static_cast<const WT*>(p.wgate);
   const WT* wfb = static_cast<const WT*>(p.wfb);
   auto layer_w = [&](int l, size_t off) {
     return reinterpret_cast<const WT*>(p.layers + static_cast<size_t>(l) * p.layer_stride + off);
   };
+  auto is_attn = [&]() { return __builtin_amdgcn_readfirstlane(tid_here() >> 6) < NA; };
 
-  WBuf<WT> wa, wb;
-  wprefetch(wa, wgate, D, 2 * D);
-  wprefetch(wb, wfb, D, D);
-  __syncthreads();
-
-  auto xf_op = [&](const WT* v) { return [=](int k) { return O::load(v + k); }; };
-  // query element r (pre-scaled): fp32 copy and, in bf16 mode, its hi/lo split
-  auto put_q = [&](int r, float v) {
-    qkv[r] = v;
-    store_from_f32(&q_hi[r], v);
-    store_from_f32(&q_lo[r], v - round_to<WT>(v));
-  };
-
-  for (int step = 0; step < p.n; ++step) {
-    const int t = p.t0 + step;   // 0-based position of this transition
-    Chunk e_next = O::zero();
-    const bool has_next = step + 1 < p.n;
-    if (has_next && tid * 8 < D) e_next = O::load(e_seq + static_cast<size_t>(t + 1) * D + tid * 8);
-
-    // ---- gated merge: xop = [e_t ; bf16(s_{t-1})] ----
-    wcompute(wa, wgate, D, 2 * D, xf_op(xop), [&](int r, float v) { gpre[r] = v + bgl[r]; });
-    wcompute(wb, wfb, D, D, xf_op(xop + D), [&](int r, float v) { fbv[r] = v; });
-    wprefetch(wa, layer_w(0, p.l_qkv), 3 * D, D);
-    wprefetch(wb, layer_w(0, p.l_wo), D, D);
+  // The two roles run their own step loops; both pass the same sequence of workgroup
+  // barriers (one per phase: merge, then P1..P9 per layer), so each role's registers are
+  // allocated for its own work only.
+  if (is_attn()) {
+    // ======== attention waves: memory rows (key rows R[2i + c], value items
+    // R[2KQ + 2i + r] of block i), window attention, cross-attention ========
+    Chunk R[4 * KQ];
+    // Attention wave w takes head w % H and share w / H of the rows of a chunk: rows
+    // c0 + share*RW + i*SLOTS + slot (i < KQ) for the scores, and for the P.V pass the
+    // value items (dim, 8-key block) lane + 64r of each block of SLOTS rows.  A wave whose
+    // first row lies past the position has nothing to do.
+    auto mem_load = [&](int l, int tpos, int c0, auto i0c, auto i1c) {
+      constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
+      const unsigned tid = tid_here();
+      const int lane = tid & 63;
+      const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int mh = wave % H, mpart = wave / H;
+      const int jw = c0 + mpart * RW;   // first row of the wave (uniform)
+      if (jw > tpos) return;
+      const int mslot = lane / LPK, msub = lane % LPK;
+      const int g = p.G == 1 ? 0 : l;
+      const WT* kb = static_cast<const WT*>(p.mem_k) + ((static_cast<size_t>(g) * p.B + b) * H + mh) *
+                                                          static_cast<size_t>(T) * DH;
+      const WT* vb = static_cast<const WT*>(p.mem_v) + ((static_cast<size_t>(g) * p.B + b) * H + mh) *
+                                                          static_cast<size_t>(p.T8) * DH;
+      const int nb8 = p.T8 / 8;
+#pragma unroll
+      for (int i = I0; i < I1; ++i) {
+        const int jb = jw + i * SLOTS;
+        const int j = min(jb + mslot, tpos);   // rows past the position are loaded but masked
+        R[2 * i] = O::load(at(kb, j * DH + msub * 16));
+        R[2 * i + 1] = O::load(at(kb, j * DH + msub * 16 + 8));
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int it = lane + 64 * r, d = it % DH, blk = it / DH;
+          const int bi = min(jb / 8 + blk, nb8 - 1);
+          R[2 * KQ + 2 * i + r] = O::load(at(vb, (bi * DH + d) * 8));
+        }
+      }
+    };
+    // rows of the next (layer, position), requested over the four phases after the cross-
+    // attention (blocks [I0, I1) in each) so the requests drain while the products run
+    auto next_rows = [&](int l, int t, bool has_next, auto i0c, auto i1c) {
+      if (l + 1 < L) mem_load(l + 1, t, 0, i0c, i1c);
+      else if (has_next) mem_load(0, t + 1, 0, i0c, i1c);
+    };
+    constexpr int QB = (KQ + 3) / 4;
+    constexpr int B1 = QB < KQ ? QB : KQ, B2 = 2 * QB < KQ ? 2 * QB : KQ, B3 = 3 * QB < KQ ? 3 * QB : KQ;
+    mem_load(0, p.t0, 0, IC<0>{}, IC<KQ>{});
     __syncthreads();
-    for (int c = tid; c < D; c += NT) {
-      const float g = sigmoid_f(gpre[c]);
-      y[c] = g * load_as_f32(xop + c) + (1.0f - g) * fbv[c];
-    }
-    __syncthreads();
+    for (int step = 0; step < p.n; ++step) {
+      const int t = p.t0 + step;
+      const bool has_next = step + 1 < p.n;
+      __syncthreads();   // merge
+      for (int l = 0; l < L; ++l) {
+        WT* rK = ringK + l * rpl;
+        WT* rV = ringV + l * vpl;
+        const bool last = l + 1 == L;
+        __syncthreads();   // P1
 
-    for (int l = 0; l < L; ++l) {
-      const float* g_self = gains + l * D;
-      const float* g_cross = gains + (L + l) * D;
-      const float* g_ffn = gains + (2 * L + l) * D;
-      WT* rK = ringK + static_cast<size_t>(l) * H * Wm1 * DH;
-      WT* rV = ringV + static_cast<size_t>(l) * H * Wm1 * DH;
-
-      // ---- P1: q,k,v = W_{Q,K,V} RMS(y; g_self); q pre-scaled by 1/sqrt(d_h) ----
-      {
-        const float inv = wave_rms_inv<D>(y, p.eps);
-        wcompute(wa, layer_w(l, p.l_qkv), 3 * D, D, [&](int k) { return norm_chunk<WT>(y, g_self, inv, k); },
-                 [&](int r, float v) {
-                   if (r < D) put_q(r, v * scale);
-                   else qkv[r] = round_to<WT>(v);
-                 });
-        wprefetch(wa, layer_w(l, p.l_wqx), D, D);
-      }
-      __syncthreads();
-
-      // ---- P2: window self-attention, one head per wave, lanes over window entries ----
-      const int npast = min(t, Wm1);        // cached entries in the window
-      const int ne = npast + 1;             // plus the current token
-      const int slot0 = Wm1 > 0 ? (t - npast) % Wm1 : 0;   // ring slot of the oldest entry
-      for (int h = wave; h < H; h += NWAVE) {
-        QSlice<WT> qs;
-        qs.set(qkv + h * DH + sub * 16, q_hi + h * DH + sub * 16, q_lo + h * DH + sub * 16);
-        float m = -INFINITY, lsum = 0.f;
-        float o[16];
+        // ---- P2: window self-attention, attention wave h for head h.  Scores with lanes
+        //      over entries (ring slots 0..8*NB-1, valid below npast, then the current
+        //      entry), weights exp2(s - max), P.V with lanes over (dim, 8-slot block). ----
+        {
+          const unsigned tid = tid_here();
+          const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
+          if (h < H) {
+            const int lane = tid & 63;
+            const int slot = lane / LPK, sub = lane % LPK;
+            const int npast = min(t, Wm1);        // cached entries in the window (slots 0..npast-1)
+            const int ecur = nbw * 8;             // entry index of the current token
+            float* ps = sws + h * FX::PSW;
+            WT* pw = swp + h * FX::PSW;
+            QVec<WT> q;
+            q.load(qb + h * DH + sub * 16);
+            auto score = [&](int e) {
+              Chunk k0, k1;
+              if (e < ecur) {
+                const WT* kr = rK + (h * Wm1 + min(e, Wm1 - 1)) * DH + sub * 16;   // padding slots: masked
+                k0 = O::load(kr);
+                k1 = O::load(kr + 8);
+              } else {
+                // the current entry (values already rounded to the storage precision)
+                float kf[8];
+                const float* kq = kv + h * DH + sub * 16;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) o[c] = 0.f;
-        for (int i0 = 0; i0 < ne; i0 += SLOTS) {
-          const int i = i0 + slot;
-          const bool ok = i < ne;
-          Chunk k0, k1, v0, v1;
-          if (i < npast) {
-            int sl = slot0 + i;
-            sl = sl >= Wm1 ? sl - Wm1 : sl;
-            const WT* kr = rK + (static_cast<size_t>(h) * Wm1 + sl) * DH + sub * 16;
-            const WT* vr = rV + (static_cast<size_t>(h) * Wm1 + sl) * DH + sub * 16;
-            k0 = O::load(kr); k1 = O::load(kr + 8); v0 = O::load(vr); v1 = O::load(vr + 8);
-          } else {
-            // the current entry (values already rounded to the storage precision)
-            float kf[8], vf[8];
-            const float* kq = qkv + D + h * DH + sub * 16;
+                for (int c = 0; c < 8; ++c) kf[c] = kq[c];
+                k0 = O::pack(kf);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) { kf[c] = kq[c]; vf[c] = kq[D + c]; }
-            k0 = O::pack(kf); v0 = O::pack(vf);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) { kf[c] = kq[8 + c]; vf[c] = kq[D + 8 + c]; }
-            k1 = O::pack(kf); v1 = O::pack(vf);
-          }
-          float s = qs.dot(k0, k1);
-          if constexpr (LPK > 1) s = group_sum<LPK>(s);
-          s = ok ? s : -INFINITY;
-          const float mnew = fmaxf(m, s);
-          const float corr = m == mnew ? 1.f : __expf(m - mnew);   // m = mnew = -inf: nothing seen yet
-          const float w = ok ? __expf(s - mnew) : 0.f;
-          lsum = lsum * corr + w;
-#pragma unroll
-          for (int c = 0; c < 16; ++c) o[c] *= corr;
-          axpy16<WT>(o, w, v0, v1);
-          m = mnew;
-        }
-        wave_combine<WT, DH>(m, lsum, o, my_scr, xop + h * DH);
-        // the current entry replaces the oldest one (position t - (W-1))
-        if (Wm1 > 0) {
-          const int sl = t % Wm1;
-          const size_t gbase = (static_cast<size_t>(l) * p.B + b) * H * Wm1 * DH;
-          for (int c = lane; c < DH; c += 64) {
-            const size_t o_ = (static_cast<size_t>(h) * Wm1 + sl) * DH + c;
-            WT kq, vq;
-            store_from_f32(&kq, qkv[D + h * DH + c]);
-            store_from_f32(&vq, qkv[2 * D + h * DH + c]);
-            rK[o_] = kq;
-            rV[o_] = vq;
-            static_cast<WT*>(p.ring_k)[gbase + o_] = kq;
-            static_cast<WT*>(p.ring_v)[gbase + o_] = vq;
-          }
-        }
-      }
-      __syncthreads();
-
-      // ---- P3: y += W_O attn; the first key batch of this layer's memory is issued here ----
-      const int grp_l = G == 1 ? 0 : l;
-      const size_t mrow0 = (static_cast<size_t>(grp_l) * p.B + b) * H * static_cast<size_t>(T) * DH * sizeof(WT);
-      const char* mkb = static_cast<const char*>(p.mem_k) + mrow0;
-      const char* mvb = static_cast<const char*>(p.mem_v) + mrow0;
-      // lane byte offset of key row j of head hh: ((hh*T + j)*DH + 16*sub) * sizeof(WT)
-      auto row_off = [&](int hh, int j) {
-        return static_cast<uint32_t>(((hh * T + j) * DH + sub * 16) * sizeof(WT));
-      };
-      // rows j = base + SLOTS*i (i < KQ), clamped to t (clamped rows are masked out later)
-      auto load_rows = [&](const char* mb, int hh, int base, Chunk (&x)[KQ][2]) {
-#pragma unroll
-        for (int i = 0; i < KQ; ++i) {
-          const uint32_t off = row_off(hh, min(base + SLOTS * i, t));
-          x[i][0] = O::load(reinterpret_cast<const WT*>(mb + off));
-          x[i][1] = O::load(reinterpret_cast<const WT*>(mb + off) + 8);
-        }
-      };
-      Chunk kq0[KQ][2];
-      const int h0 = wave < H ? wave : 0;
-      load_rows(mkb, h0, slot, kq0);
-      wcompute(wb, layer_w(l, p.l_wo), D, D, xf_op(xop), [&](int r, float v) { y[r] += v; });
-      wprefetch(wb, layer_w(l, p.l_wox), D, D);
-      __syncthreads();
-
-      // ---- P4: q_x = W_Qx RMS(y; g_cross) (pre-scaled by 1/sqrt(d_h)); first value batch ----
-      Chunk vq0[KQ][2];
-      load_rows(mvb, h0, slot, vq0);
-      {
-        const float inv = wave_rms_inv<D>(y, p.eps);
-        wcompute(wa, layer_w(l, p.l_wqx), D, D, [&](int k) { return norm_chunk<WT>(y, g_cross, inv, k); },
-                 [&](int r, float v) { put_q(r, v * scale); });
-        wprefetch(wa, layer_w(l, p.l_fin), F2, D);
-      }
-      __syncthreads();
-
-      // ---- P5: cross-attention over memory rows 0..t, one head per wave ----
-      // Keys are taken in chunks of NSC*SLOTS rows.  Per chunk: pass 1 computes every score of
-      // the lane into registers (K rows in batches of KQ, the next batch in flight while the
-      // current one is used); pass 2 streams the V rows and accumulates exp(s - m) v.  The
-      // running (m, l, o) is rescaled once per chunk.
-      for (int h = wave; h < H; h += NWAVE) {
-        QSlice<WT> qs;
-        qs.set(qkv + h * DH + sub * 16, q_hi + h * DH + sub * 16, q_lo + h * DH + sub * 16);
-        float m = -INFINITY, lsum = 0.f;
-        float o[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) o[c] = 0.f;
-        const bool first_head = h == wave;
-        for (int c0 = 0; c0 <= t; c0 += NSC * SLOTS) {
-          const int cb = c0 + slot;                 // this lane's first row in the chunk
-          float sc[NSC];
-          float cmax = -INFINITY;
-          // two load buffers used alternately by the unrolled batch sequence (no copies)
-          Chunk xa[KQ][2], xb[KQ][2];
-          if (first_head && c0 == 0) {
-#pragma unroll
-            for (int i = 0; i < KQ; ++i) { xa[i][0] = kq0[i][0]; xa[i][1] = kq0[i][1]; }
-          } else {
-            load_rows(mkb, h, cb, xa);
-          }
-#pragma unroll
-          for (int q0 = 0; q0 < NSC; q0 += KQ) {
-            if (c0 + SLOTS * q0 > t) break;         // uniform: no row of this batch exists
-            Chunk (&cur)[KQ][2] = ((q0 / KQ) & 1) ? xb : xa;
-            Chunk (&nxt)[KQ][2] = ((q0 / KQ) & 1) ? xa : xb;
-            if (q0 + KQ < NSC && c0 + SLOTS * (q0 + KQ) <= t) load_rows(mkb, h, cb + SLOTS * (q0 + KQ), nxt);
-#pragma unroll
-            for (int i = 0; i < KQ; ++i) {
-              float a = qs.dot(cur[i][0], cur[i][1]);
-              if constexpr (LPK > 1) a = group_sum<LPK>(a);
-              a = cb + SLOTS * (q0 + i) <= t ? a : -INFINITY;
-              sc[q0 + i] = a;
-              cmax = fmaxf(cmax, a);
+                for (int c = 0; c < 8; ++c) kf[c] = kq[8 + c];
+                k1 = O::pack(kf);
+              }
+              float sc = q.dot(k0, k1);
+              if constexpr (LPK > 1) sc = group_sum<LPK>(sc);
+              return (e < npast || e == ecur) ? sc : -INFINITY;
+            };
+            float ls = 0.f;
+            if (ecur < SLOTS) {
+              // one pass: every entry's score stays in its lane
+              const int e = slot;
+              const float sc = score(e);
+              const float M = group_max<64>(sc);   // finite: the current entry is always present
+              const float pr = round_to<WT>(fast_exp2(sc - M));
+              if (sub == 0 && e <= ecur) {
+                store_from_f32(&pw[e], pr);
+                ls = pr;
+              }
+            } else {
+              float mloc = -INFINITY;
+              for (int e0 = 0; e0 <= ecur; e0 += SLOTS) {
+                const int e = e0 + slot;
+                const float sc = score(e);
+                if (sub == 0 && e <= ecur) ps[e] = sc;
+                mloc = fmaxf(mloc, sc);
+              }
+              const float M = group_max<64>(mloc);
+              wave_sync_lds();
+              for (int e = lane; e <= ecur; e += 64) {
+                const float pr = round_to<WT>(fast_exp2(ps[e] - M));
+                store_from_f32(&pw[e], pr);
+                ls += pr;
+              }
             }
-          }
-          const float mnew = fmaxf(m, cmax);
-          const float corr = m == mnew ? 1.f : __expf(m - mnew);
-          lsum *= corr;
+            ls = group_sum<64>(ls);
+            wave_sync_lds();
+            float oa = 0.f, ob = 0.f;
+            for (int r = 0; lane + 64 * r < DH * nbw; ++r) {
+              const int it = lane + 64 * r, d = it % DH, blk = it / DH;
+              const Chunk pp = O::load(pw + blk * 8);
+              const Chunk vv = O::load(rV + ((h * nbw + blk) * DH + d) * 8);
+              if (DH < 128 || (r & 1) == 0) oa = O::dot(pp, vv, oa);
+              else ob = O::dot(pp, vv, ob);
+            }
 #pragma unroll
-          for (int c = 0; c < 16; ++c) o[c] *= corr;
-          m = mnew;
-          const float mref = m == -INFINITY ? 0.f : m;   // lane without rows: every exp(-inf - 0) = 0
-          if (first_head && c0 == 0) {
-#pragma unroll
-            for (int i = 0; i < KQ; ++i) { xa[i][0] = vq0[i][0]; xa[i][1] = vq0[i][1]; }
-          } else {
-            load_rows(mvb, h, cb, xa);
-          }
-#pragma unroll
-          for (int q0 = 0; q0 < NSC; q0 += KQ) {
-            if (c0 + SLOTS * q0 > t) break;
-            Chunk (&cur)[KQ][2] = ((q0 / KQ) & 1) ? xb : xa;
-            Chunk (&nxt)[KQ][2] = ((q0 / KQ) & 1) ? xa : xb;
-            if (q0 + KQ < NSC && c0 + SLOTS * (q0 + KQ) <= t) load_rows(mvb, h, cb + SLOTS * (q0 + KQ), nxt);
-#pragma unroll
-            for (int i = 0; i < KQ; ++i) {
-              const float w = __expf(sc[q0 + i] - mref);   // masked rows: exp(-inf) = 0
-              lsum += w;
-              axpy16<WT>(o, w, cur[i][0], cur[i][1]);
+            for (int off = DH; off < 64; off <<= 1) oa += __shfl_xor(oa, off, 64);
+            const float pc = load_as_f32(pw + ecur);
+            if (lane < DH) {
+              store_from_f32(&xop[h * DH + lane], (oa + pc * kv[D + h * DH + lane]) / ls);
+              if (DH == 128) store_from_f32(&xop[h * DH + 64 + lane], (ob + pc * kv[D + h * DH + 64 + lane]) / ls);
+            }
+            // the current entry replaces the oldest one (position t - (W-1)); all reads are done
+            if (Wm1 > 0) {
+              const int sl = t % Wm1;
+              for (int c = lane; c < DH; c += 64) {
+                store_from_f32(&rK[(h * Wm1 + sl) * DH + c], kv[h * DH + c]);
+                store_from_f32(&rV[((h * nbw + sl / 8) * DH + c) * 8 + sl % 8], kv[D + h * DH + c]);
+              }
             }
           }
         }
-        wave_combine<WT, DH>(m, lsum, o, my_scr, xop + h * DH);
-      }
-      __syncthreads();
+        __syncthreads();   // P2
+        __syncthreads();   // P3
+        __syncthreads();   // P4
 
-      // ---- P7: y += W_Ox attn ----
-      wcompute(wb, layer_w(l, p.l_wox), D, D, xf_op(xop), [&](int r, float v) { y[r] += v; });
-      wprefetch(wb, layer_w(l, p.l_fout), D, F);
-      __syncthreads();
-
-      // ---- P8/P9: FFN (tied with encoder layer l) ----
-      const bool last = l + 1 == L;
-      {
-        const float inv = wave_rms_inv<D>(y, p.eps);
-        auto xf = [&](int k) { return norm_chunk<WT>(y, g_ffn, inv, k); };
-        if (p.ffn_kind == RLT_FFN_GELU) {
-          wcompute(wa, layer_w(l, p.l_fin), F, D, xf,
-                   [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); });
-        } else {
-          wcompute(wa, layer_w(l, p.l_fin), F2, D, xf, [&](int r, float v) { act_raw[r] = v; });
+        // ---- P5: cross-attention over memory rows 0..t, then the rows of the next layer
+        //      (or of the next step's first layer) ----
+        {
+          const unsigned tid = tid_here();
+          const int lane = tid & 63;
+          const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+          const int mh = wave % H, mpart = wave / H;
+          const int slot = lane / LPK, sub = lane % LPK;
+          float m = -INFINITY, lsum = 0.f, oa = 0.f, ob = 0.f;
+          WT* pw = pbuf + wave * KQ * SLOTS;
+          if (mpart * RW <= t) {
+            QVec<WT> q;
+            q.load(qb + mh * DH + sub * 16);
+            for (int c0 = 0; c0 <= t; c0 += R1) {
+              const int jw = c0 + mpart * RW;
+              if (jw > t) break;                   // no row of this wave in the chunk (uniform)
+              if (c0 > 0) mem_load(l, t, c0, IC<0>{}, IC<KQ>{});
+              float s[KQ];
+              float cm = -INFINITY;
+#pragma unroll
+              for (int i = 0; i < KQ; ++i) {
+                const int j = jw + i * SLOTS + slot;
+                float a = -INFINITY;
+                if (jw + i * SLOTS <= t) {         // uniform: the block has a row
+                  a = q.dot(R[2 * i], R[2 * i + 1]);
+                  if constexpr (LPK > 1) a = group_sum<LPK>(a);
+                  a = j <= t ? a : -INFINITY;
+                }
+                s[i] = a;
+                cm = fmaxf(cm, a);
+              }
+              cm = group_max<64>(cm);              // finite: row jw <= t is here
+              const float mn = fmaxf(m, cm);
+              const float corr = fast_exp2(m - mn);  // first chunk: m = -inf -> 0 (o, l are 0)
+              lsum *= corr;
+              oa *= corr;
+              ob *= corr;
+              m = mn;
+              // blocks past the position are skipped; when every block of the wave has rows
+              // the loops run without branches so the LDS reads can be issued together
+              const bool full = jw + (KQ - 1) * SLOTS <= t;   // uniform
+              auto pv_blocks = [&](auto fullc) {
+#pragma unroll
+                for (int i = 0; i < KQ; ++i) {
+                  if (!decltype(fullc)::value && jw + i * SLOTS > t) break;   // uniform
+                  const float pr = round_to<WT>(fast_exp2(s[i] - m));   // masked rows: 0
+                  if (sub == 0) {
+                    store_from_f32(&pw[i * SLOTS + slot], pr);
+                    lsum += pr;
+                  }
+                }
+                wave_sync_lds();
+#pragma unroll
+                for (int i = 0; i < KQ; ++i) {
+                  if (!decltype(fullc)::value && jw + i * SLOTS > t) break;   // uniform
+#pragma unroll
+                  for (int r = 0; r < 2; ++r) {
+                    const int blk = (lane + 64 * r) / DH;
+                    const Chunk pp = O::load(pw + i * SLOTS + blk * 8);
+                    if (DH < 128 || r == 0) oa = O::dot(pp, R[2 * KQ + 2 * i + r], oa);
+                    else ob = O::dot(pp, R[2 * KQ + 2 * i + r], ob);
+                  }
+                }
+                wave_sync_lds();
+              };
+              if (full) pv_blocks(std::true_type{});
+              else pv_blocks(std::false_type{});
+            }
+            // lanes with the same dim hold different key blocks: sum them
+#pragma unroll
+            for (int off = DH; off < 64; off <<= 1) oa += __shfl_xor(oa, off, 64);
+            lsum = group_sum<64>(lsum);
+          }
+          float* cp = cpart + wave * (DH + 2);
+          if (lane < DH) cp[2 + lane] = oa;
+          if (DH == 128) cp[2 + 64 + lane] = ob;
+          if (lane == 0) {
+            cp[0] = m;
+            cp[1] = lsum;
+          }
         }
-        if (last) wprefetch(wa, wgate, D, 2 * D);
-        else wprefetch(wa, layer_w(l + 1, p.l_qkv), 3 * D, D);
-      }
-      __syncthreads();
-      if (p.ffn_kind != RLT_FFN_GELU) {
-        for (int i = tid; i < F; i += NT) {
-          const int gr = (i / 16) * 32 + i % 16;
-          store_from_f32(&xop[i], silu_f(act_raw[gr]) * act_raw[gr + 16]);
-        }
-        __syncthreads();
-      }
-      wcompute(wb, layer_w(l, p.l_fout), D, F, xf_op(xop), [&](int r, float v) { y[r] += v; });
-      if (last) wprefetch(wb, wfb, D, D);
-      else wprefetch(wb, layer_w(l + 1, p.l_wo), D, D);
-      __syncthreads();
-    }
+        __syncthreads();   // P5
 
-    // ---- s_t = RMSNorm(y; g_dec_final); next merge operand [e_{t+1}; bf16(s_t)] ----
-    {
-      const float inv = wave_rms_inv<D>(y, p.eps);
-      const float* g_fin = gains + 3 * L * D;
-      for (int c = tid; c < D; c += NT) {
-        const float v = g_fin[c] * (y[c] * inv);
-        s_l[c] = v;
-        store_from_f32(&xop[D + c], v);
-        if (p.s_out) p.s_out[(static_cast<size_t>(b) * p.n + step) * D + c] = v;
+        // ---- P6: combine the WPH partial states of each head (fixed order) ----
+        {
+          const unsigned tid = tid_here();
+          if (tid < static_cast<unsigned>(D)) {
+            const int h = tid / DH, d = tid % DH;
+            float M = -INFINITY;
+#pragma unroll
+            for (int q = 0; q < WPH; ++q) M = fmaxf(M, cpart[(h + H * q) * (DH + 2)]);
+            float lt = 0.f, ot = 0.f;
+#pragma unroll
+            for (int q = 0; q < WPH; ++q) {
+              const float* cp = cpart + (h + H * q) * (DH + 2);
+              const float w = fast_exp2(cp[0] - M);   // wave without rows: m = -inf -> 0
+              lt += w * cp[1];
+              ot += w * cp[2 + d];
+            }
+            store_from_f32(&xop[tid], ot / lt);
+          }
+        }
+        next_rows(l, t, has_next, IC<0>{}, IC<B1>{});
+        __syncthreads();   // P6
+        next_rows(l, t, has_next, IC<B1>{}, IC<B2>{});
+        __syncthreads();   // P7
+        next_rows(l, t, has_next, IC<B2>{}, IC<B3>{});
+        __syncthreads();   // P8
+        next_rows(l, t, has_next, IC<B3>{}, IC<KQ>{});
+        __syncthreads();   // P9
       }
-      if (has_next && tid * 8 < D) *reinterpret_cast<Chunk*>(xop + tid * 8) = e_next;
     }
+  } else {
+    // ======== product waves: the gated merge and every matrix-vector product ========
+    Chunk X[CBX], Y[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: O, Ox, FFN out; Z: merge (resident)
+    auto merge_chunk = [&](int ri, int q) {
+      const unsigned mt = mtid_here();
+      const int sub = mt & 7, grp = mt >> 3;
+      const int r = min(grp + ri * MGR, D - 1);   // rows past D (buffer slots beyond the merge): any row
+      return q < 2 * CPD ? O::load(at(wgate, r * 2 * D + (sub + 8 * q) * 8))
+                         : O::load(at(wfb, r * D + (sub + 8 * (q - 2 * CPD)) * 8));
+    };
+#pragma unroll
+    for (int pp = 0; pp < CBZ; ++pp) Z[pp] = merge_chunk(pp / (3 * CPD), pp % (3 * CPD));
+    wpre<WT, 8, CPD, CBX>(X, layer_w(0, p.l_qkv), 3 * D);
+    wpre<WT, 8, CPD, CBX>(Y, layer_w(0, p.l_wo), D);
     __syncthreads();
+    for (int step = 0; step < p.n; ++step) {
+      const int t = p.t0 + step;
+      const bool has_next = step + 1 < p.n;
+      float* y = (step & 1) ? y0 : y1;
+      float* yprev = (step & 1) ? y1 : y0;
+      Chunk e_next = O::zero();
+
+      // ---- gated merge: y = g * e_t + (1 - g) * W_fb s_{t-1},
+      //      g = sigmoid(W_gate [e_t; s_{t-1}] + b_g), s_{t-1} = RMS(y_prev; g_final) ----
+      {
+        const unsigned mt = mtid_here();
+        if (has_next && mt * 8 < D) e_next = O::load(at(e_seq, (t + 1) * D + mt * 8));
+        const float inv = step > 0 ? wave_rms_inv<D>(yprev, p.eps) : 0.f;
+        if (step > 0 && mt < D && p.s_out)
+          p.s_out[(static_cast<size_t>(b) * p.n + step - 1) * D + mt] = g_fin[mt] * (yprev[mt] * inv);
+        const int sub = mt & 7, grp = mt >> 3;
+        auto sop = [&](int k) { return step > 0 ? norm_chunk<WT>(yprev, g_fin, inv, k) : O::load(sb + k); };
+        Chunk xg[2 * CPD];
+#pragma unroll
+        for (int ci = 0; ci < 2 * CPD; ++ci) {
+          const int k = (sub + 8 * ci) * 8;
+          xg[ci] = ci < CPD ? O::load(eb + k) : sop(k - D);
+        }
+        float mine = 0.f;
+#pragma unroll
+        for (int ri = 0; ri < MRG; ++ri) {
+          float gs = 0.f, fs = 0.f;
+#pragma unroll
+          for (int q = 0; q < 3 * CPD; ++q) {
+            const int pp = ri * 3 * CPD + q;
+            const Chunk w = pp < CBZ ? Z[pp < CBZ ? pp : 0] : merge_chunk(ri, q);
+            if (q < 2 * CPD) gs = O::dot(w, xg[q], gs);
+            else fs = O::dot(w, xg[CPD + q - 2 * CPD], fs);
+          }
+          gs = group_sum<8>(gs);
+          fs = group_sum<8>(fs);
+          const int r = grp + ri * MGR;
+          const float g = sigmoid_f(gs + bgl[r]);
+          const float v = g * load_as_f32(eb + r) + (1.0f - g) * fs;
+          mine = sub == ri ? v : mine;
+        }
+        if (sub < MRG) y[grp + sub * MGR] = mine;
+      }
+      __syncthreads();   // merge
+
+      for (int l = 0; l < L; ++l) {
+        const float* g_self = gains + l * D;
+        const float* g_cross = gains + (L + l) * D;
+        const float* g_ffn = gains + (2 * L + l) * D;
+        const bool last = l + 1 == L;
+
+        // ---- P1: q, k, v = W_{Q,K,V} RMS(y; g_self); q scaled by log2(e)/sqrt(d_h) ----
+        {
+          const float inv = wave_rms_inv<D>(y, p.eps);
+          wmv<WT, 8, CPD, CBX>(X, layer_w(l, p.l_qkv), 3 * D,
+                               [&](int k) { return norm_chunk<WT>(y, g_self, inv, k); },
+                               [&](int r, float v) {
+                                 if (r < D) store_from_f32(&qb[r], v * qscale);
+                                 else kv[r - D] = round_to<WT>(v);
+                               });
+          wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D);
+          const unsigned mt = mtid_here();
+          if (l == 0 && has_next && mt * 8 < D) O::store(eb + mt * 8, e_next);
+        }
+        __syncthreads();   // P1
+        __syncthreads();   // P2
+
+        // ---- P3: y += W_O attn ----
+        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wo), D, [&](int k) { return O::load(xop + k); },
+                             [&](int r, float v) { y[r] += v; });
+        wpre<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D);
+        __syncthreads();   // P3
+
+        // ---- P4: q_x = W_Qx RMS(y; g_cross), scaled like q ----
+        {
+          const float inv = wave_rms_inv<D>(y, p.eps);
+          wmv<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D, [&](int k) { return norm_chunk<WT>(y, g_cross, inv, k); },
+                               [&](int r, float v) { store_from_f32(&qb[r], v * qscale); });
+          if (p.ffn_kind == RLT_FFN_GELU) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F);
+          else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F);
+        }
+        __syncthreads();   // P4
+        __syncthreads();   // P5
+        __syncthreads();   // P6
+
+        // ---- P7: y += W_Ox attn ----
+        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, [&](int k) { return O::load(xop + k); },
+                             [&](int r, float v) { y[r] += v; });
+        dispatch_ffn_out(D, F, [&](auto glc, auto cplc) {
+          constexpr int GL = decltype(glc)::value, CPL = decltype(cplc)::value;
+          if constexpr (CPL > 0) wpre<WT, GL, CPL, CBX>(Y, layer_w(l, p.l_fout), D);
+        });
+        __syncthreads();   // P7
+
+        // ---- P8: FFN input product (tied with encoder layer l), activation into xop ----
+        {
+          const float inv = wave_rms_inv<D>(y, p.eps);
+          auto xf = [&](int k) { return norm_chunk<WT>(y, g_ffn, inv, k); };
+          if (p.ffn_kind == RLT_FFN_GELU) {
+            wmv<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf,
+                                 [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); });
+          } else {
+            wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf, xop);
+          }
+          wpre<WT, 8, CPD, CBX>(X, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
+        }
+        __syncthreads();   // P8
+
+        // ---- P9: y += W_2 act ----
+        dispatch_ffn_out(D, F, [&](auto glc, auto cplc) {
+          constexpr int GL = decltype(glc)::value, CPL = decltype(cplc)::value;
+          auto xf = [&](int k) { return O::load(xop + k); };
+          auto epi = [&](int r, float v) { y[r] += v; };
+          if constexpr (CPL > 0) wmv<WT, GL, CPL, CBX>(Y, layer_w(l, p.l_fout), D, xf, epi);
+          else wmv_any(layer_w(l, p.l_fout), D, F, xf, epi);
+        });
+        wpre<WT, 8, CPD, CBX>(Y, layer_w(last ? 0 : l + 1, p.l_wo), D);
+        __syncthreads();   // P9
+        (void)t;
+      }
+    }
   }
-  for (int c = tid; c < D; c += NT) p.s[static_cast<size_t>(b) * D + c] = s_l[c];
+
+  // ---- s of the last step; window caches back to the state ----
+  {
+    const int tid = threadIdx.x;
+    const float* yl = ((p.n - 1) & 1) ? y0 : y1;
+    const float inv = wave_rms_inv<D>(yl, p.eps);
+    if (tid < D) {
+      const float v = g_fin[tid] * (yl[tid] * inv);
+      if (p.s_out) p.s_out[(static_cast<size_t>(b) * p.n + p.n - 1) * D + tid] = v;
+      p.s[static_cast<size_t>(b) * D + tid] = v;
+    }
+    WT* gk = static_cast<WT*>(p.ring_k);
+    WT* gv = static_cast<WT*>(p.ring_v);
+    for (int l = 0; l < L; ++l) {
+      const size_t dst = (static_cast<size_t>(l) * p.B + b) * rpl;
+      for (int i = tid; i < rpl; i += NT) {
+        const int d = i % DH, sl = (i / DH) % Wm1, h = i / (DH * Wm1);
+        gk[dst + i] = ringK[l * rpl + i];
+        gv[dst + i] = ringV[l * vpl + ((h * nbw + sl / 8) * DH + d) * 8 + sl % 8];
+      }
+    }
+  }
+}
+
+template <typename WT, int D, int DH>
+size_t lds_bytes_t(const ModelLayout& m) {
+  using FX = Fixed<sizeof(WT), D, DH, kq_of<WT>()>;
+  return smem_tail(FX::end, D, DH, m.L, m.W - 1, m.F, static_cast<int>(sizeof(WT))).total;
 }
 
 size_t lds_bytes(const ModelLayout& m) {
-  const size_t H = m.H, DH = m.DH, D = m.D, L = m.L;
-  const size_t ring = 2 * L * H * (m.W - 1) * DH * m.esz;
-  const size_t xopn = 2 * D > static_cast<size_t>(m.F) ? 2 * D : m.F;
-  const size_t floats = D + D + 3 * D + D + D + (3 * L + 1) * D + D + NWAVE * (64 * 17 + 64) + m.F2;
-  return (ring + 15) / 16 * 16 + (xopn * m.esz + 15) / 16 * 16 + floats * 4 + 2 * D * m.esz;
+  const bool bf = m.esz == 2;
+#define RLT_LDS_CASE(D_, DH_)                                                           \
+  if (m.D == D_ && m.DH == DH_) return bf ? lds_bytes_t<bf16_t, D_, DH_>(m) : lds_bytes_t<float, D_, DH_>(m);
+  RLT_LDS_CASE(64, 16)
+  RLT_LDS_CASE(64, 32)
+  RLT_LDS_CASE(64, 64)
+  RLT_LDS_CASE(128, 16)
+  RLT_LDS_CASE(128, 32)
+  RLT_LDS_CASE(128, 64)
+  RLT_LDS_CASE(128, 128)
+#undef RLT_LDS_CASE
+  return ~size_t(0);
 }
 
 template <typename WT, int D, int DH>
@@ -706,8 +1019,8 @@ hipError_t launch_t(const ModelLayout& m, const StateLayout& s, const DecSmallAr
   p.mem_k = a.state + s.mem_k;
   p.mem_v = a.state + s.mem_v;
   p.s_out = a.s_out;
-  p.B = a.B; p.T = a.T; p.t0 = a.t0; p.n = a.n; p.L = m.L; p.F = m.F; p.F2 = m.F2; p.Wm1 = m.W - 1; p.G = m.G;
-  p.ffn_kind = m.ffn_kind; p.eps = m.eps;
+  p.B = a.B; p.T = a.T; p.T8 = s.T8; p.t0 = a.t0; p.n = a.n; p.L = m.L; p.F = m.F; p.F2 = m.F2; p.Wm1 = m.W - 1;
+  p.G = m.G; p.ffn_kind = m.ffn_kind; p.eps = m.eps;
   const size_t lds = lds_bytes(m);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dec_small_k<WT, D, DH>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -723,10 +1036,13 @@ constexpr size_t kMaxLds = 160 * 1024;
 bool dec_small_supported(const ModelLayout& m, int T) {
   const bool shape = (m.D == 64 && (m.DH == 16 || m.DH == 32 || m.DH == 64)) ||
                      (m.D == 128 && (m.DH == 16 || m.DH == 32 || m.DH == 64 || m.DH == 128));
-  const int entries = std::min(m.W, T);   // window entries ever held at once
-  // 32-bit memory-row offsets within one (group, sequence)
-  const bool offsets = static_cast<size_t>(T) * m.D * m.esz < (size_t(1) << 31);
-  return shape && entries <= WCAP && offsets && m.F2 <= 4096 && lds_bytes(m) <= kMaxLds;
+  // the window ring (W-1 slots plus the current entry) is scanned whole every step
+  // 32-bit memory-row offsets within one (group, sequence), value blocks included
+  const size_t t8 = (static_cast<size_t>(T) + 7) / 8 * 8;
+  const bool offsets = t8 * m.D * m.esz < (size_t(1) << 31);
+  // SwiGLU pairs of 16 rows; FFN widths in whole 64-element chunks
+  const bool ffn = m.F % 64 == 0 && (m.ffn_kind == RLT_FFN_GELU || m.F % 16 == 0);
+  return shape && m.W <= WCAP && offsets && ffn && m.F2 <= 4096 && lds_bytes(m) <= kMaxLds;
 }
 
 size_t dec_small_lds_bytes(const ModelLayout& m, int T) {

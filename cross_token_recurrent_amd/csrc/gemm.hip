@@ -83,8 +83,13 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, int m, int n, float
       if (which < 2) {
         const int c = rel % g.sc_D, h = c / g.sc_dh, cc = c % g.sc_dh;
         const int b = g.sc_b0 + m / g.sc_n, t = g.sc_t0 + m % g.sc_n;
-        TW* dst = static_cast<TW*>(which == 0 ? g.sc_k : g.sc_v);
-        store_from_f32(dst + ((static_cast<size_t>(b) * g.sc_H + h) * g.sc_T + t) * g.sc_dh + cc, v);
+        const size_t bh = static_cast<size_t>(b) * g.sc_H + h;
+        size_t o;
+        if (which == 1 && epi == EPI_SCATTER_HEADS)   // memory values: key-blocked [..][T8/8][dh][8]
+          o = ((bh * ((g.sc_T + 7) / 8) + t / 8) * g.sc_dh + cc) * 8 + t % 8;
+        else
+          o = (bh * g.sc_T + t) * g.sc_dh + cc;
+        store_from_f32(static_cast<TW*>(which == 0 ? g.sc_k : g.sc_v) + o, v);
       }
     }
   }

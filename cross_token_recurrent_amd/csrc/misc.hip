@@ -100,7 +100,12 @@ __global__ void store_tokens_k(float* __restrict__ flat, T* __restrict__ dev, in
     const size_t bj = i / D;
     const int j = static_cast<int>(bj % n), b = static_cast<int>(bj / n);
     size_t di;
-    if (heads_layout) {
+    if (heads_layout == 2) {
+      // key-blocked values: [B][H][T8/8][dh][8]
+      const int h = c / dh, cc = c % dh, t = t0 + j;
+      const size_t nblk = static_cast<size_t>(Tmax + 7) / 8;
+      di = (((static_cast<size_t>(b) * H + h) * nblk + t / 8) * dh + cc) * 8 + t % 8;
+    } else if (heads_layout == 1) {
       const int h = c / dh, cc = c % dh;
       di = ((static_cast<size_t>(b) * H + h) * Tmax + t0 + j) * dh + cc;
     } else {

@@ -46,14 +46,17 @@ struct ModelLayout {
 //   s       fp32 [B][d]          recurrent output s_t
 //   ring_k/v  [L][B][H][W-1][dh] window caches (entry of position p in slot p mod (W-1))
 //   e         [B][T_max][d]
-//   mem_k/v   [G][B][H][T_max][dh]
+//   mem_k     [G][B][H][T_max][dh]
+//   mem_v     [G][B][H][T8/8][dh][8], T8 = T_max rounded up to a multiple of 8: keys in blocks
+//             of 8, each block stored dimension-major (8 consecutive keys of one dim are
+//             contiguous), so a lane can take 8 keys of one dim with one 16-byte load
 //   enc_k/v   [L][B][H][T_max][dh]  (only with keep_encoder_cache)
 //   encoder scratch for a chunk of Nc tokens: x fp32 [Nc][d], h [Nc][d], qkv [Nc][3d],
 //                                              attn [Nc][d], act [Nc][F]
 //   decoder scratch (batched path): see dec_batched.hip
 // ---------------------------------------------------------------------------
 struct StateLayout {
-  int B, T, keep, Wm1, Nc;
+  int B, T, T8, keep, Wm1, Nc;
   size_t flags, s, ring_k, ring_v, e, mem_k, mem_v, enc_k, enc_v;
   size_t x, h, qkv, attn, act;
   size_t dec_scratch, dec_scratch_bytes;
@@ -91,7 +94,7 @@ enum GemmEpi {
   EPI_RESID_F32 = 2,    // outf[m, n] += acc                   (fp32 residual)
   EPI_GELU = 3,         // out[m, n] = storage(gelu(acc))
   EPI_SWIGLU = 4,       // out[m, n/32*16 + n%16] = storage(silu(gate) * up), interleaved rows
-  EPI_SCATTER_HEADS = 5 // columns [c0, c0+2D) scattered to [B][H][T][dh] (K half, V half)
+  EPI_SCATTER_HEADS = 5 // columns [c0, c0+2D) scattered to the memory layouts (K half, V half)
 };
 
 struct GemmArgs {
@@ -101,8 +104,9 @@ struct GemmArgs {
   int M, N, K, lda, ldw, ldo;
   int a_f32;          // A is fp32 (converted to the storage type on load)
   int epi;
-  // EPI_STORE with scatter of columns >= scatter_c0 (K/V of QKV into a cache) and
-  // EPI_SCATTER_HEADS: destination [B][H][T][dh] for which = (n - c0) / D in {0 (k), 1 (v)}.
+  // EPI_STORE with scatter of columns >= scatter_c0 (K/V of QKV into a cache): both halves to
+  // [B][H][T][dh].  EPI_SCATTER_HEADS (memory rows): keys to [B][H][T][dh], values to the
+  // key-blocked [B][H][T8/8][dh][8] layout.  which = (n - c0) / D in {0 (k), 1 (v)}.
   void* sc_k;
   void* sc_v;
   int sc_c0;          // first scattered column (D for QKV, 0 for memory projections)
@@ -135,7 +139,8 @@ size_t dec_small_lds_bytes(const ModelLayout& m, int T);
 hipError_t launch_dec_small(const ModelLayout& m, const StateLayout& s, const DecSmallArgs& a,
                             hipStream_t st);
 
-// Test-hook conversions between fp32 [.., n, d] and the stored layouts.
+// Test-hook conversions between fp32 [.., n, d] and the stored layouts
+// (heads_layout 0: [B][T][d]; 1: [B][H][T][dh]; 2: key-blocked [B][H][T8/8][dh][8]).
 hipError_t launch_store_tokens(const float* src, void* dst, int B, int n, int D, int t0, int Tmax,
                                int dtype, int heads_layout, int H, int dh, int to_device_layout,
                                hipStream_t st);

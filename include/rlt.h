@@ -120,8 +120,11 @@ void rlt_model_release(rlt_model* model);
 
 /* ---- state H_t = (s_t, C^D_t) plus the encoder side ---------------------------------
  * One device blob holds: s [B,d] fp32; the per-layer window caches (ring buffers of
- * W-1 entries); e [B,T_max,d]; the memory K^M,V^M [G][B][H][T_max][d_h]; optionally the
- * encoder key/value cache (needed to encode incrementally); scratch; an error flag.
+ * W-1 entries); e [B,T_max,d]; the memory keys K^M [G][B][H][T_max][d_h] and values V^M
+ * in blocks of 8 positions stored dimension-major, [G][B][H][ceil(T_max/8)][d_h][8] (zeroed
+ * by rlt_state_init); optionally the encoder key/value cache (needed to encode
+ * incrementally); scratch; an error flag.  The blob layout is internal: use
+ * rlt_state_load/read_encoder_outputs to move encoder outputs in and out.
  * keep_encoder_cache = 0 allows only one rlt_encoder_forward call per reset (the whole
  * known sequence at once), which is what exact replay needs.
  * rlt_state_init sets H_0 = (s*, empty caches), t_enc = t_dec = 0 ([FI] decoder-state
