@@ -18,7 +18,15 @@ from hypothesis import given, settings, strategies as st
 import oracle as O
 from workloads import CONFIGS, ModelConfig, make_tokens, make_weights, perturb_untied
 
-torch.set_default_dtype(torch.float64)
+
+@pytest.fixture(autouse=True)
+def _fp64_default_dtype():
+    """Library references in this module build fp64 tensors; the default dtype is set per
+    test and restored, so collecting this module changes nothing for other modules."""
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def tiny_cfg(**kw):
