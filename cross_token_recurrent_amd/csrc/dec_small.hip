@@ -15,7 +15,7 @@
 // chain.  Independent sequences never synchronise, so each sequence gets one workgroup of
 // 12 waves (three per SIMD) that keeps its window caches, residual stream, gains and small
 // vectors in LDS and splits the work by role, each role running its own loop through the
-// same sequence of workgroup barriers:
+// same sequence of workgroup barriers (the gated merge, then eight phases per layer):
 //   * 4 product waves run the gated merge and every matrix-vector product: 8- or 16-lane
 //     groups per row, the weights of each product requested two products ahead into
 //     registers (the merge weights stay resident), RMSNorm fused into the operand fetch,
@@ -449,8 +449,9 @@ struct Fixed {
   static constexpr unsigned kv = al16(y1 + D * 4);                   // current key, value
   static constexpr unsigned qb = al16(kv + 2 * D * 4);               // query (self or cross)
   static constexpr unsigned bg = al16(qb + D * ESZ);
+  static constexpr unsigned CPS = DH + 4;                           // partial state: m, l, -, -, o[DH]
   static constexpr unsigned cpart = al16(bg + D * 4);                // cross partial states per attention wave
-  static constexpr unsigned pbuf = al16(cpart + NA * (DH + 2) * 4);  // cross weights per attention wave
+  static constexpr unsigned pbuf = al16(cpart + NA * CPS * 4);       // cross weights per attention wave
   static constexpr unsigned PSW = WCAP + 8;                         // window entries per head, padded
   static constexpr unsigned sws = al16(pbuf + NA * KQ * SLOTS * ESZ);    // window scores per head (fp32)
   static constexpr unsigned swp = al16(sws + H * PSW * 4);           // window weights per head
@@ -556,7 +557,8 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   // allocated for its own work only.
   if (is_attn()) {
     // ======== attention waves: memory rows (key rows R[2i + c], value items
-    // R[2KQ + 2i + r] of block i), window attention, cross-attention ========
+    // R[2KQ + 2i + r] of block i), window attention, cross-attention (partial softmax
+    // states per wave; the product waves combine them in the W_Ox operand fetch) ========
     Chunk R[4 * KQ];
     // Attention wave w takes head w % H and share w / H of the rows of a chunk: rows
     // c0 + share*RW + i*SLOTS + slot (i < KQ) for the scores, and for the P.V pass the
@@ -597,9 +599,11 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       if (l + 1 < L) mem_load(l + 1, t, 0, i0c, i1c);
       else if (has_next) mem_load(0, t + 1, 0, i0c, i1c);
     };
+    // split of the KQ blocks over the four request points: P7..P9 of the previous layer for
+    // the next rows, P1 of the layer itself for the last part
     constexpr int QB = (KQ + 3) / 4;
     constexpr int B1 = QB < KQ ? QB : KQ, B2 = 2 * QB < KQ ? 2 * QB : KQ, B3 = 3 * QB < KQ ? 3 * QB : KQ;
-    mem_load(0, p.t0, 0, IC<0>{}, IC<KQ>{});
+    mem_load(0, p.t0, 0, IC<0>{}, IC<B3>{});
     __syncthreads();
     for (int step = 0; step < p.n; ++step) {
       const int t = p.t0 + step;
@@ -609,6 +613,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
         WT* rK = ringK + l * rpl;
         WT* rV = ringV + l * vpl;
         const bool last = l + 1 == L;
+        mem_load(l, t, 0, IC<B3>{}, IC<KQ>{});
         __syncthreads();   // P1
 
         // ---- P2: window self-attention, attention wave h for head h.  Scores with lanes
@@ -705,8 +710,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
         __syncthreads();   // P3
         __syncthreads();   // P4
 
-        // ---- P5: cross-attention over memory rows 0..t, then the rows of the next layer
-        //      (or of the next step's first layer) ----
+        // ---- P5: cross-attention over memory rows 0..t ----
         {
           const unsigned tid = tid_here();
           const int lane = tid & 63;
@@ -778,42 +782,20 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             for (int off = DH; off < 64; off <<= 1) oa += __shfl_xor(oa, off, 64);
             lsum = group_sum<64>(lsum);
           }
-          float* cp = cpart + wave * (DH + 2);
-          if (lane < DH) cp[2 + lane] = oa;
-          if (DH == 128) cp[2 + 64 + lane] = ob;
+          float* cp = cpart + wave * FX::CPS;
+          if (lane < DH) cp[4 + lane] = oa;
+          if (DH == 128) cp[4 + 64 + lane] = ob;
           if (lane == 0) {
             cp[0] = m;
             cp[1] = lsum;
           }
         }
         __syncthreads();   // P5
-
-        // ---- P6: combine the WPH partial states of each head (fixed order) ----
-        {
-          const unsigned tid = tid_here();
-          if (tid < static_cast<unsigned>(D)) {
-            const int h = tid / DH, d = tid % DH;
-            float M = -INFINITY;
-#pragma unroll
-            for (int q = 0; q < WPH; ++q) M = fmaxf(M, cpart[(h + H * q) * (DH + 2)]);
-            float lt = 0.f, ot = 0.f;
-#pragma unroll
-            for (int q = 0; q < WPH; ++q) {
-              const float* cp = cpart + (h + H * q) * (DH + 2);
-              const float w = fast_exp2(cp[0] - M);   // wave without rows: m = -inf -> 0
-              lt += w * cp[1];
-              ot += w * cp[2 + d];
-            }
-            store_from_f32(&xop[tid], ot / lt);
-          }
-        }
         next_rows(l, t, has_next, IC<0>{}, IC<B1>{});
-        __syncthreads();   // P6
-        next_rows(l, t, has_next, IC<B1>{}, IC<B2>{});
         __syncthreads();   // P7
-        next_rows(l, t, has_next, IC<B2>{}, IC<B3>{});
+        next_rows(l, t, has_next, IC<B1>{}, IC<B2>{});
         __syncthreads();   // P8
-        next_rows(l, t, has_next, IC<B3>{}, IC<KQ>{});
+        next_rows(l, t, has_next, IC<B2>{}, IC<B3>{});
         __syncthreads();   // P9
       }
     }
@@ -915,11 +897,36 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
         }
         __syncthreads();   // P4
         __syncthreads();   // P5
-        __syncthreads();   // P6
 
-        // ---- P7: y += W_Ox attn ----
-        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, [&](int k) { return O::load(xop + k); },
-                             [&](int r, float v) { y[r] += v; });
+        // ---- P7: y += W_Ox attn; the operand chunk (8 dims of one head) combines the WPH
+        //      partial states of the head in a fixed order ----
+        auto cross_out = [&](int k) {
+          const int h = k / DH, d0 = k % DH;
+          float mq[WPH];
+          float M = -INFINITY;
+#pragma unroll
+          for (int q = 0; q < WPH; ++q) {
+            mq[q] = cpart[(h + H * q) * FX::CPS];
+            M = fmaxf(M, mq[q]);
+          }
+          float lt = 0.f, o[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+          for (int q = 0; q < WPH; ++q) {
+            const float* cp = cpart + (h + H * q) * FX::CPS;
+            const float w = fast_exp2(mq[q] - M);   // wave without rows: m = -inf -> 0
+            lt += w * cp[1];
+            const float4 a = *reinterpret_cast<const float4*>(cp + 4 + d0);
+            const float4 c = *reinterpret_cast<const float4*>(cp + 8 + d0);
+            o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
+            o[4] += w * c.x; o[5] += w * c.y; o[6] += w * c.z; o[7] += w * c.w;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] /= lt;
+          return O::pack(o);
+        };
+        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] += v; });
         dispatch_ffn_out(D, F, [&](auto glc, auto cplc) {
           constexpr int GL = decltype(glc)::value, CPL = decltype(cplc)::value;
           if constexpr (CPL > 0) wpre<WT, GL, CPL, CBX>(Y, layer_w(l, p.l_fout), D);
