@@ -211,10 +211,13 @@ __device__ __forceinline__ void wpre(typename Ops<WT>::Chunk* buf, const WT* __r
 }
 
 // Lane sub runs the epilogue of the group's rows base + sub (one per lane and round of
-// GL rows), so each epilogue runs once per row.
-template <typename WT, int GL, int CPL, int CB, typename XF, typename Epi>
+// GL rows), so each epilogue runs once per row.  The operand functor xf(k, ss) returns the
+// chunk k..k+8 and, for a normalised operand (NORM), adds the chunk's sum of squares to ss:
+// the group sum then covers all K and every row result is scaled by 1/rms before the
+// epilogue (RMS(y; g) . w = (g*y . w) / rms(y)), so the norm costs no separate reduction.
+template <typename WT, int GL, int CPL, int CB, bool NORM = false, typename XF, typename Epi>
 __device__ __forceinline__ void wmv(const typename Ops<WT>::Chunk* buf, const WT* __restrict__ W, int N, XF&& xf,
-                                    Epi&& epi) {
+                                    Epi&& epi, float eps = 0.f) {
   using O = Ops<WT>;
   constexpr int K = 8 * GL * CPL, NGR = NTM / GL;
   constexpr int RBU = (CB + CPL - 1) / CPL;   // rows that take chunks from the buffer
@@ -224,8 +227,12 @@ __device__ __forceinline__ void wmv(const typename Ops<WT>::Chunk* buf, const WT
   const int nrows = (N - grp0 + NGR - 1) / NGR; // rows with at least one group of this wave
   if (nrows <= 0) return;
   typename O::Chunk xr[CPL];
+  float ss = 0.f;
 #pragma unroll
-  for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf((sub + GL * ci) * 8);
+  for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf((sub + GL * ci) * 8, ss);
+  float inv = 1.f;
+  if constexpr (NORM) inv = 1.0f / sqrtf(group_sum<GL>(ss) / static_cast<float>(K) + eps);
+  auto epi_s = [&](int r, float v) { epi(r, NORM ? v * inv : v); };
   float mine = 0.f;
   int base = 0;
 #pragma unroll
@@ -233,7 +240,7 @@ __device__ __forceinline__ void wmv(const typename Ops<WT>::Chunk* buf, const WT
     if (ri < nrows) {
       if (ri - base == GL) {   // every lane of the round holds its row: run the epilogues
         const int r = grp + (base + sub) * NGR;
-        if (r < N) epi(r, mine);
+        if (r < N) epi_s(r, mine);
         base += GL;
       }
       const int r = min(grp + ri * NGR, N - 1);
@@ -251,7 +258,7 @@ __device__ __forceinline__ void wmv(const typename Ops<WT>::Chunk* buf, const WT
   for (int ri = RBU; ri < nrows; ++ri) {
     if (ri - base == GL) {
       const int r = grp + (base + sub) * NGR;
-      if (r < N) epi(r, mine);
+      if (r < N) epi_s(r, mine);
       base += GL;
     }
     const int r = min(grp + ri * NGR, N - 1);
@@ -263,7 +270,7 @@ __device__ __forceinline__ void wmv(const typename Ops<WT>::Chunk* buf, const WT
   }
   {
     const int r = grp + (base + sub) * NGR;
-    if (base + sub < nrows && r < N) epi(r, mine);
+    if (base + sub < nrows && r < N) epi_s(r, mine);
   }
 }
 
@@ -287,7 +294,7 @@ __device__ __forceinline__ void wpre_swiglu(typename Ops<WT>::Chunk* buf, const 
 
 template <typename WT, int CPL, int CB, typename XF>
 __device__ __forceinline__ void wmv_swiglu(const typename Ops<WT>::Chunk* buf, const WT* __restrict__ W, int F,
-                                           XF&& xf, WT* __restrict__ out) {
+                                           XF&& xf, WT* __restrict__ out, float eps) {
   using O = Ops<WT>;
   constexpr int GL = 8, K = 8 * GL * CPL, NGR = NTM / GL;
   constexpr int KBU = (CB + 2 * CPL - 1) / (2 * CPL);   // pairs that take chunks from the buffer
@@ -297,8 +304,10 @@ __device__ __forceinline__ void wmv_swiglu(const typename Ops<WT>::Chunk* buf, c
   const int npairs = (F - grp0 + NGR - 1) / NGR;
   if (npairs <= 0) return;
   typename O::Chunk xr[CPL];
+  float ss = 0.f;
 #pragma unroll
-  for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf((sub + GL * ci) * 8);
+  for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf((sub + GL * ci) * 8, ss);
+  const float inv = 1.0f / sqrtf(group_sum<GL>(ss) / static_cast<float>(K) + eps);   // normalised operand
   float mine = 0.f;
   int base = 0;
   auto pair = [&](int k, auto from_buf) {
@@ -319,7 +328,7 @@ __device__ __forceinline__ void wmv_swiglu(const typename Ops<WT>::Chunk* buf, c
         }
         acc = O::dot(w, xr[ci], acc);
       }
-      a[u] = group_sum<GL>(acc);
+      a[u] = group_sum<GL>(acc) * inv;
     }
     return silu_f(a[0]) * a[1];
   };
@@ -381,7 +390,8 @@ __device__ __forceinline__ void wmv_any(const WT* __restrict__ W, int N, int K, 
   for (int ri = 0; ri < nrows; ++ri) {
     const int r = min(grp + ri * NGR, N - 1);
     float acc = 0.f;
-    for (int k = sub * 8; k < K; k += 64) acc = O::dot(O::load(W + static_cast<size_t>(r) * K + k), xf(k), acc);
+    float ss = 0.f;
+    for (int k = sub * 8; k < K; k += 64) acc = O::dot(O::load(W + static_cast<size_t>(r) * K + k), xf(k, ss), acc);
     acc = group_sum<8>(acc);
     if (sub == 0 && grp + ri * NGR < N) epi(grp + ri * NGR, acc);
   }
@@ -398,14 +408,16 @@ __device__ __forceinline__ float wave_rms_inv(const float* __restrict__ y, float
   return 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
 }
 
-// Operand chunk k..k+8 of RMS(y; g) in the storage precision.
+// Operand chunk k..k+8 of g * y in the storage precision; adds sum(y^2) of the chunk to ss.
 template <typename WT>
-__device__ __forceinline__ typename Ops<WT>::Chunk norm_chunk(const float* __restrict__ y,
-                                                              const float* __restrict__ g, float inv, int k) {
+__device__ __forceinline__ typename Ops<WT>::Chunk gain_chunk(const float* __restrict__ y, const float* __restrict__ g,
+                                                              int k, float& ss) {
   const float4 y0 = *reinterpret_cast<const float4*>(y + k), y1 = *reinterpret_cast<const float4*>(y + k + 4);
   const float4 g0 = *reinterpret_cast<const float4*>(g + k), g1 = *reinterpret_cast<const float4*>(g + k + 4);
-  const float f[8] = {g0.x * (y0.x * inv), g0.y * (y0.y * inv), g0.z * (y0.z * inv), g0.w * (y0.w * inv),
-                      g1.x * (y1.x * inv), g1.y * (y1.y * inv), g1.z * (y1.z * inv), g1.w * (y1.w * inv)};
+  ss += y0.x * y0.x; ss += y0.y * y0.y; ss += y0.z * y0.z; ss += y0.w * y0.w;
+  ss += y1.x * y1.x; ss += y1.y * y1.y; ss += y1.z * y1.z; ss += y1.w * y1.w;
+  const float f[8] = {g0.x * y0.x, g0.y * y0.y, g0.z * y0.z, g0.w * y0.w,
+                      g1.x * y1.x, g1.y * y1.y, g1.z * y1.z, g1.w * y1.w};
   return Ops<WT>::pack(f);
 }
 
@@ -826,30 +838,33 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       {
         const unsigned mt = mtid_here();
         if (has_next && mt * 8 < D) e_next = O::load(at(e_seq, (t + 1) * D + mt * 8));
-        const float inv = step > 0 ? wave_rms_inv<D>(yprev, p.eps) : 0.f;
-        if (step > 0 && mt < D && p.s_out)
-          p.s_out[(static_cast<size_t>(b) * p.n + step - 1) * D + mt] = g_fin[mt] * (yprev[mt] * inv);
         const int sub = mt & 7, grp = mt >> 3;
-        auto sop = [&](int k) { return step > 0 ? norm_chunk<WT>(yprev, g_fin, inv, k) : O::load(sb + k); };
+        // operand [e_t ; g_final * y_prev] (the s part is scaled by 1/rms(y_prev) after the
+        // products, as in wmv); the first step takes s_{t0-1} as given
         Chunk xg[2 * CPD];
+        float ss = 0.f;
 #pragma unroll
         for (int ci = 0; ci < 2 * CPD; ++ci) {
           const int k = (sub + 8 * ci) * 8;
-          xg[ci] = ci < CPD ? O::load(eb + k) : sop(k - D);
+          xg[ci] = ci < CPD ? O::load(eb + k) : (step > 0 ? gain_chunk<WT>(yprev, g_fin, k - D, ss) : O::load(sb + k - D));
         }
+        const float inv = step > 0 ? 1.0f / sqrtf(group_sum<8>(ss) / static_cast<float>(D) + p.eps) : 1.f;
+        if (step > 0 && mt < D && p.s_out)
+          p.s_out[(static_cast<size_t>(b) * p.n + step - 1) * D + mt] = g_fin[mt] * (yprev[mt] * inv);
         float mine = 0.f;
 #pragma unroll
         for (int ri = 0; ri < MRG; ++ri) {
-          float gs = 0.f, fs = 0.f;
+          float ge = 0.f, gsv = 0.f, fs = 0.f;
 #pragma unroll
           for (int q = 0; q < 3 * CPD; ++q) {
             const int pp = ri * 3 * CPD + q;
             const Chunk w = pp < CBZ ? Z[pp < CBZ ? pp : 0] : merge_chunk(ri, q);
-            if (q < 2 * CPD) gs = O::dot(w, xg[q], gs);
+            if (q < CPD) ge = O::dot(w, xg[q], ge);
+            else if (q < 2 * CPD) gsv = O::dot(w, xg[q], gsv);
             else fs = O::dot(w, xg[CPD + q - 2 * CPD], fs);
           }
-          gs = group_sum<8>(gs);
-          fs = group_sum<8>(fs);
+          const float gs = group_sum<8>(ge) + group_sum<8>(gsv) * inv;
+          fs = group_sum<8>(fs) * inv;
           const int r = grp + ri * MGR;
           const float g = sigmoid_f(gs + bgl[r]);
           const float v = g * load_as_f32(eb + r) + (1.0f - g) * fs;
@@ -867,13 +882,13 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
 
         // ---- P1: q, k, v = W_{Q,K,V} RMS(y; g_self); q scaled by log2(e)/sqrt(d_h) ----
         {
-          const float inv = wave_rms_inv<D>(y, p.eps);
-          wmv<WT, 8, CPD, CBX>(X, layer_w(l, p.l_qkv), 3 * D,
-                               [&](int k) { return norm_chunk<WT>(y, g_self, inv, k); },
-                               [&](int r, float v) {
-                                 if (r < D) store_from_f32(&qb[r], v * qscale);
-                                 else kv[r - D] = round_to<WT>(v);
-                               });
+          wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_qkv), 3 * D,
+                                     [&](int k, float& ss) { return gain_chunk<WT>(y, g_self, k, ss); },
+                                     [&](int r, float v) {
+                                       if (r < D) store_from_f32(&qb[r], v * qscale);
+                                       else kv[r - D] = round_to<WT>(v);
+                                     },
+                                     p.eps);
           wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D);
           const unsigned mt = mtid_here();
           if (l == 0 && has_next && mt * 8 < D) O::store(eb + mt * 8, e_next);
@@ -882,16 +897,16 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
         __syncthreads();   // P2
 
         // ---- P3: y += W_O attn ----
-        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wo), D, [&](int k) { return O::load(xop + k); },
+        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wo), D, [&](int k, float&) { return O::load(xop + k); },
                              [&](int r, float v) { y[r] += v; });
         wpre<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D);
         __syncthreads();   // P3
 
         // ---- P4: q_x = W_Qx RMS(y; g_cross), scaled like q ----
         {
-          const float inv = wave_rms_inv<D>(y, p.eps);
-          wmv<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D, [&](int k) { return norm_chunk<WT>(y, g_cross, inv, k); },
-                               [&](int r, float v) { store_from_f32(&qb[r], v * qscale); });
+          wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_wqx), D,
+                                     [&](int k, float& ss) { return gain_chunk<WT>(y, g_cross, k, ss); },
+                                     [&](int r, float v) { store_from_f32(&qb[r], v * qscale); }, p.eps);
           if (p.ffn_kind == RLT_FFN_GELU) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F);
           else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F);
         }
@@ -900,7 +915,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
 
         // ---- P7: y += W_Ox attn; the operand chunk (8 dims of one head) combines the WPH
         //      partial states of the head in a fixed order ----
-        auto cross_out = [&](int k) {
+        auto cross_out = [&](int k, float&) {
           const int h = k / DH, d0 = k % DH;
           float mq[WPH];
           float M = -INFINITY;
@@ -935,13 +950,12 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
 
         // ---- P8: FFN input product (tied with encoder layer l), activation into xop ----
         {
-          const float inv = wave_rms_inv<D>(y, p.eps);
-          auto xf = [&](int k) { return norm_chunk<WT>(y, g_ffn, inv, k); };
+          auto xf = [&](int k, float& ss) { return gain_chunk<WT>(y, g_ffn, k, ss); };
           if (p.ffn_kind == RLT_FFN_GELU) {
-            wmv<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf,
-                                 [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); });
+            wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_fin), F, xf,
+                                       [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); }, p.eps);
           } else {
-            wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf, xop);
+            wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf, xop, p.eps);
           }
           wpre<WT, 8, CPD, CBX>(X, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
         }
@@ -950,7 +964,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
         // ---- P9: y += W_2 act ----
         dispatch_ffn_out(D, F, [&](auto glc, auto cplc) {
           constexpr int GL = decltype(glc)::value, CPL = decltype(cplc)::value;
-          auto xf = [&](int k) { return O::load(xop + k); };
+          auto xf = [&](int k, float&) { return O::load(xop + k); };
           auto epi = [&](int r, float v) { y[r] += v; };
           if constexpr (CPL > 0) wmv<WT, GL, CPL, CBX>(Y, layer_w(l, p.l_fout), D, xf, epi);
           else wmv_any(layer_w(l, p.l_fout), D, F, xf, epi);
