@@ -467,10 +467,12 @@ struct Fixed {
   static constexpr unsigned PSW = WCAP + 8;                         // window entries per head, padded
   static constexpr unsigned sws = al16(pbuf + NA * KQ * SLOTS * ESZ);    // window scores per head (fp32)
   static constexpr unsigned swp = al16(sws + H * PSW * 4);           // window weights per head
-  static constexpr unsigned end = al16(swp + H * PSW * ESZ);
+  static constexpr unsigned opart = al16(swp + H * PSW * ESZ);      // W_O partials per head [H][D] fp32
+  static constexpr unsigned yb = al16(opart + H * D * 4);            // residual after the W_O partials
+  static constexpr unsigned end = al16(yb + D * 4);
 };
 struct SmemTail {
-  unsigned gains, xop, ring, total;
+  unsigned gains, xop, wo, ring, total;
 };
 // Window caches in LDS: keys [L][H][Wm1][DH] (row per ring slot), values key-blocked
 // [L][H][NB][DH][8] with NB = ceil(Wm1 / 8) (slots past Wm1 stay zero).
@@ -479,7 +481,8 @@ __host__ __device__ inline SmemTail smem_tail(unsigned fixed_end, int D, int DH,
   const unsigned nb = (Wm1 + 7) / 8;
   p.gains = fixed_end;                                               // self, cross, ffn per layer, final
   p.xop = al16(p.gains + (3u * L + 1u) * D * 4u);                    // attention output, FFN activation
-  p.ring = al16(p.xop + static_cast<unsigned>(F > D ? F : D) * esz);
+  p.wo = al16(p.xop + static_cast<unsigned>(F > D ? F : D) * esz);    // W_O of every layer [L][D][D]
+  p.ring = al16(p.wo + static_cast<unsigned>(L) * D * D * esz);
   p.total = al16(p.ring + static_cast<unsigned>(L) * (D / DH) * (Wm1 + 8u * nb) * DH * esz);
   return p;
 }
@@ -513,7 +516,10 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   WT* ringK = reinterpret_cast<WT*>(smem + sp.ring);
   WT* ringV = ringK + L * rpl;
   WT* xop = reinterpret_cast<WT*>(smem + sp.xop);
+  WT* wol = reinterpret_cast<WT*>(smem + sp.wo);
   float* gains = reinterpret_cast<float*>(smem + sp.gains);
+  float* opart = reinterpret_cast<float*>(smem + FX::opart);
+  float* yb = reinterpret_cast<float*>(smem + FX::yb);
   WT* eb = reinterpret_cast<WT*>(smem + FX::eb);
   WT* sb = reinterpret_cast<WT*>(smem + FX::sb);
   float* y0 = reinterpret_cast<float*>(smem + FX::y0);
@@ -563,6 +569,12 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
     return reinterpret_cast<const WT*>(p.layers + static_cast<size_t>(l) * p.layer_stride + off);
   };
   auto is_attn = [&]() { return __builtin_amdgcn_readfirstlane(tid_here() >> 6) < NA; };
+  // W_O of every layer stays in LDS: the window-attention wave of head h multiplies its
+  // output by columns h*DH.. of W_O right after computing it
+  for (int l = 0; l < L; ++l) {
+    const WT* src = layer_w(l, p.l_wo);
+    for (int i = threadIdx.x * 8; i < D * D; i += NT * 8) O::store(wol + l * D * D + i, O::load(src + i));
+  }
 
   // The two roles run their own step loops; both pass the same sequence of workgroup
   // barriers (one per phase: merge, then P1..P9 per layer), so each role's registers are
@@ -708,6 +720,18 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               store_from_f32(&xop[h * DH + lane], (oa + pc * kv[D + h * DH + lane]) / ls);
               if (DH == 128) store_from_f32(&xop[h * DH + 64 + lane], (ob + pc * kv[D + h * DH + 64 + lane]) / ls);
             }
+            wave_sync_lds();
+            // W_O partial of this head: opart[h][r] = W_O[r, h*DH:(h+1)*DH] . attn_h, lanes over rows
+            {
+              const WT* wo = wol + l * D * D + h * DH;
+#pragma unroll
+              for (int r = lane; r < D; r += 64) {
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < DH; c += 8) acc = O::dot(O::load(wo + r * D + c), O::load(xop + h * DH + c), acc);
+                opart[h * D + r] = acc;
+              }
+            }
             // the current entry replaces the oldest one (position t - (W-1)); all reads are done
             if (Wm1 > 0) {
               const int sl = t % Wm1;
@@ -719,7 +743,6 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
           }
         }
         __syncthreads();   // P2
-        __syncthreads();   // P3
         __syncthreads();   // P4
 
         // ---- P5: cross-attention over memory rows 0..t ----
@@ -813,7 +836,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
     }
   } else {
     // ======== product waves: the gated merge and every matrix-vector product ========
-    Chunk X[CBX], Y[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: O, Ox, FFN out; Z: merge (resident)
+    Chunk X[CBX], Y[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: Ox, FFN out; Z: merge (resident)
     auto merge_chunk = [&](int ri, int q) {
       const unsigned mt = mtid_here();
       const int sub = mt & 7, grp = mt >> 3;
@@ -824,7 +847,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
 #pragma unroll
     for (int pp = 0; pp < CBZ; ++pp) Z[pp] = merge_chunk(pp / (3 * CPD), pp % (3 * CPD));
     wpre<WT, 8, CPD, CBX>(X, layer_w(0, p.l_qkv), 3 * D);
-    wpre<WT, 8, CPD, CBX>(Y, layer_w(0, p.l_wo), D);
+    wpre<WT, 8, CPD, CBX>(Y, layer_w(0, p.l_wox), D);
     __syncthreads();
     for (int step = 0; step < p.n; ++step) {
       const int t = p.t0 + step;
@@ -896,16 +919,21 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
         __syncthreads();   // P1
         __syncthreads();   // P2
 
-        // ---- P3: y += W_O attn ----
-        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wo), D, [&](int k, float&) { return O::load(xop + k); },
-                             [&](int r, float v) { y[r] += v; });
-        wpre<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D);
-        __syncthreads();   // P3
-
-        // ---- P4: q_x = W_Qx RMS(y; g_cross), scaled like q ----
+        // ---- P4: y_b = y + sum_h W_O[:, h] attn_h (the per-head partials of the window
+        //      attention, added in head order; each product wave writes the whole vector, so
+        //      its own reads see its own writes); q_x = W_Qx RMS(y_b; g_cross), scaled like q ----
         {
+          const int lane = mtid_here() & 63;
+#pragma unroll
+          for (int c = lane; c < D; c += 64) {
+            float v = y[c];
+#pragma unroll
+            for (int h = 0; h < H; ++h) v += opart[h * D + c];
+            yb[c] = v;
+          }
+          wave_sync_lds();
           wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_wqx), D,
-                                     [&](int k, float& ss) { return gain_chunk<WT>(y, g_cross, k, ss); },
+                                     [&](int k, float& ss) { return gain_chunk<WT>(yb, g_cross, k, ss); },
                                      [&](int r, float v) { store_from_f32(&qb[r], v * qscale); }, p.eps);
           if (p.ffn_kind == RLT_FFN_GELU) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F);
           else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F);
@@ -941,7 +969,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
           for (int i = 0; i < 8; ++i) o[i] /= lt;
           return O::pack(o);
         };
-        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] += v; });
+        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] = yb[r] + v; });
         dispatch_ffn_out(D, F, [&](auto glc, auto cplc) {
           constexpr int GL = decltype(glc)::value, CPL = decltype(cplc)::value;
           if constexpr (CPL > 0) wpre<WT, GL, CPL, CBX>(Y, layer_w(l, p.l_fout), D);
@@ -969,7 +997,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
           if constexpr (CPL > 0) wmv<WT, GL, CPL, CBX>(Y, layer_w(l, p.l_fout), D, xf, epi);
           else wmv_any(layer_w(l, p.l_fout), D, F, xf, epi);
         });
-        wpre<WT, 8, CPD, CBX>(Y, layer_w(last ? 0 : l + 1, p.l_wo), D);
+        wpre<WT, 8, CPD, CBX>(Y, layer_w(last ? 0 : l + 1, p.l_wox), D);
         __syncthreads();   // P9
         (void)t;
       }
