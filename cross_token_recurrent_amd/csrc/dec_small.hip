@@ -64,6 +64,12 @@ __device__ __forceinline__ void wave_sync_lds() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// Hardware reciprocal and reciprocal square root (about 1 ulp each): RMSNorm scales,
+// softmax normalisers and the logistic function of the gated merge and SwiGLU.
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float rsq_hw(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float sigmoid_hw(float x) { return rcp_hw(1.0f + fast_exp2(-kLog2e * x)); }
+__device__ __forceinline__ float silu_hw(float x) { return x * sigmoid_hw(x); }
 
 // threadIdx.x through an empty asm: lane-dependent offsets derived from it are recomputed
 // where they are used instead of being hoisted out of the step loop and held in registers.
@@ -231,7 +237,7 @@ __device__ __forceinline__ void wmv(const typename Ops<WT>::Chunk* buf, const WT
 #pragma unroll
   for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf((sub + GL * ci) * 8, ss);
   float inv = 1.f;
-  if constexpr (NORM) inv = 1.0f / sqrtf(group_sum<GL>(ss) / static_cast<float>(K) + eps);
+  if constexpr (NORM) inv = rsq_hw(group_sum<GL>(ss) / static_cast<float>(K) + eps);
   auto epi_s = [&](int r, float v) { epi(r, NORM ? v * inv : v); };
   float mine = 0.f;
   int base = 0;
@@ -307,7 +313,7 @@ __device__ __forceinline__ void wmv_swiglu(const typename Ops<WT>::Chunk* buf, c
   float ss = 0.f;
 #pragma unroll
   for (int ci = 0; ci < CPL; ++ci) xr[ci] = xf((sub + GL * ci) * 8, ss);
-  const float inv = 1.0f / sqrtf(group_sum<GL>(ss) / static_cast<float>(K) + eps);   // normalised operand
+  const float inv = rsq_hw(group_sum<GL>(ss) / static_cast<float>(K) + eps);   // normalised operand
   float mine = 0.f;
   int base = 0;
   auto pair = [&](int k, auto from_buf) {
@@ -330,7 +336,7 @@ __device__ __forceinline__ void wmv_swiglu(const typename Ops<WT>::Chunk* buf, c
       }
       a[u] = group_sum<GL>(acc) * inv;
     }
-    return silu_f(a[0]) * a[1];
+    return silu_hw(a[0]) * a[1];
   };
   auto flush_if_full = [&](int k) {
     if (k - base == GL) {
@@ -405,7 +411,7 @@ __device__ __forceinline__ float wave_rms_inv(const float* __restrict__ y, float
 #pragma unroll
   for (int c = lane; c < D; c += 64) ss += y[c] * y[c];
   ss = group_sum<64>(ss);
-  return 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  return rsq_hw(ss / static_cast<float>(D) + eps);
 }
 
 // Operand chunk k..k+8 of g * y in the storage precision; adds sum(y^2) of the chunk to ss.
@@ -703,7 +709,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
                 ls += pr;
               }
             }
-            ls = group_sum<64>(ls);
+            const float rls = rcp_hw(group_sum<64>(ls));
             wave_sync_lds();
             float oa = 0.f, ob = 0.f;
             for (int r = 0; lane + 64 * r < DH * nbw; ++r) {
@@ -717,8 +723,8 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             for (int off = DH; off < 64; off <<= 1) oa += __shfl_xor(oa, off, 64);
             const float pc = load_as_f32(pw + ecur);
             if (lane < DH) {
-              store_from_f32(&xop[h * DH + lane], (oa + pc * kv[D + h * DH + lane]) / ls);
-              if (DH == 128) store_from_f32(&xop[h * DH + 64 + lane], (ob + pc * kv[D + h * DH + 64 + lane]) / ls);
+              store_from_f32(&xop[h * DH + lane], (oa + pc * kv[D + h * DH + lane]) * rls);
+              if (DH == 128) store_from_f32(&xop[h * DH + 64 + lane], (ob + pc * kv[D + h * DH + 64 + lane]) * rls);
             }
             wave_sync_lds();
             // W_O partial of this head: opart[h][r] = W_O[r, h*DH:(h+1)*DH] . attn_h, lanes over rows
@@ -871,7 +877,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
           const int k = (sub + 8 * ci) * 8;
           xg[ci] = ci < CPD ? O::load(eb + k) : (step > 0 ? gain_chunk<WT>(yprev, g_fin, k - D, ss) : O::load(sb + k - D));
         }
-        const float inv = step > 0 ? 1.0f / sqrtf(group_sum<8>(ss) / static_cast<float>(D) + p.eps) : 1.f;
+        const float inv = step > 0 ? rsq_hw(group_sum<8>(ss) / static_cast<float>(D) + p.eps) : 1.f;
         if (step > 0 && mt < D && p.s_out)
           p.s_out[(static_cast<size_t>(b) * p.n + step - 1) * D + mt] = g_fin[mt] * (yprev[mt] * inv);
         float mine = 0.f;
@@ -889,7 +895,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
           const float gs = group_sum<8>(ge) + group_sum<8>(gsv) * inv;
           fs = group_sum<8>(fs) * inv;
           const int r = grp + ri * MGR;
-          const float g = sigmoid_f(gs + bgl[r]);
+          const float g = sigmoid_hw(gs + bgl[r]);
           const float v = g * load_as_f32(eb + r) + (1.0f - g) * fs;
           mine = sub == ri ? v : mine;
         }
@@ -965,8 +971,9 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
             o[4] += w * c.x; o[5] += w * c.y; o[6] += w * c.z; o[7] += w * c.w;
           }
+          const float rlt = rcp_hw(lt);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] /= lt;
+          for (int i = 0; i < 8; ++i) o[i] *= rlt;
           return O::pack(o);
         };
         wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] = yb[r] + v; });
