@@ -841,174 +841,177 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       }
     }
   } else {
-    // ======== product waves: the gated merge and every matrix-vector product ========
-    Chunk X[CBX], Y[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: Ox, FFN out; Z: merge (resident)
-    auto merge_chunk = [&](int ri, int q) {
-      const unsigned mt = mtid_here();
-      const int sub = mt & 7, grp = mt >> 3;
-      const int r = min(grp + ri * MGR, D - 1);   // rows past D (buffer slots beyond the merge): any row
-      return q < 2 * CPD ? O::load(at(wgate, r * 2 * D + (sub + 8 * q) * 8))
-                         : O::load(at(wfb, r * D + (sub + 8 * (q - 2 * CPD)) * 8));
-    };
-#pragma unroll
-    for (int pp = 0; pp < CBZ; ++pp) Z[pp] = merge_chunk(pp / (3 * CPD), pp % (3 * CPD));
-    wpre<WT, 8, CPD, CBX>(X, layer_w(0, p.l_qkv), 3 * D);
-    wpre<WT, 8, CPD, CBX>(Y, layer_w(0, p.l_wox), D);
-    __syncthreads();
-    for (int step = 0; step < p.n; ++step) {
-      const int t = p.t0 + step;
-      const bool has_next = step + 1 < p.n;
-      float* y = (step & 1) ? y0 : y1;
-      float* yprev = (step & 1) ? y1 : y0;
-      Chunk e_next = O::zero();
-
-      // ---- gated merge: y = g * e_t + (1 - g) * W_fb s_{t-1},
-      //      g = sigmoid(W_gate [e_t; s_{t-1}] + b_g), s_{t-1} = RMS(y_prev; g_final) ----
-      {
+    // ======== product waves: the gated merge and every matrix-vector product.  The loop is
+    // instantiated per FFN output-product shape (lanes per row, chunks per lane), chosen once
+    // here, so every branch inside the step loop is on a compile-time shape and the compiler
+    // tracks the outstanding weight requests exactly. ========
+    dispatch_ffn_out(D, F, [&](auto glc, auto cplc) {
+      constexpr int GL2 = decltype(glc)::value, CPL2 = decltype(cplc)::value;
+      Chunk X[CBX], Y[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: Ox, FFN out; Z: merge (resident)
+      auto merge_chunk = [&](int ri, int q) {
         const unsigned mt = mtid_here();
-        if (has_next && mt * 8 < D) e_next = O::load(at(e_seq, (t + 1) * D + mt * 8));
         const int sub = mt & 7, grp = mt >> 3;
-        // operand [e_t ; g_final * y_prev] (the s part is scaled by 1/rms(y_prev) after the
-        // products, as in wmv); the first step takes s_{t0-1} as given
-        Chunk xg[2 * CPD];
-        float ss = 0.f;
+        const int r = min(grp + ri * MGR, D - 1);   // rows past D (buffer slots beyond the merge): any row
+        return q < 2 * CPD ? O::load(at(wgate, r * 2 * D + (sub + 8 * q) * 8))
+                           : O::load(at(wfb, r * D + (sub + 8 * (q - 2 * CPD)) * 8));
+      };
 #pragma unroll
-        for (int ci = 0; ci < 2 * CPD; ++ci) {
-          const int k = (sub + 8 * ci) * 8;
-          xg[ci] = ci < CPD ? O::load(eb + k) : (step > 0 ? gain_chunk<WT>(yprev, g_fin, k - D, ss) : O::load(sb + k - D));
-        }
-        const float inv = step > 0 ? rsq_hw(group_sum<8>(ss) / static_cast<float>(D) + p.eps) : 1.f;
-        if (step > 0 && mt < D && p.s_out)
-          p.s_out[(static_cast<size_t>(b) * p.n + step - 1) * D + mt] = g_fin[mt] * (yprev[mt] * inv);
-        float mine = 0.f;
-#pragma unroll
-        for (int ri = 0; ri < MRG; ++ri) {
-          float ge = 0.f, gsv = 0.f, fs = 0.f;
-#pragma unroll
-          for (int q = 0; q < 3 * CPD; ++q) {
-            const int pp = ri * 3 * CPD + q;
-            const Chunk w = pp < CBZ ? Z[pp < CBZ ? pp : 0] : merge_chunk(ri, q);
-            if (q < CPD) ge = O::dot(w, xg[q], ge);
-            else if (q < 2 * CPD) gsv = O::dot(w, xg[q], gsv);
-            else fs = O::dot(w, xg[CPD + q - 2 * CPD], fs);
-          }
-          const float gs = group_sum<8>(ge) + group_sum<8>(gsv) * inv;
-          fs = group_sum<8>(fs) * inv;
-          const int r = grp + ri * MGR;
-          const float g = sigmoid_hw(gs + bgl[r]);
-          const float v = g * load_as_f32(eb + r) + (1.0f - g) * fs;
-          mine = sub == ri ? v : mine;
-        }
-        if (sub < MRG) y[grp + sub * MGR] = mine;
-      }
-      __syncthreads();   // merge
+      for (int pp = 0; pp < CBZ; ++pp) Z[pp] = merge_chunk(pp / (3 * CPD), pp % (3 * CPD));
+      wpre<WT, 8, CPD, CBX>(X, layer_w(0, p.l_qkv), 3 * D);
+      wpre<WT, 8, CPD, CBX>(Y, layer_w(0, p.l_wox), D);
+      __syncthreads();
+      for (int step = 0; step < p.n; ++step) {
+        const int t = p.t0 + step;
+        const bool has_next = step + 1 < p.n;
+        float* y = (step & 1) ? y0 : y1;
+        float* yprev = (step & 1) ? y1 : y0;
+        Chunk e_next = O::zero();
 
-      for (int l = 0; l < L; ++l) {
-        const float* g_self = gains + l * D;
-        const float* g_cross = gains + (L + l) * D;
-        const float* g_ffn = gains + (2 * L + l) * D;
-        const bool last = l + 1 == L;
-
-        // ---- P1: q, k, v = W_{Q,K,V} RMS(y; g_self); q scaled by log2(e)/sqrt(d_h) ----
+        // ---- gated merge: y = g * e_t + (1 - g) * W_fb s_{t-1},
+        //      g = sigmoid(W_gate [e_t; s_{t-1}] + b_g), s_{t-1} = RMS(y_prev; g_final) ----
         {
-          wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_qkv), 3 * D,
-                                     [&](int k, float& ss) { return gain_chunk<WT>(y, g_self, k, ss); },
-                                     [&](int r, float v) {
-                                       if (r < D) store_from_f32(&qb[r], v * qscale);
-                                       else kv[r - D] = round_to<WT>(v);
-                                     },
-                                     p.eps);
-          wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D);
           const unsigned mt = mtid_here();
-          if (l == 0 && has_next && mt * 8 < D) O::store(eb + mt * 8, e_next);
+          if (has_next && mt * 8 < D) e_next = O::load(at(e_seq, (t + 1) * D + mt * 8));
+          const int sub = mt & 7, grp = mt >> 3;
+          // operand [e_t ; g_final * y_prev] (the s part is scaled by 1/rms(y_prev) after the
+          // products, as in wmv); the first step takes s_{t0-1} as given
+          Chunk xg[2 * CPD];
+          float ss = 0.f;
+#pragma unroll
+          for (int ci = 0; ci < 2 * CPD; ++ci) {
+            const int k = (sub + 8 * ci) * 8;
+            xg[ci] = ci < CPD ? O::load(eb + k)
+                              : (step > 0 ? gain_chunk<WT>(yprev, g_fin, k - D, ss) : O::load(sb + k - D));
+          }
+          const float inv = step > 0 ? rsq_hw(group_sum<8>(ss) / static_cast<float>(D) + p.eps) : 1.f;
+          if (step > 0 && mt < D && p.s_out)
+            p.s_out[(static_cast<size_t>(b) * p.n + step - 1) * D + mt] = g_fin[mt] * (yprev[mt] * inv);
+          float mine = 0.f;
+#pragma unroll
+          for (int ri = 0; ri < MRG; ++ri) {
+            float ge = 0.f, gsv = 0.f, fs = 0.f;
+#pragma unroll
+            for (int q = 0; q < 3 * CPD; ++q) {
+              const int pp = ri * 3 * CPD + q;
+              const Chunk w = pp < CBZ ? Z[pp < CBZ ? pp : 0] : merge_chunk(ri, q);
+              if (q < CPD) ge = O::dot(w, xg[q], ge);
+              else if (q < 2 * CPD) gsv = O::dot(w, xg[q], gsv);
+              else fs = O::dot(w, xg[CPD + q - 2 * CPD], fs);
+            }
+            const float gs = group_sum<8>(ge) + group_sum<8>(gsv) * inv;
+            fs = group_sum<8>(fs) * inv;
+            const int r = grp + ri * MGR;
+            const float g = sigmoid_hw(gs + bgl[r]);
+            const float v = g * load_as_f32(eb + r) + (1.0f - g) * fs;
+            mine = sub == ri ? v : mine;
+          }
+          if (sub < MRG) y[grp + sub * MGR] = mine;
         }
-        __syncthreads();   // P1
-        __syncthreads();   // P2
+        __syncthreads();   // merge
 
-        // ---- P4: y_b = y + sum_h W_O[:, h] attn_h (the per-head partials of the window
-        //      attention, added in head order; each product wave writes the whole vector, so
-        //      its own reads see its own writes); q_x = W_Qx RMS(y_b; g_cross), scaled like q ----
-        {
-          const int lane = mtid_here() & 63;
-#pragma unroll
-          for (int c = lane; c < D; c += 64) {
-            float v = y[c];
-#pragma unroll
-            for (int h = 0; h < H; ++h) v += opart[h * D + c];
-            yb[c] = v;
+        for (int l = 0; l < L; ++l) {
+          const float* g_self = gains + l * D;
+          const float* g_cross = gains + (L + l) * D;
+          const float* g_ffn = gains + (2 * L + l) * D;
+          const bool last = l + 1 == L;
+
+          // ---- P1: q, k, v = W_{Q,K,V} RMS(y; g_self); q scaled by log2(e)/sqrt(d_h) ----
+          {
+            wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_qkv), 3 * D,
+                                       [&](int k, float& ss) { return gain_chunk<WT>(y, g_self, k, ss); },
+                                       [&](int r, float v) {
+                                         if (r < D) store_from_f32(&qb[r], v * qscale);
+                                         else kv[r - D] = round_to<WT>(v);
+                                       },
+                                       p.eps);
+            wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D);
+            const unsigned mt = mtid_here();
+            if (l == 0 && has_next && mt * 8 < D) O::store(eb + mt * 8, e_next);
           }
-          wave_sync_lds();
-          wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_wqx), D,
-                                     [&](int k, float& ss) { return gain_chunk<WT>(yb, g_cross, k, ss); },
-                                     [&](int r, float v) { store_from_f32(&qb[r], v * qscale); }, p.eps);
-          if (p.ffn_kind == RLT_FFN_GELU) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F);
-          else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F);
+          __syncthreads();   // P1
+          __syncthreads();   // P2
+
+          // ---- P4: y_b = y + sum_h W_O[:, h] attn_h (the per-head partials of the window
+          //      attention, added in head order; each product wave writes the whole vector, so
+          //      its own reads see its own writes); q_x = W_Qx RMS(y_b; g_cross), scaled like q ----
+          {
+            const int lane = mtid_here() & 63;
+#pragma unroll
+            for (int c = lane; c < D; c += 64) {
+              float v = y[c];
+#pragma unroll
+              for (int h = 0; h < H; ++h) v += opart[h * D + c];
+              yb[c] = v;
+            }
+            wave_sync_lds();
+            wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_wqx), D,
+                                       [&](int k, float& ss) { return gain_chunk<WT>(yb, g_cross, k, ss); },
+                                       [&](int r, float v) { store_from_f32(&qb[r], v * qscale); }, p.eps);
+            if (p.ffn_kind == RLT_FFN_GELU) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F);
+            else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F);
+          }
+          __syncthreads();   // P4
+          __syncthreads();   // P5
+
+          // ---- P7: y += W_Ox attn; the operand chunk (8 dims of one head) combines the WPH
+          //      partial states of the head in a fixed order ----
+          auto cross_out = [&](int k, float&) {
+            const int h = k / DH, d0 = k % DH;
+            float mq[WPH];
+            float M = -INFINITY;
+#pragma unroll
+            for (int q = 0; q < WPH; ++q) {
+              mq[q] = cpart[(h + H * q) * FX::CPS];
+              M = fmaxf(M, mq[q]);
+            }
+            float lt = 0.f, o[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+            for (int q = 0; q < WPH; ++q) {
+              const float* cp = cpart + (h + H * q) * FX::CPS;
+              const float w = fast_exp2(mq[q] - M);   // wave without rows: m = -inf -> 0
+              lt += w * cp[1];
+              const float4 a = *reinterpret_cast<const float4*>(cp + 4 + d0);
+              const float4 c = *reinterpret_cast<const float4*>(cp + 8 + d0);
+              o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
+              o[4] += w * c.x; o[5] += w * c.y; o[6] += w * c.z; o[7] += w * c.w;
+            }
+            const float rlt = rcp_hw(lt);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] *= rlt;
+            return O::pack(o);
+          };
+          wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] = yb[r] + v; });
+          if constexpr (CPL2 > 0) wpre<WT, GL2, CPL2, CBX>(Y, layer_w(l, p.l_fout), D);
+          __syncthreads();   // P7
+
+          // ---- P8: FFN input product (tied with encoder layer l), activation into xop ----
+          {
+            auto xf = [&](int k, float& ss) { return gain_chunk<WT>(y, g_ffn, k, ss); };
+            if (p.ffn_kind == RLT_FFN_GELU) {
+              wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_fin), F, xf,
+                                         [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); }, p.eps);
+            } else {
+              wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf, xop, p.eps);
+            }
+            wpre<WT, 8, CPD, CBX>(X, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
+          }
+          __syncthreads();   // P8
+
+          // ---- P9: y += W_2 act ----
+          {
+            auto xf = [&](int k, float&) { return O::load(xop + k); };
+            auto epi = [&](int r, float v) { y[r] += v; };
+            if constexpr (CPL2 > 0) wmv<WT, GL2, CPL2, CBX>(Y, layer_w(l, p.l_fout), D, xf, epi);
+            else wmv_any(layer_w(l, p.l_fout), D, F, xf, epi);
+          }
+          wpre<WT, 8, CPD, CBX>(Y, layer_w(last ? 0 : l + 1, p.l_wox), D);
+          __syncthreads();   // P9
+          (void)t;
         }
-        __syncthreads();   // P4
-        __syncthreads();   // P5
-
-        // ---- P7: y += W_Ox attn; the operand chunk (8 dims of one head) combines the WPH
-        //      partial states of the head in a fixed order ----
-        auto cross_out = [&](int k, float&) {
-          const int h = k / DH, d0 = k % DH;
-          float mq[WPH];
-          float M = -INFINITY;
-#pragma unroll
-          for (int q = 0; q < WPH; ++q) {
-            mq[q] = cpart[(h + H * q) * FX::CPS];
-            M = fmaxf(M, mq[q]);
-          }
-          float lt = 0.f, o[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = 0.f;
-#pragma unroll
-          for (int q = 0; q < WPH; ++q) {
-            const float* cp = cpart + (h + H * q) * FX::CPS;
-            const float w = fast_exp2(mq[q] - M);   // wave without rows: m = -inf -> 0
-            lt += w * cp[1];
-            const float4 a = *reinterpret_cast<const float4*>(cp + 4 + d0);
-            const float4 c = *reinterpret_cast<const float4*>(cp + 8 + d0);
-            o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
-            o[4] += w * c.x; o[5] += w * c.y; o[6] += w * c.z; o[7] += w * c.w;
-          }
-          const float rlt = rcp_hw(lt);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] *= rlt;
-          return O::pack(o);
-        };
-        wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] = yb[r] + v; });
-        dispatch_ffn_out(D, F, [&](auto glc, auto cplc) {
-          constexpr int GL = decltype(glc)::value, CPL = decltype(cplc)::value;
-          if constexpr (CPL > 0) wpre<WT, GL, CPL, CBX>(Y, layer_w(l, p.l_fout), D);
-        });
-        __syncthreads();   // P7
-
-        // ---- P8: FFN input product (tied with encoder layer l), activation into xop ----
-        {
-          auto xf = [&](int k, float& ss) { return gain_chunk<WT>(y, g_ffn, k, ss); };
-          if (p.ffn_kind == RLT_FFN_GELU) {
-            wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_fin), F, xf,
-                                       [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); }, p.eps);
-          } else {
-            wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf, xop, p.eps);
-          }
-          wpre<WT, 8, CPD, CBX>(X, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
-        }
-        __syncthreads();   // P8
-
-        // ---- P9: y += W_2 act ----
-        dispatch_ffn_out(D, F, [&](auto glc, auto cplc) {
-          constexpr int GL = decltype(glc)::value, CPL = decltype(cplc)::value;
-          auto xf = [&](int k, float&) { return O::load(xop + k); };
-          auto epi = [&](int r, float v) { y[r] += v; };
-          if constexpr (CPL > 0) wmv<WT, GL, CPL, CBX>(Y, layer_w(l, p.l_fout), D, xf, epi);
-          else wmv_any(layer_w(l, p.l_fout), D, F, xf, epi);
-        });
-        wpre<WT, 8, CPD, CBX>(Y, layer_w(last ? 0 : l + 1, p.l_wox), D);
-        __syncthreads();   // P9
-        (void)t;
       }
-    }
+    });
   }
 
   // ---- s of the last step; window caches back to the state ----
