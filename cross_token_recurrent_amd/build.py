@@ -3,7 +3,8 @@
     python -m cross_token_recurrent_amd.build        # or build() from __graft_entry__
 
 Every source under csrc/ is compiled with hipcc for gfx950 into _build/, in parallel,
-then linked into cross_token_recurrent_amd/librlt.so.
+then linked into cross_token_recurrent_amd/librlt.so.  The persistent decoder's kernel
+instances are compiled in four parts (one compiler process each).
 """
 from __future__ import annotations
 
@@ -28,12 +29,17 @@ FLAGS = [
     "-Wall", "-Wno-unused-result",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
-SOURCES = ["api.cpp", "misc.hip", "gemm.hip", "enc_attn.hip", "dec_small.hip", "dec_batched.hip"]
+DEC_SMALL_PARTS = 4
+# (source, object name, extra flags); the slowest units first
+UNITS = [("dec_small.hip", f"dec_small_p{k}", [f"-DRLT_DEC_PART={k}"]) for k in range(DEC_SMALL_PARTS)] + [
+    (src, os.path.splitext(src)[0], []) for src in
+    ["dec_batched.hip", "api.cpp", "misc.hip", "gemm.hip", "enc_attn.hip"]]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit) -> str:
+    src, name, extra = unit
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l and "ignoring feature" not in l)
@@ -48,8 +54,8 @@ def build(verbose: bool = True) -> str:
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(UNITS))) as ex:
+        objs = list(ex.map(_compile, UNITS))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

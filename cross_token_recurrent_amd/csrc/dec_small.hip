@@ -642,7 +642,6 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       for (int l = 0; l < L; ++l) {
         WT* rK = ringK + l * rpl;
         WT* rV = ringV + l * vpl;
-        const bool last = l + 1 == L;
         mem_load(l, t, 0, IC<B3>{}, IC<KQ>{});
         __syncthreads();   // P1
 
@@ -842,175 +841,180 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
     }
   } else {
     // ======== product waves: the gated merge and every matrix-vector product.  The loop is
-    // instantiated per FFN output-product shape (lanes per row, chunks per lane), chosen once
-    // here, so every branch inside the step loop is on a compile-time shape and the compiler
-    // tracks the outstanding weight requests exactly. ========
+    // instantiated per FFN kind and FFN output-product shape (lanes per row, chunks per lane),
+    // chosen once here, so every branch inside the step loop is on a compile-time shape and the
+    // compiler tracks the outstanding weight requests exactly. ========
     dispatch_ffn_out(D, F, [&](auto glc, auto cplc) {
-      constexpr int GL2 = decltype(glc)::value, CPL2 = decltype(cplc)::value;
-      Chunk X[CBX], Y[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: Ox, FFN out; Z: merge (resident)
-      auto merge_chunk = [&](int ri, int q) {
-        const unsigned mt = mtid_here();
-        const int sub = mt & 7, grp = mt >> 3;
-        const int r = min(grp + ri * MGR, D - 1);   // rows past D (buffer slots beyond the merge): any row
-        return q < 2 * CPD ? O::load(at(wgate, r * 2 * D + (sub + 8 * q) * 8))
-                           : O::load(at(wfb, r * D + (sub + 8 * (q - 2 * CPD)) * 8));
-      };
-#pragma unroll
-      for (int pp = 0; pp < CBZ; ++pp) Z[pp] = merge_chunk(pp / (3 * CPD), pp % (3 * CPD));
-      wpre<WT, 8, CPD, CBX>(X, layer_w(0, p.l_qkv), 3 * D);
-      wpre<WT, 8, CPD, CBX>(Y, layer_w(0, p.l_wox), D);
-      __syncthreads();
-      for (int step = 0; step < p.n; ++step) {
-        const int t = p.t0 + step;
-        const bool has_next = step + 1 < p.n;
-        float* y = (step & 1) ? y0 : y1;
-        float* yprev = (step & 1) ? y1 : y0;
-        Chunk e_next = O::zero();
-
-        // ---- gated merge: y = g * e_t + (1 - g) * W_fb s_{t-1},
-        //      g = sigmoid(W_gate [e_t; s_{t-1}] + b_g), s_{t-1} = RMS(y_prev; g_final) ----
-        {
+      auto body = [&](auto swc) {
+        constexpr int GL2 = decltype(glc)::value, CPL2 = decltype(cplc)::value;
+        constexpr bool SWI = decltype(swc)::value;
+        Chunk X[CBX], Y[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: Ox, FFN out; Z: merge (resident)
+        auto merge_chunk = [&](int ri, int q) {
           const unsigned mt = mtid_here();
-          if (has_next && mt * 8 < D) e_next = O::load(at(e_seq, (t + 1) * D + mt * 8));
           const int sub = mt & 7, grp = mt >> 3;
-          // operand [e_t ; g_final * y_prev] (the s part is scaled by 1/rms(y_prev) after the
-          // products, as in wmv); the first step takes s_{t0-1} as given
-          Chunk xg[2 * CPD];
-          float ss = 0.f;
+          const int r = min(grp + ri * MGR, D - 1);   // rows past D (buffer slots beyond the merge): any row
+          return q < 2 * CPD ? O::load(at(wgate, r * 2 * D + (sub + 8 * q) * 8))
+                             : O::load(at(wfb, r * D + (sub + 8 * (q - 2 * CPD)) * 8));
+        };
 #pragma unroll
-          for (int ci = 0; ci < 2 * CPD; ++ci) {
-            const int k = (sub + 8 * ci) * 8;
-            xg[ci] = ci < CPD ? O::load(eb + k)
-                              : (step > 0 ? gain_chunk<WT>(yprev, g_fin, k - D, ss) : O::load(sb + k - D));
-          }
-          const float inv = step > 0 ? rsq_hw(group_sum<8>(ss) / static_cast<float>(D) + p.eps) : 1.f;
-          if (step > 0 && mt < D && p.s_out)
-            p.s_out[(static_cast<size_t>(b) * p.n + step - 1) * D + mt] = g_fin[mt] * (yprev[mt] * inv);
-          float mine = 0.f;
-#pragma unroll
-          for (int ri = 0; ri < MRG; ++ri) {
-            float ge = 0.f, gsv = 0.f, fs = 0.f;
-#pragma unroll
-            for (int q = 0; q < 3 * CPD; ++q) {
-              const int pp = ri * 3 * CPD + q;
-              const Chunk w = pp < CBZ ? Z[pp < CBZ ? pp : 0] : merge_chunk(ri, q);
-              if (q < CPD) ge = O::dot(w, xg[q], ge);
-              else if (q < 2 * CPD) gsv = O::dot(w, xg[q], gsv);
-              else fs = O::dot(w, xg[CPD + q - 2 * CPD], fs);
-            }
-            const float gs = group_sum<8>(ge) + group_sum<8>(gsv) * inv;
-            fs = group_sum<8>(fs) * inv;
-            const int r = grp + ri * MGR;
-            const float g = sigmoid_hw(gs + bgl[r]);
-            const float v = g * load_as_f32(eb + r) + (1.0f - g) * fs;
-            mine = sub == ri ? v : mine;
-          }
-          if (sub < MRG) y[grp + sub * MGR] = mine;
-        }
-        __syncthreads();   // merge
+        for (int pp = 0; pp < CBZ; ++pp) Z[pp] = merge_chunk(pp / (3 * CPD), pp % (3 * CPD));
+        wpre<WT, 8, CPD, CBX>(X, layer_w(0, p.l_qkv), 3 * D);
+        wpre<WT, 8, CPD, CBX>(Y, layer_w(0, p.l_wox), D);
+        __syncthreads();
+        for (int step = 0; step < p.n; ++step) {
+          const int t = p.t0 + step;
+          const bool has_next = step + 1 < p.n;
+          float* y = (step & 1) ? y0 : y1;
+          float* yprev = (step & 1) ? y1 : y0;
+          Chunk e_next = O::zero();
 
-        for (int l = 0; l < L; ++l) {
-          const float* g_self = gains + l * D;
-          const float* g_cross = gains + (L + l) * D;
-          const float* g_ffn = gains + (2 * L + l) * D;
-          const bool last = l + 1 == L;
-
-          // ---- P1: q, k, v = W_{Q,K,V} RMS(y; g_self); q scaled by log2(e)/sqrt(d_h) ----
+          // ---- gated merge: y = g * e_t + (1 - g) * W_fb s_{t-1},
+          //      g = sigmoid(W_gate [e_t; s_{t-1}] + b_g), s_{t-1} = RMS(y_prev; g_final) ----
           {
-            wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_qkv), 3 * D,
-                                       [&](int k, float& ss) { return gain_chunk<WT>(y, g_self, k, ss); },
-                                       [&](int r, float v) {
-                                         if (r < D) store_from_f32(&qb[r], v * qscale);
-                                         else kv[r - D] = round_to<WT>(v);
-                                       },
-                                       p.eps);
-            wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D);
             const unsigned mt = mtid_here();
-            if (l == 0 && has_next && mt * 8 < D) O::store(eb + mt * 8, e_next);
-          }
-          __syncthreads();   // P1
-          __syncthreads();   // P2
-
-          // ---- P4: y_b = y + sum_h W_O[:, h] attn_h (the per-head partials of the window
-          //      attention, added in head order; each product wave writes the whole vector, so
-          //      its own reads see its own writes); q_x = W_Qx RMS(y_b; g_cross), scaled like q ----
-          {
-            const int lane = mtid_here() & 63;
+            if (has_next && mt * 8 < D) e_next = O::load(at(e_seq, (t + 1) * D + mt * 8));
+            const int sub = mt & 7, grp = mt >> 3;
+            // operand [e_t ; g_final * y_prev] (the s part is scaled by 1/rms(y_prev) after the
+            // products, as in wmv); the first step takes s_{t0-1} as given
+            Chunk xg[2 * CPD];
+            float ss = 0.f;
 #pragma unroll
-            for (int c = lane; c < D; c += 64) {
-              float v = y[c];
-#pragma unroll
-              for (int h = 0; h < H; ++h) v += opart[h * D + c];
-              yb[c] = v;
+            for (int ci = 0; ci < 2 * CPD; ++ci) {
+              const int k = (sub + 8 * ci) * 8;
+              xg[ci] = ci < CPD ? O::load(eb + k)
+                                : (step > 0 ? gain_chunk<WT>(yprev, g_fin, k - D, ss) : O::load(sb + k - D));
             }
-            wave_sync_lds();
-            wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_wqx), D,
-                                       [&](int k, float& ss) { return gain_chunk<WT>(yb, g_cross, k, ss); },
-                                       [&](int r, float v) { store_from_f32(&qb[r], v * qscale); }, p.eps);
-            if (p.ffn_kind == RLT_FFN_GELU) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F);
-            else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F);
-          }
-          __syncthreads();   // P4
-          __syncthreads();   // P5
-
-          // ---- P7: y += W_Ox attn; the operand chunk (8 dims of one head) combines the WPH
-          //      partial states of the head in a fixed order ----
-          auto cross_out = [&](int k, float&) {
-            const int h = k / DH, d0 = k % DH;
-            float mq[WPH];
-            float M = -INFINITY;
+            const float inv = step > 0 ? rsq_hw(group_sum<8>(ss) / static_cast<float>(D) + p.eps) : 1.f;
+            if (step > 0 && mt < D && p.s_out)
+              p.s_out[(static_cast<size_t>(b) * p.n + step - 1) * D + mt] = g_fin[mt] * (yprev[mt] * inv);
+            float mine = 0.f;
 #pragma unroll
-            for (int q = 0; q < WPH; ++q) {
-              mq[q] = cpart[(h + H * q) * FX::CPS];
-              M = fmaxf(M, mq[q]);
+            for (int ri = 0; ri < MRG; ++ri) {
+              float ge = 0.f, gsv = 0.f, fs = 0.f;
+#pragma unroll
+              for (int q = 0; q < 3 * CPD; ++q) {
+                const int pp = ri * 3 * CPD + q;
+                const Chunk w = pp < CBZ ? Z[pp < CBZ ? pp : 0] : merge_chunk(ri, q);
+                if (q < CPD) ge = O::dot(w, xg[q], ge);
+                else if (q < 2 * CPD) gsv = O::dot(w, xg[q], gsv);
+                else fs = O::dot(w, xg[CPD + q - 2 * CPD], fs);
+              }
+              const float gs = group_sum<8>(ge) + group_sum<8>(gsv) * inv;
+              fs = group_sum<8>(fs) * inv;
+              const int r = grp + ri * MGR;
+              const float g = sigmoid_hw(gs + bgl[r]);
+              const float v = g * load_as_f32(eb + r) + (1.0f - g) * fs;
+              mine = sub == ri ? v : mine;
             }
-            float lt = 0.f, o[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = 0.f;
-#pragma unroll
-            for (int q = 0; q < WPH; ++q) {
-              const float* cp = cpart + (h + H * q) * FX::CPS;
-              const float w = fast_exp2(mq[q] - M);   // wave without rows: m = -inf -> 0
-              lt += w * cp[1];
-              const float4 a = *reinterpret_cast<const float4*>(cp + 4 + d0);
-              const float4 c = *reinterpret_cast<const float4*>(cp + 8 + d0);
-              o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
-              o[4] += w * c.x; o[5] += w * c.y; o[6] += w * c.z; o[7] += w * c.w;
-            }
-            const float rlt = rcp_hw(lt);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] *= rlt;
-            return O::pack(o);
-          };
-          wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] = yb[r] + v; });
-          if constexpr (CPL2 > 0) wpre<WT, GL2, CPL2, CBX>(Y, layer_w(l, p.l_fout), D);
-          __syncthreads();   // P7
-
-          // ---- P8: FFN input product (tied with encoder layer l), activation into xop ----
-          {
-            auto xf = [&](int k, float& ss) { return gain_chunk<WT>(y, g_ffn, k, ss); };
-            if (p.ffn_kind == RLT_FFN_GELU) {
-              wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_fin), F, xf,
-                                         [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); }, p.eps);
-            } else {
-              wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf, xop, p.eps);
-            }
-            wpre<WT, 8, CPD, CBX>(X, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
+            if (sub < MRG) y[grp + sub * MGR] = mine;
           }
-          __syncthreads();   // P8
+          __syncthreads();   // merge
 
-          // ---- P9: y += W_2 act ----
-          {
-            auto xf = [&](int k, float&) { return O::load(xop + k); };
-            auto epi = [&](int r, float v) { y[r] += v; };
-            if constexpr (CPL2 > 0) wmv<WT, GL2, CPL2, CBX>(Y, layer_w(l, p.l_fout), D, xf, epi);
-            else wmv_any(layer_w(l, p.l_fout), D, F, xf, epi);
+          for (int l = 0; l < L; ++l) {
+            const float* g_self = gains + l * D;
+            const float* g_cross = gains + (L + l) * D;
+            const float* g_ffn = gains + (2 * L + l) * D;
+            const bool last = l + 1 == L;
+
+            // ---- P1: q, k, v = W_{Q,K,V} RMS(y; g_self); q scaled by log2(e)/sqrt(d_h) ----
+            {
+              wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_qkv), 3 * D,
+                                         [&](int k, float& ss) { return gain_chunk<WT>(y, g_self, k, ss); },
+                                         [&](int r, float v) {
+                                           if (r < D) store_from_f32(&qb[r], v * qscale);
+                                           else kv[r - D] = round_to<WT>(v);
+                                         },
+                                         p.eps);
+              wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D);
+              const unsigned mt = mtid_here();
+              if (l == 0 && has_next && mt * 8 < D) O::store(eb + mt * 8, e_next);
+            }
+            __syncthreads();   // P1
+            __syncthreads();   // P2
+
+            // ---- P4: y_b = y + sum_h W_O[:, h] attn_h (the per-head partials of the window
+            //      attention, added in head order; each product wave writes the whole vector, so
+            //      its own reads see its own writes); q_x = W_Qx RMS(y_b; g_cross), scaled like q ----
+            {
+              const int lane = mtid_here() & 63;
+#pragma unroll
+              for (int c = lane; c < D; c += 64) {
+                float v = y[c];
+#pragma unroll
+                for (int h = 0; h < H; ++h) v += opart[h * D + c];
+                yb[c] = v;
+              }
+              wave_sync_lds();
+              wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_wqx), D,
+                                         [&](int k, float& ss) { return gain_chunk<WT>(yb, g_cross, k, ss); },
+                                         [&](int r, float v) { store_from_f32(&qb[r], v * qscale); }, p.eps);
+              if constexpr (!SWI) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F);
+              else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F);
+            }
+            __syncthreads();   // P4
+            __syncthreads();   // P5
+
+            // ---- P7: y += W_Ox attn; the operand chunk (8 dims of one head) combines the WPH
+            //      partial states of the head in a fixed order ----
+            auto cross_out = [&](int k, float&) {
+              const int h = k / DH, d0 = k % DH;
+              float mq[WPH];
+              float M = -INFINITY;
+#pragma unroll
+              for (int q = 0; q < WPH; ++q) {
+                mq[q] = cpart[(h + H * q) * FX::CPS];
+                M = fmaxf(M, mq[q]);
+              }
+              float lt = 0.f, o[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+              for (int q = 0; q < WPH; ++q) {
+                const float* cp = cpart + (h + H * q) * FX::CPS;
+                const float w = fast_exp2(mq[q] - M);   // wave without rows: m = -inf -> 0
+                lt += w * cp[1];
+                const float4 a = *reinterpret_cast<const float4*>(cp + 4 + d0);
+                const float4 c = *reinterpret_cast<const float4*>(cp + 8 + d0);
+                o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
+                o[4] += w * c.x; o[5] += w * c.y; o[6] += w * c.z; o[7] += w * c.w;
+              }
+              const float rlt = rcp_hw(lt);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) o[i] *= rlt;
+              return O::pack(o);
+            };
+            wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] = yb[r] + v; });
+            if constexpr (CPL2 > 0) wpre<WT, GL2, CPL2, CBX>(Y, layer_w(l, p.l_fout), D);
+            __syncthreads();   // P7
+
+            // ---- P8: FFN input product (tied with encoder layer l), activation into xop ----
+            {
+              auto xf = [&](int k, float& ss) { return gain_chunk<WT>(y, g_ffn, k, ss); };
+              if constexpr (!SWI) {
+                wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_fin), F, xf,
+                                           [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); }, p.eps);
+              } else {
+                wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf, xop, p.eps);
+              }
+              wpre<WT, 8, CPD, CBX>(X, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
+            }
+            __syncthreads();   // P8
+
+            // ---- P9: y += W_2 act ----
+            {
+              auto xf = [&](int k, float&) { return O::load(xop + k); };
+              auto epi = [&](int r, float v) { y[r] += v; };
+              if constexpr (CPL2 > 0) wmv<WT, GL2, CPL2, CBX>(Y, layer_w(l, p.l_fout), D, xf, epi);
+              else wmv_any(layer_w(l, p.l_fout), D, F, xf, epi);
+            }
+            wpre<WT, 8, CPD, CBX>(Y, layer_w(last ? 0 : l + 1, p.l_wox), D);
+            __syncthreads();   // P9
+            (void)t;
           }
-          wpre<WT, 8, CPD, CBX>(Y, layer_w(last ? 0 : l + 1, p.l_wox), D);
-          __syncthreads();   // P9
-          (void)t;
         }
-      }
+      };
+      if (p.ffn_kind == RLT_FFN_GELU) body(std::false_type{});
+      else body(std::true_type{});
     });
   }
 
@@ -1090,6 +1094,43 @@ hipError_t launch_t(const ModelLayout& m, const StateLayout& s, const DecSmallAr
 
 }  // namespace
 
+// The kernel's (storage type, d_model, head_dim) instances are spread over four translation
+// units: the build compiles this file once per part (RLT_DEC_PART = 0..3), and part 0 also
+// holds the host-side dispatch.  Without RLT_DEC_PART one unit holds everything.
+#define RLT_DEC_SIG(I)                                                                         \
+  __attribute__((visibility("hidden"))) hipError_t dec_small_launch_##I(                       \
+      const ModelLayout& m, const StateLayout& s, const DecSmallArgs& a, hipStream_t st)
+#define RLT_DEC_DEFINE(I, WT_, D_, DH_) \
+  RLT_DEC_SIG(I) { return launch_t<WT_, D_, DH_>(m, s, a, st); }
+#define RLT_DEC_DECLARE(I) RLT_DEC_SIG(I);
+
+#if !defined(RLT_DEC_PART) || RLT_DEC_PART == 0
+RLT_DEC_DEFINE(0, float, 64, 16)
+RLT_DEC_DEFINE(1, bf16_t, 64, 16)
+RLT_DEC_DEFINE(2, float, 64, 32)
+RLT_DEC_DEFINE(3, bf16_t, 64, 32)
+#endif
+#if !defined(RLT_DEC_PART) || RLT_DEC_PART == 1
+RLT_DEC_DEFINE(4, float, 64, 64)
+RLT_DEC_DEFINE(5, bf16_t, 64, 64)
+RLT_DEC_DEFINE(6, float, 128, 16)
+RLT_DEC_DEFINE(7, bf16_t, 128, 16)
+#endif
+#if !defined(RLT_DEC_PART) || RLT_DEC_PART == 2
+RLT_DEC_DEFINE(8, float, 128, 32)
+RLT_DEC_DEFINE(9, bf16_t, 128, 32)
+RLT_DEC_DEFINE(10, float, 128, 64)
+#endif
+#if !defined(RLT_DEC_PART) || RLT_DEC_PART == 3
+RLT_DEC_DEFINE(11, bf16_t, 128, 64)
+RLT_DEC_DEFINE(12, float, 128, 128)
+RLT_DEC_DEFINE(13, bf16_t, 128, 128)
+#endif
+
+#if !defined(RLT_DEC_PART) || RLT_DEC_PART == 0
+RLT_DEC_DECLARE(4) RLT_DEC_DECLARE(5) RLT_DEC_DECLARE(6) RLT_DEC_DECLARE(7) RLT_DEC_DECLARE(8)
+RLT_DEC_DECLARE(9) RLT_DEC_DECLARE(10) RLT_DEC_DECLARE(11) RLT_DEC_DECLARE(12) RLT_DEC_DECLARE(13)
+
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool dec_small_supported(const ModelLayout& m, int T) {
@@ -1111,19 +1152,18 @@ size_t dec_small_lds_bytes(const ModelLayout& m, int T) {
 
 hipError_t launch_dec_small(const ModelLayout& m, const StateLayout& s, const DecSmallArgs& a, hipStream_t st) {
   if (!dec_small_supported(m, a.T)) return hipErrorInvalidValue;
-  const bool bf = m.dtype == RLT_DTYPE_BF16;
-#define RLT_DEC_CASE(D_, DH_)                                                            \
-  if (m.D == D_ && m.DH == DH_)                                                          \
-    return bf ? launch_t<bf16_t, D_, DH_>(m, s, a, st) : launch_t<float, D_, DH_>(m, s, a, st);
-  RLT_DEC_CASE(64, 16)
-  RLT_DEC_CASE(64, 32)
-  RLT_DEC_CASE(64, 64)
-  RLT_DEC_CASE(128, 16)
-  RLT_DEC_CASE(128, 32)
-  RLT_DEC_CASE(128, 64)
-  RLT_DEC_CASE(128, 128)
-#undef RLT_DEC_CASE
+  const int bf = m.dtype == RLT_DTYPE_BF16 ? 1 : 0;
+  static const int kD[7] = {64, 64, 64, 128, 128, 128, 128};
+  static const int kDH[7] = {16, 32, 64, 16, 32, 64, 128};
+  using Fn = hipError_t (*)(const ModelLayout&, const StateLayout&, const DecSmallArgs&, hipStream_t);
+  static const Fn kFn[14] = {dec_small_launch_0,  dec_small_launch_1,  dec_small_launch_2,  dec_small_launch_3,
+                             dec_small_launch_4,  dec_small_launch_5,  dec_small_launch_6,  dec_small_launch_7,
+                             dec_small_launch_8,  dec_small_launch_9,  dec_small_launch_10, dec_small_launch_11,
+                             dec_small_launch_12, dec_small_launch_13};
+  for (int c = 0; c < 7; ++c)
+    if (m.D == kD[c] && m.DH == kDH[c]) return kFn[2 * c + bf](m, s, a, st);
   return hipErrorInvalidValue;
 }
+#endif
 
 }  // namespace rlt
