@@ -2,10 +2,19 @@
 // paragraph: the encoder runs under a causal mask, token-parallel; [AL] §一: the memory
 // never shows future tokens).
 //
-// Grid (query blocks, heads, sequences).  Each query is owned by LPQ = dh/16 lanes, each
-// holding 16 dimensions of the (pre-scaled) query and of the output accumulator.  Key and
-// value tiles of 64 positions (32 for dh = 128) are staged through LDS as fp32; scores are processed 16
-// keys at a time with an online softmax (running max, rescaled sum and output).
+// bf16 storage: a flash-attention kernel on the matrix cores (v_mfma_f32_16x16x16_bf16).
+// A workgroup of four waves takes 64 queries of one (sequence, head), 16 per wave; key and
+// value tiles of 64 positions are staged through LDS (values transposed).  Each wave computes
+// the transposed score tile S^T = K Q^T (keys x its 16 queries), so a lane holds four keys of
+// one query: the online softmax needs only in-lane work plus a reduction over the four lane
+// rows (two lane shuffles), and the bf16 weights P^T are already laid out as the B operand
+// of O^T += V^T P^T.  Scores in the log2 domain, fp32 accumulation, weights rounded to bf16
+// before the value product (the normaliser sums the rounded weights).
+//
+// fp32 storage: each query is owned by LPQ = dh/16 lanes, each holding 16 dimensions of the
+// (pre-scaled) query and of the output accumulator.  Key and value tiles of 64 positions (32
+// for dh = 128) are staged through LDS as fp32; scores are processed 16 keys at a time with an
+// online softmax (running max, rescaled sum and output).
 #include "device_common.h"
 #include "rlt_internal.h"
 
@@ -113,17 +122,156 @@ __global__ __launch_bounds__(NTH) void enc_attn_k(AttnArgs a) {
   }
 }
 
+typedef __attribute__((ext_vector_type(4))) short s4_t;    // four bf16: a 16x16x16 MFMA operand
+typedef __attribute__((ext_vector_type(4))) float f4_t;
+
+// sum / max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float rows4_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+__device__ __forceinline__ float rows4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+template <int DH>
+__global__ __launch_bounds__(NTH) void enc_attn_mfma_k(AttnArgs a) {
+  constexpr int BQ = 64, BK = 64;
+  constexpr int KP = DH + 8;        // K tile row pitch (elements; rows stay 16-byte aligned)
+  constexpr int VP = BK + 8;        // V^T tile row pitch
+  constexpr int ND = DH / 16;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[BK * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[DH * VP];
+
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int qb = gridDim.x - 1 - blockIdx.x;            // late (longer) query blocks first
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int qi = qb * BQ + wave * 16 + col;              // this lane's query
+  const int qc = min(qi, a.n - 1);
+  const int qpos = a.t0 + qc;
+  const int kend = a.t0 + min(a.n, (qb + 1) * BQ);      // keys the block needs
+  const int wave_last = a.t0 + min(a.n - 1, qb * BQ + wave * 16 + 15);
+  const float sc = kLog2e / sqrtf(static_cast<float>(DH));
+
+  // Q^T as the B operand of S^T = K Q^T: lane holds q[col][16kk + 4grp .. +4]
+  s4_t qreg[ND];
+  const bf16_t* qp = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(b * a.n + qc) * a.ldq + h * DH;
+#pragma unroll
+  for (int kk = 0; kk < ND; ++kk) qreg[kk] = *reinterpret_cast<const s4_t*>(qp + 16 * kk + 4 * grp);
+  f4_t o[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[dt] = f4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lp = 0.f;   // running max (per query); this lane's share of the sum
+
+  const bf16_t* kb = static_cast<const bf16_t*>(a.k) + b * a.kv_ld_b + h * a.kv_ld_h;
+  const bf16_t* vb = static_cast<const bf16_t*>(a.v) + b * a.kv_ld_b + h * a.kv_ld_h;
+  for (int k0 = 0; k0 < kend; k0 += BK) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < BK * DH / 8; c += NTH) {
+      const int j = c / (DH / 8), d0 = (c % (DH / 8)) * 8;
+      uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
+      if (k0 + j < kend) {
+        kv = *reinterpret_cast<const uint4*>(kb + static_cast<size_t>(k0 + j) * a.kv_ld_t + d0);
+        vv = *reinterpret_cast<const uint4*>(vb + static_cast<size_t>(k0 + j) * a.kv_ld_t + d0);
+      }
+      *reinterpret_cast<uint4*>(Ks + j * KP + d0) = kv;
+      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Vt[(d0 + 2 * i) * VP + j] = static_cast<bf16_t>(w[i] & 0xffffu);
+        Vt[(d0 + 2 * i + 1) * VP + j] = static_cast<bf16_t>(w[i] >> 16);
+      }
+    }
+    __syncthreads();
+    if (k0 > wave_last) continue;   // uniform: the whole tile lies after this wave's queries
+
+    // S^T sub-tiles of 16 keys: lane holds keys k0 + 16ks + 4grp + v of query col
+    float s[4][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < ND; ++kk) {
+        const s4_t ka = *reinterpret_cast<const s4_t*>(Ks + (16 * ks + col) * KP + 16 * kk + 4 * grp);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qreg[kk], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key = k0 + 16 * ks + 4 * grp + v;
+        s[ks][v] = key <= qpos ? acc[v] * sc : -INFINITY;   // causal (key < kend follows)
+        mt = fmaxf(mt, s[ks][v]);
+      }
+    }
+    const float mn = fmaxf(m, rows4_max(mt));   // finite: key 0 is visible to every query
+    const float corr = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    lp *= corr;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) o[dt] *= corr;
+    s4_t pk[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float pr[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        pr[v] = round_to<bf16_t>(__builtin_amdgcn_exp2f(s[ks][v] - m));
+        lp += pr[v];
+      }
+      const uint32_t lo = pack_bf16x2(pr[0], pr[1]), hi = pack_bf16x2(pr[2], pr[3]);
+      pk[ks] = __builtin_bit_cast(s4_t, make_uint2(lo, hi));
+    }
+    // O^T[d][q] += V^T[d][keys] P^T[keys][q]
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const s4_t va = *reinterpret_cast<const s4_t*>(Vt + (16 * dt + col) * VP + 16 * ks + 4 * grp);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pk[ks], o[dt], 0, 0, 0);
+      }
+  }
+  const float inv = 1.0f / rows4_sum(lp);
+  if (qi < a.n) {
+    bf16_t* op = static_cast<bf16_t*>(a.out) + static_cast<size_t>(b * a.n + qi) * a.ldo + h * DH;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      const uint32_t lo = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), hi = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+      *reinterpret_cast<uint2*>(op + 16 * dt + 4 * grp) = make_uint2(lo, hi);
+    }
+  }
+}
+
+template <int DH>
+hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
+  dim3 grid((a.n + 63) / 64, a.H, a.Bc);
+  enc_attn_mfma_k<DH><<<grid, NTH, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-  dim3 grid(0, a.H, a.Bc);
-  switch (a.dh) {
-    case 16: grid.x = (a.n + NTH - 1) / NTH; enc_attn_k<T, 16><<<grid, NTH, 0, st>>>(a); break;
-    case 32: grid.x = (a.n + NTH / 2 - 1) / (NTH / 2); enc_attn_k<T, 32><<<grid, NTH, 0, st>>>(a); break;
-    case 64: grid.x = (a.n + NTH / 4 - 1) / (NTH / 4); enc_attn_k<T, 64><<<grid, NTH, 0, st>>>(a); break;
-    case 128: grid.x = (a.n + NTH / 8 - 1) / (NTH / 8); enc_attn_k<T, 128><<<grid, NTH, 0, st>>>(a); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (sizeof(T) == 2) {
+    switch (a.dh) {
+      case 16: return launch_mfma<16>(a, st);
+      case 32: return launch_mfma<32>(a, st);
+      case 64: return launch_mfma<64>(a, st);
+      case 128: return launch_mfma<128>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    dim3 grid(0, a.H, a.Bc);
+    switch (a.dh) {
+      case 16: grid.x = (a.n + NTH - 1) / NTH; enc_attn_k<T, 16><<<grid, NTH, 0, st>>>(a); break;
+      case 32: grid.x = (a.n + NTH / 2 - 1) / (NTH / 2); enc_attn_k<T, 32><<<grid, NTH, 0, st>>>(a); break;
+      case 64: grid.x = (a.n + NTH / 4 - 1) / (NTH / 4); enc_attn_k<T, 64><<<grid, NTH, 0, st>>>(a); break;
+      case 128: grid.x = (a.n + NTH / 8 - 1) / (NTH / 8); enc_attn_k<T, 128><<<grid, NTH, 0, st>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 }  // namespace
