@@ -6,7 +6,9 @@
 // bf16 mode: v_mfma_f32_16x16x32_bf16 with fp32 accumulation; fp32 mode:
 // v_mfma_f32_16x16x4_f32.  A block computes a 128x128 tile with 4 waves (2x2), each
 // wave a 64x64 sub-tile of 4x4 MFMA 16x16 tiles; K advances 32 per LDS stage, with the
-// next stage's global loads issued before the current stage's MFMAs.
+// next stage's global loads issued before the current stage's MFMAs.  The epilogue stages
+// each wave's results through LDS, 16 rows at a time, so every lane writes whole 16-byte
+// chunks of a row (or of a head's slice of it, for the cache scatters).
 #include "device_common.h"
 #include "rlt_internal.h"
 
@@ -66,30 +68,55 @@ __device__ __forceinline__ void store_tile(TW* __restrict__ lds, const uint4 (&r
   }
 }
 
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Eight consecutive elements in the storage type: one 16-byte store (two for fp32) when
+// vec, else element by element for the first nvalid.
 template <typename TW>
-__device__ __forceinline__ void store_out(const GemmArgs& g, int m, int n, float v) {
-  const int epi = g.epi;
-  if (epi == EPI_STORE_F32) {
-    static_cast<float*>(g.out)[static_cast<size_t>(m) * g.ldo + n] = v;
-  } else if (epi == EPI_RESID_F32) {
-    static_cast<float*>(g.out)[static_cast<size_t>(m) * g.ldo + n] += v;
-  } else if (epi == EPI_GELU) {
-    store_from_f32(static_cast<TW*>(g.out) + static_cast<size_t>(m) * g.ldo + n, gelu_erf(v));
-  } else {  // EPI_STORE / EPI_SCATTER_HEADS
-    if (epi == EPI_STORE) store_from_f32(static_cast<TW*>(g.out) + static_cast<size_t>(m) * g.ldo + n, v);
-    if (g.sc_k && n >= g.sc_c0) {
-      const int rel = n - g.sc_c0;
-      const int which = rel / g.sc_D;
-      if (which < 2) {
-        const int c = rel % g.sc_D, h = c / g.sc_dh, cc = c % g.sc_dh;
-        const int b = g.sc_b0 + m / g.sc_n, t = g.sc_t0 + m % g.sc_n;
-        const size_t bh = static_cast<size_t>(b) * g.sc_H + h;
-        size_t o;
-        if (which == 1 && epi == EPI_SCATTER_HEADS)   // memory values: key-blocked [..][T8/8][dh][8]
-          o = ((bh * ((g.sc_T + 7) / 8) + t / 8) * g.sc_dh + cc) * 8 + t % 8;
-        else
-          o = (bh * g.sc_T + t) * g.sc_dh + cc;
-        store_from_f32(static_cast<TW*>(which == 0 ? g.sc_k : g.sc_v) + o, v);
+__device__ __forceinline__ void store8(TW* p, const float (&f)[8], bool vec, int nvalid) {
+  if (vec && nvalid >= 8) {
+    if constexpr (sizeof(TW) == 2) {
+      *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                                pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    } else {
+      *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < nvalid) store_from_f32(p + e, f[e]);
+  }
+}
+
+// Columns n..n+7 of row m in the storage type (EPI_STORE, EPI_GELU, EPI_SCATTER_HEADS): the
+// output itself and/or the scatter of the key/value columns into their cache layouts.
+template <typename TW>
+__device__ __forceinline__ void store_row8(const GemmArgs& g, int m, int n, const float (&f)[8], bool vec_out) {
+  const int nvalid = g.N - n;
+  if (g.epi != EPI_SCATTER_HEADS)
+    store8(static_cast<TW*>(g.out) + static_cast<size_t>(m) * g.ldo + n, f, vec_out, nvalid);
+  if (g.sc_k && n >= g.sc_c0) {
+    const int rel = n - g.sc_c0;
+    const int which = rel / g.sc_D;
+    if (which < 2) {
+      // a chunk never straddles a head: dh and the column offsets are multiples of 8
+      const int c = rel % g.sc_D, h = c / g.sc_dh, cc = c % g.sc_dh;
+      const int b = g.sc_b0 + m / g.sc_n, t = g.sc_t0 + m % g.sc_n;
+      const size_t bh = static_cast<size_t>(b) * g.sc_H + h;
+      if (which == 1 && g.epi == EPI_SCATTER_HEADS) {
+        // memory values: key-blocked [..][T8/8][dh][8]
+        TW* base = static_cast<TW*>(g.sc_v) + (bh * ((g.sc_T + 7) / 8) + t / 8) * g.sc_dh * 8 + t % 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < nvalid) store_from_f32(base + (cc + e) * 8, f[e]);
+      } else {
+        TW* dst = static_cast<TW*>(which == 0 ? g.sc_k : g.sc_v) + (bh * g.sc_T + t) * g.sc_dh + cc;
+        store8(dst, f, true, nvalid);
       }
     }
   }
@@ -98,8 +125,13 @@ __device__ __forceinline__ void store_out(const GemmArgs& g, int m, int n, float
 template <typename TW, bool A_F32>
 __global__ __launch_bounds__(NTH) void gemm_nt_k(GemmArgs g) {
   constexpr int PITCH = BK + Tile<TW>::PAD;
-  __shared__ __attribute__((aligned(16))) TW As[BM * PITCH];
-  __shared__ __attribute__((aligned(16))) TW Ws[BN * PITCH];
+  constexpr int TILE_BYTES = BM * PITCH * static_cast<int>(sizeof(TW));
+  constexpr int SP = 64 + 4;                     // staging row pitch (floats)
+  constexpr int STAGE_BYTES = 4 * 16 * SP * 4;   // 16 rows per wave
+  constexpr int LDS_BYTES = 2 * TILE_BYTES > STAGE_BYTES ? 2 * TILE_BYTES : STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+  TW* As = reinterpret_cast<TW*>(lds);
+  TW* Ws = reinterpret_cast<TW*>(lds + TILE_BYTES);
 
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -156,39 +188,89 @@ __global__ __launch_bounds__(NTH) void gemm_nt_k(GemmArgs g) {
     }
   }
 
-  // Epilogue.  MFMA 16x16 output: lane holds rows 4*(lane/16)+v, column lane%16.
+  // Epilogue.  MFMA 16x16 output: lane holds rows 4*(lane/16)+v, column lane%16.  Per pass
+  // the wave stages 16 rows of its 64x64 sub-tile (activation applied) and writes them back
+  // as row chunks.
+  __syncthreads();   // the operand tiles are dead: their LDS becomes the staging area
+  float* st = reinterpret_cast<float*>(lds) + wave * 16 * SP;
   const int col_l = lane % 16, row_q = (lane / 16) * 4;
-  if (g.epi == EPI_SWIGLU) {
+  const int mw = m0 + wm * 64, nw = n0 + wn * 64;
+  const int epi = g.epi;
+  const bool f32_out = epi == EPI_STORE_F32 || epi == EPI_RESID_F32;
+  const size_t out_esz = f32_out ? 4 : sizeof(TW);
+  const bool vec_out = g.out && (reinterpret_cast<uintptr_t>(g.out) % 16 == 0) && ((g.ldo * out_esz) % 16 == 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    if (epi == EPI_SWIGLU) {
 #pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        const int nb = n0 + wn * 64 + j * 16;   // multiple of 32: gate block, nb+16: up block
-        if (nb >= g.N) continue;
-        const int ocol = (nb / 32) * 16 + col_l;
+      for (int jp = 0; jp < 2; ++jp)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          st[(row_q + v) * SP + jp * 16 + col_l] = silu_f(acc[i][2 * jp][v]) * acc[i][2 * jp + 1][v];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = m0 + wm * 64 + i * 16 + row_q + v;
-          if (m < g.M) {
-            const float gt = acc[i][j][v], up = acc[i][j + 1][v];
-            store_from_f32(static_cast<TW*>(g.out) + static_cast<size_t>(m) * g.ldo + ocol, silu_f(gt) * up);
+          const float x = acc[i][j][v];
+          st[(row_q + v) * SP + j * 16 + col_l] = epi == EPI_GELU ? gelu_erf(x) : x;
+        }
+    }
+    wave_sync_lds();
+    const int mr = mw + 16 * i;
+    if (f32_out) {
+      // 16 rows x 16 float4 chunks
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = lane + 64 * k, r = c / 16, c4 = (c % 16) * 4;
+        const int m = mr + r, n = nw + c4;
+        if (m >= g.M || n >= g.N) continue;
+        const float4 v = *reinterpret_cast<const float4*>(st + r * SP + c4);
+        float* p = static_cast<float*>(g.out) + static_cast<size_t>(m) * g.ldo + n;
+        if (vec_out && n + 4 <= g.N) {
+          if (epi == EPI_RESID_F32) {
+            const float4 o = *reinterpret_cast<const float4*>(p);
+            *reinterpret_cast<float4*>(p) = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+          } else {
+            *reinterpret_cast<float4*>(p) = v;
+          }
+        } else {
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e >= g.N) break;
+            if (epi == EPI_RESID_F32) p[e] += vv[e];
+            else p[e] = vv[e];
           }
         }
       }
-    return;
-  }
+    } else if (epi == EPI_SWIGLU) {
+      // 16 rows x 32 activation columns (gate/up pairs of the sub-tile), 8 per lane
+      const int r = lane / 4, c8 = (lane % 4) * 8;
+      const int m = mr + r, oc = nw / 2 + c8;
+      if (m < g.M && oc < g.N / 2) {
+        float f[8];
+        const float4 a = *reinterpret_cast<const float4*>(st + r * SP + c8);
+        const float4 b = *reinterpret_cast<const float4*>(st + r * SP + c8 + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+        store8(static_cast<TW*>(g.out) + static_cast<size_t>(m) * g.ldo + oc, f, vec_out, g.N / 2 - oc);
+      }
+    } else {
+      // 16 rows x 8 chunks of 8 columns
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + j * 16 + col_l;
-      if (n >= g.N) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * 64 + i * 16 + row_q + v;
-        if (m < g.M) store_out<TW>(g, m, n, acc[i][j][v]);
+      for (int k = 0; k < 2; ++k) {
+        const int c = lane + 64 * k, r = c / 8, c8 = (c % 8) * 8;
+        const int m = mr + r, n = nw + c8;
+        if (m >= g.M || n >= g.N) continue;
+        float f[8];
+        const float4 a = *reinterpret_cast<const float4*>(st + r * SP + c8);
+        const float4 b = *reinterpret_cast<const float4*>(st + r * SP + c8 + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+        store_row8<TW>(g, m, n, f, vec_out);
       }
     }
+    wave_sync_lds();
+  }
 }
 
 }  // namespace
