@@ -230,7 +230,9 @@ __device__ __forceinline__ void wmv(const typename Ops<WT>::Chunk* buf, const WT
   const unsigned mt = mtid_here();
   const int sub = mt % GL, grp = mt / GL;
   const int grp0 = (mt & ~63u) / GL;            // first group of this wave (uniform)
-  const int nrows = (N - grp0 + NGR - 1) / NGR; // rows with at least one group of this wave
+  // rows with at least one group of this wave; the same for every wave when NGR divides N
+  // (grp0 < NGR), which keeps the row loop free of branches for compile-time N
+  const int nrows = N % NGR == 0 ? N / NGR : (N - grp0 + NGR - 1) / NGR;
   if (nrows <= 0) return;
   typename O::Chunk xr[CPL];
   float ss = 0.f;
@@ -307,7 +309,7 @@ __device__ __forceinline__ void wmv_swiglu(const typename Ops<WT>::Chunk* buf, c
   const unsigned mt = mtid_here();
   const int sub = mt % GL, grp = mt / GL;
   const int grp0 = (mt & ~63u) / GL;
-  const int npairs = (F - grp0 + NGR - 1) / NGR;
+  const int npairs = F % NGR == 0 ? F / NGR : (F - grp0 + NGR - 1) / NGR;
   if (npairs <= 0) return;
   typename O::Chunk xr[CPL];
   float ss = 0.f;
@@ -848,6 +850,8 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       auto body = [&](auto swc) {
         constexpr int GL2 = decltype(glc)::value, CPL2 = decltype(cplc)::value;
         constexpr bool SWI = decltype(swc)::value;
+        // FFN width: a compile-time constant whenever the output product has a fixed shape
+        const int Fw = CPL2 > 0 ? 8 * GL2 * CPL2 : F;
         Chunk X[CBX], Y[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: Ox, FFN out; Z: merge (resident)
         auto merge_chunk = [&](int ri, int q) {
           const unsigned mt = mtid_here();
@@ -948,8 +952,8 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_wqx), D,
                                          [&](int k, float& ss) { return gain_chunk<WT>(yb, g_cross, k, ss); },
                                          [&](int r, float v) { store_from_f32(&qb[r], v * qscale); }, p.eps);
-              if constexpr (!SWI) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), F);
-              else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F);
+              if constexpr (!SWI) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
+              else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
             }
             __syncthreads();   // P4
             __syncthreads();   // P5
@@ -991,10 +995,10 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             {
               auto xf = [&](int k, float& ss) { return gain_chunk<WT>(y, g_ffn, k, ss); };
               if constexpr (!SWI) {
-                wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_fin), F, xf,
+                wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_fin), Fw, xf,
                                            [&](int r, float v) { store_from_f32(&xop[r], gelu_erf(v)); }, p.eps);
               } else {
-                wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), F, xf, xop, p.eps);
+                wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), Fw, xf, xop, p.eps);
               }
               wpre<WT, 8, CPD, CBX>(X, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
             }
