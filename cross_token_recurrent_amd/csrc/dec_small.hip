@@ -962,25 +962,28 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             //      partial states of the head in a fixed order ----
             auto cross_out = [&](int k, float&) {
               const int h = k / DH, d0 = k % DH;
-              float mq[WPH];
-              float M = -INFINITY;
+              // every partial state's reads are issued before any is used
+              float2 ml[WPH];
+              float4 a[WPH], c[WPH];
 #pragma unroll
               for (int q = 0; q < WPH; ++q) {
-                mq[q] = cpart[(h + H * q) * FX::CPS];
-                M = fmaxf(M, mq[q]);
+                const float* cp = cpart + (h + H * q) * FX::CPS;
+                ml[q] = *reinterpret_cast<const float2*>(cp);
+                a[q] = *reinterpret_cast<const float4*>(cp + 4 + d0);
+                c[q] = *reinterpret_cast<const float4*>(cp + 8 + d0);
               }
+              float M = -INFINITY;
+#pragma unroll
+              for (int q = 0; q < WPH; ++q) M = fmaxf(M, ml[q].x);
               float lt = 0.f, o[8];
 #pragma unroll
               for (int i = 0; i < 8; ++i) o[i] = 0.f;
 #pragma unroll
               for (int q = 0; q < WPH; ++q) {
-                const float* cp = cpart + (h + H * q) * FX::CPS;
-                const float w = fast_exp2(mq[q] - M);   // wave without rows: m = -inf -> 0
-                lt += w * cp[1];
-                const float4 a = *reinterpret_cast<const float4*>(cp + 4 + d0);
-                const float4 c = *reinterpret_cast<const float4*>(cp + 8 + d0);
-                o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
-                o[4] += w * c.x; o[5] += w * c.y; o[6] += w * c.z; o[7] += w * c.w;
+                const float w = fast_exp2(ml[q].x - M);   // wave without rows: m = -inf -> 0
+                lt += w * ml[q].y;
+                o[0] += w * a[q].x; o[1] += w * a[q].y; o[2] += w * a[q].z; o[3] += w * a[q].w;
+                o[4] += w * c[q].x; o[5] += w * c[q].y; o[6] += w * c[q].z; o[7] += w * c[q].w;
               }
               const float rlt = rcp_hw(lt);
 #pragma unroll
