@@ -208,8 +208,10 @@ __device__ __forceinline__ void wpre(typename Ops<WT>::Chunk* buf, const WT* __r
   constexpr int K = 8 * GL * CPL, NGR = NTM / GL;
   const unsigned mt = mtid_here();
   const int sub = mt % GL, grp = mt / GL;
+  const int need = (N + NGR - 1) / NGR * CPL;   // buffer slots the product reads
 #pragma unroll
   for (int p = 0; p < CB; ++p) {
+    if (p >= need) break;
     const int ri = p / CPL, ci = p % CPL;
     const int r = min(grp + ri * NGR, N - 1);
     buf[p] = Ops<WT>::load(at(W, r * K + (sub + GL * ci) * 8));
@@ -863,7 +865,6 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
 #pragma unroll
         for (int pp = 0; pp < CBZ; ++pp) Z[pp] = merge_chunk(pp / (3 * CPD), pp % (3 * CPD));
         wpre<WT, 8, CPD, CBX>(X, layer_w(0, p.l_qkv), 3 * D);
-        wpre<WT, 8, CPD, CBX>(Y, layer_w(0, p.l_wox), D);
         __syncthreads();
         for (int step = 0; step < p.n; ++step) {
           const int t = p.t0 + step;
@@ -929,11 +930,13 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
                                            else kv[r - D] = round_to<WT>(v);
                                          },
                                          p.eps);
-              wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D);
               const unsigned mt = mtid_here();
               if (l == 0 && has_next && mt * 8 < D) O::store(eb + mt * 8, e_next);
             }
             __syncthreads();   // P1
+            // the window attention runs: request the Q_x and W_Ox weights of this layer
+            wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D);
+            wpre<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D);
             __syncthreads();   // P2
 
             // ---- P4: y_b = y + sum_h W_O[:, h] attn_h (the per-head partials of the window
@@ -952,10 +955,11 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_wqx), D,
                                          [&](int k, float& ss) { return gain_chunk<WT>(yb, g_cross, k, ss); },
                                          [&](int r, float v) { store_from_f32(&qb[r], v * qscale); }, p.eps);
-              if constexpr (!SWI) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
-              else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
             }
             __syncthreads();   // P4
+            // the cross-attention runs: request the FFN input weights
+            if constexpr (!SWI) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
+            else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
             __syncthreads();   // P5
 
             // ---- P7: y += W_Ox attn; the operand chunk (8 dims of one head) combines the WPH
@@ -1014,7 +1018,6 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               if constexpr (CPL2 > 0) wmv<WT, GL2, CPL2, CBX>(Y, layer_w(l, p.l_fout), D, xf, epi);
               else wmv_any(layer_w(l, p.l_fout), D, F, xf, epi);
             }
-            wpre<WT, 8, CPD, CBX>(Y, layer_w(last ? 0 : l + 1, p.l_wox), D);
             __syncthreads();   // P9
             (void)t;
           }
