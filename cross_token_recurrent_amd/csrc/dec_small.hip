@@ -854,7 +854,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
         constexpr bool SWI = decltype(swc)::value;
         // FFN width: a compile-time constant whenever the output product has a fixed shape
         const int Fw = CPL2 > 0 ? 8 * GL2 * CPL2 : F;
-        Chunk X[CBX], Y[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: Ox, FFN out; Z: merge (resident)
+        Chunk X[CBX], Y[CBX], U[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: Ox; U: FFN out; Z: merge (resident)
         auto merge_chunk = [&](int ri, int q) {
           const unsigned mt = mtid_here();
           const int sub = mt & 7, grp = mt >> 3;
@@ -957,25 +957,19 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
                                          [&](int r, float v) { store_from_f32(&qb[r], v * qscale); }, p.eps);
             }
             __syncthreads();   // P4
-            // the cross-attention runs: request the FFN input weights
+            // the cross-attention runs: request the FFN weights
             if constexpr (!SWI) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
             else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
+            if constexpr (CPL2 > 0) wpre<WT, GL2, CPL2, CBX>(U, layer_w(l, p.l_fout), D);
             __syncthreads();   // P5
 
             // ---- P7: y += W_Ox attn; the operand chunk (8 dims of one head) combines the WPH
             //      partial states of the head in a fixed order ----
             auto cross_out = [&](int k, float&) {
               const int h = k / DH, d0 = k % DH;
-              // every partial state's reads are issued before any is used
-              float2 ml[WPH];
-              float4 a[WPH], c[WPH];
+              float2 ml[WPH];   // (m, l) of every partial state first, for the common maximum
 #pragma unroll
-              for (int q = 0; q < WPH; ++q) {
-                const float* cp = cpart + (h + H * q) * FX::CPS;
-                ml[q] = *reinterpret_cast<const float2*>(cp);
-                a[q] = *reinterpret_cast<const float4*>(cp + 4 + d0);
-                c[q] = *reinterpret_cast<const float4*>(cp + 8 + d0);
-              }
+              for (int q = 0; q < WPH; ++q) ml[q] = *reinterpret_cast<const float2*>(cpart + (h + H * q) * FX::CPS);
               float M = -INFINITY;
 #pragma unroll
               for (int q = 0; q < WPH; ++q) M = fmaxf(M, ml[q].x);
@@ -984,10 +978,13 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               for (int i = 0; i < 8; ++i) o[i] = 0.f;
 #pragma unroll
               for (int q = 0; q < WPH; ++q) {
+                const float* cp = cpart + (h + H * q) * FX::CPS;
+                const float4 a = *reinterpret_cast<const float4*>(cp + 4 + d0);
+                const float4 c = *reinterpret_cast<const float4*>(cp + 8 + d0);
                 const float w = fast_exp2(ml[q].x - M);   // wave without rows: m = -inf -> 0
                 lt += w * ml[q].y;
-                o[0] += w * a[q].x; o[1] += w * a[q].y; o[2] += w * a[q].z; o[3] += w * a[q].w;
-                o[4] += w * c[q].x; o[5] += w * c[q].y; o[6] += w * c[q].z; o[7] += w * c[q].w;
+                o[0] += w * a.x; o[1] += w * a.y; o[2] += w * a.z; o[3] += w * a.w;
+                o[4] += w * c.x; o[5] += w * c.y; o[6] += w * c.z; o[7] += w * c.w;
               }
               const float rlt = rcp_hw(lt);
 #pragma unroll
@@ -995,7 +992,6 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               return O::pack(o);
             };
             wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] = yb[r] + v; });
-            if constexpr (CPL2 > 0) wpre<WT, GL2, CPL2, CBX>(Y, layer_w(l, p.l_fout), D);
             __syncthreads();   // P7
 
             // ---- P8: FFN input product (tied with encoder layer l), activation into xop ----
@@ -1015,7 +1011,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             {
               auto xf = [&](int k, float&) { return O::load(xop + k); };
               auto epi = [&](int r, float v) { y[r] += v; };
-              if constexpr (CPL2 > 0) wmv<WT, GL2, CPL2, CBX>(Y, layer_w(l, p.l_fout), D, xf, epi);
+              if constexpr (CPL2 > 0) wmv<WT, GL2, CPL2, CBX>(U, layer_w(l, p.l_fout), D, xf, epi);
               else wmv_any(layer_w(l, p.l_fout), D, F, xf, epi);
             }
             __syncthreads();   // P9
