@@ -173,6 +173,35 @@ def test_edge_configs(dev, over, B, T, path):
     check(f"{over} logits", Z, Z_ref, cfg.dtype)
 
 
+# The persistent decoder instantiates its product loop per FFN kind and FFN output shape
+# (lanes per row x chunks per lane, or the generic loop): one case per shape class.
+FFN_SHAPES = [
+    dict(ffn_dim=384, dtype="bf16"),                                   # d=64: 16 lanes x 3 chunks
+    dict(ffn_dim=512, ffn_kind="swiglu"),                              # d=64: 16 lanes x 4 chunks, fp32
+    dict(ffn_dim=192, ffn_kind="swiglu", dtype="bf16"),                # d=64: 8 lanes x 3 chunks
+    dict(ffn_dim=64, ffn_kind="swiglu", dtype="bf16"),                 # d=64: 8 lanes x 1 chunk
+    dict(ffn_dim=320, dtype="bf16"),                                   # d=64: generic loop
+    dict(d_model=128, ffn_dim=256, dtype="bf16"),                      # d=128: 8 lanes x 4 chunks
+    dict(d_model=128, ffn_dim=384, ffn_kind="swiglu", dtype="bf16"),   # d=128: 8 lanes x 6 chunks
+    dict(d_model=128, ffn_dim=512, n_layers=1, mem_groups=1),         # d=128: 8 lanes x 8 chunks, fp32
+    dict(d_model=128, ffn_dim=320, ffn_kind="swiglu", dtype="bf16"),   # d=128: generic loop
+]
+
+
+@pytest.mark.parametrize("over", FFN_SHAPES, ids=[f"ffn{i}" for i in range(len(FFN_SHAPES))])
+def test_ffn_shape_classes(dev, over):
+    kw = dict(window=5, mem_groups=2)
+    kw.update(over)
+    cfg = mcfg(**kw)
+    w = perturb_untied(make_weights(cfg, 51), cfg, 52)
+    tok = make_tokens(cfg.vocab, 2, 20, "uniform", 53)
+    S, Z, model, _ = gpu_replay(cfg, w, tok, dev, path=1)
+    assert model.decoder_path(20) == 1
+    S_ref, Z_ref = oracle_replay(cfg, w, tok)
+    check(f"{over} s_t", S, S_ref, cfg.dtype)
+    check(f"{over} logits", Z, Z_ref, cfg.dtype)
+
+
 # ---------------------------------------------------------------------------
 # Invariants on the GPU
 # ---------------------------------------------------------------------------
