@@ -627,16 +627,18 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
         }
       }
     };
-    // rows of the next (layer, position), requested over the four phases after the cross-
-    // attention (blocks [I0, I1) in each) so the requests drain while the products run
+    // rows of the next (layer, position), requested in the phases between two cross-attentions
+    // (blocks [I0, I1) at each point) so the requests drain while the other phases run
     auto next_rows = [&](int l, int t, bool has_next, auto i0c, auto i1c) {
       if (l + 1 < L) mem_load(l + 1, t, 0, i0c, i1c);
       else if (has_next) mem_load(0, t + 1, 0, i0c, i1c);
     };
-    // split of the KQ blocks over the four request points: P7..P9 of the previous layer for
-    // the next rows, P1 of the layer itself for the last part
-    constexpr int QB = (KQ + 3) / 4;
-    constexpr int B1 = QB < KQ ? QB : KQ, B2 = 2 * QB < KQ ? 2 * QB : KQ, B3 = 3 * QB < KQ ? 3 * QB : KQ;
+    // The KQ blocks are spread over six request points: P7, P8 and P9 of the previous layer, P1,
+    // P2 and P4 of the layer itself; one block each, the remainder from P1 on.  Spreading them
+    // keeps the vector-memory path free for the product waves' weight requests (measured: the
+    // even spread beats requesting the rows early).
+    constexpr auto req = [](int i) { return KQ / 6 + ((i + 3) % 6 < KQ % 6 ? 1 : 0); };
+    constexpr int B1 = req(0), B2 = B1 + req(1), B3 = B2 + req(2), B4 = B3 + req(3), B5 = B4 + req(4);
     mem_load(0, p.t0, 0, IC<0>{}, IC<B3>{});
     __syncthreads();
     for (int step = 0; step < p.n; ++step) {
@@ -646,8 +648,9 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
       for (int l = 0; l < L; ++l) {
         WT* rK = ringK + l * rpl;
         WT* rV = ringV + l * vpl;
-        mem_load(l, t, 0, IC<B3>{}, IC<KQ>{});
+        mem_load(l, t, 0, IC<B3>{}, IC<B4>{});
         __syncthreads();   // P1
+        mem_load(l, t, 0, IC<B4>{}, IC<B5>{});
 
         // ---- P2: window self-attention, attention wave h for head h.  Scores with lanes
         //      over entries (ring slots 0..8*NB-1, valid below npast, then the current
@@ -752,6 +755,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
           }
         }
         __syncthreads();   // P2
+        mem_load(l, t, 0, IC<B5>{}, IC<KQ>{});
         __syncthreads();   // P4
 
         // ---- P5: cross-attention over memory rows 0..t ----
