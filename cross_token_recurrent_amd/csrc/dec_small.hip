@@ -470,7 +470,8 @@ struct Fixed {
   static constexpr unsigned y1 = al16(y0 + D * 4);
   static constexpr unsigned kv = al16(y1 + D * 4);                   // current key, value
   static constexpr unsigned qb = al16(kv + 2 * D * 4);               // query (self or cross)
-  static constexpr unsigned bg = al16(qb + D * ESZ);
+  static constexpr unsigned kcb = al16(qb + D * ESZ);                // current key, storage precision
+  static constexpr unsigned bg = al16(kcb + D * ESZ);
   static constexpr unsigned CPS = DH + 4;                           // partial state: m, l, -, -, o[DH]
   static constexpr unsigned cpart = al16(bg + D * 4);                // cross partial states per attention wave
   static constexpr unsigned pbuf = al16(cpart + NA * CPS * 4);       // cross weights per attention wave
@@ -536,6 +537,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   float* y1 = reinterpret_cast<float*>(smem + FX::y1);
   float* kv = reinterpret_cast<float*>(smem + FX::kv);
   WT* qb = reinterpret_cast<WT*>(smem + FX::qb);
+  WT* kcb = reinterpret_cast<WT*>(smem + FX::kcb);
   float* bgl = reinterpret_cast<float*>(smem + FX::bg);
   float* sws = reinterpret_cast<float*>(smem + FX::sws);
   WT* swp = reinterpret_cast<WT*>(smem + FX::swp);
@@ -668,27 +670,14 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             QVec<WT> q;
             q.load(qb + h * DH + sub * 16);
             auto score = [&](int e) {
-              Chunk k0, k1;
-              if (e < ecur) {
-                const WT* kr = rK + (h * Wm1 + min(e, Wm1 - 1)) * DH + sub * 16;   // padding slots: masked
-                k0 = O::load(kr);
-                k1 = O::load(kr + 8);
-              } else {
-                // the current entry (values already rounded to the storage precision)
-                float kf[8];
-                const float* kq = kv + h * DH + sub * 16;
-#pragma unroll
-                for (int c = 0; c < 8; ++c) kf[c] = kq[c];
-                k0 = O::pack(kf);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) kf[c] = kq[8 + c];
-                k1 = O::pack(kf);
-              }
+              // ring slot e (padding slots: masked) or, for the current entry, its storage-precision copy
+              const WT* kr = e < ecur ? rK + (h * Wm1 + min(e, Wm1 - 1)) * DH + sub * 16 : kcb + h * DH + sub * 16;
+              const Chunk k0 = O::load(kr), k1 = O::load(kr + 8);
               float sc = q.dot(k0, k1);
               if constexpr (LPK > 1) sc = group_sum<LPK>(sc);
               return (e < npast || e == ecur) ? sc : -INFINITY;
             };
-            float ls = 0.f;
+            float ls = 0.f, pcur = 0.f;
             if (ecur < SLOTS) {
               // one pass: every entry's score stays in its lane
               const int e = slot;
@@ -699,6 +688,8 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
                 store_from_f32(&pw[e], pr);
                 ls = pr;
               }
+              // the current entry's weight, from the lane that computed it
+              pcur = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pr), ecur * LPK));
             } else {
               float mloc = -INFINITY;
               for (int e0 = 0; e0 <= ecur; e0 += SLOTS) {
@@ -727,7 +718,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             }
 #pragma unroll
             for (int off = DH; off < 64; off <<= 1) oa += __shfl_xor(oa, off, 64);
-            const float pc = load_as_f32(pw + ecur);
+            const float pc = ecur < SLOTS ? pcur : load_as_f32(pw + ecur);
             if (lane < DH) {
               store_from_f32(&xop[h * DH + lane], (oa + pc * kv[D + h * DH + lane]) * rls);
               if (DH == 128) store_from_f32(&xop[h * DH + 64 + lane], (ob + pc * kv[D + h * DH + 64 + lane]) * rls);
@@ -931,7 +922,10 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
                                          [&](int k, float& ss) { return gain_chunk<WT>(y, g_self, k, ss); },
                                          [&](int r, float v) {
                                            if (r < D) store_from_f32(&qb[r], v * qscale);
-                                           else kv[r - D] = round_to<WT>(v);
+                                           else {
+                                             kv[r - D] = round_to<WT>(v);
+                                             if (r < 2 * D) store_from_f32(&kcb[r - D], v);
+                                           }
                                          },
                                          p.eps);
               const unsigned mt = mtid_here();
