@@ -71,6 +71,23 @@ __device__ __forceinline__ float rsq_hw(float x) { return __builtin_amdgcn_rsqf(
 __device__ __forceinline__ float sigmoid_hw(float x) { return rcp_hw(1.0f + fast_exp2(-kLog2e * x)); }
 __device__ __forceinline__ float silu_hw(float x) { return x * sigmoid_hw(x); }
 
+// Sum over the lanes that hold the same dimension of a P.V product (lanes d, d + DH, ... for
+// DH < 64) without the LDS path: v_permlane16_swap / v_permlane32_swap bring the lower row (pair)
+// up, and the total lands in the top DH lanes (lane 64 - DH + d holds dimension d), added in the
+// same grouping as a butterfly.  Only the first result of each swap is used.
+template <int DH>
+__device__ __forceinline__ float sum_to_top_rows(float v) {
+  if constexpr (DH <= 16) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_permlane16_swap(u, u, false, false)[0]);   // rows 1, 3 += rows 0, 2
+  }
+  if constexpr (DH <= 32) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_permlane32_swap(u, u, false, false)[0]);   // rows 2, 3 += rows 0, 1
+  }
+  return v;
+}
+
 // threadIdx.x through an empty asm: lane-dependent offsets derived from it are recomputed
 // where they are used instead of being hoisted out of the step loop and held in registers.
 __device__ __forceinline__ unsigned tid_here() {
@@ -509,6 +526,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   constexpr int KQ = kq_of<WT>();         // memory row blocks per attention wave and chunk
   constexpr int RW = KQ * SLOTS;          // memory rows per attention wave and chunk
   constexpr int R1 = WPH * RW;            // memory rows per chunk and head
+  constexpr int TOP = DH < 64 ? 64 - DH : 0;   // first lane holding a summed P.V dimension
   constexpr int CPD = D / 64;             // chunks per lane of a K = D product (8 lanes per row)
   constexpr int CBX = cbx_of<WT>(), CBZ = cbz_of<WT>();
   constexpr int MGR = NTM / 8;            // 8-lane groups of the product waves
@@ -716,13 +734,13 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               if (DH < 128 || (r & 1) == 0) oa = O::dot(pp, vv, oa);
               else ob = O::dot(pp, vv, ob);
             }
-#pragma unroll
-            for (int off = DH; off < 64; off <<= 1) oa += __shfl_xor(oa, off, 64);
+            oa = sum_to_top_rows<DH>(oa);
             const float pc = ecur < SLOTS ? pcur : load_as_f32(pw + ecur);
-            if (lane < DH) {
-              store_from_f32(&xop[h * DH + lane], (oa + pc * kv[D + h * DH + lane]) * rls);
-              if (DH == 128) store_from_f32(&xop[h * DH + 64 + lane], (ob + pc * kv[D + h * DH + 64 + lane]) * rls);
+            if (lane >= TOP) {
+              const int d = lane - TOP;
+              store_from_f32(&xop[h * DH + d], (oa + pc * kv[D + h * DH + d]) * rls);
             }
+            if (DH == 128) store_from_f32(&xop[h * DH + 64 + lane], (ob + pc * kv[D + h * DH + 64 + lane]) * rls);
             wave_sync_lds();
             // W_O partial of this head: opart[h][r] = W_O[r, h*DH:(h+1)*DH] . attn_h, lanes over rows
             {
@@ -817,12 +835,11 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               else pv_blocks(std::false_type{});
             }
             // lanes with the same dim hold different key blocks: sum them
-#pragma unroll
-            for (int off = DH; off < 64; off <<= 1) oa += __shfl_xor(oa, off, 64);
+            oa = sum_to_top_rows<DH>(oa);
             lsum = group_sum<64>(lsum);
           }
           float* cp = cpart + wave * FX::CPS;
-          if (lane < DH) cp[4 + lane] = oa;
+          if (lane >= TOP) cp[4 + lane - TOP] = oa;
           if (DH == 128) cp[4 + 64 + lane] = ob;
           if (lane == 0) {
             cp[0] = m;
