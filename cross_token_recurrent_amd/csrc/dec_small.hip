@@ -497,7 +497,11 @@ struct Fixed {
   static constexpr unsigned swp = al16(sws + H * PSW * 4);           // window weights per head
   static constexpr unsigned opart = al16(swp + H * PSW * ESZ);      // W_O partials per head [H][D] fp32
   static constexpr unsigned yb = al16(opart + H * D * 4);            // residual after the W_O partials
-  static constexpr unsigned end = al16(yb + D * 4);
+  // merge weights [D][3D] (W_gate row | W_fb row) in LDS for bf16 at d = 64, so the product
+  // waves' registers can hold a separate QKV buffer
+  static constexpr bool MLDS = ESZ == 2 && D == 64;
+  static constexpr unsigned wm = al16(yb + D * 4);
+  static constexpr unsigned end = al16(wm + (MLDS ? 3 * D * D * ESZ : 0));
 };
 struct SmemTail {
   unsigned gains, xop, wo, ring, total;
@@ -549,6 +553,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   float* gains = reinterpret_cast<float*>(smem + sp.gains);
   float* opart = reinterpret_cast<float*>(smem + FX::opart);
   float* yb = reinterpret_cast<float*>(smem + FX::yb);
+  WT* wml = reinterpret_cast<WT*>(smem + FX::wm);
   WT* eb = reinterpret_cast<WT*>(smem + FX::eb);
   WT* sb = reinterpret_cast<WT*>(smem + FX::sb);
   float* y0 = reinterpret_cast<float*>(smem + FX::y0);
@@ -601,6 +606,14 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   auto is_attn = [&]() { return __builtin_amdgcn_readfirstlane(tid_here() >> 6) < NA; };
   // W_O of every layer stays in LDS: the window-attention wave of head h multiplies its
   // output by columns h*DH.. of W_O right after computing it
+  if constexpr (FX::MLDS) {
+    const WT* wg = static_cast<const WT*>(p.wgate);
+    const WT* wf = static_cast<const WT*>(p.wfb);
+    for (int i = threadIdx.x * 8; i < 3 * D * D; i += NT * 8) {
+      const int r = i / (3 * D), c = i % (3 * D);
+      O::store(wml + i, O::load(c < 2 * D ? wg + r * 2 * D + c : wf + r * D + c - 2 * D));
+    }
+  }
   for (int l = 0; l < L; ++l) {
     const WT* src = layer_w(l, p.l_wo);
     for (int i = threadIdx.x * 8; i < D * D; i += NT * 8) O::store(wol + l * D * D + i, O::load(src + i));
@@ -866,17 +879,27 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
         constexpr bool SWI = decltype(swc)::value;
         // FFN width: a compile-time constant whenever the output product has a fixed shape
         const int Fw = CPL2 > 0 ? 8 * GL2 * CPL2 : F;
-        Chunk X[CBX], Y[CBX], U[CBX], Z[CBZ];   // X: QKV, Qx, FFN in; Y: Ox; U: FFN out; Z: merge (resident)
+        // weight buffers: X: Qx, FFN in (and QKV unless it has its own); Y: Ox; U: FFN out; Q: QKV
+        // when the whole plan fits the register budget; Z: merge (resident unless in LDS)
+        constexpr int CBZE = FX::MLDS ? 0 : CBZ;
+        constexpr int CBY = CBX < D / 32 * CPD ? CBX : D / 32 * CPD;
+        constexpr int CBQ0 = CBX < 3 * D / 32 * CPD ? CBX : 3 * D / 32 * CPD;
+        constexpr bool SEPQ = (CBQ0 + CBY + 2 * CBX + CBZE) * static_cast<int>(sizeof(Chunk) / 4) <= 128;
+        constexpr int CBQ = SEPQ ? CBQ0 : CBX;
+        Chunk X[CBX], Y[CBY], U[CBX], Z[CBZE > 0 ? CBZE : 1], Qs[SEPQ ? CBQ : 1];
+        Chunk* Q = SEPQ ? Qs : X;
         auto merge_chunk = [&](int ri, int q) {
           const unsigned mt = mtid_here();
           const int sub = mt & 7, grp = mt >> 3;
           const int r = min(grp + ri * MGR, D - 1);   // rows past D (buffer slots beyond the merge): any row
-          return q < 2 * CPD ? O::load(at(wgate, r * 2 * D + (sub + 8 * q) * 8))
-                             : O::load(at(wfb, r * D + (sub + 8 * (q - 2 * CPD)) * 8));
+          if constexpr (FX::MLDS) return O::load(wml + r * 3 * D + (sub + 8 * q) * 8);
+          else
+            return q < 2 * CPD ? O::load(at(wgate, r * 2 * D + (sub + 8 * q) * 8))
+                               : O::load(at(wfb, r * D + (sub + 8 * (q - 2 * CPD)) * 8));
         };
 #pragma unroll
-        for (int pp = 0; pp < CBZ; ++pp) Z[pp] = merge_chunk(pp / (3 * CPD), pp % (3 * CPD));
-        wpre<WT, 8, CPD, CBX>(X, layer_w(0, p.l_qkv), 3 * D);
+        for (int pp = 0; pp < CBZE; ++pp) Z[pp] = merge_chunk(pp / (3 * CPD), pp % (3 * CPD));
+        wpre<WT, 8, CPD, CBQ>(Q, layer_w(0, p.l_qkv), 3 * D);
         __syncthreads();
         for (int step = 0; step < p.n; ++step) {
           const int t = p.t0 + step;
@@ -911,7 +934,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
 #pragma unroll
               for (int q = 0; q < 3 * CPD; ++q) {
                 const int pp = ri * 3 * CPD + q;
-                const Chunk w = pp < CBZ ? Z[pp < CBZ ? pp : 0] : merge_chunk(ri, q);
+                const Chunk w = pp < CBZE ? Z[pp < CBZE ? pp : 0] : merge_chunk(ri, q);
                 if (q < CPD) ge = O::dot(w, xg[q], ge);
                 else if (q < 2 * CPD) gsv = O::dot(w, xg[q], gsv);
                 else fs = O::dot(w, xg[CPD + q - 2 * CPD], fs);
@@ -935,7 +958,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
 
             // ---- P1: q, k, v = W_{Q,K,V} RMS(y; g_self); q scaled by log2(e)/sqrt(d_h) ----
             {
-              wmv<WT, 8, CPD, CBX, true>(X, layer_w(l, p.l_qkv), 3 * D,
+              wmv<WT, 8, CPD, CBQ, true>(Q, layer_w(l, p.l_qkv), 3 * D,
                                          [&](int k, float& ss) { return gain_chunk<WT>(y, g_self, k, ss); },
                                          [&](int r, float v) {
                                            if (r < D) store_from_f32(&qb[r], v * qscale);
@@ -951,7 +974,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             __syncthreads();   // P1
             // the window attention runs: request the Q_x and W_Ox weights of this layer
             wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_wqx), D);
-            wpre<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D);
+            wpre<WT, 8, CPD, CBY>(Y, layer_w(l, p.l_wox), D);
             __syncthreads();   // P2
 
             // ---- P4: y_b = y + sum_h W_O[:, h] attn_h (the per-head partials of the window
@@ -976,6 +999,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
             if constexpr (!SWI) wpre<WT, 8, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
             else wpre_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), Fw);
             if constexpr (CPL2 > 0) wpre<WT, GL2, CPL2, CBX>(U, layer_w(l, p.l_fout), D);
+            if constexpr (SEPQ) wpre<WT, 8, CPD, CBQ>(Q, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
             __syncthreads();   // P5
 
             // ---- P7: y += W_Ox attn; the operand chunk (8 dims of one head) combines the WPH
@@ -1006,7 +1030,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               for (int i = 0; i < 8; ++i) o[i] *= rlt;
               return O::pack(o);
             };
-            wmv<WT, 8, CPD, CBX>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] = yb[r] + v; });
+            wmv<WT, 8, CPD, CBY>(Y, layer_w(l, p.l_wox), D, cross_out, [&](int r, float v) { y[r] = yb[r] + v; });
             __syncthreads();   // P7
 
             // ---- P8: FFN input product (tied with encoder layer l), activation into xop ----
@@ -1018,7 +1042,7 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
               } else {
                 wmv_swiglu<WT, CPD, CBX>(X, layer_w(l, p.l_fin), Fw, xf, xop, p.eps);
               }
-              wpre<WT, 8, CPD, CBX>(X, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
+              if constexpr (!SEPQ) wpre<WT, 8, CPD, CBQ>(Q, layer_w(last ? 0 : l + 1, p.l_qkv), 3 * D);
             }
             __syncthreads();   // P8
 
