@@ -13,25 +13,27 @@
 // latency-bound phases, while the memory rows of the cross-attention (a few hundred KB per
 // step and sequence) must stream from HBM or the Infinity Cache without stalling that
 // chain.  Independent sequences never synchronise, so each sequence gets one workgroup of
-// 12 waves (three per SIMD) that keeps its window caches, residual stream, gains and small
-// vectors in LDS and splits the work by role, each role running its own loop through the
-// same sequence of workgroup barriers (the gated merge, then eight phases per layer):
+// 12 waves (three per SIMD) that keeps its window caches, residual stream, gains, W_O (and at
+// d = 64 the merge weights) in LDS and splits the work by role, each role running its own
+// loop through the same sequence of workgroup barriers (the gated merge, then seven phases
+// per layer: QKV, window attention, Q_x, cross-attention, W_Ox, FFN in, FFN out):
 //   * 4 product waves run the gated merge and every matrix-vector product: 8- or 16-lane
-//     groups per row, the weights of each product requested two products ahead into
-//     registers (the merge weights stay resident), RMSNorm fused into the operand fetch,
-//     the gated merge fused into the gate/feedback products and SwiGLU into the FFN input
-//     product;
+//     groups per row, weights in registers, RMSNorm fused into the operand fetch, the gated
+//     merge fused into the gate/feedback products and SwiGLU/GELU into the FFN input product.
+//     Every weight request is issued in the two phases where these waves would otherwise
+//     wait (window and cross attention), each product into its own register buffer;
 //   * 8 attention waves hold the memory rows of one layer in registers (each a head and a
-//     contiguous share of its rows).  The rows of the next layer are requested over the
-//     four phases after the current cross-attention, while the product waves compute, so
-//     the requests drain in the background and have a whole layer to arrive; the product
-//     waves request only weights, so their loads never queue behind rows (the vector
-//     memory counter of a wave retires in order).  Scores use lanes over keys; P.V uses
-//     lanes over (dim, 8-key block) on the key-blocked value layout, so a lane's dot
-//     products run over keys and the lane reduction at the end is at most two steps;
+//     contiguous share of its rows).  The rows of the next layer are requested one 64-row
+//     block at a time in each of the six phases between two cross-attentions, so the
+//     requests drain in the background without crowding the product waves' weight requests
+//     on the CU's vector-memory path; the product waves request only weights, so their loads
+//     never queue behind rows (the vector memory counter of a wave retires in order).
+//     Scores use lanes over keys; P.V uses lanes over (dim, 8-key block) on the key-blocked
+//     value layout, so a lane's dot products run over keys and the sum over its lanes takes
+//     at most two row swaps;
 //   * window self-attention runs on one attention wave per head: scores with lanes over
 //     the ring slots, P.V with lanes over (dim, 8-slot block) of a key-blocked copy of the
-//     value ring.
+//     value ring, then the head's share of the W_O product.
 // bf16 mode: matrix-product operands (activations, q, P) are bf16 and every product
 // accumulates in fp32 (v_dot2c_f32_bf16); the residual stream, softmax statistics and s_t
 // stay fp32.  Scores are kept in the log2 domain (q pre-scaled by log2(e)/sqrt(d_h)).
@@ -620,8 +622,8 @@ __global__ __launch_bounds__(NT) void dec_small_k(DecSmallParams p) {
   }
 
   // The two roles run their own step loops; both pass the same sequence of workgroup
-  // barriers (one per phase: merge, then P1..P9 per layer), so each role's registers are
-  // allocated for its own work only.
+  // barriers (one per phase: merge, then P1, P2, P4, P5, P7, P8, P9 per layer), so each
+  // role's registers are allocated for its own work only.
   if (is_attn()) {
     // ======== attention waves: memory rows (key rows R[2i + c], value items
     // R[2KQ + 2i + r] of block i), window attention, cross-attention (partial softmax
