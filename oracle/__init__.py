@@ -16,6 +16,7 @@ from .rlt_oracle import (  # noqa: F401
     logits,
     replay,
     replay_batch,
+    score_actions,
     rms_norm,
     sigmoid,
     silu,

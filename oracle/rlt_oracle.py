@@ -44,7 +44,9 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
 Pins (tests/test_oracle_pins.py): library sub-layers (torch fp64 rms_norm, gelu, silu,
 sdpa), causal encoder vs a torch sdpa pass, gate-saturated decoder vs a token-parallel
 masked sdpa pass, W=1 and T=1 closed forms, causality, split invariance, incremental ==
-replay, G equivalence, window >= T equivalence, state path length t*L_D.
+replay, G equivalence, window >= T equivalence, state path length t*L_D; action scoring
+against closed forms (zero head, one dominant logit, normalisation over all actions,
+temperature on a hand-expanded softmax).
 """
 from __future__ import annotations
 
@@ -310,6 +312,32 @@ def decode(m: OracleModel, st: OracleState, n: int) -> np.ndarray:
 def logits(m: OracleModel, S: np.ndarray) -> np.ndarray:
     """Next-token logits read from s_t: W_out s_t (token-parallel, off the loop)."""
     return S @ m.w["w_out"].T
+
+
+def score_actions(w_out: np.ndarray, S: np.ndarray, actions: Sequence[int],
+                  behaviour_logp: Optional[Sequence[float]] = None, temperature: float = 1.0
+                  ) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Score each action under the current policy ([FI] model-RL co-design paragraph: the
+    trainer rebuilds the states under the current weights, scores every action, and the
+    recorded behaviour log-probability is the denominator of the importance ratio).
+
+    Row i: z = (W_out s_i) / temperature;  logp_i = z[a_i] - log sum_v exp(z_v)
+    (the log-sum-exp taken with its maximum subtracted);  ratio_i = exp(logp_i - behaviour_i).
+    Reading: the current policy is the full softmax at the given temperature; any
+    truncation the sampler used lives in the behaviour log-probabilities only.
+    """
+    S = np.asarray(S, dtype=F64)
+    Z = (S @ np.asarray(w_out, dtype=F64).T) / float(temperature)
+    logp = np.empty(S.shape[0], dtype=F64)
+    for i, a in enumerate(actions):
+        z = Z[i]
+        zmax = z.max()
+        lse = zmax + math.log(float(np.exp(z - zmax).sum()))
+        logp[i] = z[int(a)] - lse
+    ratio = None
+    if behaviour_logp is not None:
+        ratio = np.exp(logp - np.asarray(behaviour_logp, dtype=F64))
+    return logp, ratio
 
 
 # ---------------------------------------------------------------------------

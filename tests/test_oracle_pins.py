@@ -435,3 +435,52 @@ def test_property_teacher_forced_and_split(d_heads, L, W, grouped, kind, T, seed
     O.encode(m, st_, tok[:split])
     S2 = list(O.decode(m, st_, split)) + [O.step(m, st_, x)[0] for x in tok[split:]]
     np.testing.assert_allclose(np.array(S2), S, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Action scoring ([FI] model-RL co-design paragraph): closed forms
+# ---------------------------------------------------------------------------
+
+def test_score_actions_zero_head_is_uniform():
+    """W_out = 0: every action has probability 1/V at any temperature."""
+    V, d = 13, 5
+    rng = np.random.default_rng(3)
+    S = rng.standard_normal((4, d))
+    acts = [0, 12, 5, 7]
+    behav = [-1.0, -2.5, math.log(1 / V), 0.0]
+    for tau in (1.0, 0.3):
+        lp, r = O.score_actions(np.zeros((V, d)), S, acts, behav, temperature=tau)
+        np.testing.assert_allclose(lp, -math.log(V), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(r, [math.exp(-math.log(V) - b) for b in behav], rtol=1e-14)
+
+
+def test_score_actions_one_dominant_logit():
+    """Only row k of W_out is non-zero and aligned with s: z_k = c, every other logit 0, so
+    logp_k = c - log(e^c + V - 1) and logp_other = -log(e^c + V - 1)."""
+    V, d, k = 9, 4, 6
+    s = np.array([0.5, -1.0, 2.0, 0.25])
+    for c in (0.0, 3.0, 60.0, 700.0):
+        W = np.zeros((V, d))
+        W[k] = s * (c / float(s @ s))
+        lp, _ = O.score_actions(W, s[None, :], [k])
+        lq, _ = O.score_actions(W, s[None, :], [2])
+        # log(e^c + V - 1) = c + log1p((V - 1) e^{-c}), stable for large c
+        lse = c + math.log1p((V - 1) * math.exp(-c))
+        assert abs(lp[0] - (c - lse)) < 1e-12 * max(1.0, c)
+        assert abs(lq[0] - (-lse)) < 1e-12 * max(1.0, c)
+
+
+def test_score_actions_normalised_and_hand_expanded():
+    """exp(logp) over all V actions sums to one, and each logp matches a softmax expanded by
+    hand (pure-Python loops, math.fsum) at two temperatures."""
+    V, d = 7, 3
+    rng = np.random.default_rng(11)
+    W = rng.standard_normal((V, d))
+    s = rng.standard_normal(d)
+    for tau in (1.0, 0.7):
+        lp, _ = O.score_actions(W, np.repeat(s[None, :], V, 0), list(range(V)), temperature=tau)
+        assert abs(math.fsum(math.exp(x) for x in lp) - 1.0) < 1e-13
+        z = [math.fsum(W[v, j] * s[j] for j in range(d)) / tau for v in range(V)]
+        lse = math.log(math.fsum(math.exp(x) for x in z))
+        for v in range(V):
+            assert abs(lp[v] - (z[v] - lse)) < 1e-13
