@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_small_k_small_traffic.md")
 KERNEL_SOURCES = ["cross_token_recurrent_amd/csrc/dec_small.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
 
@@ -121,6 +122,46 @@ def cpu_baseline(wl, weights, tokens, budget_s: float = 20.0):
                       f"fp64 numpy, one sequence per worker process, {wall:.1f} s wall"}
 
 
+def scoring_leg(steps: int, warmup: int):
+    """RL action scoring (rlt_score_actions) on the 300M-class head: V=32000, d=1024, bf16,
+    N = 64 sequences x 1024 response positions.  The head GEMM dominates: 2*N*d*V flops
+    per call, priced against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import cross_token_recurrent_amd as rlt
+    from workloads import ModelConfig, make_weights
+
+    cfg = ModelConfig(vocab=32000, d_model=1024, n_heads=16, n_layers=1, ffn_dim=64, ffn_kind="swiglu",
+                      window=4, mem_groups=1, dtype="bf16")
+    dev = torch.device("cuda:0")
+    model = rlt.Model(cfg, make_weights(cfg, 7), device=dev)
+    n = 64 * 1024
+    g = torch.Generator(device="cpu").manual_seed(8)
+    s = torch.randn(n, cfg.d_model, generator=g).to(dev)
+    acts = torch.randint(0, cfg.vocab, (n,), generator=g, dtype=torch.int32).to(dev)
+    behav = torch.full((n,), -10.0, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        rlt.rlt_score_actions(model, s, acts, 1.0, behav, stream=stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(steps):
+        rlt.rlt_score_actions(model, s, acts, 1.0, behav, stream=stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    flops = 2.0 * n * cfg.d_model * cfg.vocab
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"RL action scoring, head V={cfg.vocab} d={cfg.d_model} bf16, N={n} rows "
+                        f"(64 sequences x 1024 response positions), logp + ratio, logits never written",
+            "rows_per_s": n / (ms * 1e-3), "ms_per_call": ms,
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                         "kernel": "score_lse_k + score_finish_k", "algorithmic_flops_per_call": flops}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +169,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="small")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scoring", action="store_true", help="skip the RL action-scoring measurement")
     ap.add_argument("--copy-kernel", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.copy_kernel:
@@ -217,6 +259,8 @@ def main():
                      "algorithmic_bytes_per_launch": dec_bytes},
         "cpu_baseline": None,
     }
+    if not args.no_scoring:
+        line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, weights, tokens)
     print(json.dumps(line), flush=True)

@@ -16,6 +16,7 @@ from .rlt import (  # noqa: F401
     rlt_logits,
     rlt_model_workspace_bytes,
     rlt_param_table,
+    rlt_score_actions,
     rlt_state_load_encoder_outputs,
     rlt_state_read_encoder_outputs,
 )

@@ -642,6 +642,20 @@ int rlt_logits(const rlt_model* model, const float* s, int64_t n_rows, float* lo
   return RLT_OK;
 }
 
+int rlt_score_actions(const rlt_model* model, const float* s, const int32_t* actions, int64_t n_rows,
+                      float temperature, const float* behaviour_logp, float* logp_out, float* ratio_out,
+                      void* stream) {
+  if (!model || !s || !actions || !logp_out) return fail(RLT_ERR_INVALID, "model, s, actions and logp_out must be non-NULL");
+  if (n_rows < 1 || n_rows > 0x7fffffff) return fail(RLT_ERR_INVALID, "n_rows out of range");
+  if (!(temperature > 0.f)) return fail(RLT_ERR_INVALID, "temperature must be > 0");
+  if (ratio_out && !behaviour_logp) return fail(RLT_ERR_INVALID, "ratio_out needs behaviour_logp");
+  const ModelLayout& M = model->lay;
+  RLT_HIP(launch_score_actions(s, model->ws + M.wout, actions, behaviour_logp, logp_out, ratio_out,
+                               static_cast<int>(n_rows), M.D, M.V, temperature, M.dtype, as_stream(stream)),
+          "score actions");
+  return RLT_OK;
+}
+
 int rlt_decoder_step(const rlt_model* model, rlt_state* state, const int32_t* tokens, float* s_out,
                      float* logits, void* stream) {
   int rc = check_pair(model, state);

@@ -114,6 +114,13 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
 
+// Action scoring: logp_i = log softmax(W_out s_i / temperature)[a_i] (and the ratio against
+// behav when ratio is non-null), without writing the logits.  logp holds the row
+// log-sum-exp between the two kernels.
+hipError_t launch_score_actions(const float* s, const void* w_out, const int32_t* actions, const float* behav,
+                                float* logp, float* ratio, int N, int D, int V, float temperature, int dtype,
+                                hipStream_t st);
+
 // Causal attention for Bc sequences x H heads, queries at positions t0..t0+n-1
 // (q rows from a [Bc*n, ldq] buffer, head h at column h*dh), keys/values at positions
 // 0..t0+n-1 read from a [B][H][T][dh] layout (kv_ld_b = stride between sequences,

@@ -66,6 +66,7 @@ _SIGS = {
     "rlt_decoder_replay": [_P, _P, _I32, _P, _P],
     "rlt_decoder_step": [_P, _P, _P, _P, _P, _P],
     "rlt_logits": [_P, _P, ctypes.c_int64, _P, _P],
+    "rlt_score_actions": [_P, _P, _P, ctypes.c_int64, ctypes.c_float, _P, _P, _P, _P],
     "rlt_state_load_encoder_outputs": [_P, _P, _P, _P, _P, _I32, _P],
     "rlt_state_read_encoder_outputs": [_P, _P, _I32, _I32, _P, _P, _P, _P],
     "rlt_decoder_path": [_P, _I32, ctypes.POINTER(_I32)],
@@ -176,6 +177,26 @@ def rlt_logits(model: "Model", s: torch.Tensor, out: Optional[torch.Tensor] = No
     assert out.is_contiguous() and out.numel() == rows * model.vocab
     _check(load_library().rlt_logits(model.handle, _ptr(s), rows, _ptr(out), _stream(stream)))
     return out
+
+
+def rlt_score_actions(model: "Model", s: torch.Tensor, actions: torch.Tensor, temperature: float = 1.0,
+                      behaviour_logp: Optional[torch.Tensor] = None, stream=None):
+    """logp = log softmax(W_out s / temperature)[action] per row, and the importance ratio
+    exp(logp - behaviour_logp) when behaviour_logp is given (else None)."""
+    assert s.dtype == torch.float32 and s.is_contiguous() and s.shape[-1] == model.d_model
+    rows = s.numel() // model.d_model
+    assert actions.dtype == torch.int32 and actions.is_contiguous() and actions.numel() == rows
+    logp = torch.empty(*s.shape[:-1], dtype=torch.float32, device=s.device)
+    ratio = None
+    if behaviour_logp is not None:
+        assert behaviour_logp.dtype == torch.float32 and behaviour_logp.is_contiguous()
+        assert behaviour_logp.numel() == rows
+        ratio = torch.empty_like(logp)
+    _check(load_library().rlt_score_actions(model.handle, _ptr(s), _ptr(actions), rows, float(temperature),
+                                            _ptr(behaviour_logp) if behaviour_logp is not None else None,
+                                            _ptr(logp), _ptr(ratio) if ratio is not None else None,
+                                            _stream(stream)))
+    return logp, ratio
 
 
 def rlt_state_load_encoder_outputs(model: "Model", state: "State", e: torch.Tensor, mem_k: torch.Tensor,

@@ -178,6 +178,23 @@ int rlt_decoder_step(const rlt_model* model, rlt_state* state, const int32_t* to
 int rlt_logits(const rlt_model* model, const float* s, int64_t n_rows, float* logits,
                void* stream);
 
+/* rlt_score_actions: scores actions under the current policy for RL ([FI] model-RL co-design
+ * paragraph: the trainer rebuilds every state under the current weights, scores each action,
+ * and the behaviour log-probability recorded by the sampler is the denominator of the
+ * importance ratio):
+ *   logp_i  = log softmax(W_out s_i / temperature)[a_i]
+ *   ratio_i = exp(logp_i - behaviour_logp_i)
+ * computed without writing the [N, V] logits (a running log-sum-exp over vocabulary tiles).
+ * s: device fp32 [N, d] (rows of s_t, e.g. the response positions of a replay);
+ * actions: device int32 [N], ids in [0, V) (an id outside gives logp = NaN);
+ * temperature > 0 (1 = the plain softmax); behaviour_logp: device fp32 [N] or NULL;
+ * logp_out: device fp32 [N]; ratio_out: device fp32 [N] or NULL (needs behaviour_logp).
+ * Errors: RLT_ERR_INVALID for NULL required pointers, n_rows out of range, temperature <= 0
+ * or ratio_out without behaviour_logp. */
+int rlt_score_actions(const rlt_model* model, const float* s, const int32_t* actions, int64_t n_rows,
+                      float temperature, const float* behaviour_logp, float* logp_out,
+                      float* ratio_out, void* stream);
+
 /* ---- test hooks (decoder in isolation, encoder outputs) -----------------------------
  * rlt_state_load_encoder_outputs writes externally computed e (device fp32 [B, n, d])
  * and memory rows (device fp32 [G, B, n, d] each for keys and values) for positions

@@ -1,0 +1,171 @@
+"""Action scoring on the GPU (rlt_score_actions) against the oracle's score_actions.
+
+Scoring follows the RL contract of the pages ([FI] model-RL co-design paragraph): every
+action is scored under the current weights, logp = log softmax(W_out s / temperature)[a],
+and the behaviour log-probability recorded at sampling time is the denominator of the
+importance ratio.
+
+Tolerances.  The kernel rounds s to the storage type of W_out (the operand precision of
+the token-parallel products) and accumulates in fp32.  Against the oracle fed the same
+rounded operands the only difference is fp32 accumulation order, so logp must agree to
+SCORE_ABS = 1e-4 absolute in both modes and the ratio to the matching relative bound.
+In bf16 mode the result against the unrounded fp64 oracle is checked with the mode's
+relative bound, |gpu - ref| <= 3e-2 * max(|ref|, 1).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import ModelConfig, make_weights
+
+torch = pytest.importorskip("torch")
+import cross_token_recurrent_amd as rlt  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+SCORE_ABS = 1e-4
+BF16_REL = 3e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rlt.load_library()
+    return torch.device("cuda:0")
+
+
+def _cfg(vocab, d, dtype):
+    return ModelConfig(vocab=vocab, d_model=d, n_heads=max(1, d // 64), n_layers=1, ffn_dim=64,
+                       ffn_kind="gelu", window=4, mem_groups=1, dtype=dtype)
+
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _case(dev, vocab, d, dtype, n, seed, temperature=1.0, scale=1.0, with_behaviour=True, actions=None):
+    cfg = _cfg(vocab, d, dtype)
+    w = make_weights(cfg, seed)
+    model = rlt.Model(cfg, w, device=dev)
+    g = np.random.default_rng(seed + 1)
+    S = (g.standard_normal((n, d)) * scale).astype(np.float32)
+    if actions is None:
+        actions = g.integers(0, vocab, size=n)
+    actions = np.asarray(actions, dtype=np.int32)
+    w_out = w["w_out"].astype(np.float64)
+    S_op = _round_bf16(S) if dtype == "bf16" else S.astype(np.float64)
+    lp_ref, _ = oracle.score_actions(w_out, S_op, actions, None, temperature)
+    behav = (lp_ref + 0.1 * g.standard_normal(n)).astype(np.float32) if with_behaviour else None
+    _, ratio_ref = oracle.score_actions(w_out, S_op, actions, behav, temperature) if with_behaviour else (None, None)
+    lp, ratio = rlt.rlt_score_actions(model, torch.from_numpy(S).to(dev), torch.from_numpy(actions).to(dev),
+                                      temperature, torch.from_numpy(behav).to(dev) if with_behaviour else None)
+    torch.cuda.synchronize()
+    lp = lp.cpu().numpy()
+    assert np.isfinite(lp).all()
+    err = float(np.abs(lp - lp_ref).max())
+    assert err <= SCORE_ABS, f"logp max abs error {err:.3e}"
+    if with_behaviour:
+        ratio = ratio.cpu().numpy()
+        rerr = float((np.abs(ratio - ratio_ref) / ratio_ref).max())
+        assert rerr <= 2 * SCORE_ABS, f"ratio max relative error {rerr:.3e}"
+    else:
+        assert ratio is None
+    if dtype == "bf16":
+        lp_full, _ = oracle.score_actions(w_out, S.astype(np.float64), actions, None, temperature)
+        rel = float((np.abs(lp - lp_full) / np.maximum(np.abs(lp_full), 1.0)).max())
+        assert rel <= BF16_REL, f"logp vs unrounded oracle: {rel:.3e}"
+    print(f"  V={vocab} d={d} {dtype} N={n} T={temperature}: logp max-abs {err:.3e}", flush=True)
+    return lp, lp_ref
+
+
+def test_score_tiny_fp32(dev):
+    """Tiny fp32 head (vocab 256, d=64): ragged rows over three row tiles."""
+    _case(dev, 256, 64, "fp32", 300, 11)
+
+
+def test_score_small_bf16(dev):
+    """Small bf16 head (vocab 512, d=64), temperature 0.7."""
+    _case(dev, 512, 64, "bf16", 1000, 12, temperature=0.7)
+
+
+def test_score_ragged_vocab(dev):
+    """A vocabulary smaller than one column tile and not a multiple of 16 (V=97), and one of
+    2.5 tiles (V=300), in both modes; no behaviour log-probs."""
+    for dtype in ("fp32", "bf16"):
+        _case(dev, 97, 64, dtype, 130, 13, with_behaviour=False)
+        _case(dev, 300, 128, dtype, 129, 14, temperature=1.3)
+
+
+def test_score_peaked_logits(dev):
+    """Large logits (s scaled by 60, temperature 0.5): the running log-sum-exp must stay
+    finite and exact when one column dominates each row."""
+    for dtype in ("fp32", "bf16"):
+        _case(dev, 512, 128, dtype, 200, 15, temperature=0.5, scale=60.0)
+
+
+def test_score_first_and_last_action(dev):
+    """Actions 0 and V-1 on every row pair (the first and last column of the head)."""
+    acts = np.array([0, 96] * 40, dtype=np.int32)
+    _case(dev, 97, 64, "fp32", 80, 16, actions=acts)
+    acts = np.array([0, 511] * 70, dtype=np.int32)
+    _case(dev, 512, 64, "bf16", 140, 17, actions=acts)
+
+
+def test_score_large_head_bf16(dev):
+    """The 300M-class head (vocab 32000, d=1024, bf16) on 300 ragged rows."""
+    _case(dev, 32000, 1024, "bf16", 300, 18, temperature=1.0)
+
+
+def test_score_invalid_action_is_nan(dev):
+    cfg = _cfg(97, 64, "fp32")
+    model = rlt.Model(cfg, make_weights(cfg, 19), device=dev)
+    S = torch.randn(4, 64, generator=torch.Generator().manual_seed(1)).to(dev)
+    acts = torch.tensor([-1, 97, 5, 1000], dtype=torch.int32, device=dev)
+    lp, _ = rlt.rlt_score_actions(model, S, acts)
+    lp = lp.cpu().numpy()
+    assert np.isnan(lp[[0, 1, 3]]).all() and np.isfinite(lp[2])
+
+
+def test_score_argument_errors(dev):
+    cfg = _cfg(97, 64, "fp32")
+    model = rlt.Model(cfg, make_weights(cfg, 20), device=dev)
+    S = torch.zeros(2, 64, device=dev)
+    acts = torch.zeros(2, dtype=torch.int32, device=dev)
+    with pytest.raises(rlt.RltError) as ei:
+        rlt.rlt_score_actions(model, S, acts, temperature=0.0)
+    assert ei.value.name == "RLT_ERR_INVALID"
+    lib = rlt.load_library()
+    import ctypes
+    out = torch.empty(2, device=dev)
+    rc = lib.rlt_score_actions(model.handle, ctypes.c_void_p(S.data_ptr()), ctypes.c_void_p(acts.data_ptr()), 2,
+                               1.0, None, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(out.data_ptr()), None)
+    assert rc != 0
+
+
+def test_score_after_replay(dev):
+    """Replay, then score the response half of every sequence: the GPU chain
+    (rlt_decoder_replay -> rlt_score_actions) against the oracle chain (replay -> score)."""
+    from gpu_helpers import oracle_replay
+    from workloads import make_tokens
+    cfg = ModelConfig(vocab=256, d_model=64, n_heads=4, n_layers=2, ffn_dim=256, ffn_kind="gelu", window=8,
+                      mem_groups=1, dtype="fp32")
+    w = make_weights(cfg, 21)
+    B, T, P = 3, 48, 24
+    tok = make_tokens(cfg.vocab, B, T, "uniform", 22)
+    model = rlt.Model(cfg, w, device=dev)
+    state = rlt.State(model, B, T)
+    tt = torch.from_numpy(tok).to(dev)
+    rlt.rlt_encoder_forward(model, state, tt)
+    S = torch.empty(B, T, cfg.d_model, dtype=torch.float32, device=dev)
+    rlt.rlt_decoder_replay(model, state, T, S)
+    # the action at position t is the token at t + 1 (next-token policy); score positions P-1 .. T-2
+    acts = tt[:, P:].contiguous()
+    Sr = S[:, P - 1:T - 1].contiguous()
+    lp, _ = rlt.rlt_score_actions(model, Sr, acts)
+    torch.cuda.synchronize()
+    S_ref, _ = oracle_replay(cfg, w, tok)
+    ref = np.stack([oracle.score_actions(w["w_out"], S_ref[b, P - 1:T - 1], tok[b, P:])[0] for b in range(B)])
+    err = float(np.abs(lp.cpu().numpy() - ref).max())
+    assert err <= SCORE_ABS, f"replay+score logp max abs error {err:.3e}"
