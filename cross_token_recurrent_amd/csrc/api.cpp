@@ -172,6 +172,7 @@ int pack_weights(const rlt_model& m, const float* w, hipStream_t st) {
   TRY(f32(src("g_dec_cross"), L.g_dec_cross, static_cast<size_t>(L.L) * D));
   TRY(f32(src("g_dec_ffn"), L.g_dec_ffn, static_cast<size_t>(L.L) * D));
   TRY(f32(src("g_dec_final"), L.g_dec_final, D));
+  if (L.has_wout_frag) RLT_HIP(launch_pack_score_head(src("w_out"), ws + L.wout_frag, L.V, D, st), "pack head fragments");
 #undef TRY
   return RLT_OK;
 }
@@ -259,6 +260,8 @@ bool compute_model_layout(const rlt_config& c, ModelLayout* m) {
   L.g_dec_cross = take(L.L * D * 4);
   L.g_dec_ffn = take(L.L * D * 4);
   L.g_dec_final = take(D * 4);
+  L.has_wout_frag = score_frag_eligible(L.dtype, L.D) ? 1 : 0;
+  L.wout_frag = L.has_wout_frag ? take((V + 15) / 16 * 16 * D * 2) : 0;
   L.total = off;
   return true;
 }
@@ -650,7 +653,8 @@ int rlt_score_actions(const rlt_model* model, const float* s, const int32_t* act
   if (!(temperature > 0.f)) return fail(RLT_ERR_INVALID, "temperature must be > 0");
   if (ratio_out && !behaviour_logp) return fail(RLT_ERR_INVALID, "ratio_out needs behaviour_logp");
   const ModelLayout& M = model->lay;
-  RLT_HIP(launch_score_actions(s, model->ws + M.wout, actions, behaviour_logp, logp_out, ratio_out,
+  RLT_HIP(launch_score_actions(s, model->ws + M.wout, M.has_wout_frag ? model->ws + M.wout_frag : nullptr, actions,
+                               behaviour_logp, logp_out, ratio_out,
                                static_cast<int>(n_rows), M.D, M.V, temperature, M.dtype, as_stream(stream)),
           "score actions");
   return RLT_OK;

@@ -37,8 +37,16 @@ struct ModelLayout {
   size_t wkvm, group_stride;
   size_t gains;  // fp32 region
   size_t g_enc_attn, g_enc_ffn, g_enc_final, g_dec_self, g_dec_cross, g_dec_ffn, g_dec_final;  // byte offsets
+  // fragment-major bf16 copy of w_out read by action scoring (present when has_wout_frag):
+  // 16-byte chunk ((cb * D/64 + ks) * 2 + h) * 64 + lane holds
+  // w_out[16 cb + lane % 16][64 ks + 16 (lane / 16) + 8 h .. + 8], rows past V zero
+  int has_wout_frag;
+  size_t wout_frag;
   size_t total;
 };
+
+// Heads that get the fragment-major copy (bf16, d a multiple of 256, d <= 2048).
+inline bool score_frag_eligible(int dtype, int D) { return dtype == RLT_DTYPE_BF16 && D % 256 == 0 && D <= 2048; }
 
 // ---------------------------------------------------------------------------
 // State blob (byte offsets from the state base).
@@ -117,9 +125,11 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
 // Action scoring: logp_i = log softmax(W_out s_i / temperature)[a_i] (and the ratio against
 // behav when ratio is non-null), without writing the logits.  logp holds the row
 // log-sum-exp between the two kernels.
-hipError_t launch_score_actions(const float* s, const void* w_out, const int32_t* actions, const float* behav,
-                                float* logp, float* ratio, int N, int D, int V, float temperature, int dtype,
-                                hipStream_t st);
+hipError_t launch_score_actions(const float* s, const void* w_out, const void* w_frag, const int32_t* actions,
+                                const float* behav, float* logp, float* ratio, int N, int D, int V, float temperature,
+                                int dtype, hipStream_t st);
+// Writes the fragment-major bf16 copy of the fp32 head w [V][D] (layout in ModelLayout).
+hipError_t launch_pack_score_head(const float* w, void* dst, int V, int D, hipStream_t st);
 
 // Causal attention for Bc sequences x H heads, queries at positions t0..t0+n-1
 // (q rows from a [Bc*n, ldq] buffer, head h at column h*dh), keys/values at positions

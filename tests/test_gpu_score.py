@@ -113,6 +113,19 @@ def test_score_first_and_last_action(dev):
     _case(dev, 512, 64, "bf16", 140, 17, actions=acts)
 
 
+def test_score_resident_rows_paths(dev):
+    """bf16 heads with d a multiple of 256 take the resident-rows kernel (64 rows per
+    workgroup up to d=1024, 32 rows up to d=2048): ragged row tails (129 = 2*64 + 1,
+    45 rows over two 32-row blocks), vocabularies below one 256-column step (97) and with a
+    partial last step (300, 1000), large peaked logits."""
+    _case(dev, 300, 256, "bf16", 129, 31, temperature=0.8)
+    _case(dev, 97, 512, "bf16", 70, 32)
+    _case(dev, 1000, 2048, "bf16", 45, 33, temperature=1.1)
+    _case(dev, 512, 256, "bf16", 200, 34, temperature=0.5, scale=60.0)
+    acts = np.array([0, 299] * 33, dtype=np.int32)
+    _case(dev, 300, 768, "bf16", 66, 35, actions=acts)
+
+
 def test_score_large_head_bf16(dev):
     """The 300M-class head (vocab 32000, d=1024, bf16) on 300 ragged rows."""
     _case(dev, 32000, 1024, "bf16", 300, 18, temperature=1.0)
