@@ -210,18 +210,18 @@ __global__ __launch_bounds__(NTH) void score_lse_k(ScoreArgs a) {
 // pieces of one (16-column block, stage, half) are contiguous, so each load instruction reads
 // one contiguous kilobyte.  (Read from the row-major head, each lane quad would touch four
 // different rows, and the vector memory path, not the bytes, would bound the kernel.)
-constexpr int RES_NW = 4;                // waves
 constexpr int RES_COLS = 64;             // vocabulary columns per wave per step
-constexpr int RES_VSTEP = RES_NW * RES_COLS;
 constexpr int RES_KST = 64;              // k per register stage
 constexpr int RES_LDS_ELEMS = 64 * 1032; // bf16 elements of the resident block (64 rows of d=1024 + pad)
 
-template <int RB, int NS>
-__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int RB, int NW, int NS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void score_lse_res_k(ScoreArgs a) {
   constexpr int RI = RB / 16;   // 16-row blocks
+  constexpr int NT = NW * 64;
+  constexpr int RES_VSTEP = NW * RES_COLS;
   __shared__ __attribute__((aligned(16))) bf16_t As[RES_LDS_ELEMS];
-  __shared__ float part[RES_NW][RB][2];
+  __shared__ float part[NW][RB][2];
 
   const int D = a.D, pitch = D + 8;
   const int m0 = blockIdx.x * RB;
@@ -231,7 +231,7 @@ void score_lse_res_k(ScoreArgs a) {
   const float sc = a.inv_temp * kLog2e;
 
   // resident rows: fp32 -> bf16, 8 elements per thread per pass; rows past N are zero
-  for (int c = threadIdx.x; c < RB * (D / 8); c += NTH) {
+  for (int c = threadIdx.x; c < RB * (D / 8); c += NT) {
     const int r = c / (D / 8), k = (c % (D / 8)) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (r < mrows) {
@@ -351,10 +351,10 @@ void score_lse_res_k(ScoreArgs a) {
     const int r = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < RES_NW; ++w) M = fmaxf(M, part[w][r][0]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, part[w][r][0]);
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < RES_NW; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = part[w][r][0];
       L += mw == -INFINITY ? 0.f : part[w][r][1] * __builtin_amdgcn_exp2f(mw - M);
     }
@@ -402,11 +402,11 @@ __global__ __launch_bounds__(NTH) void score_finish_k(ScoreArgs a) {
 
 template <typename TW>
 hipError_t launch_t(const ScoreArgs& a, hipStream_t st) {
-  constexpr int NS = 4;
+  constexpr int NW = 8, NS = 2;
   if (sizeof(TW) == 2 && a.w_frag && a.D % (RES_KST * NS) == 0 && a.D <= 1024) {
-    score_lse_res_k<64, NS><<<(a.N + 63) / 64, NTH, 0, st>>>(a);
+    score_lse_res_k<64, NW, NS><<<(a.N + 63) / 64, NW * 64, 0, st>>>(a);
   } else if (sizeof(TW) == 2 && a.w_frag && a.D % (RES_KST * NS) == 0 && a.D <= 2048) {
-    score_lse_res_k<32, NS><<<(a.N + 31) / 32, NTH, 0, st>>>(a);
+    score_lse_res_k<32, NW, NS><<<(a.N + 31) / 32, NW * 64, 0, st>>>(a);
   } else {
     score_lse_k<TW><<<(a.N + BM - 1) / BM, NTH, 0, st>>>(a);
   }
