@@ -26,28 +26,30 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_small_k_small_traffic.md")
 KERNEL_SOURCES = ["cross_token_recurrent_amd/csrc/dec_small.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
+SCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_lse_res_k_head32000x1024_traffic.md")
+SCORE_SOURCES = ["cross_token_recurrent_amd/csrc/score.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per decoder launch from the committed rocprofv3 counter summary, or None
-    when the summary is missing or was taken on a different version of the kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(path: str = TRAFFIC_FILE, sources=None):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when the
+    summary is missing or was taken on a different version of the kernel's sources."""
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel source sha256/16") != kernel_source_hash():
+    if fields.get("kernel source sha256/16") != kernel_source_hash(sources):
         return None
     try:
         return float(fields["traffic bytes per launch"])
@@ -122,6 +124,12 @@ def cpu_baseline(wl, weights, tokens, budget_s: float = 20.0):
                       f"fp64 numpy, one sequence per worker process, {wall:.1f} s wall"}
 
 
+def scoring_rows(n: int, d: int, V: int) -> float:
+    """Algorithmic HBM bytes of one scoring pass: s read once (fp32), the fragment-major
+    bf16 head read once, the row log-sum-exp written."""
+    return n * d * 4.0 + (V + 15) // 16 * 16 * d * 2.0 + n * 4.0
+
+
 def scoring_leg(steps: int, warmup: int):
     """RL action scoring (rlt_score_actions) on the 300M-class head: V=32000, d=1024, bf16,
     N = 64 sequences x 1024 response positions.  The head GEMM dominates: 2*N*d*V flops
@@ -135,7 +143,8 @@ def scoring_leg(steps: int, warmup: int):
     cfg = ModelConfig(vocab=32000, d_model=1024, n_heads=16, n_layers=1, ffn_dim=64, ffn_kind="swiglu",
                       window=4, mem_groups=1, dtype="bf16")
     dev = torch.device("cuda:0")
-    model = rlt.Model(cfg, make_weights(cfg, 7), device=dev)
+    weights = make_weights(cfg, 7)
+    model = rlt.Model(cfg, weights, device=dev)
     n = 64 * 1024
     g = torch.Generator(device="cpu").manual_seed(8)
     s = torch.randn(n, cfg.d_model, generator=g).to(dev)
@@ -152,14 +161,35 @@ def scoring_leg(steps: int, warmup: int):
     ev[1].record(stream)
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / steps
+    # for context: the same scores through torch's library GEMM (bf16 logits written to HBM),
+    # then log_softmax and a gather
+    w_t = torch.from_numpy(weights["w_out"]).to(dev).to(torch.bfloat16).t().contiguous()
+    s_b = s.to(torch.bfloat16)
+
+    def unfused():
+        z = torch.matmul(s_b, w_t).float()
+        return z.log_softmax(-1).gather(1, acts.long()[:, None])[:, 0]
+
+    unfused()
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(3):
+        unfused()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms_unfused = ev[0].elapsed_time(ev[1]) / 3
+    del w_t, s_b
     flops = 2.0 * n * cfg.d_model * cfg.vocab
     tflops = flops / (ms * 1e-3) / 1e12
     return {"workload": f"RL action scoring, head V={cfg.vocab} d={cfg.d_model} bf16, N={n} rows "
                         f"(64 sequences x 1024 response positions), logp + ratio, logits never written",
             "rows_per_s": n / (ms * 1e-3), "ms_per_call": ms,
+            "unfused_torch_ms_per_call": ms_unfused,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-                         "kernel": "score_lse_k + score_finish_k", "algorithmic_flops_per_call": flops}}
+                         "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                         "traffic": measured_traffic(SCORE_TRAFFIC_FILE, SCORE_SOURCES),
+                         "kernel": "score_lse_res_k (timed with score_finish_k)", "algorithmic_flops_per_call": flops,
+                         "algorithmic_bytes_per_call": scoring_rows(n, cfg.d_model, cfg.vocab)}}
 
 
 def main():

@@ -6,13 +6,15 @@
 //   logp_i  = z_i[a_i] - log sum_v exp(z_i[v]),   z_i = (W_out s_i) / temperature
 //   ratio_i = exp(logp_i - behaviour_i)
 //
-// The [N, V] logits are never written.  score_lse_k: a workgroup of four waves owns 128 rows
-// and walks the vocabulary in 128-wide tiles on the matrix cores (the same 128x128 tile and
-// register-prefetched K stages as the token-parallel GEMM); each lane keeps a running maximum
-// and sum for its 16 rows over its own columns, so a tile costs no lane reduction; the lanes
-// and the two column waves are combined once at the end.  score_finish_k: one wave per row
-// takes the target logit (a d-long dot product on the same operand precision) and forms logp
-// and the ratio.
+// The [N, V] logits are never written.  Two paths:
+//  - score_lse_res_k (bf16 heads, d a multiple of 128 up to 2048): the workgroup's rows stay
+//    resident in LDS while the head streams past them from a fragment-major copy; each lane
+//    keeps a running maximum and sum for its rows over its own columns, the lane that holds
+//    column a of a row records z[a], and logp and the ratio are formed at the end.
+//  - otherwise score_lse_k + score_finish_k: a workgroup of four waves owns 128 rows and walks
+//    the vocabulary in 128-wide tiles (the same tile and register-prefetched K stages as the
+//    token-parallel GEMM), writing the row log-sum-exp; score_finish_k then takes the target
+//    logit with one wave per row (a d-long dot product on the same operand precision).
 #include "device_common.h"
 #include "rlt_internal.h"
 
@@ -222,6 +224,7 @@ void score_lse_res_k(ScoreArgs a) {
   constexpr int RES_VSTEP = NW * RES_COLS;
   __shared__ __attribute__((aligned(16))) bf16_t As[RES_LDS_ELEMS];
   __shared__ float part[NW][RB][2];
+  __shared__ float tgt[RB];   // z[a] of each row, taken from the product itself
 
   const int D = a.D, pitch = D + 8;
   const int m0 = blockIdx.x * RB;
@@ -278,10 +281,23 @@ void score_lse_res_k(ScoreArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // the action of each of the lane's 16 rows (-1 past N); an action outside [0, V) never
+  // matches a column, so its row keeps z[a] = NaN
+  int act[RI][4];
+#pragma unroll
+  for (int i = 0; i < RI; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = i * 16 + grp * 4 + v;
+      const int av = r < mrows ? a.act[m0 + r] : -1;
+      act[i][v] = av >= 0 && av < a.V ? av : -1;   // padding columns past V never match
+    }
+  if (threadIdx.x < RB) tgt[threadIdx.x] = __builtin_nanf("");
+
   uint4 wb[NS][4][2];
 #pragma unroll
   for (int s = 0; s < NS; ++s) wload(s, wb[s]);
-  __syncthreads();   // resident rows written
+  __syncthreads();   // resident rows and tgt written
 
   for (int g0 = 0; g0 < total; g0 += NS) {
 #pragma unroll
@@ -315,6 +331,8 @@ void score_lse_res_k(ScoreArgs a) {
             for (int j = 0; j < 4; ++j) {
               x[j] = nb + j * 16 < a.V ? acc[i][j][v] * sc : -INFINITY;
               tm = fmaxf(tm, x[j]);
+              // one lane of the workgroup holds column a of this row: it records z[a]
+              if (nb + j * 16 == act[i][v]) tgt[i * 16 + grp * 4 + v] = acc[i][j][v] * a.inv_temp;
             }
             const float mn = fmaxf(mx[i][v], tm);
             if (mn != -INFINITY) {
@@ -358,7 +376,9 @@ void score_lse_res_k(ScoreArgs a) {
       const float mw = part[w][r][0];
       L += mw == -INFINITY ? 0.f : part[w][r][1] * __builtin_amdgcn_exp2f(mw - M);
     }
-    a.logp[m0 + r] = (M + log2f(L)) / kLog2e;
+    const float lp = tgt[r] - (M + log2f(L)) / kLog2e;
+    a.logp[m0 + r] = lp;
+    if (a.ratio) a.ratio[m0 + r] = expf(lp - a.behav[m0 + r]);
   }
 }
 
@@ -403,13 +423,16 @@ __global__ __launch_bounds__(NTH) void score_finish_k(ScoreArgs a) {
 template <typename TW>
 hipError_t launch_t(const ScoreArgs& a, hipStream_t st) {
   constexpr int NW = 8, NS = 2;
+  // the resident-rows kernel forms logp and the ratio itself
   if (sizeof(TW) == 2 && a.w_frag && a.D % (RES_KST * NS) == 0 && a.D <= 1024) {
     score_lse_res_k<64, NW, NS><<<(a.N + 63) / 64, NW * 64, 0, st>>>(a);
-  } else if (sizeof(TW) == 2 && a.w_frag && a.D % (RES_KST * NS) == 0 && a.D <= 2048) {
-    score_lse_res_k<32, NW, NS><<<(a.N + 31) / 32, NW * 64, 0, st>>>(a);
-  } else {
-    score_lse_k<TW><<<(a.N + BM - 1) / BM, NTH, 0, st>>>(a);
+    return hipGetLastError();
   }
+  if (sizeof(TW) == 2 && a.w_frag && a.D % (RES_KST * NS) == 0 && a.D <= 2048) {
+    score_lse_res_k<32, NW, NS><<<(a.N + 31) / 32, NW * 64, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  score_lse_k<TW><<<(a.N + BM - 1) / BM, NTH, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   score_finish_k<TW><<<(a.N + NTH / 64 - 1) / (NTH / 64), NTH, 0, st>>>(a);

@@ -132,13 +132,17 @@ def test_score_large_head_bf16(dev):
 
 
 def test_score_invalid_action_is_nan(dev):
-    cfg = _cfg(97, 64, "fp32")
-    model = rlt.Model(cfg, make_weights(cfg, 19), device=dev)
-    S = torch.randn(4, 64, generator=torch.Generator().manual_seed(1)).to(dev)
-    acts = torch.tensor([-1, 97, 5, 1000], dtype=torch.int32, device=dev)
-    lp, _ = rlt.rlt_score_actions(model, S, acts)
-    lp = lp.cpu().numpy()
-    assert np.isnan(lp[[0, 1, 3]]).all() and np.isfinite(lp[2])
+    """Actions outside [0, V) give NaN (and a NaN ratio) on both kernel paths; 100 lies in the
+    padding columns of the last 256-column step of the resident-rows path."""
+    for d, dtype in ((64, "fp32"), (256, "bf16")):
+        cfg = _cfg(97, d, dtype)
+        model = rlt.Model(cfg, make_weights(cfg, 19), device=dev)
+        S = torch.randn(5, d, generator=torch.Generator().manual_seed(1)).to(dev)
+        acts = torch.tensor([-1, 97, 5, 1000, 100], dtype=torch.int32, device=dev)
+        lp, ratio = rlt.rlt_score_actions(model, S, acts, 1.0, torch.zeros(5, device=dev))
+        lp, ratio = lp.cpu().numpy(), ratio.cpu().numpy()
+        assert np.isnan(lp[[0, 1, 3, 4]]).all() and np.isfinite(lp[2]), (d, lp)
+        assert np.isnan(ratio[[0, 1, 3, 4]]).all() and np.isfinite(ratio[2])
 
 
 def test_score_argument_errors(dev):
