@@ -18,6 +18,7 @@ from .rlt_oracle import (  # noqa: F401
     replay_batch,
     score_actions,
     rms_norm,
+    sample_tokens,
     sigmoid,
     silu,
     step,

@@ -31,7 +31,7 @@ What is computed (everything in float64, one sequence at a time):
           append (k,v) to C_l, drop the oldest entry beyond W-1
         s_t = RMS(y; g_dec_final);  logits_t = W_out s_t
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
   gated merge form (sigmoid gate between e_t and the feedback projection W_fb s_{t-1});
   decoder input built from e_t; memory projected from e_t with G groups;
   SWA keys/values are projections of the same normalised layer input as the query;
@@ -46,7 +46,9 @@ sdpa), causal encoder vs a torch sdpa pass, gate-saturated decoder vs a token-pa
 masked sdpa pass, W=1 and T=1 closed forms, causality, split invariance, incremental ==
 replay, G equivalence, window >= T equivalence, state path length t*L_D; action scoring
 against closed forms (zero head, one dominant logit, normalisation over all actions,
-temperature on a hand-expanded softmax).
+temperature on a hand-expanded softmax); token sampling against special cases (top-1 is the
+argmax, the untruncated draw partitions [0, 1) by the library softmax, hand-built top-k and
+top-p sets, truncation order, uniform logits).
 """
 from __future__ import annotations
 
@@ -338,6 +340,59 @@ def score_actions(w_out: np.ndarray, S: np.ndarray, actions: Sequence[int],
     if behaviour_logp is not None:
         ratio = np.exp(logp - np.asarray(behaviour_logp, dtype=F64))
     return logp, ratio
+
+
+def sample_tokens(logits: np.ndarray, uniforms: Sequence[float], temperature: float = 1.0, top_k: int = 0,
+                  top_p: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
+    """Draw the next token of each row and record its behaviour log-probability under the
+    distribution actually sampled ([FI] model-RL co-design paragraph: the sampler's
+    log-probability is what the trainer's ratio divides by).
+
+    Row i with uniform u_i in [0, 1):
+      z = logits_i / temperature;
+      candidates ranked by (larger z first, then smaller token id);
+      top-k (k > 0 and k < V): keep the first k of that ranking;
+      top-p (p < 1): keep the shortest prefix of the ranking whose mass, renormalised over the
+        top-k survivors, reaches p (a candidate stays while the mass before it is below p);
+      the kept tokens, taken in increasing id, partition [0, 1) in proportion to exp(z):
+        the drawn token is the first whose cumulative share exceeds u_i;
+      logp_i = z[drawn] - log sum_{kept} exp(z).
+    Readings: truncation is applied top-k first, then top-p; ties are broken by token id;
+    the uniforms are inputs, so the draw is a deterministic function of them.
+    """
+    Z = np.asarray(logits, dtype=F64) / float(temperature)
+    n, V = Z.shape
+    tok = np.empty(n, dtype=np.int64)
+    logp = np.empty(n, dtype=F64)
+    for i in range(n):
+        z = Z[i]
+        rank = np.lexsort((np.arange(V), -z))          # primary key -z, then id
+        k = V if top_k <= 0 or top_k >= V else int(top_k)
+        cand = rank[:k]
+        zmax = z[cand[0]]
+        if top_p < 1.0:
+            w = np.exp(z[cand] - zmax)
+            need = float(top_p) * float(w.sum())
+            cum, keep = 0.0, 0
+            for wj in w:
+                if keep > 0 and cum >= need:
+                    break
+                cum += float(wj)
+                keep += 1
+            cand = cand[:keep]
+        ids = np.sort(cand)
+        w_ids = np.exp(z[ids] - zmax)
+        total = float(w_ids.sum())
+        target = float(uniforms[i]) * total
+        pick, cum = int(ids[-1]), 0.0
+        for v, wv in zip(ids, w_ids):
+            cum += float(wv)
+            if cum > target:
+                pick = int(v)
+                break
+        tok[i] = pick
+        logp[i] = z[pick] - zmax - math.log(total)
+    return tok, logp
 
 
 # ---------------------------------------------------------------------------

@@ -484,3 +484,82 @@ def test_score_actions_normalised_and_hand_expanded():
         lse = math.log(math.fsum(math.exp(x) for x in z))
         for v in range(V):
             assert abs(lp[v] - (z[v] - lse)) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# Token sampling ([FI] model-RL co-design paragraph: the sampler records the
+# log-probability of the distribution it actually drew from)
+# ---------------------------------------------------------------------------
+
+def test_sample_top1_is_argmax_with_lowest_id_on_ties():
+    """top_k = 1 keeps only the best candidate: the argmax, the lowest id among equal
+    maxima, with probability one (logp = 0) for every u."""
+    z = np.array([[0.5, 2.0, -1.0, 2.0, 1.9]])
+    for u in (0.0, 0.37, 0.999999):
+        tok, lp = O.sample_tokens(z, [u], 1.0, 1, 1.0)
+        assert tok[0] == 1 and lp[0] == 0.0
+    tok, lp = O.sample_tokens(z, [0.5], 1.0, 0, 1e-12)   # a vanishing nucleus is the argmax too
+    assert tok[0] == 1 and lp[0] == 0.0
+
+
+def test_sample_untruncated_partitions_unit_interval_by_softmax():
+    """Without truncation the draw is the inverse CDF of softmax(z / T) over ids in
+    increasing order: every u strictly inside the interval of token v (bounds from the
+    library softmax) draws v, and logp is the library log_softmax."""
+    rng = np.random.default_rng(5)
+    V = 11
+    z = rng.standard_normal((1, V)) * 2.0
+    for T in (1.0, 0.6, 3.0):
+        p = torch.softmax(torch.from_numpy(z[0] / T), 0).numpy()
+        ls = torch.log_softmax(torch.from_numpy(z[0] / T), 0).numpy()
+        c = np.concatenate([[0.0], np.cumsum(p)])
+        for v in range(V):
+            for frac in (0.02, 0.5, 0.98):
+                u = c[v] + frac * (c[v + 1] - c[v])
+                tok, lp = O.sample_tokens(z, [u], T, 0, 1.0)
+                assert tok[0] == v, (T, v, frac)
+                assert abs(lp[0] - ls[v]) < 1e-12
+
+
+def test_sample_hand_built_top_k_and_top_p_sets():
+    """z = [1, 3, 2, 3, 0, 2.5]: the ranking (larger z, then smaller id) is 1, 3, 5, 2, 0, 4.
+    top_k = 3 keeps {1, 3, 5}; top_p just below the mass share of {1, 3} keeps {1, 3}, just
+    above it keeps {1, 3, 5}.  Draws run over the kept ids in increasing order and logp is
+    the log of the renormalised share."""
+    z = np.array([[1.0, 3.0, 2.0, 3.0, 0.0, 2.5]])
+    e = np.exp(z[0] - 3.0)
+    kept = [1, 3, 5]
+    tot = math.fsum(e[v] for v in kept)
+    bounds = np.cumsum([e[v] / tot for v in kept])
+    for j, v in enumerate(kept):
+        u = (bounds[j - 1] if j else 0.0) + 0.5 * (e[v] / tot)
+        tok, lp = O.sample_tokens(z, [u], 1.0, 3, 1.0)
+        assert tok[0] == v and abs(lp[0] - math.log(e[v] / tot)) < 1e-13
+    share13 = (e[1] + e[3]) / math.fsum(e)
+    tok, lp = O.sample_tokens(z, [0.99], 1.0, 0, share13 - 1e-9)
+    assert tok[0] == 3 and abs(lp[0] - math.log(0.5)) < 1e-13
+    tok, lp = O.sample_tokens(z, [0.99], 1.0, 0, share13 + 1e-9)
+    assert tok[0] == 5
+    assert abs(lp[0] - math.log(e[5] / (e[1] + e[3] + e[5]))) < 1e-13
+
+
+def test_sample_top_k_is_applied_before_top_p():
+    """z = [3, 2, 1, 0], k = 2, p = 0.7: renormalised over the top-2 the leader has share
+    e/(e+1) = 0.731 >= 0.7, so only token 0 survives (logp 0).  Applying top-p over all
+    four first (leader share 0.644 < 0.7) would keep two tokens."""
+    z = np.array([[3.0, 2.0, 1.0, 0.0]])
+    for u in (0.0, 0.5, 0.95):
+        tok, lp = O.sample_tokens(z, [u], 1.0, 2, 0.7)
+        assert tok[0] == 0 and lp[0] == 0.0
+
+
+def test_sample_uniform_logits_nucleus():
+    """Equal logits over V = 512 with top_p = 0.5 keep ids 0..255 (ties ranked by id), each
+    with probability 1/256: u draws id floor(256 u)."""
+    z = np.full((4, 512), 0.7)
+    us = [0.0, 0.25, 0.99, 0.5 + 1e-6]
+    tok, lp = O.sample_tokens(z, us, 1.0, 0, 0.5)
+    assert list(tok) == [0, 64, 253, 128]
+    np.testing.assert_allclose(lp, -math.log(256.0), rtol=0, atol=1e-13)
+    tok, _ = O.sample_tokens(z[:1], [0.999], 1.0, 300, 1.0)   # top-k over ties: ids 0..299
+    assert tok[0] == 299
