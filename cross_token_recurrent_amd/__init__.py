@@ -12,10 +12,12 @@ from .rlt import (  # noqa: F401
     replay,
     rlt_decoder_replay,
     rlt_decoder_step,
+    rlt_decoder_step_sample,
     rlt_encoder_forward,
     rlt_logits,
     rlt_model_workspace_bytes,
     rlt_param_table,
+    rlt_sample_tokens,
     rlt_score_actions,
     rlt_state_load_encoder_outputs,
     rlt_state_read_encoder_outputs,

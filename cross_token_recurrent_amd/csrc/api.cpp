@@ -681,6 +681,48 @@ int rlt_decoder_step(const rlt_model* model, rlt_state* state, const int32_t* to
   return RLT_OK;
 }
 
+namespace {
+constexpr int32_t kMaxSampleVocab = 32768;
+
+int check_sampling(const rlt_sampling* p, int64_t n_rows, int32_t vocab) {
+  if (!p) return fail(RLT_ERR_INVALID, "sampling parameters are NULL");
+  if (!(p->temperature > 0.f)) return fail(RLT_ERR_INVALID, "temperature must be > 0");
+  if (p->top_k < 0) return fail(RLT_ERR_INVALID, "top_k must be >= 0");
+  if (!(p->top_p > 0.f) || p->top_p > 1.f) return fail(RLT_ERR_INVALID, "top_p must be in (0, 1]");
+  if (n_rows < 1 || n_rows > 0x7fffffff) return fail(RLT_ERR_INVALID, "n_rows out of range");
+  if (vocab < 1) return fail(RLT_ERR_INVALID, "vocab must be >= 1");
+  if (vocab > kMaxSampleVocab) return fail(RLT_ERR_UNSUPPORTED, "sampling supports vocab <= 32768");
+  return RLT_OK;
+}
+}  // namespace
+
+int rlt_sample_tokens(const float* logits, int64_t n_rows, int32_t vocab, const rlt_sampling* params,
+                      const float* uniforms, int32_t* tokens_out, float* logp_out, void* stream) {
+  if (!logits || !uniforms || !tokens_out || !logp_out)
+    return fail(RLT_ERR_INVALID, "logits, uniforms, tokens_out and logp_out must be non-NULL");
+  int rc = check_sampling(params, n_rows, vocab);
+  if (rc) return rc;
+  RLT_HIP(launch_sample_tokens(logits, uniforms, tokens_out, logp_out, static_cast<int>(n_rows), vocab,
+                               params->temperature, params->top_k, params->top_p, as_stream(stream)),
+          "sample tokens");
+  return RLT_OK;
+}
+
+int rlt_decoder_step_sample(const rlt_model* model, rlt_state* state, const int32_t* tokens,
+                            const rlt_sampling* params, const float* uniforms, int32_t* next_tokens,
+                            float* behaviour_logp, float* s_out, float* logits, void* stream) {
+  int rc = check_pair(model, state);
+  if (rc) return rc;
+  if (!logits || !uniforms || !next_tokens || !behaviour_logp)
+    return fail(RLT_ERR_INVALID, "logits, uniforms, next_tokens and behaviour_logp must be non-NULL");
+  rc = check_sampling(params, state->lay.B, model->lay.V);
+  if (rc) return rc;
+  rc = rlt_decoder_step(model, state, tokens, s_out, logits, stream);
+  if (rc) return rc;
+  return rlt_sample_tokens(logits, state->lay.B, model->lay.V, params, uniforms, next_tokens, behaviour_logp,
+                           stream);
+}
+
 int rlt_state_load_encoder_outputs(const rlt_model* model, rlt_state* state, const float* e,
                                    const float* mem_k, const float* mem_v, int32_t n, void* stream) {
   int rc = check_pair(model, state);

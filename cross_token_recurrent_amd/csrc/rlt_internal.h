@@ -128,6 +128,9 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
 hipError_t launch_score_actions(const float* s, const void* w_out, const void* w_frag, const int32_t* actions,
                                 const float* behav, float* logp, float* ratio, int N, int D, int V, float temperature,
                                 int dtype, hipStream_t st);
+// One sampled token and its behaviour log-probability per row of logits [N][V] (V <= 32768).
+hipError_t launch_sample_tokens(const float* logits, const float* uniforms, int32_t* tokens, float* logp, int N,
+                                int V, float temperature, int top_k, float top_p, hipStream_t st);
 // Writes the fragment-major bf16 copy of the fp32 head w [V][D] (layout in ModelLayout).
 hipError_t launch_pack_score_head(const float* w, void* dst, int V, int D, hipStream_t st);
 

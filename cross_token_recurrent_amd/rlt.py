@@ -46,6 +46,10 @@ class rlt_config(ctypes.Structure):
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
+class rlt_sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float)]
+
+
 _SIGS = {
     "rlt_param_count": [ctypes.POINTER(rlt_config), ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_int64)],
     "rlt_param_info": [ctypes.POINTER(rlt_config), _I32, ctypes.POINTER(ctypes.c_char_p),
@@ -67,6 +71,8 @@ _SIGS = {
     "rlt_decoder_step": [_P, _P, _P, _P, _P, _P],
     "rlt_logits": [_P, _P, ctypes.c_int64, _P, _P],
     "rlt_score_actions": [_P, _P, _P, ctypes.c_int64, ctypes.c_float, _P, _P, _P, _P],
+    "rlt_sample_tokens": [_P, ctypes.c_int64, _I32, ctypes.POINTER(rlt_sampling), _P, _P, _P, _P],
+    "rlt_decoder_step_sample": [_P, _P, _P, ctypes.POINTER(rlt_sampling), _P, _P, _P, _P, _P, _P],
     "rlt_state_load_encoder_outputs": [_P, _P, _P, _P, _P, _I32, _P],
     "rlt_state_read_encoder_outputs": [_P, _P, _I32, _I32, _P, _P, _P, _P],
     "rlt_decoder_path": [_P, _I32, ctypes.POINTER(_I32)],
@@ -197,6 +203,45 @@ def rlt_score_actions(model: "Model", s: torch.Tensor, actions: torch.Tensor, te
                                             _ptr(logp), _ptr(ratio) if ratio is not None else None,
                                             _stream(stream)))
     return logp, ratio
+
+
+def rlt_sample_tokens(logits: torch.Tensor, uniforms: torch.Tensor, temperature: float = 1.0, top_k: int = 0,
+                      top_p: float = 1.0, stream=None):
+    """One draw per row of logits [..., V] with the caller's uniforms [...] in [0, 1):
+    (tokens int32, behaviour logp fp32) under the truncated distribution actually sampled."""
+    assert logits.dtype == torch.float32 and logits.is_contiguous()
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    assert uniforms.dtype == torch.float32 and uniforms.is_contiguous() and uniforms.numel() == rows
+    tok = torch.empty(*logits.shape[:-1], dtype=torch.int32, device=logits.device)
+    logp = torch.empty(*logits.shape[:-1], dtype=torch.float32, device=logits.device)
+    p = rlt_sampling(float(temperature), int(top_k), float(top_p))
+    _check(load_library().rlt_sample_tokens(_ptr(logits), rows, V, ctypes.byref(p), _ptr(uniforms), _ptr(tok),
+                                            _ptr(logp), _stream(stream)))
+    return tok, logp
+
+
+def rlt_decoder_step_sample(model: "Model", state: "State", tokens: torch.Tensor, uniforms: torch.Tensor,
+                            temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
+                            s_out: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                            stream=None):
+    """Incremental step at the current position, then a draw of the next token per sequence:
+    (next_tokens int32 [B], behaviour logp fp32 [B]).  ``logits`` [B, V] receives the step's
+    logits (allocated when not given)."""
+    assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tuple(tokens.shape) == (state.batch,)
+    assert uniforms.dtype == torch.float32 and uniforms.is_contiguous() and uniforms.numel() == state.batch
+    if logits is None:
+        logits = torch.empty(state.batch, model.vocab, dtype=torch.float32, device=state.device)
+    assert logits.dtype == torch.float32 and tuple(logits.shape) == (state.batch, model.vocab)
+    if s_out is not None:
+        assert s_out.dtype == torch.float32 and tuple(s_out.shape) == (state.batch, model.d_model)
+    nxt = torch.empty(state.batch, dtype=torch.int32, device=state.device)
+    logp = torch.empty(state.batch, dtype=torch.float32, device=state.device)
+    p = rlt_sampling(float(temperature), int(top_k), float(top_p))
+    _check(load_library().rlt_decoder_step_sample(model.handle, state.handle, _ptr(tokens), ctypes.byref(p),
+                                                  _ptr(uniforms), _ptr(nxt), _ptr(logp), _ptr(s_out), _ptr(logits),
+                                                  _stream(stream)))
+    return nxt, logp
 
 
 def rlt_state_load_encoder_outputs(model: "Model", state: "State", e: torch.Tensor, mem_k: torch.Tensor,

@@ -191,6 +191,39 @@ int rlt_logits(const rlt_model* model, const float* s, int64_t n_rows, float* lo
  * logp_out: device fp32 [N]; ratio_out: device fp32 [N] or NULL (needs behaviour_logp).
  * Errors: RLT_ERR_INVALID for NULL required pointers, n_rows out of range, temperature <= 0
  * or ratio_out without behaviour_logp. */
+/* ---- sampling ([FI] model-RL co-design paragraph: the sampler records the log-probability of
+ * the distribution it actually drew from, which the trainer's ratio divides by) ----------
+ * Row r with uniform u_r in [0, 1) (the caller's random numbers, so a draw is a deterministic
+ * function of its inputs):
+ *   z = logits_r / temperature; candidates ranked by larger z, then smaller token id;
+ *   top_k > 0 (and < V) keeps the first top_k of that ranking;
+ *   top_p < 1 then keeps the shortest prefix of the survivors whose mass, renormalised over
+ *   them, reaches top_p;
+ *   the kept ids in increasing order split [0, 1) in proportion to exp(z); the first id whose
+ *   cumulative share exceeds u_r is drawn (u_r at or past the top edge draws the last kept id);
+ *   logp_r = z[drawn] - log sum_kept exp(z).
+ * temperature > 0; top_k >= 0 (0 = no top-k); 0 < top_p <= 1 (1 = no top-p). */
+typedef struct rlt_sampling {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+} rlt_sampling;
+
+/* rlt_sample_tokens: one draw per row.  logits: device fp32 [n_rows, vocab], 1 <= vocab <= 32768;
+ * uniforms: device fp32 [n_rows]; tokens_out: device int32 [n_rows]; logp_out: device fp32
+ * [n_rows].  Errors: RLT_ERR_INVALID for NULL pointers, n_rows < 1 or parameters out of range;
+ * RLT_ERR_UNSUPPORTED for vocab > 32768. */
+int rlt_sample_tokens(const float* logits, int64_t n_rows, int32_t vocab, const rlt_sampling* params,
+                      const float* uniforms, int32_t* tokens_out, float* logp_out, void* stream);
+
+/* rlt_decoder_step_sample: rlt_decoder_step (logits required, device fp32 [B, V]) followed by
+ * rlt_sample_tokens on its logits: next_tokens (device int32 [B]) and behaviour_logp (device
+ * fp32 [B]) are the draws for position t+1.  All checks of both calls run before anything is
+ * enqueued. */
+int rlt_decoder_step_sample(const rlt_model* model, rlt_state* state, const int32_t* tokens,
+                            const rlt_sampling* params, const float* uniforms, int32_t* next_tokens,
+                            float* behaviour_logp, float* s_out, float* logits, void* stream);
+
 int rlt_score_actions(const rlt_model* model, const float* s, const int32_t* actions, int64_t n_rows,
                       float temperature, const float* behaviour_logp, float* logp_out,
                       float* ratio_out, void* stream);
