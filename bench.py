@@ -192,6 +192,43 @@ def scoring_leg(steps: int, warmup: int):
                          "algorithmic_bytes_per_call": scoring_rows(n, cfg.d_model, cfg.vocab)}}
 
 
+def sampling_leg(steps: int, warmup: int):
+    """Token sampling (rlt_sample_tokens) for one decode step of the 300M-class workload:
+    512 rows x V=32000 fp32 logits, temperature 0.8, top-k 50 then top-p 0.95.  The kernel
+    reads each logit once: N*V*4 + N*12 bytes per call, priced against HBM."""
+    import torch
+
+    import cross_token_recurrent_amd as rlt
+
+    dev = torch.device("cuda:0")
+    n, V = 512, 32000
+    g = torch.Generator(device="cpu").manual_seed(9)
+    logits = (torch.randn(n, V, generator=g) * 2.0).to(dev)
+    u = torch.rand(n, generator=g).to(dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, k, p in (("top_k50_top_p0.95", 50, 0.95), ("top_p0.95", 0, 0.95), ("plain", 0, 1.0)):
+        for _ in range(warmup):
+            rlt.rlt_sample_tokens(logits, u, 0.8, k, p, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(steps):
+            rlt.rlt_sample_tokens(logits, u, 0.8, k, p, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        out[name] = ev[0].elapsed_time(ev[1]) / steps
+    ms = out["top_k50_top_p0.95"]
+    nbytes = n * V * 4.0 + n * 12.0
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"token sampling, {n} rows x V={V} fp32 logits, T=0.8, top-k 50 then top-p 0.95",
+            "rows_per_s": n / (ms * 1e-3), "ms_per_call": ms,
+            "ms_per_call_by_truncation": out,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "sample_k<64>",
+                         "algorithmic_bytes_per_call": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,6 +328,7 @@ def main():
     }
     if not args.no_scoring:
         line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2)
+        line["sampling"] = sampling_leg(max(3, min(args.steps, 10)), 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, weights, tokens)
     print(json.dumps(line), flush=True)

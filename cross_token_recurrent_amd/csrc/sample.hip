@@ -25,6 +25,8 @@ namespace rlt {
 namespace {
 
 constexpr int ST = 512;            // threads per row
+constexpr int kListMax = 1024;     // undecided elements one wave finishes a threshold search on
+constexpr int kPrefixBits = 12;    // key bits decided over all elements first
 constexpr int SW = ST / 64;        // waves
 constexpr float kLog2eS = 1.4426950408889634f;
 
@@ -53,6 +55,7 @@ __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
 // Block reductions: each uses its own slot of a two-deep ring, so one barrier per call is
 // enough (a slot is rewritten only after every thread has passed the next call's barrier).
+// Every thread adds the eight wave totals in wave order, so all threads hold the same value.
 struct Red {
   float* buf;   // [2][SW]
   int k = 0;
@@ -101,16 +104,48 @@ template <int C>
 __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
   static_assert(C >= 1 && C <= 64, "values per thread");
   constexpr int NE = ST * C;
-  __shared__ float stage[NE + NE / 32 + 1];
+  // the staged row; later the survivor list of the top-p search (keys, e, tau)
+  constexpr int SZ = NE + NE / 8 > 2 * kListMax + 4 ? NE + NE / 8 : 2 * kListMax + 4;
+  __shared__ __attribute__((aligned(16))) float stage[SZ];
   __shared__ float rbuf[2 * SW];
   __shared__ int pick_lo, pick_hi;
   Red red{rbuf};
 
   const int row = blockIdx.x;
   const int V = a.V;
+  const float urow = a.u[row];   // requested early; used by the draw
   const float* src = a.logits + static_cast<size_t>(row) * V;
-  // coalesced load, one pad slot per 32 values so the per-thread runs read without conflicts
-  for (int i = threadIdx.x; i < NE; i += ST) stage[i + (i >> 5)] = i < V ? src[i] + 0.0f : -INFINITY;
+  // coalesced load into LDS with four pad slots after every 32 values (16-byte aligned runs,
+  // and the per-thread runs read back without bank conflicts); -0 becomes +0 so equal logits
+  // have equal keys
+  auto slot = [](int i) { return i + (i >> 5) * 4; };
+  // Every load is unconditional (the address is clamped into the row and padding is
+  // selected afterwards), so all of a thread's loads are in flight before the first wait.
+  if (C >= 4 && (V & 3) == 0) {
+    constexpr int NQ = C >= 4 ? C / 4 : 1;
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+    const int qmax = V / 4 - 1;
+    float4 v[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) v[i] = s4[min(static_cast<int>(threadIdx.x) + i * ST, qmax)];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = threadIdx.x + i * ST;
+      const bool in = 4 * q < V;
+      const float4 w = make_float4(in ? v[i].x + 0.0f : -INFINITY, in ? v[i].y + 0.0f : -INFINITY,
+                                   in ? v[i].z + 0.0f : -INFINITY, in ? v[i].w + 0.0f : -INFINITY);
+      *reinterpret_cast<float4*>(stage + slot(4 * q)) = w;
+    }
+  } else {
+    float v[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) v[i] = src[min(static_cast<int>(threadIdx.x) + i * ST, V - 1)];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const int q = threadIdx.x + i * ST;
+      stage[slot(q)] = q < V ? v[i] + 0.0f : -INFINITY;
+    }
+  }
   if (threadIdx.x == 0) {
     pick_lo = 0x7fffffff;
     pick_hi = -1;
@@ -120,11 +155,20 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
   // the thread's run as order-preserving keys; a logit is recovered from its key when needed
   uint32_t key[C];
   float lm = -INFINITY;
+  if constexpr (C >= 4) {
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const float xc = stage[(j0 + c) + ((j0 + c) >> 5)];
-    key[c] = fkey(xc);
-    lm = fmaxf(lm, xc);
+    for (int c = 0; c < C; c += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(stage + slot(j0 + c));
+      key[c] = fkey(v.x); key[c + 1] = fkey(v.y); key[c + 2] = fkey(v.z); key[c + 3] = fkey(v.w);
+      lm = fmaxf(lm, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const float xc = stage[slot(j0 + c)];
+      key[c] = fkey(xc);
+      lm = fmaxf(lm, xc);
+    }
   }
   const float mz = red.max(lm) * a.inv_temp;
 
@@ -135,18 +179,92 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
   for (int c = 0; c < C; ++c)
     e[c] = j0 + c < V ? __builtin_amdgcn_exp2f((funkey(key[c]) * a.inv_temp - mz) * kLog2eS) : -0.0f;
 
+  // Threshold search: the largest key tau whose weight at or above it, W(tau) = sum of w over
+  // the elements in use with key >= tau, still reaches `target` (w = 1 and in use = valid for
+  // top-k; w = e and in use = kept for top-p).  The first `pb` bits are decided over all
+  // elements with block sums.  Then only the elements whose key shares tau's pb-bit prefix are
+  // undecided; when at most kListMax remain they are gathered into LDS (id order) and wave 0
+  // decides the remaining bits alone, the decided weight above the prefix added to its sums.
+  // Otherwise the block search simply goes on.
+  auto wt = [&](int c, bool mass) { return mass ? e[c] : (j0 + c < V ? 1.f : 0.f); };
+  auto search = [&](bool mass, float target, int pb) -> uint32_t {
+    uint32_t tau = 0;
+    int bit = 31;
+#pragma nounroll
+    for (; bit >= 32 - pb; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      float n = 0.f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) n += key[c] >= cand ? wt(c, mass) : 0.f;
+      if (red.sum(n) >= target) tau = cand;
+    }
+    const uint32_t pmask = pb == 0 ? 0u : ~0u << (32 - pb);
+    float nu = 0.f, ab = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const bool use = mass ? is_kept(e[c]) : j0 + c < V;
+      nu += use && (key[c] & pmask) == tau ? 1.f : 0.f;
+      ab += use && (key[c] & pmask) > tau ? wt(c, mass) : 0.f;
+    }
+    const float U = red.sum(nu);   // undecided elements
+    if (U <= static_cast<float>(kListMax)) {
+      const float above = red.sum(ab);
+      uint32_t* lk = reinterpret_cast<uint32_t*>(stage);
+      float* lw = stage + kListMax;
+      int pos = static_cast<int>(red.excl_scan(nu));
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const bool use = mass ? is_kept(e[c]) : j0 + c < V;
+        if (use && (key[c] & pmask) == tau) {
+          lk[pos] = key[c];
+          lw[pos] = wt(c, mass);
+          ++pos;
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        constexpr int PER = kListMax / 64;
+        uint32_t wk[PER];
+        float ww[PER];
+        const int nu_all = static_cast<int>(U);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {   // slots past the list hold stale data: weight 0
+          const int j = threadIdx.x + 64 * i;
+          wk[i] = lk[j];
+          ww[i] = j < nu_all ? lw[j] : 0.f;
+        }
+        const float lim = target - above;
+#pragma nounroll
+        for (; bit >= 0; --bit) {
+          const uint32_t cand = tau | (1u << bit);
+          float n = 0.f;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) n += wk[i] >= cand ? ww[i] : 0.f;
+          if (wave_sum(n) >= lim) tau = cand;
+        }
+      }
+      __syncthreads();   // every read of the list is done
+      if (threadIdx.x == 0) lk[2 * kListMax] = tau;
+      __syncthreads();
+      tau = lk[2 * kListMax];
+      __syncthreads();   // the slot is free again
+    } else {
+#pragma nounroll
+      for (; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        float n = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) n += key[c] >= cand ? wt(c, mass) : 0.f;
+        if (red.sum(n) >= target) tau = cand;
+      }
+    }
+    return tau;
+  };
+
   // ---- top-k: the k-th largest key, then ties at it in id order
   if (a.top_k > 0 && a.top_k < V) {
     const float k = static_cast<float>(a.top_k);
-    uint32_t tau = 0;
-#pragma nounroll
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tau | (1u << bit);
-      float cnt = 0.f;
-#pragma unroll
-      for (int c = 0; c < C; ++c) cnt += key[c] >= cand ? 1.f : 0.f;
-      if (red.sum(cnt) >= k) tau = cand;
-    }
+    const uint32_t tau = search(false, k, kPrefixBits);
     float gt = 0.f, eq = 0.f;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -157,12 +275,10 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
     float r = red.excl_scan(eq);   // ties before this thread's run
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      bool keep = key[c] > tau;
-      if (key[c] == tau) {
-        keep = r < need_eq;
-        r += 1.f;
-      }
-      if (!keep) e[c] = -0.0f;
+      const bool tie = key[c] == tau;
+      const bool keep = key[c] > tau || (tie && r < need_eq);
+      r += tie ? 1.f : 0.f;
+      e[c] = keep ? e[c] : -0.0f;
     }
   }
   float sk = 0.f;
@@ -173,36 +289,27 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
   // ---- top-p over the top-k survivors (e is zero outside them)
   if (a.top_p < 1.0f) {
     const float need = a.top_p * Sk;
-    uint32_t tau = 0;
-#pragma nounroll
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tau | (1u << bit);
-      float ms = 0.f;
-#pragma unroll
-      for (int c = 0; c < C; ++c) ms += key[c] >= cand ? e[c] : 0.f;
-      if (red.sum(ms) >= need) tau = cand;
-    }
+    // after a top-k of at most kListMax the survivors are gathered at once
+    const bool few = a.top_k > 0 && a.top_k < V && a.top_k <= kListMax;
+    const uint32_t tau = search(true, need, few ? 0 : kPrefixBits);
     float gt = 0.f, eq = 0.f, e_eq = 0.f;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const bool k1 = is_kept(e[c]);
+      const bool tie = is_kept(e[c]) && key[c] == tau;
       gt += key[c] > tau ? e[c] : 0.f;
-      if (k1 && key[c] == tau) {
-        eq += 1.f;
-        e_eq = e[c];
-      }
+      eq += tie ? 1.f : 0.f;
+      e_eq = tie ? e[c] : e_eq;
     }
     const float mass_gt = red.sum(gt);
     float r = red.excl_scan(eq);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const bool k1 = is_kept(e[c]);
-      bool keep = k1 && key[c] > tau;
-      if (k1 && key[c] == tau) {
-        keep = mass_gt + r * e_eq < need;   // the mass ranked before this tie is still short
-        r += 1.f;
-      }
-      if (!keep) e[c] = -0.0f;
+      const bool tie = k1 && key[c] == tau;
+      // a tie stays while the mass ranked before it is still short of the target
+      const bool keep = (k1 && key[c] > tau) || (tie && mass_gt + r * e_eq < need);
+      r += tie ? 1.f : 0.f;
+      e[c] = keep ? e[c] : -0.0f;
     }
   }
 
@@ -212,15 +319,14 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
   for (int c = 0; c < C; ++c) mine += e[c];
   const float Sp = red.sum(mine);
   float run = red.excl_scan(mine);
-  const float target = a.u[row] * Sp;
+  const float target = urow * Sp;
   int lo = 0x7fffffff, hi = -1;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
-    if (is_kept(e[c])) {
-      run += e[c];
-      if (run > target && lo == 0x7fffffff) lo = j0 + c;
-      hi = j0 + c;
-    }
+    const bool k1 = is_kept(e[c]);
+    run += e[c];   // -0 for ids that are not kept
+    lo = (k1 && run > target && lo == 0x7fffffff) ? j0 + c : lo;
+    hi = k1 ? j0 + c : hi;
   }
   if (lo != 0x7fffffff) atomicMin(&pick_lo, lo);
   if (hi >= 0) atomicMax(&pick_hi, hi);

@@ -85,9 +85,13 @@ def test_sample_plain_and_ragged_vocab(dev):
 
 
 def test_sample_large_vocab(dev):
-    """V=32000 (64 values per thread): full nucleus 0.95, and top-k 50 + top-p 0.9."""
+    """V=32000 (64 values per thread): full nucleus 0.95; top-k 50 + top-p 0.9 (the
+    survivors are searched by one wave); top-k 2000 + top-p 0.8 and top-k 1024 + top-p 0.5
+    (above and at the size limit of that survivor list)."""
     _case(dev, 24, 32000, 1.0, 0, 0.95, 4)
     _case(dev, 24, 32000, 0.7, 50, 0.9, 5)
+    _case(dev, 16, 32000, 1.0, 2000, 0.8, 9)
+    _case(dev, 16, 32000, 1.0, 1024, 0.5, 10)
 
 
 def test_sample_peaked_and_greedy(dev):
