@@ -21,4 +21,7 @@ from .rlt import (  # noqa: F401
     rlt_score_actions,
     rlt_state_load_encoder_outputs,
     rlt_state_read_encoder_outputs,
+    rlt_state_restore,
+    rlt_state_save,
+    rlt_state_snapshot_bytes,
 )

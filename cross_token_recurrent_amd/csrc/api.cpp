@@ -310,6 +310,65 @@ void compute_state_layout(const ModelLayout& m, int B, int T, int keep, StateLay
 
 }  // namespace rlt
 
+namespace {
+
+// Snapshot header (host byte order); the packed regions follow it.
+struct SnapHeader {
+  char magic[8];
+  uint32_t header_bytes, format;
+  rlt_config cfg;
+  uint64_t version;
+  int32_t batch, t_enc, t_dec, keep;
+  int32_t window_convention;  // 1: window counts the current token, ring slot = p mod (W-1)
+  int32_t reserved;
+  uint64_t payload_bytes;
+};
+constexpr char kSnapMagic[8] = {'R', 'L', 'T', 'S', 'N', 'A', 'P', '1'};
+
+// One packed region: `height` rows of `width` bytes; rows are `pitch` bytes apart in the state
+// blob and contiguous in the snapshot.
+struct SnapRegion {
+  size_t off, width, height, pitch;
+};
+
+// The regions of a state with layout S at t positions (t <= S.T); `keep` selects the encoder cache.
+std::vector<SnapRegion> snap_regions(const ModelLayout& M, const StateLayout& S, int t, int keep) {
+  const size_t e = M.esz, D = M.D, dh = M.DH, B = S.B, L = M.L, G = M.G, H = M.H, T = S.T;
+  const size_t ring = L * B * static_cast<size_t>(S.Wm1) * D * e;
+  const size_t t8 = (static_cast<size_t>(t) + 7) / 8 * 8;
+  std::vector<SnapRegion> r = {
+      {S.flags, 256, 1, 256},
+      {S.s, B * D * 4, 1, B * D * 4},
+      {S.ring_k, ring, ring ? 1u : 0u, ring},
+      {S.ring_v, ring, ring ? 1u : 0u, ring},
+      {S.e, t * D * e, B, T * D * e},
+      {S.mem_k, t * dh * e, G * B * H, T * dh * e},
+      {S.mem_v, t8 * dh * e, G * B * H, static_cast<size_t>(S.T8) * dh * e},
+  };
+  if (keep) {
+    r.push_back({S.enc_k, t * dh * e, L * B * H, T * dh * e});
+    r.push_back({S.enc_v, t * dh * e, L * B * H, T * dh * e});
+  }
+  return r;
+}
+
+size_t snap_payload(const std::vector<SnapRegion>& r) {
+  size_t n = 0;
+  for (const auto& x : r) n += x.width * x.height;
+  return n;
+}
+
+bool is_device_pointer(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // plain pageable host memory is not registered with HIP
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* rlt_last_error(void) { return g_err.c_str(); }
@@ -450,6 +509,93 @@ int rlt_state_reset(const rlt_model* model, rlt_state* state, void* stream) {
 }
 
 void rlt_state_release(rlt_state* state) { delete state; }
+
+int rlt_state_snapshot_bytes(const rlt_state* state, size_t* bytes) {
+  if (!state || !bytes) return fail(RLT_ERR_INVALID, "state and bytes must be non-NULL");
+  ModelLayout M;
+  compute_model_layout(state->cfg, &M);
+  *bytes = sizeof(SnapHeader) + snap_payload(snap_regions(M, state->lay, state->t_enc, state->lay.keep));
+  return RLT_OK;
+}
+
+int rlt_state_save(const rlt_model* model, const rlt_state* state, void* dst, size_t dst_bytes, void* stream) {
+  int rc = check_pair(model, state);
+  if (rc) return rc;
+  if (!dst) return fail(RLT_ERR_INVALID, "dst is NULL");
+  if (is_device_pointer(dst)) return fail(RLT_ERR_INVALID, "a snapshot lives in host memory");
+  const auto regions = snap_regions(model->lay, state->lay, state->t_enc, state->lay.keep);
+  const size_t payload = snap_payload(regions);
+  if (dst_bytes < sizeof(SnapHeader) + payload)
+    return fail(RLT_ERR_INVALID, "snapshot buffer too small: need " + std::to_string(sizeof(SnapHeader) + payload));
+  SnapHeader h{};
+  std::memcpy(h.magic, kSnapMagic, sizeof(kSnapMagic));
+  h.header_bytes = sizeof(SnapHeader);
+  h.format = 1;
+  h.cfg = state->cfg;
+  h.version = state->version;
+  h.batch = state->lay.B;
+  h.t_enc = state->t_enc;
+  h.t_dec = state->t_dec;
+  h.keep = state->lay.keep;
+  h.window_convention = 1;
+  h.payload_bytes = payload;
+  std::memcpy(dst, &h, sizeof(h));
+  char* out = static_cast<char*>(dst) + sizeof(SnapHeader);
+  for (const auto& r : regions) {
+    if (r.width == 0 || r.height == 0) continue;
+    RLT_HIP(hipMemcpy2DAsync(out, r.width, state->buf + r.off, r.pitch, r.width, r.height, hipMemcpyDefault,
+                             as_stream(stream)),
+            "save snapshot");
+    out += r.width * r.height;
+  }
+  return RLT_OK;
+}
+
+int rlt_state_restore(const rlt_model* model, rlt_state* state, const void* src, size_t src_bytes, void* stream) {
+  if (!model || !state || !src) return fail(RLT_ERR_INVALID, "model, state and src must be non-NULL");
+  if (std::memcmp(&model->cfg, &state->cfg, sizeof(rlt_config)) != 0)
+    return fail(RLT_ERR_INVALID, "state was built for a different model configuration");
+  if (is_device_pointer(src)) return fail(RLT_ERR_INVALID, "a snapshot lives in host memory");
+  if (src_bytes < sizeof(SnapHeader)) return fail(RLT_ERR_INVALID, "snapshot shorter than its header");
+  SnapHeader h;
+  std::memcpy(&h, src, sizeof(h));
+  if (std::memcmp(h.magic, kSnapMagic, sizeof(kSnapMagic)) != 0 || h.header_bytes != sizeof(SnapHeader) ||
+      h.format != 1 || h.window_convention != 1)
+    return fail(RLT_ERR_INVALID, "not a snapshot of this format");
+  if (std::memcmp(&h.cfg, &model->cfg, sizeof(rlt_config)) != 0)
+    return fail(RLT_ERR_INVALID, "snapshot was taken under a different model configuration");
+  if (h.version != model->version)
+    return fail(RLT_ERR_STALE_STATE, "snapshot was taken under weights version " + std::to_string(h.version) +
+                                         ", the model is at " + std::to_string(model->version));
+  if (h.batch != state->lay.B) return fail(RLT_ERR_INVALID, "snapshot batch differs from the state's");
+  if (h.t_enc < 0 || h.t_dec < 0 || h.t_dec > h.t_enc) return fail(RLT_ERR_INVALID, "snapshot positions are corrupt");
+  if (h.t_enc > state->lay.T) return fail(RLT_ERR_CAPACITY, "snapshot holds more positions than the state's t_max");
+  if (state->lay.keep && !h.keep)
+    return fail(RLT_ERR_NO_ENC_CACHE, "the state keeps an encoder cache but the snapshot has none");
+  StateLayout Ssrc = state->lay;  // the snapshot's packed widths depend only on t, B and the model
+  Ssrc.keep = h.keep;
+  const auto src_regions = snap_regions(model->lay, Ssrc, h.t_enc, h.keep);
+  const size_t payload = snap_payload(src_regions);
+  if (h.payload_bytes != payload || src_bytes < sizeof(SnapHeader) + payload)
+    return fail(RLT_ERR_INVALID, "snapshot size does not match its header");
+  int rc = reset_state(model, state, as_stream(stream));
+  if (rc) return rc;
+  const auto dst_regions = snap_regions(model->lay, state->lay, h.t_enc, state->lay.keep);
+  const char* in = static_cast<const char*>(src) + sizeof(SnapHeader);
+  for (size_t i = 0; i < src_regions.size(); ++i) {
+    const SnapRegion& r = src_regions[i];
+    if (i < dst_regions.size() && r.width && r.height) {
+      const SnapRegion& d = dst_regions[i];
+      RLT_HIP(hipMemcpy2DAsync(state->buf + d.off, d.pitch, in, r.width, r.width, r.height, hipMemcpyDefault,
+                               as_stream(stream)),
+              "restore snapshot");
+    }
+    in += r.width * r.height;
+  }
+  state->t_enc = h.t_enc;
+  state->t_dec = h.t_dec;
+  return RLT_OK;
+}
 
 int rlt_state_position(const rlt_state* state, int32_t* t_enc, int32_t* t_dec, uint64_t* version) {
   if (!state) return fail(RLT_ERR_INVALID, "state is NULL");

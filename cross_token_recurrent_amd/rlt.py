@@ -66,6 +66,9 @@ _SIGS = {
     "rlt_state_release": [_P],
     "rlt_state_position": [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_uint64)],
     "rlt_state_device_error": [_P, _P, ctypes.POINTER(_I32)],
+    "rlt_state_snapshot_bytes": [_P, ctypes.POINTER(ctypes.c_size_t)],
+    "rlt_state_save": [_P, _P, _P, ctypes.c_size_t, _P],
+    "rlt_state_restore": [_P, _P, _P, ctypes.c_size_t, _P],
     "rlt_encoder_forward": [_P, _P, _P, _I32, _P],
     "rlt_decoder_replay": [_P, _P, _I32, _P, _P],
     "rlt_decoder_step": [_P, _P, _P, _P, _P, _P],
@@ -242,6 +245,32 @@ def rlt_decoder_step_sample(model: "Model", state: "State", tokens: torch.Tensor
                                                   _ptr(uniforms), _ptr(nxt), _ptr(logp), _ptr(s_out), _ptr(logits),
                                                   _stream(stream)))
     return nxt, logp
+
+
+def rlt_state_snapshot_bytes(state: "State") -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().rlt_state_snapshot_bytes(state.handle, ctypes.byref(n)))
+    return int(n.value)
+
+
+def rlt_state_save(model: "Model", state: "State", out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Snapshot of the state at its current position into a host uint8 tensor (pinned when
+    allocated here).  The copies are enqueued on the stream: synchronise before reading it."""
+    n = rlt_state_snapshot_bytes(state)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    assert out.dtype == torch.uint8 and out.device.type == "cpu" and out.is_contiguous()
+    _check(load_library().rlt_state_save(model.handle, state.handle, ctypes.c_void_p(out.data_ptr()), out.numel(),
+                                         _stream(stream)))
+    return out
+
+
+def rlt_state_restore(model: "Model", state: "State", snapshot: torch.Tensor, stream=None) -> None:
+    """Reset `state` and load a snapshot into it (host uint8 tensor that must stay valid until
+    the stream has run the copies)."""
+    assert snapshot.dtype == torch.uint8 and snapshot.device.type == "cpu" and snapshot.is_contiguous()
+    _check(load_library().rlt_state_restore(model.handle, state.handle, ctypes.c_void_p(snapshot.data_ptr()),
+                                            snapshot.numel(), _stream(stream)))
 
 
 def rlt_state_load_encoder_outputs(model: "Model", state: "State", e: torch.Tensor, mem_k: torch.Tensor,

@@ -145,6 +145,30 @@ int rlt_state_position(const rlt_state* state, int32_t* t_enc, int32_t* t_dec,
  * by 0).  Synchronises `stream` first.  Writes 0 when no device error occurred. */
 int rlt_state_device_error(rlt_state* state, void* stream, int32_t* flags);
 
+/* ---- prefix snapshots ([FI] serving paragraph: a conversation's state after a prefix is kept
+ * and later continued; it is only valid under the weights version it was built with) --------
+ * A snapshot is a HOST buffer: a header (magic "RLTSNAP1", format 1, the model configuration,
+ * the weights version, B, t_enc, t_dec, whether the encoder K/V cache is included, and the
+ * window convention: the window counts the current token and the ring of W-1 entries keeps
+ * position p in slot p mod (W-1)), followed by the state regions packed to the positions in
+ * use: device flags, s [B,d], the window rings, e and the memory keys/values for positions
+ * < t_enc, and the encoder K/V cache for them when the state keeps one.
+ * rlt_state_snapshot_bytes: size of a snapshot of the state at its current position.
+ * rlt_state_save: enqueues the copies into `dst` (host memory, >= that size; pinned memory
+ *   makes the copies asynchronous) on `stream`; the caller synchronises before reading it.
+ * rlt_state_restore: checks the header against the model and the target state, then resets
+ *   the target and enqueues the copies from `src` (host memory that stays valid until the
+ *   stream reaches them).  The target needs the same configuration and batch, t_max >= the
+ *   snapshot's t_enc (a prefix can be restored into a longer state), and an encoder cache in
+ *   the snapshot if it keeps one.  Errors: RLT_ERR_INVALID (bad header, size, configuration or
+ *   batch), RLT_ERR_STALE_STATE (weights version differs from the model's), RLT_ERR_CAPACITY,
+ *   RLT_ERR_NO_ENC_CACHE; nothing is enqueued on error. */
+int rlt_state_snapshot_bytes(const rlt_state* state, size_t* bytes);
+int rlt_state_save(const rlt_model* model, const rlt_state* state, void* dst, size_t dst_bytes,
+                   void* stream);
+int rlt_state_restore(const rlt_model* model, rlt_state* state, const void* src, size_t src_bytes,
+                      void* stream);
+
 /* ---- the hot path --------------------------------------------------------------------
  * rlt_encoder_forward: tokens (device int32 [B, n], row stride n) are positions
  * t_enc .. t_enc+n-1 of every sequence.  Runs the causal encoder over them (each new
