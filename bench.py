@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
+PCIE_PEAK_GBS = 64.0             # host link, PCIe 5.0 x16, one direction
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_small_k_small_traffic.md")
 KERNEL_SOURCES = ["cross_token_recurrent_amd/csrc/dec_small.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
 SCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_lse_res_k_head32000x1024_traffic.md")
@@ -229,6 +230,38 @@ def sampling_leg(steps: int, warmup: int):
                          "algorithmic_bytes_per_call": nbytes}}
 
 
+def snapshot_leg(model, state, steps: int):
+    """Prefix snapshot of the benchmarked state (the whole replayed prefix, all B sequences)
+    to pinned host memory and back: bytes per call / time, against the host link."""
+    import torch
+
+    import cross_token_recurrent_amd as rlt
+
+    stream = torch.cuda.current_stream()
+    nbytes = rlt.rlt_state_snapshot_bytes(state)
+    buf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    rlt.rlt_state_save(model, state, buf, stream=stream)
+    rlt.rlt_state_restore(model, state, buf, stream=stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        rlt.rlt_state_save(model, state, buf, stream=stream)
+    ev[1].record(stream)
+    for _ in range(steps):
+        rlt.rlt_state_restore(model, state, buf, stream=stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    save_ms = ev[0].elapsed_time(ev[1]) / steps
+    restore_ms = ev[1].elapsed_time(ev[2]) / steps
+    gbs = nbytes / (save_ms * 1e-3) / 1e9
+    return {"workload": "prefix snapshot of the benchmarked state (all sequences at t = T) to pinned host memory",
+            "bytes": nbytes, "save_ms": save_ms, "restore_ms": restore_ms,
+            "roofline": {"bound": "pcie", "achieved": gbs, "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / PCIE_PEAK_GBS, "traffic": None, "kernel": "hipMemcpy2DAsync (save)",
+                         "algorithmic_bytes_per_call": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,6 +359,7 @@ def main():
                      "algorithmic_bytes_per_launch": dec_bytes},
         "cpu_baseline": None,
     }
+    line["snapshot"] = snapshot_leg(model, state, 3)
     if not args.no_scoring:
         line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2)
         line["sampling"] = sampling_leg(max(3, min(args.steps, 10)), 2)
