@@ -29,6 +29,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_small_k_small_traffic.md")
 KERNEL_SOURCES = ["cross_token_recurrent_amd/csrc/dec_small.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
 SCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_lse_res_k_head32000x1024_traffic.md")
 SCORE_SOURCES = ["cross_token_recurrent_amd/csrc/score.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
+SAMPLE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sample_k_512x32000_traffic.md")
+SAMPLE_SOURCES = ["cross_token_recurrent_amd/csrc/sample.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -226,7 +228,8 @@ def sampling_leg(steps: int, warmup: int):
             "rows_per_s": n / (ms * 1e-3), "ms_per_call": ms,
             "ms_per_call_by_truncation": out,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "sample_k<64>",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(SAMPLE_TRAFFIC_FILE, SAMPLE_SOURCES), "kernel": "sample_k<64>",
                          "algorithmic_bytes_per_call": nbytes}}
 
 

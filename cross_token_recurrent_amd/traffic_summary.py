@@ -3,9 +3,10 @@
     python -m cross_token_recurrent_amd.traffic_summary [--score] <fetch_dir> <write_dir> \
         <copy_fetch_dir> <copy_write_dir> <out.md>
 
-Without --score the summary covers the decoder (dec_small_k on the small workload); with
+Without a flag the summary covers the decoder (dec_small_k on the small workload); with
 --score, the action-scoring kernel (score_lse_res_k on bench.py's scoring leg: head
-V=32000, d=1024, bf16, 65536 rows).
+V=32000, d=1024, bf16, 65536 rows); with --sample, the sampling kernel (sample_k on
+bench.py's sampling leg: 512 rows x V=32000).
 
 Each directory holds the counter_collection.csv of one `rocprofv3 --pmc <counter>` run:
 the decoder runs come from `bench.py --steps 1 --warmup 0 --no-cpu-baseline`, the copy
@@ -72,9 +73,42 @@ def score_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
     print(open(out).read())
 
 
+def sample_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
+    import bench  # noqa: E402
+    copy_bytes = float(1 << 30)
+    c_fetch = _value(cfetch_dir, "FETCH_SIZE", "copy") * 1024.0
+    c_write = _value(cwrite_dir, "WRITE_SIZE", "copy") * 1024.0
+    k_fetch = _value(fetch_dir, "FETCH_SIZE", "sample_k") * 1024.0
+    k_write = _value(write_dir, "WRITE_SIZE", "sample_k") * 1024.0
+    f_fetch, f_write = copy_bytes / c_fetch, copy_bytes / c_write
+    traffic = k_fetch * f_fetch + k_write * f_write
+    alg = 512 * 32000 * 4.0 + 512 * 12.0
+    with open(out, "w") as f:
+        f.write("# sample_k on the sampling leg (512 rows x V=32000 fp32 logits): HBM traffic per launch\n\n")
+        f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -- python3 <repo>/bench.py --copy-kernel\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -- python3 <repo>/bench.py --copy-kernel\n")
+        f.write("    python -m cross_token_recurrent_amd.traffic_summary --sample <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/sample_k_512x32000_traffic.md\n\n")
+        f.write("The largest dispatch of the leg is taken (all three truncation settings read the same logits).\n\n")
+        f.write(f"- copy kernel: 1 GiB read / 1 GiB written; FETCH_SIZE reads {c_fetch:.4e} B, WRITE_SIZE {c_write:.4e} B\n")
+        f.write(f"- fetch scale: {f_fetch:.4f}\n")
+        f.write(f"- write scale: {f_write:.4f}\n")
+        f.write(f"- sampling FETCH_SIZE bytes per launch (raw): {k_fetch:.4e}\n")
+        f.write(f"- sampling WRITE_SIZE bytes per launch (raw): {k_write:.4e}\n")
+        f.write(f"- traffic bytes per launch: {traffic:.6e}\n")
+        f.write(f"- algorithmic bytes per launch: {alg:.6e}\n")
+        f.write(f"- traffic / algorithmic: {traffic / alg:.4f}\n")
+        f.write(f"- kernel source sha256/16: `{bench.kernel_source_hash(bench.SAMPLE_SOURCES)}`\n")
+    print(open(out).read())
+
+
 def main(argv):
     if argv and argv[0] == "--score":
         return score_summary(*argv[1:])
+    if argv and argv[0] == "--sample":
+        return sample_summary(*argv[1:])
     fetch_dir, write_dir, cfetch_dir, cwrite_dir, out = argv
     import bench  # noqa: E402  (repository root on sys.path)
     copy_bytes = float(1 << 30)
