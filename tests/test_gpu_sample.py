@@ -175,3 +175,15 @@ def test_decoder_step_sample(dev):
     # move by about that much
     check_rows(z_ref, u, nxt.cpu().numpy(), lp.cpu().numpy(), 0.9, 40, 0.9, max_border_frac=0.2,
                border_eps=1e-3, logp_abs=1e-3)
+
+
+def test_sample_bench_size_sampled_rows(dev):
+    """The launch the bench times: 512 rows x V=32000, T=0.8, top-k 50 then top-p 0.95; 64
+    seeded rows (with the first and last) are checked against the oracle."""
+    g = np.random.default_rng(9)
+    logits = (g.standard_normal((512, 32000)) * 2.0).astype(np.float32)
+    u = g.random(512).astype(np.float32)
+    tok, lp = _run(dev, logits, u, 0.8, 50, 0.95)
+    assert ((tok >= 0) & (tok < 32000)).all() and np.isfinite(lp).all() and (lp <= 0).all()
+    rows = np.unique(np.concatenate([[0, 511], g.choice(512, 62, replace=False)]))
+    check_rows(logits[rows], u[rows], tok[rows], lp[rows], 0.8, 50, 0.95)

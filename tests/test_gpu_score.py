@@ -186,3 +186,27 @@ def test_score_after_replay(dev):
     ref = np.stack([oracle.score_actions(w["w_out"], S_ref[b, P - 1:T - 1], tok[b, P:])[0] for b in range(B)])
     err = float(np.abs(lp.cpu().numpy() - ref).max())
     assert err <= SCORE_ABS, f"replay+score logp max abs error {err:.3e}"
+
+
+def test_score_bench_size_sampled_rows(dev):
+    """The launch the bench times: head V=32000, d=1024, bf16, N=65536 rows, with ratios; 48
+    rows spread over the whole range (first, last, and seeded picks in between) are checked
+    against the oracle on the same rounded operands, and every row must be finite."""
+    cfg = _cfg(32000, 1024, "bf16")
+    w = make_weights(cfg, 7)
+    model = rlt.Model(cfg, w, device=dev)
+    n = 64 * 1024
+    g = np.random.default_rng(8)
+    S = g.standard_normal((n, cfg.d_model)).astype(np.float32)
+    acts = g.integers(0, cfg.vocab, size=n).astype(np.int32)
+    behav = np.full(n, -10.0, np.float32)
+    lp, ratio = rlt.rlt_score_actions(model, torch.from_numpy(S).to(dev), torch.from_numpy(acts).to(dev), 1.0,
+                                      torch.from_numpy(behav).to(dev))
+    torch.cuda.synchronize()
+    lp, ratio = lp.cpu().numpy(), ratio.cpu().numpy()
+    assert np.isfinite(lp).all() and np.isfinite(ratio).all()
+    rows = np.unique(np.concatenate([[0, 63, 64, n - 1], g.choice(n, 44, replace=False)]))
+    ref, rref = oracle.score_actions(w["w_out"].astype(np.float64), _round_bf16(S[rows]), acts[rows], behav[rows])
+    err = float(np.abs(lp[rows] - ref).max())
+    assert err <= SCORE_ABS, f"logp max abs error {err:.3e}"
+    assert float((np.abs(ratio[rows] - rref) / rref).max()) <= 2 * SCORE_ABS
