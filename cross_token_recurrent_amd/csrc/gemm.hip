@@ -25,38 +25,38 @@ template <> struct Tile<float> { static constexpr int PAD = 4; };    // row pitc
 // Number of 16-byte chunks of one BMxBK (or BNxBK) tile, per thread.
 template <typename TW> constexpr int chunks_per_thread() { return (BM * BK * sizeof(TW) / 16) / NTH; }
 
-// Load one tile's chunks into registers (as packed storage words).
+// One tile's chunks as loaded: 16 bytes of the storage type per chunk, or, for an fp32 source
+// feeding bf16 storage, the 32 source bytes of the chunk (converted when stored to LDS, so
+// a load in flight is not waited on until its stage is consumed).
+template <typename TW, bool SRC_F32> struct Raw {
+  static constexpr bool CONV = SRC_F32 && sizeof(TW) == 2;
+  uint4 v[chunks_per_thread<TW>()][CONV ? 2 : 1];
+};
+
+// Load one tile's chunks.  Rows past the operand are clamped to its last row (their products
+// land in rows or columns the epilogue never writes), so every load is unconditional.
 template <typename TW, bool SRC_F32>
 __device__ __forceinline__ void load_tile(const void* __restrict__ base, int ld, int row0, int rows_valid, int k0,
-                                          uint4 (&r)[chunks_per_thread<TW>()]) {
+                                          Raw<TW, SRC_F32>& r) {
   constexpr int EPC = 16 / sizeof(TW);     // elements per chunk
   constexpr int CPR = BK / EPC;            // chunks per row
 #pragma unroll
   for (int i = 0; i < chunks_per_thread<TW>(); ++i) {
     const int c = threadIdx.x + i * NTH;
-    const int row = c / CPR, kc = (c % CPR) * EPC;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < rows_valid) {
-      if constexpr (SRC_F32 && sizeof(TW) == 2) {
-        // fp32 source converted to bf16 storage (8 elements = 32 source bytes)
-        const float* p = static_cast<const float*>(base) + static_cast<size_t>(row0 + row) * ld + k0 + kc;
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        v.x = f32_to_bf16(a.x) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16);
-        v.y = f32_to_bf16(a.z) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16);
-        v.z = f32_to_bf16(b.x) | (static_cast<uint32_t>(f32_to_bf16(b.y)) << 16);
-        v.w = f32_to_bf16(b.z) | (static_cast<uint32_t>(f32_to_bf16(b.w)) << 16);
-      } else {
-        const TW* p = static_cast<const TW*>(base) + static_cast<size_t>(row0 + row) * ld + k0 + kc;
-        v = *reinterpret_cast<const uint4*>(p);
-      }
+    const int row = min(c / CPR, rows_valid - 1), kc = (c % CPR) * EPC;
+    if constexpr (Raw<TW, SRC_F32>::CONV) {
+      const float* p = static_cast<const float*>(base) + static_cast<size_t>(row0 + row) * ld + k0 + kc;
+      r.v[i][0] = *reinterpret_cast<const uint4*>(p);
+      r.v[i][1] = *reinterpret_cast<const uint4*>(p + 4);
+    } else {
+      const TW* p = static_cast<const TW*>(base) + static_cast<size_t>(row0 + row) * ld + k0 + kc;
+      r.v[i][0] = *reinterpret_cast<const uint4*>(p);
     }
-    r[i] = v;
   }
 }
 
-template <typename TW>
-__device__ __forceinline__ void store_tile(TW* __restrict__ lds, const uint4 (&r)[chunks_per_thread<TW>()]) {
+template <typename TW, bool SRC_F32>
+__device__ __forceinline__ void store_tile(TW* __restrict__ lds, const Raw<TW, SRC_F32>& r) {
   constexpr int EPC = 16 / sizeof(TW);
   constexpr int CPR = BK / EPC;
   constexpr int PITCH = BK + Tile<TW>::PAD;
@@ -64,7 +64,13 @@ __device__ __forceinline__ void store_tile(TW* __restrict__ lds, const uint4 (&r
   for (int i = 0; i < chunks_per_thread<TW>(); ++i) {
     const int c = threadIdx.x + i * NTH;
     const int row = c / CPR, kc = (c % CPR) * EPC;
-    *reinterpret_cast<uint4*>(lds + row * PITCH + kc) = r[i];
+    uint4 v = r.v[i][0];
+    if constexpr (Raw<TW, SRC_F32>::CONV) {
+      const float4 a = __builtin_bit_cast(float4, r.v[i][0]);
+      const float4 b = __builtin_bit_cast(float4, r.v[i][1]);
+      v = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+    }
+    *reinterpret_cast<uint4*>(lds + row * PITCH + kc) = v;
   }
 }
 
@@ -122,7 +128,7 @@ __device__ __forceinline__ void store_row8(const GemmArgs& g, int m, int n, cons
   }
 }
 
-template <typename TW, bool A_F32>
+template <typename TW, bool A_F32, int NS>
 __global__ __launch_bounds__(NTH) void gemm_nt_k(GemmArgs g) {
   constexpr int PITCH = BK + Tile<TW>::PAD;
   constexpr int TILE_BYTES = BM * PITCH * static_cast<int>(sizeof(TW));
@@ -144,18 +150,29 @@ __global__ __launch_bounds__(NTH) void gemm_nt_k(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[chunks_per_thread<TW>()], rw[chunks_per_thread<TW>()];
-  load_tile<TW, A_F32>(g.A, g.lda, m0, mrows, 0, ra);
-  load_tile<TW, false>(g.W, g.ldw, n0, nrows, 0, rw);
+  // NS stages of K in flight: stage k is requested NS stages before it is consumed (the
+  // requests past the end of K re-read the last stage and are never consumed)
+  Raw<TW, A_F32> ra[NS];
+  Raw<TW, false> rw[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int kk = min(s * BK, g.K - BK);
+    load_tile<TW, A_F32>(g.A, g.lda, m0, mrows, kk, ra[s]);
+    load_tile<TW, false>(g.W, g.ldw, n0, nrows, kk, rw[s]);
+  }
 
-  for (int k0 = 0; k0 < g.K; k0 += BK) {
+  for (int k00 = 0; k00 < g.K; k00 += NS * BK)
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int k0 = k00 + s * BK;   // K is a multiple of NS * BK
     __syncthreads();
-    store_tile<TW>(As, ra);
-    store_tile<TW>(Ws, rw);
+    store_tile<TW, A_F32>(As, ra[s]);
+    store_tile<TW, false>(Ws, rw[s]);
     __syncthreads();
-    if (k0 + BK < g.K) {
-      load_tile<TW, A_F32>(g.A, g.lda, m0, mrows, k0 + BK, ra);
-      load_tile<TW, false>(g.W, g.ldw, n0, nrows, k0 + BK, rw);
+    {
+      const int kk = min(k0 + NS * BK, g.K - BK);
+      load_tile<TW, A_F32>(g.A, g.lda, m0, mrows, kk, ra[s]);
+      load_tile<TW, false>(g.W, g.ldw, n0, nrows, kk, rw[s]);
     }
     const int r16 = lane % 16, kq = lane / 16;
     if constexpr (sizeof(TW) == 2) {
@@ -280,13 +297,21 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
   if (g.K % BK != 0) return hipErrorInvalidValue;
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
   if (grid.y > 65535u) return hipErrorInvalidValue;
+  // prefetch depth: as many stages as divide K (bf16 up to 4, fp32 up to 2)
+  const bool k4 = g.K % (4 * BK) == 0, k2 = g.K % (2 * BK) == 0;
   if (dtype == RLT_DTYPE_BF16) {
-    if (g.a_f32)
-      gemm_nt_k<bf16_t, true><<<grid, NTH, 0, st>>>(g);
-    else
-      gemm_nt_k<bf16_t, false><<<grid, NTH, 0, st>>>(g);
+    if (g.a_f32) {
+      if (k4) gemm_nt_k<bf16_t, true, 4><<<grid, NTH, 0, st>>>(g);
+      else if (k2) gemm_nt_k<bf16_t, true, 2><<<grid, NTH, 0, st>>>(g);
+      else gemm_nt_k<bf16_t, true, 1><<<grid, NTH, 0, st>>>(g);
+    } else {
+      if (k4) gemm_nt_k<bf16_t, false, 4><<<grid, NTH, 0, st>>>(g);
+      else if (k2) gemm_nt_k<bf16_t, false, 2><<<grid, NTH, 0, st>>>(g);
+      else gemm_nt_k<bf16_t, false, 1><<<grid, NTH, 0, st>>>(g);
+    }
   } else {
-    gemm_nt_k<float, false><<<grid, NTH, 0, st>>>(g);
+    if (k2) gemm_nt_k<float, false, 2><<<grid, NTH, 0, st>>>(g);
+    else gemm_nt_k<float, false, 1><<<grid, NTH, 0, st>>>(g);
   }
   return hipGetLastError();
 }
