@@ -31,7 +31,7 @@ namespace {
 constexpr int KCHUNK = 256;   // memory rows per cross-attention work item
 
 struct Scratch {
-  size_t y, h, xin, gpre, fb, qkv, attn, act, part, total;
+  size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, total;
   int nsmax;
 };
 
@@ -54,6 +54,7 @@ Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   s.attn = take(Bz * D * e);
   s.act = take(Bz * static_cast<size_t>(m.F) * e);
   s.part = take(Bz * m.H * static_cast<size_t>(s.nsmax) * (m.DH + 2) * 4);
+  s.splitk = take(gemm_splitk_ws_floats(B, m.D) * 4);   // split-K partials of the d-wide products
   s.total = off;
   return s;
 }
@@ -404,6 +405,8 @@ hipError_t run_t(const ModelLayout& m, const StateLayout& S, const char* ws, cha
     GemmArgs g{};
     g.A = A; g.W = W; g.out = out;
     g.M = B; g.N = N; g.K = K; g.lda = lda; g.ldw = K; g.ldo = ldo; g.epi = epi;
+    g.splitk_ws = reinterpret_cast<float*>(base + sc.splitk);
+    g.splitk_ws_floats = gemm_splitk_ws_floats(B, D);
     return launch_gemm(g, dt, st);
   };
   const int nt = std::min(256, std::max(64, D / 4));

@@ -141,6 +141,13 @@ __global__ __launch_bounds__(NTH) void gemm_nt_k(GemmArgs g) {
 
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  // split-K: this block's slice of K, and its partial goes to the workspace as plain fp32
+  const int kslice = g.K / g.k_split, kbeg = blockIdx.z * kslice;
+  if (g.k_split > 1) {
+    g.out = g.splitk_ws + static_cast<size_t>(blockIdx.z) * g.M * g.N;
+    g.ldo = g.N;
+    g.epi = EPI_STORE_F32;
+  }
   const int wm = wave / 2, wn = wave % 2;
   const int mrows = min(BM, g.M - m0), nrows = min(BN, g.N - n0);
 
@@ -154,23 +161,24 @@ __global__ __launch_bounds__(NTH) void gemm_nt_k(GemmArgs g) {
   // requests past the end of K re-read the last stage and are never consumed)
   Raw<TW, A_F32> ra[NS];
   Raw<TW, false> rw[NS];
+  const int kend = kbeg + kslice;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int kk = min(s * BK, g.K - BK);
+    const int kk = min(kbeg + s * BK, kend - BK);
     load_tile<TW, A_F32>(g.A, g.lda, m0, mrows, kk, ra[s]);
     load_tile<TW, false>(g.W, g.ldw, n0, nrows, kk, rw[s]);
   }
 
-  for (int k00 = 0; k00 < g.K; k00 += NS * BK)
+  for (int k00 = kbeg; k00 < kend; k00 += NS * BK)
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int k0 = k00 + s * BK;   // K is a multiple of NS * BK
+    const int k0 = k00 + s * BK;   // the slice is a multiple of NS * BK
     __syncthreads();
     store_tile<TW, A_F32>(As, ra[s]);
     store_tile<TW, false>(Ws, rw[s]);
     __syncthreads();
     {
-      const int kk = min(k0 + NS * BK, g.K - BK);
+      const int kk = min(k0 + NS * BK, kend - BK);
       load_tile<TW, A_F32>(g.A, g.lda, m0, mrows, kk, ra[s]);
       load_tile<TW, false>(g.W, g.ldw, n0, nrows, kk, rw[s]);
     }
@@ -290,15 +298,57 @@ __global__ __launch_bounds__(NTH) void gemm_nt_k(GemmArgs g) {
   }
 }
 
+// Split-K reduction: out = (or +=) the sum of the S partials, added in the order z = 0..S-1.
+__global__ __launch_bounds__(256) void splitk_reduce_k(const float* __restrict__ ws, float* __restrict__ out, int M,
+                                                       int N, int ldo, int S, int resid) {
+  const int n4 = N / 4;
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<size_t>(M) * n4) return;
+  const int m = static_cast<int>(i / n4), c = static_cast<int>(i % n4) * 4;
+  const size_t plane = static_cast<size_t>(M) * N;
+  float4 s = *reinterpret_cast<const float4*>(ws + static_cast<size_t>(m) * N + c);
+  for (int z = 1; z < S; ++z) {
+    const float4 v = *reinterpret_cast<const float4*>(ws + z * plane + static_cast<size_t>(m) * N + c);
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(m) * ldo + c);
+  if (resid) {
+    const float4 r = *o;
+    s.x += r.x; s.y += r.y; s.z += r.z; s.w += r.w;
+  }
+  *o = s;
+}
+
+constexpr int kMaxSplit = 8;
+constexpr int kFillBlocks = 256;   // one block per CU
+
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
+size_t gemm_splitk_ws_floats(int M, int N) { return static_cast<size_t>(kMaxSplit) * M * N; }
+
+hipError_t launch_gemm(const GemmArgs& g0, int dtype, hipStream_t st) {
+  GemmArgs g = g0;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.K % BK != 0) return hipErrorInvalidValue;
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
   if (grid.y > 65535u) return hipErrorInvalidValue;
   // prefetch depth: as many stages as divide K (bf16 up to 4, fp32 up to 2)
-  const bool k4 = g.K % (4 * BK) == 0, k2 = g.K % (2 * BK) == 0;
+  const int nsd = dtype == RLT_DTYPE_BF16 ? (g.K % (4 * BK) == 0 ? 4 : g.K % (2 * BK) == 0 ? 2 : 1)
+                                          : (g.K % (2 * BK) == 0 ? 2 : 1);
+  // split K when the output tiles leave most CUs idle (fp32-output epilogues only): the
+  // largest S <= 8 whose slices stay multiples of the prefetch depth and fit the workspace
+  g.k_split = 1;
+  const int tiles = static_cast<int>(grid.x * grid.y);
+  const bool vec4 = g.N % 4 == 0 && g.ldo % 4 == 0 && reinterpret_cast<uintptr_t>(g.out) % 16 == 0;
+  if (g.splitk_ws && vec4 && (g.epi == EPI_STORE_F32 || g.epi == EPI_RESID_F32) && 2 * tiles <= kFillBlocks) {
+    int S = 1;
+    while (S * 2 <= kMaxSplit && tiles * S * 2 <= kFillBlocks && g.K % (S * 2 * nsd * BK) == 0 &&
+           static_cast<size_t>(S) * 2 * g.M * g.N <= g.splitk_ws_floats)
+      S *= 2;
+    g.k_split = S;
+  }
+  grid.z = g.k_split;
+  const bool k4 = nsd == 4, k2 = nsd == 2;
   if (dtype == RLT_DTYPE_BF16) {
     if (g.a_f32) {
       if (k4) gemm_nt_k<bf16_t, true, 4><<<grid, NTH, 0, st>>>(g);
@@ -313,6 +363,11 @@ hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
     if (k2) gemm_nt_k<float, false, 2><<<grid, NTH, 0, st>>>(g);
     else gemm_nt_k<float, false, 1><<<grid, NTH, 0, st>>>(g);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.k_split == 1) return e;
+  const size_t n = static_cast<size_t>(g.M) * (g.N / 4);
+  splitk_reduce_k<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(
+      g.splitk_ws, static_cast<float*>(g.out), g.M, g.N, g.ldo, g.k_split, g.epi == EPI_RESID_F32 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -119,7 +119,15 @@ struct GemmArgs {
   void* sc_v;
   int sc_c0;          // first scattered column (D for QKV, 0 for memory projections)
   int sc_n, sc_b0, sc_t0, sc_T, sc_H, sc_dh, sc_D, sc_B;  // row m -> (b0 + m/n, t0 + m%n)
+  // Optional split-K workspace (fp32, splitk_ws_floats long) for EPI_STORE_F32 / EPI_RESID_F32
+  // products with too few output tiles to fill the chip: K is split over blockIdx.z, the
+  // partials land in the workspace and a second kernel adds them in a fixed order.
+  float* splitk_ws;
+  size_t splitk_ws_floats;
+  int k_split;        // set by launch_gemm
 };
+// Workspace floats split-K needs for an M x N product (the most launch_gemm will use).
+size_t gemm_splitk_ws_floats(int M, int N);
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
 
 // Action scoring: logp_i = log softmax(W_out s_i / temperature)[a_i] (and the ratio against
