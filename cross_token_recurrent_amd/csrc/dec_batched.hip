@@ -269,7 +269,11 @@ __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx,
   const WT* vb = mem_v + (static_cast<size_t>(b) * H + h) * T8 * DH;
   const int j0 = split * KCHUNK, j1 = min(j0 + KCHUNK, t + 1);
   float mloc = -INFINITY;
-  for (int i = slot; i < KCHUNK; i += SLOTS) {
+  // compile-time trip counts and clamped rows: every load of the chunk is unconditional, so
+  // the loads of all iterations can be in flight together
+#pragma unroll
+  for (int it = 0; it < KCHUNK / SLOTS; ++it) {
+    const int i = slot + it * SLOTS;
     const int j = min(j0 + i, j1 - 1);   // rows past the chunk end are loaded but masked
     float k[16];
     Row16<WT>::load(kb + static_cast<size_t>(j) * DH + sub * 16, k);
@@ -296,14 +300,18 @@ __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx,
   float o[ND];
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) o[nd] = 0.f;
-  for (int blk = bq; blk < nblk; blk += BSTEP) {
+#pragma unroll
+  for (int it = 0; it < KCHUNK / 8 / BSTEP; ++it) {
+    // blocks past the chunk end hold zero weights (masked keys); their loads are clamped
+    const int blk = bq + it * BSTEP;
+    const int lb = min(blk, nblk - 1);
     const float4 p0 = *reinterpret_cast<const float4*>(ps + blk * 8);
     const float4 p1 = *reinterpret_cast<const float4*>(ps + blk * 8 + 4);
     const float pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
       float v[8];
-      load8(vb + ((static_cast<size_t>(j0 / 8 + blk)) * DH + d0 + nd * 64) * 8, v);
+      load8(vb + ((static_cast<size_t>(j0 / 8 + lb)) * DH + d0 + nd * 64) * 8, v);
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[nd] += pw[k] * v[k];
     }
