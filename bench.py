@@ -233,6 +233,55 @@ def sampling_leg(steps: int, warmup: int):
                          "algorithmic_bytes_per_call": nbytes}}
 
 
+def decoder_300m_leg(t0: int = 1024, n: int = 64):
+    """The batched decoder on the 300M-class workload (d=1024, 12+12 layers, SwiGLU 4096,
+    W=128, G=L, V=32000, B=512, bf16): encode t0+n positions, replay 1..t0 (timed as a whole),
+    then n more steps timed with HIP events; both against the decoder's algorithmic bytes.
+    The workload's full T=2048 does not fit a bench run of minutes, so the late steps are
+    taken at t0 = 1024."""
+    import time
+
+    import torch
+
+    import cross_token_recurrent_amd as rlt
+    from workloads import CONFIGS, make_tokens, make_weights
+
+    wl = CONFIGS["300m"]
+    cfg, B = wl.model, wl.batch
+    w = make_weights(cfg, wl.weight_seed)
+    model = rlt.Model(cfg, w, device=torch.device("cuda:0"))
+    del w
+    state = rlt.State(model, B, t0 + n)
+    tok = torch.from_numpy(make_tokens(cfg.vocab, B, t0 + n, wl.token_dist, wl.token_seed)).cuda()
+    stream = torch.cuda.current_stream()
+    rlt.rlt_encoder_forward(model, state, tok)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    rlt.rlt_decoder_replay(model, state, t0)
+    ev[1].record(stream)
+    rlt.rlt_decoder_replay(model, state, n)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    ms_a, ms_b = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+    bytes_a = algorithmic_decoder_bytes(cfg, B, t0)
+    bytes_b = algorithmic_decoder_bytes(cfg, B, t0 + n) - bytes_a
+    gbs_a, gbs_b = bytes_a / (ms_a * 1e-3) / 1e9, bytes_b / (ms_b * 1e-3) / 1e9
+    path = {1: "persistent-per-sequence", 2: "batched-phases"}[model.decoder_path(t0 + n)]
+    del state, model
+    torch.cuda.empty_cache()
+    return {"workload": f"300m: RLT d={cfg.d_model} H={cfg.n_heads} L_E=L_D={cfg.n_layers} F={cfg.ffn_dim} "
+                        f"{cfg.ffn_kind} W={cfg.window} G={cfg.mem_groups} V={cfg.vocab}, B={B}, Zipf tokens",
+            "decoder_path": path,
+            "steps_1_to_t0": {"t0": t0, "ms": ms_a, "tokens_per_s": B * t0 / (ms_a * 1e-3),
+                              "achieved_GBps": gbs_a, "frac_of_hbm": gbs_a / HBM_PEAK_GBS},
+            "late_steps": {"t": [t0 + 1, t0 + n], "ms_per_step": ms_b / n, "tokens_per_s": B * n / (ms_b * 1e-3),
+                           "roofline": {"bound": "hbm", "achieved": gbs_b, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": gbs_b / HBM_PEAK_GBS, "traffic": None,
+                                        "kernel": "batched decoder step (cross_part_k dominant)",
+                                        "algorithmic_bytes": bytes_b}}}
+
+
 def snapshot_leg(model, state, steps: int):
     """Prefix snapshot of the benchmarked state (the whole replayed prefix, all B sequences)
     to pinned host memory and back: bytes per call / time, against the host link."""
@@ -273,10 +322,16 @@ def main():
     ap.add_argument("--config", default="small")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scoring", action="store_true", help="skip the RL action-scoring measurement")
+    ap.add_argument("--no-300m", action="store_true", help="skip the 300M-class batched decoder measurement")
+    ap.add_argument("--only-300m", action="store_true",
+                    help="run only the 300M-class batched decoder measurement (for profiling)")
     ap.add_argument("--copy-kernel", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.copy_kernel:
         copy_kernel()
+        return
+    if args.only_300m:
+        print(json.dumps({"decoder_300m": decoder_300m_leg()}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the replay shards over sequences with no communication, "
@@ -363,6 +418,10 @@ def main():
         "cpu_baseline": None,
     }
     line["snapshot"] = snapshot_leg(model, state, 3)
+    if not args.no_300m:
+        del state, model, S, Z
+        torch.cuda.empty_cache()
+        line["decoder_300m"] = decoder_300m_leg()
     if not args.no_scoring:
         line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2)
         line["sampling"] = sampling_leg(max(3, min(args.steps, 10)), 2)
