@@ -89,6 +89,54 @@ __global__ void rmsnorm_rows_k(const float* __restrict__ x, const float* __restr
   }
 }
 
+// The same for D = 256 * NV: each lane keeps its NV float4 of the row in registers (one read
+// of x, every load in flight at once) and writes 4 elements per store.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void rmsnorm_rows_v_k(const float* __restrict__ x, const float* __restrict__ gain,
+                                                        T* __restrict__ out, int rows, float eps,
+                                                        T* __restrict__ e_store, int n, int b0, int t0, int Tmax) {
+  constexpr int D = 256 * NV;
+  const int row = blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  if (row >= rows) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + static_cast<size_t>(row) * D);
+  float4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = xr[lane + 64 * i];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+  ss = group_sum<64>(ss);
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  T* o = out + static_cast<size_t>(row) * D;
+  T* es = nullptr;
+  if (e_store) {
+    const int b = b0 + row / n, t = t0 + row % n;
+    es = e_store + (static_cast<size_t>(b) * Tmax + t) * D;
+  }
+  const float4* g4 = reinterpret_cast<const float4*>(gain);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c4 = lane + 64 * i;
+    const float4 g = g4[c4];
+    const float a = g.x * (v[i].x * inv), b = g.y * (v[i].y * inv), c = g.z * (v[i].z * inv),
+                d = g.w * (v[i].w * inv);
+    store4<T>(o + 4 * c4, a, b, c, d);
+    if (es) store4<T>(es + 4 * c4, a, b, c, d);
+  }
+}
+
 // fp32 [B, n, D] <-> stored layout.  heads_layout 0: [B][T][D]; 1: [B][H][T][dh].
 template <typename T>
 __global__ void store_tokens_k(float* __restrict__ flat, T* __restrict__ dev, int B, int n, int D, int t0, int Tmax,
@@ -161,8 +209,28 @@ hipError_t launch_embed(const int32_t* tokens, int n, int b0, int rows, const vo
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_rmsnorm_v(const float* x, const float* gain, T* out, int rows, int D, float eps, T* e_store, int n,
+                            int b0, int t0, int Tmax, hipStream_t st) {
+  const int g = (rows + 3) / 4;
+  switch (D / 256) {
+    case 1: rmsnorm_rows_v_k<T, 1><<<g, 256, 0, st>>>(x, gain, out, rows, eps, e_store, n, b0, t0, Tmax); break;
+    case 2: rmsnorm_rows_v_k<T, 2><<<g, 256, 0, st>>>(x, gain, out, rows, eps, e_store, n, b0, t0, Tmax); break;
+    case 4: rmsnorm_rows_v_k<T, 4><<<g, 256, 0, st>>>(x, gain, out, rows, eps, e_store, n, b0, t0, Tmax); break;
+    default: rmsnorm_rows_v_k<T, 8><<<g, 256, 0, st>>>(x, gain, out, rows, eps, e_store, n, b0, t0, Tmax); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm_rows(const float* x, const float* gain, void* out, int rows, int D, float eps, int dtype,
                                void* e_store, int n, int b0, int t0, int Tmax, hipStream_t st) {
+  if (D == 256 || D == 512 || D == 1024 || D == 2048) {
+    if (dtype == RLT_DTYPE_BF16)
+      return launch_rmsnorm_v<bf16_t>(x, gain, static_cast<bf16_t*>(out), rows, D, eps, static_cast<bf16_t*>(e_store),
+                                      n, b0, t0, Tmax, st);
+    return launch_rmsnorm_v<float>(x, gain, static_cast<float*>(out), rows, D, eps, static_cast<float*>(e_store), n,
+                                   b0, t0, Tmax, st);
+  }
   const int g = (rows + 3) / 4;
   if (dtype == RLT_DTYPE_BF16)
     rmsnorm_rows_k<bf16_t><<<g, 256, 0, st>>>(x, gain, static_cast<bf16_t*>(out), rows, D, eps,
