@@ -205,29 +205,44 @@ __global__ __launch_bounds__(64) void swa_k(const float* __restrict__ qkv, WT* _
   const int ne = npast + 1;
   const int slot0 = Wm1 > 0 ? (t - npast) % Wm1 : 0;
   const size_t rbase = ((static_cast<size_t>(b) * H + h) * Wm1) * DH;   // ring is pre-offset to layer l
+  // the current entry (position t), in the storage precision of the ring
+  float kc[16], vc[16];
+  {
+    const float* kr = qkv + static_cast<size_t>(b) * 3 * D + D + h * DH + sub * 16;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      kc[c] = round_to<WT>(kr[c]);
+      vc[c] = round_to<WT>(kr[D + c]);
+    }
+  }
   SoftState st;
   st.init();
-  for (int i0 = 0; i0 < ne; i0 += SLOTS) {
-    const int i = i0 + slot;
-    float k[16], v[16];
-    if (i < npast) {
-      int sl = slot0 + i;
-      sl = sl >= Wm1 ? sl - Wm1 : sl;
-      Row16<WT>::load(ring_k + rbase + static_cast<size_t>(sl) * DH + sub * 16, k);
-      Row16<WT>::load(ring_v + rbase + static_cast<size_t>(sl) * DH + sub * 16, v);
-    } else {
-      const float* kr = qkv + static_cast<size_t>(b) * 3 * D + D + h * DH + sub * 16;
+  // entries i < npast come from the ring, i == npast is the current one, i > npast are masked;
+  // ring slots are clamped so that every load is unconditional, and four rounds are unrolled
+  // so their loads are in flight together
+  for (int i0 = 0; i0 < ne; i0 += 4 * SLOTS) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + r * SLOTS + slot;
+      float k[16], v[16];
+      if (npast > 0) {
+        int sl = slot0 + min(i, npast - 1);
+        sl = sl >= Wm1 ? sl - Wm1 : sl;
+        Row16<WT>::load(ring_k + rbase + static_cast<size_t>(sl) * DH + sub * 16, k);
+        Row16<WT>::load(ring_v + rbase + static_cast<size_t>(sl) * DH + sub * 16, v);
+      }
+      const bool cur = i >= npast;
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
-        k[c] = round_to<WT>(kr[c]);
-        v[c] = round_to<WT>(kr[D + c]);
+        k[c] = cur ? kc[c] : k[c];
+        v[c] = cur ? vc[c] : v[c];
       }
-    }
-    float a = 0.f;
+      float a = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) a += q[c] * k[c];
-    a = group_sum<LPK>(a);
-    st.add(i < ne ? a : -INFINITY, v);
+      for (int c = 0; c < 16; ++c) a += q[c] * k[c];
+      a = group_sum<LPK>(a);
+      st.add(i < ne ? a : -INFINITY, v);
+    }
   }
   wave_finish<DH>(st, lds, nullptr, nullptr, nullptr, outf, lane);
   __syncthreads();
