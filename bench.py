@@ -133,7 +133,20 @@ def scoring_rows(n: int, d: int, V: int) -> float:
     return n * d * 4.0 + (V + 15) // 16 * 16 * d * 2.0 + n * 4.0
 
 
-def scoring_leg(steps: int, warmup: int):
+def _oracle_rows_per_s(fn, rows_total: int, budget_s: float = 6.0):
+    """Time an oracle call on growing row samples until about budget_s of host work."""
+    import time
+    n, used, done = 8, 0.0, 0
+    while used < budget_s and done < rows_total:
+        t0 = time.perf_counter()
+        fn(done, min(n, rows_total - done))
+        used += time.perf_counter() - t0
+        done += min(n, rows_total - done)
+        n *= 2
+    return done / used, done, used
+
+
+def scoring_leg(steps: int, warmup: int, with_cpu: bool = True):
     """RL action scoring (rlt_score_actions) on the 300M-class head: V=32000, d=1024, bf16,
     N = 64 sequences x 1024 response positions.  The head GEMM dominates: 2*N*d*V flops
     per call, priced against the bf16 MFMA peak."""
@@ -182,12 +195,25 @@ def scoring_leg(steps: int, warmup: int):
     torch.cuda.synchronize()
     ms_unfused = ev[0].elapsed_time(ev[1]) / 3
     del w_t, s_b
+    cpu = None
+    if with_cpu:
+        import numpy as np
+        import oracle
+        w_out = np.asarray(weights["w_out"], dtype=np.float64)
+        s_host = s.cpu().numpy()
+        a_host = acts.cpu().numpy()
+        rate, done, used = _oracle_rows_per_s(
+            lambda i, k: oracle.score_actions(w_out, s_host[i:i + k], a_host[i:i + k]), n)
+        blas = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "0")) or 10 ** 6)
+        cpu = {"value": rate, "unit": "rows/s", "cores": blas, "kind": "oracle",
+               "sample": f"{done} of {n} rows through oracle.score_actions (fp64 numpy; the head product "
+                         f"on up to {blas} BLAS threads), {used:.1f} s"}
     flops = 2.0 * n * cfg.d_model * cfg.vocab
     tflops = flops / (ms * 1e-3) / 1e12
     return {"workload": f"RL action scoring, head V={cfg.vocab} d={cfg.d_model} bf16, N={n} rows "
                         f"(64 sequences x 1024 response positions), logp + ratio, logits never written",
             "rows_per_s": n / (ms * 1e-3), "ms_per_call": ms,
-            "unfused_torch_ms_per_call": ms_unfused,
+            "unfused_torch_ms_per_call": ms_unfused, "cpu_baseline": cpu,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                          "traffic": measured_traffic(SCORE_TRAFFIC_FILE, SCORE_SOURCES),
@@ -195,7 +221,7 @@ def scoring_leg(steps: int, warmup: int):
                          "algorithmic_bytes_per_call": scoring_rows(n, cfg.d_model, cfg.vocab)}}
 
 
-def sampling_leg(steps: int, warmup: int):
+def sampling_leg(steps: int, warmup: int, with_cpu: bool = True):
     """Token sampling (rlt_sample_tokens) for one decode step of the 300M-class workload:
     512 rows x V=32000 fp32 logits, temperature 0.8, top-k 50 then top-p 0.95.  The kernel
     reads each logit once: N*V*4 + N*12 bytes per call, priced against HBM."""
@@ -222,11 +248,20 @@ def sampling_leg(steps: int, warmup: int):
         torch.cuda.synchronize()
         out[name] = ev[0].elapsed_time(ev[1]) / steps
     ms = out["top_k50_top_p0.95"]
+    cpu = None
+    if with_cpu:
+        import oracle
+        l_host = logits.cpu().numpy()
+        u_host = u.cpu().numpy()
+        rate, done, used = _oracle_rows_per_s(
+            lambda i, k: oracle.sample_tokens(l_host[i:i + k], u_host[i:i + k], 0.8, 50, 0.95), n)
+        cpu = {"value": rate, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} of {n} rows through oracle.sample_tokens (fp64 numpy), {used:.1f} s"}
     nbytes = n * V * 4.0 + n * 12.0
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": f"token sampling, {n} rows x V={V} fp32 logits, T=0.8, top-k 50 then top-p 0.95",
             "rows_per_s": n / (ms * 1e-3), "ms_per_call": ms,
-            "ms_per_call_by_truncation": out,
+            "ms_per_call_by_truncation": out, "cpu_baseline": cpu,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
                          "traffic": measured_traffic(SAMPLE_TRAFFIC_FILE, SAMPLE_SOURCES), "kernel": "sample_k<64>",
@@ -423,8 +458,8 @@ def main():
         torch.cuda.empty_cache()
         line["decoder_300m"] = decoder_300m_leg()
     if not args.no_scoring:
-        line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2)
-        line["sampling"] = sampling_leg(max(3, min(args.steps, 10)), 2)
+        line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
+        line["sampling"] = sampling_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, weights, tokens)
     print(json.dumps(line), flush=True)
