@@ -328,8 +328,14 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
     lo = (k1 && run > target && lo == 0x7fffffff) ? j0 + c : lo;
     hi = k1 ? j0 + c : hi;
   }
-  if (lo != 0x7fffffff) atomicMin(&pick_lo, lo);
-  if (hi >= 0) atomicMax(&pick_hi, hi);
+  // one LDS atomic per wave: the wave's minimum candidate and maximum kept id first (ids are
+  // below 2^24, exact as floats)
+  const float wlo = -wave_max(-static_cast<float>(lo == 0x7fffffff ? (1 << 24) : lo));
+  const float whi = wave_max(static_cast<float>(hi));
+  if (threadIdx.x % 64 == 0) {
+    if (wlo < static_cast<float>(1 << 24)) atomicMin(&pick_lo, static_cast<int>(wlo));
+    if (whi >= 0.f) atomicMax(&pick_hi, static_cast<int>(whi));
+  }
   __syncthreads();
   const int pick = pick_lo != 0x7fffffff ? pick_lo : pick_hi;   // u at the top edge: the last kept id
   if (pick >= j0 && pick < j0 + C) {
