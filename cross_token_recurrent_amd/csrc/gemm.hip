@@ -5,8 +5,8 @@
 // co-design: encoder features and memory projections are token-parallel).
 // bf16 mode: v_mfma_f32_16x16x32_bf16 with fp32 accumulation; fp32 mode:
 // v_mfma_f32_16x16x4_f32.  A block computes a 128x128 tile with 4 waves (2x2), each
-// wave a 64x64 sub-tile of 4x4 MFMA 16x16 tiles; K advances 32 per LDS stage, with the
-// next stage's global loads issued before the current stage's MFMAs.  The epilogue stages
+// wave a 64x64 sub-tile of 4x4 MFMA 16x16 tiles; K advances 64 per LDS stage (two MFMA
+// k-steps between barriers), with up to two stages of global loads in flight ahead of it.  The epilogue stages
 // each wave's results through LDS, 16 rows at a time, so every lane writes whole 16-byte
 // chunks of a row (or of a head's slice of it, for the cache scatters).
 #include "device_common.h"
@@ -15,7 +15,7 @@
 namespace rlt {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int NTH = 256;
 
 template <typename TW> struct Tile;
@@ -184,18 +184,21 @@ __global__ __launch_bounds__(NTH) void gemm_nt_k(GemmArgs g) {
     }
     const int r16 = lane % 16, kq = lane / 16;
     if constexpr (sizeof(TW) == 2) {
-      bf16x8_t af[4], bfr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 16 + r16) * PITCH + kq * 8);
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        bf16x8_t af[4], bfr[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Ws + (wn * 64 + j * 16 + r16) * PITCH + kq * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + i * 16 + r16) * PITCH + ks * 32 + kq * 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Ws + (wn * 64 + j * 16 + r16) * PITCH + ks * 32 + kq * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < BK / 4; ++kk) {
@@ -332,9 +335,8 @@ hipError_t launch_gemm(const GemmArgs& g0, int dtype, hipStream_t st) {
   if (g.K % BK != 0) return hipErrorInvalidValue;
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
   if (grid.y > 65535u) return hipErrorInvalidValue;
-  // prefetch depth: as many stages as divide K (bf16 up to 4, fp32 up to 2)
-  const int nsd = dtype == RLT_DTYPE_BF16 ? (g.K % (4 * BK) == 0 ? 4 : g.K % (2 * BK) == 0 ? 2 : 1)
-                                          : (g.K % (2 * BK) == 0 ? 2 : 1);
+  // prefetch depth: two stages when they divide K
+  const int nsd = g.K % (2 * BK) == 0 ? 2 : 1;
   // split K when the output tiles leave most CUs idle (fp32-output epilogues only): the
   // largest S <= 8 whose slices stay multiples of the prefetch depth and fit the workspace
   g.k_split = 1;
@@ -348,15 +350,13 @@ hipError_t launch_gemm(const GemmArgs& g0, int dtype, hipStream_t st) {
     g.k_split = S;
   }
   grid.z = g.k_split;
-  const bool k4 = nsd == 4, k2 = nsd == 2;
+  const bool k2 = nsd == 2;
   if (dtype == RLT_DTYPE_BF16) {
     if (g.a_f32) {
-      if (k4) gemm_nt_k<bf16_t, true, 4><<<grid, NTH, 0, st>>>(g);
-      else if (k2) gemm_nt_k<bf16_t, true, 2><<<grid, NTH, 0, st>>>(g);
+      if (k2) gemm_nt_k<bf16_t, true, 2><<<grid, NTH, 0, st>>>(g);
       else gemm_nt_k<bf16_t, true, 1><<<grid, NTH, 0, st>>>(g);
     } else {
-      if (k4) gemm_nt_k<bf16_t, false, 4><<<grid, NTH, 0, st>>>(g);
-      else if (k2) gemm_nt_k<bf16_t, false, 2><<<grid, NTH, 0, st>>>(g);
+      if (k2) gemm_nt_k<bf16_t, false, 2><<<grid, NTH, 0, st>>>(g);
       else gemm_nt_k<bf16_t, false, 1><<<grid, NTH, 0, st>>>(g);
     }
   } else {
