@@ -184,17 +184,19 @@ __device__ __forceinline__ void wave_finish(const SoftState& st, float* __restri
   }
 }
 
-// Window self-attention, one wave per (head, sequence).
-template <typename WT, int DH>
-__global__ __launch_bounds__(64) void swa_k(const float* __restrict__ qkv, WT* __restrict__ ring_k,
-                                            WT* __restrict__ ring_v, WT* __restrict__ attn, int B, int H, int Wm1,
-                                            int t, float scale) {
+// Window self-attention, one workgroup of SWA_WAVES waves per (head, sequence): each wave takes a
+// contiguous share of the window entries with its own online softmax, and wave 0 combines the
+// waves' (m, l, o) in wave order.  Several waves only pay when (head, sequence) pairs are few.
+template <typename WT, int DH, int SWA_WAVES>
+__global__ __launch_bounds__(64 * SWA_WAVES) void swa_k(const float* __restrict__ qkv, WT* __restrict__ ring_k,
+                                                        WT* __restrict__ ring_v, WT* __restrict__ attn, int B, int H,
+                                                        int Wm1, int t, float scale) {
   constexpr int LPK = DH / 16;
   constexpr int SLOTS = 64 / LPK;
-  __shared__ float lds[64 * 17 + 64];
-  __shared__ float outf[DH];
+  __shared__ float lds[SWA_WAVES][64 * 17 + 64];
+  __shared__ float pm[SWA_WAVES], pl[SWA_WAVES], po[SWA_WAVES][DH];
   const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int slot = lane / LPK, sub = lane % LPK;
   const int D = H * DH;
   const float* qr = qkv + static_cast<size_t>(b) * 3 * D + h * DH + sub * 16;
@@ -217,10 +219,12 @@ __global__ __launch_bounds__(64) void swa_k(const float* __restrict__ qkv, WT* _
   }
   SoftState st;
   st.init();
-  // entries i < npast come from the ring, i == npast is the current one, i > npast are masked;
+  // this wave's entries [e0, e1); i < npast come from the ring, i == npast is the current one;
   // ring slots are clamped so that every load is unconditional, and four rounds are unrolled
   // so their loads are in flight together
-  for (int i0 = 0; i0 < ne; i0 += 4 * SLOTS) {
+  const int share = ((ne + SWA_WAVES - 1) / SWA_WAVES + SLOTS - 1) / SLOTS * SLOTS;
+  const int e0 = wave * share, e1 = min(e0 + share, ne);
+  for (int i0 = e0; i0 < e1; i0 += 4 * SLOTS) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + r * SLOTS + slot;
@@ -241,17 +245,32 @@ __global__ __launch_bounds__(64) void swa_k(const float* __restrict__ qkv, WT* _
 #pragma unroll
       for (int c = 0; c < 16; ++c) a += q[c] * k[c];
       a = group_sum<LPK>(a);
-      st.add(i < ne ? a : -INFINITY, v);
+      st.add(i < e1 ? a : -INFINITY, v);
     }
   }
-  wave_finish<DH>(st, lds, nullptr, nullptr, nullptr, outf, lane);
+  wave_finish<DH>(st, lds[wave], &pm[wave], &pl[wave], po[wave], nullptr, lane);
   __syncthreads();
-  for (int d = lane; d < DH; d += 64) store_from_f32(&attn[static_cast<size_t>(b) * D + h * DH + d], outf[d]);
-  // the current entry replaces the oldest one (position t - (W-1)); all reads are done
+  if (wave == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < SWA_WAVES; ++w) M = fmaxf(M, pm[w]);
+    for (int d = lane; d < DH; d += 64) {
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < SWA_WAVES; ++w) {
+        const float f = pm[w] == -INFINITY ? 0.f : __expf(pm[w] - M);
+        num += po[w][d] * f;
+        den += pl[w] * f;
+      }
+      store_from_f32(&attn[static_cast<size_t>(b) * D + h * DH + d], num / den);
+    }
+  }
+  // the current entry replaces the oldest one (position t - (W-1)); every read of the ring
+  // happened before the barrier above
   if (Wm1 > 0) {
     const int sl = t % Wm1;
     const float* kr = qkv + static_cast<size_t>(b) * 3 * D + D + h * DH;
-    for (int d = lane; d < DH; d += 64) {
+    for (int d = threadIdx.x; d < DH; d += 64 * SWA_WAVES) {
       store_from_f32(&ring_k[rbase + static_cast<size_t>(sl) * DH + d], kr[d]);
       store_from_f32(&ring_v[rbase + static_cast<size_t>(sl) * DH + d], kr[D + d]);
     }
@@ -373,10 +392,14 @@ hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratc
   const float scale = 1.0f / sqrtf(static_cast<float>(DH));
   if (self) {
     const size_t lay = static_cast<size_t>(l) * B * H * S.Wm1 * DH;
-    swa_k<WT, DH><<<dim3(H, B), 64, 0, st>>>(reinterpret_cast<const float*>(base + sc.qkv),
-                                             reinterpret_cast<WT*>(state + S.ring_k) + lay,
-                                             reinterpret_cast<WT*>(state + S.ring_v) + lay,
-                                             reinterpret_cast<WT*>(base + sc.attn), B, H, S.Wm1, t, scale);
+    const float* q = reinterpret_cast<const float*>(base + sc.qkv);
+    WT* rk = reinterpret_cast<WT*>(state + S.ring_k) + lay;
+    WT* rv = reinterpret_cast<WT*>(state + S.ring_v) + lay;
+    WT* out = reinterpret_cast<WT*>(base + sc.attn);
+    if (B * H >= 2048)
+      swa_k<WT, DH, 1><<<dim3(H, B), 64, 0, st>>>(q, rk, rv, out, B, H, S.Wm1, t, scale);
+    else
+      swa_k<WT, DH, 4><<<dim3(H, B), 256, 0, st>>>(q, rk, rv, out, B, H, S.Wm1, t, scale);
   } else {
     const int g = m.G == 1 ? 0 : l;
     const size_t goff = static_cast<size_t>(g) * B * S.T * m.D;
