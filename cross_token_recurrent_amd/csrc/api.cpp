@@ -173,6 +173,23 @@ int pack_weights(const rlt_model& m, const float* w, hipStream_t st) {
   TRY(f32(src("g_dec_ffn"), L.g_dec_ffn, static_cast<size_t>(L.L) * D));
   TRY(f32(src("g_dec_final"), L.g_dec_final, D));
   if (L.has_wout_frag) RLT_HIP(launch_pack_score_head(src("w_out"), ws + L.wout_frag, L.V, D, st), "pack head fragments");
+  if (L.has_frag) {
+    auto frag = [&](size_t from, size_t to, int N, int K) -> int {
+      RLT_HIP(launch_pack_frag(ws + from, ws + to, N, K, st), "pack weight fragments");
+      return RLT_OK;
+    };
+    TRY(frag(L.wgate, L.frag_wgate, D, 2 * D));
+    TRY(frag(L.wfb, L.frag_wfb, D, D));
+    for (int l = 0; l < L.L; ++l) {
+      const size_t src_l = L.layers + l * L.layer_stride, dst_l = L.frag_layers + l * L.layer_stride;
+      TRY(frag(src_l + L.l_qkv, dst_l + L.l_qkv, 3 * D, D));
+      TRY(frag(src_l + L.l_wo, dst_l + L.l_wo, D, D));
+      TRY(frag(src_l + L.l_wqx, dst_l + L.l_wqx, D, D));
+      TRY(frag(src_l + L.l_wox, dst_l + L.l_wox, D, D));
+      TRY(frag(src_l + L.l_fin, dst_l + L.l_fin, L.F2, D));
+      TRY(frag(src_l + L.l_fout, dst_l + L.l_fout, D, F));
+    }
+  }
 #undef TRY
   return RLT_OK;
 }
@@ -260,6 +277,14 @@ bool compute_model_layout(const rlt_config& c, ModelLayout* m) {
   L.g_dec_cross = take(L.L * D * 4);
   L.g_dec_ffn = take(L.L * D * 4);
   L.g_dec_final = take(D * 4);
+  L.has_frag = L.dtype == RLT_DTYPE_BF16 && L.D >= 256 ? 1 : 0;
+  if (L.has_frag) {
+    L.frag_layers = take(L.L * L.layer_stride);
+    L.frag_wgate = take(2 * D * D * e);
+    L.frag_wfb = take(D * D * e);
+  } else {
+    L.frag_layers = L.frag_wgate = L.frag_wfb = 0;
+  }
   L.has_wout_frag = score_frag_eligible(L.dtype, L.D) ? 1 : 0;
   L.wout_frag = L.has_wout_frag ? take((V + 15) / 16 * 16 * D * 2) : 0;
   L.total = off;

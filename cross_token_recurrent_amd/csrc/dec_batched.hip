@@ -54,7 +54,9 @@ Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   s.attn = take(Bz * D * e);
   s.act = take(Bz * static_cast<size_t>(m.F) * e);
   s.part = take(Bz * m.H * static_cast<size_t>(s.nsmax) * (m.DH + 2) * 4);
-  s.splitk = take(gemm_splitk_ws_floats(B, m.D) * 4);   // split-K partials of the d-wide products
+  // split-K partials: of the d-wide products, and of every product on the weight-streaming path
+  const size_t wsf = m.has_frag && B <= 64 ? wsgemm_ws_floats(B, std::max(m.D * 3, m.F2), m.D) : 0;
+  s.splitk = take(std::max(gemm_splitk_ws_floats(B, m.D), wsf) * 4);
   s.total = off;
   return s;
 }
@@ -447,7 +449,22 @@ hipError_t run_t(const ModelLayout& m, const StateLayout& S, const char* ws, cha
     e = (x);                             \
     if (e != hipSuccess) return e;       \
   } while (0)
+  // decode-sized batches stream the weights of the long-K products (FFN output, merge) from
+  // their fragment-major copies; where N >= K the tiled product is as fast (the activation
+  // slice every 64-column tile reloads costs as much as the weights it saves)
+  const bool stream_w = m.has_frag && B <= 64 && dt == RLT_DTYPE_BF16;
+  const size_t frag_shift = m.frag_layers - m.layers;   // same block layout
   auto gemm = [&](const void* A, int lda, const void* W, int N, int K, void* out, int ldo, int epi) {
+    if (stream_w && K > N && wsgemm_supported(B, N, K)) {
+      const char* wp = static_cast<const char*>(W);
+      const char* wf = wp == ws + m.wgate ? ws + m.frag_wgate
+                     : wp == ws + m.wfb   ? ws + m.frag_wfb
+                                          : wp + frag_shift;
+      return launch_wsgemm(A, lda, wf, B, N, K, out, ldo, epi, reinterpret_cast<float*>(base + sc.splitk),
+                           std::max(gemm_splitk_ws_floats(B, D),
+                                    wsgemm_ws_floats(B, std::max(m.D * 3, m.F2), m.D)),
+                           st);
+    }
     GemmArgs g{};
     g.A = A; g.W = W; g.out = out;
     g.M = B; g.N = N; g.K = K; g.lda = lda; g.ldw = K; g.ldo = ldo; g.epi = epi;

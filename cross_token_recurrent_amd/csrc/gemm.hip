@@ -372,3 +372,173 @@ hipError_t launch_gemm(const GemmArgs& g0, int dtype, hipStream_t st) {
 }
 
 }  // namespace rlt
+
+// ---------------------------------------------------------------------------------------------
+// Weight-streaming products for decode-sized batches (M <= 64 rows, bf16): the rows' K-slice
+// sits in LDS once per block, and the weights stream from a fragment-major copy straight into
+// the matrix-core B operand (each load one contiguous kilobyte of 64 lanes x 16 bytes), through
+// a ring of register stages.  Four waves each own a 16-column block of a 64-column tile; K is
+// split over blockIdx.y so that about 256 blocks fill the chip; the fp32 partials are summed in
+// slice order by a second kernel that also applies the epilogue.
+//
+// Fragment-major copy of a packed [N][K] matrix (N % 16 == 0, K % 64 == 0): the 16-byte piece
+// ((cb * K/64 + ks) * 2 + h) * 64 + lane holds W[16 cb + lane % 16][64 ks + 16 (lane / 16) + 8 h .. +8].
+// ---------------------------------------------------------------------------------------------
+namespace rlt {
+namespace {
+
+constexpr int WS_MAXK = 1024;   // K-slice a block keeps in LDS (64 rows x 1024 bf16 + pad)
+constexpr int WS_NS = 4;        // register stages of the weight ring
+
+struct WsArgs {
+  const bf16_t* A;     // [M, K] row-major, lda
+  const uint4* Wf;     // fragment-major copy of W [N, K]
+  float* ws;           // [S][M][N] partials
+  int M, N, K, lda, S;
+};
+
+__global__ __launch_bounds__(256) void wsgemm_k(WsArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[64 * (WS_MAXK + 8)];
+  const int kslice = a.K / a.S, kb = blockIdx.y * kslice;
+  const int pitch = kslice + 8;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int l16 = lane % 16, grp = lane / 16;
+  // rows of A for this K-slice into LDS (rows past M are zero)
+  for (int c = threadIdx.x; c < 64 * (kslice / 8); c += 256) {
+    const int r = c / (kslice / 8), k = (c % (kslice / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < a.M) v = *reinterpret_cast<const uint4*>(a.A + static_cast<size_t>(r) * a.lda + kb + k);
+    *reinterpret_cast<uint4*>(As + r * pitch + k) = v;
+  }
+  const int KST = a.K / 64, ks0 = kb / 64, nst = kslice / 64;
+  const int cb = blockIdx.x * 4 + wave;
+  const uint4* wbase = a.Wf + static_cast<size_t>(cb) * KST * 128 + lane;
+  auto wload = [&](int s, uint4 (&b)[2]) {
+    const uint4* q = wbase + static_cast<size_t>(ks0 + min(s, nst - 1)) * 128;
+    b[0] = q[0];
+    b[1] = q[64];
+  };
+  uint4 wb[WS_NS][2];
+#pragma unroll
+  for (int s = 0; s < WS_NS; ++s) wload(s, wb[s]);
+  __syncthreads();
+  f32x4_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bf16_t* arow = As + l16 * pitch + 16 * grp;
+  for (int s0 = 0; s0 < nst; s0 += WS_NS) {
+#pragma unroll
+    for (int s = 0; s < WS_NS; ++s) {
+      if (s0 + s < nst) {   // uniform
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x8_t af =
+                *reinterpret_cast<const bf16x8_t*>(arow + i * 16 * pitch + (s0 + s) * 64 + 8 * h);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8_t, wb[s][h]), acc[i], 0,
+                                                             0, 0);
+          }
+        wload(s0 + s + WS_NS, wb[s]);
+      }
+    }
+  }
+  // partial: lane holds rows 16 i + 4 (lane / 16) + v of column 16 cb + lane % 16
+  float* out = a.ws + static_cast<size_t>(blockIdx.y) * a.M * a.N + cb * 16 + l16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * i + 4 * grp + v;
+      if (r < a.M) out[static_cast<size_t>(r) * a.N] = acc[i][v];
+    }
+}
+
+// The sum of the S partials (slice order) with an activation, into the storage type:
+// GELU over N columns, or SwiGLU over N/2 (gate and up interleaved in blocks of 16 columns).
+template <int MODE>
+__global__ __launch_bounds__(256) void ws_reduce_act_k(const float* __restrict__ ws, bf16_t* __restrict__ out, int M,
+                                                       int N, int ldo, int S) {
+  const int NO = MODE == EPI_SWIGLU ? N / 2 : N;
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<size_t>(M) * NO) return;
+  const int m = static_cast<int>(i / NO), j = static_cast<int>(i % NO);
+  const size_t plane = static_cast<size_t>(M) * N;
+  float r;
+  if constexpr (MODE == EPI_SWIGLU) {
+    const int cg = (j / 16) * 32 + j % 16;
+    float g = 0.f, u = 0.f;
+    for (int z = 0; z < S; ++z) {
+      g += ws[z * plane + static_cast<size_t>(m) * N + cg];
+      u += ws[z * plane + static_cast<size_t>(m) * N + cg + 16];
+    }
+    r = silu_f(g) * u;
+  } else {
+    float x = 0.f;
+    for (int z = 0; z < S; ++z) x += ws[z * plane + static_cast<size_t>(m) * N + j];
+    r = gelu_erf(x);
+  }
+  out[static_cast<size_t>(m) * ldo + j] = f32_to_bf16(r);
+}
+
+__global__ __launch_bounds__(256) void pack_frag_k(const bf16_t* __restrict__ w, uint4* __restrict__ dst, int N, int K,
+                                                   size_t n_pieces) {
+  const size_t c = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (c >= n_pieces) return;
+  const int lane = static_cast<int>(c % 64), h = static_cast<int>((c / 64) % 2);
+  const size_t t = c / 128;
+  const int KS = K / 64;
+  const int ks = static_cast<int>(t % KS), cb = static_cast<int>(t / KS);
+  const int row = cb * 16 + lane % 16, k = ks * 64 + 16 * (lane / 16) + 8 * h;
+  dst[c] = *reinterpret_cast<const uint4*>(w + static_cast<size_t>(row) * K + k);
+}
+
+}  // namespace
+
+size_t wsgemm_ws_floats(int M, int N, int K) {
+  // the largest split launch_wsgemm picks is 8
+  (void)K;
+  return static_cast<size_t>(8) * M * N;
+}
+
+bool wsgemm_supported(int M, int N, int K) { return M >= 1 && M <= 64 && N % 64 == 0 && K % 64 == 0; }
+
+hipError_t launch_pack_frag(const void* w, void* dst, int N, int K, hipStream_t st) {
+  if (N % 16 != 0 || K % 64 != 0) return hipErrorInvalidValue;
+  const size_t n = static_cast<size_t>(N) * K / 8;
+  pack_frag_k<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(static_cast<const bf16_t*>(w),
+                                                                        static_cast<uint4*>(dst), N, K, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_wsgemm(const void* A, int lda, const void* wfrag, int M, int N, int K, void* out, int ldo, int epi,
+                         float* ws, size_t ws_floats, hipStream_t st) {
+  if (!wsgemm_supported(M, N, K)) return hipErrorInvalidValue;
+  const int tiles = N / 64, kst = K / 64;
+  int S = 1;
+  while (kst % S != 0 || kst / S > WS_MAXK / 64) ++S;   // smallest split whose slice fits LDS
+  while (S * 2 <= 8 && kst % (S * 2) == 0 && tiles * S * 2 <= 256) S *= 2;
+  if (static_cast<size_t>(S) * M * N > ws_floats) return hipErrorInvalidValue;
+  WsArgs a{static_cast<const bf16_t*>(A), static_cast<const uint4*>(wfrag), ws, M, N, K, lda, S};
+  wsgemm_k<<<dim3(tiles, S), 256, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (epi == EPI_STORE_F32 || epi == EPI_RESID_F32) {
+    const size_t n = static_cast<size_t>(M) * (N / 4);
+    splitk_reduce_k<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(ws, static_cast<float*>(out), M, N, ldo, S,
+                                                                            epi == EPI_RESID_F32 ? 1 : 0);
+  } else if (epi == EPI_GELU) {
+    const size_t n = static_cast<size_t>(M) * N;
+    ws_reduce_act_k<EPI_GELU><<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(ws, static_cast<bf16_t*>(out),
+                                                                                    M, N, ldo, S);
+  } else if (epi == EPI_SWIGLU) {
+    const size_t n = static_cast<size_t>(M) * (N / 2);
+    ws_reduce_act_k<EPI_SWIGLU><<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(ws, static_cast<bf16_t*>(out),
+                                                                                      M, N, ldo, S);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rlt

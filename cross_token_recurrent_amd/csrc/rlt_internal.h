@@ -42,6 +42,11 @@ struct ModelLayout {
   // w_out[16 cb + lane % 16][64 ks + 16 (lane / 16) + 8 h .. + 8], rows past V zero
   int has_wout_frag;
   size_t wout_frag;
+  // fragment-major copies of the decoder's in-loop weights for the weight-streaming products
+  // (bf16, d >= 256): the same per-layer block layout as `layers` at frag_layers, and the
+  // merge matrices at frag_wgate / frag_wfb
+  int has_frag;
+  size_t frag_layers, frag_wgate, frag_wfb;
   size_t total;
 };
 
@@ -128,6 +133,15 @@ struct GemmArgs {
 };
 // Workspace floats split-K needs for an M x N product (the most launch_gemm will use).
 size_t gemm_splitk_ws_floats(int M, int N);
+// Weight-streaming product for decode-sized batches: out (epilogue epi: EPI_STORE_F32,
+// EPI_RESID_F32, EPI_GELU, EPI_SWIGLU) = A[M, K] (bf16, lda) * W^T, W given by its
+// fragment-major copy; ws holds the K-split partials (wsgemm_ws_floats(M, N, K) floats).
+bool wsgemm_supported(int M, int N, int K);
+size_t wsgemm_ws_floats(int M, int N, int K);
+hipError_t launch_wsgemm(const void* A, int lda, const void* wfrag, int M, int N, int K, void* out, int ldo, int epi,
+                         float* ws, size_t ws_floats, hipStream_t st);
+// Fragment-major copy of a packed bf16 [N][K] matrix (N % 16 == 0, K % 64 == 0).
+hipError_t launch_pack_frag(const void* w, void* dst, int N, int K, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
 
 // Action scoring: logp_i = log softmax(W_out s_i / temperature)[a_i] (and the ratio against

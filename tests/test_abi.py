@@ -48,7 +48,8 @@ def test_workspace_bytes(name):
     nbytes = rlt.rlt_model_workspace_bytes(make_config(cfg))
     esz = 2 if cfg.dtype == "bf16" else 4
     nparams = sum(int(np.prod(s)) for _, s, _ in param_shapes(cfg))
-    assert nparams * esz <= nbytes <= nparams * 4 + (1 << 20)
+    # bf16 models with d >= 256 also hold fragment-major copies of the decoder weights and the head
+    assert nparams * esz <= nbytes <= nparams * 4 + cfg.vocab * cfg.d_model * 2 + (1 << 20)
 
 
 def _cfg(**kw):
