@@ -268,7 +268,7 @@ def sampling_leg(steps: int, warmup: int, with_cpu: bool = True):
                          "algorithmic_bytes_per_call": nbytes}}
 
 
-def decoder_300m_leg(t0: int = 1024, n: int = 64):
+def decoder_300m_leg(t0: int = 1024, n: int = 64, name: str = "300m"):
     """The batched decoder on the 300M-class workload (d=1024, 12+12 layers, SwiGLU 4096,
     W=128, G=L, V=32000, B=512, bf16): encode t0+n positions, replay 1..t0 (timed as a whole),
     then n more steps timed with HIP events; both against the decoder's algorithmic bytes.
@@ -281,7 +281,7 @@ def decoder_300m_leg(t0: int = 1024, n: int = 64):
     import cross_token_recurrent_amd as rlt
     from workloads import CONFIGS, make_tokens, make_weights
 
-    wl = CONFIGS["300m"]
+    wl = CONFIGS[name]
     cfg, B = wl.model, wl.batch
     w = make_weights(cfg, wl.weight_seed)
     model = rlt.Model(cfg, w, device=torch.device("cuda:0"))
@@ -305,7 +305,7 @@ def decoder_300m_leg(t0: int = 1024, n: int = 64):
     path = {1: "persistent-per-sequence", 2: "batched-phases"}[model.decoder_path(t0 + n)]
     del state, model
     torch.cuda.empty_cache()
-    return {"workload": f"300m: RLT d={cfg.d_model} H={cfg.n_heads} L_E=L_D={cfg.n_layers} F={cfg.ffn_dim} "
+    return {"workload": f"{name}: RLT d={cfg.d_model} H={cfg.n_heads} L_E=L_D={cfg.n_layers} F={cfg.ffn_dim} "
                         f"{cfg.ffn_kind} W={cfg.window} G={cfg.mem_groups} V={cfg.vocab}, B={B}, Zipf tokens",
             "decoder_path": path,
             "steps_1_to_t0": {"t0": t0, "ms": ms_a, "tokens_per_s": B * t0 / (ms_a * 1e-3),
@@ -360,6 +360,8 @@ def main():
     ap.add_argument("--no-300m", action="store_true", help="skip the 300M-class batched decoder measurement")
     ap.add_argument("--only-300m", action="store_true",
                     help="run only the 300M-class batched decoder measurement (for profiling)")
+    ap.add_argument("--only-ref48", action="store_true",
+                    help="run only the same measurement on the 48+48-layer reference model (B=64)")
     ap.add_argument("--copy-kernel", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.copy_kernel:
@@ -367,6 +369,9 @@ def main():
         return
     if args.only_300m:
         print(json.dumps({"decoder_300m": decoder_300m_leg()}), flush=True)
+        return
+    if args.only_ref48:
+        print(json.dumps({"decoder_ref48": decoder_300m_leg(1024, 32, "ref48")}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the replay shards over sequences with no communication, "
