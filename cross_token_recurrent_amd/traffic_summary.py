@@ -54,8 +54,8 @@ def score_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
     with open(out, "w") as f:
         f.write("# score_lse_res_k on the scoring leg (head V=32000, d=1024, bf16, 65536 rows): HBM traffic per launch\n\n")
         f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
-        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
-        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
         f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    python -m cross_token_recurrent_amd.traffic_summary --score <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/score_lse_res_k_head32000x1024_traffic.md\n\n")
@@ -86,8 +86,8 @@ def sample_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
     with open(out, "w") as f:
         f.write("# sample_k on the sampling leg (512 rows x V=32000 fp32 logits): HBM traffic per launch\n\n")
         f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
-        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
-        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
         f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    python -m cross_token_recurrent_amd.traffic_summary --sample <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/sample_k_512x32000_traffic.md\n\n")
@@ -124,8 +124,8 @@ def main(argv):
     with open(out, "w") as f:
         f.write("# dec_small_k on the small workload: HBM traffic per launch (rocprofv3 counters)\n\n")
         f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
-        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
-        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
         f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    python -m cross_token_recurrent_amd.traffic_summary <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/dec_small_k_small_traffic.md\n\n")
