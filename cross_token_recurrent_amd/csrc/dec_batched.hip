@@ -29,6 +29,7 @@ namespace rlt {
 namespace {
 
 constexpr int KCHUNK = 256;   // memory rows per cross-attention work item
+constexpr int kWideCombineSplits = 16;   // splits from which the 256-thread combine is faster
 
 struct Scratch {
   size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, total;
@@ -387,6 +388,55 @@ __global__ void cross_combine_k(const float* __restrict__ part, WT* __restrict__
   }
 }
 
+// The same combine for many splits (long memories): 256 threads per (head, sequence).  The
+// split maxima and the normaliser are taken across the threads, and the weighted sum of the
+// split outputs is divided among 256/DH groups of threads (group g takes splits g, g + G, ...,
+// eight loads in flight); the groups' sums and the waves' normaliser sums are folded in a
+// fixed order, so the result does not depend on timing.
+template <typename WT, int DH>
+__global__ __launch_bounds__(256) void cross_combine_wide_k(const float* __restrict__ part, WT* __restrict__ attn,
+                                                            int H, int ns, int nsmax) {
+  constexpr int G = 256 / DH;
+  constexpr int P = DH + 2;
+  __shared__ float red[8];
+  __shared__ float po[G][DH];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const float* pr = part + (static_cast<size_t>(b) * H + h) * nsmax * P;
+  float m = -INFINITY;
+  for (int s = tid; s < ns; s += 256) m = fmaxf(m, pr[s * P]);
+  m = group_max<64>(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float l = 0.f;
+  for (int s = tid; s < ns; s += 256) l += __expf(pr[s * P] - M) * pr[s * P + 1];
+  l = group_sum<64>(l);
+  if (lane == 0) red[4 + wave] = l;
+  const int g = tid / DH, d = tid % DH;
+  float o = 0.f;
+  int s = g;
+  for (; s + 7 * G < ns; s += 8 * G) {
+    float mv[8], v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      mv[u] = pr[(s + u * G) * P];
+      v[u] = pr[(s + u * G) * P + 2 + d];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o += __expf(mv[u] - M) * v[u];
+  }
+  for (; s < ns; s += G) o += __expf(pr[s * P] - M) * pr[s * P + 2 + d];
+  po[g][d] = o;
+  __syncthreads();
+  if (tid < DH) {
+    float acc = po[0][tid];
+#pragma unroll
+    for (int q = 1; q < G; ++q) acc += po[q][tid];
+    const float L = (red[4] + red[5]) + (red[6] + red[7]);
+    store_from_f32(&attn[static_cast<size_t>(b) * H * DH + h * DH + tid], acc / L);
+  }
+}
+
 template <typename WT, int DH>
 hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratch& sc, char* base, char* state,
                                    const StateLayout& S, int l, int t, hipStream_t st) {
@@ -413,9 +463,13 @@ hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratc
         sc.nsmax, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    cross_combine_k<WT><<<dim3(H, B), std::min(DH, 128), 0, st>>>(reinterpret_cast<const float*>(base + sc.part),
-                                                                  reinterpret_cast<WT*>(base + sc.attn), H, DH, ns,
-                                                                  sc.nsmax);
+    const float* part = reinterpret_cast<const float*>(base + sc.part);
+    WT* out = reinterpret_cast<WT*>(base + sc.attn);
+    // a few splits: one thread per dimension walks them; many: the wide combine
+    if (ns >= kWideCombineSplits)
+      cross_combine_wide_k<WT, DH><<<dim3(H, B), 256, 0, st>>>(part, out, H, ns, sc.nsmax);
+    else
+      cross_combine_k<WT><<<dim3(H, B), std::min(DH, 128), 0, st>>>(part, out, H, DH, ns, sc.nsmax);
   }
   return hipGetLastError();
 }

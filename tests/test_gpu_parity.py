@@ -173,6 +173,25 @@ def test_edge_configs(dev, over, B, T, path):
     check(f"{over} logits", Z, Z_ref, cfg.dtype)
 
 
+
+# Past 16 key chunks of 256 rows (t >= 3840) the batched decoder folds the chunk partials of
+# the cross-attention with a 256-thread combine; both sides of that switch against the oracle.
+LONG_MEMORY = [
+    (dict(n_heads=1, ffn_dim=64, window=5, mem_groups=2), 2, 4300),                  # head_dim 64, G = L
+    (dict(n_heads=4, ffn_dim=64, window=9, dtype="bf16"), 2, 4100),                  # head_dim 16, bf16
+]
+
+
+@pytest.mark.parametrize("over,B,T", LONG_MEMORY, ids=["dh64_fp32", "dh16_bf16"])
+def test_batched_long_memory_combine(dev, over, B, T):
+    cfg = mcfg(**over)
+    w = make_weights(cfg, 91)
+    tok = make_tokens(cfg.vocab, B, T, "uniform", 92)
+    S, Z, model, _ = gpu_replay(cfg, w, tok, dev, path=2)
+    S_ref, Z_ref = oracle_replay(cfg, w, tok)
+    check(f"{over} s_t", S, S_ref, cfg.dtype)
+    check(f"{over} logits", Z, Z_ref, cfg.dtype)
+
 # The persistent decoder instantiates its product loop per FFN kind and FFN output shape
 # (lanes per row x chunks per lane, or the generic loop): one case per shape class.
 FFN_SHAPES = [
