@@ -690,8 +690,6 @@ int rlt_encoder_forward(const rlt_model* model, rlt_state* state, const int32_t*
   const int bc_max = std::max(1, std::min(S.B, S.Nc / n));
   float* x = reinterpret_cast<float*>(sb + S.x);
   int32_t* flags = reinterpret_cast<int32_t*>(sb + S.flags);
-  const float* gains = nullptr;
-  (void)gains;
   for (int b0 = 0; b0 < S.B; b0 += bc_max) {
     const int bc = std::min(bc_max, S.B - b0);
     const int rows = bc * n;

@@ -125,6 +125,30 @@ def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
+def _need(cond: bool, msg: str) -> None:
+    """Argument check that stays active under ``python -O`` (a pointer of the wrong kind or
+    size must never reach the library)."""
+    if not cond:
+        raise ValueError(msg)
+
+
+def _tensor(t, name: str, dtype, device, shape=None, numel=None) -> None:
+    """t must be a contiguous tensor of dtype on device (and of the given shape or size)."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.device == device, f"{name} must be on {device}, got {t.device}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None:
+        _need(t.numel() == numel, f"{name} must hold {numel} elements, got {t.numel()}")
+
+
+def _host_bytes(t, name: str) -> None:
+    _need(isinstance(t, torch.Tensor) and t.dtype == torch.uint8 and t.device.type == "cpu" and t.is_contiguous(),
+          f"{name} must be a contiguous uint8 tensor in host memory")
+
+
 def make_config(model_cfg) -> rlt_config:
     """rlt_config from any object with the model-shape attributes (e.g. workloads.ModelConfig)."""
     c = model_cfg
@@ -153,8 +177,8 @@ def rlt_model_workspace_bytes(cfg: rlt_config) -> int:
 
 
 def rlt_encoder_forward(model: "Model", state: "State", tokens: torch.Tensor, stream=None) -> None:
-    assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tokens.dim() == 2
-    assert tokens.shape[0] == state.batch and tokens.device == state.device
+    _tensor(tokens, "tokens", torch.int32, state.device)
+    _need(tokens.dim() == 2 and tokens.shape[0] == state.batch, f"tokens must be [{state.batch}, n]")
     _check(load_library().rlt_encoder_forward(model.handle, state.handle, _ptr(tokens), tokens.shape[1],
                                               _stream(stream)))
 
@@ -162,28 +186,28 @@ def rlt_encoder_forward(model: "Model", state: "State", tokens: torch.Tensor, st
 def rlt_decoder_replay(model: "Model", state: "State", n: int, s_out: Optional[torch.Tensor] = None,
                        stream=None) -> None:
     if s_out is not None:
-        assert s_out.dtype == torch.float32 and s_out.is_contiguous()
-        assert tuple(s_out.shape) == (state.batch, n, model.d_model) and s_out.device == state.device
+        _tensor(s_out, "s_out", torch.float32, state.device, shape=(state.batch, n, model.d_model))
     _check(load_library().rlt_decoder_replay(model.handle, state.handle, n, _ptr(s_out), _stream(stream)))
 
 
 def rlt_decoder_step(model: "Model", state: "State", tokens: torch.Tensor, s_out: Optional[torch.Tensor] = None,
                      logits: Optional[torch.Tensor] = None, stream=None) -> None:
-    assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tuple(tokens.shape) == (state.batch,)
+    _tensor(tokens, "tokens", torch.int32, state.device, shape=(state.batch,))
     if s_out is not None:
-        assert s_out.dtype == torch.float32 and tuple(s_out.shape) == (state.batch, model.d_model)
+        _tensor(s_out, "s_out", torch.float32, state.device, shape=(state.batch, model.d_model))
     if logits is not None:
-        assert logits.dtype == torch.float32 and tuple(logits.shape) == (state.batch, model.vocab)
+        _tensor(logits, "logits", torch.float32, state.device, shape=(state.batch, model.vocab))
     _check(load_library().rlt_decoder_step(model.handle, state.handle, _ptr(tokens), _ptr(s_out), _ptr(logits),
                                            _stream(stream)))
 
 
 def rlt_logits(model: "Model", s: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    assert s.dtype == torch.float32 and s.is_contiguous() and s.shape[-1] == model.d_model
+    _tensor(s, "s", torch.float32, model.device)
+    _need(s.dim() >= 1 and s.shape[-1] == model.d_model, f"s must be [..., {model.d_model}]")
     rows = s.numel() // model.d_model
     if out is None:
         out = torch.empty(*s.shape[:-1], model.vocab, dtype=torch.float32, device=s.device)
-    assert out.is_contiguous() and out.numel() == rows * model.vocab
+    _tensor(out, "out", torch.float32, model.device, numel=rows * model.vocab)
     _check(load_library().rlt_logits(model.handle, _ptr(s), rows, _ptr(out), _stream(stream)))
     return out
 
@@ -192,14 +216,14 @@ def rlt_score_actions(model: "Model", s: torch.Tensor, actions: torch.Tensor, te
                       behaviour_logp: Optional[torch.Tensor] = None, stream=None):
     """logp = log softmax(W_out s / temperature)[action] per row, and the importance ratio
     exp(logp - behaviour_logp) when behaviour_logp is given (else None)."""
-    assert s.dtype == torch.float32 and s.is_contiguous() and s.shape[-1] == model.d_model
+    _tensor(s, "s", torch.float32, model.device)
+    _need(s.dim() >= 1 and s.shape[-1] == model.d_model, f"s must be [..., {model.d_model}]")
     rows = s.numel() // model.d_model
-    assert actions.dtype == torch.int32 and actions.is_contiguous() and actions.numel() == rows
+    _tensor(actions, "actions", torch.int32, model.device, numel=rows)
     logp = torch.empty(*s.shape[:-1], dtype=torch.float32, device=s.device)
     ratio = None
     if behaviour_logp is not None:
-        assert behaviour_logp.dtype == torch.float32 and behaviour_logp.is_contiguous()
-        assert behaviour_logp.numel() == rows
+        _tensor(behaviour_logp, "behaviour_logp", torch.float32, model.device, numel=rows)
         ratio = torch.empty_like(logp)
     _check(load_library().rlt_score_actions(model.handle, _ptr(s), _ptr(actions), rows, float(temperature),
                                             _ptr(behaviour_logp) if behaviour_logp is not None else None,
@@ -212,10 +236,13 @@ def rlt_sample_tokens(logits: torch.Tensor, uniforms: torch.Tensor, temperature:
                       top_p: float = 1.0, stream=None):
     """One draw per row of logits [..., V] with the caller's uniforms [...] in [0, 1):
     (tokens int32, behaviour logp fp32) under the truncated distribution actually sampled."""
-    assert logits.dtype == torch.float32 and logits.is_contiguous()
+    _need(isinstance(logits, torch.Tensor) and logits.is_cuda and logits.dim() >= 1,
+          "logits must be a [..., V] tensor in device memory")
+    _tensor(logits, "logits", torch.float32, logits.device)
     V = logits.shape[-1]
+    _need(V >= 1, "logits must have at least one column")
     rows = logits.numel() // V
-    assert uniforms.dtype == torch.float32 and uniforms.is_contiguous() and uniforms.numel() == rows
+    _tensor(uniforms, "uniforms", torch.float32, logits.device, numel=rows)
     tok = torch.empty(*logits.shape[:-1], dtype=torch.int32, device=logits.device)
     logp = torch.empty(*logits.shape[:-1], dtype=torch.float32, device=logits.device)
     p = rlt_sampling(float(temperature), int(top_k), float(top_p))
@@ -231,13 +258,13 @@ def rlt_decoder_step_sample(model: "Model", state: "State", tokens: torch.Tensor
     """Incremental step at the current position, then a draw of the next token per sequence:
     (next_tokens int32 [B], behaviour logp fp32 [B]).  ``logits`` [B, V] receives the step's
     logits (allocated when not given)."""
-    assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tuple(tokens.shape) == (state.batch,)
-    assert uniforms.dtype == torch.float32 and uniforms.is_contiguous() and uniforms.numel() == state.batch
+    _tensor(tokens, "tokens", torch.int32, state.device, shape=(state.batch,))
+    _tensor(uniforms, "uniforms", torch.float32, state.device, numel=state.batch)
     if logits is None:
         logits = torch.empty(state.batch, model.vocab, dtype=torch.float32, device=state.device)
-    assert logits.dtype == torch.float32 and tuple(logits.shape) == (state.batch, model.vocab)
+    _tensor(logits, "logits", torch.float32, state.device, shape=(state.batch, model.vocab))
     if s_out is not None:
-        assert s_out.dtype == torch.float32 and tuple(s_out.shape) == (state.batch, model.d_model)
+        _tensor(s_out, "s_out", torch.float32, state.device, shape=(state.batch, model.d_model))
     nxt = torch.empty(state.batch, dtype=torch.int32, device=state.device)
     logp = torch.empty(state.batch, dtype=torch.float32, device=state.device)
     p = rlt_sampling(float(temperature), int(top_k), float(top_p))
@@ -259,7 +286,7 @@ def rlt_state_save(model: "Model", state: "State", out: Optional[torch.Tensor] =
     n = rlt_state_snapshot_bytes(state)
     if out is None:
         out = torch.empty(n, dtype=torch.uint8, pin_memory=True)
-    assert out.dtype == torch.uint8 and out.device.type == "cpu" and out.is_contiguous()
+    _host_bytes(out, "out")
     _check(load_library().rlt_state_save(model.handle, state.handle, ctypes.c_void_p(out.data_ptr()), out.numel(),
                                          _stream(stream)))
     return out
@@ -268,21 +295,25 @@ def rlt_state_save(model: "Model", state: "State", out: Optional[torch.Tensor] =
 def rlt_state_restore(model: "Model", state: "State", snapshot: torch.Tensor, stream=None) -> None:
     """Reset `state` and load a snapshot into it (host uint8 tensor that must stay valid until
     the stream has run the copies)."""
-    assert snapshot.dtype == torch.uint8 and snapshot.device.type == "cpu" and snapshot.is_contiguous()
+    _host_bytes(snapshot, "snapshot")
     _check(load_library().rlt_state_restore(model.handle, state.handle, ctypes.c_void_p(snapshot.data_ptr()),
                                             snapshot.numel(), _stream(stream)))
 
 
 def rlt_state_load_encoder_outputs(model: "Model", state: "State", e: torch.Tensor, mem_k: torch.Tensor,
                                    mem_v: torch.Tensor, stream=None) -> None:
+    _need(isinstance(e, torch.Tensor) and e.dim() == 3, "e must be [B, n, d]")
     n = e.shape[1]
     G = model.mem_groups
-    assert e.dtype == mem_k.dtype == mem_v.dtype == torch.float32
-    assert tuple(e.shape) == (state.batch, n, model.d_model)
-    assert tuple(mem_k.shape) == (G, state.batch, n, model.d_model) == tuple(mem_v.shape)
-    _check(load_library().rlt_state_load_encoder_outputs(model.handle, state.handle, _ptr(e.contiguous()),
-                                                         _ptr(mem_k.contiguous()), _ptr(mem_v.contiguous()), n,
-                                                         _stream(stream)))
+    # contiguous copies are held by name until the call has enqueued its reads and the stream
+    # has run them (a temporary freed early could be handed to the next allocation)
+    e_c, mk_c, mv_c = (x.contiguous() if isinstance(x, torch.Tensor) else x for x in (e, mem_k, mem_v))
+    _tensor(e_c, "e", torch.float32, state.device, shape=(state.batch, n, model.d_model))
+    _tensor(mk_c, "mem_k", torch.float32, state.device, shape=(G, state.batch, n, model.d_model))
+    _tensor(mv_c, "mem_v", torch.float32, state.device, shape=(G, state.batch, n, model.d_model))
+    _check(load_library().rlt_state_load_encoder_outputs(model.handle, state.handle, _ptr(e_c), _ptr(mk_c),
+                                                         _ptr(mv_c), n, _stream(stream)))
+    (stream or torch.cuda.current_stream()).synchronize()
 
 
 def rlt_state_read_encoder_outputs(model: "Model", state: "State", t0: int, n: int, stream=None):
@@ -304,7 +335,11 @@ class Model:
                  stream=None):
         lib = load_library()
         self.cfg = make_config(model_cfg)
-        self.device = torch.device(device)
+        dev = torch.device(device)
+        _need(dev.type == "cuda", f"the model lives in device memory, not on {dev}")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
         self.d_model, self.vocab = self.cfg.d_model, self.cfg.vocab
         self.mem_groups = self.cfg.mem_groups
         ws_bytes = rlt_model_workspace_bytes(self.cfg)

@@ -104,3 +104,13 @@ def test_null_and_alignment_arguments_rejected():
     assert lib.rlt_encoder_forward(None, None, None, 1, None) == -1
     assert lib.rlt_decoder_replay(None, None, 1, None, None) == -1
     assert lib.rlt_state_reset(None, None, None) == -1
+
+
+def test_binding_rejects_host_tensors_before_the_library():
+    """The binding checks its tensors itself (active under python -O): host memory, a wrong
+    dtype or a wrong size never reaches a kernel."""
+    import torch
+    with pytest.raises(ValueError, match="device memory"):
+        rlt.rlt_sample_tokens(torch.zeros(2, 10), torch.zeros(2))
+    with pytest.raises(ValueError, match="device memory"):
+        rlt.Model(CONFIGS["tiny"].model, {}, device="cpu")

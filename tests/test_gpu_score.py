@@ -153,6 +153,9 @@ def test_score_argument_errors(dev):
     with pytest.raises(rlt.RltError) as ei:
         rlt.rlt_score_actions(model, S, acts, temperature=0.0)
     assert ei.value.name == "RLT_ERR_INVALID"
+    for bad in ((S.cpu(), acts), (S, acts.cpu()), (S.double(), acts), (S, acts[:1])):
+        with pytest.raises(ValueError):
+            rlt.rlt_score_actions(model, *bad)
     lib = rlt.load_library()
     import ctypes
     out = torch.empty(2, device=dev)
