@@ -8,8 +8,10 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "rlt_internal.h"
@@ -392,6 +394,31 @@ bool is_device_pointer(const void* p) {
   return attr.type == hipMemoryTypeDevice;
 }
 
+// Memory a kernel will read or write must be known to HIP (device, managed or pinned host
+// memory).  Plain pageable host memory is not, and a kernel touching it would fault, so it is
+// refused before anything is enqueued.  A NULL pointer passes: required arguments are checked
+// for NULL separately.
+int need_gpu_memory(const void* p, const char* what) {
+  if (!p) return RLT_OK;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(RLT_ERR_INVALID, std::string(what) + " is not memory the GPU can access (plain host memory?)");
+  }
+  if (attr.type == hipMemoryTypeUnregistered)
+    return fail(RLT_ERR_INVALID, std::string(what) + " is not memory the GPU can access (plain host memory?)");
+  return RLT_OK;
+}
+
+// need_gpu_memory over a list of (pointer, name) pairs; the first failure is returned.
+int need_gpu_memory(std::initializer_list<std::pair<const void*, const char*>> args) {
+  for (const auto& a : args) {
+    int rc = need_gpu_memory(a.first, a.second);
+    if (rc) return rc;
+  }
+  return RLT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -445,6 +472,8 @@ int rlt_model_create(const rlt_config* cfg, const float* weights, uint64_t versi
   compute_model_layout(*cfg, &L);
   if (workspace_bytes < L.total)
     return fail(RLT_ERR_INVALID, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  rc = need_gpu_memory({{weights, "weights"}, {workspace, "workspace"}});
+  if (rc) return rc;
   rlt_model* m = new (std::nothrow) rlt_model;
   if (!m) return fail(RLT_ERR_INVALID, "out of host memory");
   m->cfg = *cfg;
@@ -466,7 +495,9 @@ int rlt_model_update_weights(rlt_model* model, const float* weights, uint64_t ne
   if (!model || !weights) return fail(RLT_ERR_INVALID, "model and weights must be non-NULL");
   if (new_version == model->version)
     return fail(RLT_ERR_INVALID, "a weight update must carry a new version");
-  int rc = pack_weights(*model, weights, as_stream(stream));
+  int rc = need_gpu_memory(weights, "weights");
+  if (rc) return rc;
+  rc = pack_weights(*model, weights, as_stream(stream));
   if (rc) return rc;
   model->version = new_version;
   return RLT_OK;
@@ -501,6 +532,7 @@ int rlt_state_init(const rlt_model* model, void* buffer, size_t buffer_bytes, in
   compute_state_layout(model->lay, batch, t_max, keep_encoder_cache ? 1 : 0, &S);
   if (buffer_bytes < S.total)
     return fail(RLT_ERR_INVALID, "state buffer too small: need " + std::to_string(S.total) + " bytes");
+  if (int rc0 = need_gpu_memory(buffer, "state buffer")) return rc0;
   rlt_state* s = new (std::nothrow) rlt_state;
   if (!s) return fail(RLT_ERR_INVALID, "out of host memory");
   s->cfg = model->cfg;
@@ -675,6 +707,8 @@ int rlt_encoder_forward(const rlt_model* model, rlt_state* state, const int32_t*
   if (rc) return rc;
   if (!tokens) return fail(RLT_ERR_INVALID, "tokens is NULL");
   if (n < 1) return fail(RLT_ERR_INVALID, "n must be >= 1");
+  rc = need_gpu_memory(tokens, "tokens");
+  if (rc) return rc;
   const StateLayout& S = state->lay;
   const ModelLayout& M = model->lay;
   if (static_cast<int64_t>(state->t_enc) + n > S.T)
@@ -779,6 +813,8 @@ int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, floa
   if (n < 1) return fail(RLT_ERR_INVALID, "n must be >= 1");
   if (static_cast<int64_t>(state->t_dec) + n > state->t_enc)
     return fail(RLT_ERR_ORDER, "decoder would run ahead of the encoder (t_dec + n > t_enc)");
+  rc = need_gpu_memory(s_out, "s_out");
+  if (rc) return rc;
   const ModelLayout& M = model->lay;
   const StateLayout& S = state->lay;
   hipStream_t st = as_stream(stream);
@@ -805,6 +841,7 @@ int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, floa
 int rlt_logits(const rlt_model* model, const float* s, int64_t n_rows, float* logits, void* stream) {
   if (!model || !s || !logits) return fail(RLT_ERR_INVALID, "model, s and logits must be non-NULL");
   if (n_rows < 1 || n_rows > 0x7fffffff) return fail(RLT_ERR_INVALID, "n_rows out of range");
+  if (int rc = need_gpu_memory({{s, "s"}, {logits, "logits"}})) return rc;
   const ModelLayout& M = model->lay;
   GemmArgs g{};
   g.A = s; g.a_f32 = 1; g.W = model->ws + M.wout; g.out = logits;
@@ -821,6 +858,9 @@ int rlt_score_actions(const rlt_model* model, const float* s, const int32_t* act
   if (n_rows < 1 || n_rows > 0x7fffffff) return fail(RLT_ERR_INVALID, "n_rows out of range");
   if (!(temperature > 0.f)) return fail(RLT_ERR_INVALID, "temperature must be > 0");
   if (ratio_out && !behaviour_logp) return fail(RLT_ERR_INVALID, "ratio_out needs behaviour_logp");
+  if (int rc = need_gpu_memory({{s, "s"}, {actions, "actions"}, {behaviour_logp, "behaviour_logp"},
+                                {logp_out, "logp_out"}, {ratio_out, "ratio_out"}}))
+    return rc;
   const ModelLayout& M = model->lay;
   RLT_HIP(launch_score_actions(s, model->ws + M.wout, M.has_wout_frag ? model->ws + M.wout_frag : nullptr, actions,
                                behaviour_logp, logp_out, ratio_out,
@@ -838,6 +878,10 @@ int rlt_decoder_step(const rlt_model* model, rlt_state* state, const int32_t* to
   if (state->t_enc >= state->lay.T) return fail(RLT_ERR_CAPACITY, "state is full (t == T_max)");
   if (state->t_enc > 0 && !state->lay.keep)
     return fail(RLT_ERR_NO_ENC_CACHE, "incremental generation needs keep_encoder_cache");
+  if (!tokens) return fail(RLT_ERR_INVALID, "tokens is NULL");
+  // every pointer is checked before the first launch, so a failure enqueues nothing
+  rc = need_gpu_memory({{tokens, "tokens"}, {s_out, "s_out"}, {logits, "logits"}});
+  if (rc) return rc;
   rc = rlt_encoder_forward(model, state, tokens, 1, stream);
   if (rc) return rc;
   rc = rlt_decoder_replay(model, state, 1, s_out, stream);
@@ -871,6 +915,8 @@ int rlt_sample_tokens(const float* logits, int64_t n_rows, int32_t vocab, const 
     return fail(RLT_ERR_INVALID, "logits, uniforms, tokens_out and logp_out must be non-NULL");
   int rc = check_sampling(params, n_rows, vocab);
   if (rc) return rc;
+  rc = need_gpu_memory({{logits, "logits"}, {uniforms, "uniforms"}, {tokens_out, "tokens_out"}, {logp_out, "logp_out"}});
+  if (rc) return rc;
   RLT_HIP(launch_sample_tokens(logits, uniforms, tokens_out, logp_out, static_cast<int>(n_rows), vocab,
                                params->temperature, params->top_k, params->top_p, as_stream(stream)),
           "sample tokens");
@@ -886,6 +932,8 @@ int rlt_decoder_step_sample(const rlt_model* model, rlt_state* state, const int3
     return fail(RLT_ERR_INVALID, "logits, uniforms, next_tokens and behaviour_logp must be non-NULL");
   rc = check_sampling(params, state->lay.B, model->lay.V);
   if (rc) return rc;
+  rc = need_gpu_memory({{uniforms, "uniforms"}, {next_tokens, "next_tokens"}, {behaviour_logp, "behaviour_logp"}});
+  if (rc) return rc;
   rc = rlt_decoder_step(model, state, tokens, s_out, logits, stream);
   if (rc) return rc;
   return rlt_sample_tokens(logits, state->lay.B, model->lay.V, params, uniforms, next_tokens, behaviour_logp,
@@ -898,6 +946,8 @@ int rlt_state_load_encoder_outputs(const rlt_model* model, rlt_state* state, con
   if (rc) return rc;
   if (!e || !mem_k || !mem_v) return fail(RLT_ERR_INVALID, "e, mem_k and mem_v must be non-NULL");
   if (n < 1) return fail(RLT_ERR_INVALID, "n must be >= 1");
+  rc = need_gpu_memory({{e, "e"}, {mem_k, "mem_k"}, {mem_v, "mem_v"}});
+  if (rc) return rc;
   const StateLayout& S = state->lay;
   const ModelLayout& M = model->lay;
   if (static_cast<int64_t>(state->t_enc) + n > S.T) return fail(RLT_ERR_CAPACITY, "positions exceed T_max");
@@ -926,6 +976,7 @@ int rlt_state_read_encoder_outputs(const rlt_model* model, const rlt_state* stat
   if (std::memcmp(&model->cfg, &state->cfg, sizeof(rlt_config)) != 0)
     return fail(RLT_ERR_INVALID, "state was built for a different model configuration");
   if (n < 1 || t0 < 0 || t0 + n > state->t_enc) return fail(RLT_ERR_INVALID, "positions not encoded yet");
+  if (int rc = need_gpu_memory({{e, "e"}, {mem_k, "mem_k"}, {mem_v, "mem_v"}})) return rc;
   const StateLayout& S = state->lay;
   const ModelLayout& M = model->lay;
   hipStream_t st = as_stream(stream);

@@ -23,6 +23,9 @@
  * Conventions
  *  - Every pointer marked "device" is device memory owned by the caller; the
  *    library never allocates or frees device memory.  It keeps small host handles.
+ *    Such a pointer must be known to HIP (hipMalloc'd, managed or pinned host memory);
+ *    plain pageable host memory is refused with RLT_ERR_INVALID before anything is
+ *    enqueued, since a kernel reading it would fault.
  *  - Every call that takes a stream only enqueues work on that stream (a
  *    hipStream_t passed as void*; NULL = the default stream) and returns before the
  *    work runs.  Host-side argument and ordering checks happen before anything is

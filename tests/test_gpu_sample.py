@@ -144,6 +144,18 @@ def test_sample_argument_errors(dev):
     with pytest.raises(rlt.RltError) as ei:
         rlt.rlt_sample_tokens(big, ut[:1], 1.0, 0, 1.0)
     assert ei.value.name == "RLT_ERR_UNSUPPORTED"
+    # plain host memory is refused by the library before anything is launched
+    import ctypes
+    lib = rlt.load_library()
+    host = torch.zeros(2, 10)
+    tok = torch.empty(2, dtype=torch.int32, device=dev)
+    lp = torch.empty(2, device=dev)
+    from cross_token_recurrent_amd.rlt import rlt_sampling
+    params = rlt_sampling(1.0, 0, 1.0)
+    rc = lib.rlt_sample_tokens(ctypes.c_void_p(host.data_ptr()), 2, 10, ctypes.byref(params),
+                               ctypes.c_void_p(ut.data_ptr()), ctypes.c_void_p(tok.data_ptr()),
+                               ctypes.c_void_p(lp.data_ptr()), None)
+    assert rlt.RltError(rc, "").name == "RLT_ERR_INVALID" and b"GPU can access" in lib.rlt_last_error()
 
 
 def test_decoder_step_sample(dev):

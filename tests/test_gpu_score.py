@@ -162,6 +162,11 @@ def test_score_argument_errors(dev):
     rc = lib.rlt_score_actions(model.handle, ctypes.c_void_p(S.data_ptr()), ctypes.c_void_p(acts.data_ptr()), 2,
                                1.0, None, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(out.data_ptr()), None)
     assert rc != 0
+    # the library itself refuses plain host memory before launching anything
+    host = torch.zeros(2, 64)
+    rc = lib.rlt_score_actions(model.handle, ctypes.c_void_p(host.data_ptr()), ctypes.c_void_p(acts.data_ptr()), 2,
+                               1.0, None, ctypes.c_void_p(out.data_ptr()), None, None)
+    assert rlt.RltError(rc, "").name == "RLT_ERR_INVALID" and b"GPU can access" in lib.rlt_last_error()
 
 
 def test_score_after_replay(dev):
