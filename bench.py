@@ -317,12 +317,13 @@ def decoder_300m_leg(t0: int = 1024, n: int = 64, name: str = "300m"):
                                         "algorithmic_bytes": bytes_b}}}
 
 
-def long_context_leg(chunk: int = 2048):
-    """The long-context workload (d=1024, 48+48 layers, SwiGLU 2816, W=512, G=1, V=32000,
-    B=16, T=32768, bf16, Zipf tokens) replayed in full: the encoder over all T positions, then
-    the decoder over t = 1..T in segments of `chunk` steps, each timed with HIP events and
-    set against its algorithmic bytes (cross-attention to M_{<=t} grows with t and dominates
-    the late segments).  A line per segment goes to stderr as the run proceeds."""
+def full_replay_leg(name: str = "long", chunk: int = 2048):
+    """A large workload replayed over its full T: the encoder over all T positions, then the
+    decoder over t = 1..T in segments of `chunk` steps, each timed with HIP events and set
+    against its algorithmic bytes (cross-attention to M_{<=t} grows with t and dominates the
+    late segments).  Used for the long-context workload (d=1024, 48+48 layers, SwiGLU 2816,
+    W=512, G=1, B=16, T=32768) and the 48+48-layer reference model (d=2048, SwiGLU 5632,
+    W=256, G=1, B=64, T=4096).  A line per segment goes to stderr as the run proceeds."""
     import time
 
     import torch
@@ -330,7 +331,7 @@ def long_context_leg(chunk: int = 2048):
     import cross_token_recurrent_amd as rlt
     from workloads import CONFIGS, make_tokens, make_weights
 
-    wl = CONFIGS["long"]
+    wl = CONFIGS[name]
     cfg, B, T = wl.model, wl.batch, wl.seq_len
     t_start = time.time()
     w = make_weights(cfg, wl.weight_seed)
@@ -338,7 +339,7 @@ def long_context_leg(chunk: int = 2048):
     del w
     state = rlt.State(model, B, T)
     tok = torch.from_numpy(make_tokens(cfg.vocab, B, T, wl.token_dist, wl.token_seed)).cuda()
-    print(f"long: model and state ready in {time.time() - t_start:.1f} s", file=sys.stderr, flush=True)
+    print(f"{name}: model and state ready in {time.time() - t_start:.1f} s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
@@ -346,7 +347,7 @@ def long_context_leg(chunk: int = 2048):
     ev[1].record(stream)
     torch.cuda.synchronize()
     enc_ms = ev[0].elapsed_time(ev[1])
-    print(f"long: encoder over {B} x {T} tokens in {enc_ms:.0f} ms", file=sys.stderr, flush=True)
+    print(f"{name}: encoder over {B} x {T} tokens in {enc_ms:.0f} ms", file=sys.stderr, flush=True)
     segments, done, prev_bytes = [], 0, 0.0
     while done < T:
         n = min(chunk, T - done)
@@ -359,7 +360,7 @@ def long_context_leg(chunk: int = 2048):
         gbs = (cum - prev_bytes) / (ms * 1e-3) / 1e9
         segments.append({"t": [done + 1, done + n], "ms_per_step": ms / n, "tokens_per_s": B * n / (ms * 1e-3),
                          "achieved_GBps": gbs, "frac_of_hbm": gbs / HBM_PEAK_GBS})
-        print(f"long: steps {done + 1}..{done + n}: {ms / n:.2f} ms/step, {gbs:.0f} GB/s "
+        print(f"{name}: steps {done + 1}..{done + n}: {ms / n:.2f} ms/step, {gbs:.0f} GB/s "
               f"({100 * gbs / HBM_PEAK_GBS:.1f} % of HBM)", file=sys.stderr, flush=True)
         done += n
         prev_bytes = cum
@@ -370,7 +371,7 @@ def long_context_leg(chunk: int = 2048):
     torch.cuda.empty_cache()
     gbs_all = prev_bytes / (dec_ms * 1e-3) / 1e9
     late = segments[-1]
-    return {"workload": f"long: RLT d={cfg.d_model} H={cfg.n_heads} L_E=L_D={cfg.n_layers} F={cfg.ffn_dim} "
+    return {"workload": f"{name}: RLT d={cfg.d_model} H={cfg.n_heads} L_E=L_D={cfg.n_layers} F={cfg.ffn_dim} "
                         f"{cfg.ffn_kind} W={cfg.window} G={cfg.mem_groups} V={cfg.vocab}, B={B}, T={T}, Zipf tokens",
             "decoder_path": path, "encoder_ms": enc_ms,
             "replay": {"ms": dec_ms, "tokens_per_s": B * T / (dec_ms * 1e-3), "achieved_GBps": gbs_all,
@@ -429,6 +430,8 @@ def main():
                     help="run only the same measurement on the 48+48-layer reference model (B=64)")
     ap.add_argument("--only-long", action="store_true",
                     help="run only the full replay of the long-context workload (B=16, T=32768; several minutes)")
+    ap.add_argument("--full-ref48", action="store_true",
+                    help="run only the full replay of the 48+48-layer reference model (B=64, T=4096; minutes)")
     ap.add_argument("--copy-kernel", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.copy_kernel:
@@ -441,7 +444,10 @@ def main():
         print(json.dumps({"decoder_ref48": decoder_300m_leg(1024, 32, "ref48")}), flush=True)
         return
     if args.only_long:
-        print(json.dumps({"decoder_long": long_context_leg()}), flush=True)
+        print(json.dumps({"decoder_long": full_replay_leg("long", 2048)}), flush=True)
+        return
+    if args.full_ref48:
+        print(json.dumps({"decoder_ref48_full": full_replay_leg("ref48", 512)}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the replay shards over sequences with no communication, "

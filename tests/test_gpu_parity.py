@@ -179,10 +179,11 @@ def test_edge_configs(dev, over, B, T, path):
 LONG_MEMORY = [
     (dict(n_heads=1, ffn_dim=64, window=5, mem_groups=2), 2, 4300),                  # head_dim 64, G = L
     (dict(n_heads=4, ffn_dim=64, window=9, dtype="bf16"), 2, 4100),                  # head_dim 16, bf16
+    (dict(d_model=128, n_heads=1, ffn_dim=64, window=3, dtype="bf16"), 1, 3900),     # head_dim 128, bf16
 ]
 
 
-@pytest.mark.parametrize("over,B,T", LONG_MEMORY, ids=["dh64_fp32", "dh16_bf16"])
+@pytest.mark.parametrize("over,B,T", LONG_MEMORY, ids=["dh64_fp32", "dh16_bf16", "dh128_bf16"])
 def test_batched_long_memory_combine(dev, over, B, T):
     cfg = mcfg(**over)
     w = make_weights(cfg, 91)
