@@ -322,8 +322,9 @@ def full_replay_leg(name: str = "long", chunk: int = 2048):
     decoder over t = 1..T in segments of `chunk` steps, each timed with HIP events and set
     against its algorithmic bytes (cross-attention to M_{<=t} grows with t and dominates the
     late segments).  Used for the long-context workload (d=1024, 48+48 layers, SwiGLU 2816,
-    W=512, G=1, B=16, T=32768) and the 48+48-layer reference model (d=2048, SwiGLU 5632,
-    W=256, G=1, B=64, T=4096).  A line per segment goes to stderr as the run proceeds."""
+    W=512, G=1, B=16, T=32768), the 48+48-layer reference model (d=2048, SwiGLU 5632,
+    W=256, G=1, B=64, T=4096) and the 300M-class workload (d=1024, 12+12 layers, SwiGLU
+    4096, W=128, G=12, B=512, T=2048).  A line per segment goes to stderr as the run proceeds."""
     import time
 
     import torch
@@ -430,6 +431,8 @@ def main():
                     help="run only the same measurement on the 48+48-layer reference model (B=64)")
     ap.add_argument("--only-long", action="store_true",
                     help="run only the full replay of the long-context workload (B=16, T=32768; several minutes)")
+    ap.add_argument("--full-300m", action="store_true",
+                    help="run only the full replay of the 300M-class workload (B=512, T=2048)")
     ap.add_argument("--full-ref48", action="store_true",
                     help="run only the full replay of the 48+48-layer reference model (B=64, T=4096; minutes)")
     ap.add_argument("--copy-kernel", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
@@ -448,6 +451,9 @@ def main():
         return
     if args.full_ref48:
         print(json.dumps({"decoder_ref48_full": full_replay_leg("ref48", 512)}), flush=True)
+        return
+    if args.full_300m:
+        print(json.dumps({"decoder_300m_full": full_replay_leg("300m", 256)}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the replay shards over sequences with no communication, "
