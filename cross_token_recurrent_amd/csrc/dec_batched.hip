@@ -30,6 +30,11 @@ namespace {
 
 constexpr int KCHUNK = 256;   // memory rows per cross-attention work item
 constexpr int kWideCombineSplits = 16;   // splits from which the 256-thread combine is faster
+// The weight-streaming product re-reads the block's B activation rows once per 64 output
+// columns, B/64 of the weight bytes it streams.  It is used where K > N, and for every shape
+// when B <= 16 (a quarter of the weight bytes or less): at B = 16 a 48-layer step drops from
+// 5.4 to 4.5 ms, while at B = 64 the tiled products stay faster for N >= K.
+constexpr int kWsAllShapesMaxB = 16;
 
 struct Scratch {
   size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, total;
@@ -509,7 +514,7 @@ hipError_t run_t(const ModelLayout& m, const StateLayout& S, const char* ws, cha
   const bool stream_w = m.has_frag && B <= 64 && dt == RLT_DTYPE_BF16;
   const size_t frag_shift = m.frag_layers - m.layers;   // same block layout
   auto gemm = [&](const void* A, int lda, const void* W, int N, int K, void* out, int ldo, int epi) {
-    if (stream_w && K > N && wsgemm_supported(B, N, K)) {
+    if (stream_w && (K > N || B <= kWsAllShapesMaxB) && wsgemm_supported(B, N, K)) {
       const char* wp = static_cast<const char*>(W);
       const char* wf = wp == ws + m.wgate ? ws + m.frag_wgate
                      : wp == ws + m.wfb   ? ws + m.frag_wfb

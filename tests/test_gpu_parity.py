@@ -399,14 +399,17 @@ def test_paths_can_alternate_on_one_state(dev):
     np.testing.assert_allclose(S, S_ref, rtol=0, atol=2e-5)
 
 
-def test_batched_split_k_is_deterministic(dev):
-    """The batched decoder splits its d-wide products over K when few output tiles exist
-    (here M = B = 6 rows, d = 256: two output tiles, two to four K slices) and adds the partials in a fixed
-    order: two replays of the same input are bitwise equal, and both match the oracle."""
-    cfg = mcfg(vocab=128, d_model=256, n_heads=4, n_layers=2, ffn_dim=512, ffn_kind="swiglu", window=6,
+@pytest.mark.parametrize("B,ffn", [(6, "swiglu"), (5, "gelu"), (24, "swiglu")], ids=["ws_swiglu", "ws_gelu", "tiled"])
+def test_batched_split_k_is_deterministic(dev, B, ffn):
+    """The batched decoder splits its products over K and adds the partials in a fixed order.
+    With B <= 16 rows (bf16, d = 256) every product streams the weights from their fragment
+    copies (SwiGLU and GELU epilogues); with B = 24 the products with N >= K take the tiled
+    kernel split over K (two output tiles, two to four K slices).  Two replays of the same
+    input are bitwise equal, and both match the oracle."""
+    cfg = mcfg(vocab=128, d_model=256, n_heads=4, n_layers=2, ffn_dim=512, ffn_kind=ffn, window=6,
                mem_groups=2, dtype="bf16")
     w = make_weights(cfg, 91)
-    tok = make_tokens(cfg.vocab, 6, 40, "uniform", 92)
+    tok = make_tokens(cfg.vocab, B, 40, "uniform", 92)
     runs = [gpu_replay(cfg, w, tok, dev, path=2) for _ in range(2)]
     assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1])
     S_ref, Z_ref = oracle_replay(cfg, w, tok)
