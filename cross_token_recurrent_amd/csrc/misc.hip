@@ -137,6 +137,31 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_v_k(const float* __restrict_
   }
 }
 
+// The same for D = 64 and 128: D/4 lanes per row (4 or 2 rows per wave), one float4 each.
+// Rows past the end are read clamped so that every lane of a group joins the sum.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rmsnorm_rows_s_k(const float* __restrict__ x, const float* __restrict__ gain,
+                                                        T* __restrict__ out, int rows, float eps,
+                                                        T* __restrict__ e_store, int n, int b0, int t0, int Tmax) {
+  constexpr int G = D / 4;
+  constexpr int RPW = 64 / G;
+  const int row = (blockIdx.x * 4 + static_cast<int>(threadIdx.x) / 64) * RPW + (threadIdx.x % 64) / G;
+  const int l = threadIdx.x % G;
+  const int r = min(row, rows - 1);
+  const float4 v = reinterpret_cast<const float4*>(x + static_cast<size_t>(r) * D)[l];
+  float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  ss = group_sum<G>(ss);
+  if (row >= rows) return;
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+  const float4 g = reinterpret_cast<const float4*>(gain)[l];
+  const float a = g.x * (v.x * inv), b = g.y * (v.y * inv), c = g.z * (v.z * inv), d = g.w * (v.w * inv);
+  store4<T>(out + static_cast<size_t>(row) * D + 4 * l, a, b, c, d);
+  if (e_store) {
+    const int bb = b0 + row / n, t = t0 + row % n;
+    store4<T>(e_store + (static_cast<size_t>(bb) * Tmax + t) * D + 4 * l, a, b, c, d);
+  }
+}
+
 // fp32 [B, n, D] <-> stored layout.  heads_layout 0: [B][T][D]; 1: [B][H][T][dh].
 template <typename T>
 __global__ void store_tokens_k(float* __restrict__ flat, T* __restrict__ dev, int B, int n, int D, int t0, int Tmax,
@@ -230,6 +255,22 @@ hipError_t launch_rmsnorm_rows(const float* x, const float* gain, void* out, int
                                       n, b0, t0, Tmax, st);
     return launch_rmsnorm_v<float>(x, gain, static_cast<float*>(out), rows, D, eps, static_cast<float*>(e_store), n,
                                    b0, t0, Tmax, st);
+  }
+  if (D == 64 || D == 128) {
+    const int per_block = 4 * (64 / (D / 4));   // rows per 256-thread block
+    const int gs = (rows + per_block - 1) / per_block;
+    if (dtype == RLT_DTYPE_BF16) {
+      bf16_t* o = static_cast<bf16_t*>(out);
+      bf16_t* es = static_cast<bf16_t*>(e_store);
+      if (D == 64) rmsnorm_rows_s_k<bf16_t, 64><<<gs, 256, 0, st>>>(x, gain, o, rows, eps, es, n, b0, t0, Tmax);
+      else rmsnorm_rows_s_k<bf16_t, 128><<<gs, 256, 0, st>>>(x, gain, o, rows, eps, es, n, b0, t0, Tmax);
+    } else {
+      float* o = static_cast<float*>(out);
+      float* es = static_cast<float*>(e_store);
+      if (D == 64) rmsnorm_rows_s_k<float, 64><<<gs, 256, 0, st>>>(x, gain, o, rows, eps, es, n, b0, t0, Tmax);
+      else rmsnorm_rows_s_k<float, 128><<<gs, 256, 0, st>>>(x, gain, o, rows, eps, es, n, b0, t0, Tmax);
+    }
+    return hipGetLastError();
   }
   const int g = (rows + 3) / 4;
   if (dtype == RLT_DTYPE_BF16)
