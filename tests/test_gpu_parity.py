@@ -10,6 +10,7 @@ import pytest
 import oracle
 from gpu_helpers import check, oracle_replay
 from workloads import CONFIGS, ModelConfig, make_tokens, make_weights, perturb_untied
+from workloads.synth import bf16_round
 
 torch = pytest.importorskip("torch")
 import cross_token_recurrent_amd as rlt  # noqa: E402
@@ -108,8 +109,12 @@ def test_decoder_with_injected_encoder_outputs(dev, dtype):
     S = torch.empty(B, T, cfg.d_model, dtype=torch.float32, device=dev)
     rlt.rlt_decoder_replay(model, state, T, S)
     torch.cuda.synchronize()
-    # oracle decoder on the same (stored-precision) encoder outputs
-    e_st, mk_st, mv_st = (x.cpu().numpy().astype(np.float64) for x in rlt.rlt_state_read_encoder_outputs(model, state, 0, T))
+    # oracle decoder on the same encoder outputs, rounded on the host to what the state stores:
+    # float32 as uploaded, then bf16 (round to nearest even) in bf16 mode
+    def stored(a):
+        a32 = a.astype(np.float32)
+        return (bf16_round(a32) if dtype == "bf16" else a32).astype(np.float64)
+    e_st, mk_st, mv_st = stored(e), stored(mk), stored(mv)
     S_ref = []
     for b in range(B):
         st = oracle.init_state(m)
@@ -178,12 +183,13 @@ def test_edge_configs(dev, over, B, T, path):
 # the cross-attention with a 256-thread combine; both sides of that switch against the oracle.
 LONG_MEMORY = [
     (dict(n_heads=1, ffn_dim=64, window=5, mem_groups=2), 2, 4300),                  # head_dim 64, G = L
+    (dict(n_heads=1, ffn_dim=64, window=9, dtype="bf16"), 2, 4100),                  # head_dim 64, bf16
     (dict(n_heads=4, ffn_dim=64, window=9, dtype="bf16"), 2, 4100),                  # head_dim 16, bf16
     (dict(d_model=128, n_heads=1, ffn_dim=64, window=3, dtype="bf16"), 1, 3900),     # head_dim 128, bf16
 ]
 
 
-@pytest.mark.parametrize("over,B,T", LONG_MEMORY, ids=["dh64_fp32", "dh16_bf16", "dh128_bf16"])
+@pytest.mark.parametrize("over,B,T", LONG_MEMORY, ids=["dh64_fp32", "dh64_bf16", "dh16_bf16", "dh128_bf16"])
 def test_batched_long_memory_combine(dev, over, B, T):
     cfg = mcfg(**over)
     w = make_weights(cfg, 91)
