@@ -180,8 +180,8 @@ int pack_weights(const rlt_model& m, const float* w, hipStream_t st) {
       RLT_HIP(launch_pack_frag(ws + from, ws + to, N, K, st), "pack weight fragments");
       return RLT_OK;
     };
-    TRY(frag(L.wgate, L.frag_wgate, D, 2 * D));
-    TRY(frag(L.wfb, L.frag_wfb, D, D));
+    RLT_HIP(launch_pack_merge_frag(src("w_ge"), src("w_gs"), src("w_fb"), ws + L.frag_merge, D, st),
+            "pack merge fragments");
     for (int l = 0; l < L.L; ++l) {
       const size_t src_l = L.layers + l * L.layer_stride, dst_l = L.frag_layers + l * L.layer_stride;
       TRY(frag(src_l + L.l_qkv, dst_l + L.l_qkv, 3 * D, D));
@@ -217,6 +217,9 @@ int reset_state(const rlt_model* m, rlt_state* s, hipStream_t st) {
   if (S.ring_v > S.ring_k) {
     RLT_HIP(launch_zero(s->buf + S.ring_k, S.e - S.ring_k, st), "reset window caches");
   }
+  size_t cnt_off = 0, cnt_bytes = 0;
+  dec_batched_counters(m->lay, S.B, S.T, &cnt_off, &cnt_bytes);
+  if (cnt_bytes) RLT_HIP(launch_zero(s->buf + S.dec_scratch + cnt_off, cnt_bytes, st), "reset decoder counters");
   s->version = m->version;
   s->t_enc = 0;
   s->t_dec = 0;
@@ -282,10 +285,9 @@ bool compute_model_layout(const rlt_config& c, ModelLayout* m) {
   L.has_frag = L.dtype == RLT_DTYPE_BF16 && L.D >= 256 ? 1 : 0;
   if (L.has_frag) {
     L.frag_layers = take(L.L * L.layer_stride);
-    L.frag_wgate = take(2 * D * D * e);
-    L.frag_wfb = take(D * D * e);
+    L.frag_merge = take(4 * D * D * e);
   } else {
-    L.frag_layers = L.frag_wgate = L.frag_wfb = 0;
+    L.frag_layers = L.frag_merge = 0;
   }
   L.has_wout_frag = score_frag_eligible(L.dtype, L.D) ? 1 : 0;
   L.wout_frag = L.has_wout_frag ? take((V + 15) / 16 * 16 * D * 2) : 0;
@@ -830,7 +832,8 @@ int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, floa
     a.n = n;
     RLT_HIP(launch_dec_small(M, S, a, st), "decoder replay (persistent)");
   } else if (path == RLT_PATH_BATCHED) {
-    RLT_HIP(run_dec_batched(M, S, model->ws, state->buf, s_out, state->t_dec, n, st), "decoder replay (batched)");
+    RLT_HIP(run_dec_batched(M, S, model->ws, state->buf, state->buf + S.dec_scratch, s_out, state->t_dec, n, st),
+            "decoder replay (batched)");
   } else {
     return fail(RLT_ERR_UNSUPPORTED, "no decoder implementation for this configuration");
   }

@@ -30,16 +30,40 @@ namespace {
 
 constexpr int KCHUNK = 256;   // memory rows per cross-attention work item
 constexpr int kWideCombineSplits = 16;   // splits from which the 256-thread combine is faster
-// The weight-streaming product re-reads the block's B activation rows once per 64 output
-// columns, B/64 of the weight bytes it streams.  It is used where K > N, and for every shape
-// when B <= 16 (a quarter of the weight bytes or less): at B = 16 a 48-layer step drops from
-// 5.4 to 4.5 ms, while at B = 64 the tiled products stay faster for N >= K.
-constexpr int kWsAllShapesMaxB = 16;
+// Whether the step runs on the weight-streaming products (wstream.hip) or the tiled ones.
+bool use_wst(const ModelLayout& m, int B) {
+  return m.has_frag && m.dtype == RLT_DTYPE_BF16 && B <= 64 && m.D <= 2048;
+}
 
 struct Scratch {
-  size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, total;
+  size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, ssp, cnt, wpart, total;
+  size_t cnt_bytes;
   int nsmax;
 };
+
+// Row blocks per workgroup and K split of a weight-streaming product over B rows.
+struct WstPlan {
+  int mb, S;
+};
+// One 16-row block per workgroup: the row groups of a tile re-read its weights from L2, which
+// is cheaper than splitting K (the split's partial round trip); K is split only past 2048.
+WstPlan wst_plan(int B, int N, int K) {
+  (void)B;
+  (void)N;
+  return {1, wst_choose_split(1, K)};
+}
+
+// Largest split-K partial buffer and counter array any weight-streaming product of the step needs.
+void wst_scratch_max(const ModelLayout& m, int B, size_t* part_floats, size_t* counters) {
+  const int D = m.D;
+  const int shapes[5][2] = {{2 * D, 2 * D}, {3 * D, D}, {D, D}, {m.F2, D}, {D, m.F}};
+  *part_floats = *counters = 0;
+  for (const auto& nk : shapes) {
+    const WstPlan p = wst_plan(B, nk[0], nk[1]);
+    *part_floats = std::max(*part_floats, wst_part_floats(B, p.mb, nk[0], p.S));
+    *counters = std::max(*counters, wst_counters(B, p.mb, nk[0]));
+  }
+}
 
 Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   Scratch s{};
@@ -60,9 +84,15 @@ Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   s.attn = take(Bz * D * e);
   s.act = take(Bz * static_cast<size_t>(m.F) * e);
   s.part = take(Bz * m.H * static_cast<size_t>(s.nsmax) * (m.DH + 2) * 4);
-  // split-K partials: of the d-wide products, and of every product on the weight-streaming path
-  const size_t wsf = m.has_frag && B <= 64 ? wsgemm_ws_floats(B, std::max(m.D * 3, m.F2), m.D) : 0;
-  s.splitk = take(std::max(gemm_splitk_ws_floats(B, m.D), wsf) * 4);
+  s.splitk = take(gemm_splitk_ws_floats(B, m.D) * 4);
+  // weight-streaming products: per-tile row sums of squares, arrival counters, partials
+  const bool w = use_wst(m, B);
+  size_t part_floats = 0, counters = 0;
+  if (w) wst_scratch_max(m, B, &part_floats, &counters);
+  s.ssp = take(w ? 2 * D * 4 : 0);
+  s.cnt_bytes = counters * 4;
+  s.cnt = take(s.cnt_bytes);
+  s.wpart = take(part_floats * 4);
   s.total = off;
   return s;
 }
@@ -285,6 +315,144 @@ __global__ __launch_bounds__(64 * SWA_WAVES) void swa_k(const float* __restrict_
   }
 }
 
+// Window self-attention, two-pass: one workgroup per (head, sequence), wave w takes window
+// entries [KW w, KW w + KW).  Every key and value row of the wave's entries is requested at
+// once (lanes = (slot, 16-dim part), so one load instruction covers SLOTS whole rows), then
+// scores -> workgroup max -> exp(s - M) -> P.V over the same registers; the lanes' partial sums
+// are folded over slots with lane exchanges, and the waves' sums in wave order, so the result
+// does not depend on timing.  Entries past the window are loaded clamped and masked.
+template <typename WT> struct SwaKw { static constexpr int v(int DH) { return DH == 128 ? 32 : 64; } };
+template <> struct SwaKw<float> { static constexpr int v(int DH) { return DH >= 64 ? 32 : 64; } };
+
+// 16 stored elements of a row as loaded (two 16-byte pieces for bf16, four for fp32), converted
+// to fp32 where they are used, so the registers hold the storage precision.
+template <typename WT> struct Raw16 {
+  static constexpr int N = 16 * sizeof(WT) / 16;
+  uint4 v[N];
+  __device__ __forceinline__ void load(const WT* p) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = reinterpret_cast<const uint4*>(p)[i];
+  }
+  __device__ __forceinline__ float get(int c) const {
+    if constexpr (sizeof(WT) == 2) {
+      const uint4 q = v[c / 8];
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+      const uint32_t x = w[(c % 8) / 2];
+      return __uint_as_float(c % 2 ? (x & 0xffff0000u) : (x << 16));
+    } else {
+      const uint4 q = v[c / 4];
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+      return __uint_as_float(w[c % 4]);
+    }
+  }
+};
+
+template <typename WT, int DH>
+__global__ __launch_bounds__(512) void swa2_k(const float* __restrict__ qkv, WT* __restrict__ ring_k,
+                                               WT* __restrict__ ring_v, WT* __restrict__ attn, int H, int Wm1, int t,
+                                               float scale) {
+  constexpr int LPK = DH / 16;              // lanes per key row (16 dims each)
+  constexpr int SLOTS = 64 / LPK;           // rows per load instruction
+  constexpr int KW = SwaKw<WT>::v(DH);      // entries per wave
+  constexpr int KPL = KW / SLOTS;           // entries per lane
+  __shared__ float wmax[8], pl[8], po[8][DH];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int nw = blockDim.x / 64, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int slot = lane / LPK, sub = lane % LPK;
+  const int D = H * DH;
+  const int npast = min(t, Wm1), ne = npast + 1;
+  const int slot0 = Wm1 > 0 ? (t - npast) % Wm1 : 0;
+  const size_t rbase = ((static_cast<size_t>(b) * H + h) * Wm1) * DH;   // ring is pre-offset to layer l
+  const float* cur = qkv + static_cast<size_t>(b) * 3 * D + D + h * DH + sub * 16;
+  // 1. all key and value rows of this lane's entries
+  Raw16<WT> kr[KPL], vr[KPL];
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const int i = wave * KW + u * SLOTS + slot;
+    int sl = slot0 + min(i, max(npast - 1, 0));
+    sl = sl >= Wm1 ? sl - Wm1 : sl;
+    if (npast > 0) {
+      kr[u].load(ring_k + rbase + static_cast<size_t>(sl) * DH + sub * 16);
+      vr[u].load(ring_v + rbase + static_cast<size_t>(sl) * DH + sub * 16);
+    } else {   // an empty ring (first position, or W = 1): only the current entry is read
+#pragma unroll
+      for (int j = 0; j < Raw16<WT>::N; ++j) kr[u].v[j] = vr[u].v[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  float q[16], kc[16], vc[16];
+  {
+    const float* qr = qkv + static_cast<size_t>(b) * 3 * D + h * DH + sub * 16;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      q[c] = qr[c] * scale;
+      kc[c] = round_to<WT>(cur[c]);          // the current entry in the ring's storage precision
+      vc[c] = round_to<WT>(cur[D + c]);
+    }
+  }
+  // 2. scores (entry npast is the current one; entries >= ne are masked)
+  float sc[KPL];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const int i = wave * KW + u * SLOTS + slot;
+    const bool is_cur = i == npast;
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) a += q[c] * (is_cur ? kc[c] : kr[u].get(c));
+    a = group_sum<LPK>(a);
+    sc[u] = i < ne ? a : -INFINITY;
+    mloc = fmaxf(mloc, sc[u]);
+  }
+  mloc = group_max<64>(mloc);
+  if (lane == 0) wmax[wave] = mloc;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int w = 0; w < nw; ++w) M = fmaxf(M, wmax[w]);   // finite: entry 0 is in wave 0
+  // 3. P.V over the lane's entries, then folded over the slots (lanes with the same part)
+  float o[16], l = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) o[c] = 0.f;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const int i = wave * KW + u * SLOTS + slot;
+    const bool is_cur = i == npast;
+    const float p = __expf(sc[u] - M);   // masked entries: exp(-inf) = 0
+    l += p;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[c] += p * (is_cur ? vc[c] : vr[u].get(c));
+  }
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    l += __shfl_xor(l, off, 64);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[c] += __shfl_xor(o[c], off, 64);
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) po[wave][sub * 16 + c] = o[c];
+    if (sub == 0) pl[wave] = l;
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < DH; d += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      num += po[w][d];
+      den += pl[w];
+    }
+    store_from_f32(&attn[static_cast<size_t>(b) * D + h * DH + d], num / den);
+  }
+  // 4. the current entry replaces the oldest one (position t - (W-1)); every read of the ring
+  //    happened before the barrier above
+  if (Wm1 > 0) {
+    const int sl = t % Wm1;
+    const float* kr = qkv + static_cast<size_t>(b) * 3 * D + D + h * DH;
+    for (int d = threadIdx.x; d < DH; d += blockDim.x) {
+      store_from_f32(&ring_k[rbase + static_cast<size_t>(sl) * DH + d], kr[d]);
+      store_from_f32(&ring_v[rbase + static_cast<size_t>(sl) * DH + d], kr[D + d]);
+    }
+  }
+}
+
 // Cross-attention partial states: one wave per (key chunk, head, sequence).
 // Scores with lanes over keys (LPK lanes per key row), then exp(s - M) for the chunk in
 // LDS, then P.V with lanes over (dim, 8-key block) reading the key-blocked value layout.
@@ -453,7 +621,11 @@ hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratc
     WT* rk = reinterpret_cast<WT*>(state + S.ring_k) + lay;
     WT* rv = reinterpret_cast<WT*>(state + S.ring_v) + lay;
     WT* out = reinterpret_cast<WT*>(base + sc.attn);
-    if (B * H >= 2048)
+    constexpr int KW = SwaKw<WT>::v(DH);
+    const int nw = (S.Wm1 + 1 + KW - 1) / KW;
+    if (nw <= 8)
+      swa2_k<WT, DH><<<dim3(H, B), 64 * nw, 0, st>>>(q, rk, rv, out, H, S.Wm1, t, scale);
+    else if (B * H >= 2048)
       swa_k<WT, DH, 1><<<dim3(H, B), 64, 0, st>>>(q, rk, rv, out, B, H, S.Wm1, t, scale);
     else
       swa_k<WT, DH, 4><<<dim3(H, B), 256, 0, st>>>(q, rk, rv, out, B, H, S.Wm1, t, scale);
@@ -491,39 +663,23 @@ hipError_t attention(bool self, const ModelLayout& m, const Scratch& sc, char* b
   }
 }
 
+#define RLT_CK(x)                  \
+  do {                             \
+    hipError_t e_ = (x);           \
+    if (e_ != hipSuccess) return e_; \
+  } while (0)
+
+// One step on the tiled products (fp32 models, models without fragment-major copies, B > 64).
 template <typename WT>
-hipError_t run_t(const ModelLayout& m, const StateLayout& S, const char* ws, char* state, float* s_out, int t0, int n,
-                 hipStream_t st) {
-  const Scratch sc = scratch_layout(m, S.B, S.T);
-  char* base = state + S.dec_scratch;
+hipError_t step_tiled(const ModelLayout& m, const StateLayout& S, const Scratch& sc, const char* ws, char* state,
+                      char* base, float* s_out, int t, int step, int n, hipStream_t st) {
   const int B = S.B, D = m.D, dt = m.dtype;
   float* y = reinterpret_cast<float*>(base + sc.y);
   float* s = reinterpret_cast<float*>(state + S.s);
   const float* gains_self = reinterpret_cast<const float*>(ws + m.g_dec_self);
   const float* gains_cross = reinterpret_cast<const float*>(ws + m.g_dec_cross);
   const float* gains_ffn = reinterpret_cast<const float*>(ws + m.g_dec_ffn);
-  hipError_t e;
-#define RLT_CK(x)                        \
-  do {                                   \
-    e = (x);                             \
-    if (e != hipSuccess) return e;       \
-  } while (0)
-  // decode-sized batches stream the weights of the long-K products (FFN output, merge) from
-  // their fragment-major copies; where N >= K the tiled product is as fast (the activation
-  // slice every 64-column tile reloads costs as much as the weights it saves)
-  const bool stream_w = m.has_frag && B <= 64 && dt == RLT_DTYPE_BF16;
-  const size_t frag_shift = m.frag_layers - m.layers;   // same block layout
   auto gemm = [&](const void* A, int lda, const void* W, int N, int K, void* out, int ldo, int epi) {
-    if (stream_w && (K > N || B <= kWsAllShapesMaxB) && wsgemm_supported(B, N, K)) {
-      const char* wp = static_cast<const char*>(W);
-      const char* wf = wp == ws + m.wgate ? ws + m.frag_wgate
-                     : wp == ws + m.wfb   ? ws + m.frag_wfb
-                                          : wp + frag_shift;
-      return launch_wsgemm(A, lda, wf, B, N, K, out, ldo, epi, reinterpret_cast<float*>(base + sc.splitk),
-                           std::max(gemm_splitk_ws_floats(B, D),
-                                    wsgemm_ws_floats(B, std::max(m.D * 3, m.F2), m.D)),
-                           st);
-    }
     GemmArgs g{};
     g.A = A; g.W = W; g.out = out;
     g.M = B; g.N = N; g.K = K; g.lda = lda; g.ldw = K; g.ldo = ldo; g.epi = epi;
@@ -532,48 +688,124 @@ hipError_t run_t(const ModelLayout& m, const StateLayout& S, const char* ws, cha
     return launch_gemm(g, dt, st);
   };
   const int nt = std::min(256, std::max(64, D / 4));
+  // gated merge
+  merge_prep_k<WT><<<B, nt, 0, st>>>(reinterpret_cast<const WT*>(state + S.e), s,
+                                     reinterpret_cast<WT*>(base + sc.xin), S.T, D, t);
+  RLT_CK(hipGetLastError());
+  RLT_CK(gemm(base + sc.xin, 2 * D, ws + m.wgate, D, 2 * D, base + sc.gpre, D, EPI_STORE_F32));
+  RLT_CK(gemm(base + sc.xin + static_cast<size_t>(D) * m.esz, 2 * D, ws + m.wfb, D, D, base + sc.fb, D,
+              EPI_STORE_F32));
+  merge_combine_k<WT><<<B, nt, 0, st>>>(reinterpret_cast<const float*>(base + sc.gpre),
+                                        reinterpret_cast<const float*>(base + sc.fb),
+                                        reinterpret_cast<const float*>(ws + m.bg),
+                                        reinterpret_cast<const WT*>(base + sc.xin), y, D);
+  RLT_CK(hipGetLastError());
+  for (int l = 0; l < m.L; ++l) {
+    const char* lw = ws + m.layers + l * m.layer_stride;
+    // window self-attention
+    RLT_CK(launch_rmsnorm_rows(y, gains_self + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr,
+                               1, 0, 0, 1, st));
+    RLT_CK(gemm(base + sc.h, D, lw + m.l_qkv, 3 * D, D, base + sc.qkv, 3 * D, EPI_STORE_F32));
+    RLT_CK(attention<WT>(true, m, sc, base, state, S, l, t, st));
+    RLT_CK(gemm(base + sc.attn, D, lw + m.l_wo, D, D, y, D, EPI_RESID_F32));
+    // cross-attention to memory entries 0..t
+    RLT_CK(launch_rmsnorm_rows(y, gains_cross + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr,
+                               1, 0, 0, 1, st));
+    RLT_CK(gemm(base + sc.h, D, lw + m.l_wqx, D, D, base + sc.qkv, D, EPI_STORE_F32));
+    RLT_CK(attention<WT>(false, m, sc, base, state, S, l, t, st));
+    RLT_CK(gemm(base + sc.attn, D, lw + m.l_wox, D, D, y, D, EPI_RESID_F32));
+    // FFN
+    RLT_CK(launch_rmsnorm_rows(y, gains_ffn + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr, 1,
+                               0, 0, 1, st));
+    RLT_CK(gemm(base + sc.h, D, lw + m.l_fin, m.F2, D, base + sc.act, m.F,
+                m.ffn_kind == RLT_FFN_GELU ? EPI_GELU : EPI_SWIGLU));
+    RLT_CK(gemm(base + sc.act, m.F, lw + m.l_fout, D, m.F, y, D, EPI_RESID_F32));
+  }
+  final_norm_k<<<(B + 3) / 4, 256, 0, st>>>(y, reinterpret_cast<const float*>(ws + m.g_dec_final), s, s_out, B, D,
+                                           m.eps, step, n);
+  return hipGetLastError();
+}
+
+// One step on the weight-streaming products: each norm is folded into the residual product
+// before it (bf16(g * y) and per-tile sums of squares) and the product after it (rows scaled by
+// 1 / rms), the split-K partials are added by each tile's last workgroup, and the merge is one
+// product over [e_t ; s_{t-1}].
+hipError_t step_wst(const ModelLayout& m, const StateLayout& S, const Scratch& sc, const char* ws, char* state,
+                    char* base, float* s_out, int t, int step, int n, hipStream_t st) {
+  const int B = S.B, D = m.D;
+  float* y = reinterpret_cast<float*>(base + sc.y);
+  float* ssp = reinterpret_cast<float*>(base + sc.ssp);
+  uint16_t* xb = reinterpret_cast<uint16_t*>(base + sc.h);
+  const char* frag = ws + m.frag_layers;
+  auto prod = [&](int in, int epi, const void* x, int ldx, int nt_in, const char* wf, int N, int K, float* outf,
+                  uint16_t* outb, int ldo, const float* gain_next) {
+    WstArgs a{};
+    a.in = in; a.epi = epi;
+    a.x = x; a.ldx = ldx; a.ssp = ssp; a.nt_in = nt_in; a.eps = m.eps;
+    a.e = reinterpret_cast<const uint16_t*>(state + S.e);
+    a.s = reinterpret_cast<const float*>(state + S.s);
+    a.T = S.T; a.t = t; a.D = D;
+    a.wf = reinterpret_cast<const uint4*>(wf);
+    a.M = B; a.N = N; a.K = K;
+    const WstPlan plan = wst_plan(B, N, K);
+    a.mb = plan.mb;
+    a.S = plan.S;
+    a.KS = K / a.S;
+    a.outf = outf; a.outb = outb; a.ldo = ldo;
+    a.ssp_out = ssp;
+    a.gain_next = gain_next;
+    a.xb_out = xb;
+    a.bias = reinterpret_cast<const float*>(ws + m.bg);
+    a.part = reinterpret_cast<float*>(base + sc.wpart);
+    a.cnt = reinterpret_cast<int*>(base + sc.cnt);
+    return launch_wst(a, st);
+  };
+  const float* gains_self = reinterpret_cast<const float*>(ws + m.g_dec_self);
+  const float* gains_cross = reinterpret_cast<const float*>(ws + m.g_dec_cross);
+  const float* gains_ffn = reinterpret_cast<const float*>(ws + m.g_dec_ffn);
+  float* qkv = reinterpret_cast<float*>(base + sc.qkv);
+  uint16_t* attn = reinterpret_cast<uint16_t*>(base + sc.attn);
+  uint16_t* act = reinterpret_cast<uint16_t*>(base + sc.act);
+  // gated merge: y, bf16(g_self^0 * y) and the sums of squares of its 32-column tiles
+  RLT_CK(prod(WIN_MERGE, WEPI_MERGE, nullptr, 0, 0, ws + m.frag_merge, 2 * D, 2 * D, y, nullptr, D, gains_self));
+  int nt = 2 * D / 64;
+  for (int l = 0; l < m.L; ++l) {
+    const char* lw = frag + l * m.layer_stride;
+    const size_t go = static_cast<size_t>(l) * D;
+    const float* next_self = l + 1 < m.L ? gains_self + go + D : nullptr;
+    RLT_CK(prod(WIN_BF16, WEPI_F32, xb, D, nt, lw + m.l_qkv, 3 * D, D, qkv, nullptr, 3 * D, nullptr));
+    RLT_CK(attention<bf16_t>(true, m, sc, base, state, S, l, t, st));
+    RLT_CK(prod(WIN_BF16, WEPI_RESID, attn, D, 0, lw + m.l_wo, D, D, y, nullptr, D, gains_cross + go));
+    nt = D / 64;
+    RLT_CK(prod(WIN_BF16, WEPI_F32, xb, D, nt, lw + m.l_wqx, D, D, qkv, nullptr, D, nullptr));
+    RLT_CK(attention<bf16_t>(false, m, sc, base, state, S, l, t, st));
+    RLT_CK(prod(WIN_BF16, WEPI_RESID, attn, D, 0, lw + m.l_wox, D, D, y, nullptr, D, gains_ffn + go));
+    RLT_CK(prod(WIN_BF16, m.ffn_kind == RLT_FFN_GELU ? WEPI_GELU : WEPI_SWIGLU, xb, D, nt, lw + m.l_fin, m.F2, D,
+                nullptr, act, m.F, nullptr));
+    RLT_CK(prod(WIN_BF16, WEPI_RESID, act, m.F, 0, lw + m.l_fout, D, m.F, y, nullptr, D, next_self));
+  }
+  return launch_final_norm_ssp(y, ssp, nt, reinterpret_cast<const float*>(ws + m.g_dec_final),
+                               reinterpret_cast<float*>(state + S.s), s_out, B, D, m.eps, step, n, st);
+}
+
+template <typename WT>
+hipError_t run_t(const ModelLayout& m, const StateLayout& S, const char* ws, char* state, char* base, float* s_out,
+                 int t0, int n, hipStream_t st) {
+  const Scratch sc = scratch_layout(m, S.B, S.T);
+  const bool w = use_wst(m, S.B);
   for (int step = 0; step < n; ++step) {
     const int t = t0 + step;
-    // gated merge
-    merge_prep_k<WT><<<B, nt, 0, st>>>(reinterpret_cast<const WT*>(state + S.e), s,
-                                       reinterpret_cast<WT*>(base + sc.xin), S.T, D, t);
-    RLT_CK(hipGetLastError());
-    RLT_CK(gemm(base + sc.xin, 2 * D, ws + m.wgate, D, 2 * D, base + sc.gpre, D, EPI_STORE_F32));
-    RLT_CK(gemm(base + sc.xin + static_cast<size_t>(D) * m.esz, 2 * D, ws + m.wfb, D, D, base + sc.fb, D,
-                EPI_STORE_F32));
-    merge_combine_k<WT><<<B, nt, 0, st>>>(reinterpret_cast<const float*>(base + sc.gpre),
-                                          reinterpret_cast<const float*>(base + sc.fb),
-                                          reinterpret_cast<const float*>(ws + m.bg),
-                                          reinterpret_cast<const WT*>(base + sc.xin), y, D);
-    RLT_CK(hipGetLastError());
-    for (int l = 0; l < m.L; ++l) {
-      const char* lw = ws + m.layers + l * m.layer_stride;
-      // window self-attention
-      RLT_CK(launch_rmsnorm_rows(y, gains_self + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr,
-                                 1, 0, 0, 1, st));
-      RLT_CK(gemm(base + sc.h, D, lw + m.l_qkv, 3 * D, D, base + sc.qkv, 3 * D, EPI_STORE_F32));
-      RLT_CK(attention<WT>(true, m, sc, base, state, S, l, t, st));
-      RLT_CK(gemm(base + sc.attn, D, lw + m.l_wo, D, D, y, D, EPI_RESID_F32));
-      // cross-attention to memory entries 0..t
-      RLT_CK(launch_rmsnorm_rows(y, gains_cross + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr,
-                                 1, 0, 0, 1, st));
-      RLT_CK(gemm(base + sc.h, D, lw + m.l_wqx, D, D, base + sc.qkv, D, EPI_STORE_F32));
-      RLT_CK(attention<WT>(false, m, sc, base, state, S, l, t, st));
-      RLT_CK(gemm(base + sc.attn, D, lw + m.l_wox, D, D, y, D, EPI_RESID_F32));
-      // FFN
-      RLT_CK(launch_rmsnorm_rows(y, gains_ffn + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr, 1,
-                                 0, 0, 1, st));
-      RLT_CK(gemm(base + sc.h, D, lw + m.l_fin, m.F2, D, base + sc.act, m.F,
-                  m.ffn_kind == RLT_FFN_GELU ? EPI_GELU : EPI_SWIGLU));
-      RLT_CK(gemm(base + sc.act, m.F, lw + m.l_fout, D, m.F, y, D, EPI_RESID_F32));
+    if constexpr (sizeof(WT) == 2) {
+      if (w) {
+        RLT_CK(step_wst(m, S, sc, ws, state, base, s_out, t, step, n, st));
+        continue;
+      }
     }
-    final_norm_k<<<(B + 3) / 4, 256, 0, st>>>(y, reinterpret_cast<const float*>(ws + m.g_dec_final), s, s_out, B, D,
-                                             m.eps, step, n);
-    RLT_CK(hipGetLastError());
+    RLT_CK(step_tiled<WT>(m, S, sc, ws, state, base, s_out, t, step, n, st));
   }
-#undef RLT_CK
   return hipSuccess;
 }
+#undef RLT_CK
 
 }  // namespace
 
@@ -583,11 +815,17 @@ bool dec_batched_supported(const ModelLayout& m) {
 
 size_t dec_batched_scratch_bytes(const ModelLayout& m, int B, int T) { return scratch_layout(m, B, T).total; }
 
-hipError_t run_dec_batched(const ModelLayout& m, const StateLayout& s, const char* ws, char* state, float* s_out,
-                           int t0, int n, hipStream_t st) {
+void dec_batched_counters(const ModelLayout& m, int B, int T, size_t* offset, size_t* bytes) {
+  const Scratch sc = scratch_layout(m, B, T);
+  *offset = sc.cnt;
+  *bytes = sc.cnt_bytes;
+}
+
+hipError_t run_dec_batched(const ModelLayout& m, const StateLayout& s, const char* ws, char* state, char* scratch,
+                           float* s_out, int t0, int n, hipStream_t st) {
   if (!dec_batched_supported(m)) return hipErrorInvalidValue;
-  return m.dtype == RLT_DTYPE_BF16 ? run_t<bf16_t>(m, s, ws, state, s_out, t0, n, st)
-                                   : run_t<float>(m, s, ws, state, s_out, t0, n, st);
+  return m.dtype == RLT_DTYPE_BF16 ? run_t<bf16_t>(m, s, ws, state, scratch, s_out, t0, n, st)
+                                   : run_t<float>(m, s, ws, state, scratch, s_out, t0, n, st);
 }
 
 }  // namespace rlt

@@ -44,9 +44,10 @@ struct ModelLayout {
   size_t wout_frag;
   // fragment-major copies of the decoder's in-loop weights for the weight-streaming products
   // (bf16, d >= 256): the same per-layer block layout as `layers` at frag_layers, and the
-  // merge matrices at frag_wgate / frag_wfb
+  // merge matrix [2D][2D] (gate rows [W_ge | W_gs] and feedback rows [0 | W_fb] interleaved in
+  // blocks of 16) at frag_merge
   int has_frag;
-  size_t frag_layers, frag_wgate, frag_wfb;
+  size_t frag_layers, frag_merge;
   size_t total;
 };
 
@@ -133,15 +134,51 @@ struct GemmArgs {
 };
 // Workspace floats split-K needs for an M x N product (the most launch_gemm will use).
 size_t gemm_splitk_ws_floats(int M, int N);
-// Weight-streaming product for decode-sized batches: out (epilogue epi: EPI_STORE_F32,
-// EPI_RESID_F32, EPI_GELU, EPI_SWIGLU) = A[M, K] (bf16, lda) * W^T, W given by its
-// fragment-major copy; ws holds the K-split partials (wsgemm_ws_floats(M, N, K) floats).
-bool wsgemm_supported(int M, int N, int K);
-size_t wsgemm_ws_floats(int M, int N, int K);
-hipError_t launch_wsgemm(const void* A, int lda, const void* wfrag, int M, int N, int K, void* out, int ldo, int epi,
-                         float* ws, size_t ws_floats, hipStream_t st);
 // Fragment-major copy of a packed bf16 [N][K] matrix (N % 16 == 0, K % 64 == 0).
 hipError_t launch_pack_frag(const void* w, void* dst, int N, int K, hipStream_t st);
+
+// Weight-streaming products of the decoder step for M <= 64 rows (bf16, wstream.hip):
+// Y[M, N] = X[M, K] W^T with W from its fragment-major copy, K split over S workgroups per
+// 64-column tile, the partials added in slice order by the tile's last workgroup.  RMSNorm is
+// folded in: a residual product also writes xb = bf16(g_next * y) and per-tile row sums of
+// squares; the next product reads xb and scales its rows by 1 / rms(y).
+enum WstIn { WIN_BF16 = 0, WIN_MERGE = 2 };
+enum WstEpi { WEPI_F32 = 0, WEPI_RESID = 1, WEPI_GELU = 2, WEPI_SWIGLU = 3, WEPI_MERGE = 4 };
+struct WstArgs {
+  int in, epi;
+  const void* x;            // WIN_BF16: bf16 [M][ldx]
+  int ldx;
+  const float* ssp;         // WEPI_F32 / GELU / SWIGLU: per-tile row sums of squares of y, [nt_in][64]
+  int nt_in;
+  float eps;
+  const uint16_t* e;        // WIN_MERGE / WEPI_MERGE: e of the state, bf16 [M][T][D], row t
+  const float* s;           // WIN_MERGE: s_{t-1} fp32 [M][D]
+  int T, t, D;
+  const uint4* wf;          // fragment-major W [N][K]
+  int M, N, K, KS, S;       // KS = K / S: a power-of-two multiple of 64
+  int mb;                   // 16-row blocks per workgroup (1, 2, 4); ceil(M / (16 mb)) row groups
+  float* outf;              // WEPI_F32 output, WEPI_RESID / WEPI_MERGE residual y (fp32, ldo)
+  uint16_t* outb;           // WEPI_GELU / WEPI_SWIGLU activation (bf16, ldo)
+  int ldo;
+  float* ssp_out;           // WEPI_RESID / WEPI_MERGE: [N/64][64] row sums of squares of the tile
+  const float* gain_next;   // WEPI_RESID (optional) / WEPI_MERGE: gain of the next norm [D]
+  uint16_t* xb_out;         // with gain_next: bf16(gain_next * y) [M][ldo]
+  const float* bias;        // WEPI_MERGE: b_g [D]
+  float* part;              // S > 1: wst_part_floats(M, mb, N, S) floats
+  int* cnt;                 // S > 1: wst_counters(M, mb, N) arrival counters, zero before and after the launch
+};
+bool wst_supported(int M, int N, int K);
+// S for a product with mb 16-row blocks per workgroup: the smallest split whose K slice fits.
+int wst_choose_split(int mb, int K);
+size_t wst_part_floats(int M, int mb, int N, int S);   // split-K partial floats
+size_t wst_counters(int M, int mb, int N);             // arrival counters
+hipError_t launch_wst(const WstArgs& a, hipStream_t st);
+// s = g * y / rms(y) from the per-tile sums of squares (nt tiles); also s_out[b][step] when set.
+hipError_t launch_final_norm_ssp(const float* y, const float* ssp, int nt, const float* gain, float* s, float* s_out,
+                                 int B, int D, float eps, int step, int n, hipStream_t st);
+// Fragment-major bf16 copy of the merge matrix [2D][2D] from the fp32 W_ge, W_gs, W_fb [D][D].
+hipError_t launch_pack_merge_frag(const float* wge, const float* wgs, const float* wfb, void* dst, int D,
+                                  hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t st);
 
 // Action scoring: logp_i = log softmax(W_out s_i / temperature)[a_i] (and the ratio against
@@ -187,10 +224,13 @@ hipError_t launch_store_tokens(const float* src, void* dst, int B, int n, int D,
                                int dtype, int heads_layout, int H, int dh, int to_device_layout,
                                hipStream_t st);
 
-// Batched (large-d) decoder step loop.
+// Batched (large-d) decoder step loop.  `scratch` is the decoder scratch region
+// (dec_batched_scratch_bytes long); its arrival counters (dec_batched_counters, relative to the
+// region) must be zero when a replay starts, and every replay leaves them zero.
 bool dec_batched_supported(const ModelLayout& m);
 size_t dec_batched_scratch_bytes(const ModelLayout& m, int B, int T);
-hipError_t run_dec_batched(const ModelLayout& m, const StateLayout& s, const char* ws, char* state,
+void dec_batched_counters(const ModelLayout& m, int B, int T, size_t* offset, size_t* bytes);
+hipError_t run_dec_batched(const ModelLayout& m, const StateLayout& s, const char* ws, char* state, char* scratch,
                            float* s_out, int t0, int n, hipStream_t st);
 
 }  // namespace rlt
