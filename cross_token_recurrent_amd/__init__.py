@@ -11,6 +11,7 @@ from .rlt import (  # noqa: F401
     make_config,
     replay,
     rlt_decoder_replay,
+    rlt_decoder_replay_noalloc,
     rlt_decoder_step,
     rlt_decoder_step_sample,
     rlt_encoder_forward,

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <new>
 #include <string>
 #include <utility>
@@ -418,6 +419,41 @@ int need_gpu_memory(std::initializer_list<std::pair<const void*, const char*>> a
     int rc = need_gpu_memory(a.first, a.second);
     if (rc) return rc;
   }
+  return RLT_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// Library-owned decoder scratch for rlt_decoder_replay_noalloc: one array per GPU, allocated
+// with the code object when the library loads on that GPU and held until the process ends.  In
+// host code the array's name is only a stand-in; its device address on each GPU comes from
+// hipGetSymbolAddress with that GPU current, looked up once per device.
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+__device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on `device` (looked up once, with that device current).
+int static_scratch(int device, char** out) {
+  if (device < 0 || device >= kMaxDevices) return fail(RLT_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int cur = -1;
+    RLT_HIP(hipGetDevice(&cur), "current device");
+    if (cur != device) RLT_HIP(hipSetDevice(device), "select device");
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != device) RLT_HIP(hipSetDevice(cur), "restore device");
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[device]);
   return RLT_OK;
 }
 
@@ -834,6 +870,52 @@ int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, floa
   } else if (path == RLT_PATH_BATCHED) {
     RLT_HIP(run_dec_batched(M, S, model->ws, state->buf, state->buf + S.dec_scratch, s_out, state->t_dec, n, st),
             "decoder replay (batched)");
+  } else {
+    return fail(RLT_ERR_UNSUPPORTED, "no decoder implementation for this configuration");
+  }
+  state->t_dec += n;
+  return RLT_OK;
+}
+
+int rlt_decoder_replay_noalloc(const rlt_model* model, rlt_state* state, int32_t n, float* s_out, void* stream) {
+  int rc = check_pair(model, state);
+  if (rc) return rc;
+  if (n < 1) return fail(RLT_ERR_INVALID, "n must be >= 1");
+  if (static_cast<int64_t>(state->t_dec) + n > state->t_enc)
+    return fail(RLT_ERR_ORDER, "decoder would run ahead of the encoder (t_dec + n > t_enc)");
+  rc = need_gpu_memory(s_out, "s_out");
+  if (rc) return rc;
+  const ModelLayout& M = model->lay;
+  const StateLayout& S = state->lay;
+  hipStream_t st = as_stream(stream);
+  const int path = choose_path(model, S.T);
+  if (path == RLT_PATH_PERSISTENT) {
+    // the persistent decoder keeps everything in LDS and registers: no scratch at all
+    DecSmallArgs a{};
+    a.ws = model->ws;
+    a.state = state->buf;
+    a.s_out = s_out;
+    a.B = S.B;
+    a.T = S.T;
+    a.t0 = state->t_dec;
+    a.n = n;
+    RLT_HIP(launch_dec_small(M, S, a, st), "decoder replay (persistent)");
+  } else if (path == RLT_PATH_BATCHED) {
+    if (S.dec_scratch_bytes > kStaticScratchBytes)
+      return fail(RLT_ERR_UNSUPPORTED, "the batched decoder needs " + std::to_string(S.dec_scratch_bytes) +
+                                           " bytes of scratch for this batch and t_max; the library's static scratch holds " +
+                                           std::to_string(kStaticScratchBytes));
+    hipPointerAttribute_t attr;
+    RLT_HIP(hipPointerGetAttributes(&attr, state->buf), "state device");
+    char* base = nullptr;
+    rc = static_scratch(attr.device, &base);
+    if (rc) return rc;
+    // the arrival counters of the weight-streaming products start at zero (cleared with a fill
+    // kernel, which graph capture records like any launch)
+    size_t cnt_off = 0, cnt_bytes = 0;
+    dec_batched_counters(M, S.B, S.T, &cnt_off, &cnt_bytes);
+    if (cnt_bytes) RLT_HIP(launch_zero(base + cnt_off, cnt_bytes, st), "clear decoder counters");
+    RLT_HIP(run_dec_batched(M, S, model->ws, state->buf, base, s_out, state->t_dec, n, st), "decoder replay (batched)");
   } else {
     return fail(RLT_ERR_UNSUPPORTED, "no decoder implementation for this configuration");
   }

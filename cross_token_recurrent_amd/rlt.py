@@ -71,6 +71,7 @@ _SIGS = {
     "rlt_state_restore": [_P, _P, _P, ctypes.c_size_t, _P],
     "rlt_encoder_forward": [_P, _P, _P, _I32, _P],
     "rlt_decoder_replay": [_P, _P, _I32, _P, _P],
+    "rlt_decoder_replay_noalloc": [_P, _P, _I32, _P, _P],
     "rlt_decoder_step": [_P, _P, _P, _P, _P, _P],
     "rlt_logits": [_P, _P, ctypes.c_int64, _P, _P],
     "rlt_score_actions": [_P, _P, _P, ctypes.c_int64, ctypes.c_float, _P, _P, _P, _P],
@@ -188,6 +189,13 @@ def rlt_decoder_replay(model: "Model", state: "State", n: int, s_out: Optional[t
     if s_out is not None:
         _tensor(s_out, "s_out", torch.float32, state.device, shape=(state.batch, n, model.d_model))
     _check(load_library().rlt_decoder_replay(model.handle, state.handle, n, _ptr(s_out), _stream(stream)))
+
+
+def rlt_decoder_replay_noalloc(model: "Model", state: "State", n: int, s_out: Optional[torch.Tensor] = None,
+                               stream=None) -> None:
+    if s_out is not None:
+        _tensor(s_out, "s_out", torch.float32, state.device, shape=(state.batch, n, model.d_model))
+    _check(load_library().rlt_decoder_replay_noalloc(model.handle, state.handle, n, _ptr(s_out), _stream(stream)))
 
 
 def rlt_decoder_step(model: "Model", state: "State", tokens: torch.Tensor, s_out: Optional[torch.Tensor] = None,

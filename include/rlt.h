@@ -192,6 +192,20 @@ int rlt_encoder_forward(const rlt_model* model, rlt_state* state, const int32_t*
 int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, float* s_out,
                        void* stream);
 
+/* rlt_decoder_replay_noalloc: rlt_decoder_replay for callers that cannot allocate device
+ * memory at call time (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, ordering rules, errors and results as
+ * rlt_decoder_replay; it allocates nothing (no hipMalloc, no allocating library call).  The
+ * batched decoder's per-step scratch (residual stream, projections, attention partials,
+ * split-K partials and their arrival counters) lives in a library-owned static device array of
+ * 64 MiB, one per GPU, held until the process ends, instead of the state's scratch region.
+ * RLT_ERR_UNSUPPORTED when the batch and t_max need more scratch than that.  Every call on one
+ * GPU shares that GPU's array, which keeps the last call's contents: calls that overlap on one
+ * GPU (two streams, or two threads) race and must be serialised by the caller.  The arrival
+ * counters are cleared by a fill kernel at the start of each call. */
+int rlt_decoder_replay_noalloc(const rlt_model* model, rlt_state* state, int32_t n, float* s_out,
+                               void* stream);
+
 /* rlt_decoder_step: incremental generation ([DS] §2.5): equals
  * rlt_encoder_forward(n = 1) + rlt_decoder_replay(n = 1) + rlt_logits on s_t.
  * tokens: device int32 [B]; s_out: device fp32 [B, d] or NULL; logits: device fp32
