@@ -1,15 +1,18 @@
 """RLT exact-replay benchmark on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic sequences:
-state reset to H_0, causal encoder over all T tokens (e_t and memory M), the
-recurrent decoder over t = 1..T for all B sequences (one persistent launch), and
-logits for every position.  value = B*T / step time (tokens/s), inputs resident in
-HBM before the timed region.
+The headline is the decoder replay of the 48+48-layer reference model (d=2048, SwiGLU 5632,
+W=256, G=1, V=32000, bf16) over B=64 sequences of T=4096 Zipf tokens.  One step = one
+contiguous segment of that replay: --steps K splits t = 1..T into K segments, so the K timed
+steps are together one exact replay from H_0 (the encoder has run over all T tokens before the
+timed region, with the inputs resident in HBM).  value = B*T / (decoder time of the K steps)
+in tokens/s; the roofline is the decoder's algorithmic bytes (weights once per step, window
+cache read + write, memory rows 1..t of every layer, e_t in and s_t out) over that time,
+against 8 TB/s and against the read and copy bandwidth measured on the box in the same run.
 
-    python bench.py [--steps K] [--warmup W] [--config small] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config ref48] [--no-cpu-baseline]
 
-Prints ONE JSON line.  Extra per-phase timings (HIP events on the launch stream)
-and the decoder kernel's roofline figures are included in the same line.
+Prints ONE JSON line.  Further legs in the same line: the small workload on the persistent
+decoder, a 300M-class prefix, RL action scoring, token sampling, prefix snapshots.
 """
 from __future__ import annotations
 
@@ -75,13 +78,14 @@ def copy_kernel(gib: float = 1.0):
 def algorithmic_decoder_bytes(cfg, B: int, T: int) -> float:
     """Bytes the decoder replay must move, summed over t = 1..T for the whole batch.
 
-    Per step: the in-loop weights once (shared by the B sequences), and per sequence
-    the window cache read + write, every layer's read of memory entries 1..t, e_t in
-    and s_t out (fp32, plus the fp32 state)."""
+    Per step: the in-loop weights once (shared by the B sequences: per layer W_Q, W_K, W_V,
+    W_O, W_Qx, W_Ox and the FFN; the merge's W_ge, W_gs, W_fb), and per sequence the window
+    cache read + write, every layer's read of memory entries 1..t, e_t in and s_t out (fp32,
+    plus the fp32 state)."""
     d, L, F, W = cfg.d_model, cfg.n_layers, cfg.ffn_dim, cfg.window
     p = 2 if cfg.dtype == "bf16" else 4
     ffn = (2 if cfg.ffn_kind == "gelu" else 3) * d * F
-    p_loop = L * (6 * d * d + ffn) + 2 * d * d
+    p_loop = L * (6 * d * d + ffn) + 3 * d * d
     total = 0.0
     for t in range(1, T + 1):
         ring = L * 2 * d * p * (min(t - 1, W - 1) + 1)
@@ -99,14 +103,19 @@ def _oracle_one(args):
     return oracle.replay(m, tok, t_limit)
 
 
+def host_cores():
+    """Cores this process may run on, and the BLAS threads numpy uses on them."""
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", "0")) or cores)
+    return cores, threads
+
+
 def cpu_baseline(wl, weights, tokens, budget_s: float = 20.0):
     """The fp64 oracle (test infrastructure) timed on this host's cores over a bounded
-    sample of whole sequences of the same workload."""
+    sample of whole sequences of the same workload, one sequence per worker process."""
     import multiprocessing as mp
 
-    import numpy as np
-
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    cores, _ = host_cores()
     # one probe sequence prefix sizes the sample to about budget_s of CPU work
     t_probe = min(wl.seq_len, 128)
     t0 = time.perf_counter()
@@ -115,16 +124,168 @@ def cpu_baseline(wl, weights, tokens, budget_s: float = 20.0):
     # cost grows ~linearly in t for the memory part; scale by (T/t_probe)^1.5 as an estimate
     est_seq = probe * (wl.seq_len / t_probe) ** 1.5
     n_seq = int(max(1, min(wl.batch, round(budget_s / max(est_seq, 1e-3)))))
-    workers = min(cores, n_seq)
+    workers = min(cores, 16, n_seq)
     jobs = [(wl.model, weights, tokens[b], None) for b in range(n_seq)]
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
     with ctx.Pool(workers) as pool:
         pool.map(_oracle_one, jobs)
     wall = time.perf_counter() - t0
-    return {"value": n_seq * wl.seq_len / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+    return {"value": n_seq * wl.seq_len / wall, "unit": "tokens/s", "cores": cores, "workers": workers,
+            "kind": "oracle",
             "sample": f"{n_seq} of {wl.batch} sequences x T={wl.seq_len} (full replay incl. encoder and logits), "
-                      f"fp64 numpy, one sequence per worker process, {wall:.1f} s wall"}
+                      f"fp64 numpy, one sequence per worker process ({workers} workers on {cores} cores), "
+                      f"{wall:.1f} s wall"}
+
+
+def cpu_baseline_prefix(wl, weights, tokens, budget_s: float = 15.0):
+    """The fp64 oracle on a prefix of one sequence of a workload whose full sequences take the
+    oracle hours: encoder over t_limit tokens, t_limit decoder steps, logits, with t_limit sized
+    by an 8-position probe to about budget_s.  Optimistic as a rate for the whole replay, since
+    late steps read more memory rows."""
+    import oracle
+
+    cores, threads = host_cores()
+    t0 = time.perf_counter()
+    m = oracle.OracleModel.from_config(wl.model, weights)
+    t1 = time.perf_counter()
+    oracle.replay(m, tokens[0], 8)
+    probe = time.perf_counter() - t1
+    t_limit = int(max(8, min(wl.seq_len, 8 * budget_s / max(probe, 1e-3))))
+    t1 = time.perf_counter()
+    oracle.replay(m, tokens[0], t_limit)
+    wall = time.perf_counter() - t1
+    del m
+    return {"value": t_limit / wall, "unit": "tokens/s", "cores": cores, "threads": threads, "kind": "oracle",
+            "sample": f"sequence 0, positions 1..{t_limit} of T={wl.seq_len} (encoder over {t_limit} tokens, "
+                      f"{t_limit} decoder steps, logits), fp64 numpy on {threads} BLAS threads, {wall:.1f} s "
+                      f"(+{t1 - t0:.1f} s to convert the weights to fp64, not counted); a prefix rate, "
+                      f"optimistic for the whole replay"}
+
+
+def measured_bandwidth(gib: float = 2.0, reps: int = 5):
+    """Read and copy bandwidth of this GPU, measured in the same run with torch kernels."""
+    import torch
+
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    b.copy_(a)
+    a.sum()
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    copy = 2.0 * n * 4 * reps / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    ev[0].record(stream)
+    for _ in range(reps):
+        a.sum()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    read = 1.0 * n * 4 * reps / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": copy, "sum_read_GBps": read,
+            "how": f"torch copy_ (bytes read + written) and torch sum (bytes read) over {gib:g} GiB fp32, "
+                   f"{reps} each; the copy is the second roofline denominator"}
+
+
+def hbm_roofline(nbytes: float, ms: float, bw, kernel: str, traffic=None, **extra):
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+         "traffic": traffic, "kernel": kernel}
+    if bw:
+        r["measured_copy_GBps"] = bw["copy_GBps"]
+        r["frac_of_measured_copy"] = achieved / bw["copy_GBps"]
+    r.update(extra)
+    return r
+
+
+def segment_sizes(T: int, K: int):
+    """K contiguous segments covering positions 1..T (the first T % K one longer)."""
+    return [T // K + (1 if i < T % K else 0) for i in range(K)]
+
+
+REF48_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_batched_ref48_traffic.md")
+BATCHED_SOURCES = ["cross_token_recurrent_amd/csrc/dec_batched.hip", "cross_token_recurrent_amd/csrc/wstream.hip",
+                   "cross_token_recurrent_amd/csrc/device_common.h"]
+
+
+def headline_replay(wl, steps: int, warmup: int, bw, with_cpu: bool = True):
+    """The exact replay of one workload, timed as `steps` contiguous segments of the decoder
+    (see the module docstring).  Returns the headline fields."""
+    import torch
+
+    import cross_token_recurrent_amd as rlt
+    from workloads import make_tokens, make_weights
+
+    cfg, B, T = wl.model, wl.batch, wl.seq_len
+    if steps < 1 or steps > T:
+        raise SystemExit(f"--steps must be in 1..{T} (segments of the {T}-position replay)")
+    t_setup = time.perf_counter()
+    weights = make_weights(cfg, wl.weight_seed)
+    tokens = make_tokens(cfg.vocab, B, T, wl.token_dist, wl.token_seed)
+    dev = torch.device("cuda:0")
+    model = rlt.Model(cfg, weights, device=dev)
+    state = rlt.State(model, B, T, keep_encoder_cache=False)
+    tok = torch.from_numpy(tokens).to(dev)
+    stream = torch.cuda.current_stream()
+    seg = segment_sizes(T, steps)
+    print(f"{wl.name}: model and state ready in {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+    if warmup > 0:
+        state.reset()
+        rlt.rlt_encoder_forward(model, state, tok)
+        for n in seg[:warmup]:
+            rlt.rlt_decoder_replay(model, state, n)
+        torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 3)]
+    state.reset()
+    ev[0].record(stream)
+    rlt.rlt_encoder_forward(model, state, tok)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev[2].record(stream)
+    for k, n in enumerate(seg):
+        rlt.rlt_decoder_replay(model, state, n)
+        ev[3 + k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    assert state.device_error() == 0
+    enc_ms = ev[0].elapsed_time(ev[1])
+    seg_ms = [ev[2 + k].elapsed_time(ev[3 + k]) for k in range(steps)]
+    dec_ms = sum(seg_ms)
+    segments, done, prev = [], 0, 0.0
+    for n, ms in zip(seg, seg_ms):
+        cum = algorithmic_decoder_bytes(cfg, B, done + n)
+        gbs = (cum - prev) / (ms * 1e-3) / 1e9
+        segments.append({"t": [done + 1, done + n], "ms": ms, "GBps": gbs, "frac_of_hbm": gbs / HBM_PEAK_GBS})
+        done, prev = done + n, cum
+    path = {1: "persistent-per-sequence", 2: "batched-phases"}[model.decoder_path(T)]
+    del state, model
+    torch.cuda.empty_cache()
+    ms_step = wall * 1e3 / steps
+    out = {
+        "value": B * T / wall,
+        "ms_per_step": ms_step,
+        "decoder_event_ms": dec_ms,
+        "decoder_tokens_per_s_events": B * T / (dec_ms * 1e-3),
+        "end_to_end_tokens_per_s": B * T / ((enc_ms + dec_ms) * 1e-3),
+        "phase_ms": {"encoder": enc_ms, "decoder_replay": dec_ms},
+        "decoder_path": path,
+        "roofline": hbm_roofline(prev, dec_ms, bw, "decoder step loop (one launch per product, window and "
+                                 "cross-attention per layer; cross_part_k streams the memory rows)",
+                                 traffic=None, algorithmic_bytes=prev, unit_of_work="one exact replay, t = 1..T"),
+        "segments": segments,
+    }
+    if with_cpu:
+        out["cpu_baseline"] = (cpu_baseline(wl, weights, tokens) if wl.seq_len * wl.model.d_model <= (1 << 20)
+                               else cpu_baseline_prefix(wl, weights, tokens))
+    return out
 
 
 def scoring_rows(n: int, d: int, V: int) -> float:
@@ -416,63 +577,21 @@ def snapshot_leg(model, state, steps: int):
                          "algorithmic_bytes_per_call": nbytes}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="small")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-scoring", action="store_true", help="skip the RL action-scoring measurement")
-    ap.add_argument("--no-300m", action="store_true", help="skip the 300M-class batched decoder measurement")
-    ap.add_argument("--only-300m", action="store_true",
-                    help="run only the 300M-class batched decoder measurement (for profiling)")
-    ap.add_argument("--only-ref48", action="store_true",
-                    help="run only the same measurement on the 48+48-layer reference model (B=64)")
-    ap.add_argument("--only-long", action="store_true",
-                    help="run only the full replay of the long-context workload (B=16, T=32768; several minutes)")
-    ap.add_argument("--full-300m", action="store_true",
-                    help="run only the full replay of the 300M-class workload (B=512, T=2048)")
-    ap.add_argument("--full-ref48", action="store_true",
-                    help="run only the full replay of the 48+48-layer reference model (B=64, T=4096; minutes)")
-    ap.add_argument("--copy-kernel", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
-    args = ap.parse_args()
-    if args.copy_kernel:
-        copy_kernel()
-        return
-    if args.only_300m:
-        print(json.dumps({"decoder_300m": decoder_300m_leg()}), flush=True)
-        return
-    if args.only_ref48:
-        print(json.dumps({"decoder_ref48": decoder_300m_leg(1024, 32, "ref48")}), flush=True)
-        return
-    if args.only_long:
-        print(json.dumps({"decoder_long": full_replay_leg("long", 2048)}), flush=True)
-        return
-    if args.full_ref48:
-        print(json.dumps({"decoder_ref48_full": full_replay_leg("ref48", 512)}), flush=True)
-        return
-    if args.full_300m:
-        print(json.dumps({"decoder_300m_full": full_replay_leg("300m", 256)}), flush=True)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the replay shards over sequences with no communication, "
-              "so a multi-GPU figure is not measured here.", file=sys.stderr)
-        sys.exit(2)
-
+def small_leg(steps: int, warmup: int, bw, with_cpu: bool = True):
+    """The small workload (d=64, 4+4 layers, W=32, G=L, B=64, T=1024, bf16) on the persistent
+    decoder: one step = reset to H_0 + encoder over all T tokens + decoder replay + logits for
+    every position; the decoder launch is timed with HIP events."""
     import numpy as np
     import torch
 
     import cross_token_recurrent_amd as rlt
     from workloads import CONFIGS, make_tokens, make_weights
 
-    wl = CONFIGS[args.config]
-    cfg = wl.model
-    B, T = wl.batch, wl.seq_len
+    wl = CONFIGS["small"]
+    cfg, B, T = wl.model, wl.batch, wl.seq_len
     dev = torch.device("cuda:0")
     weights = make_weights(cfg, wl.weight_seed)
     tokens = make_tokens(cfg.vocab, B, T, wl.token_dist, wl.token_seed)
-
     model = rlt.Model(cfg, weights, device=dev)
     state = rlt.State(model, B, T, keep_encoder_cache=False)
     tok = torch.from_numpy(tokens).to(dev)
@@ -494,61 +613,135 @@ def main():
         if ev:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         step(events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
     enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     head_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-
     path = model.decoder_path(T)
     dec_bytes = algorithmic_decoder_bytes(cfg, B, T)
-    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    out = {
+        "workload": f"{wl.name}: RLT d={cfg.d_model} H={cfg.n_heads} L_E=L_D={cfg.n_layers} F={cfg.ffn_dim} "
+                    f"{cfg.ffn_kind} W={cfg.window} G={cfg.mem_groups} V={cfg.vocab}, B={B} T={T}, exact replay",
+        "decoder_tokens_per_s": B * T / (dec_ms * 1e-3),
+        "end_to_end_tokens_per_s": B * T / (wall / steps),
+        "ms_per_step": wall * 1e3 / steps,
+        "phase_ms": {"encoder": enc_ms, "decoder_replay": dec_ms, "logits": head_ms},
+        "decoder_path": {1: "persistent-per-sequence", 2: "batched-phases"}[path],
+        "roofline": hbm_roofline(dec_bytes, dec_ms, bw, "dec_small_k" if path == 1 else "batched decoder phases",
+                                 traffic=measured_traffic() if path == 1 else None,
+                                 algorithmic_bytes_per_launch=dec_bytes),
+    }
+    out["snapshot"] = snapshot_leg(model, state, 3)
+    del state, model, S, Z
+    torch.cuda.empty_cache()
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, weights, tokens)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8, help="segments the headline replay is timed in")
+    ap.add_argument("--warmup", type=int, default=2, help="segments of an untimed replay run first")
+    ap.add_argument("--config", default="ref48", help="headline workload (a name from workloads.CONFIGS)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-legs", action="store_true", help="only the headline replay")
+    ap.add_argument("--no-scoring", action="store_true", help="skip the RL action-scoring measurement")
+    ap.add_argument("--no-300m", action="store_true", help="skip the 300M-class batched decoder measurement")
+    ap.add_argument("--only-small", action="store_true",
+                    help="run only the small-workload leg (persistent decoder; for profiling)")
+    ap.add_argument("--only-scoring", action="store_true",
+                    help="run only the RL scoring and sampling legs (for profiling)")
+    ap.add_argument("--only-300m", action="store_true",
+                    help="run only the 300M-class batched decoder measurement (for profiling)")
+    ap.add_argument("--only-ref48", action="store_true",
+                    help="run only the same measurement on the 48+48-layer reference model (B=64)")
+    ap.add_argument("--only-long", action="store_true",
+                    help="run only the full replay of the long-context workload (B=16, T=32768; several minutes)")
+    ap.add_argument("--full-300m", action="store_true",
+                    help="run only the full replay of the 300M-class workload (B=512, T=2048)")
+    ap.add_argument("--full-ref48", action="store_true",
+                    help="run only the full replay of the 48+48-layer reference model (B=64, T=4096; minutes)")
+    ap.add_argument("--copy-kernel", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.copy_kernel:
+        copy_kernel()
+        return
+    if args.only_small:
+        print(json.dumps({"small": small_leg(max(1, args.steps), args.warmup, None, False)}), flush=True)
+        return
+    if args.only_scoring:
+        print(json.dumps({"rl_scoring": scoring_leg(max(1, args.steps), args.warmup, not args.no_cpu_baseline),
+                          "sampling": sampling_leg(max(1, args.steps), args.warmup, not args.no_cpu_baseline)}),
+              flush=True)
+        return
+    if args.only_300m:
+        print(json.dumps({"decoder_300m": decoder_300m_leg()}), flush=True)
+        return
+    if args.only_ref48:
+        print(json.dumps({"decoder_ref48": decoder_300m_leg(1024, 32, "ref48")}), flush=True)
+        return
+    if args.only_long:
+        print(json.dumps({"decoder_long": full_replay_leg("long", 2048)}), flush=True)
+        return
+    if args.full_ref48:
+        print(json.dumps({"decoder_ref48_full": full_replay_leg("ref48", 512)}), flush=True)
+        return
+    if args.full_300m:
+        print(json.dumps({"decoder_300m_full": full_replay_leg("300m", 256)}), flush=True)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the replay shards over sequences with no communication, "
+              "so a multi-GPU figure is not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    from workloads import CONFIGS
+
+    wl = CONFIGS[args.config]
+    cfg = wl.model
+    bw = measured_bandwidth()
+    head = headline_replay(wl, args.steps, args.warmup, bw, not args.no_cpu_baseline)
     line = {
         "metric": "RLT replay decoder tokens/sec (B*T/s) at 1 GPU; % of HBM/MFMA roofline",
-        "value": B * T / (ms_step * 1e-3),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,0.02) weights, uniform/Zipf token ids)",
         "config": {"workload": f"{wl.name}: RLT d={cfg.d_model} H={cfg.n_heads} L_E=L_D={cfg.n_layers} "
-                               f"F={cfg.ffn_dim} {cfg.ffn_kind} W={cfg.window} G={cfg.mem_groups} "
-                               f"V={cfg.vocab}, B={B} T={T}, exact replay",
-                   "batch": B, "seq_len": T},
-        "decoder_only_tokens_per_s": B * T / (dec_ms * 1e-3),
-        "phase_ms": {"encoder": enc_ms, "decoder_replay": dec_ms, "logits": head_ms},
-        "decoder_path": {1: "persistent-per-sequence", 2: "batched-phases"}[path],
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if path == 1 else None,
-                     "kernel": "dec_small_k" if path == 1 else "batched decoder phases",
-                     "algorithmic_bytes_per_launch": dec_bytes},
-        "cpu_baseline": None,
+                               f"F={cfg.ffn_dim} {cfg.ffn_kind} W={cfg.window} G={cfg.mem_groups} V={cfg.vocab}, "
+                               f"B={wl.batch} T={wl.seq_len}, exact replay timed as {args.steps} contiguous "
+                               f"segments of the decoder (encoder over all T tokens before the timed region)",
+                   "batch": wl.batch, "seq_len": wl.seq_len},
+        "roofline": head.pop("roofline"),
+        "cpu_baseline": head.pop("cpu_baseline", None),
+        "measured_bandwidth": bw,
     }
-    line["snapshot"] = snapshot_leg(model, state, 3)
-    if not args.no_300m:
-        del state, model, S, Z
-        torch.cuda.empty_cache()
-        line["decoder_300m"] = decoder_300m_leg()
-    if not args.no_scoring:
-        line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
-        line["sampling"] = sampling_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, weights, tokens)
+    for k in ("value", "ms_per_step"):
+        head.pop(k)
+    line["replay"] = head
+    if not args.no_legs:
+        line["small"] = small_leg(max(3, min(args.steps, 20)), 2, bw, not args.no_cpu_baseline)
+        if not args.no_300m:
+            line["decoder_300m"] = decoder_300m_leg()
+        if not args.no_scoring:
+            line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
+            line["sampling"] = sampling_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
     print(json.dumps(line), flush=True)
 
 

@@ -964,9 +964,12 @@ int rlt_decoder_step(const rlt_model* model, rlt_state* state, const int32_t* to
   if (state->t_enc > 0 && !state->lay.keep)
     return fail(RLT_ERR_NO_ENC_CACHE, "incremental generation needs keep_encoder_cache");
   if (!tokens) return fail(RLT_ERR_INVALID, "tokens is NULL");
-  // every pointer is checked before the first launch, so a failure enqueues nothing
+  // every pointer and the decoder implementation are checked before the first launch, so a
+  // failure enqueues nothing and leaves the state's positions as they were
   rc = need_gpu_memory({{tokens, "tokens"}, {s_out, "s_out"}, {logits, "logits"}});
   if (rc) return rc;
+  if (choose_path(model, state->lay.T) < 0)
+    return fail(RLT_ERR_UNSUPPORTED, "no decoder implementation for this configuration");
   rc = rlt_encoder_forward(model, state, tokens, 1, stream);
   if (rc) return rc;
   rc = rlt_decoder_replay(model, state, 1, s_out, stream);

@@ -27,7 +27,7 @@ def closed_form_bytes(cfg, B, T):
     d, L, F, W = cfg.d_model, cfg.n_layers, cfg.ffn_dim, cfg.window
     p = 2 if cfg.dtype == "bf16" else 4
     ffn = (2 if cfg.ffn_kind == "gelu" else 3) * d * F
-    p_loop = L * (6 * d * d + ffn) + 2 * d * d
+    p_loop = L * (6 * d * d + ffn) + 3 * d * d
     # sum_{k=0}^{T-1} min(k, W-1)
     cached = T * (T - 1) // 2 if T <= W else (W - 1) * W // 2 + (T - W) * (W - 1)
     ring = L * 2 * d * p * (cached + T)
@@ -47,4 +47,4 @@ def test_algorithmic_bytes_match_the_closed_form(name):
 
 def test_small_workload_bytes_are_the_quoted_figure():
     wl = CONFIGS["small"]
-    assert round(bench.algorithmic_decoder_bytes(wl.model, wl.batch, wl.seq_len) / 1e9, 2) == 37.04
+    assert round(bench.algorithmic_decoder_bytes(wl.model, wl.batch, wl.seq_len) / 1e9, 2) == 37.05

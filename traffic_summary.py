@@ -1,6 +1,6 @@
 """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter runs into the traffic summaries.
 
-    python -m cross_token_recurrent_amd.traffic_summary [--score] <fetch_dir> <write_dir> \
+    python traffic_summary.py [--score] <fetch_dir> <write_dir> \
         <copy_fetch_dir> <copy_write_dir> <out.md>
 
 Without a flag the summary covers the decoder (dec_small_k on the small workload); with
@@ -9,7 +9,8 @@ V=32000, d=1024, bf16, 65536 rows); with --sample, the sampling kernel (sample_k
 bench.py's sampling leg: 512 rows x V=32000).
 
 Each directory holds the counter_collection.csv of one `rocprofv3 --pmc <counter>` run:
-the decoder runs come from `bench.py --steps 1 --warmup 0 --no-cpu-baseline`, the copy
+the decoder runs come from `bench.py --only-small --steps 1 --warmup 0`, the scoring and
+sampling runs from `bench.py --only-scoring --steps 1 --warmup 0 --no-cpu-baseline`, the copy
 runs from `bench.py --copy-kernel` (1 GiB read + 1 GiB written).  The counters report
 KiB per dispatch; each is scaled by the ratio true bytes / counter bytes measured on the
 copy kernel, and the decoder's per-launch traffic is reported together with the kernel
@@ -22,7 +23,7 @@ import glob
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 
@@ -54,11 +55,11 @@ def score_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
     with open(out, "w") as f:
         f.write("# score_lse_res_k on the scoring leg (head V=32000, d=1024, bf16, 65536 rows): HBM traffic per launch\n\n")
         f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
-        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
-        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --only-scoring --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --only-scoring --steps 1 --warmup 0 --no-cpu-baseline\n")
         f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -- python3 <repo>/bench.py --copy-kernel\n")
-        f.write("    python -m cross_token_recurrent_amd.traffic_summary --score <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/score_lse_res_k_head32000x1024_traffic.md\n\n")
+        f.write("    python traffic_summary.py --score <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/score_lse_res_k_head32000x1024_traffic.md\n\n")
         f.write("The kernel is bound by the matrix cores and the L2-to-CU path (the head is re-read from L2 once per\n")
         f.write("64-row block), not by HBM; the counters show that the s rows and the head leave HBM about once.\n\n")
         f.write(f"- copy kernel: 1 GiB read / 1 GiB written; FETCH_SIZE reads {c_fetch:.4e} B, WRITE_SIZE {c_write:.4e} B\n")
@@ -86,11 +87,11 @@ def sample_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
     with open(out, "w") as f:
         f.write("# sample_k on the sampling leg (512 rows x V=32000 fp32 logits): HBM traffic per launch\n\n")
         f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
-        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
-        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --only-scoring --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --only-scoring --steps 1 --warmup 0 --no-cpu-baseline\n")
         f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -- python3 <repo>/bench.py --copy-kernel\n")
-        f.write("    python -m cross_token_recurrent_amd.traffic_summary --sample <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/sample_k_512x32000_traffic.md\n\n")
+        f.write("    python traffic_summary.py --sample <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/sample_k_512x32000_traffic.md\n\n")
         f.write("The largest dispatch of the leg is taken (all three truncation settings read the same logits).\n\n")
         f.write(f"- copy kernel: 1 GiB read / 1 GiB written; FETCH_SIZE reads {c_fetch:.4e} B, WRITE_SIZE {c_write:.4e} B\n")
         f.write(f"- fetch scale: {f_fetch:.4f}\n")
@@ -124,11 +125,11 @@ def main(argv):
     with open(out, "w") as f:
         f.write("# dec_small_k on the small workload: HBM traffic per launch (rocprofv3 counters)\n\n")
         f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
-        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
-        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-300m\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --only-small --steps 1 --warmup 0\n")
+        f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --only-small --steps 1 --warmup 0\n")
         f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -- python3 <repo>/bench.py --copy-kernel\n")
-        f.write("    python -m cross_token_recurrent_amd.traffic_summary <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/dec_small_k_small_traffic.md\n\n")
+        f.write("    python traffic_summary.py <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/dec_small_k_small_traffic.md\n\n")
         f.write(f"- copy kernel: 1 GiB read / 1 GiB written; FETCH_SIZE reads {c_fetch:.4e} B, WRITE_SIZE {c_write:.4e} B\n")
         f.write(f"- fetch scale: {f_fetch:.4f}\n")
         f.write(f"- write scale: {f_write:.4f}\n")
