@@ -36,7 +36,7 @@ bool use_wst(const ModelLayout& m, int B) {
 }
 
 struct Scratch {
-  size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, ssp, cnt, wpart, total;
+  size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, ssp, cnt, xcnt, wpart, total;
   size_t cnt_bytes;
   int nsmax;
 };
@@ -90,8 +90,12 @@ Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   size_t part_floats = 0, counters = 0;
   if (w) wst_scratch_max(m, B, &part_floats, &counters);
   s.ssp = take(w ? 2 * D * 4 : 0);
-  s.cnt_bytes = counters * 4;
-  s.cnt = take(s.cnt_bytes);
+  // arrival counters: the products' (first) and the cross-attention heads' (after them), one
+  // range that the state's reset zeroes
+  s.cnt = off;
+  s.xcnt = s.cnt + counters * 4;
+  s.cnt_bytes = counters * 4 + Bz * m.H * 4;
+  take(s.cnt_bytes);
   s.wpart = take(part_floats * 4);
   s.total = off;
   return s;
@@ -456,10 +460,15 @@ __global__ __launch_bounds__(512) void swa2_k(const float* __restrict__ qkv, WT*
 // Cross-attention partial states: one wave per (key chunk, head, sequence).
 // Scores with lanes over keys (LPK lanes per key row), then exp(s - M) for the chunk in
 // LDS, then P.V with lanes over (dim, 8-key block) reading the key-blocked value layout.
-template <typename WT, int DH>
+// With FUSE the chunks' partial states are combined in this launch: one chunk writes the head's
+// output directly; several write their partials at agent scope and the last of them to arrive (a
+// per-(sequence, head) counter, reset to zero by it) combines them in split order:
+// attn[b, h*DH + d] = sum_s e^{m_s - M} o_s[d] / sum_s e^{m_s - M} l_s.
+template <typename WT, int DH, bool FUSE>
 __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx, const WT* __restrict__ mem_k,
-                                                   const WT* __restrict__ mem_v, float* __restrict__ part, int B,
-                                                   int H, int T, int t, int nsmax, float scale) {
+                                                   const WT* __restrict__ mem_v, float* __restrict__ part,
+                                                   WT* __restrict__ attn, int* __restrict__ cnt, int B, int H, int T,
+                                                   int t, int nsmax, float scale) {
   constexpr int LPK = DH / 16;
   constexpr int SLOTS = 64 / LPK;
   constexpr int DL = DH < 64 ? DH : 64;   // lanes per block in the P.V pass
@@ -531,37 +540,81 @@ __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx,
 #pragma unroll
     for (int off = DL; off < 64; off <<= 1) o[nd] += __shfl_xor(o[nd], off, 64);
   }
-  float* pr = part + ((static_cast<size_t>(b) * H + h) * nsmax + split) * (DH + 2);
-  if (bq == 0) {
+  const int ns = (t + 1 + KCHUNK - 1) / KCHUNK;
+  WT* out = attn + static_cast<size_t>(b) * D + h * DH;
+  if (FUSE && ns == 1) {
+    if (bq == 0) {
 #pragma unroll
-    for (int nd = 0; nd < ND; ++nd) pr[2 + d0 + nd * 64] = o[nd];
-  }
-  if (lane == 0) {
-    pr[0] = M;
-    pr[1] = lsum;
-  }
-}
-
-// attn[b, h*DH + d] = sum_s e^{m_s - M} o_s[d] / sum_s e^{m_s - M} l_s, splits in order.
-template <typename WT>
-__global__ void cross_combine_k(const float* __restrict__ part, WT* __restrict__ attn, int H, int DH, int ns,
-                                int nsmax) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const float* pr = part + (static_cast<size_t>(b) * H + h) * nsmax * (DH + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pr[s * (DH + 2)]);
-  for (int d = threadIdx.x; d < DH; d += blockDim.x) {
-    float o = 0.f, l = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = __expf(pr[s * (DH + 2)] - M);
-      l += w * pr[s * (DH + 2) + 1];
-      o += w * pr[s * (DH + 2) + 2 + d];
+      for (int nd = 0; nd < ND; ++nd) store_from_f32(&out[d0 + nd * 64], o[nd] / lsum);
     }
-    store_from_f32(&attn[static_cast<size_t>(b) * H * DH + h * DH + d], o / l);
+    return;
+  }
+  float* pb = part + (static_cast<size_t>(b) * H + h) * nsmax * (DH + 2);
+  float* pr = pb + split * (DH + 2);
+  if constexpr (!FUSE) {
+    if (bq == 0) {
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) pr[2 + d0 + nd * 64] = o[nd];
+    }
+    if (lane == 0) {
+      pr[0] = M;
+      pr[1] = lsum;
+    }
+  } else {
+    if (bq == 0) {
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd)
+        __hip_atomic_store(pr + 2 + d0 + nd * 64, o[nd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane == 0) {
+      __hip_atomic_store(pr, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pr + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's partial has been written
+    int last = 0;
+    if (lane == 0) {
+      int* c = cnt + static_cast<size_t>(b) * H + h;
+      last = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1;
+      if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!__builtin_amdgcn_readfirstlane(last)) return;
+    // the last chunk: lane s holds chunk s's maximum and normaliser; every dimension's
+    // weighted sum runs over the chunks in split order (ns < kWideCombineSplits)
+    constexpr int NSF = kWideCombineSplits - 1;
+    const float mv = lane < ns ? __hip_atomic_load(pb + lane * (DH + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : -INFINITY;
+    const float lv = lane < ns ? __hip_atomic_load(pb + lane * (DH + 2) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.f;
+    float ov[NSF][ND];
+#pragma unroll
+    for (int sp = 0; sp < NSF; ++sp)
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd)
+        ov[sp][nd] = __hip_atomic_load(pb + min(sp, ns - 1) * (DH + 2) + 2 + min(d0, DH - 1) + nd * 64,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float Mx = group_max<64>(mv);
+    const float wv = lane < ns ? __expf(mv - Mx) : 0.f;
+    float acc[ND], lsum_all = 0.f;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) acc[nd] = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < NSF; ++sp) {
+      if (sp < ns) {   // uniform
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), sp));
+        const float lw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), sp));
+        lsum_all += w * lw;
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) acc[nd] += w * ov[sp][nd];
+      }
+    }
+    if (bq == 0) {
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) store_from_f32(&out[d0 + nd * 64], acc[nd] / lsum_all);
+    }
   }
 }
 
-// The same combine for many splits (long memories): 256 threads per (head, sequence).  The
+// The combine for many splits (long memories), as its own launch: 256 threads per (head, sequence).  The
 // split maxima and the normaliser are taken across the threads, and the weighted sum of the
 // split outputs is divided among 256/DH groups of threads (group g takes splits g, g + G, ...,
 // eight loads in flight); the groups' sums and the waves' normaliser sums are folded in a
@@ -634,19 +687,24 @@ hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratc
     const size_t goff = static_cast<size_t>(g) * B * S.T * m.D;
     const size_t goff_v = static_cast<size_t>(g) * B * S.T8 * m.D;
     const int ns = (t + 1 + KCHUNK - 1) / KCHUNK;
-    cross_part_k<WT, DH><<<dim3(ns, H, B), 64, 0, st>>>(
-        reinterpret_cast<const float*>(base + sc.qkv), reinterpret_cast<const WT*>(state + S.mem_k) + goff,
-        reinterpret_cast<const WT*>(state + S.mem_v) + goff_v, reinterpret_cast<float*>(base + sc.part), B, H, S.T, t,
-        sc.nsmax, scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const float* part = reinterpret_cast<const float*>(base + sc.part);
+    const float* qx = reinterpret_cast<const float*>(base + sc.qkv);
+    const WT* mk = reinterpret_cast<const WT*>(state + S.mem_k) + goff;
+    const WT* mv = reinterpret_cast<const WT*>(state + S.mem_v) + goff_v;
+    float* part = reinterpret_cast<float*>(base + sc.part);
     WT* out = reinterpret_cast<WT*>(base + sc.attn);
-    // a few splits: one thread per dimension walks them; many: the wide combine
-    if (ns >= kWideCombineSplits)
+    int* xcnt = reinterpret_cast<int*>(base + sc.xcnt);
+    // up to kWideCombineSplits - 1 chunks the combine runs in the same launch; past that, the
+    // 256-thread combine kernel folds the partials
+    if (ns < kWideCombineSplits) {
+      cross_part_k<WT, DH, true><<<dim3(ns, H, B), 64, 0, st>>>(qx, mk, mv, part, out, xcnt, B, H, S.T, t, sc.nsmax,
+                                                                 scale);
+    } else {
+      cross_part_k<WT, DH, false><<<dim3(ns, H, B), 64, 0, st>>>(qx, mk, mv, part, out, xcnt, B, H, S.T, t, sc.nsmax,
+                                                                  scale);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
       cross_combine_wide_k<WT, DH><<<dim3(H, B), 256, 0, st>>>(part, out, H, ns, sc.nsmax);
-    else
-      cross_combine_k<WT><<<dim3(H, B), std::min(DH, 128), 0, st>>>(part, out, H, DH, ns, sc.nsmax);
+    }
   }
   return hipGetLastError();
 }
