@@ -369,7 +369,9 @@ template <int MB, int IN, int EPI>
 hipError_t launch_ns(const WstArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(a.N / 64 * a.S), static_cast<unsigned>((a.M + 16 * MB - 1) / (16 * MB)));
   const int nst = a.KS / 64;
-  if (nst >= 8) wst_k<MB, IN, EPI, 8><<<grid, WNT, 0, st>>>(a);
+  // a 16-stage weight ring for the long bf16 slices (the merge's slice holds fp32 rows too)
+  if (IN == WIN_BF16 && nst >= 16) wst_k<MB, IN, EPI, (IN == WIN_BF16 ? 16 : 8)><<<grid, WNT, 0, st>>>(a);
+  else if (nst >= 8) wst_k<MB, IN, EPI, 8><<<grid, WNT, 0, st>>>(a);
   else if (nst >= 4) wst_k<MB, IN, EPI, 4><<<grid, WNT, 0, st>>>(a);
   else wst_k<MB, IN, EPI, 2><<<grid, WNT, 0, st>>>(a);
   return hipGetLastError();
