@@ -23,3 +23,9 @@ from .rlt_oracle import (  # noqa: F401
     silu,
     step,
 )
+from .rlt_backward import (  # noqa: F401
+    DETACH_PATHS,
+    bptt,
+    bptt_batch,
+    next_token_loss,
+)
