@@ -10,6 +10,8 @@ from .rlt import (  # noqa: F401
     load_library,
     make_config,
     replay,
+    rlt_bptt,
+    rlt_bptt_workspace_bytes,
     rlt_decoder_replay,
     rlt_decoder_replay_noalloc,
     rlt_decoder_step,

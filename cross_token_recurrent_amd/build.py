@@ -33,7 +33,8 @@ DEC_SMALL_PARTS = 4
 # (source, object name, extra flags); the slowest units first
 UNITS = [("dec_small.hip", f"dec_small_p{k}", [f"-DRLT_DEC_PART={k}"]) for k in range(DEC_SMALL_PARTS)] + [
     (src, os.path.splitext(src)[0], []) for src in
-    ["dec_batched.hip", "api.cpp", "misc.hip", "gemm.hip", "wstream.hip", "enc_attn.hip", "score.hip", "sample.hip"]]
+    ["dec_batched.hip", "api.cpp", "misc.hip", "gemm.hip", "wstream.hip", "enc_attn.hip", "score.hip", "sample.hip",
+     "bptt.hip"]]
 
 
 def _compile(unit) -> str:

@@ -1028,6 +1028,68 @@ int rlt_decoder_step_sample(const rlt_model* model, rlt_state* state, const int3
                            stream);
 }
 
+int rlt_bptt_workspace_bytes(const rlt_config* cfg, int32_t batch, int32_t seq_len, size_t* bytes) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(RLT_ERR_INVALID, "bytes is NULL");
+  const char* why = "";
+  if (!bptt_supported(*cfg, batch, seq_len, &why)) return fail(RLT_ERR_UNSUPPORTED, why);
+  *bytes = bptt_workspace_bytes(*cfg, batch, seq_len);
+  return RLT_OK;
+}
+
+int rlt_bptt(const rlt_config* cfg, const float* weights, const int32_t* tokens, const float* mask, int32_t batch,
+             int32_t seq_len, int32_t detach, float* grads, float* loss, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!weights || !tokens || !grads || !loss || !workspace)
+    return fail(RLT_ERR_INVALID, "weights, tokens, grads, loss and workspace must be non-NULL");
+  if (detach & ~(RLT_DETACH_S | RLT_DETACH_KV | RLT_DETACH_MEMORY))
+    return fail(RLT_ERR_INVALID, "detach holds unknown bits");
+  const char* why = "";
+  if (!bptt_supported(*cfg, batch, seq_len, &why)) return fail(RLT_ERR_UNSUPPORTED, why);
+  if (workspace_bytes < bptt_workspace_bytes(*cfg, batch, seq_len))
+    return fail(RLT_ERR_INVALID, "workspace is smaller than rlt_bptt_workspace_bytes");
+  rc = need_gpu_memory({{weights, "weights"}, {tokens, "tokens"}, {mask, "mask"}, {grads, "grads"}, {loss, "loss"},
+                        {workspace, "workspace"}});
+  if (rc) return rc;
+  BpttOffsets o{};
+  const bool sw = cfg->ffn_kind == RLT_FFN_SWIGLU;
+  o.embed = param_offset(*cfg, "embed", nullptr);
+  o.w_out = param_offset(*cfg, "w_out", nullptr);
+  o.s_star = param_offset(*cfg, "s_star", nullptr);
+  o.w_ge = param_offset(*cfg, "w_ge", nullptr);
+  o.w_gs = param_offset(*cfg, "w_gs", nullptr);
+  o.w_fb = param_offset(*cfg, "w_fb", nullptr);
+  o.b_g = param_offset(*cfg, "b_g", nullptr);
+  o.wq = param_offset(*cfg, "wq", nullptr);
+  o.wk = param_offset(*cfg, "wk", nullptr);
+  o.wv = param_offset(*cfg, "wv", nullptr);
+  o.wo = param_offset(*cfg, "wo", nullptr);
+  o.f1 = param_offset(*cfg, sw ? "ffn_gate" : "ffn_w1", nullptr);
+  o.f2 = param_offset(*cfg, sw ? "ffn_up" : "ffn_w2", nullptr);
+  o.f3 = sw ? param_offset(*cfg, "ffn_down", nullptr) : -1;
+  o.wqx = param_offset(*cfg, "wqx", nullptr);
+  o.wox = param_offset(*cfg, "wox", nullptr);
+  o.wkm = param_offset(*cfg, "wkm", nullptr);
+  o.wvm = param_offset(*cfg, "wvm", nullptr);
+  o.g_enc_attn = param_offset(*cfg, "g_enc_attn", nullptr);
+  o.g_enc_ffn = param_offset(*cfg, "g_enc_ffn", nullptr);
+  o.g_enc_final = param_offset(*cfg, "g_enc_final", nullptr);
+  o.g_dec_self = param_offset(*cfg, "g_dec_self", nullptr);
+  o.g_dec_cross = param_offset(*cfg, "g_dec_cross", nullptr);
+  o.g_dec_ffn = param_offset(*cfg, "g_dec_ffn", nullptr);
+  o.g_dec_final = param_offset(*cfg, "g_dec_final", nullptr);
+  int32_t nt = 0;
+  int64_t total = 0;
+  rlt_param_count(cfg, &nt, &total);
+  RLT_HIP(run_bptt(*cfg, o, weights, tokens, mask, batch, seq_len, detach, grads, loss,
+                   static_cast<char*>(workspace), static_cast<size_t>(total), as_stream(stream)),
+          "bptt");
+  return RLT_OK;
+}
+
 int rlt_state_load_encoder_outputs(const rlt_model* model, rlt_state* state, const float* e,
                                    const float* mem_k, const float* mem_v, int32_t n, void* stream) {
   int rc = check_pair(model, state);

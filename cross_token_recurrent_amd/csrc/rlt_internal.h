@@ -233,4 +233,19 @@ void dec_batched_counters(const ModelLayout& m, int B, int T, size_t* offset, si
 hipError_t run_dec_batched(const ModelLayout& m, const StateLayout& s, const char* ws, char* state, char* scratch,
                            float* s_out, int t0, int n, hipStream_t st);
 
+// Full-BPTT backward of the replay (bptt.hip), fp32 arithmetic on the canonical fp32 weights.
+// Element offsets of the canonical tensors; f1, f2, f3 = ffn_w1, ffn_w2, - (GELU) or
+// ffn_gate, ffn_up, ffn_down (SwiGLU).
+struct BpttOffsets {
+  int64_t embed, w_out, s_star, w_ge, w_gs, w_fb, b_g, wq, wk, wv, wo, f1, f2, f3, wqx, wox, wkm, wvm;
+  int64_t g_enc_attn, g_enc_ffn, g_enc_final, g_dec_self, g_dec_cross, g_dec_ffn, g_dec_final;
+};
+bool bptt_supported(const rlt_config& c, int B, int T, const char** why);
+size_t bptt_workspace_bytes(const rlt_config& c, int B, int T);
+// detach: bit 0 cuts s_{t-1} into the merge (t >= 2), bit 1 the earlier window entries, bit 2
+// the memory rows.  grads (total_numel floats, canonical layout) are overwritten; loss [B].
+hipError_t run_bptt(const rlt_config& c, const BpttOffsets& o, const float* w, const int32_t* tok, const float* mask,
+                    int B, int T, int detach, float* grads, float* loss, char* ws, size_t total_numel,
+                    hipStream_t st);
+
 }  // namespace rlt

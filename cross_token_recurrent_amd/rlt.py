@@ -79,6 +79,8 @@ _SIGS = {
     "rlt_decoder_step_sample": [_P, _P, _P, ctypes.POINTER(rlt_sampling), _P, _P, _P, _P, _P, _P],
     "rlt_state_load_encoder_outputs": [_P, _P, _P, _P, _P, _I32, _P],
     "rlt_state_read_encoder_outputs": [_P, _P, _I32, _I32, _P, _P, _P, _P],
+    "rlt_bptt_workspace_bytes": [ctypes.POINTER(rlt_config), _I32, _I32, ctypes.POINTER(ctypes.c_size_t)],
+    "rlt_bptt": [ctypes.POINTER(rlt_config), _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
     "rlt_decoder_path": [_P, _I32, ctypes.POINTER(_I32)],
     "rlt_model_set_decoder_path": [_P, _I32],
     "rlt_last_error": [],
@@ -335,6 +337,49 @@ def rlt_state_read_encoder_outputs(model: "Model", state: "State", t0: int, n: i
 
 
 # ---- owners of device memory and handles --------------------------------------------------
+
+DETACH_FLAGS = {"s": 1, "kv": 2, "memory": 4}
+
+
+def rlt_bptt_workspace_bytes(cfg: rlt_config, batch: int, seq_len: int) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().rlt_bptt_workspace_bytes(ctypes.byref(cfg), batch, seq_len, ctypes.byref(out)))
+    return out.value
+
+
+def rlt_bptt(cfg: rlt_config, weights: torch.Tensor, tokens: torch.Tensor, mask: Optional[torch.Tensor] = None,
+             detach=(), grads: Optional[torch.Tensor] = None, loss: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Loss per sequence and the full-BPTT gradient (canonical flat layout) of the next-token loss.
+
+    weights: flat fp32 canonical buffer on the device; tokens int32 [B, T]; mask fp32 [B, T-1] or
+    None; detach: names from DETACH_FLAGS.  Returns (loss [B], grads [total])."""
+    dev = weights.device
+    total = sum(n for _, n in rlt_param_table(cfg).values())
+    _tensor(weights, "weights", torch.float32, dev, numel=total)
+    _need(tokens.dim() == 2, "tokens must be [batch, seq_len]")
+    B, T = tokens.shape
+    _tensor(tokens, "tokens", torch.int32, dev, shape=(B, T))
+    if mask is not None:
+        _tensor(mask, "mask", torch.float32, dev, shape=(B, max(T - 1, 0)))
+    bits = 0
+    for name in detach:
+        _need(name in DETACH_FLAGS, f"unknown detach path {name!r}")
+        bits |= DETACH_FLAGS[name]
+    if grads is None:
+        grads = torch.empty(total, dtype=torch.float32, device=dev)
+    _tensor(grads, "grads", torch.float32, dev, numel=total)
+    if loss is None:
+        loss = torch.empty(B, dtype=torch.float32, device=dev)
+    _tensor(loss, "loss", torch.float32, dev, shape=(B,))
+    nbytes = rlt_bptt_workspace_bytes(cfg, B, T)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _tensor(workspace, "workspace", torch.uint8, dev)
+    _check(load_library().rlt_bptt(ctypes.byref(cfg), _ptr(weights), _ptr(tokens), _ptr(mask), B, T, bits,
+                                   _ptr(grads), _ptr(loss), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return loss, grads
+
 
 class Model:
     """Packed weights (device workspace owned here) and the C model handle."""

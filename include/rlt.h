@@ -269,6 +269,35 @@ int rlt_score_actions(const rlt_model* model, const float* s, const int32_t* act
                       float temperature, const float* behaviour_logp, float* logp_out,
                       float* ratio_out, void* stream);
 
+/* ---- full back-propagation through time --------------------------------------------
+ * The exact gradient of the next-token loss of a replay from H_0 ([DS] deepsonar
+ * "技术拆解 009｜RLT…" §2.5 and the recipe of §六: teacher forcing, every valid next-token
+ * prediction supervised, gradient through the whole recurrent trajectory; §2.6, second
+ * point: the gradient runs through s_{t-1}, the decoder window keys/values and the encoder
+ * memory, and a detach only approximates it).  For each sequence b:
+ *   loss[b] = sum_{t=0}^{T-2} mask[b][t] * CE(W_out s_t, tokens[b][t+1])
+ * (mask NULL = all ones; SFT passes zeros off the assistant targets while the state still runs
+ * over every position).  grads receives d(sum_b loss[b]) / d(every parameter), s* included, in
+ * the canonical layout above (total_numel floats, overwritten).
+ *   weights   device fp32, the canonical buffer (the backward computes in fp32 from it; a bf16
+ *             model's buffer holds its bf16-representable values)
+ *   tokens    device int32 [batch][seq_len]; an id outside [0, vocab) makes every loss NaN
+ *   mask      device fp32 [batch][seq_len-1] or NULL
+ *   detach    0 for the exact gradient, or an OR of RLT_DETACH_* approximations
+ *   grads     device fp32 [total_numel]; loss device fp32 [batch]
+ *   workspace device memory of rlt_bptt_workspace_bytes bytes, owned by the caller
+ * All work is enqueued on `stream`.  Errors: RLT_ERR_INVALID (NULL or host pointers, bad
+ * sizes, workspace too small), RLT_ERR_UNSUPPORTED (d_model > 256, head_dim > 64,
+ * ffn_dim > 1024, window > 1024, or a sequence too long for the sweep's per-sequence LDS:
+ * about 4 (2 H T + 2 H W + 30 d) bytes must fit 160 KB); nothing is enqueued on error. */
+#define RLT_DETACH_S 1          /* s_{t-1} is a constant in the merge for t >= 1 (0-based) */
+#define RLT_DETACH_KV 2         /* earlier window entries are constants for later steps   */
+#define RLT_DETACH_MEMORY 4     /* memory rows are constants for cross-attention          */
+int rlt_bptt_workspace_bytes(const rlt_config* cfg, int32_t batch, int32_t seq_len, size_t* bytes);
+int rlt_bptt(const rlt_config* cfg, const float* weights, const int32_t* tokens, const float* mask,
+             int32_t batch, int32_t seq_len, int32_t detach, float* grads, float* loss,
+             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- test hooks (decoder in isolation, encoder outputs) -----------------------------
  * rlt_state_load_encoder_outputs writes externally computed e (device fp32 [B, n, d])
  * and memory rows (device fp32 [G, B, n, d] each for keys and values) for positions

@@ -62,3 +62,29 @@ def check(name: str, gpu: np.ndarray, ref: np.ndarray, dtype: str) -> float:
     print(f"  {name}: {'max-abs' if dtype == 'fp32' else 'max row-rel'} = {err:.3e}", flush=True)
     sys.stdout.flush()
     return err
+
+
+def _oracle_bptt_one(args):
+    cfg, weights, tok, mask, detach = args
+    import oracle
+    m = oracle.OracleModel.from_config(cfg, weights)
+    loss, grads, _ = oracle.bptt(m, tok, mask, detach)
+    return loss, grads
+
+
+def oracle_bptt(cfg, weights: Dict[str, np.ndarray], tokens: np.ndarray, masks: Optional[np.ndarray] = None,
+                detach=(), seqs: Optional[Sequence[int]] = None, workers: Optional[int] = None):
+    """(per-sequence losses [nb], summed gradients {name: array}) of the fp64 backward oracle over
+    the chosen sequences, computed in spawned worker processes."""
+    seqs = list(range(tokens.shape[0])) if seqs is None else list(seqs)
+    jobs = [(cfg, weights, tokens[b], None if masks is None else masks[b], tuple(detach)) for b in seqs]
+    if workers is None:
+        workers = min(len(jobs), 8, len(os.sched_getaffinity(0)))
+    if workers <= 1 or len(jobs) == 1:
+        out = [_oracle_bptt_one(j) for j in jobs]
+    else:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers) as pool:
+            out = pool.map(_oracle_bptt_one, jobs)
+    grads = {k: sum(o[1][k] for o in out) for k in out[0][1]}
+    return np.array([o[0] for o in out]), grads
