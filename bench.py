@@ -647,6 +647,86 @@ def small_leg(steps: int, warmup: int, bw, with_cpu: bool = True):
     return out
 
 
+def bptt_leg(steps: int, warmup: int, with_cpu: bool = True):
+    """Full-BPTT backward of the small workload (d=64, 4+4 layers, W=32, G=L, V=512, B=64,
+    T=1024): one call = encoder and decoder forward with the tape, loss, reverse sweep and every
+    parameter gradient; timed with HIP events around the call."""
+    import numpy as np
+    import torch
+
+    import cross_token_recurrent_amd as rlt
+    from workloads import CONFIGS, make_tokens, make_weights
+
+    wl = CONFIGS["small"]
+    cfg, B, T = wl.model, wl.batch, wl.seq_len
+    dev = torch.device("cuda:0")
+    weights = make_weights(cfg, wl.weight_seed)
+    tokens = make_tokens(cfg.vocab, B, T, wl.token_dist, wl.token_seed)
+    c = rlt.make_config(cfg)
+    table = rlt.rlt_param_table(c)
+    total = sum(n for _, n in table.values())
+    flat = torch.empty(total, dtype=torch.float32)
+    for name, (off, n) in table.items():
+        flat[off:off + n] = torch.from_numpy(np.ascontiguousarray(weights[name], dtype=np.float32).reshape(-1))
+    flat = flat.to(dev)
+    tok = torch.from_numpy(tokens.astype(np.int32)).to(dev)
+    grads = torch.empty(total, dtype=torch.float32, device=dev)
+    loss = torch.empty(B, dtype=torch.float32, device=dev)
+    ws = torch.empty(rlt.rlt_bptt_workspace_bytes(c, B, T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        rlt.rlt_bptt(c, flat, tok, None, (), grads, loss, ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for k in range(steps):
+        rlt.rlt_bptt(c, flat, tok, None, (), grads, loss, ws)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]
+    avg = float(np.mean(ms))
+    out = {
+        "workload": f"{wl.name}: RLT d={cfg.d_model} H={cfg.n_heads} L_E=L_D={cfg.n_layers} F={cfg.ffn_dim} "
+                    f"{cfg.ffn_kind} W={cfg.window} G={cfg.mem_groups} V={cfg.vocab}, B={B} T={T}, full BPTT of "
+                    f"the summed next-token loss (fp32 arithmetic on the bf16-valued weights)",
+        "ms_per_call": avg,
+        "ms_min": float(np.min(ms)),
+        "tokens_per_s": B * T / (avg * 1e-3),
+        "loss_mean_per_token": float(loss.sum().item()) / (B * (T - 1)),
+        "workspace_GB": ws.numel() / 1e9,
+    }
+    del ws, grads, flat
+    torch.cuda.empty_cache()
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline_bptt(wl, weights, tokens)
+    return out
+
+
+def _oracle_bptt_one(args):
+    cfg, weights, tok = args
+    import oracle
+    m = oracle.OracleModel.from_config(cfg, weights)
+    return oracle.bptt(m, tok)[0]
+
+
+def cpu_baseline_bptt(wl, weights, tokens, n_seq: int = 4):
+    """The fp64 backward oracle on n_seq whole sequences of the workload, one per worker."""
+    import multiprocessing as mp
+
+    cores, _ = host_cores()
+    workers = min(cores, 16, n_seq)
+    jobs = [(wl.model, weights, tokens[b]) for b in range(n_seq)]
+    t0 = time.perf_counter()
+    with mp.get_context("spawn").Pool(workers) as pool:
+        pool.map(_oracle_bptt_one, jobs)
+    wall = time.perf_counter() - t0
+    return {"value": n_seq * wl.seq_len / wall, "unit": "tokens/s", "cores": cores, "workers": workers,
+            "kind": "oracle",
+            "sample": f"{n_seq} of {wl.batch} sequences x T={wl.seq_len}, full BPTT (loss and every gradient), "
+                      f"fp64 numpy, one sequence per worker process ({workers} workers on {cores} cores), "
+                      f"{wall:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -671,6 +751,8 @@ def main():
                     help="run only the full replay of the 300M-class workload (B=512, T=2048)")
     ap.add_argument("--full-ref48", action="store_true",
                     help="run only the full replay of the 48+48-layer reference model (B=64, T=4096; minutes)")
+    ap.add_argument("--only-bptt", action="store_true",
+                    help="run only the full-BPTT backward of the small workload (B=64, T=1024)")
     ap.add_argument("--copy-kernel", action="store_true", help="run only a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.copy_kernel:
@@ -678,6 +760,9 @@ def main():
         return
     if args.only_small:
         print(json.dumps({"small": small_leg(max(1, args.steps), args.warmup, None, False)}), flush=True)
+        return
+    if args.only_bptt:
+        print(json.dumps({"bptt": bptt_leg(max(1, args.steps), args.warmup, not args.no_cpu_baseline)}), flush=True)
         return
     if args.only_scoring:
         print(json.dumps({"rl_scoring": scoring_leg(max(1, args.steps), args.warmup, not args.no_cpu_baseline),

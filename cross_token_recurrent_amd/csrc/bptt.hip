@@ -377,23 +377,33 @@ __global__ __launch_bounds__(64) void enc_attn_bwd_q_k(const float* QKV, const f
   for (int c = 0; c < DH; ++c) dQKV[(rb + i) * 3 * D + h * DH + c] = dq[c] * scale;
 }
 
-// dk_j = scale sum_{i>=j} p_ij (dp_ij - D_i) q_i;  dv_j = sum_{i>=j} p_ij dO_i.
+// Key side of a causal attention's adjoint (queries i attend keys j <= i of the same sequence):
+// dk_j = scale sum_{i>=j} p_ij (dp_ij - D_i) q_i;  dv_j = sum_{i>=j} p_ij dO_i, with
+// p_ij = exp(scale q_i.k_j - lse_i), dp_ij = dO_i.v_j.  Rows r = b T + t of every operand with
+// their own strides; the head's columns start at h DH.  accumulate: dK, dV += (else =).
+struct KvArgs {
+  const float* Q; long long ldq;
+  const float* K; const float* V; long long ldkv;
+  const float* dO; long long lddo;
+  const float* LSE; const float* Dsum;     // [B][H][T]
+  float* dK; float* dV; long long lddkv;
+  int T, H, accumulate;
+  float scale;
+};
 template <int DH>
-__global__ __launch_bounds__(64) void enc_attn_bwd_kv_k(const float* QKV, const float* dO, const float* LSE,
-                                                        const float* Dsum, float* dQKV, int T, int H, int D,
-                                                        float scale) {
+__global__ __launch_bounds__(64) void attn_bwd_kv_k(KvArgs a) {
   __shared__ float Qs[64][DH + 1];
   __shared__ float Gs[64][DH + 1];
   __shared__ float Ls[64], Ds[64];
-  const int b = blockIdx.z, h = blockIdx.y, j = blockIdx.x * 64 + threadIdx.x;
+  const int b = blockIdx.z, h = blockIdx.y, j = blockIdx.x * 64 + threadIdx.x, T = a.T;
   const size_t rb = static_cast<size_t>(b) * T;
   const bool live = j < T;
   const size_t rj = rb + min(j, T - 1);
   float k[DH], v[DH], dk[DH], dv[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
-    k[c] = QKV[rj * 3 * D + D + h * DH + c];
-    v[c] = QKV[rj * 3 * D + 2 * D + h * DH + c];
+    k[c] = a.K[rj * a.ldkv + h * DH + c];
+    v[c] = a.V[rj * a.ldkv + h * DH + c];
     dk[c] = 0.f;
     dv[c] = 0.f;
   }
@@ -402,11 +412,11 @@ __global__ __launch_bounds__(64) void enc_attn_bwd_kv_k(const float* QKV, const 
     const size_t ri = rb + min(i, T - 1);
 #pragma unroll
     for (int c = 0; c < DH; ++c) {
-      Qs[threadIdx.x][c] = QKV[ri * 3 * D + h * DH + c] * scale;
-      Gs[threadIdx.x][c] = dO[ri * D + h * DH + c];
+      Qs[threadIdx.x][c] = a.Q[ri * a.ldq + h * DH + c] * a.scale;
+      Gs[threadIdx.x][c] = a.dO[ri * a.lddo + h * DH + c];
     }
-    Ls[threadIdx.x] = LSE[(static_cast<size_t>(b) * H + h) * T + min(i, T - 1)];
-    Ds[threadIdx.x] = Dsum[(static_cast<size_t>(b) * H + h) * T + min(i, T - 1)];
+    Ls[threadIdx.x] = a.LSE[(static_cast<size_t>(b) * a.H + h) * T + min(i, T - 1)];
+    Ds[threadIdx.x] = a.Dsum[(static_cast<size_t>(b) * a.H + h) * T + min(i, T - 1)];
     __syncthreads();
     const int ii0 = max(0, j - i0), in = min(64, T - i0);
     for (int ii = ii0; live && ii < in; ++ii) {
@@ -424,9 +434,22 @@ __global__ __launch_bounds__(64) void enc_attn_bwd_kv_k(const float* QKV, const 
   // Qs holds q * scale, so dk already carries the scale.
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
-    dQKV[rj * 3 * D + D + h * DH + c] = dk[c];
-    dQKV[rj * 3 * D + 2 * D + h * DH + c] = dv[c];
+    float* pk = a.dK + rj * a.lddkv + h * DH + c;
+    float* pv = a.dV + rj * a.lddkv + h * DH + c;
+    *pk = a.accumulate ? *pk + dk[c] : dk[c];
+    *pv = a.accumulate ? *pv + dv[c] : dv[c];
   }
+}
+
+// Dsum[b][h][t] = dO_r . O_r over head h's columns (r = b T + t).
+__global__ void head_dots_k(const float* dO, const float* O, long long ld, int B, int T, int H, int DH, float* Dsum) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<size_t>(B) * H * T) return;
+  const int t = static_cast<int>(i % T), h = static_cast<int>((i / T) % H), b = static_cast<int>(i / (static_cast<size_t>(T) * H));
+  const size_t r = static_cast<size_t>(b) * T + t;
+  float s = 0.f;
+  for (int c = 0; c < DH; ++c) s = fmaf(dO[r * ld + h * DH + c], O[r * ld + h * DH + c], s);
+  Dsum[i] = s;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -447,6 +470,8 @@ struct DecArgs {
   float* SPREV;              // [R][D]       s_{t-1} (s* at t = 0)
   const float* DS;           // [R][D]       logit-term adjoint of s_t
   float *DQKV, *H1, *DY1, *O1, *DQX, *H2, *DY2, *O2, *DU, *H3, *DY3, *ACT;   // [L][R][.]
+  float *QXS, *DO2S;         // [L][R][D]   cross-attention query and output adjoint per step
+  float* CLSE;               // [L][B][H][T] cross-attention row log-sum-exp
   float *DA, *DF, *DE;       // [R][D]
   float* DM;                 // [G][R][2D]
   float* RING;               // [L][B][W][2D]
@@ -470,9 +495,6 @@ struct DecLds {
   }
 };
 
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // s_waitcnt vmcnt(0): this wave's global stores have completed.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -484,25 +506,50 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// out[n] = sum_k W[n][k] x[k] with W^T [K][N] given (coalesced over n); one thread per output.
-__device__ __forceinline__ void matvec(const float* __restrict__ Wt, int N, int K, const float* x, float* out,
-                                       bool accumulate = false) {
-  for (int n = threadIdx.x; n < N; n += NT) {
+// out[i] (+)= sum_j M[i][j] x[j] for a row-major M [Nout][Kin] (Kin a multiple of 64) and x in
+// LDS: G contiguous lanes per row, each over a contiguous share of it with 16-byte loads (all
+// issued before the sums), then a lane-group sum in a fixed order.
+template <int G>
+__device__ __forceinline__ void rowdot_g(const float* __restrict__ M, int Nout, int Kin, const float* x, float* out,
+                                         bool accumulate) {
+  const int per = Kin / G;
+  for (int base = 0; base < Nout * G; base += NT) {
+    const int tid = base + static_cast<int>(threadIdx.x);
+    const int i = tid / G, gi = tid % G;
     float a = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < K; ++k) a = fmaf(Wt[static_cast<size_t>(k) * N + n], x[k], a);
-    out[n] = accumulate ? out[n] + a : a;
+    if (i < Nout) {
+      const float4* mr = reinterpret_cast<const float4*>(M + static_cast<size_t>(i) * Kin + gi * per);
+      const float* xr = x + gi * per;
+#pragma unroll 4
+      for (int k = 0; k < per / 4; ++k) {
+        const float4 w = mr[k];
+        a = fmaf(w.x, xr[4 * k], a);
+        a = fmaf(w.y, xr[4 * k + 1], a);
+        a = fmaf(w.z, xr[4 * k + 2], a);
+        a = fmaf(w.w, xr[4 * k + 3], a);
+      }
+    }
+    a = group_sum<G>(a);
+    if (i < Nout && gi == 0) out[i] = accumulate ? out[i] + a : a;
   }
 }
-// out[k] = sum_n W[n][k] x[n] with W [N][K] given (coalesced over k).
-__device__ __forceinline__ void matvec_t(const float* __restrict__ W, int N, int K, const float* x, float* out,
+__device__ __noinline__ void rowdot(const float* M, int Nout, int Kin, const float* x, float* out,
+                                       bool accumulate) {
+  if (Nout * 16 <= NT) rowdot_g<16>(M, Nout, Kin, x, out, accumulate);
+  else if (Nout * 8 <= NT) rowdot_g<8>(M, Nout, Kin, x, out, accumulate);
+  else if (Nout * 4 <= NT) rowdot_g<4>(M, Nout, Kin, x, out, accumulate);
+  else if (Nout * 2 <= NT) rowdot_g<2>(M, Nout, Kin, x, out, accumulate);
+  else rowdot_g<1>(M, Nout, Kin, x, out, accumulate);
+}
+// out[n] (+)= sum_k W[n][k] x[k] for W [N][K] (canonical layout).
+__device__ __forceinline__ void matvec(const float* W, int N, int K, const float* x, float* out,
+                                       bool accumulate = false) {
+  rowdot(W, N, K, x, out, accumulate);
+}
+// out[k] (+)= sum_n W[n][k] x[n], given the transposed copy WT = W^T [K][N].
+__device__ __forceinline__ void matvec_t(const float* WT, int N, int K, const float* x, float* out,
                                          bool accumulate = false) {
-  for (int k = threadIdx.x; k < K; k += NT) {
-    float a = 0.f;
-#pragma unroll 8
-    for (int n = 0; n < N; ++n) a = fmaf(W[static_cast<size_t>(n) * K + k], x[n], a);
-    out[k] = accumulate ? out[k] + a : a;
-  }
+  rowdot(WT, K, N, x, out, accumulate);
 }
 
 // out = g x / rms(x) over an LDS vector.
@@ -531,21 +578,31 @@ __device__ __forceinline__ void rms_vec_bwd(const float* x, const float* g, cons
 }
 
 // Attention of one query (LDS, D wide) over n rows per head, one wave per head (heads h = wave,
-// wave + 4, ...).  Row i of head h: key at krow(i) + h DH, value at krow(i) + voff + h DH.  The
-// probabilities go to P[h * ldp + i], the output to out (LDS).  AGENT: rows read at agent scope
-// (rows written earlier in the same launch by other waves).
-template <bool AGENT, typename RowFn>
-__device__ __forceinline__ void attend_heads(const float* q, RowFn krow, int voff, int n, int H, int DH, float scale,
-                                             float* P, int ldp, float* out) {
+// wave + 4, ...) and one lane per row: row i of head h has its key at krow(i) + h DH and its
+// value at krow(i) + voff + h DH (16-byte loads).  The probabilities go to P[h * ldp + i], the
+// output to out (LDS), the row log-sum-exp to lse[h * ldl] when lse is given.  Each lane reads
+// back only the P entries it wrote; the per-dimension sums over lanes run in a fixed order.
+template <int DH, typename RowFn>
+__device__ __forceinline__ void attend_heads(const float* q, RowFn krow, int voff, int n, int H, float scale, float* P,
+                                             int ldp, float* out, float* lse = nullptr, long long ldl = 0) {
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int JG = 64 / DH, c = lane % DH, jg = lane / DH;
   for (int h = wave; h < H; h += 4) {
     float* ph = P + h * ldp;
+    float qh[DH];
+#pragma unroll
+    for (int c = 0; c < DH; ++c) qh[c] = q[h * DH + c];
     float mx = -INFINITY;
     for (int i = lane; i < n; i += 64) {
-      const float* kr = krow(i) + h * DH;
+      const float4* kr = reinterpret_cast<const float4*>(krow(i) + h * DH);
       float s = 0.f;
-      for (int cc = 0; cc < DH; ++cc) s = fmaf(q[h * DH + cc], AGENT ? ld_agent(kr + cc) : kr[cc], s);
+#pragma unroll
+      for (int c4 = 0; c4 < DH / 4; ++c4) {
+        const float4 k = kr[c4];
+        s = fmaf(qh[4 * c4], k.x, s);
+        s = fmaf(qh[4 * c4 + 1], k.y, s);
+        s = fmaf(qh[4 * c4 + 2], k.z, s);
+        s = fmaf(qh[4 * c4 + 3], k.w, s);
+      }
       s *= scale;
       ph[i] = s;
       mx = fmaxf(mx, s);
@@ -558,50 +615,82 @@ __device__ __forceinline__ void attend_heads(const float* q, RowFn krow, int vof
       sum += p;
     }
     sum = group_sum<64>(sum);
+    if (lse && lane == 0) lse[h * ldl] = mx + logf(sum);
     const float inv = 1.0f / sum;
-    for (int i = lane; i < n; i += 64) ph[i] *= inv;
-    // the wave's own writes to ph are read back by other lanes below
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float acc = 0.f;
-    for (int i = jg; i < n; i += JG) {
-      const float* vr = krow(i) + voff + h * DH + c;
-      acc = fmaf(ph[i], AGENT ? ld_agent(vr) : *vr, acc);
+    float acc[DH];
+#pragma unroll
+    for (int c = 0; c < DH; ++c) acc[c] = 0.f;
+    for (int i = lane; i < n; i += 64) {
+      const float p = ph[i] * inv;
+      ph[i] = p;
+      const float4* vr = reinterpret_cast<const float4*>(krow(i) + voff + h * DH);
+#pragma unroll
+      for (int c4 = 0; c4 < DH / 4; ++c4) {
+        const float4 v = vr[c4];
+        acc[4 * c4] = fmaf(p, v.x, acc[4 * c4]);
+        acc[4 * c4 + 1] = fmaf(p, v.y, acc[4 * c4 + 1]);
+        acc[4 * c4 + 2] = fmaf(p, v.z, acc[4 * c4 + 2]);
+        acc[4 * c4 + 3] = fmaf(p, v.w, acc[4 * c4 + 3]);
+      }
     }
-    for (int off = DH; off < 64; off *= 2) acc += __shfl_xor(acc, off, 64);
-    if (jg == 0) out[h * DH + c] = acc;
+#pragma unroll
+    for (int c = 0; c < DH; ++c) {
+      const float v = group_sum<64>(acc[c]);
+      if (lane == c % 64) out[h * DH + c] = v;
+    }
   }
   __syncthreads();
 }
 
-// Adjoint of attend_heads for the query side: with P and dout (LDS), per head
+// Adjoint of attend_heads for the query side: with P and dout (LDS), per head (one lane per row)
 // dz_i = p_i (dout.v_i - sum_j p_j dout.v_j) into Z[h * ldp + i], and dq (LDS) = scale sum_i dz_i k_i.
-template <typename RowFn>
+template <int DH, typename RowFn>
 __device__ __forceinline__ void attend_heads_bwd(const float* P, const float* dout, RowFn krow, int voff, int n, int H,
-                                                 int DH, float scale, float* Z, int ldp, float* dq) {
+                                                 float scale, float* Z, int ldp, float* dq) {
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int JG = 64 / DH, c = lane % DH, jg = lane / DH;
   for (int h = wave; h < H; h += 4) {
     const float* ph = P + h * ldp;
     float* zh = Z + h * ldp;
+    float gh[DH];
+#pragma unroll
+    for (int c = 0; c < DH; ++c) gh[c] = dout[h * DH + c];
     float sdp = 0.f;
     for (int i = lane; i < n; i += 64) {
-      const float* vr = krow(i) + voff + h * DH;
+      const float4* vr = reinterpret_cast<const float4*>(krow(i) + voff + h * DH);
       float dp = 0.f;
-      for (int cc = 0; cc < DH; ++cc) dp = fmaf(dout[h * DH + cc], vr[cc], dp);
+#pragma unroll
+      for (int c4 = 0; c4 < DH / 4; ++c4) {
+        const float4 v = vr[c4];
+        dp = fmaf(gh[4 * c4], v.x, dp);
+        dp = fmaf(gh[4 * c4 + 1], v.y, dp);
+        dp = fmaf(gh[4 * c4 + 2], v.z, dp);
+        dp = fmaf(gh[4 * c4 + 3], v.w, dp);
+      }
       zh[i] = dp;
       sdp = fmaf(ph[i], dp, sdp);
     }
     sdp = group_sum<64>(sdp);
-    for (int i = lane; i < n; i += 64) zh[i] = ph[i] * (zh[i] - sdp);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float acc = 0.f;
-    for (int i = jg; i < n; i += JG) acc = fmaf(zh[i], krow(i)[h * DH + c], acc);
-    for (int off = DH; off < 64; off *= 2) acc += __shfl_xor(acc, off, 64);
-    if (jg == 0) dq[h * DH + c] = acc * scale;
+    float acc[DH];
+#pragma unroll
+    for (int c = 0; c < DH; ++c) acc[c] = 0.f;
+    for (int i = lane; i < n; i += 64) {
+      const float z = ph[i] * (zh[i] - sdp);
+      zh[i] = z;
+      const float4* kr = reinterpret_cast<const float4*>(krow(i) + h * DH);
+#pragma unroll
+      for (int c4 = 0; c4 < DH / 4; ++c4) {
+        const float4 k = kr[c4];
+        acc[4 * c4] = fmaf(z, k.x, acc[4 * c4]);
+        acc[4 * c4 + 1] = fmaf(z, k.y, acc[4 * c4 + 1]);
+        acc[4 * c4 + 2] = fmaf(z, k.z, acc[4 * c4 + 2]);
+        acc[4 * c4 + 3] = fmaf(z, k.w, acc[4 * c4 + 3]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < DH; ++c) {
+      const float v = group_sum<64>(acc[c]);
+      if (lane == c % 64) dq[h * DH + c] = v * scale;
+    }
   }
   __syncthreads();
 }
@@ -610,25 +699,28 @@ __device__ __forceinline__ void attend_heads_bwd(const float* P, const float* do
 // TAPE: the tape pass (computes k, v and writes them to KVT; reads earlier window rows at agent
 // scope); otherwise k, v come from the tape.  Ends with m.y2 and the FFN pre-activation m.u /
 // activation m.act computed; the caller adds the FFN output.
-template <bool TAPE>
+template <bool TAPE, int DH>
 __device__ void layer_fwd(const DecArgs& a, float* sm, const DecLds& m, int b, int t, int l) {
-  const int D = a.D, H = a.H, DH = a.DH, W = a.W;
+  const int D = a.D, H = a.H, W = a.W;
   const size_t R = static_cast<size_t>(a.B) * a.T, r = static_cast<size_t>(b) * a.T + t;
   float* red = sm + m.total;
   const float* P = a.P;
   rms_vec(sm + m.y, P + a.o.g_dec_self + l * D, sm + m.h, D, a.eps, red);
   const size_t dd = static_cast<size_t>(D) * D;
-  matvec(a.WT + a.ot.wq + l * dd, D, D, sm + m.h, sm + m.q);
+  matvec(a.P + a.o.wq + l * dd, D, D, sm + m.h, sm + m.q);
   float* kvt = a.KVT + static_cast<size_t>(l) * R * 2 * D;
   if (TAPE) {
-    matvec(a.WT + a.ot.wk + l * dd, D, D, sm + m.h, sm + m.k);
-    matvec(a.WT + a.ot.wv + l * dd, D, D, sm + m.h, sm + m.v);
+    matvec(a.P + a.o.wk + l * dd, D, D, sm + m.h, sm + m.k);
+    matvec(a.P + a.o.wv + l * dd, D, D, sm + m.h, sm + m.v);
     __syncthreads();
     for (int c = threadIdx.x; c < D; c += NT) {
       kvt[r * 2 * D + c] = sm[m.k + c];
       kvt[r * 2 * D + D + c] = sm[m.v + c];
     }
-    // the window below reads this row back through other waves
+    // The window below reads this row back through other waves with ordinary loads.  That is
+    // safe because the row's stores complete before the workgroup barrier (vmcnt(0)) and no
+    // wave of this launch has read the row's cache lines before (rows are 256-byte aligned and
+    // only positions <= t are read), so no stale line can sit in the CU's cache.
     wait_stores();
   } else {
     for (int c = threadIdx.x; c < D; c += NT) {
@@ -640,31 +732,32 @@ __device__ void layer_fwd(const DecArgs& a, float* sm, const DecLds& m, int b, i
   // window: positions j0 .. t, every row (the current one included) from the tape
   const int j0 = max(0, t - W + 1), n = t - j0 + 1;
   auto wrow = [&](int i) -> const float* { return kvt + (static_cast<size_t>(b) * a.T + j0 + i) * 2 * D; };
-  attend_heads<TAPE>(sm + m.q, wrow, D, n, H, DH, a.scale, sm + m.pw, W, sm + m.o);
-  matvec(a.WT + a.ot.wo + l * dd, D, D, sm + m.o, sm + m.y1);
+  attend_heads<DH>(sm + m.q, wrow, D, n, H, a.scale, sm + m.pw, W, sm + m.o);
+  matvec(a.P + a.o.wo + l * dd, D, D, sm + m.o, sm + m.y1);
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += NT) sm[m.y1 + c] += sm[m.y + c];
   __syncthreads();
   rms_vec(sm + m.y1, P + a.o.g_dec_cross + l * D, sm + m.h2, D, a.eps, red);
-  matvec(a.WT + a.ot.wqx + l * dd, D, D, sm + m.h2, sm + m.qx);
+  matvec(a.P + a.o.wqx + l * dd, D, D, sm + m.h2, sm + m.qx);
   __syncthreads();
   const int g = a.G == 1 ? 0 : l;
   const float* mkv = a.MKV + (static_cast<size_t>(g) * R + static_cast<size_t>(b) * a.T) * 2 * D;
   auto mrow = [&](int i) -> const float* { return mkv + static_cast<size_t>(i) * 2 * D; };
-  attend_heads<false>(sm + m.qx, mrow, D, t + 1, H, DH, a.scale, sm + m.pc, a.T, sm + m.o2);
-  matvec(a.WT + a.ot.wox + l * dd, D, D, sm + m.o2, sm + m.y2);
+  float* clse = TAPE ? nullptr : a.CLSE + ((static_cast<size_t>(l) * a.B + b) * H) * a.T + t;
+  attend_heads<DH>(sm + m.qx, mrow, D, t + 1, H, a.scale, sm + m.pc, a.T, sm + m.o2, clse, a.T);
+  matvec(a.P + a.o.wox + l * dd, D, D, sm + m.o2, sm + m.y2);
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += NT) sm[m.y2 + c] += sm[m.y1 + c];
   __syncthreads();
   rms_vec(sm + m.y2, P + a.o.g_dec_ffn + l * D, sm + m.h3, D, a.eps, red);
   const size_t fd = static_cast<size_t>(a.F) * D;
   if (a.swiglu) {
-    matvec(a.WT + a.ot.f1 + l * fd, a.F, D, sm + m.h3, sm + m.u);
-    matvec(a.WT + a.ot.f2 + l * fd, a.F, D, sm + m.h3, sm + m.u + a.F);
+    matvec(a.P + a.o.f1 + l * fd, a.F, D, sm + m.h3, sm + m.u);
+    matvec(a.P + a.o.f2 + l * fd, a.F, D, sm + m.h3, sm + m.u + a.F);
     __syncthreads();
     for (int f = threadIdx.x; f < a.F; f += NT) sm[m.act + f] = silu_f(sm[m.u + f]) * sm[m.u + a.F + f];
   } else {
-    matvec(a.WT + a.ot.f1 + l * fd, a.F, D, sm + m.h3, sm + m.u);
+    matvec(a.P + a.o.f1 + l * fd, a.F, D, sm + m.h3, sm + m.u);
     __syncthreads();
     for (int f = threadIdx.x; f < a.F; f += NT) sm[m.act + f] = gelu_erf(sm[m.u + f]);
   }
@@ -685,10 +778,10 @@ __device__ void merge_fwd(const DecArgs& a, float* sm, const DecLds& m, size_t r
   const int D = a.D;
   for (int c = threadIdx.x; c < D; c += NT) sm[m.e + c] = a.E[r * D + c];
   __syncthreads();
-  matvec(a.WT + a.ot.w_fb, D, D, sm + m.s, sm + m.f);
-  matvec(a.WT + a.ot.w_ge, D, D, sm + m.e, sm + m.gate);
+  matvec(a.P + a.o.w_fb, D, D, sm + m.s, sm + m.f);
+  matvec(a.P + a.o.w_ge, D, D, sm + m.e, sm + m.gate);
   __syncthreads();
-  matvec(a.WT + a.ot.w_gs, D, D, sm + m.s, sm + m.gate, true);
+  matvec(a.P + a.o.w_gs, D, D, sm + m.s, sm + m.gate, true);
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += NT) {
     const float gt = sigmoid_f(sm[m.gate + c] + a.P[a.o.b_g + c]);
@@ -698,6 +791,7 @@ __device__ void merge_fwd(const DecArgs& a, float* sm, const DecLds& m, size_t r
   __syncthreads();
 }
 
+template <int DH>
 __global__ __launch_bounds__(NT) void dec_tape_k(DecArgs a) {
   extern __shared__ float sm[];
   const int b = blockIdx.x, D = a.D, L = a.L;
@@ -711,8 +805,8 @@ __global__ __launch_bounds__(NT) void dec_tape_k(DecArgs a) {
     merge_fwd(a, sm, m, r);
     for (int l = 0; l < L; ++l) {
       for (int c = threadIdx.x; c < D; c += NT) a.YT[(r * (L + 1) + l) * D + c] = sm[m.y + c];
-      layer_fwd<true>(a, sm, m, b, t, l);
-      matvec(ffn_out_t(a, l), D, a.F, sm + m.act, sm + m.y);
+      layer_fwd<true, DH>(a, sm, m, b, t, l);
+      matvec(ffn_out_w(a, l), D, a.F, sm + m.act, sm + m.y);
       __syncthreads();
       for (int c = threadIdx.x; c < D; c += NT) sm[m.y + c] += sm[m.y2 + c];
       __syncthreads();
@@ -726,9 +820,10 @@ __global__ __launch_bounds__(NT) void dec_tape_k(DecArgs a) {
   }
 }
 
+template <int DH>
 __global__ __launch_bounds__(NT) void dec_sweep_k(DecArgs a) {
   extern __shared__ float sm[];
-  const int b = blockIdx.x, D = a.D, L = a.L, H = a.H, W = a.W, DH = a.DH;
+  const int b = blockIdx.x, D = a.D, L = a.L, H = a.H, W = a.W;
   const DecLds m(D, a.F, a.F2, a.H, a.W, a.T);
   float* red = sm + m.total;
   float* gacc = red + 8;   // [g_dec_self L D][g_dec_cross L D][g_dec_ffn L D][g_dec_final D][b_g D][s* D]
@@ -752,14 +847,14 @@ __global__ __launch_bounds__(NT) void dec_sweep_k(DecArgs a) {
       const size_t rl = static_cast<size_t>(l) * R + r;
       for (int c = threadIdx.x; c < D; c += NT) sm[m.y + c] = a.YT[(r * (L + 1) + l) * D + c];
       __syncthreads();
-      layer_fwd<false>(a, sm, m, b, t, l);
+      layer_fwd<false, DH>(a, sm, m, b, t, l);
       // FFN sub-block: y3 = y2 + W2 act(u), u from h3
       for (int c = threadIdx.x; c < D; c += NT) {
         a.DY3[rl * D + c] = sm[m.dy + c];
         a.H3[rl * D + c] = sm[m.h3 + c];
       }
       for (int f = threadIdx.x; f < a.F; f += NT) a.ACT[rl * a.F + f] = sm[m.act + f];
-      matvec_t(ffn_out_w(a, l), D, a.F, sm + m.dy, sm + m.dact);
+      matvec_t(ffn_out_t(a, l), D, a.F, sm + m.dy, sm + m.dact);
       __syncthreads();
       const size_t fd = static_cast<size_t>(a.F) * D;
       if (a.swiglu) {
@@ -769,13 +864,13 @@ __global__ __launch_bounds__(NT) void dec_sweep_k(DecArgs a) {
           sm[m.du + a.F + f] = da * silu_f(gt);
         }
         __syncthreads();
-        matvec_t(a.P + a.o.f1 + l * fd, a.F, D, sm + m.du, sm + m.dh);
+        matvec_t(a.WT + a.ot.f1 + l * fd, a.F, D, sm + m.du, sm + m.dh);
         __syncthreads();
-        matvec_t(a.P + a.o.f2 + l * fd, a.F, D, sm + m.du + a.F, sm + m.dh, true);
+        matvec_t(a.WT + a.ot.f2 + l * fd, a.F, D, sm + m.du + a.F, sm + m.dh, true);
       } else {
         for (int f = threadIdx.x; f < a.F; f += NT) sm[m.du + f] = sm[m.dact + f] * gelu_grad(sm[m.u + f]);
         __syncthreads();
-        matvec_t(a.P + a.o.f1 + l * fd, a.F, D, sm + m.du, sm + m.dh);
+        matvec_t(a.WT + a.ot.f1 + l * fd, a.F, D, sm + m.du, sm + m.dh);
       }
       for (int f = threadIdx.x; f < a.F2; f += NT) a.DU[rl * a.F2 + f] = sm[m.du + f];
       __syncthreads();
@@ -786,25 +881,23 @@ __global__ __launch_bounds__(NT) void dec_sweep_k(DecArgs a) {
         a.DY2[rl * D + c] = sm[m.dy + c];
         a.O2[rl * D + c] = sm[m.o2 + c];
       }
-      matvec_t(a.P + a.o.wox + l * dd, D, D, sm + m.dy, sm + m.dvec);
+      matvec_t(a.WT + a.ot.wox + l * dd, D, D, sm + m.dy, sm + m.dvec);
       __syncthreads();
       const int g = a.G == 1 ? 0 : l;
       const float* mkv = a.MKV + (static_cast<size_t>(g) * R + static_cast<size_t>(b) * a.T) * 2 * D;
       auto mrow = [&](int i) -> const float* { return mkv + static_cast<size_t>(i) * 2 * D; };
-      attend_heads_bwd(sm + m.pc, sm + m.dvec, mrow, D, t + 1, H, DH, a.scale, sm + m.pc2, a.T, sm + m.dq);
-      if (!(a.detach & 4)) {
-        float* dm = a.DM + (static_cast<size_t>(g) * R + static_cast<size_t>(b) * a.T) * 2 * D;
-        for (int e = threadIdx.x; e < (t + 1) * D; e += NT) {
-          const int j = e / D, c = e % D, h = c / DH;
-          dm[static_cast<size_t>(j) * 2 * D + c] += sm[m.pc2 + h * a.T + j] * sm[m.qx + c] * a.scale;
-          dm[static_cast<size_t>(j) * 2 * D + D + c] += sm[m.pc + h * a.T + j] * sm[m.dvec + c];
-        }
+      attend_heads_bwd<DH>(sm + m.pc, sm + m.dvec, mrow, D, t + 1, H, a.scale, sm + m.pc2, a.T, sm + m.dq);
+      // the memory rows' adjoints are formed after the sweep, token-parallel, from q_x, this
+      // output adjoint and the row log-sum-exp
+      for (int c = threadIdx.x; c < D; c += NT) {
+        a.QXS[rl * D + c] = sm[m.qx + c];
+        a.DO2S[rl * D + c] = sm[m.dvec + c];
       }
       for (int c = threadIdx.x; c < D; c += NT) {
         a.DQX[rl * D + c] = sm[m.dq + c];
         a.H2[rl * D + c] = sm[m.h2 + c];
       }
-      matvec_t(a.P + a.o.wqx + l * dd, D, D, sm + m.dq, sm + m.dh);
+      matvec_t(a.WT + a.ot.wqx + l * dd, D, D, sm + m.dq, sm + m.dh);
       __syncthreads();
       rms_vec_bwd(sm + m.y1, a.P + a.o.g_dec_cross + l * D, sm + m.dh, sm + m.dy, gacc + (L + l) * D, D, a.eps, red);
       // window self-attention sub-block: y1 = y + W_O attn(q over window rows j0..t)
@@ -812,12 +905,12 @@ __global__ __launch_bounds__(NT) void dec_sweep_k(DecArgs a) {
         a.DY1[rl * D + c] = sm[m.dy + c];
         a.O1[rl * D + c] = sm[m.o + c];
       }
-      matvec_t(a.P + a.o.wo + l * dd, D, D, sm + m.dy, sm + m.dvec);
+      matvec_t(a.WT + a.ot.wo + l * dd, D, D, sm + m.dy, sm + m.dvec);
       __syncthreads();
       const int j0 = max(0, t - W + 1), n = t - j0 + 1;
       const float* kvt = a.KVT + static_cast<size_t>(l) * R * 2 * D;
       auto wrow = [&](int i) -> const float* { return kvt + (static_cast<size_t>(b) * a.T + j0 + i) * 2 * D; };
-      attend_heads_bwd(sm + m.pw, sm + m.dvec, wrow, D, n, H, DH, a.scale, sm + m.pw2, W, sm + m.dq);
+      attend_heads_bwd<DH>(sm + m.pw, sm + m.dvec, wrow, D, n, H, a.scale, sm + m.pw2, W, sm + m.dq);
       // window key/value adjoints: slot j mod W of this layer's ring; each (slot, column) element
       // is always handled by the same thread, so its read-modify-writes stay in program order
       float* ring = a.RING + (static_cast<size_t>(l) * a.B + b) * W * 2 * D;
@@ -846,11 +939,11 @@ __global__ __launch_bounds__(NT) void dec_sweep_k(DecArgs a) {
         a.DQKV[rl * 3 * D + 2 * D + c] = sm[m.dv + c];
         a.H1[rl * D + c] = sm[m.h + c];
       }
-      matvec_t(a.P + a.o.wq + l * dd, D, D, sm + m.dq, sm + m.dh);
+      matvec_t(a.WT + a.ot.wq + l * dd, D, D, sm + m.dq, sm + m.dh);
       __syncthreads();
-      matvec_t(a.P + a.o.wk + l * dd, D, D, sm + m.dk, sm + m.dh, true);
+      matvec_t(a.WT + a.ot.wk + l * dd, D, D, sm + m.dk, sm + m.dh, true);
       __syncthreads();
-      matvec_t(a.P + a.o.wv + l * dd, D, D, sm + m.dv, sm + m.dh, true);
+      matvec_t(a.WT + a.ot.wv + l * dd, D, D, sm + m.dv, sm + m.dh, true);
       __syncthreads();
       rms_vec_bwd(sm + m.y, a.P + a.o.g_dec_self + l * D, sm + m.dh, sm + m.dy, gacc + l * D, D, a.eps, red);
     }
@@ -869,10 +962,10 @@ __global__ __launch_bounds__(NT) void dec_sweep_k(DecArgs a) {
       gacc[(3 * L + 1) * D + c] += da;
     }
     __syncthreads();
-    matvec_t(a.P + a.o.w_ge, D, D, sm + m.dq, sm + m.dh);
-    matvec_t(a.P + a.o.w_fb, D, D, sm + m.dk, sm + m.ds);
+    matvec_t(a.WT + a.ot.w_ge, D, D, sm + m.dq, sm + m.dh);
+    matvec_t(a.WT + a.ot.w_fb, D, D, sm + m.dk, sm + m.ds);
     __syncthreads();
-    matvec_t(a.P + a.o.w_gs, D, D, sm + m.dq, sm + m.ds, true);
+    matvec_t(a.WT + a.ot.w_gs, D, D, sm + m.dq, sm + m.ds, true);
     __syncthreads();
     for (int c = threadIdx.x; c < D; c += NT) {
       a.DE[r * D + c] = sm[m.dv + c] + sm[m.dh + c];
@@ -898,7 +991,7 @@ __global__ void part_reduce_k(const float* part, int B, int NP, int src, int n, 
 // ---------------------------------------------------------------------------------------------
 struct BpLayout {
   size_t X, XMID, E, MKV, YT, KVT, S, SPREV, Z, DS, LOSSR, ERR;
-  size_t DQKV, H1, DY1, O1, DQX, H2, DY2, O2, DU, H3, DY3, ACT, DA, DF, DE, DM, RING, PART;
+  size_t DQKV, H1, DY1, O1, DQX, H2, DY2, O2, DU, H3, DY3, ACT, QXS, DO2S, CLSE, DA, DF, DE, DM, RING, PART;
   size_t DX, HF, U, EACT, DACT, DUE, DHF, HA, QKV, O, LSE, DSUM, DO, DQKVE, DHA, GROWS, COLP, WT, GP;
   size_t gp_floats, total;   // floats
 };
@@ -923,6 +1016,7 @@ BpLayout bp_layout(const rlt_config& c, int B, int T) {
   b.DQKV = take(L * R * 3 * D); b.H1 = take(L * R * D); b.DY1 = take(L * R * D); b.O1 = take(L * R * D);
   b.DQX = take(L * R * D); b.H2 = take(L * R * D); b.DY2 = take(L * R * D); b.O2 = take(L * R * D);
   b.DU = take(L * R * F2); b.H3 = take(L * R * D); b.DY3 = take(L * R * D); b.ACT = take(L * R * F);
+  b.QXS = take(L * R * D); b.DO2S = take(L * R * D); b.CLSE = take(L * B * H * T);
   b.DA = take(R * D); b.DF = take(R * D); b.DE = take(R * D); b.DM = take(G * R * 2 * D);
   b.RING = take(L * B * W * 2 * D); b.PART = take(static_cast<size_t>(B) * (3 * L + 3) * D);
   b.DX = take(R * D); b.HF = take(R * D); b.U = take(R * F2); b.EACT = take(R * F); b.DACT = take(R * F);
@@ -1001,7 +1095,11 @@ void launch_enc_attn(int which, const float* QKV, const float* O, const float* d
   const dim3 grid((T + 63) / 64, H, B);
   if (which == 0) enc_attn_fwd_k<DH><<<grid, 64, 0, st>>>(QKV, out, LSE, T, H, D, scale);
   else if (which == 1) enc_attn_bwd_q_k<DH><<<grid, 64, 0, st>>>(QKV, O, dO, LSE, Dsum, out, T, H, D, scale);
-  else enc_attn_bwd_kv_k<DH><<<grid, 64, 0, st>>>(QKV, dO, LSE, Dsum, out, T, H, D, scale);
+  else {
+    KvArgs k{QKV, 3LL * D, QKV + D, QKV + 2 * D, 3LL * D, dO, D, LSE, Dsum, out + D, out + 2 * D, 3LL * D, T, H, 0,
+             scale};
+    attn_bwd_kv_k<DH><<<grid, 64, 0, st>>>(k);
+  }
 }
 hipError_t enc_attn(int which, const float* QKV, const float* O, const float* dO, float* LSE, float* Dsum, float* out,
                     int B, int T, int H, int D, hipStream_t st) {
@@ -1010,6 +1108,30 @@ hipError_t enc_attn(int which, const float* QKV, const float* O, const float* dO
   if (DH == 16) launch_enc_attn<16>(which, QKV, O, dO, LSE, Dsum, out, B, T, H, D, scale, st);
   else if (DH == 32) launch_enc_attn<32>(which, QKV, O, dO, LSE, Dsum, out, B, T, H, D, scale, st);
   else launch_enc_attn<64>(which, QKV, O, dO, LSE, Dsum, out, B, T, H, D, scale, st);
+  return hipGetLastError();
+}
+
+template <int DH>
+hipError_t dec_launch_dh(int which, const DecArgs& a, int B, size_t lds, hipStream_t st) {
+  const void* fn = which == 0 ? reinterpret_cast<const void*>(&dec_tape_k<DH>)
+                              : reinterpret_cast<const void*>(&dec_sweep_k<DH>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  if (which == 0) dec_tape_k<DH><<<B, NT, lds, st>>>(a);
+  else dec_sweep_k<DH><<<B, NT, lds, st>>>(a);
+  return hipGetLastError();
+}
+hipError_t dec_launch(int which, int DH, const DecArgs& a, int B, size_t lds, hipStream_t st) {
+  if (DH == 16) return dec_launch_dh<16>(which, a, B, lds, st);
+  if (DH == 32) return dec_launch_dh<32>(which, a, B, lds, st);
+  return dec_launch_dh<64>(which, a, B, lds, st);
+}
+
+hipError_t attn_kv(const KvArgs& k, int B, int DH, hipStream_t st) {
+  const dim3 grid((k.T + 63) / 64, k.H, B);
+  if (DH == 16) attn_bwd_kv_k<16><<<grid, 64, 0, st>>>(k);
+  else if (DH == 32) attn_bwd_kv_k<32><<<grid, 64, 0, st>>>(k);
+  else attn_bwd_kv_k<64><<<grid, 64, 0, st>>>(k);
   return hipGetLastError();
 }
 
@@ -1136,14 +1258,12 @@ hipError_t run_bptt(const rlt_config& c, const BpttOffsets& o, const float* w, c
   a.SPREV = ws + lay.SPREV; a.DS = ws + lay.DS;
   a.DQKV = ws + lay.DQKV; a.H1 = ws + lay.H1; a.DY1 = ws + lay.DY1; a.O1 = ws + lay.O1; a.DQX = ws + lay.DQX;
   a.H2 = ws + lay.H2; a.DY2 = ws + lay.DY2; a.O2 = ws + lay.O2; a.DU = ws + lay.DU; a.H3 = ws + lay.H3;
-  a.DY3 = ws + lay.DY3; a.ACT = ws + lay.ACT; a.DA = ws + lay.DA; a.DF = ws + lay.DF; a.DE = ws + lay.DE;
+  a.DY3 = ws + lay.DY3; a.ACT = ws + lay.ACT; a.QXS = ws + lay.QXS; a.DO2S = ws + lay.DO2S; a.CLSE = ws + lay.CLSE;
+  a.DA = ws + lay.DA; a.DF = ws + lay.DF; a.DE = ws + lay.DE;
   a.DM = ws + lay.DM; a.RING = ws + lay.RING; a.PART = ws + lay.PART;
   const size_t lds = static_cast<size_t>(dec_lds_floats(c, T)) * 4;
-  BP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&dec_tape_k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(lds)));
-  BP_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&dec_sweep_k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(lds)));
-  dec_tape_k<<<B, NT, lds, st>>>(a);
+  const int DHd = D / H;
+  BP_TRY(dec_launch(0, DHd, a, B, lds, st));
   BP_TRY(hipGetLastError());
 
   // 3. logits, loss, dS and dW_out
@@ -1156,7 +1276,7 @@ hipError_t run_bptt(const rlt_config& c, const BpttOffsets& o, const float* w, c
   BP_TRY(gemm_wgrad(x, ws + lay.Z, V, ws + lay.S, D, gr + o.w_out, V, D, R));
 
   // 4. reverse sweep
-  dec_sweep_k<<<B, NT, lds, st>>>(a);
+  BP_TRY(dec_launch(1, DHd, a, B, lds, st));
   BP_TRY(hipGetLastError());
   {
     const int NP = (3 * L + 3) * D;
@@ -1165,6 +1285,25 @@ hipError_t run_bptt(const rlt_config& c, const BpttOffsets& o, const float* w, c
     part_reduce_k<<<(D + 255) / 256, 256, 0, st>>>(ws + lay.PART, B, NP, ng, D, gr + o.b_g);
     part_reduce_k<<<(D + 255) / 256, 256, 0, st>>>(ws + lay.PART, B, NP, ng + D, D, gr + o.s_star);
     BP_TRY(hipGetLastError());
+  }
+
+  // memory-row adjoints of every layer's cross-attention, token-parallel (queries t attend rows j <= t)
+  if (!(detach & 4)) {
+    const int DH = D / H;
+    for (int l = 0; l < L; ++l) {
+      const size_t rl = static_cast<size_t>(l) * R;
+      const int g = G == 1 ? 0 : l;
+      const size_t n = static_cast<size_t>(B) * H * T;
+      head_dots_k<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(ws + lay.DO2S + rl * D, ws + lay.O2 + rl * D,
+                                                                            D, B, T, H, DH, ws + lay.DSUM);
+      BP_TRY(hipGetLastError());
+      const float* mkv = ws + lay.MKV + static_cast<size_t>(g) * RD * 2;
+      float* dm = ws + lay.DM + static_cast<size_t>(g) * RD * 2;
+      KvArgs k{ws + lay.QXS + rl * D, D, mkv, mkv + D, 2LL * D, ws + lay.DO2S + rl * D, D,
+               ws + lay.CLSE + static_cast<size_t>(l) * B * H * T, ws + lay.DSUM, dm, dm + D, 2LL * D, T, H, 1,
+               a.scale};
+      BP_TRY(attn_kv(k, B, DH, st));
+    }
   }
 
   // 5. decoder weight gradients over all rows
