@@ -647,6 +647,32 @@ def small_leg(steps: int, warmup: int, bw, with_cpu: bool = True):
     return out
 
 
+def algorithmic_bptt_bytes(cfg, B: int, T: int) -> float:
+    """HBM bytes the two sequential decoder kernels of the backward must move (fp32), the
+    schedule of the tape pass, the recomputing sweep and its saved rows:
+      tape, per step t: weights once (P_loop elements), the window rows (min(t, W-1) + 1) and the
+        memory rows 1..t of every layer (keys and values), the tape written (layer inputs,
+        window entry, s_t, s_{t-1}) and e_t read;
+      sweep, per step: weights twice (W for the recompute, W^T for the adjoints), the window and
+        memory rows twice (recompute; value rows for the output adjoint and key rows for the query
+        adjoint), the tape read back, the saved rows of every product written
+        (14 d + FFN_in + F per layer: product inputs and output adjoints), the merge adjoints and
+        the logit adjoint of s_t.
+    The token-parallel parts (encoder, logits, weight gradients) are not counted, so the rate
+    derived from a whole call is conservative."""
+    p = 4
+    d, L, F, W = cfg.d_model, cfg.n_layers, cfg.ffn_dim, cfg.window
+    f_in = 2 * F if cfg.ffn_kind == "swiglu" else F
+    p_loop = L * (6 * d * d + (3 if cfg.ffn_kind == "swiglu" else 2) * F * d) + 3 * d * d
+    sum_mem = T * (T + 1) / 2.0
+    sum_win = sum(min(t, W - 1) + 1 for t in range(T))
+    rows = B * L * 2 * d * p * (sum_win + sum_mem)
+    tape = T * p_loop * p + rows + B * T * ((L + 1) * d + L * 2 * d + 3 * d) * p
+    sweep = (2 * T * p_loop * p + 2 * rows + B * T * ((L + 1) * d + L * 2 * d) * p
+             + B * T * L * (14 * d + f_in + F) * p + B * T * 4 * d * p)
+    return float(tape + sweep)
+
+
 def bptt_leg(steps: int, warmup: int, with_cpu: bool = True):
     """Full-BPTT backward of the small workload (d=64, 4+4 layers, W=32, G=L, V=512, B=64,
     T=1024): one call = encoder and decoder forward with the tape, loss, reverse sweep and every
@@ -692,6 +718,11 @@ def bptt_leg(steps: int, warmup: int, with_cpu: bool = True):
         "ms_per_call": avg,
         "ms_min": float(np.min(ms)),
         "tokens_per_s": B * T / (avg * 1e-3),
+        "roofline": hbm_roofline(algorithmic_bptt_bytes(cfg, B, T), avg, None,
+                                 "rlt_bptt whole call (dec_sweep_k and dec_tape_k dominant: one workgroup per "
+                                 "sequence, a latency-bound chain per step)",
+                                 algorithmic_bytes=algorithmic_bptt_bytes(cfg, B, T),
+                                 unit_of_work="one backward over B x T tokens"),
         "loss_mean_per_token": float(loss.sum().item()) / (B * (T - 1)),
         "workspace_GB": ws.numel() / 1e9,
     }
@@ -827,6 +858,7 @@ def main():
         if not args.no_scoring:
             line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
             line["sampling"] = sampling_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
+        line["bptt"] = bptt_leg(3, 1, not args.no_cpu_baseline)
     print(json.dumps(line), flush=True)
 
 

@@ -77,7 +77,8 @@ def oracle_bptt(cfg, weights: Dict[str, np.ndarray], tokens: np.ndarray, masks: 
     """(per-sequence losses [nb], summed gradients {name: array}) of the fp64 backward oracle over
     the chosen sequences, computed in spawned worker processes."""
     seqs = list(range(tokens.shape[0])) if seqs is None else list(seqs)
-    jobs = [(cfg, weights, tokens[b], None if masks is None else masks[b], tuple(detach)) for b in seqs]
+    # masks, when given, has one row per chosen sequence
+    jobs = [(cfg, weights, tokens[b], None if masks is None else masks[i], tuple(detach)) for i, b in enumerate(seqs)]
     if workers is None:
         workers = min(len(jobs), 8, len(os.sched_getaffinity(0)))
     if workers <= 1 or len(jobs) == 1:

@@ -150,3 +150,20 @@ def test_bptt_errors():
     loss, _ = rlt.rlt_bptt(c, wf, bad)
     torch.cuda.synchronize()
     assert torch.isnan(loss).all()
+
+
+def test_bptt_small_workload_full_size_sampled_sequences():
+    """The small workload at its full size (B=64, T=1024, its own seeded weights and tokens), the
+    launch configuration the bench times; the mask supervises sequences 0 and 63 only, so the
+    gradient is the oracle's for those two sequences (the other 62 contribute exact zeros)."""
+    wl = CONFIGS["small"]
+    cfg, B, T = wl.model, wl.batch, wl.seq_len
+    w = make_weights(cfg, wl.weight_seed)
+    tokens = make_tokens(cfg.vocab, B, T, wl.token_dist, wl.token_seed)
+    masks = np.zeros((B, T - 1))
+    masks[0] = 1.0
+    masks[B - 1] = 1.0
+    loss, grads = run_gpu(cfg, w, tokens, masks)
+    ref_loss, ref_grads = oracle_bptt(cfg, w, tokens, masks[[0, B - 1]], seqs=[0, B - 1])
+    assert np.all(loss[1:B - 1] == 0.0)
+    compare("small full size, sequences 0 and 63", loss[[0, B - 1]], grads, ref_loss, ref_grads)

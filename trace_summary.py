@@ -1,6 +1,9 @@
 """Summarise a rocprofv3 kernel trace of the batched decoder as per-kernel statistics.
 
     python trace_summary.py <kernel_trace.csv> [--from-step S] [--title TEXT] [--command TEXT] > out.md
+    python trace_summary.py --stats <kernel_stats.csv> [--title TEXT] [--command TEXT] [--note TEXT] > out.md
+
+The second form renders the `--stats` table rocprofv3 writes (kernel_stats.csv) as markdown.
 
 The batched decoder ends every step with one final_norm_ssp_k (or final_norm_k) dispatch, so
 --from-step S keeps only the dispatches after the S-th of those: the steps S+1 .. of the
@@ -46,13 +49,41 @@ def roles(seq):
     return out
 
 
+def header(w, title, command, note=""):
+    w(f"# {title}\n\n")
+    if command:
+        w("Command (on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
+        for line in command.split(";"):
+            w(f"    {line.strip()}\n")
+        w("\n")
+    if note:
+        w(note.strip() + "\n\n")
+
+
+def stats_table(path, title, command, note):
+    rows = list(csv.DictReader(open(path)))
+    w = sys.stdout.write
+    header(w, title, command, note)
+    w("| kernel | calls | avg us | total ms | % |\n|---|---:|---:|---:|---:|\n")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = short_name(r["Name"])
+        if len(name) > 90:
+            name = name[:87] + "..."
+        w(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+          f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("trace")
+    ap.add_argument("trace", nargs="?")
+    ap.add_argument("--stats", help="a rocprofv3 kernel_stats.csv to render instead of a trace")
     ap.add_argument("--from-step", type=int, default=0)
     ap.add_argument("--title", default="Kernel trace statistics")
     ap.add_argument("--command", default="")
+    ap.add_argument("--note", default="")
     args = ap.parse_args()
+    if args.stats:
+        return stats_table(args.stats, args.title, args.command, args.note)
     seq = []
     with open(args.trace) as f:
         for r in csv.DictReader(f):
@@ -75,12 +106,7 @@ def main():
     total = sum(sum(v) for v in stats.values())
     span = (seq[-1][2] - seq[0][1]) if seq else 0
     w = sys.stdout.write
-    w(f"# {args.title}\n\n")
-    if args.command:
-        w("Command (on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
-        for line in args.command.split(";"):
-            w(f"    {line.strip()}\n")
-        w("\n")
+    header(w, args.title, args.command, args.note)
     w(f"Dispatches after decoder step {args.from_step}: {len(seq)} kernels over {steps} decoder steps; "
       f"sum of kernel durations {total / 1e9:.3f} s, first start to last end {span / 1e9:.3f} s "
       f"({total / max(span, 1) * 100:.1f} % busy).\n\n")

@@ -105,7 +105,42 @@ def sample_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
     print(open(out).read())
 
 
+def mfma_summary(counter_dir, out):
+    """Executed bf16 matrix operations of the scoring kernel against 2 N d V (N = 65536 rows,
+    d = 1024, V = 32000), from a `rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16` run of the scoring
+    leg; the counter is in units of 512 operations."""
+    rows = _rows(counter_dir)
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != "SQ_INSTS_VALU_MFMA_MOPS_BF16":
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    alg = 2.0 * 65536 * 1024 * 32000
+    with open(out, "w") as f:
+        f.write("# MFMA operation count: action scoring, head V=32000 x d=1024 (bf16), N=65536 rows\n\n")
+        f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
+        f.write("    rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv -d <dir> -- python3 <repo>/bench.py --only-scoring --steps 1 --warmup 0 --no-cpu-baseline\n")
+        f.write("    python traffic_summary.py --mfma <dir> profiles/score_lse_res_k_head32000x1024_mfma.md\n\n")
+        f.write("`SQ_INSTS_VALU_MFMA_MOPS_BF16` counts bf16 matrix operations in units of 512.  Per dispatch,\n")
+        f.write("averaged over the run's dispatches of each kernel that issues any:\n\n")
+        f.write("| kernel | dispatches | executed bf16 FLOP (x 512) | algorithmic 2 N d V | executed / algorithmic |\n")
+        f.write("|---|---:|---:|---:|---:|\n")
+        for name, vals in sorted(per.items(), key=lambda kv: -max(kv[1])):
+            avg = sum(vals) / len(vals) * 512.0
+            if avg == 0:
+                continue
+            short = name.replace("rlt::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            if len(short) > 70:
+                short = short[:67] + "..."
+            f.write(f"| `{short}` | {len(vals)} | {avg:.4e} | {alg:.4e} | {avg / alg:.4f} |\n")
+        f.write("\nThe scoring kernel sweeps the vocabulary in 512-column steps, 63 x 512 = 32256 columns for\n")
+        f.write("V = 32000 (32256 / 32000 = 1.0080), so it executes that much more than the algorithmic count.\n")
+    print(open(out).read())
+
+
 def main(argv):
+    if argv and argv[0] == "--mfma":
+        return mfma_summary(*argv[1:])
     if argv and argv[0] == "--score":
         return score_summary(*argv[1:])
     if argv and argv[0] == "--sample":
