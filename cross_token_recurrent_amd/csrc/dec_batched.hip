@@ -32,42 +32,20 @@ constexpr int KCHUNK = 256;   // memory rows per cross-attention work item
 constexpr int kWideCombineSplits = 16;   // splits from which the 256-thread combine is faster
 // Whether the step runs on the weight-streaming products (wstream.hip) or the tiled ones.
 bool use_wst(const ModelLayout& m, int B) {
-  return m.has_frag && m.dtype == RLT_DTYPE_BF16 && B <= 64 && m.D <= 2048;
+  return m.has_frag && m.dtype == RLT_DTYPE_BF16 && B <= 64 && m.D <= 2048 && m.D % 64 == 0 && m.F % 32 == 0;
 }
 
 struct Scratch {
-  size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, ssp, cnt, xcnt, wpart, total;
+  size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, ssp, cnt, xcnt, total;
   size_t cnt_bytes;
   int nsmax;
 };
 
-// Row blocks per workgroup and K split of a weight-streaming product over B rows.
-struct WstPlan {
-  int mb, S;
-};
-// One 16-row block per workgroup: the row groups of a tile re-read its weights from L2, which
-// is cheaper than splitting K (the split's partial round trip); K is split only past 2048.
-WstPlan wst_plan(int B, int N, int K) {
-  (void)B;
-  (void)N;
-  return {1, wst_choose_split(1, K)};
-}
-
-// Largest split-K partial buffer and counter array any weight-streaming product of the step needs.
-void wst_scratch_max(const ModelLayout& m, int B, size_t* part_floats, size_t* counters) {
-  const int D = m.D;
-  const int shapes[5][2] = {{2 * D, 2 * D}, {3 * D, D}, {D, D}, {m.F2, D}, {D, m.F}};
-  *part_floats = *counters = 0;
-  for (const auto& nk : shapes) {
-    const WstPlan p = wst_plan(B, nk[0], nk[1]);
-    *part_floats = std::max(*part_floats, wst_part_floats(B, p.mb, nk[0], p.S));
-    *counters = std::max(*counters, wst_counters(B, p.mb, nk[0]));
-  }
-}
-
 Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   Scratch s{};
-  const size_t D = m.D, Bz = B, e = m.esz;
+  // activation operands are padded to whole 16-row blocks (the fragment-major layout of the
+  // weight-streaming products; the padding rows are never read into a stored result)
+  const size_t D = m.D, Bz = B, Bp = (Bz + 15) / 16 * 16, e = m.esz;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -76,27 +54,21 @@ Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   };
   s.nsmax = (T + KCHUNK - 1) / KCHUNK;
   s.y = take(Bz * D * 4);
-  s.h = take(Bz * D * e);
-  s.xin = take(Bz * 2 * D * e);
+  s.h = take(Bp * D * e);
+  s.xin = take(Bp * 2 * D * e);
   s.gpre = take(Bz * D * 4);
   s.fb = take(Bz * D * 4);
   s.qkv = take(Bz * 3 * D * 4);
-  s.attn = take(Bz * D * e);
-  s.act = take(Bz * static_cast<size_t>(m.F) * e);
+  s.attn = take(Bp * D * e);
+  s.act = take(Bp * static_cast<size_t>(m.F) * e);
   s.part = take(Bz * m.H * static_cast<size_t>(s.nsmax) * (m.DH + 2) * 4);
   s.splitk = take(gemm_splitk_ws_floats(B, m.D) * 4);
-  // weight-streaming products: per-tile row sums of squares, arrival counters, partials
-  const bool w = use_wst(m, B);
-  size_t part_floats = 0, counters = 0;
-  if (w) wst_scratch_max(m, B, &part_floats, &counters);
-  s.ssp = take(w ? 2 * D * 4 : 0);
-  // arrival counters: the products' (first) and the cross-attention heads' (after them), one
-  // range that the state's reset zeroes
-  s.cnt = off;
-  s.xcnt = s.cnt + counters * 4;
-  s.cnt_bytes = counters * 4 + Bz * m.H * 4;
+  // weight-streaming products: per-16-column-block row sums of squares, [D/16][64]
+  s.ssp = take(use_wst(m, B) ? D / 16 * 64 * 4 : 0);
+  // arrival counters of the cross-attention heads, zeroed by the state's reset
+  s.cnt = s.xcnt = off;
+  s.cnt_bytes = Bz * m.H * 4;
   take(s.cnt_bytes);
-  s.wpart = take(part_floats * 4);
   s.total = off;
   return s;
 }
@@ -232,7 +204,7 @@ __device__ __forceinline__ void wave_finish(const SoftState& st, float* __restri
 template <typename WT, int DH, int SWA_WAVES>
 __global__ __launch_bounds__(64 * SWA_WAVES) void swa_k(const float* __restrict__ qkv, WT* __restrict__ ring_k,
                                                         WT* __restrict__ ring_v, WT* __restrict__ attn, int B, int H,
-                                                        int Wm1, int t, float scale) {
+                                                        int Wm1, int t, float scale, int xf) {
   constexpr int LPK = DH / 16;
   constexpr int SLOTS = 64 / LPK;
   __shared__ float lds[SWA_WAVES][64 * 17 + 64];
@@ -304,7 +276,7 @@ __global__ __launch_bounds__(64 * SWA_WAVES) void swa_k(const float* __restrict_
         num += po[w][d] * f;
         den += pl[w] * f;
       }
-      store_from_f32(&attn[static_cast<size_t>(b) * D + h * DH + d], num / den);
+      store_from_f32(&attn[act_offset(b, h * DH + d, D, xf)], num / den);
     }
   }
   // the current entry replaces the oldest one (position t - (W-1)); every read of the ring
@@ -354,7 +326,7 @@ template <typename WT> struct Raw16 {
 template <typename WT, int DH>
 __global__ __launch_bounds__(512) void swa2_k(const float* __restrict__ qkv, WT* __restrict__ ring_k,
                                                WT* __restrict__ ring_v, WT* __restrict__ attn, int H, int Wm1, int t,
-                                               float scale) {
+                                               float scale, int xf) {
   constexpr int LPK = DH / 16;              // lanes per key row (16 dims each)
   constexpr int SLOTS = 64 / LPK;           // rows per load instruction
   constexpr int KW = SwaKw<WT>::v(DH);      // entries per wave
@@ -443,7 +415,7 @@ __global__ __launch_bounds__(512) void swa2_k(const float* __restrict__ qkv, WT*
       num += po[w][d];
       den += pl[w];
     }
-    store_from_f32(&attn[static_cast<size_t>(b) * D + h * DH + d], num / den);
+    store_from_f32(&attn[act_offset(b, h * DH + d, D, xf)], num / den);
   }
   // 4. the current entry replaces the oldest one (position t - (W-1)); every read of the ring
   //    happened before the barrier above
@@ -468,7 +440,7 @@ template <typename WT, int DH, bool FUSE>
 __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx, const WT* __restrict__ mem_k,
                                                    const WT* __restrict__ mem_v, float* __restrict__ part,
                                                    WT* __restrict__ attn, int* __restrict__ cnt, int B, int H, int T,
-                                                   int t, int nsmax, float scale) {
+                                                   int t, int nsmax, float scale, int xf) {
   constexpr int LPK = DH / 16;
   constexpr int SLOTS = 64 / LPK;
   constexpr int DL = DH < 64 ? DH : 64;   // lanes per block in the P.V pass
@@ -541,11 +513,11 @@ __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx,
     for (int off = DL; off < 64; off <<= 1) o[nd] += __shfl_xor(o[nd], off, 64);
   }
   const int ns = (t + 1 + KCHUNK - 1) / KCHUNK;
-  WT* out = attn + static_cast<size_t>(b) * D + h * DH;
+  const int oc = h * DH;   // first output column of the head
   if (FUSE && ns == 1) {
     if (bq == 0) {
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) store_from_f32(&out[d0 + nd * 64], o[nd] / lsum);
+      for (int nd = 0; nd < ND; ++nd) store_from_f32(&attn[act_offset(b, oc + d0 + nd * 64, D, xf)], o[nd] / lsum);
     }
     return;
   }
@@ -609,7 +581,7 @@ __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx,
     }
     if (bq == 0) {
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) store_from_f32(&out[d0 + nd * 64], acc[nd] / lsum_all);
+      for (int nd = 0; nd < ND; ++nd) store_from_f32(&attn[act_offset(b, oc + d0 + nd * 64, D, xf)], acc[nd] / lsum_all);
     }
   }
 }
@@ -621,7 +593,7 @@ __global__ __launch_bounds__(64) void cross_part_k(const float* __restrict__ qx,
 // fixed order, so the result does not depend on timing.
 template <typename WT, int DH>
 __global__ __launch_bounds__(256) void cross_combine_wide_k(const float* __restrict__ part, WT* __restrict__ attn,
-                                                            int H, int ns, int nsmax) {
+                                                            int H, int ns, int nsmax, int xf) {
   constexpr int G = 256 / DH;
   constexpr int P = DH + 2;
   __shared__ float red[8];
@@ -659,13 +631,13 @@ __global__ __launch_bounds__(256) void cross_combine_wide_k(const float* __restr
 #pragma unroll
     for (int q = 1; q < G; ++q) acc += po[q][tid];
     const float L = (red[4] + red[5]) + (red[6] + red[7]);
-    store_from_f32(&attn[static_cast<size_t>(b) * H * DH + h * DH + tid], acc / L);
+    store_from_f32(&attn[act_offset(b, h * DH + tid, H * DH, xf)], acc / L);
   }
 }
 
 template <typename WT, int DH>
 hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratch& sc, char* base, char* state,
-                                   const StateLayout& S, int l, int t, hipStream_t st) {
+                                   const StateLayout& S, int l, int t, int xf, hipStream_t st) {
   const int B = S.B, H = m.H;
   const float scale = 1.0f / sqrtf(static_cast<float>(DH));
   if (self) {
@@ -677,11 +649,11 @@ hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratc
     constexpr int KW = SwaKw<WT>::v(DH);
     const int nw = (S.Wm1 + 1 + KW - 1) / KW;
     if (nw <= 8)
-      swa2_k<WT, DH><<<dim3(H, B), 64 * nw, 0, st>>>(q, rk, rv, out, H, S.Wm1, t, scale);
+      swa2_k<WT, DH><<<dim3(H, B), 64 * nw, 0, st>>>(q, rk, rv, out, H, S.Wm1, t, scale, xf);
     else if (B * H >= 2048)
-      swa_k<WT, DH, 1><<<dim3(H, B), 64, 0, st>>>(q, rk, rv, out, B, H, S.Wm1, t, scale);
+      swa_k<WT, DH, 1><<<dim3(H, B), 64, 0, st>>>(q, rk, rv, out, B, H, S.Wm1, t, scale, xf);
     else
-      swa_k<WT, DH, 4><<<dim3(H, B), 256, 0, st>>>(q, rk, rv, out, B, H, S.Wm1, t, scale);
+      swa_k<WT, DH, 4><<<dim3(H, B), 256, 0, st>>>(q, rk, rv, out, B, H, S.Wm1, t, scale, xf);
   } else {
     const int g = m.G == 1 ? 0 : l;
     const size_t goff = static_cast<size_t>(g) * B * S.T * m.D;
@@ -697,13 +669,13 @@ hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratc
     // 256-thread combine kernel folds the partials
     if (ns < kWideCombineSplits) {
       cross_part_k<WT, DH, true><<<dim3(ns, H, B), 64, 0, st>>>(qx, mk, mv, part, out, xcnt, B, H, S.T, t, sc.nsmax,
-                                                                 scale);
+                                                                 scale, xf);
     } else {
       cross_part_k<WT, DH, false><<<dim3(ns, H, B), 64, 0, st>>>(qx, mk, mv, part, out, xcnt, B, H, S.T, t, sc.nsmax,
-                                                                  scale);
+                                                                  scale, xf);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      cross_combine_wide_k<WT, DH><<<dim3(H, B), 256, 0, st>>>(part, out, H, ns, sc.nsmax);
+      cross_combine_wide_k<WT, DH><<<dim3(H, B), 256, 0, st>>>(part, out, H, ns, sc.nsmax, xf);
     }
   }
   return hipGetLastError();
@@ -711,12 +683,12 @@ hipError_t step_attention_launches(bool self, const ModelLayout& m, const Scratc
 
 template <typename WT>
 hipError_t attention(bool self, const ModelLayout& m, const Scratch& sc, char* base, char* state, const StateLayout& S,
-                     int l, int t, hipStream_t st) {
+                     int l, int t, int xf, hipStream_t st) {
   switch (m.DH) {
-    case 16: return step_attention_launches<WT, 16>(self, m, sc, base, state, S, l, t, st);
-    case 32: return step_attention_launches<WT, 32>(self, m, sc, base, state, S, l, t, st);
-    case 64: return step_attention_launches<WT, 64>(self, m, sc, base, state, S, l, t, st);
-    case 128: return step_attention_launches<WT, 128>(self, m, sc, base, state, S, l, t, st);
+    case 16: return step_attention_launches<WT, 16>(self, m, sc, base, state, S, l, t, xf, st);
+    case 32: return step_attention_launches<WT, 32>(self, m, sc, base, state, S, l, t, xf, st);
+    case 64: return step_attention_launches<WT, 64>(self, m, sc, base, state, S, l, t, xf, st);
+    case 128: return step_attention_launches<WT, 128>(self, m, sc, base, state, S, l, t, xf, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -764,13 +736,13 @@ hipError_t step_tiled(const ModelLayout& m, const StateLayout& S, const Scratch&
     RLT_CK(launch_rmsnorm_rows(y, gains_self + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr,
                                1, 0, 0, 1, st));
     RLT_CK(gemm(base + sc.h, D, lw + m.l_qkv, 3 * D, D, base + sc.qkv, 3 * D, EPI_STORE_F32));
-    RLT_CK(attention<WT>(true, m, sc, base, state, S, l, t, st));
+    RLT_CK(attention<WT>(true, m, sc, base, state, S, l, t, 0, st));
     RLT_CK(gemm(base + sc.attn, D, lw + m.l_wo, D, D, y, D, EPI_RESID_F32));
     // cross-attention to memory entries 0..t
     RLT_CK(launch_rmsnorm_rows(y, gains_cross + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr,
                                1, 0, 0, 1, st));
     RLT_CK(gemm(base + sc.h, D, lw + m.l_wqx, D, D, base + sc.qkv, D, EPI_STORE_F32));
-    RLT_CK(attention<WT>(false, m, sc, base, state, S, l, t, st));
+    RLT_CK(attention<WT>(false, m, sc, base, state, S, l, t, 0, st));
     RLT_CK(gemm(base + sc.attn, D, lw + m.l_wox, D, D, y, D, EPI_RESID_F32));
     // FFN
     RLT_CK(launch_rmsnorm_rows(y, gains_ffn + static_cast<size_t>(l) * D, base + sc.h, B, D, m.eps, dt, nullptr, 1,
@@ -785,38 +757,33 @@ hipError_t step_tiled(const ModelLayout& m, const StateLayout& S, const Scratch&
 }
 
 // One step on the weight-streaming products: each norm is folded into the residual product
-// before it (bf16(g * y) and per-tile sums of squares) and the product after it (rows scaled by
-// 1 / rms), the split-K partials are added by each tile's last workgroup, and the merge is one
-// product over [e_t ; s_{t-1}].
+// before it (bf16(g * y) and per-block sums of squares) and the product after it (rows scaled by
+// 1 / rms), every product's input is written in the fragment-major layout by its producer, and the
+// merge is one product over [e_t ; s_{t-1}].
 hipError_t step_wst(const ModelLayout& m, const StateLayout& S, const Scratch& sc, const char* ws, char* state,
                     char* base, float* s_out, int t, int step, int n, hipStream_t st) {
   const int B = S.B, D = m.D;
   float* y = reinterpret_cast<float*>(base + sc.y);
   float* ssp = reinterpret_cast<float*>(base + sc.ssp);
   uint16_t* xb = reinterpret_cast<uint16_t*>(base + sc.h);
+  const uint16_t* e = reinterpret_cast<const uint16_t*>(state + S.e);
   const char* frag = ws + m.frag_layers;
-  auto prod = [&](int in, int epi, const void* x, int ldx, int nt_in, const char* wf, int N, int K, float* outf,
-                  uint16_t* outb, int ldo, const float* gain_next) {
+  const int nt = D / 16;   // sums-of-squares blocks of the residual stream
+  auto prod = [&](int epi, const void* x, int nt_in, const char* wf, int N, int K, float* outf, uint16_t* outb,
+                  int ldo, const float* gain_next) {
     WstArgs a{};
-    a.in = in; a.epi = epi;
-    a.x = x; a.ldx = ldx; a.ssp = ssp; a.nt_in = nt_in; a.eps = m.eps;
-    a.e = reinterpret_cast<const uint16_t*>(state + S.e);
-    a.s = reinterpret_cast<const float*>(state + S.s);
-    a.T = S.T; a.t = t; a.D = D;
+    a.epi = epi;
+    a.xf = static_cast<const uint4*>(x);
+    a.ssp = ssp; a.nt_in = nt_in; a.eps = m.eps;
+    a.e = e; a.T = S.T; a.t = t; a.D = D;
     a.wf = reinterpret_cast<const uint4*>(wf);
     a.M = B; a.N = N; a.K = K;
-    const WstPlan plan = wst_plan(B, N, K);
-    a.mb = plan.mb;
-    a.S = plan.S;
-    a.KS = K / a.S;
     a.outf = outf; a.outb = outb; a.ldo = ldo;
     a.ssp_out = ssp;
     a.gain_next = gain_next;
     a.xb_out = xb;
     a.bias = reinterpret_cast<const float*>(ws + m.bg);
-    a.part = reinterpret_cast<float*>(base + sc.wpart);
-    a.cnt = reinterpret_cast<int*>(base + sc.cnt);
-    return launch_wst(a, st);
+    return launch_wsn(a, st);
   };
   const float* gains_self = reinterpret_cast<const float*>(ws + m.g_dec_self);
   const float* gains_cross = reinterpret_cast<const float*>(ws + m.g_dec_cross);
@@ -824,23 +791,22 @@ hipError_t step_wst(const ModelLayout& m, const StateLayout& S, const Scratch& s
   float* qkv = reinterpret_cast<float*>(base + sc.qkv);
   uint16_t* attn = reinterpret_cast<uint16_t*>(base + sc.attn);
   uint16_t* act = reinterpret_cast<uint16_t*>(base + sc.act);
-  // gated merge: y, bf16(g_self^0 * y) and the sums of squares of its 32-column tiles
-  RLT_CK(prod(WIN_MERGE, WEPI_MERGE, nullptr, 0, 0, ws + m.frag_merge, 2 * D, 2 * D, y, nullptr, D, gains_self));
-  int nt = 2 * D / 64;
+  // gated merge: y, bf16(g_self^0 * y) and the sums of squares of its 16-column blocks
+  RLT_CK(launch_merge_x(e, reinterpret_cast<const float*>(state + S.s), base + sc.xin, B, S.T, D, t, st));
+  RLT_CK(prod(WEPI_MERGE, base + sc.xin, 0, ws + m.frag_merge, 2 * D, 2 * D, y, nullptr, D, gains_self));
   for (int l = 0; l < m.L; ++l) {
     const char* lw = frag + l * m.layer_stride;
     const size_t go = static_cast<size_t>(l) * D;
     const float* next_self = l + 1 < m.L ? gains_self + go + D : nullptr;
-    RLT_CK(prod(WIN_BF16, WEPI_F32, xb, D, nt, lw + m.l_qkv, 3 * D, D, qkv, nullptr, 3 * D, nullptr));
-    RLT_CK(attention<bf16_t>(true, m, sc, base, state, S, l, t, st));
-    RLT_CK(prod(WIN_BF16, WEPI_RESID, attn, D, 0, lw + m.l_wo, D, D, y, nullptr, D, gains_cross + go));
-    nt = D / 64;
-    RLT_CK(prod(WIN_BF16, WEPI_F32, xb, D, nt, lw + m.l_wqx, D, D, qkv, nullptr, D, nullptr));
-    RLT_CK(attention<bf16_t>(false, m, sc, base, state, S, l, t, st));
-    RLT_CK(prod(WIN_BF16, WEPI_RESID, attn, D, 0, lw + m.l_wox, D, D, y, nullptr, D, gains_ffn + go));
-    RLT_CK(prod(WIN_BF16, m.ffn_kind == RLT_FFN_GELU ? WEPI_GELU : WEPI_SWIGLU, xb, D, nt, lw + m.l_fin, m.F2, D,
-                nullptr, act, m.F, nullptr));
-    RLT_CK(prod(WIN_BF16, WEPI_RESID, act, m.F, 0, lw + m.l_fout, D, m.F, y, nullptr, D, next_self));
+    RLT_CK(prod(WEPI_F32, xb, nt, lw + m.l_qkv, 3 * D, D, qkv, nullptr, 3 * D, nullptr));
+    RLT_CK(attention<bf16_t>(true, m, sc, base, state, S, l, t, 1, st));
+    RLT_CK(prod(WEPI_RESID, attn, 0, lw + m.l_wo, D, D, y, nullptr, D, gains_cross + go));
+    RLT_CK(prod(WEPI_F32, xb, nt, lw + m.l_wqx, D, D, qkv, nullptr, D, nullptr));
+    RLT_CK(attention<bf16_t>(false, m, sc, base, state, S, l, t, 1, st));
+    RLT_CK(prod(WEPI_RESID, attn, 0, lw + m.l_wox, D, D, y, nullptr, D, gains_ffn + go));
+    RLT_CK(prod(m.ffn_kind == RLT_FFN_GELU ? WEPI_GELU : WEPI_SWIGLU, xb, nt, lw + m.l_fin, m.F2, D, nullptr, act,
+                m.F, nullptr));
+    RLT_CK(prod(WEPI_RESID, act, 0, lw + m.l_fout, D, m.F, y, nullptr, D, next_self));
   }
   return launch_final_norm_ssp(y, ssp, nt, reinterpret_cast<const float*>(ws + m.g_dec_final),
                                reinterpret_cast<float*>(state + S.s), s_out, B, D, m.eps, step, n, st);

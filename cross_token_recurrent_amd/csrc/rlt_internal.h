@@ -138,42 +138,34 @@ size_t gemm_splitk_ws_floats(int M, int N);
 hipError_t launch_pack_frag(const void* w, void* dst, int N, int K, hipStream_t st);
 
 // Weight-streaming products of the decoder step for M <= 64 rows (bf16, wstream.hip):
-// Y[M, N] = X[M, K] W^T with W from its fragment-major copy, K split over S workgroups per
-// 64-column tile, the partials added in slice order by the tile's last workgroup.  RMSNorm is
-// folded in: a residual product also writes xb = bf16(g_next * y) and per-tile row sums of
-// squares; the next product reads xb and scales its rows by 1 / rms(y).
-enum WstIn { WIN_BF16 = 0, WIN_MERGE = 2 };
+// Y[M, N] = X[M, K] W^T with W and X both in fragment-major layout (act_offset), one
+// 16-column block (or a pair of blocks) per workgroup, K split over its waves.  RMSNorm is folded
+// in: a residual product also writes xb = bf16(g_next * y) and per-block row sums of squares;
+// the next product reads xb and scales its rows by 1 / rms(y).
 enum WstEpi { WEPI_F32 = 0, WEPI_RESID = 1, WEPI_GELU = 2, WEPI_SWIGLU = 3, WEPI_MERGE = 4 };
 struct WstArgs {
-  int in, epi;
-  const void* x;            // WIN_BF16: bf16 [M][ldx]
-  int ldx;
-  const float* ssp;         // WEPI_F32 / GELU / SWIGLU: per-tile row sums of squares of y, [nt_in][64]
-  int nt_in;
+  int epi;
+  const uint4* xf;          // X, fragment-major bf16 [ceil(M/16)*16][K]
+  const float* ssp;         // WEPI_F32 / GELU / SWIGLU: per-block row sums of squares of y, [nt_in][64]
+  int nt_in;                // D / 16 blocks (<= 128)
   float eps;
-  const uint16_t* e;        // WIN_MERGE / WEPI_MERGE: e of the state, bf16 [M][T][D], row t
-  const float* s;           // WIN_MERGE: s_{t-1} fp32 [M][D]
+  const uint16_t* e;        // WEPI_MERGE: e of the state, bf16 [M][T][D], row t
   int T, t, D;
   const uint4* wf;          // fragment-major W [N][K]
-  int M, N, K, KS, S;       // KS = K / S: a power-of-two multiple of 64
-  int mb;                   // 16-row blocks per workgroup (1, 2, 4); ceil(M / (16 mb)) row groups
-  float* outf;              // WEPI_F32 output, WEPI_RESID / WEPI_MERGE residual y (fp32, ldo)
-  uint16_t* outb;           // WEPI_GELU / WEPI_SWIGLU activation (bf16, ldo)
-  int ldo;
-  float* ssp_out;           // WEPI_RESID / WEPI_MERGE: [N/64][64] row sums of squares of the tile
+  int M, N, K;
+  float* outf;              // WEPI_F32 output (row-major), WEPI_RESID / WEPI_MERGE residual y (fp32, ldo)
+  uint16_t* outb;           // WEPI_GELU / WEPI_SWIGLU activation, fragment-major bf16 with K = ldo
+  int ldo;                  // output columns (N, or N / 2 for the paired epilogues)
+  float* ssp_out;           // WEPI_RESID / WEPI_MERGE: [ldo/16][64] row sums of squares of each 16-column block
   const float* gain_next;   // WEPI_RESID (optional) / WEPI_MERGE: gain of the next norm [D]
-  uint16_t* xb_out;         // with gain_next: bf16(gain_next * y) [M][ldo]
+  uint16_t* xb_out;         // with gain_next: bf16(gain_next * y), fragment-major with K = ldo
   const float* bias;        // WEPI_MERGE: b_g [D]
-  float* part;              // S > 1: wst_part_floats(M, mb, N, S) floats
-  int* cnt;                 // S > 1: wst_counters(M, mb, N) arrival counters, zero before and after the launch
 };
-bool wst_supported(int M, int N, int K);
-// S for a product with mb 16-row blocks per workgroup: the smallest split whose K slice fits.
-int wst_choose_split(int mb, int K);
-size_t wst_part_floats(int M, int mb, int N, int S);   // split-K partial floats
-size_t wst_counters(int M, int mb, int N);             // arrival counters
-hipError_t launch_wst(const WstArgs& a, hipStream_t st);
-// s = g * y / rms(y) from the per-tile sums of squares (nt tiles); also s_out[b][step] when set.
+bool wsn_supported(int M, int N, int K);
+hipError_t launch_wsn(const WstArgs& a, hipStream_t st);
+// The merge's X = [e_t ; bf16(s)] as a fragment-major bf16 [ceil(M/16)*16][2D] matrix (padding rows zero).
+hipError_t launch_merge_x(const uint16_t* e, const float* s, void* xf, int M, int T, int D, int t, hipStream_t st);
+// s = g * y / rms(y) from the per-block sums of squares (nt blocks); also s_out[b][step] when set.
 hipError_t launch_final_norm_ssp(const float* y, const float* ssp, int nt, const float* gain, float* s, float* s_out,
                                  int B, int D, float eps, int step, int n, hipStream_t st);
 // Fragment-major bf16 copy of the merge matrix [2D][2D] from the fp32 W_ge, W_gs, W_fb [D][D].

@@ -7,7 +7,7 @@ The second form renders the `--stats` table rocprofv3 writes (kernel_stats.csv) 
 
 The batched decoder ends every step with one final_norm_ssp_k (or final_norm_k) dispatch, so
 --from-step S keeps only the dispatches after the S-th of those: the steps S+1 .. of the
-replay that was traced.  The weight-streaming products (wst_k) are split by their role in the
+replay that was traced.  The weight-streaming products (wsn_k) are split by their role in the
 layer, read from the kernel order: the projection before the window attention (qkv) or before
 the cross-attention (qx); the residual product after the window attention (wo), after the
 cross-attention (wox) or after the FFN input product (ffn_out); the FFN input product (ffn_in)
@@ -31,20 +31,20 @@ def roles(seq):
     out = []
     for i, (n, s, e) in enumerate(seq):
         role = n
-        if n.startswith("wst_k"):
-            args = n[len("wst_k<"):-1].replace(" ", "").split(",")
-            epi = int(args[2]) if len(args) >= 3 else -1
+        if n.startswith("wsn_k"):
+            args = n[len("wsn_k<"):-1].replace(" ", "").split(",")
+            epi = int(args[1]) if len(args) >= 2 else -1
             prev = seq[i - 1][0] if i else ""
             nxt = seq[i + 1][0] if i + 1 < len(seq) else ""
             if epi == 0:
-                role = "wst_k qkv" if nxt.startswith("swa") else ("wst_k qx" if nxt.startswith("cross") else n)
+                role = "wsn_k qkv" if nxt.startswith("swa") else ("wsn_k qx" if nxt.startswith("cross") else n)
             elif epi == 1:
-                role = ("wst_k wo" if prev.startswith("swa") else "wst_k wox" if prev.startswith("cross")
-                        else "wst_k ffn_out" if prev.startswith("wst_k") else n)
+                role = ("wsn_k wo" if prev.startswith("swa") else "wsn_k wox" if prev.startswith("cross")
+                        else "wsn_k ffn_out" if prev.startswith("wsn_k") else n)
             elif epi in (2, 3):
-                role = "wst_k ffn_in"
+                role = "wsn_k ffn_in"
             elif epi == 4:
-                role = "wst_k merge"
+                role = "wsn_k merge"
         out.append((role, e - s))
     return out
 
