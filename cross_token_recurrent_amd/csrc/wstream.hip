@@ -43,9 +43,12 @@ constexpr int kWsnMaxTiles = 128;  // most 16-column sums of squares per row (D 
 
 constexpr bool scales_rows(int EPI) { return EPI == WEPI_F32 || EPI == WEPI_GELU || EPI == WEPI_SWIGLU; }
 
-template <int MB, int EPI, int NW, int NSR>
+template <int MB, int EPI, int NW, int NSR, int NCB>
 __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
-  constexpr int NCB = (EPI == WEPI_SWIGLU || EPI == WEPI_MERGE) ? 2 : 1;   // column blocks per workgroup
+  // NCB column blocks per workgroup: the two members of a pair for the paired epilogues, else
+  // one or two independent blocks (two share each X load through the CU's L1)
+  constexpr bool PAIRED = EPI == WEPI_SWIGLU || EPI == WEPI_MERGE;
+  static_assert(!PAIRED || NCB == 2, "paired epilogues take two blocks");
   constexpr int KW = NW / NCB;                                               // K runs per column block
   constexpr int NT = NW * 64;
   constexpr int ROWS = 16 * MB;
@@ -125,18 +128,21 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
     }
     __syncthreads();
   }
-  // epilogue: output o = (row, column c of the block); 16 lanes hold the 16 columns of one row
-  const int oc0 = unit * 16;
+  // epilogue: output o = (block b, row, column c of the block); 16 lanes hold the 16 columns of
+  // one row.  A pair yields one output block (the pair's index), independent blocks one each.
+  constexpr int NOB = PAIRED ? 1 : NCB;   // output blocks per workgroup
 #pragma unroll
-  for (int j = 0; j < (ROWS * 16 + NT - 1) / NT; ++j) {
-    const int o = tid + NT * j;
-    if (o >= ROWS * 16) break;   // uniform per wave (ROWS * 16 is a multiple of 64)
-    const int row = o / 16, c = o % 16, oc = oc0 + c;
-    float v0 = red[0][o];
+  for (int j = 0; j < (NOB * ROWS * 16 + NT - 1) / NT; ++j) {
+    const int ob = tid + NT * j;
+    if (ob >= NOB * ROWS * 16) break;   // uniform per wave (ROWS * 16 is a multiple of 64)
+    const int b = ob / (ROWS * 16), o = ob % (ROWS * 16);
+    const int row = o / 16, c = o % 16;
+    const int blk = unit * NOB + b, oc = blk * 16 + c;
+    float v0 = red[b][o];
 #pragma unroll
-    for (int k = 1; k < KW; ++k) v0 += red[k * NCB][o];
+    for (int k = 1; k < KW; ++k) v0 += red[k * NCB + b][o];
     float v1 = 0.f;
-    if constexpr (NCB == 2) {
+    if constexpr (PAIRED) {
       v1 = red[1][o];
 #pragma unroll
       for (int k = 1; k < KW; ++k) v1 += red[k * NCB + 1][o];
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
         sq = y * y;
       }
       sq = group_sum<16>(sq);
-      if (c == 0) a.ssp_out[unit * 64 + row] = sq;
+      if (c == 0) a.ssp_out[blk * 64 + row] = sq;
     }
   }
 }
@@ -240,34 +246,36 @@ __global__ __launch_bounds__(256) void pack_merge_frag_k(const float* __restrict
   dst[c] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
 }
 
-// Register ring depth: every stage holds its W pair and MB X pairs.
+// Register ring depth: every stage holds its W pair and MB X pairs (8 + 8 MB VGPRs); at 16 waves
+// per workgroup a wave has 128 VGPRs, of which about 40 go to addresses, sums and accumulators.
 template <int MB, int NW>
 constexpr int wsn_ring() {
-  constexpr int per_stage = 8 + MB * 8;                                // VGPRs
-  constexpr int budget = (NW <= 8 ? 256 : 512 / (NW / 4)) - 96;       // left after addresses, sums, accumulators
-  constexpr int r = budget / per_stage;
+  constexpr int per_stage = 8 + MB * 8;
+  constexpr int budget = 512 / (NW / 4 > 0 ? NW / 4 : 1) - 40;
+  constexpr int r = (budget > 256 ? 256 : budget) / per_stage;
   return r >= 8 ? 8 : r >= 4 ? 4 : r >= 2 ? 2 : 1;
 }
 
-template <int MB, int EPI, int NW>
+template <int MB, int EPI, int NCB>
 hipError_t launch_wsn_t(const WstArgs& a, hipStream_t st) {
-  constexpr int NCB = (EPI == WEPI_SWIGLU || EPI == WEPI_MERGE) ? 2 : 1;
-  wsn_k<MB, EPI, NW, wsn_ring<MB, NW>()><<<a.N / (16 * NCB), NW * 64, 0, st>>>(a);
+  constexpr int NW = 16;
+  wsn_k<MB, EPI, NW, wsn_ring<MB, NW>(), NCB><<<a.N / (16 * NCB), NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
-template <int EPI, int NW>
+template <int EPI, int NCB>
 hipError_t launch_wsn_mb(const WstArgs& a, hipStream_t st) {
-  if (a.M <= 16) return launch_wsn_t<1, EPI, NW>(a, st);
-  if (a.M <= 32) return launch_wsn_t<2, EPI, NW>(a, st);
-  return launch_wsn_t<4, EPI, NW>(a, st);
+  if (a.M <= 16) return launch_wsn_t<1, EPI, NCB>(a, st);
+  if (a.M <= 32) return launch_wsn_t<2, EPI, NCB>(a, st);
+  return launch_wsn_t<4, EPI, NCB>(a, st);
 }
 
 template <int EPI>
 hipError_t launch_wsn_nw(const WstArgs& a, hipStream_t st) {
-  // four waves per workgroup where the grid alone fills the chip, eight where it does not
-  return a.N / ((EPI == WEPI_SWIGLU || EPI == WEPI_MERGE) ? 32 : 16) >= 256 ? launch_wsn_mb<EPI, 4>(a, st)
-                                                                             : launch_wsn_mb<EPI, 8>(a, st);
+  // 16 waves per workgroup; two independent column blocks per workgroup once the single-block
+  // grid would take more than one round of the chip's CUs (measured on the step's shapes)
+  if constexpr (EPI == WEPI_SWIGLU || EPI == WEPI_MERGE) return launch_wsn_mb<EPI, 2>(a, st);
+  else return a.N / 16 >= 384 ? launch_wsn_mb<EPI, 2>(a, st) : launch_wsn_mb<EPI, 1>(a, st);
 }
 
 }  // namespace
