@@ -206,10 +206,11 @@ __global__ __launch_bounds__(256) void final_norm_ssp_k(const float* __restrict_
                                                         float* __restrict__ s_out, int D, float eps, int step, int n) {
   const int b = blockIdx.x;
   __shared__ float inv_s;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {   // lane j adds blocks j, j + 64, ...; the lanes' sums in a fixed order
     float ss = 0.f;
-    for (int j = 0; j < nt; ++j) ss += ssp[j * 64 + b];
-    inv_s = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+    for (int j = threadIdx.x; j < nt; j += 64) ss += ssp[j * 64 + b];
+    ss = group_sum<64>(ss);
+    if (threadIdx.x == 0) inv_s = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
   }
   __syncthreads();
   const float inv = inv_s;
