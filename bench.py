@@ -210,11 +210,6 @@ def segment_sizes(T: int, K: int):
     return [T // K + (1 if i < T % K else 0) for i in range(K)]
 
 
-REF48_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_batched_ref48_traffic.md")
-BATCHED_SOURCES = ["cross_token_recurrent_amd/csrc/dec_batched.hip", "cross_token_recurrent_amd/csrc/wstream.hip",
-                   "cross_token_recurrent_amd/csrc/device_common.h"]
-
-
 def headline_replay(wl, steps: int, warmup: int, bw, with_cpu: bool = True):
     """The exact replay of one workload, timed as `steps` contiguous segments of the decoder
     (see the module docstring).  Returns the headline fields."""

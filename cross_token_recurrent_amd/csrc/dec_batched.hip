@@ -32,8 +32,13 @@ constexpr int KCHUNK = 256;   // memory rows per cross-attention work item
 constexpr int kWideCombineSplits = 16;   // splits from which the 256-thread combine is faster
 // Whether the step runs on the weight-streaming products (wstream.hip) or the tiled ones.
 bool use_wst(const ModelLayout& m, int B) {
-  return m.has_frag && m.dtype == RLT_DTYPE_BF16 && B <= 64 && m.D <= 2048 && m.D % 64 == 0 && m.F % 32 == 0;
+  return m.has_frag && m.dtype == RLT_DTYPE_BF16 && B <= 512 && m.D <= 2048 && m.D % 64 == 0 && m.F % 32 == 0;
 }
+
+// Rows of the products' fragment-major operands (whole 16-row blocks, whole 64-row groups past
+// 64 rows) and the row stride of their sums-of-squares arrays.
+int padded_rows(int B) { return B <= 64 ? (B + 15) / 16 * 16 : (B + 63) / 64 * 64; }
+int ss_stride(int B) { return B <= 64 ? 64 : (B + 63) / 64 * 64; }
 
 struct Scratch {
   size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, ssp, cnt, xcnt, total;
@@ -43,9 +48,9 @@ struct Scratch {
 
 Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   Scratch s{};
-  // activation operands are padded to whole 16-row blocks (the fragment-major layout of the
-  // weight-streaming products; the padding rows are never read into a stored result)
-  const size_t D = m.D, Bz = B, Bp = (Bz + 15) / 16 * 16, e = m.esz;
+  // activation operands are padded to the row blocks / row groups of the weight-streaming
+  // products' fragment-major layout (the padding rows are never read into a stored result)
+  const size_t D = m.D, Bz = B, Bp = padded_rows(B), e = m.esz;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -63,8 +68,8 @@ Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   s.act = take(Bp * static_cast<size_t>(m.F) * e);
   s.part = take(Bz * m.H * static_cast<size_t>(s.nsmax) * (m.DH + 2) * 4);
   s.splitk = take(gemm_splitk_ws_floats(B, m.D) * 4);
-  // weight-streaming products: per-16-column-block row sums of squares, [D/16][64]
-  s.ssp = take(use_wst(m, B) ? D / 16 * 64 * 4 : 0);
+  // weight-streaming products: per-16-column-block row sums of squares, [D/16][ss_stride(B)]
+  s.ssp = take(use_wst(m, B) ? D / 16 * ss_stride(B) * 4 : 0);
   // arrival counters of the cross-attention heads, zeroed by the state's reset
   s.cnt = s.xcnt = off;
   s.cnt_bytes = Bz * m.H * 4;
@@ -699,7 +704,7 @@ hipError_t attention(bool self, const ModelLayout& m, const Scratch& sc, char* b
     if (e_ != hipSuccess) return e_; \
   } while (0)
 
-// One step on the tiled products (fp32 models, models without fragment-major copies, B > 64).
+// One step on the tiled products (fp32 models, models without fragment-major copies, B > 512).
 template <typename WT>
 hipError_t step_tiled(const ModelLayout& m, const StateLayout& S, const Scratch& sc, const char* ws, char* state,
                       char* base, float* s_out, int t, int step, int n, hipStream_t st) {
@@ -774,7 +779,7 @@ hipError_t step_wst(const ModelLayout& m, const StateLayout& S, const Scratch& s
     WstArgs a{};
     a.epi = epi;
     a.xf = static_cast<const uint4*>(x);
-    a.ssp = ssp; a.nt_in = nt_in; a.eps = m.eps;
+    a.ssp = ssp; a.nt_in = nt_in; a.ld_ss = ss_stride(B); a.eps = m.eps;
     a.e = e; a.T = S.T; a.t = t; a.D = D;
     a.wf = reinterpret_cast<const uint4*>(wf);
     a.M = B; a.N = N; a.K = K;
@@ -792,7 +797,8 @@ hipError_t step_wst(const ModelLayout& m, const StateLayout& S, const Scratch& s
   uint16_t* attn = reinterpret_cast<uint16_t*>(base + sc.attn);
   uint16_t* act = reinterpret_cast<uint16_t*>(base + sc.act);
   // gated merge: y, bf16(g_self^0 * y) and the sums of squares of its 16-column blocks
-  RLT_CK(launch_merge_x(e, reinterpret_cast<const float*>(state + S.s), base + sc.xin, B, S.T, D, t, st));
+  RLT_CK(launch_merge_x(e, reinterpret_cast<const float*>(state + S.s), base + sc.xin, B, padded_rows(B), S.T, D, t,
+                        st));
   RLT_CK(prod(WEPI_MERGE, base + sc.xin, 0, ws + m.frag_merge, 2 * D, 2 * D, y, nullptr, D, gains_self));
   for (int l = 0; l < m.L; ++l) {
     const char* lw = frag + l * m.layer_stride;
@@ -808,7 +814,7 @@ hipError_t step_wst(const ModelLayout& m, const StateLayout& S, const Scratch& s
                 m.F, nullptr));
     RLT_CK(prod(WEPI_RESID, act, 0, lw + m.l_fout, D, m.F, y, nullptr, D, next_self));
   }
-  return launch_final_norm_ssp(y, ssp, nt, reinterpret_cast<const float*>(ws + m.g_dec_final),
+  return launch_final_norm_ssp(y, ssp, nt, ss_stride(B), reinterpret_cast<const float*>(ws + m.g_dec_final),
                                reinterpret_cast<float*>(state + S.s), s_out, B, D, m.eps, step, n, st);
 }
 

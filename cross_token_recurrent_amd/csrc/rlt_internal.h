@@ -137,17 +137,19 @@ size_t gemm_splitk_ws_floats(int M, int N);
 // Fragment-major copy of a packed bf16 [N][K] matrix (N % 16 == 0, K % 64 == 0).
 hipError_t launch_pack_frag(const void* w, void* dst, int N, int K, hipStream_t st);
 
-// Weight-streaming products of the decoder step for M <= 64 rows (bf16, wstream.hip):
+// Weight-streaming products of the decoder step for M <= 512 rows (bf16, wstream.hip):
 // Y[M, N] = X[M, K] W^T with W and X both in fragment-major layout (act_offset), one
-// 16-column block (or a pair of blocks) per workgroup, K split over its waves.  RMSNorm is folded
+// 16-column block (or a pair of blocks) and one group of up to 64 rows per workgroup, K split
+// over its waves.  RMSNorm is folded
 // in: a residual product also writes xb = bf16(g_next * y) and per-block row sums of squares;
 // the next product reads xb and scales its rows by 1 / rms(y).
 enum WstEpi { WEPI_F32 = 0, WEPI_RESID = 1, WEPI_GELU = 2, WEPI_SWIGLU = 3, WEPI_MERGE = 4 };
 struct WstArgs {
   int epi;
-  const uint4* xf;          // X, fragment-major bf16 [ceil(M/16)*16][K]
-  const float* ssp;         // WEPI_F32 / GELU / SWIGLU: per-block row sums of squares of y, [nt_in][64]
+  const uint4* xf;          // X, fragment-major bf16 [Mp][K]: Mp = M rounded up to 16 (M <= 64) or to 64
+  const float* ssp;         // WEPI_F32 / GELU / SWIGLU: per-block row sums of squares of y, [nt_in][ld_ss]
   int nt_in;                // D / 16 blocks (<= 128)
+  int ld_ss;                // row stride of the sums-of-squares arrays: a multiple of 64, >= M
   float eps;
   const uint16_t* e;        // WEPI_MERGE: e of the state, bf16 [M][T][D], row t
   int T, t, D;
@@ -156,18 +158,19 @@ struct WstArgs {
   float* outf;              // WEPI_F32 output (row-major), WEPI_RESID / WEPI_MERGE residual y (fp32, ldo)
   uint16_t* outb;           // WEPI_GELU / WEPI_SWIGLU activation, fragment-major bf16 with K = ldo
   int ldo;                  // output columns (N, or N / 2 for the paired epilogues)
-  float* ssp_out;           // WEPI_RESID / WEPI_MERGE: [ldo/16][64] row sums of squares of each 16-column block
+  float* ssp_out;           // WEPI_RESID / WEPI_MERGE: [ldo/16][ld_ss] row sums of squares of each 16-column block
   const float* gain_next;   // WEPI_RESID (optional) / WEPI_MERGE: gain of the next norm [D]
   uint16_t* xb_out;         // with gain_next: bf16(gain_next * y), fragment-major with K = ldo
   const float* bias;        // WEPI_MERGE: b_g [D]
 };
 bool wsn_supported(int M, int N, int K);
 hipError_t launch_wsn(const WstArgs& a, hipStream_t st);
-// The merge's X = [e_t ; bf16(s)] as a fragment-major bf16 [ceil(M/16)*16][2D] matrix (padding rows zero).
-hipError_t launch_merge_x(const uint16_t* e, const float* s, void* xf, int M, int T, int D, int t, hipStream_t st);
+// The merge's X = [e_t ; bf16(s)] as a fragment-major bf16 [Mp][2D] matrix (rows M..Mp-1 zero).
+hipError_t launch_merge_x(const uint16_t* e, const float* s, void* xf, int M, int Mp, int T, int D, int t,
+                          hipStream_t st);
 // s = g * y / rms(y) from the per-block sums of squares (nt blocks); also s_out[b][step] when set.
-hipError_t launch_final_norm_ssp(const float* y, const float* ssp, int nt, const float* gain, float* s, float* s_out,
-                                 int B, int D, float eps, int step, int n, hipStream_t st);
+hipError_t launch_final_norm_ssp(const float* y, const float* ssp, int nt, int ld_ss, const float* gain, float* s,
+                                 float* s_out, int B, int D, float eps, int step, int n, hipStream_t st);
 // Fragment-major bf16 copy of the merge matrix [2D][2D] from the fp32 W_ge, W_gs, W_fb [D][D].
 hipError_t launch_pack_merge_frag(const float* wge, const float* wgs, const float* wfb, void* dst, int D,
                                   hipStream_t st);

@@ -1,11 +1,12 @@
-// Weight-streaming products of the batched decoder step at decode-sized batches (M <= 64
-// sequences, bf16): Y[M, N] = X[M, K] W^T, with every weight byte read from HBM once per step
-// and shared by the M sequences ([FI] feinterview "普林斯顿提出 RLT：跨 Token 携带解码器状态的循环
+// Weight-streaming products of the batched decoder step (M <= 512 sequences, bf16):
+// Y[M, N] = X[M, K] W^T, with every weight byte read from HBM once per step and shared by the
+// M sequences ([FI] feinterview "普林斯顿提出 RLT：跨 Token 携带解码器状态的循环
 // Transformer", model-hardware co-design principle: ready updates of independent sequences
 // share one batched kernel; the tied layer weights are streamed once per step).
 //
 // One workgroup of NW waves owns one 16-column block of the output (a gate/up or gate/feedback
-// pair of blocks for the paired epilogues) over all M rows and the whole of K.  Its waves split K
+// pair of blocks for the paired epilogues) over one group of up to 64 rows and the whole of K
+// (past 64 rows, grid y walks the row groups; their reads of a weight block meet in L2).  Its waves split K
 // into contiguous runs of 64-wide stages, so every CU streams weight bytes that no other CU
 // reads, and no workgroup waits for another.  Both operands come from fragment-major copies, so
 // every load instruction of a wave reads one contiguous kilobyte:
@@ -40,6 +41,7 @@ namespace rlt {
 namespace {
 
 constexpr int kWsnMaxTiles = 128;  // most 16-column sums of squares per row (D <= 2048)
+constexpr int kWsnMaxRows = 512;   // rows of one product: up to 8 row groups of 64
 
 constexpr bool scales_rows(int EPI) { return EPI == WEPI_F32 || EPI == WEPI_GELU || EPI == WEPI_SWIGLU; }
 
@@ -59,14 +61,15 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
   __shared__ float rpart[NP][64];
   __shared__ float inv[64];
   const int unit = blockIdx.x;
+  const int r0 = blockIdx.y * 64;   // first row of this workgroup's row group (one group up to 64 rows)
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int cbw = wave % NCB, kw = wave / NCB;
   const int cb = unit * NCB + cbw;
   const int nst_all = a.K / 64, base = nst_all / KW, rem = nst_all % KW;
   const int s_lo = kw * base + min(kw, rem), nst = base + (kw < rem ? 1 : 0);
   const uint4* wbase = a.wf + (static_cast<size_t>(cb) * nst_all + s_lo) * 128 + lane;
-  const uint4* xbase = a.xf + static_cast<size_t>(s_lo) * 128 + lane;
   const size_t xblk = static_cast<size_t>(nst_all) * 128;   // pieces per 16-row block of X
+  const uint4* xbase = a.xf + (r0 / 16) * xblk + static_cast<size_t>(s_lo) * 128 + lane;
   uint4 wb[NSR][2], xr[NSR][MB][2];
   auto load_stage = [&](int r, int s) {
     const uint4* q = wbase + static_cast<size_t>(s) * 128;
@@ -87,7 +90,8 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
   const int srow = tid % 64, spart = tid / 64;
   if constexpr (scales_rows(EPI)) {
 #pragma unroll
-    for (int u = 0; u < UM; ++u) ssv[u] = a.ssp[min(spart + NP * u, a.nt_in - 1) * 64 + min(srow, ROWS - 1)];
+    for (int u = 0; u < UM; ++u)
+      ssv[u] = a.ssp[static_cast<size_t>(min(spart + NP * u, a.nt_in - 1)) * a.ld_ss + r0 + min(srow, ROWS - 1)];
   }
   f32x4_t acc[MB];
 #pragma unroll
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
     const int ob = tid + NT * j;
     if (ob >= NOB * ROWS * 16) break;   // uniform per wave (ROWS * 16 is a multiple of 64)
     const int b = ob / (ROWS * 16), o = ob % (ROWS * 16);
-    const int row = o / 16, c = o % 16;
+    const int lrow = o / 16, c = o % 16, row = r0 + lrow;
     const int blk = unit * NOB + b, oc = blk * 16 + c;
     float v0 = red[b][o];
 #pragma unroll
@@ -149,8 +153,8 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
     }
     const bool ok = row < a.M;
     if constexpr (scales_rows(EPI)) {
-      v0 *= inv[row];
-      v1 *= inv[row];
+      v0 *= inv[lrow];
+      v1 *= inv[lrow];
     }
     if constexpr (EPI == WEPI_F32) {
       if (ok) a.outf[static_cast<size_t>(row) * a.ldo + oc] = v0;
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
         sq = y * y;
       }
       sq = group_sum<16>(sq);
-      if (c == 0) a.ssp_out[blk * 64 + row] = sq;
+      if (c == 0) a.ssp_out[static_cast<size_t>(blk) * a.ld_ss + row] = sq;
     }
   }
 }
@@ -202,13 +206,13 @@ __global__ __launch_bounds__(256) void merge_x_k(const bf16_t* __restrict__ e, c
 
 // s = g * y / rms(y) with the row sums of squares from per-block partials; also s_out[b][step].
 __global__ __launch_bounds__(256) void final_norm_ssp_k(const float* __restrict__ y, const float* __restrict__ ssp,
-                                                        int nt, const float* __restrict__ gain, float* __restrict__ s,
+                                                        int nt, int ld_ss, const float* __restrict__ gain, float* __restrict__ s,
                                                         float* __restrict__ s_out, int D, float eps, int step, int n) {
   const int b = blockIdx.x;
   __shared__ float inv_s;
   if (threadIdx.x < 64) {   // lane j adds blocks j, j + 64, ...; the lanes' sums in a fixed order
     float ss = 0.f;
-    for (int j = threadIdx.x; j < nt; j += 64) ss += ssp[j * 64 + b];
+    for (int j = threadIdx.x; j < nt; j += 64) ss += ssp[static_cast<size_t>(j) * ld_ss + b];
     ss = group_sum<64>(ss);
     if (threadIdx.x == 0) inv_s = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
   }
@@ -260,7 +264,8 @@ constexpr int wsn_ring() {
 template <int MB, int EPI, int NCB>
 hipError_t launch_wsn_t(const WstArgs& a, hipStream_t st) {
   constexpr int NW = 16;
-  wsn_k<MB, EPI, NW, wsn_ring<MB, NW>(), NCB><<<a.N / (16 * NCB), NW * 64, 0, st>>>(a);
+  const dim3 grid(static_cast<unsigned>(a.N / (16 * NCB)), static_cast<unsigned>((a.M + 63) / 64));
+  wsn_k<MB, EPI, NW, wsn_ring<MB, NW>(), NCB><<<grid, NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -276,17 +281,19 @@ hipError_t launch_wsn_nw(const WstArgs& a, hipStream_t st) {
   // 16 waves per workgroup; two independent column blocks per workgroup once the single-block
   // grid would take more than one round of the chip's CUs (measured on the step's shapes)
   if constexpr (EPI == WEPI_SWIGLU || EPI == WEPI_MERGE) return launch_wsn_mb<EPI, 2>(a, st);
-  else return a.N / 16 >= 384 ? launch_wsn_mb<EPI, 2>(a, st) : launch_wsn_mb<EPI, 1>(a, st);
+  else return a.N / 16 * ((a.M + 63) / 64) >= 384 ? launch_wsn_mb<EPI, 2>(a, st) : launch_wsn_mb<EPI, 1>(a, st);
 }
 
 }  // namespace
 
 bool wsn_supported(int M, int N, int K) {
-  return M >= 1 && M <= 64 && N % 32 == 0 && K % 64 == 0;
+  return M >= 1 && M <= kWsnMaxRows && N % 32 == 0 && K % 64 == 0;
 }
 
 hipError_t launch_wsn(const WstArgs& a, hipStream_t st) {
-  if (!wsn_supported(a.M, a.N, a.K) || !a.wf || !a.xf) return hipErrorInvalidValue;
+  if (!wsn_supported(a.M, a.N, a.K) || !a.wf || !a.xf || a.ld_ss < 64 || a.ld_ss % 64 != 0 ||
+      a.ld_ss < (a.M + 63) / 64 * 64)
+    return hipErrorInvalidValue;
   const bool scale = scales_rows(a.epi);
   if ((scale && (!a.ssp || a.nt_in < 1 || a.nt_in > kWsnMaxTiles)) ||
       (a.epi == WEPI_F32 && !a.outf) || ((a.epi == WEPI_GELU || a.epi == WEPI_SWIGLU) && !a.outb) ||
@@ -304,17 +311,18 @@ hipError_t launch_wsn(const WstArgs& a, hipStream_t st) {
   }
 }
 
-hipError_t launch_merge_x(const uint16_t* e, const float* s, void* xf, int M, int T, int D, int t, hipStream_t st) {
-  if (M < 1 || M > 64 || D % 64 != 0) return hipErrorInvalidValue;
-  const int n = (M + 15) / 16 * (2 * D / 64) * 128;
+hipError_t launch_merge_x(const uint16_t* e, const float* s, void* xf, int M, int Mp, int T, int D, int t,
+                          hipStream_t st) {
+  if (M < 1 || Mp < M || Mp % 16 != 0 || D % 64 != 0) return hipErrorInvalidValue;
+  const int n = Mp / 16 * (2 * D / 64) * 128;
   merge_x_k<<<(n + 255) / 256, 256, 0, st>>>(e, s, static_cast<uint4*>(xf), M, T, D, t, n);
   return hipGetLastError();
 }
 
-hipError_t launch_final_norm_ssp(const float* y, const float* ssp, int nt, const float* gain, float* s, float* s_out,
-                                 int B, int D, float eps, int step, int n, hipStream_t st) {
-  if (D % 4 != 0 || B > 64) return hipErrorInvalidValue;
-  final_norm_ssp_k<<<B, 256, 0, st>>>(y, ssp, nt, gain, s, s_out, D, eps, step, n);
+hipError_t launch_final_norm_ssp(const float* y, const float* ssp, int nt, int ld_ss, const float* gain, float* s,
+                                 float* s_out, int B, int D, float eps, int step, int n, hipStream_t st) {
+  if (D % 4 != 0 || ld_ss < B) return hipErrorInvalidValue;
+  final_norm_ssp_k<<<B, 256, 0, st>>>(y, ssp, nt, ld_ss, gain, s, s_out, D, eps, step, n);
   return hipGetLastError();
 }
 

@@ -40,12 +40,16 @@ def dev():
 
 
 # (workload, layers kept, T replayed, sequences compared).
-#   300m: B=512 (B*H = 8192 pairs: the one-wave window kernel), W=128 so the ring of 127 entries
-#         wraps twice by t=300, two 256-key memory chunks, G = L.
-#   long: B=16 (every product on the weight-streaming kernel), W=512 so the ring of 511 wraps
-#         three times by t=2100, nine memory chunks, G = 1.
+#   300m:  B=512 (B*H = 8192 pairs: the one-wave window kernel), W=128 so the ring of 127 entries
+#          wraps twice by t=300, two 256-key memory chunks, G = L.
+#   ref48: B=64, d=2048, head_dim 128 (the weight-streaming products with two column blocks per
+#          workgroup for QKV, the 8-wave window kernel), W=256 so the ring of 255 entries wraps
+#          by t=300, two memory chunks, five 64-key encoder tiles, G = 1.
+#   long:  B=16 (one 16-row block in every product), W=512 so the ring of 511 wraps three times
+#          by t=2100, nine memory chunks, G = 1.
 SHAPES = [
     ("300m", 2, 300, [0, 511]),
+    ("ref48", 2, 300, [0, 63]),
     ("long", 2, 2100, [0]),
 ]
 
@@ -73,7 +77,8 @@ def test_large_shape_two_layers_every_position(dev, name, layers, T, seqs):
     del model, state, S, Z
     torch.cuda.empty_cache()
     t0 = time.time()
-    S_ref, Z_ref = oracle_replay(cfg, w, tok, seqs)
+    # the 2048-wide weights (about 1 GB) are not worth pickling to worker processes
+    S_ref, Z_ref = oracle_replay(cfg, w, tok, seqs, workers=1 if cfg.d_model >= 2048 else None)
     log(f"  [{name}] oracle done in {time.time() - t0:.1f} s")
     check(f"{name} x{layers} s_t", S_gpu, S_ref, cfg.dtype)
     check(f"{name} x{layers} logits", Z_gpu, Z_ref, cfg.dtype)

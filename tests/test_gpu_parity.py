@@ -405,19 +405,27 @@ def test_paths_can_alternate_on_one_state(dev):
     np.testing.assert_allclose(S, S_ref, rtol=0, atol=2e-5)
 
 
-@pytest.mark.parametrize("B,ffn", [(6, "swiglu"), (5, "gelu"), (24, "swiglu")], ids=["ws_swiglu", "ws_gelu", "tiled"])
-def test_batched_split_k_is_deterministic(dev, B, ffn):
-    """The batched decoder splits its products over K and adds the partials in a fixed order.
-    With B <= 16 rows (bf16, d = 256) every product streams the weights from their fragment
-    copies (SwiGLU and GELU epilogues); with B = 24 the products with N >= K take the tiled
-    kernel split over K (two output tiles, two to four K slices).  Two replays of the same
-    input are bitwise equal, and both match the oracle."""
-    cfg = mcfg(vocab=128, d_model=256, n_heads=4, n_layers=2, ffn_dim=512, ffn_kind=ffn, window=6,
+# (B, FFN kind, FFN width): the weight-streaming products over one, two and four 16-row blocks
+# with padding rows (B = 5, 6, 24, 40), a GELU input product wide enough (F = 6144 >= 384
+# sixteen-column blocks) for two independent blocks per workgroup, and past 64 rows the tiled
+# products with K split over workgroups.
+SPLIT_CASES = [(6, "swiglu", 512), (5, "gelu", 512), (24, "swiglu", 512), (40, "gelu", 512), (8, "gelu", 6144),
+               (80, "swiglu", 512)]
+
+
+@pytest.mark.parametrize("B,ffn,F", SPLIT_CASES, ids=["ws_rows6", "ws_gelu_rows5", "ws_rows24", "ws_gelu_rows40",
+                                                      "ws_gelu_two_blocks", "tiled_rows80"])
+def test_batched_split_k_is_deterministic(dev, B, ffn, F):
+    """The batched decoder's products add partial sums in fixed orders: a weight-streaming
+    product (bf16, B <= 64, d = 256) adds its waves' K runs in wave order; past 64 rows the tiled
+    products split K over workgroups and add the slices in slice order.  Two replays of the
+    same input are bitwise equal, and both match the oracle."""
+    cfg = mcfg(vocab=128, d_model=256, n_heads=4, n_layers=2, ffn_dim=F, ffn_kind=ffn, window=6,
                mem_groups=2, dtype="bf16")
     w = make_weights(cfg, 91)
     tok = make_tokens(cfg.vocab, B, 40, "uniform", 92)
     runs = [gpu_replay(cfg, w, tok, dev, path=2) for _ in range(2)]
     assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1])
     S_ref, Z_ref = oracle_replay(cfg, w, tok)
-    check("split-K batched s_t", runs[0][0], S_ref, "bf16")
-    check("split-K batched logits", runs[0][1], Z_ref, "bf16")
+    check("batched s_t", runs[0][0], S_ref, "bf16")
+    check("batched logits", runs[0][1], Z_ref, "bf16")
