@@ -47,10 +47,11 @@ constexpr bool scales_rows(int EPI) { return EPI == WEPI_F32 || EPI == WEPI_GELU
 
 template <int MB, int EPI, int NW, int NSR, int NCB>
 __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
-  // NCB column blocks per workgroup: the two members of a pair for the paired epilogues, else
-  // one or two independent blocks (two share each X load through the CU's L1)
+  // NCB column blocks per workgroup (their waves share each X load through the CU's L1): whole
+  // pairs for the paired epilogues (block 2p the gate, 2p+1 its partner), else independent blocks
   constexpr bool PAIRED = EPI == WEPI_SWIGLU || EPI == WEPI_MERGE;
-  static_assert(!PAIRED || NCB == 2, "paired epilogues take two blocks");
+  static_assert(NCB == 1 || NCB == 2 || NCB == 4 || NCB == 8, "column blocks per workgroup");
+  static_assert(!PAIRED || NCB >= 2, "paired epilogues take whole pairs");
   constexpr int KW = NW / NCB;                                               // K runs per column block
   constexpr int NT = NW * 64;
   constexpr int ROWS = 16 * MB;
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
   }
   // epilogue: output o = (block b, row, column c of the block); 16 lanes hold the 16 columns of
   // one row.  A pair yields one output block (the pair's index), independent blocks one each.
-  constexpr int NOB = PAIRED ? 1 : NCB;   // output blocks per workgroup
+  constexpr int NOB = PAIRED ? NCB / 2 : NCB;   // output blocks per workgroup
 #pragma unroll
   for (int j = 0; j < (NOB * ROWS * 16 + NT - 1) / NT; ++j) {
     const int ob = tid + NT * j;
@@ -142,14 +143,15 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
     const int b = ob / (ROWS * 16), o = ob % (ROWS * 16);
     const int lrow = o / 16, c = o % 16, row = r0 + lrow;
     const int blk = unit * NOB + b, oc = blk * 16 + c;
-    float v0 = red[b][o];
+    const int c0 = PAIRED ? 2 * b : b;   // this output's (first) column block in the workgroup
+    float v0 = red[c0][o];
 #pragma unroll
-    for (int k = 1; k < KW; ++k) v0 += red[k * NCB + b][o];
+    for (int k = 1; k < KW; ++k) v0 += red[k * NCB + c0][o];
     float v1 = 0.f;
     if constexpr (PAIRED) {
-      v1 = red[1][o];
+      v1 = red[c0 + 1][o];
 #pragma unroll
-      for (int k = 1; k < KW; ++k) v1 += red[k * NCB + 1][o];
+      for (int k = 1; k < KW; ++k) v1 += red[k * NCB + c0 + 1][o];
     }
     const bool ok = row < a.M;
     if constexpr (scales_rows(EPI)) {
@@ -278,10 +280,19 @@ hipError_t launch_wsn_mb(const WstArgs& a, hipStream_t st) {
 
 template <int EPI>
 hipError_t launch_wsn_nw(const WstArgs& a, hipStream_t st) {
-  // 16 waves per workgroup; two independent column blocks per workgroup once the single-block
-  // grid would take more than one round of the chip's CUs (measured on the step's shapes)
-  if constexpr (EPI == WEPI_SWIGLU || EPI == WEPI_MERGE) return launch_wsn_mb<EPI, 2>(a, st);
-  else return a.N / 16 * ((a.M + 63) / 64) >= 384 ? launch_wsn_mb<EPI, 2>(a, st) : launch_wsn_mb<EPI, 1>(a, st);
+  // 16 waves per workgroup (measured on the step's shapes).  Up to 64 rows: two independent
+  // column blocks per workgroup once the single-block grid would take more than one round of the
+  // chip's CUs, one pair for the paired epilogues.  Past 64 rows every row group re-reads X per
+  // workgroup, so a workgroup takes more columns: two independent blocks, or the most pairs
+  // (up to four) that still leave at least 256 workgroups.
+  const int groups = (a.M + 63) / 64, nb = a.N / 16;
+  if constexpr (EPI == WEPI_SWIGLU || EPI == WEPI_MERGE) {
+    if (groups > 1 && nb % 8 == 0 && nb / 8 * groups >= 256) return launch_wsn_mb<EPI, 8>(a, st);
+    if (groups > 1 && nb % 4 == 0 && nb / 4 * groups >= 256) return launch_wsn_mb<EPI, 4>(a, st);
+    return launch_wsn_mb<EPI, 2>(a, st);
+  } else {
+    return nb * groups >= 384 ? launch_wsn_mb<EPI, 2>(a, st) : launch_wsn_mb<EPI, 1>(a, st);
+  }
 }
 
 }  // namespace
