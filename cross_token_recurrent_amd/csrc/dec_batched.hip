@@ -22,6 +22,7 @@
 //   qkv fp32 [B][3D] | attn [B][D] | act [B][F] | part fp32 [B][H][NSMAX][DH+2]
 #include <algorithm>
 
+#include "act_layout.h"
 #include "device_common.h"
 #include "rlt_internal.h"
 

@@ -72,20 +72,7 @@ __device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
 }
 
-// Offset of element [row][k] of a bf16 activation matrix with K columns (K % 64 == 0).  With
-// frag == 0 it is row-major.  With frag != 0 it is the fragment-major layout the weight-streaming
-// products read as their matrix-core A operand: the 16-byte piece ((i * K/64 + s) * 2 + h) * 64 +
-// lane holds X[16 i + lane % 16][64 s + 16 (lane / 16) + 8 h .. + 8], so that one load
-// instruction of a wave reads one contiguous kilobyte of a 16-row block.
-__device__ __forceinline__ size_t act_offset(int row, int k, int K, int frag) {
-  if (!frag) return static_cast<size_t>(row) * K + k;
-  const int kk = k & 63;
-  const size_t piece =
-      ((static_cast<size_t>(row >> 4) * (K >> 6) + (k >> 6)) * 2 + ((kk >> 3) & 1)) * 64 + (row & 15) + 16 * (kk >> 4);
-  return piece * 8 + (kk & 7);
-}
-
-__device__ __forceinline__ float gelu_erf(float x){ return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 

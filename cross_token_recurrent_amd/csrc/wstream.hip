@@ -34,6 +34,7 @@
 //               interleaved in blocks of 16, plus xb and the sums of squares for the first norm.
 // Rows past M are carried through the products (their fragment pieces are never written) and
 // never stored: a matrix-core output row depends only on the same row of A.
+#include "act_layout.h"
 #include "device_common.h"
 #include "rlt_internal.h"
 
