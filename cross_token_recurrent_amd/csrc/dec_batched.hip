@@ -36,10 +36,10 @@ bool use_wst(const ModelLayout& m, int B) {
   return m.has_frag && m.dtype == RLT_DTYPE_BF16 && B <= 512 && m.D <= 2048 && m.D % 64 == 0 && m.F % 32 == 0;
 }
 
-// Rows of the products' fragment-major operands (whole 16-row blocks, whole 64-row groups past
-// 64 rows) and the row stride of their sums-of-squares arrays.
-int padded_rows(int B) { return B <= 64 ? (B + 15) / 16 * 16 : (B + 63) / 64 * 64; }
-int ss_stride(int B) { return B <= 64 ? 64 : (B + 63) / 64 * 64; }
+// Rows of the products' fragment-major operands (whole 64-row groups, so that every row-group
+// size the products choose stays inside them) and the row stride of their sums-of-squares arrays.
+int padded_rows(int B) { return (B + 63) / 64 * 64; }
+int ss_stride(int B) { return (B + 63) / 64 * 64; }
 
 struct Scratch {
   size_t y, h, xin, gpre, fb, qkv, attn, act, part, splitk, ssp, cnt, xcnt, total;

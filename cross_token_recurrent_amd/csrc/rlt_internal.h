@@ -146,7 +146,7 @@ hipError_t launch_pack_frag(const void* w, void* dst, int N, int K, hipStream_t 
 enum WstEpi { WEPI_F32 = 0, WEPI_RESID = 1, WEPI_GELU = 2, WEPI_SWIGLU = 3, WEPI_MERGE = 4 };
 struct WstArgs {
   int epi;
-  const uint4* xf;          // X, fragment-major bf16 [Mp][K]: Mp = M rounded up to 16 (M <= 64) or to 64
+  const uint4* xf;          // X, fragment-major bf16 [Mp][K]: Mp = M rounded up to 64
   const float* ssp;         // WEPI_F32 / GELU / SWIGLU: per-block row sums of squares of y, [nt_in][ld_ss]
   int nt_in;                // D / 16 blocks (<= 128)
   int ld_ss;                // row stride of the sums-of-squares arrays: a multiple of 64, >= M

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(NW * 64) void wsn_k(WstArgs a) {
   __shared__ float rpart[NP][64];
   __shared__ float inv[64];
   const int unit = blockIdx.x;
-  const int r0 = blockIdx.y * 64;   // first row of this workgroup's row group (one group up to 64 rows)
+  const int r0 = blockIdx.y * ROWS;   // first row of this workgroup's group of ROWS rows
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int cbw = wave % NCB, kw = wave / NCB;
   const int cb = unit * NCB + cbw;
@@ -267,15 +267,23 @@ constexpr int wsn_ring() {
 template <int MB, int EPI, int NCB>
 hipError_t launch_wsn_t(const WstArgs& a, hipStream_t st) {
   constexpr int NW = 16;
-  const dim3 grid(static_cast<unsigned>(a.N / (16 * NCB)), static_cast<unsigned>((a.M + 63) / 64));
+  const dim3 grid(static_cast<unsigned>(a.N / (16 * NCB)), static_cast<unsigned>((a.M + 16 * MB - 1) / (16 * MB)));
   wsn_k<MB, EPI, NW, wsn_ring<MB, NW>(), NCB><<<grid, NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
 template <int EPI, int NCB>
 hipError_t launch_wsn_mb(const WstArgs& a, hipStream_t st) {
-  if (a.M <= 16) return launch_wsn_t<1, EPI, NCB>(a, st);
-  if (a.M <= 32) return launch_wsn_t<2, EPI, NCB>(a, st);
+  // 16-row blocks per row group: enough for all rows up to 64; a product whose grid would leave
+  // half the CUs without a weight stream of their own takes groups of half the rows when the
+  // doubled grid still fits one round of the chip (the groups of one column block are adjacent
+  // in dispatch order modulo the XCD count when N/(16 NCB) is a multiple of 8, so they share its
+  // weight stream through one L2)
+  int mb = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
+  const int units = a.N / (16 * NCB);
+  if (a.M <= 64 && mb > 1 && 2 * units * ((a.M + 16 * mb - 1) / (16 * mb)) <= 256) mb /= 2;
+  if (mb == 1) return launch_wsn_t<1, EPI, NCB>(a, st);
+  if (mb == 2) return launch_wsn_t<2, EPI, NCB>(a, st);
   return launch_wsn_t<4, EPI, NCB>(a, st);
 }
 
@@ -304,7 +312,7 @@ bool wsn_supported(int M, int N, int K) {
 
 hipError_t launch_wsn(const WstArgs& a, hipStream_t st) {
   if (!wsn_supported(a.M, a.N, a.K) || !a.wf || !a.xf || a.ld_ss < 64 || a.ld_ss % 64 != 0 ||
-      a.ld_ss < (a.M + 63) / 64 * 64)
+      a.ld_ss < (a.M + 63) / 64 * 64)   // (operands are padded to whole 64-row groups)
     return hipErrorInvalidValue;
   const bool scale = scales_rows(a.epi);
   if ((scale && (!a.ssp || a.nt_in < 1 || a.nt_in > kWsnMaxTiles)) ||
