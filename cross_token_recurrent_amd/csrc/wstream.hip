@@ -291,13 +291,16 @@ template <int EPI>
 hipError_t launch_wsn_nw(const WstArgs& a, hipStream_t st) {
   // 16 waves per workgroup (measured on the step's shapes).  Up to 64 rows: two independent
   // column blocks per workgroup once the single-block grid would take more than one round of the
-  // chip's CUs, one pair for the paired epilogues.  Past 64 rows every row group re-reads X per
+  // chip's CUs, one or two pairs for the paired epilogues.  Past 64 rows every row group re-reads X per
   // workgroup, so a workgroup takes more columns: two independent blocks, or the most pairs
   // (up to four) that still leave at least 256 workgroups.
   const int groups = (a.M + 63) / 64, nb = a.N / 16;
   if constexpr (EPI == WEPI_SWIGLU || EPI == WEPI_MERGE) {
     if (groups > 1 && nb % 8 == 0 && nb / 8 * groups >= 256) return launch_wsn_mb<EPI, 8>(a, st);
     if (groups > 1 && nb % 4 == 0 && nb / 4 * groups >= 256) return launch_wsn_mb<EPI, 4>(a, st);
+    // up to 64 rows: two pairs per workgroup when one pair per workgroup would take more than
+    // one round of the CUs and two take at most one (the reference model's FFN input)
+    if (groups == 1 && nb % 4 == 0 && nb / 2 > 256 && nb / 4 <= 256) return launch_wsn_mb<EPI, 4>(a, st);
     return launch_wsn_mb<EPI, 2>(a, st);
   } else {
     return nb * groups >= 384 ? launch_wsn_mb<EPI, 2>(a, st) : launch_wsn_mb<EPI, 1>(a, st);
