@@ -140,6 +140,10 @@ __global__ __launch_bounds__(NTH) void enc_attn_mfma_k(AttnArgs a) {
   constexpr int BQ = 64, BK = 64;
   constexpr int KP = DH + 8;        // K tile row pitch (elements; rows stay 16-byte aligned)
   constexpr int VP = BK + 8;        // V^T tile row pitch
+  // V^T row d holds key j at column j ^ vsw(d): the 16 lanes that store one key's 8-dim chunks
+  // (dims 8 apart) then land in 8 different banks instead of one, and the groups of four keys
+  // the products read stay contiguous (the swizzle only flips key bits 2..4)
+  auto vsw = [](int d) { return 4 * ((d >> 3) & 7); };
   constexpr int ND = DH / 16;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[BK * KP];
@@ -179,10 +183,11 @@ __global__ __launch_bounds__(NTH) void enc_attn_mfma_k(AttnArgs a) {
       }
       *reinterpret_cast<uint4*>(Ks + j * KP + d0) = kv;
       const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+      const int jc = j ^ vsw(d0);   // the eight dims of a chunk share their 8-block
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Vt[(d0 + 2 * i) * VP + j] = static_cast<bf16_t>(w[i] & 0xffffu);
-        Vt[(d0 + 2 * i + 1) * VP + j] = static_cast<bf16_t>(w[i] >> 16);
+        Vt[(d0 + 2 * i) * VP + jc] = static_cast<bf16_t>(w[i] & 0xffffu);
+        Vt[(d0 + 2 * i + 1) * VP + jc] = static_cast<bf16_t>(w[i] >> 16);
       }
     }
     __syncthreads();
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(NTH) void enc_attn_mfma_k(AttnArgs a) {
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const s4_t va = *reinterpret_cast<const s4_t*>(Vt + (16 * dt + col) * VP + 16 * ks + 4 * grp);
+        const s4_t va = *reinterpret_cast<const s4_t*>(Vt + (16 * dt + col) * VP + ((16 * ks + 4 * grp) ^ vsw(16 * dt + col)));
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pk[ks], o[dt], 0, 0, 0);
       }
   }
