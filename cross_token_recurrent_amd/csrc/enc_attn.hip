@@ -172,25 +172,43 @@ __global__ __launch_bounds__(NTH) void enc_attn_mfma_k(AttnArgs a) {
 
   const bf16_t* kb = static_cast<const bf16_t*>(a.k) + b * a.kv_ld_b + h * a.kv_ld_h;
   const bf16_t* vb = static_cast<const bf16_t*>(a.v) + b * a.kv_ld_b + h * a.kv_ld_h;
-  for (int k0 = 0; k0 < kend; k0 += BK) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < BK * DH / 8; c += NTH) {
+  // the next tile's K and V chunks are requested into registers before this tile's products, so
+  // their latency overlaps the matrix work; they go to LDS after the next barrier
+  constexpr int NCH = (BK * DH / 8 + NTH - 1) / NTH;   // 16-byte chunks per thread and tile
+  uint4 kpre[NCH], vpre[NCH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = threadIdx.x + i * NTH;
       const int j = c / (DH / 8), d0 = (c % (DH / 8)) * 8;
       uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
-      if (k0 + j < kend) {
+      if (c < BK * DH / 8 && k0 + j < kend) {
         kv = *reinterpret_cast<const uint4*>(kb + static_cast<size_t>(k0 + j) * a.kv_ld_t + d0);
         vv = *reinterpret_cast<const uint4*>(vb + static_cast<size_t>(k0 + j) * a.kv_ld_t + d0);
       }
-      *reinterpret_cast<uint4*>(Ks + j * KP + d0) = kv;
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+      kpre[i] = kv;
+      vpre[i] = vv;
+    }
+  };
+  gload(0);
+  for (int k0 = 0; k0 < kend; k0 += BK) {
+    __syncthreads();   // every read of the previous tile is done
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = threadIdx.x + i * NTH;
+      if (c >= BK * DH / 8) break;
+      const int j = c / (DH / 8), d0 = (c % (DH / 8)) * 8;
+      *reinterpret_cast<uint4*>(Ks + j * KP + d0) = kpre[i];
+      const uint32_t w[4] = {vpre[i].x, vpre[i].y, vpre[i].z, vpre[i].w};
       const int jc = j ^ vsw(d0);   // the eight dims of a chunk share their 8-block
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Vt[(d0 + 2 * i) * VP + jc] = static_cast<bf16_t>(w[i] & 0xffffu);
-        Vt[(d0 + 2 * i + 1) * VP + jc] = static_cast<bf16_t>(w[i] >> 16);
+      for (int q = 0; q < 4; ++q) {
+        Vt[(d0 + 2 * q) * VP + jc] = static_cast<bf16_t>(w[q] & 0xffffu);
+        Vt[(d0 + 2 * q + 1) * VP + jc] = static_cast<bf16_t>(w[q] >> 16);
       }
     }
     __syncthreads();
+    if (k0 + BK < kend) gload(k0 + BK);
     if (k0 > wave_last) continue;   // uniform: the whole tile lies after this wave's queries
 
     // S^T sub-tiles of 16 keys: lane holds keys k0 + 16ks + 4grp + v of query col
