@@ -125,6 +125,15 @@ __global__ __launch_bounds__(NTH) void enc_attn_k(AttnArgs a) {
 typedef __attribute__((ext_vector_type(4))) short s4_t;    // four bf16: a 16x16x16 MFMA operand
 typedef __attribute__((ext_vector_type(4))) float f4_t;
 
+// D += A B on v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16][8 (l / 16) .. +8] and
+// B[8 (l / 16) .. +8][l % 16] as eight bf16 (any fixed order of the 32 contracted indices that the
+// two operands share), and D[4 (l / 16) + v][l % 16].
+__device__ __forceinline__ f4_t mfma32(const uint4& a, const uint4& b, f4_t c) {
+  return __builtin_bit_cast(f4_t, __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                          __builtin_bit_cast(bf16x8_t, b),
+                                                                          __builtin_bit_cast(f32x4_t, c), 0, 0, 0));
+}
+
 // sum / max over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float rows4_sum(float v) {
   v += __shfl_xor(v, 16, 64);
@@ -160,11 +169,20 @@ __global__ __launch_bounds__(NTH) void enc_attn_mfma_k(AttnArgs a) {
   const int wave_last = a.t0 + min(a.n - 1, qb * BQ + wave * 16 + 15);
   const float sc = kLog2e / sqrtf(static_cast<float>(DH));
 
-  // Q^T as the B operand of S^T = K Q^T: lane holds q[col][16kk + 4grp .. +4]
-  s4_t qreg[ND];
+  // Q^T as the B operand of S^T = K Q^T: lane holds q[col][32kc + 8grp .. +8] (d_h >= 32, the
+  // 16x16x32 products) or q[col][16kk + 4grp .. +4] (d_h = 16)
+  constexpr bool K32 = DH >= 32;
+  constexpr int NQ8 = K32 ? DH / 32 : 1, NQ4 = K32 ? 1 : ND;
+  uint4 qreg8[NQ8];
+  s4_t qreg[NQ4];
   const bf16_t* qp = static_cast<const bf16_t*>(a.q) + static_cast<size_t>(b * a.n + qc) * a.ldq + h * DH;
+  if constexpr (K32) {
 #pragma unroll
-  for (int kk = 0; kk < ND; ++kk) qreg[kk] = *reinterpret_cast<const s4_t*>(qp + 16 * kk + 4 * grp);
+    for (int kc = 0; kc < NQ8; ++kc) qreg8[kc] = *reinterpret_cast<const uint4*>(qp + 32 * kc + 8 * grp);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < ND; ++kk) qreg[kk] = *reinterpret_cast<const s4_t*>(qp + 16 * kk + 4 * grp);
+  }
   f4_t o[ND];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) o[dt] = f4_t{0.f, 0.f, 0.f, 0.f};
@@ -217,10 +235,16 @@ __global__ __launch_bounds__(NTH) void enc_attn_mfma_k(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (K32) {
 #pragma unroll
-      for (int kk = 0; kk < ND; ++kk) {
-        const s4_t ka = *reinterpret_cast<const s4_t*>(Ks + (16 * ks + col) * KP + 16 * kk + 4 * grp);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qreg[kk], acc, 0, 0, 0);
+        for (int kc = 0; kc < NQ8; ++kc)
+          acc = mfma32(*reinterpret_cast<const uint4*>(Ks + (16 * ks + col) * KP + 32 * kc + 8 * grp), qreg8[kc], acc);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < ND; ++kk) {
+          const s4_t ka = *reinterpret_cast<const s4_t*>(Ks + (16 * ks + col) * KP + 16 * kk + 4 * grp);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, qreg[kk], acc, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -247,14 +271,21 @@ __global__ __launch_bounds__(NTH) void enc_attn_mfma_k(AttnArgs a) {
       const uint32_t lo = pack_bf16x2(pr[0], pr[1]), hi = pack_bf16x2(pr[2], pr[3]);
       pk[ks] = __builtin_bit_cast(s4_t, make_uint2(lo, hi));
     }
-    // O^T[d][q] += V^T[d][keys] P^T[keys][q]
+    // O^T[d][q] += V^T[d][keys] P^T[keys][q], 32 keys per product: lane grp contracts keys
+    // 32p + 4grp .. +3 (from score tile 2p) and 32p + 16 + 4grp .. +3 (tile 2p + 1) on both operands
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
+    for (int dt = 0; dt < ND; ++dt) {
+      const int row = 16 * dt + col;
+      const bf16_t* vr = Vt + row * VP;
+      const int sw = vsw(row);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const s4_t va = *reinterpret_cast<const s4_t*>(Vt + (16 * dt + col) * VP + ((16 * ks + 4 * grp) ^ vsw(16 * dt + col)));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pk[ks], o[dt], 0, 0, 0);
+      for (int p = 0; p < 2; ++p) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr + ((32 * p + 4 * grp) ^ sw));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + ((32 * p + 16 + 4 * grp) ^ sw));
+        const uint2 p0 = __builtin_bit_cast(uint2, pk[2 * p]), p1 = __builtin_bit_cast(uint2, pk[2 * p + 1]);
+        o[dt] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), make_uint4(p0.x, p0.y, p1.x, p1.y), o[dt]);
       }
+    }
   }
   const float inv = 1.0f / rows4_sum(lp);
   if (qi < a.n) {
