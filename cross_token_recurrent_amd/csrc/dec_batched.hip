@@ -68,7 +68,7 @@ Scratch scratch_layout(const ModelLayout& m, int B, int T) {
   s.attn = take(Bp * D * e);
   s.act = take(Bp * static_cast<size_t>(m.F) * e);
   s.part = take(Bz * m.H * static_cast<size_t>(s.nsmax) * (m.DH + 2) * 4);
-  s.splitk = take(gemm_splitk_ws_floats(B, m.D) * 4);
+  s.splitk = take(use_wst(m, B) ? 0 : gemm_splitk_ws_floats(B, m.D) * 4);   // tiled products only
   // weight-streaming products: per-16-column-block row sums of squares, [D/16][ss_stride(B)]
   s.ssp = take(use_wst(m, B) ? D / 16 * ss_stride(B) * 4 : 0);
   // arrival counters of the cross-attention heads, zeroed by the state's reset

@@ -196,8 +196,9 @@ int rlt_decoder_replay(const rlt_model* model, rlt_state* state, int32_t n, floa
  * memory at call time (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation).  Same arguments, ordering rules, errors and results as
  * rlt_decoder_replay; it allocates nothing (no hipMalloc, no allocating library call).  The
- * batched decoder's per-step scratch (residual stream, projections, attention partials,
- * split-K partials and their arrival counters) lives in a library-owned static device array of
+ * batched decoder's per-step scratch (residual stream, projections, fragment-major product
+ * operands, norm partial sums, attention partials and their arrival counters, and the split-K
+ * partials of the tiled products) lives in a library-owned static device array of
  * 64 MiB, one per GPU, held until the process ends, instead of the state's scratch region.
  * RLT_ERR_UNSUPPORTED when the batch and t_max need more scratch than that.  Every call on one
  * GPU shares that GPU's array, which keeps the last call's contents: calls that overlap on one

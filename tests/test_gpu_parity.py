@@ -409,13 +409,13 @@ def test_paths_can_alternate_on_one_state(dev):
 # with padding rows (B = 5, 6, 24, 40), a GELU input product wide enough (F = 6144 >= 384
 # sixteen-column blocks) for two independent blocks per workgroup, two 64-row groups (B = 80),
 # and past 512 rows the tiled products with K split over workgroups (B = 520).
-SPLIT_CASES = [(6, "swiglu", 512), (5, "gelu", 512), (24, "swiglu", 512), (40, "gelu", 512), (8, "gelu", 6144),
+PRODUCT_CASES = [(6, "swiglu", 512), (5, "gelu", 512), (24, "swiglu", 512), (40, "gelu", 512), (8, "gelu", 6144),
                (80, "swiglu", 512), (520, "swiglu", 512)]
 
 
-@pytest.mark.parametrize("B,ffn,F", SPLIT_CASES, ids=["ws_rows6", "ws_gelu_rows5", "ws_rows24", "ws_gelu_rows40",
+@pytest.mark.parametrize("B,ffn,F", PRODUCT_CASES, ids=["ws_rows6", "ws_gelu_rows5", "ws_rows24", "ws_gelu_rows40",
                                                       "ws_gelu_two_blocks", "ws_row_groups80", "tiled_rows520"])
-def test_batched_split_k_is_deterministic(dev, B, ffn, F):
+def test_batched_products_are_deterministic(dev, B, ffn, F):
     """The batched decoder's products add partial sums in fixed orders: a weight-streaming
     product (bf16, B <= 512, d = 256) adds its waves' K runs in wave order; past 512 rows the
     tiled products split K over workgroups and add the slices in slice order.  Two replays of

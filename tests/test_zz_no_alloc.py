@@ -35,8 +35,8 @@ def _replay(model, tokens, dev, fn):
     return S.cpu().numpy()
 
 
-# (config, path): the weight-streaming batched step (bf16, d = 256: split-K partials, arrival
-# counters, fused norms) and the persistent decoder (no scratch at all)
+# (config, path): the weight-streaming batched step (bf16, d = 256: fragment-major operands, norm
+# partial sums, cross-attention arrival counters) and the persistent decoder (no scratch at all)
 CASES = [
     (dict(vocab=128, d_model=256, n_heads=4, n_layers=2, ffn_dim=512, ffn_kind="swiglu", window=6, mem_groups=2,
           dtype="bf16"), 2),
