@@ -11,22 +11,36 @@
 //   logp = z[drawn] - log sum_kept exp(z).
 //
 // One workgroup of 512 threads per row.  The row is staged through LDS so that thread t holds
-// the C consecutive logits [t*C, t*C + C) in registers (token-id order is then thread order
-// for every scan).  Both thresholds are found by a bitwise search over order-preserving
-// 32-bit keys: bit by bit from the top, a candidate key stays if the count (top-k) or the
-// mass (top-p) of elements at or above it still reaches the target.  Every count, sum and
-// scan is a fixed-order block reduction (wave shuffles, then the eight wave totals read in
-// wave order), so a row's result does not depend on scheduling.  Ties at a threshold are
-// resolved in id order with an exclusive scan of the per-thread tie counts.
+// the C consecutive logits [t*C, t*C + C) in registers as order-preserving 32-bit keys
+// (token-id order is then thread order for every scan).
+//
+// Top-k (k at most the thread count): the k-th largest of the per-thread maxima bounds the
+// k-th largest logit from below (k threads each hold an element at least that large).  The
+// elements at or above the bound are gathered into LDS in id order; when they fit one wave's
+// list, wave 0 finishes the row alone: the exact top-k threshold and its ties, the
+// probabilities of the survivors only, the top-p threshold and its ties, and the draw.  No
+// further pass over the whole row is made.
+//
+// Otherwise (no top-k, a larger k, or a bound that admits too many elements) every thread
+// keeps its C probabilities and both thresholds are found by a bitwise search: bit by bit from
+// the top, a candidate key stays if the count (top-k) or the mass (top-p) of elements at or
+// above it still reaches the target; the first bits are decided over all elements with block
+// reductions, the rest by one wave over the elements that share the decided prefix.  Ties at
+// a threshold are resolved in id order with an exclusive scan of the per-thread tie counts.
+//
+// Counts are taken with wave ballots (exact integers); every sum and scan is a fixed-order
+// reduction (wave shuffles, then the wave totals read in wave order), so a row's result does
+// not depend on scheduling.
 #include "device_common.h"
 #include "rlt_internal.h"
 
 namespace rlt {
 namespace {
 
-constexpr int ST = 512;            // threads per row
 constexpr int kListMax = 1024;     // undecided elements one wave finishes a threshold search on
 constexpr int kPrefixBits = 12;    // key bits decided over all elements first
+constexpr int kBoundBits = 16;     // top bits of the k-th largest thread maximum kept as the bound
+constexpr int ST = 512;            // threads per row
 constexpr int SW = ST / 64;        // waves
 constexpr float kLog2eS = 1.4426950408889634f;
 
@@ -52,15 +66,18 @@ __device__ __forceinline__ bool is_kept(float e) { return (__builtin_bit_cast(ui
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
+// lanes of the wave for which p holds (the same value on every lane)
+__device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
 
-// Block reductions: each uses its own slot of a two-deep ring, so one barrier per call is
-// enough (a slot is rewritten only after every thread has passed the next call's barrier).
-// Every thread adds the eight wave totals in wave order, so all threads hold the same value.
+// Block reductions over SW waves: each uses its own slot of a two-deep ring, so one barrier per
+// call is enough (a slot is rewritten only after every thread has passed the next call's
+// barrier).  Every thread adds the wave totals in wave order, so all threads hold the same value.
+template <int SW>
 struct Red {
   float* buf;   // [2][SW]
   int k = 0;
-  __device__ float sum(float v) {
-    v = wave_sum(v);
+  // v already equal on every lane of its wave (a ballot count)
+  __device__ float sum_waves(float v) {
     float* b = buf + (k & 1) * SW;
     ++k;
     if (threadIdx.x % 64 == 0) b[threadIdx.x / 64] = v;
@@ -70,6 +87,7 @@ struct Red {
     for (int w = 0; w < SW; ++w) s += b[w];
     return s;
   }
+  __device__ float sum(float v) { return sum_waves(wave_sum(v)); }
   __device__ float max(float v) {
     v = wave_max(v);
     float* b = buf + (k & 1) * SW;
@@ -81,8 +99,8 @@ struct Red {
     for (int w = 0; w < SW; ++w) s = fmaxf(s, b[w]);
     return s;
   }
-  // exclusive prefix of v over threads in order
-  __device__ float excl_scan(float v) {
+  // exclusive prefix of v over threads in order; `total` gets the sum over all threads
+  __device__ float excl_scan(float v, float& total) {
     const int lane = threadIdx.x % 64;
     float inc = v;
 #pragma unroll
@@ -94,25 +112,162 @@ struct Red {
     ++k;
     if (lane == 63) b[threadIdx.x / 64] = inc;
     __syncthreads();
-    float pre = 0.f;
-    for (int w = 0; w < static_cast<int>(threadIdx.x / 64); ++w) pre += b[w];
+    const int me = static_cast<int>(threadIdx.x / 64);
+    float pre = 0.f, tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < SW; ++w) {
+      pre += w < me ? b[w] : 0.f;
+      tot += b[w];
+    }
+    total = tot;
     return pre + inc - v;
   }
 };
+
+// Exclusive prefix over the lanes of one wave (lane order); lane 0 gets 0.
+__device__ __forceinline__ float wave_excl_scan(float v, float& inclusive) {
+  const int lane = threadIdx.x % 64;
+  float inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  inclusive = inc;
+  const float ex = __shfl_up(inc, 1, 64);
+  return lane == 0 ? 0.f : ex;
+}
+
+// Wave 0 finishes a row whose top-k candidates (every element at or above a bound that is at
+// most the k-th largest key) are listed in id order: keys lk[0..n), ids lid[0..n), n <= 64*P.
+// Lane l holds list entries l*P .. l*P + P - 1, so list order is lane order, then slot order.
+template <int P>
+__device__ void finish_on_list(const SampleArgs& a, int row, const uint32_t* lk, const int* lid, int n, float mz,
+                               float urow) {
+  const int lane = threadIdx.x;
+  uint32_t kk[P];
+  int id[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int j = lane * P + i;
+    kk[i] = j < n ? lk[j] : 0u;   // past the list: below every candidate key
+    id[i] = j < n ? lid[j] : 0;
+  }
+  // top-k: the largest key whose count at or above it still reaches k
+  const int k = a.top_k;
+  uint32_t tk = 0;
+#pragma nounroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tk | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) cnt += wave_count(kk[i] >= cand);
+    tk = cnt >= k ? cand : tk;
+  }
+  // ties at it stay in id order while fewer than k ids rank above them
+  int gt = 0;
+  float ties = 0.f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    gt += wave_count(kk[i] > tk);
+    ties += kk[i] == tk ? 1.f : 0.f;
+  }
+  const float need_eq = static_cast<float>(k - gt);
+  float tie_all;
+  float r = wave_excl_scan(ties, tie_all);
+  bool keep[P];
+  float e[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const bool tie = kk[i] == tk;
+    keep[i] = kk[i] > tk || (tie && r < need_eq);
+    r += tie ? 1.f : 0.f;
+    const float ev = __builtin_amdgcn_exp2f((funkey(kk[i]) * a.inv_temp - mz) * kLog2eS);
+    e[i] = keep[i] ? ev : 0.f;
+  }
+  // top-p over the survivors
+  if (a.top_p < 1.0f) {
+    float sk = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) sk += e[i];
+    const float need = a.top_p * wave_sum(sk);
+    uint32_t tp = 0;
+#pragma nounroll
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tp | (1u << bit);
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < P; ++i) m += kk[i] >= cand ? e[i] : 0.f;
+      tp = wave_sum(m) >= need ? cand : tp;
+    }
+    float gtm = 0.f, pt = 0.f, e_eq = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const bool tie = keep[i] && kk[i] == tp;
+      gtm += keep[i] && kk[i] > tp ? e[i] : 0.f;
+      pt += tie ? 1.f : 0.f;
+      e_eq = tie ? e[i] : e_eq;
+    }
+    const float mass_gt = wave_sum(gtm);
+    e_eq = wave_max(e_eq);   // every tie has the same key, so the same probability
+    float pt_all;
+    float rp = wave_excl_scan(pt, pt_all);
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const bool tie = keep[i] && kk[i] == tp;
+      // a tie stays while the mass ranked before it is still short of the target
+      keep[i] = (keep[i] && kk[i] > tp) || (tie && mass_gt + rp * e_eq < need);
+      rp += tie ? 1.f : 0.f;
+      e[i] = keep[i] ? e[i] : 0.f;
+    }
+  }
+  // draw: inverse CDF over the kept ids in increasing order
+  float mine = 0.f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) mine += e[i];
+  float inc;
+  float run = wave_excl_scan(mine, inc);
+  const float Sp = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inc), 63));
+  const float target = urow * Sp;
+  int lo = 0x7fffffff, hi = -1;
+  uint32_t klo = 0, khi = 0;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    run += e[i];
+    const bool first = keep[i] && run > target && lo == 0x7fffffff;
+    lo = first ? id[i] : lo;
+    klo = first ? kk[i] : klo;
+    hi = keep[i] ? id[i] : hi;
+    khi = keep[i] ? kk[i] : khi;
+  }
+  // the first lane with a candidate holds the draw; u at the top edge: the last kept id
+  const unsigned long long has_lo = __ballot(lo != 0x7fffffff);
+  const unsigned long long has_hi = __ballot(hi >= 0);
+  const int src = has_lo ? __ffsll(has_lo) - 1 : 63 - __clzll(has_hi);
+  if (lane == src) {
+    const int pick = has_lo ? lo : hi;
+    const uint32_t kv = has_lo ? klo : khi;
+    a.tok[row] = pick;
+    a.logp[row] = (funkey(kv) * a.inv_temp - mz) - logf(Sp);
+  }
+}
 
 template <int C>
 __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
   static_assert(C >= 1 && C <= 64, "values per thread");
   constexpr int NE = ST * C;
-  // the staged row; later the survivor list of the top-p search (keys, e, tau)
-  constexpr int SZ = NE + NE / 8 > 2 * kListMax + 4 ? NE + NE / 8 : 2 * kListMax + 4;
+  // the staged row; later the list of a threshold search (keys and weights or ids)
+  constexpr int SZ = NE + NE / 8 > 2 * kListMax ? NE + NE / 8 : 2 * kListMax;
   __shared__ __attribute__((aligned(16))) float stage[SZ];
+  __shared__ uint32_t tmx[ST];   // per-thread maximum keys (the top-k bound)
   __shared__ float rbuf[2 * SW];
+  __shared__ uint32_t bcast;
   __shared__ int pick_lo, pick_hi;
-  Red red{rbuf};
+  Red<SW> red{rbuf};
 
   const int row = blockIdx.x;
   const int V = a.V;
+  const int lane = threadIdx.x % 64;
   const float urow = a.u[row];   // requested early; used by the draw
   const float* src = a.logits + static_cast<size_t>(row) * V;
   // coalesced load into LDS with four pad slots after every 32 values (16-byte aligned runs,
@@ -152,7 +307,9 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
   }
   __syncthreads();
   const int j0 = threadIdx.x * C;
-  // the thread's run as order-preserving keys; a logit is recovered from its key when needed
+  // the thread's run as order-preserving keys; a logit is recovered from its key when needed.
+  // Ids past V get key 0, below the key of every float (-inf included), so no count, bound or
+  // tie test ever takes them.
   uint32_t key[C];
   float lm = -INFINITY;
   if constexpr (C >= 4) {
@@ -170,99 +327,187 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
       lm = fmaxf(lm, xc);
     }
   }
-  const float mz = red.max(lm) * a.inv_temp;
+  uint32_t km = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    key[c] = j0 + c < V ? key[c] : 0u;
+    km = key[c] > km ? key[c] : km;
+  }
+  const bool topk = a.top_k > 0 && a.top_k < V;
+  tmx[threadIdx.x] = km;
+  const float mz = red.max(lm) * a.inv_temp;   // its barrier also ends every read of the stage
 
+  if (topk && a.top_k <= ST) {
+    // bound: the k-th largest per-thread maximum, its low bits cleared, found by wave 0 (its
+    // counts are ballots on the CU's one scalar unit) and broadcast
+    if (threadIdx.x < 64) {
+      uint32_t tv[SW];
+#pragma unroll
+      for (int i = 0; i < SW; ++i) tv[i] = tmx[lane + 64 * i];
+      uint32_t b = 0;
+#pragma nounroll
+      for (int bit = 31; bit >= 32 - kBoundBits; --bit) {
+        const uint32_t cand = b | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < SW; ++i) n += wave_count(tv[i] >= cand);
+        b = n >= a.top_k ? cand : b;
+      }
+      if (threadIdx.x == 0) bcast = b;
+    }
+    __syncthreads();
+    const uint32_t lo = bcast;
+    if (lo != 0) {
+      float nu = 0.f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) nu += key[c] >= lo ? 1.f : 0.f;
+      float U;
+      int pos = static_cast<int>(red.excl_scan(nu, U));
+      if (U <= static_cast<float>(kListMax)) {
+        uint32_t* lk = reinterpret_cast<uint32_t*>(stage);
+        int* lid = reinterpret_cast<int*>(stage + kListMax);
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          if (key[c] >= lo) {
+            lk[pos] = key[c];
+            lid[pos] = j0 + c;
+            ++pos;
+          }
+        __syncthreads();
+        if (threadIdx.x < 64) {
+          const int n = static_cast<int>(U);
+          if (n <= 64) finish_on_list<1>(a, row, lk, lid, n, mz, urow);
+          else if (n <= 128) finish_on_list<2>(a, row, lk, lid, n, mz, urow);
+          else if (n <= 256) finish_on_list<4>(a, row, lk, lid, n, mz, urow);
+          else if (n <= 512) finish_on_list<8>(a, row, lk, lid, n, mz, urow);
+          else finish_on_list<16>(a, row, lk, lid, n, mz, urow);
+        }
+        return;   // the whole workgroup (U is the same on every thread)
+      }
+    }
+  }
+
+  // ---- general path
   // unnormalised probabilities exp(z - max z); an id that is not (or no longer) kept holds
   // -0.0, which adds nothing to any sum and is told apart from an underflowed +0 by its sign
+  // (branch-free: the exponential is taken for every id, then ids past V get -0)
   float e[C];
 #pragma unroll
-  for (int c = 0; c < C; ++c)
-    e[c] = j0 + c < V ? __builtin_amdgcn_exp2f((funkey(key[c]) * a.inv_temp - mz) * kLog2eS) : -0.0f;
+  for (int c = 0; c < C; ++c) {
+    const bool in = key[c] != 0u;
+    const float x = (funkey(key[c]) * a.inv_temp - mz) * kLog2eS;
+    const float ev = __builtin_amdgcn_exp2f(in ? x : -INFINITY);
+    e[c] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, ev) | (in ? 0u : 0x80000000u));
+  }
+
+  auto in_use = [&](int c, bool mass) { return mass ? is_kept(e[c]) : key[c] != 0u; };
+  // weight at or above a candidate key over the block: an exact count (ballots) or a
+  // fixed-order mass
+  auto block_weight = [&](bool mass, uint32_t cand) -> float {
+    if (mass) {
+      float n = 0.f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) n += key[c] >= cand ? e[c] : 0.f;
+      return red.sum(n);
+    }
+    float n = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) n += key[c] >= cand ? 1.f : 0.f;
+    return red.sum(n);
+  };
 
   // Threshold search: the largest key tau whose weight at or above it, W(tau) = sum of w over
   // the elements in use with key >= tau, still reaches `target` (w = 1 and in use = valid for
   // top-k; w = e and in use = kept for top-p).  The first `pb` bits are decided over all
-  // elements with block sums.  Then only the elements whose key shares tau's pb-bit prefix are
-  // undecided; when at most kListMax remain they are gathered into LDS (id order) and wave 0
-  // decides the remaining bits alone, the decided weight above the prefix added to its sums.
-  // Otherwise the block search simply goes on.
-  auto wt = [&](int c, bool mass) { return mass ? e[c] : (j0 + c < V ? 1.f : 0.f); };
+  // elements with block sums.  Then only the elements in use whose key shares tau's pb-bit
+  // prefix are undecided; when at most kListMax remain they are gathered into LDS (id order)
+  // and wave 0 decides the remaining bits alone, the decided weight above the prefix added to
+  // its sums.  Otherwise the block search goes on.
   auto search = [&](bool mass, float target, int pb) -> uint32_t {
     uint32_t tau = 0;
     int bit = 31;
 #pragma nounroll
     for (; bit >= 32 - pb; --bit) {
       const uint32_t cand = tau | (1u << bit);
-      float n = 0.f;
-#pragma unroll
-      for (int c = 0; c < C; ++c) n += key[c] >= cand ? wt(c, mass) : 0.f;
-      if (red.sum(n) >= target) tau = cand;
+      if (block_weight(mass, cand) >= target) tau = cand;
     }
     const uint32_t pmask = pb == 0 ? 0u : ~0u << (32 - pb);
     float nu = 0.f, ab = 0.f;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const bool use = mass ? is_kept(e[c]) : j0 + c < V;
+      const bool use = in_use(c, mass);
       nu += use && (key[c] & pmask) == tau ? 1.f : 0.f;
-      ab += use && (key[c] & pmask) > tau ? wt(c, mass) : 0.f;
+      ab += use && (key[c] & pmask) > tau ? (mass ? e[c] : 1.f) : 0.f;
     }
-    const float U = red.sum(nu);   // undecided elements
+    float U;
+    const float pos0 = red.excl_scan(nu, U);   // undecided elements before this thread, and in all
     if (U <= static_cast<float>(kListMax)) {
-      const float above = red.sum(ab);
+      const float above = pb == 0 ? 0.f : red.sum(ab);
       uint32_t* lk = reinterpret_cast<uint32_t*>(stage);
       float* lw = stage + kListMax;
-      int pos = static_cast<int>(red.excl_scan(nu));
+      int pos = static_cast<int>(pos0);
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        const bool use = mass ? is_kept(e[c]) : j0 + c < V;
-        if (use && (key[c] & pmask) == tau) {
+        if (in_use(c, mass) && (key[c] & pmask) == tau) {
           lk[pos] = key[c];
-          lw[pos] = wt(c, mass);
+          lw[pos] = mass ? e[c] : 1.f;
           ++pos;
         }
       }
       __syncthreads();
       if (threadIdx.x < 64) {
+        // slot i of lane l is list entry l + 64 i; only the slots the list reaches are read
         constexpr int PER = kListMax / 64;
+        const int n_all = static_cast<int>(U);
+        const int np = (n_all + 63) / 64;
         uint32_t wk[PER];
         float ww[PER];
-        const int nu_all = static_cast<int>(U);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {   // slots past the list hold stale data: weight 0
-          const int j = threadIdx.x + 64 * i;
-          wk[i] = lk[j];
-          ww[i] = j < nu_all ? lw[j] : 0.f;
+        for (int i = 0; i < PER; ++i) {
+          wk[i] = 0u;   // past the list: below every candidate key
+          ww[i] = 0.f;
+          const int j = lane + 64 * i;
+          if (i < np && j < n_all) {
+            wk[i] = lk[j];
+            ww[i] = lw[j];
+          }
         }
         const float lim = target - above;
 #pragma nounroll
         for (; bit >= 0; --bit) {
           const uint32_t cand = tau | (1u << bit);
-          float n = 0.f;
+          float n;
+          if (mass) {
+            float sm = 0.f;
 #pragma unroll
-          for (int i = 0; i < PER; ++i) n += wk[i] >= cand ? ww[i] : 0.f;
-          if (wave_sum(n) >= lim) tau = cand;
+            for (int i = 0; i < PER; ++i)
+              if (i < np) sm += wk[i] >= cand ? ww[i] : 0.f;
+            n = wave_sum(sm);
+          } else {
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+              if (i < np) cnt += wave_count(wk[i] >= cand);
+            n = static_cast<float>(cnt);
+          }
+          if (n >= lim) tau = cand;
         }
+        if (threadIdx.x == 0) bcast = tau;
       }
-      __syncthreads();   // every read of the list is done
-      if (threadIdx.x == 0) lk[2 * kListMax] = tau;
+      // the list is read by wave 0 only; the next gather comes after further barriers
       __syncthreads();
-      tau = lk[2 * kListMax];
-      __syncthreads();   // the slot is free again
-    } else {
+      return bcast;
+    }
 #pragma nounroll
-      for (; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
-        float n = 0.f;
-#pragma unroll
-        for (int c = 0; c < C; ++c) n += key[c] >= cand ? wt(c, mass) : 0.f;
-        if (red.sum(n) >= target) tau = cand;
-      }
+    for (; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      if (block_weight(mass, cand) >= target) tau = cand;
     }
     return tau;
   };
 
   // ---- top-k: the k-th largest key, then ties at it in id order
-  if (a.top_k > 0 && a.top_k < V) {
+  if (topk) {
     const float k = static_cast<float>(a.top_k);
     const uint32_t tau = search(false, k, kPrefixBits);
     float gt = 0.f, eq = 0.f;
@@ -272,7 +517,8 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
       eq += key[c] == tau ? 1.f : 0.f;
     }
     const float need_eq = k - red.sum(gt);
-    float r = red.excl_scan(eq);   // ties before this thread's run
+    float n_eq;
+    float r = red.excl_scan(eq, n_eq);   // ties before this thread's run
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const bool tie = key[c] == tau;
@@ -290,7 +536,7 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
   if (a.top_p < 1.0f) {
     const float need = a.top_p * Sk;
     // after a top-k of at most kListMax the survivors are gathered at once
-    const bool few = a.top_k > 0 && a.top_k < V && a.top_k <= kListMax;
+    const bool few = topk && a.top_k <= kListMax;
     const uint32_t tau = search(true, need, few ? 0 : kPrefixBits);
     float gt = 0.f, eq = 0.f, e_eq = 0.f;
 #pragma unroll
@@ -301,7 +547,8 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
       e_eq = tie ? e[c] : e_eq;
     }
     const float mass_gt = red.sum(gt);
-    float r = red.excl_scan(eq);
+    float n_eq;
+    float r = red.excl_scan(eq, n_eq);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const bool k1 = is_kept(e[c]);
@@ -317,8 +564,8 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
   float mine = 0.f;
 #pragma unroll
   for (int c = 0; c < C; ++c) mine += e[c];
-  const float Sp = red.sum(mine);
-  float run = red.excl_scan(mine);
+  float Sp;
+  float run = red.excl_scan(mine, Sp);
   const float target = urow * Sp;
   int lo = 0x7fffffff, hi = -1;
 #pragma unroll

@@ -85,13 +85,43 @@ def test_sample_plain_and_ragged_vocab(dev):
 
 
 def test_sample_large_vocab(dev):
-    """V=32000 (64 values per thread): full nucleus 0.95; top-k 50 + top-p 0.9 (the
-    survivors are searched by one wave); top-k 2000 + top-p 0.8 and top-k 1024 + top-p 0.5
-    (above and at the size limit of that survivor list)."""
+    """V=32000 (1024 threads, 32 values each): full nucleus 0.95; top-k 50 + top-p 0.9 (the
+    bound from the per-thread maxima, then one wave over the survivors); top-k 2000 + top-p 0.8
+    (k above the thread count: the prefix search) and top-k 1024 + top-p 0.5 (k at the thread
+    count, where threads past V hold no element, so the bound is empty)."""
     _case(dev, 24, 32000, 1.0, 0, 0.95, 4)
     _case(dev, 24, 32000, 0.7, 50, 0.9, 5)
     _case(dev, 16, 32000, 1.0, 2000, 0.8, 9)
     _case(dev, 16, 32000, 1.0, 1024, 0.5, 10)
+
+
+def test_sample_mid_vocab(dev):
+    """8192 < V <= 16384 (1024 threads, 16 values each): top-k + top-p, top-p alone, and a
+    ragged V that leaves the last thread partly empty."""
+    _case(dev, 24, 12000, 0.9, 50, 0.9, 11)
+    _case(dev, 24, 16384, 1.0, 0, 0.8, 12)
+    _case(dev, 16, 9001, 1.0, 300, 0.95, 13)
+
+
+def test_sample_top_values_in_few_threads(dev):
+    """Logits that grow with the id put the largest values in the last threads' runs: the
+    k-th largest per-thread maximum then admits more than one wave's list, and the search
+    falls back to deciding the top bits over the whole row.  Falling logits put them in the
+    first threads; a row whose top values are all in one thread's run is the extreme case."""
+    V = 32000
+    g = np.random.default_rng(14)
+    rising = np.tile(np.linspace(-4.0, 4.0, V, dtype=np.float32), (8, 1))
+    rising += (g.standard_normal((8, V)) * 1e-3).astype(np.float32)
+    u = g.random(8).astype(np.float32)
+    for logits in (rising, rising[:, ::-1].copy()):
+        for k, p in ((50, 0.9), (1000, 0.95), (50, 1.0)):
+            tok, lp = _run(dev, logits, u, 1.0, k, p)
+            check_rows(logits, u, tok, lp, 1.0, k, p)
+    one = (g.standard_normal((8, V)) * 0.5).astype(np.float32)
+    one[:, 640:672] += 10.0   # ids 640..671: the run of thread 20
+    tok, lp = _run(dev, one, u, 1.0, 40, 0.9)
+    check_rows(one, u, tok, lp, 1.0, 40, 0.9)
+    assert ((tok >= 640) & (tok < 672)).all()
 
 
 def test_sample_peaked_and_greedy(dev):
