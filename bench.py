@@ -17,6 +17,7 @@ decoder, a 300M-class prefix, RL action scoring, token sampling, prefix snapshot
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -391,18 +392,29 @@ def sampling_leg(steps: int, warmup: int, with_cpu: bool = True):
     logits = (torch.randn(n, V, generator=g) * 2.0).to(dev)
     u = torch.rand(n, generator=g).to(dev)
     stream = torch.cuda.current_stream()
+    # The C-ABI call with its arguments marshalled once: a call through the Python binding
+    # (output allocation, checks) takes longer on the host than the kernel on the GPU, so
+    # back-to-back binding calls would time the host's launch gaps, not the kernel.
+    lib = rlt.load_library()
+    tok = torch.empty(n, dtype=torch.int32, device=dev)
+    logp = torch.empty(n, dtype=torch.float32, device=dev)
+    calls = max(20, steps)
     out = {}
     for name, k, p in (("top_k50_top_p0.95", 50, 0.95), ("top_p0.95", 0, 0.95), ("plain", 0, 1.0)):
-        for _ in range(warmup):
-            rlt.rlt_sample_tokens(logits, u, 0.8, k, p, stream=stream)
+        params = rlt.rlt_sampling(0.8, k, p)
+        args = (ctypes.c_void_p(logits.data_ptr()), n, V, ctypes.byref(params), ctypes.c_void_p(u.data_ptr()),
+                ctypes.c_void_p(tok.data_ptr()), ctypes.c_void_p(logp.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(max(1, warmup)):
+            if lib.rlt_sample_tokens(*args) != 0:
+                raise RuntimeError(lib.rlt_last_error().decode())
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         ev[0].record(stream)
-        for _ in range(steps):
-            rlt.rlt_sample_tokens(logits, u, 0.8, k, p, stream=stream)
+        for _ in range(calls):
+            lib.rlt_sample_tokens(*args)
         ev[1].record(stream)
         torch.cuda.synchronize()
-        out[name] = ev[0].elapsed_time(ev[1]) / steps
+        out[name] = ev[0].elapsed_time(ev[1]) / calls
     ms = out["top_k50_top_p0.95"]
     cpu = None
     if with_cpu:
