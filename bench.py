@@ -33,7 +33,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_small_k_small_traffic.md")
 KERNEL_SOURCES = ["cross_token_recurrent_amd/csrc/dec_small.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
 SCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_lse_res_k_head32000x1024_traffic.md")
 SCORE_SOURCES = ["cross_token_recurrent_amd/csrc/score.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
-SAMPLE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sample_k_512x32000_traffic.md")
+SAMPLE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sample_topk_k_512x32000_traffic.md")
 SAMPLE_SOURCES = ["cross_token_recurrent_amd/csrc/sample.hip", "cross_token_recurrent_amd/csrc/device_common.h"]
 
 
@@ -395,13 +395,14 @@ def sampling_leg(steps: int, warmup: int, with_cpu: bool = True):
     # The C-ABI call with its arguments marshalled once: a call through the Python binding
     # (output allocation, checks) takes longer on the host than the kernel on the GPU, so
     # back-to-back binding calls would time the host's launch gaps, not the kernel.
-    lib = rlt.load_library()
+    from cross_token_recurrent_amd import rlt as rlt_binding
+    lib = rlt_binding.load_library()
     tok = torch.empty(n, dtype=torch.int32, device=dev)
     logp = torch.empty(n, dtype=torch.float32, device=dev)
     calls = max(20, steps)
     out = {}
     for name, k, p in (("top_k50_top_p0.95", 50, 0.95), ("top_p0.95", 0, 0.95), ("plain", 0, 1.0)):
-        params = rlt.rlt_sampling(0.8, k, p)
+        params = rlt_binding.rlt_sampling(0.8, k, p)
         args = (ctypes.c_void_p(logits.data_ptr()), n, V, ctypes.byref(params), ctypes.c_void_p(u.data_ptr()),
                 ctypes.c_void_p(tok.data_ptr()), ctypes.c_void_p(logp.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
         for _ in range(max(1, warmup)):
@@ -432,7 +433,7 @@ def sampling_leg(steps: int, warmup: int, with_cpu: bool = True):
             "ms_per_call_by_truncation": out, "cpu_baseline": cpu,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic(SAMPLE_TRAFFIC_FILE, SAMPLE_SOURCES), "kernel": "sample_k<64>",
+                         "traffic": measured_traffic(SAMPLE_TRAFFIC_FILE, SAMPLE_SOURCES), "kernel": "sample_topk_k<16>",
                          "algorithmic_bytes_per_call": nbytes}}
 
 

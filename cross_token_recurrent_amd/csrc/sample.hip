@@ -40,6 +40,8 @@ namespace {
 constexpr int kListMax = 1024;     // undecided elements one wave finishes a threshold search on
 constexpr int kPrefixBits = 12;    // key bits decided over all elements first
 constexpr int kBoundBits = 16;     // top bits of the k-th largest thread maximum kept as the bound
+constexpr int kLeanK = 128;        // largest top-k the lean kernel takes
+constexpr int kLeanList = 256;     // its candidate list (at most four entries per lane of one wave)
 constexpr int ST = 512;            // threads per row
 constexpr int SW = ST / 64;        // waves
 constexpr float kLog2eS = 1.4426950408889634f;
@@ -252,20 +254,12 @@ __device__ void finish_on_list(const SampleArgs& a, int row, const uint32_t* lk,
   }
 }
 
+// One row of the general path (the workgroup's threads all call it for the same row).
 template <int C>
-__global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
+__device__ __forceinline__ void sample_row(const SampleArgs& a, int row, float* stage, uint32_t* tmx, float* rbuf,
+                                           uint32_t& bcast, int& pick_lo, int& pick_hi) {
   static_assert(C >= 1 && C <= 64, "values per thread");
-  constexpr int NE = ST * C;
-  // the staged row; later the list of a threshold search (keys and weights or ids)
-  constexpr int SZ = NE + NE / 8 > 2 * kListMax ? NE + NE / 8 : 2 * kListMax;
-  __shared__ __attribute__((aligned(16))) float stage[SZ];
-  __shared__ uint32_t tmx[ST];   // per-thread maximum keys (the top-k bound)
-  __shared__ float rbuf[2 * SW];
-  __shared__ uint32_t bcast;
-  __shared__ int pick_lo, pick_hi;
   Red<SW> red{rbuf};
-
-  const int row = blockIdx.x;
   const int V = a.V;
   const int lane = threadIdx.x % 64;
   const float urow = a.u[row];   // requested early; used by the draw
@@ -596,6 +590,184 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
 }
 
 template <int C>
+__global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
+  static_assert(C >= 1 && C <= 64, "values per thread");
+  constexpr int NE = ST * C;
+  // the staged row; later the list of a threshold search (keys and weights or ids)
+  constexpr int SZ = NE + NE / 8 > 2 * kListMax ? NE + NE / 8 : 2 * kListMax;
+  __shared__ __attribute__((aligned(16))) float stage[SZ];
+  __shared__ uint32_t tmx[ST];   // per-thread maximum keys (the top-k bound)
+  __shared__ float rbuf[2 * SW];
+  __shared__ uint32_t bcast;
+  __shared__ int pick_lo, pick_hi;
+  sample_row<C>(a, blockIdx.x, stage, tmx, rbuf, bcast, pick_lo, pick_hi);
+}
+
+// Lean top-k kernel (0 < k <= kLeanK, 4096 < V, V a multiple of 4): no LDS stage and at most
+// 128 VGPRs, so two rows share a CU and one row's load overlaps another row's work.  Thread t
+// loads the 16-byte pieces t, t + 512, ... of the row straight into registers as keys (ids
+// 4q..4q+3 of piece q).  The bound and the gather are those of the list path above, with at
+// most kLeanList candidates.  When the bound admits more (for example logits that grow with the
+// id), the exact top-k threshold is found by block count passes over the keys, the ties at it
+// are cut in id order (a bitwise search for the need-th smallest tie id, when more tie than
+// are needed), and exactly the k survivors are gathered.  The gather's order is
+// thread-major, so wave 0 places every entry at its rank by id (ids are distinct) before
+// finishing the row on the list.
+template <int NQ>
+__global__ __launch_bounds__(ST) __attribute__((amdgpu_waves_per_eu(4)))
+void sample_topk_k(SampleArgs a) {
+  constexpr int C = 4 * NQ;
+  __shared__ uint32_t tmx[ST];
+  __shared__ float rbuf[2 * SW];
+  __shared__ uint32_t bcast;
+  __shared__ uint32_t lk[kLeanList], sk[kLeanList];
+  __shared__ int lid[kLeanList], sid[kLeanList];
+  Red<SW> red{rbuf};
+
+  const int row = blockIdx.x;
+  const int V = a.V;
+  const int lane = threadIdx.x % 64;
+  const float urow = a.u[row];
+  const float4* s4 = reinterpret_cast<const float4*>(a.logits + static_cast<size_t>(row) * V);
+  const int qmax = V / 4 - 1;
+  float4 v[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) v[i] = s4[min(static_cast<int>(threadIdx.x) + i * ST, qmax)];
+  // keys (ids past V: 0, below every float's key); -0 becomes +0 so equal logits have equal keys
+  uint32_t key[C];
+  float lm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const bool in = 4 * (static_cast<int>(threadIdx.x) + i * ST) < V;
+    key[4 * i] = in ? fkey(v[i].x + 0.0f) : 0u;
+    key[4 * i + 1] = in ? fkey(v[i].y + 0.0f) : 0u;
+    key[4 * i + 2] = in ? fkey(v[i].z + 0.0f) : 0u;
+    key[4 * i + 3] = in ? fkey(v[i].w + 0.0f) : 0u;
+    lm = in ? fmaxf(lm, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w))) : lm;
+  }
+  uint32_t km = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) km = key[c] > km ? key[c] : km;
+  tmx[threadIdx.x] = km;
+  const float mz = red.max(lm) * a.inv_temp;
+  if (threadIdx.x < 64) {
+    uint32_t tv[SW];
+#pragma unroll
+    for (int i = 0; i < SW; ++i) tv[i] = tmx[lane + 64 * i];
+    uint32_t b = 0;
+#pragma nounroll
+    for (int bit = 31; bit >= 32 - kBoundBits; --bit) {
+      const uint32_t cand = b | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < SW; ++i) n += wave_count(tv[i] >= cand);
+      b = n >= a.top_k ? cand : b;
+    }
+    if (threadIdx.x == 0) bcast = b;
+  }
+  __syncthreads();
+  const uint32_t lo = bcast;
+  float nu = 0.f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) nu += key[c] >= lo ? 1.f : 0.f;
+  float U;
+  int pos = static_cast<int>(red.excl_scan(nu, U));
+  auto id_of = [&](int c) { return 4 * (static_cast<int>(threadIdx.x) + (c / 4) * ST) + c % 4; };
+  int n;
+  if (lo != 0u && U <= static_cast<float>(kLeanList)) {   // the same on every thread
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      if (key[c] >= lo) {
+        lk[pos] = key[c];
+        lid[pos] = id_of(c);
+        ++pos;
+      }
+    n = static_cast<int>(U);
+  } else {
+    // The exact path re-reads the row (from L2) one 16-byte piece at a time instead of
+    // keeping the keys live across it, which would push the kernel past 128 VGPRs.
+    // fn(q, c, key) for every id 4q + c of the thread's pieces q = t, t + 512, ... (key 0 past V)
+    auto each = [&](auto fn) {
+#pragma nounroll
+      for (int i = 0; i < NQ; ++i) {
+        const int q = static_cast<int>(threadIdx.x) + i * ST;
+        const float4 v = s4[min(q, qmax)];
+        const bool in = 4 * q < V;
+        fn(q, 0, in ? fkey(v.x + 0.0f) : 0u);
+        fn(q, 1, in ? fkey(v.y + 0.0f) : 0u);
+        fn(q, 2, in ? fkey(v.z + 0.0f) : 0u);
+        fn(q, 3, in ? fkey(v.w + 0.0f) : 0u);
+      }
+    };
+    // the exact threshold: the largest key whose count at or above it still reaches k
+    const float k = static_cast<float>(a.top_k);
+    uint32_t tau = 0;
+#pragma nounroll
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      float cnt = 0.f;
+      each([&](int, int, uint32_t kc) { cnt += kc >= cand ? 1.f : 0.f; });
+      if (red.sum(cnt) >= k) tau = cand;
+    }
+    float gtc = 0.f, tc = 0.f;
+    each([&](int, int, uint32_t kc) {
+      gtc += kc > tau ? 1.f : 0.f;
+      tc += kc == tau ? 1.f : 0.f;
+    });
+    const float need_eq = k - red.sum(gtc);
+    // ties at it are taken in id order: all of them, or those up to the need_eq-th smallest
+    // tie id (the largest id x with fewer than need_eq ties below it; ids are below 2^15)
+    int id_cut = 0x7fffffff;
+    if (red.sum(tc) > need_eq) {
+      int x = 0;
+#pragma nounroll
+      for (int bit = 14; bit >= 0; --bit) {
+        const int cand = x | (1 << bit);
+        float below = 0.f;
+        each([&](int q, int c, uint32_t kc) { below += kc == tau && 4 * q + c < cand ? 1.f : 0.f; });
+        if (red.sum(below) < need_eq) x = cand;
+      }
+      id_cut = x;
+    }
+    auto take = [&](int q, int c, uint32_t kc) { return kc > tau || (kc == tau && 4 * q + c <= id_cut); };
+    float m = 0.f;
+    each([&](int q, int c, uint32_t kc) { m += take(q, c, kc) ? 1.f : 0.f; });
+    float total;
+    pos = static_cast<int>(red.excl_scan(m, total));   // total = k
+    each([&](int q, int c, uint32_t kc) {
+      if (take(q, c, kc)) {
+        lk[pos] = kc;
+        lid[pos] = 4 * q + c;
+        ++pos;
+      }
+    });
+    n = static_cast<int>(total);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    for (int j = lane; j < n; j += 64) {
+      const int idj = lid[j];
+      int r = 0;
+      for (int m = 0; m < n; ++m) r += lid[m] < idj ? 1 : 0;
+      sk[r] = lk[j];
+      sid[r] = idj;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    if (n <= 64) finish_on_list<1>(a, row, sk, sid, n, mz, urow);
+    else if (n <= 128) finish_on_list<2>(a, row, sk, sid, n, mz, urow);
+    else finish_on_list<4>(a, row, sk, sid, n, mz, urow);
+  }
+}
+
+template <int NQ>
+hipError_t launch_lean(const SampleArgs& a, hipStream_t st) {
+  sample_topk_k<NQ><<<a.N, ST, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int C>
 hipError_t launch_c(const SampleArgs& a, hipStream_t st) {
   sample_k<C><<<a.N, ST, 0, st>>>(a);
   return hipGetLastError();
@@ -609,6 +781,8 @@ hipError_t launch_sample_tokens(const float* logits, const float* uniforms, int3
   if (V < 1 || V > ST * 64 || !(temperature > 0.f) || top_k < 0 || !(top_p > 0.f) || top_p > 1.f)
     return hipErrorInvalidValue;
   SampleArgs a{logits, uniforms, tokens, logp, N, V, top_k, 1.0f / temperature, top_p};
+  if (top_k > 0 && top_k <= kLeanK && top_k < V && V > 8 * ST && V % 4 == 0)
+    return V > 32 * ST ? launch_lean<16>(a, st) : V > 16 * ST ? launch_lean<8>(a, st) : launch_lean<4>(a, st);
   const int need = (V + ST - 1) / ST;
   if (need <= 1) return launch_c<1>(a, st);
   if (need <= 2) return launch_c<2>(a, st);

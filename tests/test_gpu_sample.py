@@ -124,6 +124,41 @@ def test_sample_top_values_in_few_threads(dev):
     assert ((tok >= 640) & (tok < 672)).all()
 
 
+def test_sample_lean_top_k(dev):
+    """Top-k <= 128 with 4096 < V and V a multiple of 4 (the lean kernel, keys loaded straight
+    into registers and the candidates ranked by id): V = 6000, 12000 and 32000; ties at the
+    k-th place resolved by id; one call mixing rows finished on the bound's list and rows whose
+    bound admits too many elements (logits growing with the id: the exact threshold over the
+    whole row); and that exact path with more ties at the threshold than places left."""
+    _case(dev, 24, 6000, 1.0, 100, 0.9, 15)
+    _case(dev, 24, 12000, 0.7, 128, 1.0, 16)
+    g = np.random.default_rng(17)
+    V = 32000
+    logits = (g.standard_normal((6, V)) * 0.5).astype(np.float32)
+    logits[:, 100:110] = 5.0   # ten equal maxima; top-k 5 keeps ids 100..104
+    u = g.random(6).astype(np.float32)
+    tok, lp = _run(dev, logits, u, 1.0, 5, 1.0)
+    assert ((tok >= 100) & (tok < 105)).all()
+    check_rows(logits, u, tok, lp, 1.0, 5, 1.0)
+    mixed = (g.standard_normal((8, V)) * 2.0).astype(np.float32)
+    mixed[1::2] = np.linspace(-4.0, 4.0, V, dtype=np.float32)
+    u = g.random(8).astype(np.float32)
+    tok, lp = _run(dev, mixed, u, 0.9, 50, 0.9)
+    check_rows(mixed, u, tok, lp, 0.9, 50, 0.9)
+    assert (tok[1::2] >= V - 200).all()
+    # the bound admits too many elements and the k-th place falls inside 100 equal logits:
+    # top-k 50 keeps ids 31900..31949, top-p 0.9 of those the first 45
+    tied = np.tile(np.linspace(-4.0, 4.0, V, dtype=np.float32), (6, 1))
+    tied[:, V - 100:] = 10.0
+    u = g.random(6).astype(np.float32)
+    tok, lp = _run(dev, tied, u, 1.0, 50, 1.0)
+    check_rows(tied, u, tok, lp, 1.0, 50, 1.0)
+    assert ((tok >= V - 100) & (tok < V - 50)).all()
+    tok, lp = _run(dev, tied, u, 1.0, 50, 0.9)
+    check_rows(tied, u, tok, lp, 1.0, 50, 0.9)
+    assert ((tok >= V - 100) & (tok < V - 55)).all()
+
+
 def test_sample_peaked_and_greedy(dev):
     """Peaked logits (scale 30): the nucleus holds one or two ids; top_k = 1 is the argmax
     with logp 0."""

@@ -5,8 +5,8 @@
 
 Without a flag the summary covers the decoder (dec_small_k on the small workload); with
 --score, the action-scoring kernel (score_lse_res_k on bench.py's scoring leg: head
-V=32000, d=1024, bf16, 65536 rows); with --sample, the sampling kernel (sample_k on
-bench.py's sampling leg: 512 rows x V=32000).
+V=32000, d=1024, bf16, 65536 rows); with --sample, the sampling kernel (sample_topk_k, top-k 50 then top-p
+0.95, on bench.py's sampling leg: 512 rows x V=32000).
 
 Each directory holds the counter_collection.csv of one `rocprofv3 --pmc <counter>` run:
 the decoder runs come from `bench.py --only-small --steps 1 --warmup 0`, the scoring and
@@ -79,20 +79,20 @@ def sample_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out):
     copy_bytes = float(1 << 30)
     c_fetch = _value(cfetch_dir, "FETCH_SIZE", "copy") * 1024.0
     c_write = _value(cwrite_dir, "WRITE_SIZE", "copy") * 1024.0
-    k_fetch = _value(fetch_dir, "FETCH_SIZE", "sample_k") * 1024.0
-    k_write = _value(write_dir, "WRITE_SIZE", "sample_k") * 1024.0
+    k_fetch = _value(fetch_dir, "FETCH_SIZE", "sample_topk_k") * 1024.0
+    k_write = _value(write_dir, "WRITE_SIZE", "sample_topk_k") * 1024.0
     f_fetch, f_write = copy_bytes / c_fetch, copy_bytes / c_write
     traffic = k_fetch * f_fetch + k_write * f_write
     alg = 512 * 32000 * 4.0 + 512 * 12.0
     with open(out, "w") as f:
-        f.write("# sample_k on the sampling leg (512 rows x V=32000 fp32 logits): HBM traffic per launch\n\n")
+        f.write("# sample_topk_k on the sampling leg (512 rows x V=32000 fp32 logits, top-k 50 then top-p 0.95): HBM traffic per launch\n\n")
         f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first):\n\n")
         f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- python3 <repo>/bench.py --only-scoring --steps 1 --warmup 0 --no-cpu-baseline\n")
         f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- python3 <repo>/bench.py --only-scoring --steps 1 --warmup 0 --no-cpu-baseline\n")
         f.write("    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch_dir> -- python3 <repo>/bench.py --copy-kernel\n")
         f.write("    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write_dir> -- python3 <repo>/bench.py --copy-kernel\n")
-        f.write("    python traffic_summary.py --sample <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/sample_k_512x32000_traffic.md\n\n")
-        f.write("The largest dispatch of the leg is taken (all three truncation settings read the same logits).\n\n")
+        f.write("    python traffic_summary.py --sample <fetch_dir> <write_dir> <copy_fetch_dir> <copy_write_dir> profiles/sample_topk_k_512x32000_traffic.md\n\n")
+        f.write("The lean top-k kernel's dispatches are taken (the leg's headline setting); the other two settings run sample_k.\n\n")
         f.write(f"- copy kernel: 1 GiB read / 1 GiB written; FETCH_SIZE reads {c_fetch:.4e} B, WRITE_SIZE {c_write:.4e} B\n")
         f.write(f"- fetch scale: {f_fetch:.4f}\n")
         f.write(f"- write scale: {f_write:.4f}\n")
