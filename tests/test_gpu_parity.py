@@ -409,12 +409,14 @@ def test_paths_can_alternate_on_one_state(dev):
 # with padding rows (B = 5, 6, 24, 40), a GELU input product wide enough (F = 6144 >= 384
 # sixteen-column blocks) for two independent blocks per workgroup, two 64-row groups (B = 80),
 # and past 512 rows the tiled products with K split over workgroups (B = 520).
+# F = 1856 = 29 * 64: a K run (and, past 512 rows, a split of K) that no power of two divides
 PRODUCT_CASES = [(6, "swiglu", 512), (5, "gelu", 512), (24, "swiglu", 512), (40, "gelu", 512), (8, "gelu", 6144),
-               (80, "swiglu", 512), (520, "swiglu", 512)]
+                 (80, "swiglu", 512), (520, "swiglu", 512), (8, "gelu", 1856), (520, "gelu", 1856)]
 
 
 @pytest.mark.parametrize("B,ffn,F", PRODUCT_CASES, ids=["ws_rows6", "ws_gelu_rows5", "ws_rows24", "ws_gelu_rows40",
-                                                      "ws_gelu_two_blocks", "ws_row_groups80", "tiled_rows520"])
+                                                      "ws_gelu_two_blocks", "ws_row_groups80", "tiled_rows520",
+                                                      "ws_gelu_f1856", "tiled_gelu_f1856"])
 def test_batched_products_are_deterministic(dev, B, ffn, F):
     """The batched decoder's products add partial sums in fixed orders: a weight-streaming
     product (bf16, B <= 512, d = 256) adds its waves' K runs in wave order; past 512 rows the
