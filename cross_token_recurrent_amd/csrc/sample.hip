@@ -761,6 +761,111 @@ void sample_topk_k(SampleArgs a) {
   }
 }
 
+// Lean kernel without truncation (top-k off, top-p = 1; 4096 < V, V a multiple of 4): the same
+// register layout as the top-k kernel (piece row i of the row holds ids 2048i .. 2048i + 2047 in
+// thread order), the probabilities computed in place of the loaded logits.  The draw takes the
+// id-order inverse CDF in two levels: the piece row where the cumulative mass first exceeds u*S
+// (from the rows' totals, added in a fixed order), then an exclusive scan over the threads of
+// that piece row.  The drawn logit is read again for logp.
+template <int NQ>
+__global__ __launch_bounds__(ST) __attribute__((amdgpu_waves_per_eu(4)))
+void sample_full_k(SampleArgs a) {
+  __shared__ float rbuf[2 * SW];
+  __shared__ float rowtot[SW][NQ];   // each wave's mass of every piece row
+  __shared__ int pick_lo;
+  Red<SW> red{rbuf};
+
+  const int row = blockIdx.x;
+  const int V = a.V;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const float urow = a.u[row];
+  const float* zrow = a.logits + static_cast<size_t>(row) * V;
+  const float4* s4 = reinterpret_cast<const float4*>(zrow);
+  const int qmax = V / 4 - 1;
+  float4 v[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) v[i] = s4[min(static_cast<int>(threadIdx.x) + i * ST, qmax)];
+  float lm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const bool in = 4 * (static_cast<int>(threadIdx.x) + i * ST) < V;
+    lm = in ? fmaxf(lm, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w))) : lm;
+  }
+  if (threadIdx.x == 0) pick_lo = 0x7fffffff;
+  const float mz = red.max(lm) * a.inv_temp;
+  // unnormalised probabilities exp(z - max z) in place (0 past V); each wave's mass of every
+  // piece row to LDS
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const bool in = 4 * (static_cast<int>(threadIdx.x) + i * ST) < V;
+    auto ex = [&](float z) { return in ? __builtin_amdgcn_exp2f((z * a.inv_temp - mz) * kLog2eS) : 0.f; };
+    v[i] = make_float4(ex(v[i].x), ex(v[i].y), ex(v[i].z), ex(v[i].w));
+    const float w = wave_sum((v[i].x + v[i].y) + (v[i].z + v[i].w));
+    if (lane == 0) rowtot[wave][i] = w;
+  }
+  __syncthreads();
+  // piece-row totals (waves added in order) and the total mass, the same on every thread
+  auto row_total = [&](int i) {
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < SW; ++w) r += rowtot[w][i];
+    return r;
+  };
+  float Sp = 0.f;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) Sp += row_total(i);
+  const float target = urow * Sp;
+  // the first piece row whose cumulative mass exceeds the target (u at the top edge: the last
+  // piece row holding an id below V), and the mass of the rows before it
+  int istar = (V - 1) / (4 * ST);
+  float cum = 0.f, cum_star = 0.f;
+  bool found = false;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const float r = row_total(i);
+    const bool hit = !found && cum + r > target;
+    istar = hit ? i : istar;
+    cum_star = hit ? cum : cum_star;
+    found = found || hit;
+    cum += r;
+  }
+  if (!found) {
+    cum_star = 0.f;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) cum_star += i < istar ? row_total(i) : 0.f;
+  }
+  float4 vi = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i)
+    if (i == istar) vi = v[i];
+  const float mi = (vi.x + vi.y) + (vi.z + vi.w);
+  float tot;
+  float run = cum_star + red.excl_scan(mi, tot);
+  const int id0 = 4 * (static_cast<int>(threadIdx.x) + istar * ST);
+  int lo = 0x7fffffff;
+  const float ev[4] = {vi.x, vi.y, vi.z, vi.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    run += ev[c];
+    lo = (id0 + c < V && run > target && lo == 0x7fffffff) ? id0 + c : lo;
+  }
+  const float wlo = -wave_max(-static_cast<float>(lo == 0x7fffffff ? (1 << 24) : lo));
+  if (lane == 0 && wlo < static_cast<float>(1 << 24)) atomicMin(&pick_lo, static_cast<int>(wlo));
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // no id of the piece row passed the target (rounding at its end): its last id below V
+    const int pick = pick_lo != 0x7fffffff ? pick_lo : min(V - 1, (istar + 1) * 4 * ST - 1);
+    a.tok[row] = pick;
+    a.logp[row] = (zrow[pick] * a.inv_temp - mz) - logf(Sp);
+  }
+}
+
+template <int NQ>
+hipError_t launch_full(const SampleArgs& a, hipStream_t st) {
+  sample_full_k<NQ><<<a.N, ST, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <int NQ>
 hipError_t launch_lean(const SampleArgs& a, hipStream_t st) {
   sample_topk_k<NQ><<<a.N, ST, 0, st>>>(a);
@@ -783,6 +888,8 @@ hipError_t launch_sample_tokens(const float* logits, const float* uniforms, int3
   SampleArgs a{logits, uniforms, tokens, logp, N, V, top_k, 1.0f / temperature, top_p};
   if (top_k > 0 && top_k <= kLeanK && top_k < V && V > 8 * ST && V % 4 == 0)
     return V > 32 * ST ? launch_lean<16>(a, st) : V > 16 * ST ? launch_lean<8>(a, st) : launch_lean<4>(a, st);
+  if ((top_k == 0 || top_k >= V) && top_p >= 1.0f && V > 8 * ST && V % 4 == 0)
+    return V > 32 * ST ? launch_full<16>(a, st) : V > 16 * ST ? launch_full<8>(a, st) : launch_full<4>(a, st);
   const int need = (V + ST - 1) / ST;
   if (need <= 1) return launch_c<1>(a, st);
   if (need <= 2) return launch_c<2>(a, st);

@@ -159,6 +159,24 @@ def test_sample_lean_top_k(dev):
     assert ((tok >= V - 100) & (tok < V - 55)).all()
 
 
+def test_sample_lean_no_truncation(dev):
+    """No truncation with 4096 < V and V a multiple of 4 (the lean kernel's two-level draw:
+    the piece row of 2048 ids where the cumulative mass passes u*S, then a scan inside it):
+    V = 6000, 12000 and 32000, top-k = V (no truncation either), and u at both edges."""
+    _case(dev, 24, 6000, 0.7, 0, 1.0, 18)
+    _case(dev, 24, 12000, 1.3, 0, 1.0, 19)
+    _case(dev, 32, 32000, 1.0, 0, 1.0, 20)
+    _case(dev, 8, 8192, 1.0, 8192, 1.0, 21)
+    g = np.random.default_rng(22)
+    logits = g.standard_normal((8, 32000)).astype(np.float32)
+    for uu in (0.0, np.float32(1.0 - 2 ** -24)):
+        u = np.full(8, uu, np.float32)
+        tok, lp = _run(dev, logits, u, 1.0, 0, 1.0)
+        check_rows(logits, u, tok, lp, 1.0, 0, 1.0, max_border_frac=1.0)
+        if uu == 0.0:
+            assert (tok == 0).all()
+
+
 def test_sample_peaked_and_greedy(dev):
     """Peaked logits (scale 30): the nucleus holds one or two ids; top_k = 1 is the argmax
     with logp 0."""
