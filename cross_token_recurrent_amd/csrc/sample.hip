@@ -761,18 +761,34 @@ void sample_topk_k(SampleArgs a) {
   }
 }
 
-// Lean kernel without truncation (top-k off, top-p = 1; 4096 < V, V a multiple of 4): the same
-// register layout as the top-k kernel (piece row i of the row holds ids 2048i .. 2048i + 2047 in
-// thread order), the probabilities computed in place of the loaded logits.  The draw takes the
-// id-order inverse CDF in two levels: the piece row where the cumulative mass first exceeds u*S
-// (from the rows' totals, added in a fixed order), then an exclusive scan over the threads of
-// that piece row.  The drawn logit is read again for logp.
-template <int NQ>
+// Lean kernels without top-k (4096 < V, V a multiple of 4): the same register layout as the
+// top-k kernel (piece row i of the row holds ids 2048i .. 2048i + 2047 in thread order), the
+// probabilities computed in place of the loaded logits.
+//
+// NUCLEUS (top-p < 1): the threshold is searched on the probabilities' bit patterns, which order
+// non-negative floats as their values, so only the probabilities stay in registers.  Ranking by
+// probability instead of by logit merges logits whose fp32 probabilities are equal; those become
+// ties and are resolved by id.  The first 12 bits are decided over the row with block mass sums;
+// when at most 512 elements share the decided prefix, wave 0 decides the rest on a list.
+// Ties at the threshold stay in id order while the mass ranked before them is short of the
+// target: their number comes from that same comparison (monotone in the rank, so a binary
+// search), and when fewer ties are kept than exist, a bitwise search finds the id of the last
+// kept one.  Everything not kept gets probability 0.
+//
+// The draw takes the id-order inverse CDF in two levels: the piece row where the cumulative
+// mass first exceeds u*S (from the rows' totals, added in a fixed order), then an exclusive scan
+// over the threads of that piece row.  The drawn logit is read again for logp.
+template <int NQ, bool NUCLEUS>
 __global__ __launch_bounds__(ST) __attribute__((amdgpu_waves_per_eu(4)))
 void sample_full_k(SampleArgs a) {
   __shared__ float rbuf[2 * SW];
   __shared__ float rowtot[SW][NQ];   // each wave's mass of every piece row
-  __shared__ int pick_lo;
+  // the single-wave list of the nucleus search: 512 entries (8 per lane) keep the kernel within
+  // 128 VGPRs beside the 64 probabilities; longer prefixes go on with block passes
+  constexpr int kNucList = 512;
+  __shared__ uint32_t lk[NUCLEUS ? kNucList : 1];
+  __shared__ uint32_t bcast;
+  __shared__ int pick_lo, pick_hi;
   Red<SW> red{rbuf};
 
   const int row = blockIdx.x;
@@ -791,15 +807,134 @@ void sample_full_k(SampleArgs a) {
     const bool in = 4 * (static_cast<int>(threadIdx.x) + i * ST) < V;
     lm = in ? fmaxf(lm, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w))) : lm;
   }
-  if (threadIdx.x == 0) pick_lo = 0x7fffffff;
+  if (threadIdx.x == 0) {
+    pick_lo = 0x7fffffff;
+    pick_hi = -1;
+  }
   const float mz = red.max(lm) * a.inv_temp;
-  // unnormalised probabilities exp(z - max z) in place (0 past V); each wave's mass of every
-  // piece row to LDS
+  // unnormalised probabilities exp(z - max z) in place (0 past V)
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     const bool in = 4 * (static_cast<int>(threadIdx.x) + i * ST) < V;
     auto ex = [&](float z) { return in ? __builtin_amdgcn_exp2f((z * a.inv_temp - mz) * kLog2eS) : 0.f; };
     v[i] = make_float4(ex(v[i].x), ex(v[i].y), ex(v[i].z), ex(v[i].w));
+  }
+  // fn(i, c, x): every element of the thread, x its probability (id 4(t + 512 i) + c)
+  auto each = [&](auto fn) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      fn(i, 0, v[i].x);
+      fn(i, 1, v[i].y);
+      fn(i, 2, v[i].z);
+      fn(i, 3, v[i].w);
+    }
+  };
+  auto id_of = [&](int i, int c) { return 4 * (static_cast<int>(threadIdx.x) + i * ST) + c; };
+
+  if constexpr (NUCLEUS) {
+    auto bits = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+    float st = 0.f;
+    each([&](int, int, float x) { st += x; });
+    const float need = a.top_p * red.sum(st);
+    auto mass_ge = [&](uint32_t cand) {
+      float m = 0.f;
+      each([&](int, int, float x) { m += bits(x) >= cand ? x : 0.f; });
+      return red.sum(m);
+    };
+    // the largest bit pattern tau whose mass at or above it still reaches the target
+    uint32_t tau = 0;
+    int bit = 30;   // the sign bit of a probability is 0
+#pragma nounroll
+    for (; bit >= 31 - kPrefixBits; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      if (mass_ge(cand) >= need) tau = cand;
+    }
+    const uint32_t pmask = ~0u << (bit + 1);
+    float nu = 0.f, ab = 0.f;
+    each([&](int, int, float x) {
+      nu += (bits(x) & pmask) == tau ? 1.f : 0.f;
+      ab += (bits(x) & pmask) > tau ? x : 0.f;
+    });
+    float U;
+    int pos = static_cast<int>(red.excl_scan(nu, U));
+    if (U <= static_cast<float>(kNucList)) {
+      const float above = red.sum(ab);
+      each([&](int, int, float x) {
+        if ((bits(x) & pmask) == tau) lk[pos++] = bits(x);
+      });
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        constexpr int PER = kNucList / 64;
+        const int n_all = static_cast<int>(U);
+        const int np = (n_all + 63) / 64;
+        uint32_t wk[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          wk[i] = 0u;   // past the list: probability 0, below every candidate
+          const int j = lane + 64 * i;
+          if (i < np && j < n_all) wk[i] = lk[j];
+        }
+        const float lim = need - above;
+#pragma nounroll
+        for (; bit >= 0; --bit) {
+          const uint32_t cand = tau | (1u << bit);
+          float sm = 0.f;
+#pragma unroll
+          for (int i = 0; i < PER; ++i)
+            if (i < np) sm += wk[i] >= cand ? __builtin_bit_cast(float, wk[i]) : 0.f;
+          if (wave_sum(sm) >= lim) tau = cand;
+        }
+        if (threadIdx.x == 0) bcast = tau;
+      }
+      __syncthreads();
+      tau = bcast;
+    } else {
+#pragma nounroll
+      for (; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        if (mass_ge(cand) >= need) tau = cand;
+      }
+    }
+    float gt = 0.f, eq = 0.f;
+    each([&](int, int, float x) {
+      gt += bits(x) > tau ? x : 0.f;
+      eq += bits(x) == tau ? 1.f : 0.f;
+    });
+    const float mass_gt = red.sum(gt);
+    const int n_eq = static_cast<int>(red.sum(eq));
+    const float e_eq = __builtin_bit_cast(float, tau);
+    // ties kept: the ranks r with mass_gt + r * e_eq < need (true at r = 0, monotone in r)
+    int lo_r = 0, hi_r = n_eq;
+    while (lo_r < hi_r) {
+      const int mid = (lo_r + hi_r) / 2;
+      if (mass_gt + static_cast<float>(mid) * e_eq < need) lo_r = mid + 1;
+      else hi_r = mid;
+    }
+    const int n_keep = lo_r;
+    // fewer kept than tied: the id of the last kept tie (the largest id x with fewer than
+    // n_keep ties below it; ids are below 2^15)
+    int id_cut = 0x7fffffff;
+    if (n_keep < n_eq) {
+      int x = 0;
+#pragma nounroll
+      for (int b = 14; b >= 0; --b) {
+        const int cand = x | (1 << b);
+        float below = 0.f;
+        each([&](int i, int c, float y) { below += bits(y) == tau && id_of(i, c) < cand ? 1.f : 0.f; });
+        if (red.sum(below) < static_cast<float>(n_keep)) x = cand;
+      }
+      id_cut = x;
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      auto keep = [&](int c, float x) { return bits(x) > tau || (bits(x) == tau && id_of(i, c) <= id_cut) ? x : 0.f; };
+      v[i] = make_float4(keep(0, v[i].x), keep(1, v[i].y), keep(2, v[i].z), keep(3, v[i].w));
+    }
+  }
+
+  // each wave's mass of every piece row
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
     const float w = wave_sum((v[i].x + v[i].y) + (v[i].z + v[i].w));
     if (lane == 0) rowtot[wave][i] = w;
   }
@@ -815,9 +950,13 @@ void sample_full_k(SampleArgs a) {
 #pragma unroll
   for (int i = 0; i < NQ; ++i) Sp += row_total(i);
   const float target = urow * Sp;
-  // the first piece row whose cumulative mass exceeds the target (u at the top edge: the last
-  // piece row holding an id below V), and the mass of the rows before it
+  // the first piece row whose cumulative mass exceeds the target; failing that (u at the top
+  // edge) the last piece row holding a kept id; and the mass of the rows before it
   int istar = (V - 1) / (4 * ST);
+  if constexpr (NUCLEUS) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) istar = row_total(i) > 0.f ? i : istar;
+  }
   float cum = 0.f, cum_star = 0.f;
   bool found = false;
 #pragma unroll
@@ -842,27 +981,36 @@ void sample_full_k(SampleArgs a) {
   float tot;
   float run = cum_star + red.excl_scan(mi, tot);
   const int id0 = 4 * (static_cast<int>(threadIdx.x) + istar * ST);
-  int lo = 0x7fffffff;
+  int lo = 0x7fffffff, hi = -1;
   const float ev[4] = {vi.x, vi.y, vi.z, vi.w};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
+    // kept: an id below V (no truncation) or a probability left nonzero (nucleus)
+    const bool kept = NUCLEUS ? ev[c] > 0.f : id0 + c < V;
     run += ev[c];
-    lo = (id0 + c < V && run > target && lo == 0x7fffffff) ? id0 + c : lo;
+    lo = (kept && run > target && lo == 0x7fffffff) ? id0 + c : lo;
+    hi = kept ? id0 + c : hi;
   }
   const float wlo = -wave_max(-static_cast<float>(lo == 0x7fffffff ? (1 << 24) : lo));
-  if (lane == 0 && wlo < static_cast<float>(1 << 24)) atomicMin(&pick_lo, static_cast<int>(wlo));
+  const float whi = wave_max(static_cast<float>(hi));
+  if (lane == 0) {
+    if (wlo < static_cast<float>(1 << 24)) atomicMin(&pick_lo, static_cast<int>(wlo));
+    if (whi >= 0.f) atomicMax(&pick_hi, static_cast<int>(whi));
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    // no id of the piece row passed the target (rounding at its end): its last id below V
-    const int pick = pick_lo != 0x7fffffff ? pick_lo : min(V - 1, (istar + 1) * 4 * ST - 1);
-    a.tok[row] = pick;
-    a.logp[row] = (zrow[pick] * a.inv_temp - mz) - logf(Sp);
+    // no id of the piece row passed the target (rounding at its end): its last kept id
+    const int pick = pick_lo != 0x7fffffff ? pick_lo : pick_hi;
+    if (pick >= 0) {
+      a.tok[row] = pick;
+      a.logp[row] = (zrow[pick] * a.inv_temp - mz) - logf(Sp);
+    }
   }
 }
 
-template <int NQ>
+template <int NQ, bool NUCLEUS>
 hipError_t launch_full(const SampleArgs& a, hipStream_t st) {
-  sample_full_k<NQ><<<a.N, ST, 0, st>>>(a);
+  sample_full_k<NQ, NUCLEUS><<<a.N, ST, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -888,8 +1036,13 @@ hipError_t launch_sample_tokens(const float* logits, const float* uniforms, int3
   SampleArgs a{logits, uniforms, tokens, logp, N, V, top_k, 1.0f / temperature, top_p};
   if (top_k > 0 && top_k <= kLeanK && top_k < V && V > 8 * ST && V % 4 == 0)
     return V > 32 * ST ? launch_lean<16>(a, st) : V > 16 * ST ? launch_lean<8>(a, st) : launch_lean<4>(a, st);
-  if ((top_k == 0 || top_k >= V) && top_p >= 1.0f && V > 8 * ST && V % 4 == 0)
-    return V > 32 * ST ? launch_full<16>(a, st) : V > 16 * ST ? launch_full<8>(a, st) : launch_full<4>(a, st);
+  if ((top_k == 0 || top_k >= V) && V > 8 * ST && V % 4 == 0) {
+    if (top_p >= 1.0f)
+      return V > 32 * ST ? launch_full<16, false>(a, st) : V > 16 * ST ? launch_full<8, false>(a, st)
+                                                          : launch_full<4, false>(a, st);
+    return V > 32 * ST ? launch_full<16, true>(a, st) : V > 16 * ST ? launch_full<8, true>(a, st)
+                                                       : launch_full<4, true>(a, st);
+  }
   const int need = (V + ST - 1) / ST;
   if (need <= 1) return launch_c<1>(a, st);
   if (need <= 2) return launch_c<2>(a, st);

@@ -177,6 +177,31 @@ def test_sample_lean_no_truncation(dev):
             assert (tok == 0).all()
 
 
+def test_sample_lean_nucleus(dev):
+    """Top-p without top-k for 4096 < V, V a multiple of 4 (the lean kernel's search on the
+    probabilities' bit patterns): V = 6000 and 12000; logits that grow with the id; equal logits
+    (every id ties at the threshold: the nucleus p = 0.5 over V = 8192 is ids 0..4095 and u
+    draws floor(4096 u)); logits within 1e-4 of each other (more than 512 ids share the first
+    12 bits, so the block search decides every bit)."""
+    _case(dev, 24, 6000, 0.9, 0, 0.9, 23)
+    _case(dev, 24, 12000, 1.1, 0, 0.7, 24)
+    g = np.random.default_rng(25)
+    V = 32000
+    rising = np.tile(np.linspace(-4.0, 4.0, V, dtype=np.float32), (6, 1))
+    u = g.random(6).astype(np.float32)
+    tok, lp = _run(dev, rising, u, 1.0, 0, 0.9)
+    check_rows(rising, u, tok, lp, 1.0, 0, 0.9)
+    flat = np.full((4, 8192), 0.7, np.float32)
+    u = np.array([0.0, 0.25, 0.99, 0.5 + 1e-4], np.float32)
+    tok, lp = _run(dev, flat, u, 1.0, 0, 0.5)
+    assert list(tok) == [0, 1024, 4055, 2048]
+    np.testing.assert_allclose(lp, -np.log(4096.0), atol=1e-6)
+    near = (0.7 + 1e-4 * g.standard_normal((8, V))).astype(np.float32)
+    u = g.random(8).astype(np.float32)
+    tok, lp = _run(dev, near, u, 1.0, 0, 0.6)
+    check_rows(near, u, tok, lp, 1.0, 0, 0.6)
+
+
 def test_sample_peaked_and_greedy(dev):
     """Peaked logits (scale 30): the nucleus holds one or two ids; top_k = 1 is the argmax
     with logp 0."""
