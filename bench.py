@@ -362,7 +362,7 @@ def scoring_leg(steps: int, warmup: int, with_cpu: bool = True):
         rate, done, used = _oracle_rows_per_s(
             lambda i, k: oracle.score_actions(w_out, s_host[i:i + k], a_host[i:i + k]), n)
         blas = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "0")) or 10 ** 6)
-        cpu = {"value": rate, "unit": "rows/s", "cores": blas, "kind": "oracle",
+        cpu = {"value": rate, "unit": "rows/s", "cores": len(os.sched_getaffinity(0)), "threads": blas, "kind": "oracle",
                "sample": f"{done} of {n} rows through oracle.score_actions (fp64 numpy; the head product "
                          f"on up to {blas} BLAS threads), {used:.1f} s"}
     flops = 2.0 * n * cfg.d_model * cfg.vocab
@@ -424,7 +424,7 @@ def sampling_leg(steps: int, warmup: int, with_cpu: bool = True):
         u_host = u.cpu().numpy()
         rate, done, used = _oracle_rows_per_s(
             lambda i, k: oracle.sample_tokens(l_host[i:i + k], u_host[i:i + k], 0.8, 50, 0.95), n)
-        cpu = {"value": rate, "unit": "rows/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": rate, "unit": "rows/s", "cores": len(os.sched_getaffinity(0)), "threads": 1, "kind": "oracle",
                "sample": f"{done} of {n} rows through oracle.sample_tokens (fp64 numpy), {used:.1f} s"}
     nbytes = n * V * 4.0 + n * 12.0
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -867,7 +867,22 @@ def main():
             line["rl_scoring"] = scoring_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
             line["sampling"] = sampling_leg(max(3, min(args.steps, 10)), 2, not args.no_cpu_baseline)
         line["bptt"] = bptt_leg(3, 1, not args.no_cpu_baseline)
+    add_copy_denominator(line, bw)
     print(json.dumps(line), flush=True)
+
+
+def add_copy_denominator(x, bw) -> None:
+    """Give every HBM roofline block of the line the copy bandwidth measured in the same run as its
+    second denominator (the legs that build theirs without it included)."""
+    if isinstance(x, dict):
+        if x.get("bound") == "hbm" and "achieved" in x and "measured_copy_GBps" not in x and bw:
+            x["measured_copy_GBps"] = bw["copy_GBps"]
+            x["frac_of_measured_copy"] = x["achieved"] / bw["copy_GBps"]
+        for v in x.values():
+            add_copy_denominator(v, bw)
+    elif isinstance(x, list):
+        for v in x:
+            add_copy_denominator(v, bw)
 
 
 if __name__ == "__main__":

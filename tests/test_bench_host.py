@@ -48,3 +48,18 @@ def test_algorithmic_bytes_match_the_closed_form(name):
 def test_small_workload_bytes_are_the_quoted_figure():
     wl = CONFIGS["small"]
     assert round(bench.algorithmic_decoder_bytes(wl.model, wl.batch, wl.seq_len) / 1e9, 2) == 37.05
+
+
+def test_every_hbm_roofline_block_gets_the_copy_denominator():
+    """bench.py gives each HBM roofline block of its line, nested legs included, the copy
+    bandwidth measured in the same run as a second denominator, and leaves other bounds and
+    blocks that already carry one as they are."""
+    import bench
+    line = {"roofline": {"bound": "hbm", "achieved": 4000.0, "measured_copy_GBps": 4900.0},
+            "leg": {"late_steps": {"roofline": {"bound": "hbm", "achieved": 2500.0}}},
+            "scoring": {"roofline": {"bound": "mfma", "achieved": 1000.0}}}
+    bench.add_copy_denominator(line, {"copy_GBps": 5000.0})
+    assert line["roofline"]["measured_copy_GBps"] == 4900.0 and "frac_of_measured_copy" not in line["roofline"]
+    late = line["leg"]["late_steps"]["roofline"]
+    assert late["measured_copy_GBps"] == 5000.0 and late["frac_of_measured_copy"] == 0.5
+    assert "measured_copy_GBps" not in line["scoring"]["roofline"]
