@@ -768,8 +768,9 @@ void sample_topk_k(SampleArgs a) {
 // NUCLEUS (top-p < 1): the threshold is searched on the probabilities' bit patterns, which order
 // non-negative floats as their values, so only the probabilities stay in registers.  Ranking by
 // probability instead of by logit merges logits whose fp32 probabilities are equal; those become
-// ties and are resolved by id.  The first 12 bits are decided over the row with block mass sums;
-// when at most 512 elements share the decided prefix, wave 0 decides the rest on a list.
+// ties and are resolved by id.  The 12 bits below the two that are always 0 are decided over the
+// row with block mass sums; when at most 512 elements share the decided prefix, wave 0 decides the
+// rest on a list.
 // Ties at the threshold stay in id order while the mass ranked before them is short of the
 // target: their number comes from that same comparison (monotone in the rank, so a binary
 // search), and when fewer ties are kept than exist, a bitwise search finds the id of the last
@@ -842,10 +843,12 @@ void sample_full_k(SampleArgs a) {
       return red.sum(m);
     };
     // the largest bit pattern tau whose mass at or above it still reaches the target
+    // probabilities lie in [0, 1] (the largest logit gives exp2(0) = 1 exactly), so bits 31 and 30
+    // of every pattern are 0 and the search starts at bit 29
     uint32_t tau = 0;
-    int bit = 30;   // the sign bit of a probability is 0
+    int bit = 29;
 #pragma nounroll
-    for (; bit >= 31 - kPrefixBits; --bit) {
+    for (; bit >= 30 - kPrefixBits; --bit) {
       const uint32_t cand = tau | (1u << bit);
       if (mass_ge(cand) >= need) tau = cand;
     }
@@ -903,7 +906,7 @@ void sample_full_k(SampleArgs a) {
     const float mass_gt = red.sum(gt);
     const int n_eq = static_cast<int>(red.sum(eq));
     const float e_eq = __builtin_bit_cast(float, tau);
-    // ties kept: the ranks r with mass_gt + r * e_eq < need (true at r = 0, monotone in r)
+    // ties kept: the ranks r with mass_gt + r * e_eq < need (monotone in r)
     int lo_r = 0, hi_r = n_eq;
     while (lo_r < hi_r) {
       const int mid = (lo_r + hi_r) / 2;
@@ -911,10 +914,32 @@ void sample_full_k(SampleArgs a) {
       else hi_r = mid;
     }
     const int n_keep = lo_r;
-    // fewer kept than tied: the id of the last kept tie (the largest id x with fewer than
-    // n_keep ties below it; ids are below 2^15)
+    // The search and mass_gt add the same masses in different orders, so mass_gt can round to
+    // need or above: then no tie is kept (the mass above the threshold already reaches the
+    // target), as the comparison at rank 0 says.
+    // Fewer kept than tied: the id of the last kept tie.  Up to 64 ties are gathered and wave 0
+    // ranks their ids; more take a bitwise search (the largest id x with fewer than n_keep ties
+    // below it; ids are below 2^15).
     int id_cut = 0x7fffffff;
-    if (n_keep < n_eq) {
+    if (n_keep == 0) {
+      id_cut = -1;
+    } else if (n_keep < n_eq && n_eq <= 64) {
+      float n_all;
+      int tp = static_cast<int>(red.excl_scan(eq, n_all));
+      int* tid = reinterpret_cast<int*>(lk);   // the list is no longer read
+      each([&](int i, int c, float y) {
+        if (bits(y) == tau) tid[tp++] = id_of(i, c);
+      });
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        const int mine = lane < n_eq ? tid[lane] : 0x7fffffff;
+        int rank = 0;
+        for (int j = 0; j < n_eq; ++j) rank += tid[j] < mine ? 1 : 0;
+        if (lane < n_eq && rank == n_keep - 1) bcast = static_cast<uint32_t>(mine);
+      }
+      __syncthreads();
+      id_cut = static_cast<int>(bcast);
+    } else if (n_keep < n_eq) {
       int x = 0;
 #pragma nounroll
       for (int b = 14; b >= 0; --b) {

@@ -200,6 +200,24 @@ def test_sample_lean_nucleus(dev):
     u = g.random(8).astype(np.float32)
     tok, lp = _run(dev, near, u, 1.0, 0, 0.6)
     check_rows(near, u, tok, lp, 1.0, 0, 0.6)
+    # 20 equal maxima spread over threads and pieces, the rest far below: the nucleus 0.5 ends
+    # inside the ties, which keep the first 11 by id (the gathered-ties rank in one wave)
+    ties = np.array([5, 700, 2049, 2050, 4000, 4097, 5000, 6000, 6001, 7000, 7001, 7500, 7600, 7700, 7800,
+                     7900, 8000, 8100, 8150, 8191])
+    tied = np.full((8, 8192), -10.0, np.float32)
+    tied[:, ties] = 3.0
+    u = ((np.arange(8) + 0.5) / 8).astype(np.float32)
+    tok, lp = _run(dev, tied, u, 1.0, 0, 0.5)
+    check_rows(tied, u, tok, lp, 1.0, 0, 0.5)
+    assert np.isin(tok, ties[:11]).all() and tok[-1] == ties[10]
+    # torch-generated rows (the bench's sampling input): in one row the fp32 mass above the
+    # nucleus threshold rounds up to the target, so the tie at the threshold is not kept
+    tg = torch.Generator(device="cpu").manual_seed(9)
+    logits = (torch.randn(512, V, generator=tg) * 2.0).numpy()
+    u = torch.rand(512, generator=tg).numpy()
+    tok, lp = _run(dev, logits, u, 0.8, 0, 0.95)
+    rows = np.arange(430, 450)
+    check_rows(logits[rows], u[rows], tok[rows], lp[rows], 0.8, 0, 0.95, max_border_frac=0.1)
 
 
 def test_sample_peaked_and_greedy(dev):
