@@ -244,6 +244,9 @@ int rlt_logits(const rlt_model* model, const float* s, int64_t n_rows, float* lo
  *   the kept ids in increasing order split [0, 1) in proportion to exp(z); the first id whose
  *   cumulative share exceeds u_r is drawn (u_r at or past the top edge draws the last kept id);
  *   logp_r = z[drawn] - log sum_kept exp(z).
+ * The decisions are taken in fp32.  With top-p and no top-k at 4096 < V (V a multiple of 4)
+ * the ranking is by the fp32 probability exp(z - max z), so logits whose probabilities round
+ * to the same fp32 value rank as ties, by id; the other settings rank by z itself.
  * temperature > 0; top_k >= 0 (0 = no top-k); 0 < top_p <= 1 (1 = no top-p). */
 typedef struct rlt_sampling {
   float temperature;
