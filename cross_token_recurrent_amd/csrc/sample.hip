@@ -10,9 +10,12 @@
 //   proportion to exp(z) and the first whose cumulative share exceeds u is drawn;
 //   logp = z[drawn] - log sum_kept exp(z).
 //
-// One workgroup of 512 threads per row.  The row is staged through LDS so that thread t holds
-// the C consecutive logits [t*C, t*C + C) in registers as order-preserving 32-bit keys
-// (token-id order is then thread order for every scan).
+// Three kernels, one workgroup of 512 threads per row, chosen per call:
+//  - sample_topk_k (0 < top-k <= 128, 4096 < V, V a multiple of 4) and sample_full_k (no top-k,
+//    same V) load the row straight into registers (at most 128 VGPRs, two rows per CU);
+//  - sample_k (every other case) stages the row through LDS so that thread t holds the C
+//    consecutive logits [t*C, t*C + C) in registers as order-preserving 32-bit keys (token-id
+//    order is then thread order for every scan).  Its two paths:
 //
 // Top-k (k at most the thread count): the k-th largest of the per-thread maxima bounds the
 // k-th largest logit from below (k threads each hold an element at least that large).  The
@@ -604,15 +607,15 @@ __global__ __launch_bounds__(ST) void sample_k(SampleArgs a) {
 }
 
 // Lean top-k kernel (0 < k <= kLeanK, 4096 < V, V a multiple of 4): no LDS stage and at most
-// 128 VGPRs, so two rows share a CU and one row's load overlaps another row's work.  Thread t
-// loads the 16-byte pieces t, t + 512, ... of the row straight into registers as keys (ids
-// 4q..4q+3 of piece q).  The bound and the gather are those of the list path above, with at
-// most kLeanList candidates.  When the bound admits more (for example logits that grow with the
-// id), the exact top-k threshold is found by block count passes over the keys, the ties at it
-// are cut in id order (a bitwise search for the need-th smallest tie id, when more tie than
-// are needed), and exactly the k survivors are gathered.  The gather's order is
-// thread-major, so wave 0 places every entry at its rank by id (ids are distinct) before
-// finishing the row on the list.
+// 128 VGPRs, so two rows share a CU and each fills the other's waits (a row's single-wave
+// finish leaves the rest of its workgroup idle).  Thread t loads the 16-byte pieces t, t + 512,
+// ... of the row straight into registers as keys (ids 4q..4q+3 of piece q).  The bound and the
+// gather are those of the list path above, with at most kLeanList candidates.  When the bound
+// admits more (for example logits that grow with the id), the exact top-k threshold is found by
+// block count passes over the row re-read from L2, the ties at it are cut in id order (a
+// bitwise search for the need-th smallest tie id, when more tie than are needed), and exactly
+// the k survivors are gathered.  The gather's order is thread-major, so wave 0 places every
+// entry at its rank by id (ids are distinct) before finishing the row on the list.
 template <int NQ>
 __global__ __launch_bounds__(ST) __attribute__((amdgpu_waves_per_eu(4)))
 void sample_topk_k(SampleArgs a) {
