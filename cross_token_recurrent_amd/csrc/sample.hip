@@ -73,6 +73,24 @@ __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 // lanes of the wave for which p holds (the same value on every lane)
 __device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
+// the smallest and largest key of the wave (every lane gets both)
+__device__ __forceinline__ void wave_min_max(uint32_t& lo, uint32_t& hi) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), d, 64)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), d, 64)));
+  }
+}
+// A bitwise search for the largest key with a property that every key of a set has can start
+// below the bits all the keys share: those bits come out as the shared prefix either way.
+// Returns the prefix and sets `bit` to the highest bit where the keys differ (-1 if all equal).
+__device__ __forceinline__ uint32_t shared_prefix(uint32_t kmin, uint32_t kmax, int& bit) {
+  const uint32_t diff = kmin ^ kmax;
+  bit = diff ? 31 - __clz(static_cast<int>(diff)) : -1;
+  if (bit < 0) return kmin;     // one key: it is the answer
+  if (bit == 31) return 0u;     // no shared bit
+  return kmin & ~((2u << bit) - 1u);
+}
 
 // Block reductions over SW waves: each uses its own slot of a two-deep ring, so one barrier per
 // call is enough (a slot is rewritten only after every thread has passed the next call's
@@ -158,11 +176,21 @@ __device__ void finish_on_list(const SampleArgs& a, int row, const uint32_t* lk,
     kk[i] = j < n ? lk[j] : 0u;   // past the list: below every candidate key
     id[i] = j < n ? lid[j] : 0;
   }
-  // top-k: the largest key whose count at or above it still reaches k
+  // top-k: the largest key whose count at or above it still reaches k (every list entry counts
+  // at the list's shared prefix, n >= k)
   const int k = a.top_k;
-  uint32_t tk = 0;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (lane * P + i < n) {
+      kmin = min(kmin, kk[i]);
+      kmax = max(kmax, kk[i]);
+    }
+  wave_min_max(kmin, kmax);
+  int bit0;
+  uint32_t tk = shared_prefix(kmin, kmax, bit0);
 #pragma nounroll
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = bit0; bit >= 0; --bit) {
     const uint32_t cand = tk | (1u << bit);
     int cnt = 0;
 #pragma unroll
@@ -196,9 +224,19 @@ __device__ void finish_on_list(const SampleArgs& a, int row, const uint32_t* lk,
 #pragma unroll
     for (int i = 0; i < P; ++i) sk += e[i];
     const float need = a.top_p * wave_sum(sk);
-    uint32_t tp = 0;
+    // the survivors' whole mass (the same sums as need's) reaches need at their shared prefix
+    uint32_t smin = 0xffffffffu, smax = 0u;
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      if (keep[i]) {
+        smin = min(smin, kk[i]);
+        smax = max(smax, kk[i]);
+      }
+    wave_min_max(smin, smax);
+    int bitp;
+    uint32_t tp = shared_prefix(smin, smax, bitp);
 #pragma nounroll
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = bitp; bit >= 0; --bit) {
       const uint32_t cand = tp | (1u << bit);
       float m = 0.f;
 #pragma unroll
